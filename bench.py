@@ -1,0 +1,207 @@
+"""Benchmark of the KDA chunked forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload i]
+
+A step is one kda_fwd call (chunk table, prep, state/output stages) over one batch of
+seeded synthetic input already resident in HBM.  Default workload: B=2, T=4096, H=16,
+K=V=128, fp32 initial and final state (index 1 of workloads.config).  Prints one JSON line.
+
+roofline: the dominant kernel (largest average duration, from HIP events recorded around
+each stage on the launch stream over the timed steps) against HBM: achieved = that
+kernel's algorithmic bytes per launch / its average duration.  Algorithmic bytes:
+prep = q, k, g (3 x 256 B) + beta (2 B) per head-token; state = v + out (2 x 256 B) per
+head-token + initial/final state; whole path = 1282 B per head-token + states.
+cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
+
+--copy-calibration runs only a plain device-to-device copy of known size (for scaling the
+FETCH_SIZE / WRITE_SIZE hardware counters); it prints the bytes copied per launch.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+BYTES_PER_HT = 1282              # q, k, v, g (4 x 256) + beta (2) + out (256)
+FLOPS_PER_HT = 122880            # dense contractions per head-token (three 16x128x128 per chunk + intra-chunk)
+METRIC = "KDA fwd head-tokens/sec on 1 MI355X + % of HBM/MFMA roofline"
+
+
+def state_bytes(w):
+    per = 128 * 128
+    b = 0
+    if w.initial_state is not None:
+        b += w.N * w.H * per * (2 if w.state_dtype == "bf16" else 4)
+    if w.final_dtype != "none":
+        b += w.N * w.H * per * (2 if w.final_dtype == "bf16" else 4)
+    return b
+
+
+def hip_runtime():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def copy_calibration(steps):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                                           "launches": steps}}), flush=True)
+
+
+def cpu_baseline(w):
+    import numpy as np
+
+    import oracle
+    from gated_delta_rule_86_amd import workloads as W
+    oracle.build()
+    threads = oracle.max_threads()
+    chains = w.N * w.H
+    if w.head_tokens <= 3_000_000:
+        ws, sample = w, "the whole workload"
+    else:  # first T' tokens of every sequence of a single long batch row
+        Tp = max(16, 2_000_000 // (w.H * w.B))
+        sl = lambda a: np.ascontiguousarray(a[:, :Tp])
+        ws = W.Workload(w.name, w.B, Tp, w.H, sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), w.A_log,
+                        w.dt_bias, w.lower_bound, w.scale, w.initial_state, w.state_dtype, w.final_dtype,
+                        None)
+        sample = f"first {Tp} tokens of each of the {w.B * w.H} (row, head) chains"
+    t0 = time.perf_counter()
+    oracle.kda_fwd(ws.q, ws.k, ws.v, ws.g, ws.beta, ws.scale, ws.A_log, ws.dt_bias, ws.lower_bound,
+                   ws.initial_state, cu_seqlens=ws.cu_seqlens)
+    dt = time.perf_counter() - t0
+    return {"value": ws.head_tokens / dt, "unit": "head-tokens/s", "cores": min(threads, chains),
+            "kind": "oracle", "sample": f"{sample} ({ws.head_tokens} head-tokens, {dt:.2f} s wall, "
+            f"{threads} threads for {chains} chains)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="index into workloads.config (0..4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the (sequence, "
+              "head) chains shard across GPUs with no communication, but no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    from gated_delta_rule_86_amd import kda
+    from gated_delta_rule_86_amd import workloads as W
+
+    w = W.config(args.workload)
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+    q, k, v, g, beta = (t(getattr(w, n)) for n in ("q", "k", "v", "g", "beta"))
+    A_log = torch.from_numpy(w.A_log).to(dev)
+    dt_bias = torch.from_numpy(w.dt_bias).to(dev)
+    h0 = None
+    if w.initial_state is not None:
+        h0 = t(w.initial_state) if w.initial_state.dtype.name == "uint16" else torch.from_numpy(w.initial_state).to(dev)
+    cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens).to(dev)
+    out = torch.empty_like(q)
+    fin = None
+    if w.final_dtype != "none":
+        fin = torch.empty((w.N, w.H, 128, 128), device=dev,
+                          dtype=torch.float32 if w.final_dtype == "fp32" else torch.bfloat16)
+    ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.N, cu is not None), dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        kda.fwd(q, k, v, g, beta, w.scale, out, A_log, dt_bias, w.lower_bound, h0, fin, cu,
+                workspace=ws, stage_events=events)
+
+    hip = hip_runtime()
+    ev = []
+    for _ in range(args.steps):
+        row = []
+        for _ in range(4):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            row.append(e.value)
+        ev.append(row)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_names = ["chunk_table_kernel", "prep_kernel", "state_kernel"]
+    stage_ms = [0.0, 0.0, 0.0]
+    for i in range(args.steps):
+        for j in range(3):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[i][j], ev[i][j + 1]) == 0
+            stage_ms[j] += ms.value / args.steps
+    for row in ev:
+        for e in row:
+            hip.hipEventDestroy(e)
+
+    ht = w.head_tokens
+    ms_per_step = elapsed / args.steps * 1e3
+    value = ht / (elapsed / args.steps)
+    kernel_bytes = {"chunk_table_kernel": 8 * (w.N + 1),
+                    "prep_kernel": ht * (3 * 256 + 2),
+                    "state_kernel": ht * 2 * 256 + state_bytes(w)}
+    dom = max(range(3), key=lambda j: stage_ms[j])
+    dname = stage_names[dom]
+    achieved = kernel_bytes[dname] / (stage_ms[dom] * 1e-3) / 1e9
+    path_bytes = ht * BYTES_PER_HT + state_bytes(w)
+    path_gbps = path_bytes / (ms_per_step * 1e-3) / 1e9
+    path_tflops = ht * FLOPS_PER_HT / (ms_per_step * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(w.describe(), head_tokens=ht),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": dname,
+                     "kernel_ms": stage_ms[dom], "kernel_algorithmic_bytes": kernel_bytes[dname]},
+        "path": {"algorithmic_bytes": path_bytes, "achieved_GBps": path_gbps,
+                 "hbm_frac": path_gbps / HBM_PEAK_GBPS, "achieved_TFLOPs": path_tflops,
+                 "mfma_frac": path_tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "stage_ms": dict(zip(stage_names, stage_ms))},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+// kda_api.cpp -- host side of libkda.so: argument validation, workspace layout and the
+// C ABI declared in include/kda.h.  Validation is plain host code that touches no HIP
+// API, so every error path can be exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void *p, size_t bytes)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+size_t state_elem_bytes(kda_state_dtype d) { return d == KDA_STATE_BF16 ? 2 : 4; }
+
+// Everything kda_fwd checks before touching the device.
+kda_status validate(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    float scale, void *out, const float *A_log, const float *dt_bias,
+                    float lower_bound, const void *h0, kda_state_dtype h0_dt, void *ht,
+                    kda_state_dtype ht_dt, const int64_t *cu, const int64_t *cu_host, int64_t B,
+                    int64_t T, int64_t H, int64_t N, int64_t K, int64_t V, void *ws,
+                    size_t ws_bytes, kda::Layout *lay)
+{
+    // token tensors may be NULL only when they hold no elements (B * T == 0)
+    const bool no_tokens = (T == 0);
+    if ((!no_tokens && (!q || !k || !v || !g || !beta || !out)) || !A_log || !dt_bias)
+        return KDA_ERR_NULL;
+    if (B < 1 || T < 0 || H < 1)
+        return KDA_ERR_SHAPE;
+    if (cu) {
+        if (B != 1 || N < 1)
+            return KDA_ERR_SHAPE;
+    } else if (N != 0 && N != B) {
+        return KDA_ERR_SHAPE;
+    }
+    // overflow guard on element counts (tokens * heads * 128 must fit comfortably)
+    if (T > ((int64_t)1 << 40) / B || (B * T) > ((int64_t)1 << 46) / (H * kda::kD))
+        return KDA_ERR_SHAPE;
+    if (K != kda::kD || V != kda::kD)
+        return KDA_ERR_HEAD_DIM;
+    auto dt_ok = [](kda_state_dtype d) {
+        return d == KDA_STATE_NONE || d == KDA_STATE_BF16 || d == KDA_STATE_FP32;
+    };
+    if (!dt_ok(h0_dt) || !dt_ok(ht_dt))
+        return KDA_ERR_DTYPE;
+    if ((h0 == nullptr) != (h0_dt == KDA_STATE_NONE) || (ht == nullptr) != (ht_dt == KDA_STATE_NONE))
+        return KDA_ERR_DTYPE;
+    if (h0 && ht && h0_dt != ht_dt)
+        return KDA_ERR_DTYPE;
+    if (!(lower_bound >= -5.0f && lower_bound <= 0.0f))  // also rejects NaN
+        return KDA_ERR_LOWER_BOUND;
+    if (!isfinite(scale))
+        return KDA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(out, 16) || !aligned(beta, 2) || !aligned(A_log, 4) || !aligned(dt_bias, 16) ||
+        (h0 && !aligned(h0, 16)) || (ht && !aligned(ht, 16)) || (cu && !aligned(cu, 8)) ||
+        (ws && !aligned(ws, kda::kAlign)))
+        return KDA_ERR_ALIGN;
+
+    const int64_t n_seq = cu ? N : B;
+    const size_t tok_bytes = (size_t)B * (size_t)T * (size_t)H * kda::kD * 2;
+    const size_t beta_bytes = (size_t)B * (size_t)T * (size_t)H * 2;
+    const Range rq = range_of(q, tok_bytes), rk = range_of(k, tok_bytes), rv = range_of(v, tok_bytes),
+                rg = range_of(g, tok_bytes), rb = range_of(beta, beta_bytes), ro = range_of(out, tok_bytes);
+    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rg) || overlap(ro, rb))
+        return KDA_ERR_ALIAS;
+    if (ht) {
+        const Range rs = range_of(ht, (size_t)n_seq * (size_t)H * kda::kD * kda::kD * state_elem_bytes(ht_dt));
+        if (overlap(rs, rq) || overlap(rs, rk) || overlap(rs, rv) || overlap(rs, rg) ||
+            overlap(rs, rb) || overlap(rs, ro))
+            return KDA_ERR_ALIAS;
+        if (h0 && h0 != ht) {
+            const Range ri = range_of(h0, (size_t)n_seq * (size_t)H * kda::kD * kda::kD * state_elem_bytes(h0_dt));
+            if (overlap(rs, ri))
+                return KDA_ERR_ALIAS;
+        }
+    }
+    if (h0) {
+        const Range ri = range_of(h0, (size_t)n_seq * (size_t)H * kda::kD * kda::kD * state_elem_bytes(h0_dt));
+        if (overlap(ri, ro))
+            return KDA_ERR_ALIAS;
+    }
+
+    if (!kda::make_layout(B, T, H, cu ? N : 0, cu != nullptr, lay))
+        return KDA_ERR_SHAPE;
+    if (!ws || ws_bytes < lay->total)
+        return KDA_ERR_WORKSPACE;
+    if (cu && cu_host) {
+        if (cu_host[0] != 0 || cu_host[N] != T)
+            return KDA_ERR_CU_SEQLENS;
+        for (int64_t i = 0; i < N; ++i)
+            if (cu_host[i + 1] < cu_host[i])
+                return KDA_ERR_CU_SEQLENS;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char *kda_status_string(int s)
+{
+    switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid B/T/H/N or cu_seqlens with B != 1";
+    case KDA_ERR_HEAD_DIM: return "KDA_ERR_HEAD_DIM: K and V must be 128";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: invalid or mismatched state dtypes";
+    case KDA_ERR_LOWER_BOUND: return "KDA_ERR_LOWER_BOUND: lower_bound must be in [-5, 0]";
+    case KDA_ERR_SCALE: return "KDA_ERR_SCALE: scale must be finite";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer alignment requirement violated";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_CU_SEQLENS: return "KDA_ERR_CU_SEQLENS: cu_seqlens content invalid";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP launch or query failed";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens)
+{
+    kda::Layout lay;
+    if (!kda::make_layout(B, T, H, has_cu_seqlens ? N : (N == B ? B : 0), has_cu_seqlens != 0, &lay))
+        return 0;
+    return lay.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    float scale, void *out, const float *A_log, const float *dt_bias,
+                    float lower_bound, const void *initial_state, kda_state_dtype initial_state_dtype,
+                    void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                    const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                    int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                    void *const *events)
+{
+    kda::Layout lay;
+    kda_status st = validate(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                             initial_state, initial_state_dtype, final_state, final_state_dtype,
+                             cu_seqlens, cu_seqlens_host, B, T, H, N, K, V, workspace,
+                             workspace_bytes, &lay);
+    if (st != KDA_OK)
+        return st;
+    kda::FwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.g = static_cast<const uint16_t *>(g);
+    a.beta = static_cast<const uint16_t *>(beta);
+    a.out = static_cast<uint16_t *>(out);
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.scale = scale;
+    a.lower_bound = lower_bound;
+    a.h0 = initial_state;
+    a.ht = final_state;
+    a.h0_dtype = (int)initial_state_dtype;
+    a.ht_dtype = (int)final_state_dtype;
+    a.cu = cu_seqlens;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.N = lay.n_seq;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.lay = lay;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+        return events == nullptr || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+    };
+    if (!mark(0) || kda::launch_chunk_table(a, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (!mark(1) || kda::launch_prep(a, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (!mark(2) || kda::launch_state(a, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (!mark(3))
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                   float scale, void *out, const float *A_log, const float *dt_bias,
+                   float lower_bound, const void *initial_state, kda_state_dtype initial_state_dtype,
+                   void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                   const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                   int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                         float scale, void *out, const float *A_log, const float *dt_bias,
+                         float lower_bound, const void *initial_state,
+                         kda_state_dtype initial_state_dtype, void *final_state,
+                         kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                         const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                         int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                         void *const *stage_events)
+{
+    if (!stage_events || !stage_events[0] || !stage_events[1] || !stage_events[2] || !stage_events[3])
+        return KDA_ERR_NULL;
+    return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, stage_events);
+}
+
+kda_status kda_fwd_device_status(const void *workspace, int32_t *status_out, void *stream)
+{
+    if (!workspace || !status_out)
+        return KDA_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(status_out, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status kda_chunk_table(const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
+                           void *workspace, size_t workspace_bytes, int64_t *seq_off_host,
+                           int64_t *n_total_host, int32_t *status_host, void *stream)
+{
+    kda::Layout lay;
+    if (B < 1 || T < 0 || H < 1)
+        return KDA_ERR_SHAPE;
+    if (!kda::make_layout(B, T, H, cu_seqlens ? N : 0, cu_seqlens != nullptr, &lay))
+        return KDA_ERR_SHAPE;
+    if (!workspace || workspace_bytes < lay.total)
+        return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, kda::kAlign) || (cu_seqlens && !aligned(cu_seqlens, 8)))
+        return KDA_ERR_ALIGN;
+    kda::FwdArgs a;
+    memset(&a, 0, sizeof a);
+    a.cu = cu_seqlens;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.N = lay.n_seq;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.lay = lay;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::launch_chunk_table(a, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    bool copied = false;
+    if (seq_off_host) {
+        if (hipMemcpyAsync(seq_off_host, a.ws + lay.off_seq_off, sizeof(int64_t) * (lay.n_seq + 1),
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return KDA_ERR_HIP;
+        copied = true;
+    }
+    if (n_total_host) {
+        if (hipMemcpyAsync(n_total_host, a.ws + lay.off_status + 8, sizeof(int64_t),
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return KDA_ERR_HIP;
+        copied = true;
+    }
+    if (status_host) {
+        if (hipMemcpyAsync(status_host, a.ws + lay.off_status, sizeof(int32_t), hipMemcpyDeviceToHost,
+                           s) != hipSuccess)
+            return KDA_ERR_HIP;
+        copied = true;
+    }
+    if (copied && hipStreamSynchronize(s) != hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+"""Thin Python binding of libkda.so (the C ABI in include/kda.h).
+
+Argument marshalling only: every step of the forward pass runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  If libkda.so is
+missing or cannot be loaded, every call raises; there is no fallback path.
+
+``fwd`` mirrors the FlashKDA README "Kernel API" entry point:
+
+    fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+        initial_state=None, final_state=None, cu_seqlens=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_OK = 0
+STATUS_NAMES = {
+    0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_HEAD_DIM", 4: "KDA_ERR_DTYPE",
+    5: "KDA_ERR_LOWER_BOUND", 6: "KDA_ERR_SCALE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_WORKSPACE",
+    9: "KDA_ERR_CU_SEQLENS", 10: "KDA_ERR_HIP", 11: "KDA_ERR_ALIAS",
+}
+STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
+
+# every symbol include/kda.h declares
+EXPORTS = ("kda_fwd", "kda_fwd_timed", "kda_fwd_workspace_size", "kda_status_string",
+           "kda_fwd_device_status", "kda_chunk_table", "kda_version")
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str = "kda_fwd"):
+        self.status = status
+        super().__init__(f"{what} failed: {STATUS_NAMES.get(status, status)}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libkda.so (built in-tree by ``python -m gated_delta_rule_86_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gated_delta_rule_86_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    L.kda_fwd.restype = ctypes.c_int
+    L.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, ctypes.c_int, vp,
+                          ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    L.kda_fwd_timed.restype = ctypes.c_int
+    L.kda_fwd_timed.argtypes = L.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+    L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_fwd_device_status.restype = ctypes.c_int
+    L.kda_fwd_device_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+    L.kda_chunk_table.restype = ctypes.c_int
+    L.kda_chunk_table.argtypes = [vp, i64, i64, i64, i64, vp, ctypes.c_size_t,
+                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                  ctypes.POINTER(ctypes.c_int32), vp]
+    L.kda_version.restype = ctypes.c_int
+    L.kda_version.argtypes = []
+    _lib = L
+    return L
+
+
+def workspace_size(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -> int:
+    return int(lib().kda_fwd_workspace_size(B, T, H, N, 1 if varlen else 0))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _state_code(t) -> int:
+    import torch
+    if t is None:
+        return STATE_NONE
+    if t.dtype == torch.bfloat16:
+        return STATE_BF16
+    if t.dtype == torch.float32:
+        return STATE_FP32
+    raise ValueError(f"state dtype must be bf16 or fp32, got {t.dtype}")
+
+
+def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
+        final_state=None, cu_seqlens=None, *, cu_seqlens_host=None, workspace=None, stream=None,
+        stage_events=None):
+    """KDA forward pass on torch device tensors; writes ``out`` and ``final_state`` in place.
+
+    q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; out: bf16 [B, T, H, 128];
+    A_log: fp32 [H]; dt_bias: fp32 [H, 128]; states: bf16/fp32 [N, H, 128, 128] or None;
+    cu_seqlens: int64 [N+1] device tensor or None (then N = B).
+    cu_seqlens_host: optional host copy (sequence or CPU tensor) for a synchronous check.
+    workspace: optional uint8 device tensor of at least workspace_size(...) bytes.
+    stage_events: optional sequence of 4 raw hipEvent_t handles (ints); when given the call
+    goes through kda_fwd_timed, which records them around the three stages.
+    """
+    import torch
+    L = lib()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("g", g)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, T, H, K) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [B, T, H, K] tensor")
+    for name, t in (("v", v), ("out", out)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, T, H, V) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [B, T, H, V] tensor")
+    if beta.dtype != torch.bfloat16 or tuple(beta.shape) != (B, T, H) or not beta.is_contiguous():
+        raise ValueError("beta must be a contiguous bf16 [B, T, H] tensor")
+    if A_log.dtype != torch.float32 or A_log.numel() != H or not A_log.is_contiguous():
+        raise ValueError("A_log must be a contiguous fp32 [H] tensor")
+    if dt_bias.dtype != torch.float32 or tuple(dt_bias.shape) != (H, K) or not dt_bias.is_contiguous():
+        raise ValueError("dt_bias must be a contiguous fp32 [H, K] tensor")
+    if initial_state is not None and final_state is not None and initial_state.dtype != final_state.dtype:
+        raise ValueError("initial_state and final_state dtypes must match")
+    N = B
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int64 [N+1] tensor")
+        N = cu_seqlens.numel() - 1
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (tuple(t.shape) != (N, H, V, K) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [N, H, V, K] tensor")
+    host_cu = None
+    if cu_seqlens_host is not None:
+        import numpy as np
+        host_cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int64))
+    ws_bytes = workspace_size(B, T, H, N if cu_seqlens is not None else B, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+            _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+            _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+            _ptr(cu_seqlens), None if host_cu is None else host_cu.ctypes.data,
+            B, T, H, N if cu_seqlens is not None else B, K, V, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream, q.device))
+    if stage_events is None:
+        st = L.kda_fwd(*args)
+    else:
+        evs = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e)) for e in stage_events])
+        st = L.kda_fwd_timed(*args, evs)
+    if st != KDA_OK:
+        raise KDAError(st)
+    return workspace
+
+
+def device_status(workspace, stream=None) -> int:
+    """Read the device status word after a call (synchronises the stream)."""
+    out = ctypes.c_int32(-1)
+    st = lib().kda_fwd_device_status(_ptr(workspace), ctypes.byref(out),
+                                     _stream_handle(stream, workspace.device))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_fwd_device_status")
+    return int(out.value)
+
+
+def chunk_table(cu_seqlens, B: int, T: int, H: int, workspace=None, stream=None):
+    """Run only the chunk-table stage; returns (seq_off int64 [N+1], n_total, status)."""
+    import numpy as np
+    import torch
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = cu_seqlens.device if cu_seqlens is not None else torch.device("cuda")
+    ws_bytes = workspace_size(B, T, H, N if cu_seqlens is not None else B, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    seq_off = np.zeros(N + 1, dtype=np.int64)
+    n_total = ctypes.c_int64(-1)
+    status = ctypes.c_int32(-1)
+    st = lib().kda_chunk_table(_ptr(cu_seqlens), B, T, H, N if cu_seqlens is not None else 0,
+                               _ptr(workspace), workspace.numel(),
+                               seq_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                               ctypes.byref(n_total), ctypes.byref(status),
+                               _stream_handle(stream, dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_table")
+    return seq_off, int(n_total.value), int(status.value)

@@ -17,12 +17,14 @@ deviation):
   not a multiple of 16 and the total is within 10% of N * (1 + Lmax) / 2,
   otherwise the next seed attempt is used.
 Seeds: numpy SeedSequence([config_id, attempt]).spawn(9) in the order
-  [lengths, q, k, v, g, beta, A_log, dt_bias, initial_state].
+  [lengths, q, k, v, g, beta, A_log, dt_bias, initial_state]; each tensor is drawn
+  in blocks of 2^24 values, block i from child i of that tensor's seed (PCG64).
 """
 from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -34,10 +36,10 @@ STATE_NONE, STATE_BF16, STATE_FP32 = "none", "bf16", "fp32"
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    r = ((u + bias) >> 16).astype(np.uint16)
+    u = x.view(np.uint32).copy()
     nan = np.isnan(x)
+    u += ((u >> 16) & 1) + np.uint32(0x7FFF)
+    r = (u >> 16).astype(np.uint16)
     if nan.any():
         r[nan] = 0x7FC0
     return r
@@ -89,17 +91,37 @@ class Workload:
         return d
 
 
-def _normal_bf16(rng: np.random.Generator, shape, std=1.0) -> np.ndarray:
-    n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.uint16)
-    step = 1 << 26
-    for i in range(0, n, step):
-        m = min(step, n - i)
-        x = rng.standard_normal(m, dtype=np.float32)
+_BLOCK = 1 << 24
+
+
+def _fill_normal(seq: np.random.SeedSequence, n: int, std: float, to_bf16: bool) -> np.ndarray:
+    """n draws of N(0, std) in float32 (or bf16 bits), in fixed blocks of 2^24 with one
+    spawned child seed per block, so the values do not depend on the thread count."""
+    out = np.empty(n, dtype=np.uint16 if to_bf16 else np.float32)
+    nblk = max(1, -(-n // _BLOCK))
+    kids = seq.spawn(nblk)
+
+    def work(i):
+        lo = i * _BLOCK
+        m = min(_BLOCK, n - lo)
+        if m <= 0:
+            return
+        x = np.random.Generator(np.random.PCG64(kids[i])).standard_normal(m, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
-        out[i:i + m] = f32_to_bf16_bits(x)
-    return out.reshape(shape)
+        out[lo:lo + m] = f32_to_bf16_bits(x) if to_bf16 else x
+
+    if nblk == 1:
+        work(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(16, nblk, os.cpu_count() or 1)) as ex:
+            list(ex.map(work, range(nblk)))
+    return out
+
+
+def _normal_bf16(seq, shape, std=1.0) -> np.ndarray:
+    return _fill_normal(seq, int(np.prod(shape)), std, True).reshape(shape)
 
 
 def _lengths(config_id: int, N: int, Lmax: int):
@@ -120,7 +142,6 @@ def make(name: str, B: int, T: int, H: int, *, lengths=None, lower_bound=-5.0,
     """General generator.  ``lengths`` (list) switches to varlen with B = 1, T = sum(lengths)."""
     if seeds is None:
         seeds = np.random.SeedSequence([seed, 0]).spawn(9)
-    rngs = [np.random.Generator(np.random.PCG64(s)) for s in seeds]
     cu = None
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
@@ -128,17 +149,16 @@ def make(name: str, B: int, T: int, H: int, *, lengths=None, lower_bound=-5.0,
         cu[1:] = np.cumsum(lengths)
         B, T = 1, int(cu[-1])
     N = B if cu is None else lengths.size
-    q = _normal_bf16(rngs[1], (B, T, H, D))
-    k = _normal_bf16(rngs[2], (B, T, H, D))
-    v = _normal_bf16(rngs[3], (B, T, H, D))
-    g = _normal_bf16(rngs[4], (B, T, H, D))
-    beta = _normal_bf16(rngs[5], (B, T, H))
-    A_log = np.log(rngs[6].uniform(1.0, 16.0, size=H)).astype(np.float32)
-    dt_bias = (rngs[7].standard_normal((H, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    q = _normal_bf16(seeds[1], (B, T, H, D))
+    k = _normal_bf16(seeds[2], (B, T, H, D))
+    v = _normal_bf16(seeds[3], (B, T, H, D))
+    g = _normal_bf16(seeds[4], (B, T, H, D))
+    beta = _normal_bf16(seeds[5], (B, T, H))
+    A_log = np.log(np.random.Generator(np.random.PCG64(seeds[6])).uniform(1.0, 16.0, size=H)).astype(np.float32)
+    dt_bias = _fill_normal(seeds[7], H * D, 0.1, False).reshape(H, D)
     h0 = None
     if with_initial and state_dtype != STATE_NONE:
-        x = rngs[8].standard_normal((N, H, D, D), dtype=np.float32) * np.float32(0.05)
-        h0 = f32_to_bf16_bits(x) if state_dtype == STATE_BF16 else x.astype(np.float32)
+        h0 = _fill_normal(seeds[8], N * H * D * D, 0.05, state_dtype == STATE_BF16).reshape(N, H, D, D)
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(D)))
     if final_dtype is None:

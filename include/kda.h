@@ -1,0 +1,161 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library (libkda.so).
+ *
+ * The one operation is the chunked forward pass of KDA as the "Kernel API" table of the
+ * FlashKDA README ("MoonshotAI/FlashKDA" repository page) states it:
+ *
+ *   fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+ *       initial_state=None, final_state=None, cu_seqlens=None)
+ *
+ * with the in-kernel gate activation, q/k l2 normalisation and beta sigmoid that the
+ * README section "Using FlashKDA as an FLA backend" switches on (use_gate_in_kernel,
+ * use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, safe_gate) and the V-major state
+ * layout it selects (transpose_state_layout).  Per (sequence, head) chain, per token:
+ *   q^ = q/sqrt(|q|^2+1e-6), k^ = k/sqrt(|k|^2+1e-6), beta = sigmoid(beta_logit),
+ *   a_c = lower_bound * sigmoid(exp(A_log[h]) * (g_c + dt_bias[h,c])),
+ *   S <- S Diag(exp(a)),  S <- S + beta (v - S k^) k^T,  out = scale * S q^.
+ * The library evaluates this in 16-token chunks (FlashKDA article index: "processes
+ * 16-token chunks"; "Neumann-series expansion" for the intra-chunk inverse).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
+ *   - The caller owns every buffer; the library allocates no device memory.  Scratch
+ *     space comes from the caller's workspace (size from kda_fwd_workspace_size).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
+ *     asynchronously; no entry point synchronises the host except kda_fwd_device_status.
+ *   - Arguments are fully validated on the host before anything is launched; on any
+ *     error nothing is launched and an error status is returned.  Nothing throws.
+ *   - No global mutable state; entry points are safe to call from several host threads
+ *     on different streams with different workspaces.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128 /* K = V = 128 is the only supported head size (Kernel API table) */
+#define KDA_CHUNK 16     /* tokens per chunk */
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* A_log or dt_bias is NULL, or a token tensor is NULL while T > 0 */
+    KDA_ERR_SHAPE = 2,       /* B < 1, T < 0, H < 1, N inconsistent, or cu_seqlens with B != 1 */
+    KDA_ERR_HEAD_DIM = 3,    /* K or V is not 128 */
+    KDA_ERR_DTYPE = 4,       /* state dtype unknown, or initial/final state dtypes differ */
+    KDA_ERR_LOWER_BOUND = 5, /* lower_bound not finite or outside [-5, 0] */
+    KDA_ERR_SCALE = 6,       /* scale not finite */
+    KDA_ERR_ALIGN = 7,       /* a pointer misses its alignment (see kda_fwd) */
+    KDA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than kda_fwd_workspace_size */
+    KDA_ERR_CU_SEQLENS = 9,  /* cu_seqlens_host given and cu[0] != 0, decreasing, or cu[N] != T */
+    KDA_ERR_HIP = 10,        /* a HIP launch or query failed */
+    KDA_ERR_ALIAS = 11       /* out overlaps an input, or final_state overlaps a non-state input */
+} kda_status;
+
+typedef enum kda_state_dtype {
+    KDA_STATE_NONE = 0, /* pointer is NULL: no initial state (zeros) / final state not written */
+    KDA_STATE_BF16 = 1,
+    KDA_STATE_FP32 = 2
+} kda_state_dtype;
+
+/*
+ * kda_fwd -- chunked KDA forward pass (Kernel API table of the FlashKDA README).
+ *
+ *   q, k, g   bf16 [B, T, H, 128], contiguous, 16-byte aligned.  Query, key, gate before
+ *             activation.
+ *   v         bf16 [B, T, H, 128], contiguous, 16-byte aligned.
+ *   beta      bf16 [B, T, H], contiguous, 2-byte aligned.  Beta logits (sigmoid applied here).
+ *   scale     output scaling factor, finite.
+ *   out       bf16 [B, T, H, 128], contiguous, 16-byte aligned; fully overwritten (every
+ *             token of every sequence).  Must not overlap any input.
+ *   A_log     fp32 [H], 4-byte aligned.   dt_bias  fp32 [H, 128], 16-byte aligned.
+ *   lower_bound  gate lower bound in [-5, 0] (the table's stated range); the per-token
+ *             log-decay lies in (lower_bound, 0].
+ *   initial_state  NULL (zeros) or [N, H, 128(V), 128(K)] of initial_state_dtype, 16-byte aligned.
+ *   final_state    NULL (not written) or [N, H, 128(V), 128(K)] of final_state_dtype,
+ *             16-byte aligned.  May be the same buffer as initial_state (in-place state carry).
+ *             bf16 states are widened on load and rounded (nearest-even) once on store.
+ *   initial_state_dtype / final_state_dtype  KDA_STATE_NONE exactly when the pointer is NULL;
+ *             when both states are given the two dtypes must be equal (KDA_ERR_DTYPE).
+ *   cu_seqlens  NULL, or device int64 [N+1] cumulative sequence lengths (8-byte aligned);
+ *             then B must be 1, T is the total length and sequence i is tokens
+ *             [cu[i], cu[i+1]).  Without it each of the B batch rows is one sequence (N = B;
+ *             pass N = B or N = 0).
+ *   cu_seqlens_host  optional host copy of cu_seqlens.  When given, its content is checked
+ *             synchronously (KDA_ERR_CU_SEQLENS).  Without it the device checks the content;
+ *             an invalid cu_seqlens then turns every sequence into an empty one (out is not
+ *             written, final_state = initial_state or zeros) and sets the device status word
+ *             that kda_fwd_device_status reads.
+ *   B, T, H, N  sizes as above.  K, V must both be 128.
+ *   workspace, workspace_bytes  device scratch, 256-byte aligned, at least
+ *             kda_fwd_workspace_size(B, T, H, N, cu_seqlens != NULL) bytes.  It must not be
+ *             used by another call until this one has finished on the stream.
+ *   stream    hipStream_t (NULL = default stream).
+ * Returns KDA_OK once the work is enqueued, or the first validation error found.
+ */
+kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                   float scale, void *out, const float *A_log, const float *dt_bias,
+                   float lower_bound, const void *initial_state, kda_state_dtype initial_state_dtype,
+                   void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                   const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                   int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_fwd_timed -- kda_fwd with stage timing, for measurement.  Same arguments and behaviour
+ * as kda_fwd, plus stage_events: four hipEvent_t handles (created by the caller) that are
+ * recorded on `stream` before the chunk-table stage, before the prep stage, before the state
+ * stage, and after the state stage.  hipEventElapsedTime between consecutive events gives
+ * each stage's duration.  Returns KDA_ERR_NULL if any of the four handles is NULL.
+ */
+kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                         float scale, void *out, const float *A_log, const float *dt_bias,
+                         float lower_bound, const void *initial_state,
+                         kda_state_dtype initial_state_dtype, void *final_state,
+                         kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                         const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                         int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                         void *const *stage_events);
+
+/*
+ * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs.  Linear in H times the
+ * number of 16-token chunk slots, ceil(T/16) + N with cu_seqlens (every sequence may end
+ * in a partial chunk) or B * ceil(T/16) without (the FlashKDA article index: workspace
+ * "linear scaling with attention heads and sequence tiles").  Returns 0 for invalid sizes.
+ */
+size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
+
+/* Human-readable name of a kda_status value (static string; never NULL). */
+const char *kda_status_string(int status);
+
+/*
+ * kda_fwd_device_status -- after kda_fwd on `stream`, wait for the stream and read the
+ * device status word from the workspace: 0 = inputs valid; otherwise a bit mask
+ * (1: cu[0] != 0, 2: cu decreasing somewhere, 4: cu[N] != T).  Synchronises the stream.
+ */
+kda_status kda_fwd_device_status(const void *workspace, int32_t *status_out, void *stream);
+
+/*
+ * kda_chunk_table -- run only the first stage of kda_fwd: the integer chunk table built
+ * from cu_seqlens (or from B and T).  Writes into the workspace and, when the host
+ * pointers are non-NULL, copies back (synchronising the stream):
+ *   seq_off_host  int64 [N+1]  exclusive prefix sum of ceil(L_i / 16)
+ *   n_total_host  int64        total number of chunks
+ *   status_host   int32        device status word (as kda_fwd_device_status)
+ * Used to check the integer indexing bit for bit.
+ */
+kda_status kda_chunk_table(const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
+                           void *workspace, size_t workspace_bytes, int64_t *seq_off_host,
+                           int64_t *n_total_host, int32_t *status_host, void *stream);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libkda.so loads and exports every function include/kda.h declares.
+* Every validation error of kda_fwd is returned before anything touches the device:
+  the pointers below are never dereferenced, so fake aligned addresses are fine.
+* kda_fwd_workspace_size is linear in H times the chunk-slot bound
+  (ceil(T/16) + N with cu_seqlens, B * ceil(T/16) without).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_86_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+REC_BYTES = 23040
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTS)
+    L = ctypes.CDLL(kda.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = kda.lib()
+    assert L.kda_version() >= 100
+    for code, name in kda.STATUS_NAMES.items():
+        assert L.kda_status_string(code).decode().startswith(name)
+    assert L.kda_status_string(999).decode() == "KDA_ERR_UNKNOWN"
+
+
+def ws_size(B, T, H, N=0, varlen=False):
+    return kda.workspace_size(B, T, H, N, varlen)
+
+
+def test_workspace_size_formula():
+    for B, T, H in [(1, 64, 1), (2, 4096, 16), (3, 17, 5), (1, 0, 4)]:
+        base = ws_size(B, T, H)
+        more_heads = ws_size(B, T, H + 1)
+        slots = B * -(-T // 16)
+        assert more_heads - base == slots * REC_BYTES
+    for N, T in [(8, 32000), (256, 65000), (3, 5)]:
+        s1 = ws_size(1, T, 2, N, True)
+        s2 = ws_size(1, T, 3, N, True)
+        assert s2 - s1 == (-(-T // 16) + N) * REC_BYTES
+    assert ws_size(0, 10, 1) == 0            # B < 1
+    assert ws_size(2, 10, 1, 3, True) == 0   # cu_seqlens needs B == 1
+    assert ws_size(1, -1, 1) == 0
+
+
+class Args:
+    """A consistent set of arguments whose pointers are fake but aligned and disjoint."""
+
+    def __init__(self, B=1, T=16, H=1, varlen=False, N=0):
+        self.B, self.T, self.H = B, T, H
+        tok = max(B * T * H * 128 * 2, 16)
+        base = 1 << 32
+        step = 1 << 28
+        self.q, self.k, self.v, self.g, self.beta, self.out = (base + i * step for i in range(6))
+        self.A_log = base + 6 * step
+        self.dt_bias = base + 7 * step
+        self.h0, self.h0_dt = base + 8 * step, kda.STATE_FP32
+        self.ht, self.ht_dt = base + 9 * step, kda.STATE_FP32
+        self.cu = base + 10 * step if varlen else None
+        self.cu_host = None
+        self.N = N if varlen else B
+        self.K = self.V = 128
+        self.scale, self.lb = 0.125, -5.0
+        self.ws = base + 11 * step
+        self.ws_bytes = ws_size(B, T, H, self.N if varlen else B, varlen)
+        assert tok < step
+
+    def call(self):
+        L = kda.lib()
+        cu_host = None if self.cu_host is None else self.cu_host.ctypes.data
+        return L.kda_fwd(self.q, self.k, self.v, self.g, self.beta, self.scale, self.out, self.A_log,
+                         self.dt_bias, self.lb, self.h0, self.h0_dt, self.ht, self.ht_dt, self.cu, cu_host,
+                         self.B, self.T, self.H, self.N, self.K, self.V, self.ws, self.ws_bytes, None)
+
+
+def expect(code, **changes):
+    a = Args(**{k: changes.pop(k) for k in list(changes) if k in ("B", "T", "H", "varlen", "N")})
+    for k, val in changes.items():
+        setattr(a, k, val)
+    assert a.call() == code, (changes, kda.STATUS_NAMES.get(a.call()))
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"])
+def test_null_pointers(name):
+    expect(1, **{name: None})
+
+
+def test_shape_errors():
+    expect(2, B=0)
+    expect(2, T=-1)
+    expect(2, H=0)
+    expect(2, B=2, varlen=True, N=2)   # cu_seqlens requires B == 1
+    expect(2, varlen=True, N=0)        # cu_seqlens with N < 1
+    a = Args(B=2)
+    a.N = 3                            # without cu_seqlens N must be B (or 0)
+    assert a.call() == 2
+
+
+def test_head_dim_errors():
+    expect(3, K=64)
+    expect(3, V=256)
+
+
+def test_dtype_errors():
+    expect(4, h0_dt=kda.STATE_BF16)                    # both given, dtypes differ
+    expect(4, h0_dt=7)                                 # unknown dtype
+    expect(4, h0=None)                                 # NULL pointer with a dtype
+    expect(4, ht_dt=kda.STATE_NONE)                    # pointer without a dtype
+
+
+def test_lower_bound_and_scale_errors():
+    for lb in (-5.01, 0.01, float("nan"), float("-inf")):
+        expect(5, lb=lb)
+    for sc in (float("nan"), float("inf")):
+        expect(6, scale=sc)
+
+
+def test_alignment_errors():
+    expect(7, q=Args().q + 8)
+    expect(7, out=Args().out + 2)
+    expect(7, beta=Args().beta + 1)
+    expect(7, dt_bias=Args().dt_bias + 4)
+    expect(7, ws=Args().ws + 128)
+    expect(7, h0=Args().h0 + 8)
+
+
+def test_alias_errors():
+    a = Args()
+    expect(11, out=a.q)
+    expect(11, out=a.beta)
+    expect(11, ht=a.v)
+    expect(11, ht=a.out)
+    expect(11, h0=a.out)
+    expect(11, ht=a.h0 + 4096)    # overlapping but distinct state buffers
+
+
+def test_workspace_errors():
+    expect(8, ws=None)
+    a = Args()
+    expect(8, ws_bytes=a.ws_bytes - 1)
+
+
+def test_cu_seqlens_host_checks():
+    for cu in ([1, 8, 16], [0, 9, 8, 16], [0, 8, 15]):
+        a = Args(T=16, varlen=True, N=len(cu) - 1)
+        a.ws_bytes = ws_size(1, 16, 1, a.N, True)
+        a.cu_host = np.array(cu, dtype=np.int64)
+        assert a.call() == 9, cu
+
+
+def test_chunk_table_argument_errors():
+    L = kda.lib()
+    p = ctypes.c_void_p(1 << 32)
+    assert L.kda_chunk_table(None, 0, 16, 1, 0, p, 1 << 20, None, None, None, None) == 2
+    assert L.kda_chunk_table(None, 1, 16, 1, 0, p, 16, None, None, None, None) == 8
+    assert L.kda_chunk_table(None, 1, 16, 1, 0, ctypes.c_void_p((1 << 32) + 64), 1 << 20, None, None,
+                             None, None) == 7
+    assert L.kda_fwd_device_status(None, None, None) == 1
