@@ -419,10 +419,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
         u32x4_t wk, wl, wq;
-        { const u32x2_t t2 = split_bf16x2(KG[4 * gg], KG[4 * gg + 1]); wk[0] = t2[0]; wl[0] = t2[1]; }
-        { const u32x2_t t2 = split_bf16x2(KG[4 * gg + 2], KG[4 * gg + 3]); wk[1] = t2[0]; wl[1] = t2[1]; }
-        { const u32x2_t t2 = split_bf16x2(KG[16 + 4 * gg], KG[16 + 4 * gg + 1]); wk[2] = t2[0]; wl[2] = t2[1]; }
-        { const u32x2_t t2 = split_bf16x2(KG[16 + 4 * gg + 2], KG[16 + 4 * gg + 3]); wk[3] = t2[0]; wl[3] = t2[1]; }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c0 = (e < 2 ? 4 * gg : 16 + 4 * gg) + 2 * (e & 1);
+            const u32x2_t t2 = split_bf16x2(KG[c0], KG[c0 + 1]);
+            wk[e] = t2[0];
+            wl[e] = t2[1];
+        }
         wq[0] = pack_bf16x2(QG[4 * gg], QG[4 * gg + 1]);
         wq[1] = pack_bf16x2(QG[4 * gg + 2], QG[4 * gg + 3]);
         wq[2] = pack_bf16x2(QG[16 + 4 * gg], QG[16 + 4 * gg + 1]);
@@ -499,128 +502,237 @@ struct StateArgs {
     const unsigned char *recs;
 };
 
-__global__ __launch_bounds__(64) void state_kernel(StateArgs a)
+// The state stage splits each (chain, 16-column value block) over 4 wavefronts of one
+// workgroup: wavefront w owns channels 32w .. 32w+31 of the state (channel tiles 2w, 2w+1).
+// Z = KG S^T and Y = QG S^T are summed over the 4 channel quarters through LDS (one
+// barrier per chunk); every wavefront then forms X = V - Z and V' itself and updates its
+// own quarter.  Each wavefront streams the slice of the per-chunk record it reads into a
+// private LDS ring, kRing chunks ahead, with direct global->LDS loads.
+constexpr int kRing = 4;
+constexpr int kSlot = 8192;          // bytes of one wavefront's ring slot
+constexpr int kSlotKG = 0, kSlotKGL = 1024, kSlotQG = 2048, kSlotKD = 3072;  // KD: 2 tiles
+constexpr int kSlotTB = 5120, kSlotMQ = 6144, kSlotGAM = 7168, kSlotV = 7424;  // GAM 256 B, V 512 B
+constexpr int kDmaPerChunk = 10;     // direct-to-LDS load instructions issued per chunk per wave
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(n), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    const int lane = threadIdx.x;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0), other counters untouched
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Issue the direct-to-LDS loads of one chunk's operand slice for wavefront w (exactly
+// kDmaPerChunk load instructions, all lanes active, every address inside its buffer).
+__device__ __forceinline__ void dma_chunk(unsigned char *slot, const unsigned char *rec,
+                                          const uint16_t *vrow0, int64_t vrow_stride, int tlen,
+                                          int w, int lane)
+{
+    const unsigned char *r = rec + (size_t)lane * 16;
+    __builtin_amdgcn_global_load_lds(r + kRecKG + w * 1024, (lds_void *)(slot + kSlotKG), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(r + kRecKGL + w * 1024, (lds_void *)(slot + kSlotKGL), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(r + kRecQG + w * 1024, (lds_void *)(slot + kSlotQG), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(r + kRecKD + (2 * w) * 1024, (lds_void *)(slot + kSlotKD), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(r + kRecKD + (2 * w + 1) * 1024, (lds_void *)(slot + kSlotKD + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(r + kRecTB, (lds_void *)(slot + kSlotTB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(r + kRecMQ, (lds_void *)(slot + kSlotMQ), 16, 0, 0);
+    // gamma of channels 32w .. 32w+31 (lanes 32..63 load a second copy)
+    __builtin_amdgcn_global_load_lds(rec + kRecGAM + (size_t)(32 * w + (lane & 31)) * 4,
+                                     (lds_void *)(slot + kSlotGAM), 4, 0, 0);
+    // values: token row t = 8i + L/8 holds 16 bf16 = 8 dwords; rows past the chunk's end
+    // read row 0 instead (their LDS copy is never used)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = 8 * i + (lane >> 3);
+        const int tr = t < tlen ? t : 0;
+        const unsigned char *src = reinterpret_cast<const unsigned char *>(vrow0 + (int64_t)tr * vrow_stride) + (lane & 7) * 4;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(slot + kSlotV + i * 256), 4, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256) void state_kernel(StateArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_state[];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    // Workgroups are dealt round-robin to the 8 XCDs (workgroup i -> XCD i % 8); place the
+    // kNVB value blocks of one chain on the same XCD so that they share its L2 copy of the
+    // chain's prep records.
     const int64_t item = blockIdx.x;
-    const int64_t chain = item / kNVB;
-    const int vb = (int)(item % kNVB);
+    const int64_t xcd = item & 7;
+    const int64_t jj = item >> 3;
+    const int vb = (int)(jj % kNVB);
+    const int64_t chain = (jj / kNVB) * 8 + xcd;
     const int64_t n = chain / a.H;
     const int h = (int)(chain % a.H);
     if (n >= a.N)
-        return;
+        return;  // whole workgroup
     const int64_t H = a.H;
     const int g = lane >> 4;
     const int col = lane & 15;
     const int v = vb * kVB + col;
 
-    f32x4_t S[8];
-    const int64_t sbase = ((n * H + h) * kD + v) * kD + 4 * g;
+    unsigned char *ring = s_state + (size_t)w * kRing * kSlot;
+    float *part = reinterpret_cast<float *>(s_state + 4 * kRing * kSlot);  // [2][4 waves][Z,Y][64][4]
+
+    f32x4_t S[2];
+    const int64_t sbase = ((n * H + h) * kD + v) * kD + 4 * g + 32 * w;
     if (a.h0_dtype == 2) {
         const float *p = reinterpret_cast<const float *>(a.h0) + sbase;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            S[ct] = *reinterpret_cast<const f32x4_t *>(p + 16 * ct);
+        S[0] = *reinterpret_cast<const f32x4_t *>(p);
+        S[1] = *reinterpret_cast<const f32x4_t *>(p + 16);
     } else if (a.h0_dtype == 1) {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(a.h0) + sbase;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const u32x2_t u = *reinterpret_cast<const u32x2_t *>(p + 16 * ct);
-            f32x4_t s = {bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1])};
-            S[ct] = s;
+        for (int t = 0; t < 2; ++t) {
+            const u32x2_t u = *reinterpret_cast<const u32x2_t *>(p + 16 * t);
+            S[t] = f32x4_t{bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1])};
         }
     } else {
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        S[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        S[1] = S[0];
     }
 
     const int64_t len = a.seq_len[n];
     const int64_t start = a.seq_start[n];
     const int64_t off = a.seq_off[n];
     const int64_t nch = (len + kCH - 1) / kCH;
-    for (int64_t j = 0; j < nch; ++j) {
-        const unsigned char *rec = a.recs + ((size_t)(off + j) * (size_t)H + (size_t)h) * kRecBytes;
-        const int64_t tok0 = start + j * kCH;
+    const int64_t vstride = H * kD;
+    auto rec_of = [&](int64_t j) {
+        return a.recs + ((size_t)(off + j) * (size_t)H + (size_t)h) * kRecBytes;
+    };
+    auto tlen_of = [&](int64_t j) {
         const int64_t rem = len - j * kCH;
-        const int tlen = rem < kCH ? (int)rem : kCH;
+        return rem < kCH ? (int)rem : kCH;
+    };
+    auto vrow_of = [&](int64_t j) { return a.v + ((start + j * kCH) * H + h) * kD + vb * kVB; };
 
-        // Z = KG S^T (three bf16 products: hi*hi + lo*hi + hi*lo) and Y = QG S^T (one),
-        // contracting the 128 channels in 4 pair steps
-        f32x4_t Z = {0.f, 0.f, 0.f, 0.f}, Y = Z;
+    // prologue: chunks 0 .. kRing-2 in flight
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const size_t o = (size_t)(p * 64 + lane) * 16;
-            const u32x4_t kg = *reinterpret_cast<const u32x4_t *>(rec + kRecKG + o);
-            const u32x4_t kgl = *reinterpret_cast<const u32x4_t *>(rec + kRecKGL + o);
-            const u32x4_t qg = *reinterpret_cast<const u32x4_t *>(rec + kRecQG + o);
-            u32x4_t sb, sl;
-            { const u32x2_t t2 = split_bf16x2(S[2 * p][0], S[2 * p][1]); sb[0] = t2[0]; sl[0] = t2[1]; }
-            { const u32x2_t t2 = split_bf16x2(S[2 * p][2], S[2 * p][3]); sb[1] = t2[0]; sl[1] = t2[1]; }
-            { const u32x2_t t2 = split_bf16x2(S[2 * p + 1][0], S[2 * p + 1][1]); sb[2] = t2[0]; sl[2] = t2[1]; }
-            { const u32x2_t t2 = split_bf16x2(S[2 * p + 1][2], S[2 * p + 1][3]); sb[3] = t2[0]; sl[3] = t2[1]; }
-            Z = mfma32(kg, sb, Z);
-            Z = mfma32(kgl, sb, Z);
-            Z = mfma32(kg, sl, Z);
-            Y = mfma32(qg, sb, Y);
+    for (int jp = 0; jp < kRing - 1; ++jp)
+        if (jp < nch)
+            dma_chunk(ring + jp * kSlot, rec_of(jp), vrow_of(jp), vstride, tlen_of(jp), w, lane);
+
+    for (int64_t j = 0; j < nch; ++j) {
+        unsigned char *slot = ring + (j % kRing) * kSlot;
+        const int tlen = tlen_of(j);
+        // wait for this chunk's loads: the loads of the (up to kRing-2) later chunks
+        // already issued may stay in flight
+        const int64_t ahead = (nch - 1 - j) < (kRing - 2) ? (nch - 1 - j) : (kRing - 2);
+        if (ahead >= 2)
+            wait_vmcnt<2 * kDmaPerChunk>();
+        else if (ahead == 1)
+            wait_vmcnt<kDmaPerChunk>();
+        else
+            wait_vmcnt<0>();
+
+        // partial Z and Y over this wavefront's 32 channels
+        const u32x4_t kg = *reinterpret_cast<const u32x4_t *>(slot + kSlotKG + lane * 16);
+        const u32x4_t kgl = *reinterpret_cast<const u32x4_t *>(slot + kSlotKGL + lane * 16);
+        const u32x4_t qg = *reinterpret_cast<const u32x4_t *>(slot + kSlotQG + lane * 16);
+        u32x4_t sb, sl;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const u32x2_t t0 = split_bf16x2(S[0][2 * e], S[0][2 * e + 1]);
+            const u32x2_t t1 = split_bf16x2(S[1][2 * e], S[1][2 * e + 1]);
+            sb[e] = t0[0];
+            sl[e] = t0[1];
+            sb[2 + e] = t1[0];
+            sl[2 + e] = t1[1];
         }
+        f32x4_t Zp = {0.f, 0.f, 0.f, 0.f}, Yp = Zp;
+        Zp = mfma32(kg, sb, Zp);
+        Zp = mfma32(kgl, sb, Zp);
+        Zp = mfma32(kg, sl, Zp);
+        Yp = mfma32(qg, sb, Yp);
+        float *pb = part + (size_t)(j & 1) * (4 * 2 * 64 * 4);
+        *reinterpret_cast<f32x4_t *>(pb + ((w * 2 + 0) * 64 + lane) * 4) = Zp;
+        *reinterpret_cast<f32x4_t *>(pb + ((w * 2 + 1) * 64 + lane) * 4) = Yp;
+        // Barrier for the partials only: they are plain LDS stores, complete once
+        // lgkmcnt reaches 0.  The ring loads (vmcnt) stay in flight across it.
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+
+        // every wavefront has finished chunk j-1: its ring slot can be refilled
+        if (j + kRing - 1 < nch) {
+            const int64_t jn = j + kRing - 1;
+            dma_chunk(ring + (jn % kRing) * kSlot, rec_of(jn), vrow_of(jn), vstride, tlen_of(jn), w, lane);
+        }
+
+        f32x4_t Z = *reinterpret_cast<const f32x4_t *>(pb + ((0 * 2 + 0) * 64 + lane) * 4);
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            Z += *reinterpret_cast<const f32x4_t *>(pb + ((q * 2 + 0) * 64 + lane) * 4);
         // X = V - Z (rows = tokens 4g+i of this lane's column), split hi/lo
+        const uint16_t *vs = reinterpret_cast<const uint16_t *>(slot + kSlotV);
         f32x4_t X;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = 4 * g + i;
-            const float vv = rr < tlen ? bf16f(a.v[((tok0 + rr) * H + h) * kD + v]) : 0.f;
-            X[i] = vv - Z[i];
+            const float vv = bf16f(vs[rr * kVB + col]);  // rows past the chunk end hold stale data
+            X[i] = (rr < tlen ? vv : 0.f) - Z[i];
         }
-        const u32x2_t xh = {pack_bf16x2(X[0], X[1]), pack_bf16x2(X[2], X[3])};
-        const f32x4_t Xr = {bf_lo(xh[0]), bf_hi(xh[0]), bf_lo(xh[1]), bf_hi(xh[1])};
-        const u32x2_t xl = {pack_bf16x2(X[0] - Xr[0], X[1] - Xr[1]), pack_bf16x2(X[2] - Xr[2], X[3] - Xr[3])};
-
-        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(rec + kRecTB + (size_t)lane * 16);
-        const u32x4_t mq = *reinterpret_cast<const u32x4_t *>(rec + kRecMQ + (size_t)lane * 16);
-        const u32x4_t xhh = {xh[0], xh[1], xh[0], xh[1]};
+        const u32x2_t x01 = split_bf16x2(X[0], X[1]);
+        const u32x2_t x23 = split_bf16x2(X[2], X[3]);
+        const u32x4_t xhh = {x01[0], x23[0], x01[0], x23[0]};
+        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(slot + kSlotTB + lane * 16);
         // V' = Tb X, three bf16 products as two K-concatenated steps:
         //   [Tb_hi | Tb_lo] [X_hi ; X_hi]  +  [Tb_hi | Tb_hi] [X_lo ; 0]
         // Every accumulation chain uses a single MFMA opcode.
         f32x4_t Vp = {0.f, 0.f, 0.f, 0.f};
         Vp = mfma32(tb, xhh, Vp);
-        Vp = mfma32(u32x4_t{tb[0], tb[1], tb[0], tb[1]}, u32x4_t{xl[0], xl[1], 0u, 0u}, Vp);
-        // O = Y + (A_qk Tb) X_hi  with  [Mq_hi | Mq_lo] [X_hi ; X_hi]
-        const f32x4_t O = mfma32(mq, xhh, Y);
+        Vp = mfma32(u32x4_t{tb[0], tb[1], tb[0], tb[1]}, u32x4_t{x01[1], x23[1], 0u, 0u}, Vp);
+        if (w == 0) {
+            // O = Y + (A_qk Tb) X_hi  with  [Mq_hi | Mq_lo] [X_hi ; X_hi]
+            f32x4_t Y = *reinterpret_cast<const f32x4_t *>(pb + ((0 * 2 + 1) * 64 + lane) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * g + i;
-            if (rr < tlen)
-                a.out[((tok0 + rr) * H + h) * kD + v] = to_bf16(O[i]);
+            for (int q = 1; q < 4; ++q)
+                Y += *reinterpret_cast<const f32x4_t *>(pb + ((q * 2 + 1) * 64 + lane) * 4);
+            const u32x4_t mq = *reinterpret_cast<const u32x4_t *>(slot + kSlotMQ + lane * 16);
+            const f32x4_t O = mfma32(mq, xhh, Y);
+            uint16_t *op = a.out + ((start + j * kCH) * H + h) * kD + v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * g + i;
+                if (rr < tlen)
+                    op[(int64_t)rr * vstride] = to_bf16(O[i]);
+            }
         }
-        const u32x2_t vh = {pack_bf16x2(Vp[0], Vp[1]), pack_bf16x2(Vp[2], Vp[3])};
-        const f32x4_t Vr = {bf_lo(vh[0]), bf_hi(vh[0]), bf_lo(vh[1]), bf_hi(vh[1])};
-        const u32x2_t vl = {pack_bf16x2(Vp[0] - Vr[0], Vp[1] - Vr[1]), pack_bf16x2(Vp[2] - Vr[2], Vp[3] - Vr[3])};
-        const u32x4_t vhh = {vh[0], vh[1], vh[0], vh[1]};
-        const u32x4_t vl0 = {vl[0], vl[1], 0u, 0u};
+        const u32x2_t v01 = split_bf16x2(Vp[0], Vp[1]);
+        const u32x2_t v23 = split_bf16x2(Vp[2], Vp[3]);
+        const u32x4_t vhh = {v01[0], v23[0], v01[0], v23[0]};
+        const u32x4_t vl0 = {v01[1], v23[1], 0u, 0u};
         // S <- S diag(gamma) + KD^T V':  [KD_hi | KD_lo] [V'_hi ; V'_hi] + [KD_hi | KD_hi] [V'_lo ; 0]
+        const float *gs = reinterpret_cast<const float *>(slot + kSlotGAM);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const f32x4_t gm = *reinterpret_cast<const f32x4_t *>(rec + kRecGAM + (size_t)(16 * ct + 4 * g) * 4);
-            const u32x4_t kd = *reinterpret_cast<const u32x4_t *>(rec + kRecKD + (size_t)(ct * 64 + lane) * 16);
-            f32x4_t s = S[ct] * gm;
-            s = mfma32(kd, vhh, s);
-            s = mfma32(u32x4_t{kd[0], kd[1], kd[0], kd[1]}, vl0, s);
-            S[ct] = s;
+        for (int t = 0; t < 2; ++t) {
+            const f32x4_t gm = *reinterpret_cast<const f32x4_t *>(gs + 16 * t + 4 * g);
+            const u32x4_t kd = *reinterpret_cast<const u32x4_t *>(slot + kSlotKD + t * 1024 + lane * 16);
+            f32x4_t st = S[t] * gm;
+            st = mfma32(kd, vhh, st);
+            st = mfma32(u32x4_t{kd[0], kd[1], kd[0], kd[1]}, vl0, st);
+            S[t] = st;
         }
     }
 
     if (a.ht_dtype == 2) {
         float *p = reinterpret_cast<float *>(a.ht) + sbase;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            *reinterpret_cast<f32x4_t *>(p + 16 * ct) = S[ct];
+        *reinterpret_cast<f32x4_t *>(p) = S[0];
+        *reinterpret_cast<f32x4_t *>(p + 16) = S[1];
     } else if (a.ht_dtype == 1) {
         uint16_t *p = reinterpret_cast<uint16_t *>(a.ht) + sbase;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            u32x2_t u = {pack_bf16x2(S[ct][0], S[ct][1]), pack_bf16x2(S[ct][2], S[ct][3])};
-            *reinterpret_cast<u32x2_t *>(p + 16 * ct) = u;
+        for (int t = 0; t < 2; ++t) {
+            u32x2_t u = {pack_bf16x2(S[t][0], S[t][1]), pack_bf16x2(S[t][2], S[t][3])};
+            *reinterpret_cast<u32x2_t *>(p + 16 * t) = u;
         }
     }
 }
@@ -686,8 +798,14 @@ hipError_t launch_state(const FwdArgs &f, hipStream_t s)
     a.seq_len = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_off);
     a.recs = f.ws + f.lay.off_recs;
-    const int64_t blocks = f.lay.n_seq * f.H * kNVB;
-    hipLaunchKernelGGL(state_kernel, dim3((unsigned)blocks), dim3(64), 0, s, a);
+    const int64_t chains = f.lay.n_seq * f.H;
+    const int64_t blocks = cdiv(chains, 8) * 8 * kNVB;
+    const size_t lds = (size_t)4 * kRing * kSlot + 2 * 4 * 2 * 64 * 16;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&state_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)blocks), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
