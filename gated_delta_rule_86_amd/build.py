@@ -27,6 +27,8 @@ HIPCC_FLAGS = [
     # no packed fp32 (v_pk_*_f32) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # keep MFMA accumulators in ordinary VGPRs (no accvgpr copies around VALU use)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

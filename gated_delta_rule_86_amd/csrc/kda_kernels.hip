@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     __shared__ float s_tile[4][256];
     __shared__ uint16_t s_kd[4][2][kD * kCH];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t item = (int64_t)blockIdx.x * 4 + wave;
     const int64_t slot = item / a.H;
     const int h = (int)(item % a.H);
@@ -532,37 +532,57 @@ __device__ __forceinline__ void wait_lgkmcnt0()
 
 // Issue the direct-to-LDS loads of one chunk's operand slice for wavefront w (exactly
 // kDmaPerChunk load instructions, all lanes active, every address inside its buffer).
-__device__ __forceinline__ void dma_chunk(unsigned char *slot, const unsigned char *rec,
-                                          const uint16_t *vrow0, int64_t vrow_stride, int tlen,
-                                          int w, int lane)
+// Buffer descriptor over [base, base + bytes): loads past the end return zeros without
+// touching memory.  Word 3 = raw (untyped) buffer access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
-    const unsigned char *r = rec + (size_t)lane * 16;
-    __builtin_amdgcn_global_load_lds(r + kRecKG + w * 1024, (lds_void *)(slot + kSlotKG), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(r + kRecKGL + w * 1024, (lds_void *)(slot + kSlotKGL), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(r + kRecQG + w * 1024, (lds_void *)(slot + kSlotQG), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(r + kRecKD + (2 * w) * 1024, (lds_void *)(slot + kSlotKD), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(r + kRecKD + (2 * w + 1) * 1024, (lds_void *)(slot + kSlotKD + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(r + kRecTB, (lds_void *)(slot + kSlotTB), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(r + kRecMQ, (lds_void *)(slot + kSlotMQ), 16, 0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// lane offsets used by the ring loads, computed once per wavefront
+struct DmaLane {
+    uint32_t o16;   // lane * 16
+    uint32_t ogm;   // (lane % 32) * 4
+    uint32_t ov[2]; // value row 8i + lane/8, dword lane % 8
+};
+
+__device__ __forceinline__ void dma_chunk(unsigned char *slot, const unsigned char *rec,
+                                          const uint16_t *vrow0, uint32_t vrow_bytes, int tlen,
+                                          int w, const DmaLane &dl)
+{
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, (uint32_t)kRecBytes);
+    // Scalar offsets of the blocks this wavefront reads, kept opaque to constant folding:
+    // folding several of them into one descriptor's loads crashes instruction selection.
+    const int sKG = __builtin_amdgcn_readfirstlane(kRecKG + w * 1024);
+    const int sKGL = __builtin_amdgcn_readfirstlane(kRecKGL + w * 1024);
+    const int sQG = __builtin_amdgcn_readfirstlane(kRecQG + w * 1024);
+    const int sKD0 = __builtin_amdgcn_readfirstlane(kRecKD + 2 * w * 1024);
+    const int sKD1 = __builtin_amdgcn_readfirstlane(kRecKD + (2 * w + 1) * 1024);
+    const int sTB = __builtin_amdgcn_readfirstlane((int)kRecTB);
+    const int sMQ = __builtin_amdgcn_readfirstlane((int)kRecMQ);
+    const int sGM = __builtin_amdgcn_readfirstlane(kRecGAM + 128 * w);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKG), 16, dl.o16, sKG, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKGL), 16, dl.o16, sKGL, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotQG), 16, dl.o16, sQG, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKD), 16, dl.o16, sKD0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKD + 1024), 16, dl.o16, sKD1, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotTB), 16, dl.o16, sTB, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotMQ), 16, dl.o16, sMQ, 0, 0);
     // gamma of channels 32w .. 32w+31 (lanes 32..63 load a second copy)
-    __builtin_amdgcn_global_load_lds(rec + kRecGAM + (size_t)(32 * w + (lane & 31)) * 4,
-                                     (lds_void *)(slot + kSlotGAM), 4, 0, 0);
-    // values: token row t = 8i + L/8 holds 16 bf16 = 8 dwords; rows past the chunk's end
-    // read row 0 instead (their LDS copy is never used)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = 8 * i + (lane >> 3);
-        const int tr = t < tlen ? t : 0;
-        const unsigned char *src = reinterpret_cast<const unsigned char *>(vrow0 + (int64_t)tr * vrow_stride) + (lane & 7) * 4;
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(slot + kSlotV + i * 256), 4, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotGAM), 4, dl.ogm, sGM, 0, 0);
+    // values: token row t = 8i + L/8 holds 16 bf16 = 8 dwords (direct-to-LDS loads write one
+    // dword per lane).  The descriptor ends after the chunk's last token, so rows past the
+    // end of a partial chunk load zeros.
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vrow0, (uint32_t)(tlen - 1) * vrow_bytes + 32u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(slot + kSlotV), 4, dl.ov[0], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(slot + kSlotV + 256), 4, dl.ov[1], 0, 0, 0);
 }
 
 __global__ __launch_bounds__(256) void state_kernel(StateArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char s_state[];
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keep it scalar
     // Workgroups are dealt round-robin to the 8 XCDs (workgroup i -> XCD i % 8); place the
     // kNVB value blocks of one chain on the same XCD so that they share its L2 copy of the
     // chain's prep records.
@@ -615,29 +635,57 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a)
     };
     auto vrow_of = [&](int64_t j) { return a.v + ((start + j * kCH) * H + h) * kD + vb * kVB; };
 
+    DmaLane dl;
+    dl.o16 = (uint32_t)lane * 16u;
+    dl.ogm = (uint32_t)(lane & 31) * 4u;
+    const uint32_t vrow_bytes = (uint32_t)(vstride * 2);
+    dl.ov[0] = (uint32_t)(lane >> 3) * vrow_bytes + (uint32_t)(lane & 7) * 4u;
+    dl.ov[1] = dl.ov[0] + 8u * vrow_bytes;
+
     // prologue: chunks 0 .. kRing-2 in flight
 #pragma unroll
     for (int jp = 0; jp < kRing - 1; ++jp)
         if (jp < nch)
-            dma_chunk(ring + jp * kSlot, rec_of(jp), vrow_of(jp), vstride, tlen_of(jp), w, lane);
+            dma_chunk(ring + jp * kSlot, rec_of(jp), vrow_of(jp), vrow_bytes, tlen_of(jp), w, dl);
 
+    // vmcnt bookkeeping.  Per chunk every wavefront issues exactly kDmaPerChunk ring loads
+    // and, for every chunk but a partial last one, exactly one store of output.  The ring
+    // loads of chunk j are complete once at most N later vector-memory operations are
+    // outstanding, N counting only operations certainly issued after them: the ring loads
+    // of the (up to kRing-2) later chunks already in flight, plus one output store when
+    // waiting from inside the loop.
+    auto ahead_of = [&](int64_t j) {
+        return (nch - 1 - j) < (kRing - 2) ? (nch - 1 - j) : (int64_t)(kRing - 2);
+    };
+    auto wait_chunk = [&](int64_t j, bool after_store) {
+        const int64_t ahead = ahead_of(j);
+        if (ahead >= 2) {
+            if (after_store)
+                wait_vmcnt<2 * kDmaPerChunk + 1>();
+            else
+                wait_vmcnt<2 * kDmaPerChunk>();
+        } else if (ahead == 1) {
+            if (after_store)
+                wait_vmcnt<kDmaPerChunk + 1>();
+            else
+                wait_vmcnt<kDmaPerChunk>();
+        } else {
+            wait_vmcnt<0>();
+        }
+    };
+
+    u32x4_t kg = {0u, 0u, 0u, 0u}, kgl = kg, qg = kg;
+    if (nch > 0) {
+        wait_chunk(0, false);
+        kg = *reinterpret_cast<const u32x4_t *>(ring + kSlotKG + lane * 16);
+        kgl = *reinterpret_cast<const u32x4_t *>(ring + kSlotKGL + lane * 16);
+        qg = *reinterpret_cast<const u32x4_t *>(ring + kSlotQG + lane * 16);
+    }
     for (int64_t j = 0; j < nch; ++j) {
         unsigned char *slot = ring + (j % kRing) * kSlot;
         const int tlen = tlen_of(j);
-        // wait for this chunk's loads: the loads of the (up to kRing-2) later chunks
-        // already issued may stay in flight
-        const int64_t ahead = (nch - 1 - j) < (kRing - 2) ? (nch - 1 - j) : (kRing - 2);
-        if (ahead >= 2)
-            wait_vmcnt<2 * kDmaPerChunk>();
-        else if (ahead == 1)
-            wait_vmcnt<kDmaPerChunk>();
-        else
-            wait_vmcnt<0>();
 
         // partial Z and Y over this wavefront's 32 channels
-        const u32x4_t kg = *reinterpret_cast<const u32x4_t *>(slot + kSlotKG + lane * 16);
-        const u32x4_t kgl = *reinterpret_cast<const u32x4_t *>(slot + kSlotKGL + lane * 16);
-        const u32x4_t qg = *reinterpret_cast<const u32x4_t *>(slot + kSlotQG + lane * 16);
         u32x4_t sb, sl;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -661,65 +709,77 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a)
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
 
-        // every wavefront has finished chunk j-1: its ring slot can be refilled
-        if (j + kRing - 1 < nch) {
-            const int64_t jn = j + kRing - 1;
-            dma_chunk(ring + (jn % kRing) * kSlot, rec_of(jn), vrow_of(jn), vstride, tlen_of(jn), w, lane);
-        }
-
+        // the rest of this chunk's operands, and the partials of all four quarters
+        const uint16_t *vs = reinterpret_cast<const uint16_t *>(slot + kSlotV);  // [token][16]
+        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(slot + kSlotTB + lane * 16);
+        const float *gs = reinterpret_cast<const float *>(slot + kSlotGAM);
+        const f32x4_t gm0 = *reinterpret_cast<const f32x4_t *>(gs + 4 * g);
+        const f32x4_t gm1 = *reinterpret_cast<const f32x4_t *>(gs + 16 + 4 * g);
+        const u32x4_t kd0 = *reinterpret_cast<const u32x4_t *>(slot + kSlotKD + lane * 16);
+        const u32x4_t kd1 = *reinterpret_cast<const u32x4_t *>(slot + kSlotKD + 1024 + lane * 16);
         f32x4_t Z = *reinterpret_cast<const f32x4_t *>(pb + ((0 * 2 + 0) * 64 + lane) * 4);
 #pragma unroll
         for (int q = 1; q < 4; ++q)
             Z += *reinterpret_cast<const f32x4_t *>(pb + ((q * 2 + 0) * 64 + lane) * 4);
         // X = V - Z (rows = tokens 4g+i of this lane's column), split hi/lo
-        const uint16_t *vs = reinterpret_cast<const uint16_t *>(slot + kSlotV);
+        float vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            vv[i] = bf16f(vs[(4 * g + i) * kVB + col]);
         f32x4_t X;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * g + i;
-            const float vv = bf16f(vs[rr * kVB + col]);  // rows past the chunk end hold stale data
-            X[i] = (rr < tlen ? vv : 0.f) - Z[i];
-        }
+        for (int i = 0; i < 4; ++i)
+            X[i] = (4 * g + i < tlen ? vv[i] : 0.f) - Z[i];  // rows past the end hold stale data
         const u32x2_t x01 = split_bf16x2(X[0], X[1]);
         const u32x2_t x23 = split_bf16x2(X[2], X[3]);
         const u32x4_t xhh = {x01[0], x23[0], x01[0], x23[0]};
-        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(slot + kSlotTB + lane * 16);
         // V' = Tb X, three bf16 products as two K-concatenated steps:
         //   [Tb_hi | Tb_lo] [X_hi ; X_hi]  +  [Tb_hi | Tb_hi] [X_lo ; 0]
         // Every accumulation chain uses a single MFMA opcode.
         f32x4_t Vp = {0.f, 0.f, 0.f, 0.f};
         Vp = mfma32(tb, xhh, Vp);
         Vp = mfma32(u32x4_t{tb[0], tb[1], tb[0], tb[1]}, u32x4_t{x01[1], x23[1], 0u, 0u}, Vp);
-        if (w == 0) {
-            // O = Y + (A_qk Tb) X_hi  with  [Mq_hi | Mq_lo] [X_hi ; X_hi]
+        const u32x2_t v01 = split_bf16x2(Vp[0], Vp[1]);
+        const u32x2_t v23 = split_bf16x2(Vp[2], Vp[3]);
+        const u32x4_t vhh = {v01[0], v23[0], v01[0], v23[0]};
+        const u32x4_t vl0 = {v01[1], v23[1], 0u, 0u};
+        // S <- S diag(gamma) + KD^T V':  [KD_hi | KD_lo] [V'_hi ; V'_hi] + [KD_hi | KD_hi] [V'_lo ; 0]
+        {
+            f32x4_t s0 = S[0] * gm0, s1 = S[1] * gm1;
+            s0 = mfma32(kd0, vhh, s0);
+            s1 = mfma32(kd1, vhh, s1);
+            s0 = mfma32(u32x4_t{kd0[0], kd0[1], kd0[0], kd0[1]}, vl0, s0);
+            s1 = mfma32(u32x4_t{kd1[0], kd1[1], kd1[0], kd1[1]}, vl0, s1);
+            S[0] = s0;
+            S[1] = s1;
+        }
+        // O = Y + (A_qk Tb) X_hi  with  [Mq_hi | Mq_lo] [X_hi ; X_hi].  Every wavefront forms
+        // it (one MFMA) and stores one of the four token rows it holds: row 4g + w.
+        {
             f32x4_t Y = *reinterpret_cast<const f32x4_t *>(pb + ((0 * 2 + 1) * 64 + lane) * 4);
 #pragma unroll
             for (int q = 1; q < 4; ++q)
                 Y += *reinterpret_cast<const f32x4_t *>(pb + ((q * 2 + 1) * 64 + lane) * 4);
             const u32x4_t mq = *reinterpret_cast<const u32x4_t *>(slot + kSlotMQ + lane * 16);
             const f32x4_t O = mfma32(mq, xhh, Y);
-            uint16_t *op = a.out + ((start + j * kCH) * H + h) * kD + v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 4 * g + i;
-                if (rr < tlen)
-                    op[(int64_t)rr * vstride] = to_bf16(O[i]);
-            }
+            const float ow = w == 0 ? O[0] : w == 1 ? O[1] : w == 2 ? O[2] : O[3];
+            const int rr = 4 * g + w;
+            if (rr < tlen)
+                a.out[((start + j * kCH + rr) * H + h) * kD + v] = to_bf16(ow);
         }
-        const u32x2_t v01 = split_bf16x2(Vp[0], Vp[1]);
-        const u32x2_t v23 = split_bf16x2(Vp[2], Vp[3]);
-        const u32x4_t vhh = {v01[0], v23[0], v01[0], v23[0]};
-        const u32x4_t vl0 = {v01[1], v23[1], 0u, 0u};
-        // S <- S diag(gamma) + KD^T V':  [KD_hi | KD_lo] [V'_hi ; V'_hi] + [KD_hi | KD_hi] [V'_lo ; 0]
-        const float *gs = reinterpret_cast<const float *>(slot + kSlotGAM);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const f32x4_t gm = *reinterpret_cast<const f32x4_t *>(gs + 16 * t + 4 * g);
-            const u32x4_t kd = *reinterpret_cast<const u32x4_t *>(slot + kSlotKD + t * 1024 + lane * 16);
-            f32x4_t st = S[t] * gm;
-            st = mfma32(kd, vhh, st);
-            st = mfma32(u32x4_t{kd[0], kd[1], kd[0], kd[1]}, vl0, st);
-            S[t] = st;
+
+        // every wavefront has finished chunk j-1 (barrier above): refill its ring slot
+        if (j + kRing - 1 < nch) {
+            const int64_t jn = j + kRing - 1;
+            dma_chunk(ring + (jn % kRing) * kSlot, rec_of(jn), vrow_of(jn), vrow_bytes, tlen_of(jn), w, dl);
+        }
+        // first operands of the next chunk
+        if (j + 1 < nch) {
+            wait_chunk(j + 1, true);
+            unsigned char *ns = ring + ((j + 1) % kRing) * kSlot;
+            kg = *reinterpret_cast<const u32x4_t *>(ns + kSlotKG + lane * 16);
+            kgl = *reinterpret_cast<const u32x4_t *>(ns + kSlotKGL + lane * 16);
+            qg = *reinterpret_cast<const u32x4_t *>(ns + kSlotQG + lane * 16);
         }
     }
 
