@@ -43,6 +43,24 @@ def state_bytes(w):
     return b
 
 
+def committed_traffic(workload_name, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary of this workload
+    (profiles/kda_fwd_<workload>.md), or None when there is none or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"kda_fwd_{workload_name}.md")
+    src = os.path.join(ROOT, "gated_delta_rule_86_amd", "csrc", "kda_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for line in open(path):
+        if line.startswith("traffic_bytes_per_launch:"):
+            fields = dict(f.split("=", 1) for f in line.split(":", 1)[1].split())
+            if fields.get("source_sha256") == sha and kernel in fields:
+                return int(fields[kernel])
+    return None
+
+
 def hip_runtime():
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -191,7 +209,8 @@ def main():
         "data": "synthetic",
         "config": dict(w.describe(), head_tokens=ht),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": dname,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name, dname),
+                     "kernel": dname,
                      "kernel_ms": stage_ms[dom], "kernel_algorithmic_bytes": kernel_bytes[dname]},
         "path": {"algorithmic_bytes": path_bytes, "achieved_GBps": path_gbps,
                  "hbm_frac": path_gbps / HBM_PEAK_GBPS, "achieved_TFLOPs": path_tflops,
