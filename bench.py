@@ -8,9 +8,9 @@ K=V=128, fp32 initial and final state (index 1 of workloads.config).  Prints one
 
 roofline: the dominant kernel (largest average duration, from HIP events recorded around
 each stage on the launch stream over the timed steps) against HBM: achieved = that
-kernel's algorithmic bytes per launch / its average duration.  Algorithmic bytes:
-prep = q, k, g (3 x 256 B) + beta (2 B) per head-token; state = v + out (2 x 256 B) per
-head-token + initial/final state; whole path = 1282 B per head-token + states.
+kernel's algorithmic bytes per launch / its average duration.  Algorithmic bytes of the
+forward kernel = the whole path: q, k, v, g (4 x 256 B) + beta (2 B) + out (256 B) per
+head-token, plus initial/final state.
 cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
 
 --copy-calibration runs only a plain device-to-device copy of known size (for scaling the
@@ -156,7 +156,7 @@ def main():
     ev = []
     for _ in range(args.steps):
         row = []
-        for _ in range(4):
+        for _ in range(3):
             e = ctypes.c_void_p()
             assert hip.hipEventCreate(ctypes.byref(e)) == 0
             row.append(e.value)
@@ -171,10 +171,10 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    stage_names = ["chunk_table_kernel", "prep_kernel", "state_kernel"]
-    stage_ms = [0.0, 0.0, 0.0]
+    stage_names = ["chunk_table_kernel", "fused_kernel"]
+    stage_ms = [0.0, 0.0]
     for i in range(args.steps):
-        for j in range(3):
+        for j in range(2):
             ms = ctypes.c_float()
             assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[i][j], ev[i][j + 1]) == 0
             stage_ms[j] += ms.value / args.steps
@@ -186,9 +186,8 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     value = ht / (elapsed / args.steps)
     kernel_bytes = {"chunk_table_kernel": 8 * (w.N + 1),
-                    "prep_kernel": ht * (3 * 256 + 2),
-                    "state_kernel": ht * 2 * 256 + state_bytes(w)}
-    dom = max(range(3), key=lambda j: stage_ms[j])
+                    "fused_kernel": ht * BYTES_PER_HT + state_bytes(w)}
+    dom = max(range(2), key=lambda j: stage_ms[j])
     dname = stage_names[dom]
     achieved = kernel_bytes[dname] / (stage_ms[dom] * 1e-3) / 1e9
     path_bytes = ht * BYTES_PER_HT + state_bytes(w)

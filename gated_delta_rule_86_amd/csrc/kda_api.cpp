@@ -188,11 +188,9 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
     };
     if (!mark(0) || kda::launch_chunk_table(a, s) != hipSuccess)
         return KDA_ERR_HIP;
-    if (!mark(1) || kda::launch_prep(a, s) != hipSuccess)
+    if (!mark(1) || kda::launch_fused(a, s) != hipSuccess)
         return KDA_ERR_HIP;
-    if (!mark(2) || kda::launch_state(a, s) != hipSuccess)
-        return KDA_ERR_HIP;
-    if (!mark(3))
+    if (!mark(2))
         return KDA_ERR_HIP;
     return KDA_OK;
 }
@@ -222,7 +220,7 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
                          int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *stage_events)
 {
-    if (!stage_events || !stage_events[0] || !stage_events[1] || !stage_events[2] || !stage_events[3])
+    if (!stage_events || !stage_events[0] || !stage_events[1] || !stage_events[2])
         return KDA_ERR_NULL;
     return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                     initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,

@@ -11,21 +11,6 @@ namespace kda {
 
 constexpr int kD = 128;   // head dim, K = V
 constexpr int kCH = 16;   // tokens per chunk
-constexpr int kVB = 16;   // value columns per state wave
-constexpr int kNVB = kD / kVB;
-
-// Per (chunk, head) record written by the prep kernel and read by the state kernel.
-// Every block is stored in the exact register layout the state kernel's MFMA operands
-// use, so that each lane fetches its operand with one 16-byte (or 8-byte) load.
-constexpr size_t kRecKG = 0;       // K^*Gamma (hi), bf16, [4 channel pairs][64 lanes][8]
-constexpr size_t kRecKGL = 4096;   // K^*Gamma (lo), same layout
-constexpr size_t kRecQG = 8192;    // scale*q^*Gamma, bf16, same layout
-constexpr size_t kRecKD = 12288;   // K^*gamma/Gamma (hi, lo bf16), [8 channel tiles][64 lanes][4+4]
-constexpr size_t kRecGAM = 20480;  // gamma = Gamma at the chunk's last token, fp32 [128]
-constexpr size_t kRecTB = 20992;   // T*diag(beta) (hi, lo bf16), [64 lanes][4+4]
-constexpr size_t kRecMQ = 22016;   // A_qk*T*diag(beta) (hi, lo bf16), [64 lanes][4+4]
-constexpr size_t kRecBytes = 23040;
-
 constexpr size_t kAlign = 256;
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -33,10 +18,8 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
     int64_t n_seq;     // N (or B without cu_seqlens)
-    int64_t n_slots;   // chunk slots reserved per head (upper bound of the chunk count)
     size_t off_status; // int32 status word; int64 n_total at +8
     size_t off_seq_start, off_seq_len, off_seq_off;
-    size_t off_recs;
     size_t total;
 };
 
@@ -54,7 +37,6 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
         N = B;
     }
     L->n_seq = N;
-    L->n_slots = varlen ? cdiv(T, kCH) + N : B * cdiv(T, kCH);
     size_t off = 0;
     L->off_status = off;
     off += kAlign;
@@ -64,8 +46,6 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)N, kAlign);
     L->off_seq_off = off;
     off = round_up(off + sizeof(int64_t) * (size_t)(N + 1), kAlign);
-    L->off_recs = off;
-    off += kRecBytes * (size_t)L->n_slots * (size_t)H;
     L->total = off;
     return true;
 }
@@ -85,7 +65,6 @@ struct FwdArgs {
 };
 
 hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s);
-hipError_t launch_prep(const FwdArgs &a, hipStream_t s);
-hipError_t launch_state(const FwdArgs &a, hipStream_t s);
+hipError_t launch_fused(const FwdArgs &a, hipStream_t s);
 
 }  // namespace kda

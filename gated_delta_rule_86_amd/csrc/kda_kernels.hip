@@ -5,16 +5,16 @@
 // state).  FlashKDA article index: 16-token chunks, Neumann-series inverse, base-2
 // exponentials, lower_bound as the exponent-range guard.
 //
-// Three stages, each its own kernel:
+// Two kernels:
 //   chunk table  (integer)  sequences -> chunk offsets, validity word
-//   prep         one wavefront per (chunk, head), fully parallel: gate, cumulative
-//                log-decay, l2norm, sigmoid, A_kk / A_qk on MFMA, Neumann inverse on fp32
-//                MFMA, writes MFMA-ready operand blocks for the state stage
-//   state        one wavefront per (sequence, head, 16 value columns), serial over the
-//                chunks: Z = KG S^T, Y = QG S^T, V' = Tb (V - Z), O = Y + Mq (V - Z),
-//                S <- S diag(gamma) + KD^T V', all on bf16 MFMA; the products that feed
-//                the carried state (Z, V', the update, and A_kk in prep) use a hi/lo bf16
-//                split (three products), the output-only ones (Y, Mq X, A_qk) one.
+//   forward      one workgroup per (sequence, head): four producer wavefronts prepare
+//                chunks (gate, cumulative log-decay, l2norm, sigmoid, A_kk / A_qk on MFMA,
+//                Neumann inverse on fp32 MFMA) into LDS; four consumer wavefronts hold the
+//                128 x 128 fp32 state in registers and run, per chunk, Z = KG S^T,
+//                Y = QG S^T, V' = Tb (V - Z), O = Y + Mq (V - Z), S <- S diag(gamma) + KD^T V'
+//                on bf16 MFMA.  The products that feed the carried state (Z, V', the update,
+//                and A_kk) use a hi/lo bf16 split (three products, two for the update), the
+//                output-only ones (Y, Mq X, A_qk) one.
 //
 // Chunk algebra (per chunk of l <= 16 tokens, b = inclusive cumsum of the log-decay a):
 //   Gamma_r = exp(b_r), gamma = Gamma_{l-1}
@@ -65,6 +65,12 @@ __device__ __forceinline__ u32x2_t split_bf16x2(float a, float b)
 }
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// c + a.lo*b.lo + a.hi*b.hi for two packed bf16 pairs, fp32 accumulation
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float sigmoidf_fast(float x) { return frcp(1.0f + fexp2(-x * kLog2e)); }
 
@@ -180,18 +186,8 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(TableArgs a)
 }
 
 // ---------------------------------------------------------------------------------------
-// Stage 2: prep.  One wavefront per (chunk slot, head); 4 wavefronts per workgroup.
-// Lane L works on token r = L % 16 of the chunk and channels 32*(L/16) .. +31.
+// Helpers of the forward kernel: 16x16 fp32 products, DPP scans, direct-to-LDS loads
 // ---------------------------------------------------------------------------------------
-struct PrepArgs {
-    const uint16_t *q, *k, *g, *beta;
-    const float *A_log, *dt_bias;
-    float scale, lower_bound;
-    int64_t H, N, n_slots;
-    const int64_t *n_total, *seq_start, *seq_len, *seq_off;
-    unsigned char *recs;
-};
-
 // 16x16 fp32 product on v_mfma_f32_16x16x4_f32 with both factors held in the D layout
 // (lane n + 16*(m/4), element m%4 holds X[m][n]).  xt is X^T in that layout, y is Y.
 // Step j contracts over k = 4*(L/16) + j, which is element j of both operands.
@@ -237,283 +233,6 @@ __device__ __forceinline__ float dpp_row_last(float x)
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x15f, 0xf, 0xf, false));
 }
 
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
-{
-    __shared__ float s_tile[4][256];
-    __shared__ uint16_t s_kd[4][2][kD * kCH];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    const int64_t slot = item / a.H;
-    const int h = (int)(item % a.H);
-    if (slot >= a.n_slots)
-        return;
-    const int64_t n_total = *a.n_total;
-    if (slot >= n_total)
-        return;
-
-    // sequence owning this chunk: the largest n with seq_off[n] <= slot
-    int64_t lo = 0, hi = a.N;
-    while (hi - lo > 1) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (a.seq_off[mid] <= slot)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int64_t n = lo;
-    const int64_t j = slot - a.seq_off[n];
-    const int64_t t0 = a.seq_start[n] + j * kCH;
-    const int64_t rem = a.seq_len[n] - j * kCH;
-    const int tlen = rem < kCH ? (int)rem : kCH;
-
-    const int r = lane & 15;   // token within the chunk
-    const int qb = lane >> 4;  // channel block: channels 32*qb .. 32*qb+31
-    const bool valid = r < tlen;
-    const int64_t H = a.H;
-
-    float qf[32], kf[32], gf[32];
-    if (valid) {
-        const int64_t row = ((t0 + r) * H + h) * kD + 32 * qb;
-        const u32x4_t *qp = reinterpret_cast<const u32x4_t *>(a.q + row);
-        const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(a.k + row);
-        const u32x4_t *gp = reinterpret_cast<const u32x4_t *>(a.g + row);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            u32x4_t uq = qp[w], uk = kp[w], ug = gp[w];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qf[8 * w + 2 * e] = bf_lo(uq[e]);
-                qf[8 * w + 2 * e + 1] = bf_hi(uq[e]);
-                kf[8 * w + 2 * e] = bf_lo(uk[e]);
-                kf[8 * w + 2 * e + 1] = bf_hi(uk[e]);
-                gf[8 * w + 2 * e] = bf_lo(ug[e]);
-                gf[8 * w + 2 * e + 1] = bf_hi(ug[e]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < 32; ++c) {
-            qf[c] = 0.f;
-            kf[c] = 0.f;
-            gf[c] = 0.f;
-        }
-    }
-    const float bt = valid ? sigmoidf_fast(bf16f(a.beta[(t0 + r) * H + h])) : 0.f;
-
-    // l2 norms over the token's 128 channels (4 lanes share a token)
-    float ssq = 0.f, ssk = 0.f;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        ssq = fmaf(qf[c], qf[c], ssq);
-        ssk = fmaf(kf[c], kf[c], ssk);
-    }
-    ssq += __shfl_xor(ssq, 16);
-    ssq += __shfl_xor(ssq, 32);
-    ssk += __shfl_xor(ssk, 16);
-    ssk += __shfl_xor(ssk, 32);
-    const float rq = __builtin_amdgcn_rsqf(ssq + 1e-6f) * a.scale;
-    const float rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
-
-    // gate: log2-domain log-decay a2 = lb*log2e * sigmoid(exp(A_log) * (g + dt_bias)),
-    // then the inclusive cumulative sum over the chunk's tokens (lanes of a row).
-    const float c1 = fexp2(a.A_log[h] * kLog2e);
-    const float lb2 = a.lower_bound * kLog2e;
-    const f32x4_t *dtp = reinterpret_cast<const f32x4_t *>(a.dt_bias + (int64_t)h * kD + 32 * qb);
-    float b2[32];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        const f32x4_t dt = dtp[w];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = 4 * w + e;
-            float x = c1 * (gf[c] + dt[e]);
-            float av = valid ? lb2 * sigmoidf_fast(x) : 0.f;
-            av += dpp_row_shr(av, 1);
-            av += dpp_row_shr(av, 2);
-            av += dpp_row_shr(av, 4);
-            av += dpp_row_shr(av, 8);
-            b2[c] = av;
-        }
-    }
-
-    // decay-weighted operands (bl = b at the chunk's last token, broadcast along the row)
-    //   KG = k^ Gamma, QG = scale q^ Gamma          (state stage, with S at chunk start)
-    //   KD = k^ gamma / Gamma                        (state update)
-    //   KE = k^ Gamma / gamma, QE = scale q^ Gamma / gamma  (A_kk = KE KD^T, A_qk = QE KD^T)
-    float KG[32], QG[32], KD[32], KE[32], QE[32];
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        const float bl = dpp_row_last(b2[c]);
-        const float G = fexp2(b2[c]);
-        const float E = fexp2(b2[c] - bl);
-        const float Dk = fexp2(bl - b2[c]);
-        const float kn = kf[c] * rk;
-        const float qn = qf[c] * rq;
-        KG[c] = kn * G;
-        QG[c] = qn * G;
-        KD[c] = kn * Dk;
-        KE[c] = kn * E;
-        QE[c] = qn * E;
-    }
-    // MFMA operands for the intra-chunk matrices: step s contracts channels
-    // 32*qb + 8s .. +7 of this lane's token (the same k-slot mapping for A and B).
-    // A_kk feeds the inverse and through it the carried state, so it takes three bf16
-    // products (hi*hi + lo*hi + hi*lo); A_qk only feeds the output and takes one.
-    u32x4_t keb[4], kel[4], qeb[4], kdb[4], kdlo[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c0 = 8 * s + 2 * e;
-            const u32x2_t ke = split_bf16x2(KE[c0], KE[c0 + 1]);
-            keb[s][e] = ke[0];
-            kel[s][e] = ke[1];
-            const u32x2_t kd = split_bf16x2(KD[c0], KD[c0 + 1]);
-            kdb[s][e] = kd[0];
-            kdlo[s][e] = kd[1];
-            qeb[s][e] = pack_bf16x2(QE[c0], QE[c0 + 1]);
-        }
-    }
-
-    f32x4_t akk = {0.f, 0.f, 0.f, 0.f}, aqkT = akk;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        akk = mfma32(keb[s], kdb[s], akk);
-        akk = mfma32(kel[s], kdb[s], akk);
-        akk = mfma32(keb[s], kdlo[s], akk);
-        aqkT = mfma32(kdb[s], qeb[s], aqkT);
-    }
-
-    // masks; D layout: element i of lane L is row 4*(L/16)+i, column L%16
-    const int g4 = (lane >> 4) * 4, col = lane & 15;
-    f32x4_t A, AqT, I4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = g4 + i;
-        const float brow = __shfl(bt, row);
-        A[i] = col < row ? brow * akk[i] : 0.f;
-        AqT[i] = row <= col ? aqkT[i] : 0.f;
-        I4[i] = row == col ? 1.f : 0.f;
-    }
-
-    // Neumann product (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8), fp32
-    float *tile = s_tile[wave];
-    const f32x4_t AT = transpose16(A, tile, lane);
-    const f32x4_t P2 = mm16(AT, A);
-    const f32x4_t P2T = transpose16(P2, tile, lane);
-    const f32x4_t P4 = mm16(P2T, P2);
-    const f32x4_t P4T = transpose16(P4, tile, lane);
-    const f32x4_t P8 = mm16(P4T, P4);
-    const f32x4_t R1 = mm16(I4 + P4T, I4 + P8);
-    const f32x4_t R2 = mm16(I4 + P2T, R1);
-    const f32x4_t Tm = mm16(I4 - AT, R2);
-    const f32x4_t Tb = Tm * bt;              // column s scaled by beta_s (own token)
-    const f32x4_t Mq = mm16(AqT, Tb);        // A_qk T diag(beta)
-    const f32x4_t TbT = transpose16(Tb, tile, lane);
-    const f32x4_t MqT = transpose16(Mq, tile, lane);
-
-    // ---- write the record ----
-    unsigned char *rec = a.recs + ((size_t)slot * (size_t)H + (size_t)h) * kRecBytes;
-    // KG (hi, lo) / QG: record [pair qb][lane r + 16*gg] = channels (4gg..+3, 16+4gg..+3)
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-        u32x4_t wk, wl, wq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c0 = (e < 2 ? 4 * gg : 16 + 4 * gg) + 2 * (e & 1);
-            const u32x2_t t2 = split_bf16x2(KG[c0], KG[c0 + 1]);
-            wk[e] = t2[0];
-            wl[e] = t2[1];
-        }
-        wq[0] = pack_bf16x2(QG[4 * gg], QG[4 * gg + 1]);
-        wq[1] = pack_bf16x2(QG[4 * gg + 2], QG[4 * gg + 3]);
-        wq[2] = pack_bf16x2(QG[16 + 4 * gg], QG[16 + 4 * gg + 1]);
-        wq[3] = pack_bf16x2(QG[16 + 4 * gg + 2], QG[16 + 4 * gg + 3]);
-        const size_t o = (size_t)(qb * 64 + r + 16 * gg) * 16;
-        *reinterpret_cast<u32x4_t *>(rec + kRecKG + o) = wk;
-        *reinterpret_cast<u32x4_t *>(rec + kRecKGL + o) = wl;
-        *reinterpret_cast<u32x4_t *>(rec + kRecQG + o) = wq;
-    }
-    // KD through LDS: [channel][token] hi and lo, then records [tile][lane][hi4, lo4]
-    uint16_t *kdh = s_kd[wave][0];
-    uint16_t *kdl = s_kd[wave][1];
-    lds_sync_wave();
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        const uint16_t hb = to_bf16(KD[c]);
-        const float hf = bf16f(hb);
-        kdh[(32 * qb + c) * kCH + r] = hb;
-        kdl[(32 * qb + c) * kCH + r] = to_bf16(KD[c] - hf);
-    }
-    lds_sync_wave();
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        const int ch = 16 * ct + col;
-        const u32x2_t h2 = *reinterpret_cast<const u32x2_t *>(kdh + ch * kCH + g4);
-        const u32x2_t l2 = *reinterpret_cast<const u32x2_t *>(kdl + ch * kCH + g4);
-        u32x4_t w = {h2[0], h2[1], l2[0], l2[1]};
-        *reinterpret_cast<u32x4_t *>(rec + kRecKD + (size_t)(ct * 64 + lane) * 16) = w;
-    }
-    // gamma: Gamma at the last token; the row's lane 15 holds it (padding adds no decay)
-    if (r == 15) {
-        f32x4_t *gp = reinterpret_cast<f32x4_t *>(rec + kRecGAM + (size_t)(32 * qb) * 4);
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            f32x4_t gv = {fexp2(b2[4 * w]), fexp2(b2[4 * w + 1]), fexp2(b2[4 * w + 2]),
-                          fexp2(b2[4 * w + 3])};
-            gp[w] = gv;
-        }
-    }
-    // Tb and Mq: lane L holds X[L%16][4g..4g+3] (from the transposes), hi and lo
-    {
-        u32x4_t w;
-        const float h0 = bf16f(to_bf16(TbT[0])), h1 = bf16f(to_bf16(TbT[1]));
-        const float h2 = bf16f(to_bf16(TbT[2])), h3 = bf16f(to_bf16(TbT[3]));
-        w[0] = pack_bf16x2(TbT[0], TbT[1]);
-        w[1] = pack_bf16x2(TbT[2], TbT[3]);
-        w[2] = pack_bf16x2(TbT[0] - h0, TbT[1] - h1);
-        w[3] = pack_bf16x2(TbT[2] - h2, TbT[3] - h3);
-        *reinterpret_cast<u32x4_t *>(rec + kRecTB + (size_t)lane * 16) = w;
-        const float m0 = bf16f(to_bf16(MqT[0])), m1 = bf16f(to_bf16(MqT[1]));
-        const float m2 = bf16f(to_bf16(MqT[2])), m3 = bf16f(to_bf16(MqT[3]));
-        u32x4_t m;
-        m[0] = pack_bf16x2(MqT[0], MqT[1]);
-        m[1] = pack_bf16x2(MqT[2], MqT[3]);
-        m[2] = pack_bf16x2(MqT[0] - m0, MqT[1] - m1);
-        m[3] = pack_bf16x2(MqT[2] - m2, MqT[3] - m3);
-        *reinterpret_cast<u32x4_t *>(rec + kRecMQ + (size_t)lane * 16) = m;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Stage 3: state propagation and output.  One wavefront per (sequence, head, value block).
-// Lane L owns value column v = 16*vb + L%16 and, for each channel tile ct, the state
-// entries S[v][16ct + 4*(L/16) + i], i = 0..3 (S^T in the MFMA D layout).
-// ---------------------------------------------------------------------------------------
-struct StateArgs {
-    const uint16_t *v;
-    uint16_t *out;
-    const void *h0;
-    void *ht;
-    int h0_dtype, ht_dtype;
-    int64_t H, N;
-    const int64_t *seq_start, *seq_len, *seq_off;
-    const unsigned char *recs;
-};
-
-// The state stage splits each (chain, 16-column value block) over 4 wavefronts of one
-// workgroup: wavefront w owns channels 32w .. 32w+31 of the state (channel tiles 2w, 2w+1).
-// Z = KG S^T and Y = QG S^T are summed over the 4 channel quarters through LDS (one
-// barrier per chunk); every wavefront then forms X = V - Z and V' itself and updates its
-// own quarter.  Each wavefront streams the slice of the per-chunk record it reads into a
-// private LDS ring, kRing chunks ahead, with direct global->LDS loads.
-constexpr int kRing = 4;
-constexpr int kSlot = 8192;          // bytes of one wavefront's ring slot
-constexpr int kSlotKG = 0, kSlotKGL = 1024, kSlotQG = 2048, kSlotKD = 3072;  // KD: 2 tiles
-constexpr int kSlotTB = 5120, kSlotMQ = 6144, kSlotGAM = 7168, kSlotV = 7424;  // GAM 256 B, V 512 B
-constexpr int kDmaPerChunk = 10;     // direct-to-LDS load instructions issued per chunk per wave
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt vmcnt(n), other counters untouched
@@ -530,8 +249,6 @@ __device__ __forceinline__ void wait_lgkmcnt0()
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Issue the direct-to-LDS loads of one chunk's operand slice for wavefront w (exactly
-// kDmaPerChunk load instructions, all lanes active, every address inside its buffer).
 // Buffer descriptor over [base, base + bytes): loads past the end return zeros without
 // touching memory.  Word 3 = raw (untyped) buffer access.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -539,262 +256,584 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// lane offsets used by the ring loads, computed once per wavefront
-struct DmaLane {
-    uint32_t o16;   // lane * 16
-    uint32_t ogm;   // (lane % 32) * 4
-    uint32_t ov[2]; // value row 8i + lane/8, dword lane % 8
+
+// ---------------------------------------------------------------------------------------
+// Fused forward pass: one workgroup of 8 wavefronts per chain (sequence, head).
+//
+//   waves 0-3  producers.  Producer p prepares chunks p, p+4, p+8, ...: it streams the
+//              chunk's q, k, g, beta into LDS with direct global->LDS loads (one chunk
+//              ahead), then computes gate, cumulative log-decay, l2norm, sigmoid(beta),
+//              A_kk / A_qk, the Neumann inverse, Tb and Mq exactly as the chunk algebra at
+//              the top of this file, and writes the chunk's operand block (same layout as
+//              kBlk*) into one of kNS LDS slots.
+//   waves 4-7  consumers.  Consumer c owns value columns 32c .. 32c+31 of the state, all
+//              128 channels, in registers (two 16-column blocks, 8 channel tiles each),
+//              runs the chunk recurrence on bf16 MFMA and writes the output.
+//
+// Slot hand-off through LDS words: ready[s] = index of the chunk that slot s holds;
+// taken[s][c] = number of chunks consumer c has read out of slot s.  Each word has a
+// single writer (plain LDS stores).  Every wait is a bounded spin: on time-out the wave
+// records kStatusSpin in the status word and goes on, so no input can hang the kernel.
+// ---------------------------------------------------------------------------------------
+// Operand block of one chunk (what a producer hands to the consumers), in the exact
+// register layout of the consumers' MFMA operands, so that each lane fetches an operand
+// with one 16-byte LDS read.
+constexpr int kBlkKG = 0;       // K^*Gamma (hi), bf16, [4 channel pairs][64 lanes][8]
+constexpr int kBlkKGL = 4096;   // K^*Gamma (lo), same layout
+constexpr int kBlkQG = 8192;    // scale*q^*Gamma, bf16, same layout
+constexpr int kBlkKD = 12288;   // K^*gamma/Gamma (hi, lo bf16), [8 channel tiles][64 lanes][4+4]
+constexpr int kBlkGAM = 20480;  // gamma = Gamma at the chunk's last token, fp32 [128]
+constexpr int kBlkTB = 20992;   // T*diag(beta) (hi, lo bf16), [64 lanes][4+4]
+constexpr int kBlkMQ = 22016;   // A_qk*T*diag(beta) (hi, lo bf16), [64 lanes][4+4]
+constexpr int kBlkBytes = 23040;
+
+constexpr int kNS = 4;                           // operand slots
+constexpr int kStageBytes = 3 * 4096 + 256;      // q, k, g tiles (swizzled rows) + beta
+constexpr int kNV = 3;                           // value-tile ring depth per consumer
+constexpr int kOffStage = kNS * kBlkBytes;
+constexpr int kOffVring = kOffStage + 4 * kStageBytes;
+constexpr int kOffTile = kOffVring + 4 * kNV * 1024;
+constexpr int kOffDt = kOffTile + 4 * 1024;
+constexpr int kOffFlags = kOffDt + 512;
+constexpr int kFusedLds = kOffFlags + 128;
+static_assert(kFusedLds <= 160 * 1024, "LDS budget");
+static_assert(kBlkBytes % 16 == 0, "slot alignment");
+constexpr int32_t kStatusSpin = 0x100;
+constexpr int kSpinMax = 1 << 22;
+
+struct FusedArgs {
+    const uint16_t *q, *k, *v, *g, *beta;
+    const float *A_log, *dt_bias;
+    float scale, lower_bound;
+    uint16_t *out;
+    const void *h0;
+    void *ht;
+    int h0_dtype, ht_dtype;
+    int64_t H, N;
+    const int64_t *seq_start, *seq_len;
+    int32_t *status;
 };
 
-__device__ __forceinline__ void dma_chunk(unsigned char *slot, const unsigned char *rec,
-                                          const uint16_t *vrow0, uint32_t vrow_bytes, int tlen,
-                                          int w, const DmaLane &dl)
+typedef __attribute__((address_space(3))) volatile int lds_flag_t;
+
+// Spin until *p == want (all lanes read the same LDS word).  Returns false on time-out.
+__device__ __forceinline__ bool lds_wait_eq(lds_flag_t *p, int want)
 {
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, (uint32_t)kRecBytes);
-    // Scalar offsets of the blocks this wavefront reads, kept opaque to constant folding:
-    // folding several of them into one descriptor's loads crashes instruction selection.
-    const int sKG = __builtin_amdgcn_readfirstlane(kRecKG + w * 1024);
-    const int sKGL = __builtin_amdgcn_readfirstlane(kRecKGL + w * 1024);
-    const int sQG = __builtin_amdgcn_readfirstlane(kRecQG + w * 1024);
-    const int sKD0 = __builtin_amdgcn_readfirstlane(kRecKD + 2 * w * 1024);
-    const int sKD1 = __builtin_amdgcn_readfirstlane(kRecKD + (2 * w + 1) * 1024);
-    const int sTB = __builtin_amdgcn_readfirstlane((int)kRecTB);
-    const int sMQ = __builtin_amdgcn_readfirstlane((int)kRecMQ);
-    const int sGM = __builtin_amdgcn_readfirstlane(kRecGAM + 128 * w);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKG), 16, dl.o16, sKG, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKGL), 16, dl.o16, sKGL, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotQG), 16, dl.o16, sQG, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKD), 16, dl.o16, sKD0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotKD + 1024), 16, dl.o16, sKD1, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotTB), 16, dl.o16, sTB, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotMQ), 16, dl.o16, sMQ, 0, 0);
-    // gamma of channels 32w .. 32w+31 (lanes 32..63 load a second copy)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(slot + kSlotGAM), 4, dl.ogm, sGM, 0, 0);
-    // values: token row t = 8i + L/8 holds 16 bf16 = 8 dwords (direct-to-LDS loads write one
-    // dword per lane).  The descriptor ends after the chunk's last token, so rows past the
-    // end of a partial chunk load zeros.
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vrow0, (uint32_t)(tlen - 1) * vrow_bytes + 32u);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(slot + kSlotV), 4, dl.ov[0], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(slot + kSlotV + 256), 4, dl.ov[1], 0, 0, 0);
+    for (int it = 0; it < kSpinMax; ++it) {
+        const int v = __builtin_amdgcn_readfirstlane(*p);
+        if (v == want) {
+            __asm__ volatile("" ::: "memory");
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+// Spin until the four words p[0..3] all equal want.
+__device__ __forceinline__ bool lds_wait_eq4(lds_flag_t *p, int want)
+{
+    for (int it = 0; it < kSpinMax; ++it) {
+        const int v0 = __builtin_amdgcn_readfirstlane(p[0]);
+        const int v1 = __builtin_amdgcn_readfirstlane(p[1]);
+        const int v2 = __builtin_amdgcn_readfirstlane(p[2]);
+        const int v3 = __builtin_amdgcn_readfirstlane(p[3]);
+        if (v0 == want && v1 == want && v2 == want && v3 == want) {
+            __asm__ volatile("" ::: "memory");
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
 }
 
-__global__ __launch_bounds__(256) void state_kernel(StateArgs a)
+// s_waitcnt vmcnt(n) for a run-time n in [0, 4]
+__device__ __forceinline__ void wait_vmcnt_rt(int n)
 {
-    extern __shared__ __attribute__((aligned(16))) unsigned char s_state[];
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keep it scalar
-    // Workgroups are dealt round-robin to the 8 XCDs (workgroup i -> XCD i % 8); place the
-    // kNVB value blocks of one chain on the same XCD so that they share its L2 copy of the
-    // chain's prep records.
-    const int64_t item = blockIdx.x;
-    const int64_t xcd = item & 7;
-    const int64_t jj = item >> 3;
-    const int vb = (int)(jj % kNVB);
-    const int64_t chain = (jj / kNVB) * 8 + xcd;
-    const int64_t n = chain / a.H;
-    const int h = (int)(chain % a.H);
-    if (n >= a.N)
-        return;  // whole workgroup
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    default: wait_vmcnt<4>(); break;
+    }
+}
+
+__device__ void fused_producer(const FusedArgs &a, unsigned char *lds, int p, int lane, int64_t n,
+                               int h, int64_t start, int64_t len, int64_t nch)
+{
+    const int64_t H = a.H;
+    const int r = lane & 15;   // token within the chunk
+    const int qb = lane >> 4;  // channels 32*qb .. 32*qb+31
+    unsigned char *stage = lds + kOffStage + p * kStageBytes;
+    float *tile = reinterpret_cast<float *>(lds + kOffTile + p * 1024);
+    const float *dtc = reinterpret_cast<const float *>(lds + kOffDt);
+    lds_flag_t *ready = (lds_flag_t *)(lds + kOffFlags);
+    lds_flag_t *taken = ready + kNS;
+    const uint32_t rowb = (uint32_t)(H * kD * 2);  // bytes between consecutive tokens of a head
+
+    // Direct-to-LDS loads of chunk j: 4 loads of 16 B per lane per tensor (4 token rows
+    // each) and one 2-byte load per lane for beta.  Row t, 16-byte segment s of a tensor
+    // goes to LDS segment s ^ (t & 7) of row t, so that the reads below (8 lanes = 8 rows
+    // of one segment) hit distinct banks.  Rows past the chunk's end load zeros.
+    auto issue_stage = [&](int64_t j) {
+        const int64_t t0 = start + j * kCH;
+        const int64_t rem = len - j * kCH;
+        const int tl = rem < kCH ? (int)rem : kCH;
+        const size_t elem0 = ((size_t)t0 * (size_t)H + (size_t)h) * kD;
+        const uint32_t nb = (uint32_t)(tl - 1) * rowb + 256u;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + elem0, nb);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + elem0, nb);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + elem0, nb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t row = 4 * i + (lane >> 4);
+            const uint32_t seg = (uint32_t)(lane & 15) ^ (row & 7u);
+            const uint32_t vo = row * rowb + seg * 16u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(stage + i * 1024), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(stage + 4096 + i * 1024), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void *)(stage + 8192 + i * 1024), 16, vo, 0, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(a.beta + (size_t)t0 * (size_t)H + (size_t)h, (uint32_t)(tl - 1) * (uint32_t)(H * 2) + 2u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage + 12288), 2,
+                                                 (uint32_t)lane * (uint32_t)(H * 2), 0, 0, 0);
+    };
+
+    const float m1 = -kLog2e * fexp2(a.A_log[h] * kLog2e);
+    const float lb2 = a.lower_bound * kLog2e;
+
+    bool spun_out = false;
+    if (p < nch)
+        issue_stage(p);
+    for (int64_t j = p; j < nch; j += 4) {
+        const int64_t rem = len - j * kCH;
+        const int tlen = rem < kCH ? (int)rem : kCH;
+        const bool valid = r < tlen;
+
+        wait_vmcnt<0>();
+        float qf[32], kf[32], gf[32];
+        float ssq = 0.f, ssk = 0.f;  // squared norms over this lane's 32 channels (bf16 dot2)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t seg = (uint32_t)(4 * qb + w) ^ (uint32_t)(r & 7);
+            const uint32_t o = (uint32_t)r * 256u + seg * 16u;
+            const u32x4_t uq = *reinterpret_cast<const u32x4_t *>(stage + o);
+            const u32x4_t uk = *reinterpret_cast<const u32x4_t *>(stage + 4096 + o);
+            const u32x4_t ug = *reinterpret_cast<const u32x4_t *>(stage + 8192 + o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qf[8 * w + 2 * e] = bf_lo(uq[e]);
+                qf[8 * w + 2 * e + 1] = bf_hi(uq[e]);
+                kf[8 * w + 2 * e] = bf_lo(uk[e]);
+                kf[8 * w + 2 * e + 1] = bf_hi(uk[e]);
+                gf[8 * w + 2 * e] = bf_lo(ug[e]);
+                gf[8 * w + 2 * e + 1] = bf_hi(ug[e]);
+                ssq = dot2_bf16(uq[e], uq[e], ssq);
+                ssk = dot2_bf16(uk[e], uk[e], ssk);
+            }
+        }
+        const uint32_t braw = *reinterpret_cast<const uint32_t *>(stage + 12288 + 4 * r);
+        wait_lgkmcnt0();
+        // the staging tile is consumed: fetch this wavefront's next chunk into it
+        if (j + 4 < nch)
+            issue_stage(j + 4);
+
+        const float bt = valid ? sigmoidf_fast(bf16f((uint16_t)(braw & 0xffffu))) : 0.f;
+
+        ssq += __shfl_xor(ssq, 16);
+        ssq += __shfl_xor(ssq, 32);
+        ssk += __shfl_xor(ssk, 16);
+        ssk += __shfl_xor(ssk, 32);
+        const float rq = __builtin_amdgcn_rsqf(ssq + 1e-6f) * a.scale;
+        const float rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
+
+        // log2-domain log-decay lb*log2e*sigmoid(x), x = exp(A_log)*(g + dt_bias):
+        // sigmoid(x) = 1 / (1 + 2^(g*m1 + d1)), m1 = -log2e*exp(A_log), d1 = m1*dt_bias.
+        // Tokens past the chunk's end get a zero log-decay.
+        const float lbv = valid ? lb2 : 0.f;
+        float b2[32];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(dtc + 32 * qb + 4 * w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 4 * w + e;
+                float av = lbv * frcp(1.0f + fexp2(fmaf(gf[c], m1, d4[e])));
+                av += dpp_row_shr(av, 1);
+                av += dpp_row_shr(av, 2);
+                av += dpp_row_shr(av, 4);
+                av += dpp_row_shr(av, 8);
+                b2[c] = av;
+            }
+        }
+
+        // Gamma = 2^b, 1/Gamma = 2^-b; gamma and 1/gamma are their values at the chunk's
+        // last token (lane 15 of the row): E = Gamma/gamma, Dk = gamma/Gamma.
+        float KG[32], QG[32], KD[32], KE[32], QE[32], GL[32];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            const float G = fexp2(b2[c]);
+            const float Gi = fexp2(-b2[c]);
+            const float E = G * dpp_row_last(Gi);
+            const float Dk = Gi * dpp_row_last(G);
+            const float kn = kf[c] * rk;
+            const float qn = qf[c] * rq;
+            KG[c] = kn * G;
+            QG[c] = qn * G;
+            KD[c] = kn * Dk;
+            KE[c] = kn * E;
+            QE[c] = qn * E;
+            GL[c] = G;
+        }
+        u32x4_t keb[4], kel[4], qeb[4], kdb[4], kdlo[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c0 = 8 * s + 2 * e;
+                const u32x2_t ke = split_bf16x2(KE[c0], KE[c0 + 1]);
+                keb[s][e] = ke[0];
+                kel[s][e] = ke[1];
+                const u32x2_t kd = split_bf16x2(KD[c0], KD[c0 + 1]);
+                kdb[s][e] = kd[0];
+                kdlo[s][e] = kd[1];
+                qeb[s][e] = pack_bf16x2(QE[c0], QE[c0 + 1]);
+            }
+        }
+        f32x4_t akk = {0.f, 0.f, 0.f, 0.f}, aqkT = akk;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            akk = mfma32(keb[s], kdb[s], akk);
+            akk = mfma32(kel[s], kdb[s], akk);
+            akk = mfma32(keb[s], kdlo[s], akk);
+            aqkT = mfma32(kdb[s], qeb[s], aqkT);
+        }
+        const int g4 = (lane >> 4) * 4, col = lane & 15;
+        f32x4_t A, AqT, I4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = g4 + i;
+            const float brow = __shfl(bt, row);
+            A[i] = col < row ? brow * akk[i] : 0.f;
+            AqT[i] = row <= col ? aqkT[i] : 0.f;
+            I4[i] = row == col ? 1.f : 0.f;
+        }
+        const f32x4_t AT = transpose16(A, tile, lane);
+        const f32x4_t P2 = mm16(AT, A);
+        const f32x4_t P2T = transpose16(P2, tile, lane);
+        const f32x4_t P4 = mm16(P2T, P2);
+        const f32x4_t P4T = transpose16(P4, tile, lane);
+        const f32x4_t P8 = mm16(P4T, P4);
+        const f32x4_t R1 = mm16(I4 + P4T, I4 + P8);
+        const f32x4_t R2 = mm16(I4 + P2T, R1);
+        const f32x4_t Tm = mm16(I4 - AT, R2);
+        const f32x4_t Tb = Tm * bt;
+        const f32x4_t Mq = mm16(AqT, Tb);
+        const f32x4_t TbT = transpose16(Tb, tile, lane);
+        const f32x4_t MqT = transpose16(Mq, tile, lane);
+
+        // ---- hand the operand block to the consumers ----
+        const int s = (int)(j % kNS);
+        if (!spun_out && !lds_wait_eq4(taken + 4 * s, (int)(j / kNS))) {
+            spun_out = true;  // stop waiting from here on; the status word reports it
+            atomicOr(a.status, kStatusSpin);
+        }
+        unsigned char *rec = lds + (size_t)s * kBlkBytes;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            u32x4_t wk, wl, wq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c0 = (e < 2 ? 4 * gg : 16 + 4 * gg) + 2 * (e & 1);
+                const u32x2_t t2 = split_bf16x2(KG[c0], KG[c0 + 1]);
+                wk[e] = t2[0];
+                wl[e] = t2[1];
+            }
+            wq[0] = pack_bf16x2(QG[4 * gg], QG[4 * gg + 1]);
+            wq[1] = pack_bf16x2(QG[4 * gg + 2], QG[4 * gg + 3]);
+            wq[2] = pack_bf16x2(QG[16 + 4 * gg], QG[16 + 4 * gg + 1]);
+            wq[3] = pack_bf16x2(QG[16 + 4 * gg + 2], QG[16 + 4 * gg + 3]);
+            const int o = (qb * 64 + r + 16 * gg) * 16;
+            *reinterpret_cast<u32x4_t *>(rec + kBlkKG + o) = wk;
+            *reinterpret_cast<u32x4_t *>(rec + kBlkKGL + o) = wl;
+            *reinterpret_cast<u32x4_t *>(rec + kBlkQG + o) = wq;
+        }
+        // KD: tile ct = ch/16, lane position ch%16 + 16*(r/4), token r%4 of the hi and lo
+        // quarters of the 16-byte fragment
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            const int ch = 32 * qb + c;
+            const int o = (int)kBlkKD + (((ch >> 4) * 64 + (ch & 15) + 16 * (r >> 2)) * 16) + 2 * (r & 3);
+            const uint32_t word = (c & 1) ? kdb[c >> 3][(c & 7) >> 1] >> 16 : kdb[c >> 3][(c & 7) >> 1] & 0xffffu;
+            const uint32_t wlo = (c & 1) ? kdlo[c >> 3][(c & 7) >> 1] >> 16 : kdlo[c >> 3][(c & 7) >> 1] & 0xffffu;
+            *reinterpret_cast<uint16_t *>(rec + o) = (uint16_t)word;
+            *reinterpret_cast<uint16_t *>(rec + o + 8) = (uint16_t)wlo;
+        }
+        if (r == 15) {
+            f32x4_t *gp = reinterpret_cast<f32x4_t *>(rec + kBlkGAM + (size_t)(32 * qb) * 4);
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                gp[w] = f32x4_t{GL[4 * w], GL[4 * w + 1], GL[4 * w + 2], GL[4 * w + 3]};
+        }
+        {
+            u32x4_t w;
+            const float h0 = bf16f(to_bf16(TbT[0])), h1 = bf16f(to_bf16(TbT[1]));
+            const float h2 = bf16f(to_bf16(TbT[2])), h3 = bf16f(to_bf16(TbT[3]));
+            w[0] = pack_bf16x2(TbT[0], TbT[1]);
+            w[1] = pack_bf16x2(TbT[2], TbT[3]);
+            w[2] = pack_bf16x2(TbT[0] - h0, TbT[1] - h1);
+            w[3] = pack_bf16x2(TbT[2] - h2, TbT[3] - h3);
+            *reinterpret_cast<u32x4_t *>(rec + kBlkTB + (size_t)lane * 16) = w;
+            const float m0 = bf16f(to_bf16(MqT[0])), m1 = bf16f(to_bf16(MqT[1]));
+            const float m2 = bf16f(to_bf16(MqT[2])), m3 = bf16f(to_bf16(MqT[3]));
+            u32x4_t m;
+            m[0] = pack_bf16x2(MqT[0], MqT[1]);
+            m[1] = pack_bf16x2(MqT[2], MqT[3]);
+            m[2] = pack_bf16x2(MqT[0] - m0, MqT[1] - m1);
+            m[3] = pack_bf16x2(MqT[2] - m2, MqT[3] - m3);
+            *reinterpret_cast<u32x4_t *>(rec + kBlkMQ + (size_t)lane * 16) = m;
+        }
+        wait_lgkmcnt0();
+        __asm__ volatile("" ::: "memory");
+        if (lane == 0)
+            ready[s] = (int)j;
+    }
+}
+
+__device__ void fused_consumer(const FusedArgs &a, unsigned char *lds, int cw, int lane, int64_t n,
+                               int h, int64_t start, int64_t len, int64_t nch)
+{
     const int64_t H = a.H;
     const int g = lane >> 4;
     const int col = lane & 15;
-    const int v = vb * kVB + col;
+    lds_flag_t *ready = (lds_flag_t *)(lds + kOffFlags);
+    lds_flag_t *taken = ready + kNS;
+    unsigned char *vring = lds + kOffVring + cw * (kNV * 1024);
+    const uint32_t rowb = (uint32_t)(H * kD * 2);
 
-    unsigned char *ring = s_state + (size_t)w * kRing * kSlot;
-    float *part = reinterpret_cast<float *>(s_state + 4 * kRing * kSlot);  // [2][4 waves][Z,Y][64][4]
-
-    f32x4_t S[2];
-    const int64_t sbase = ((n * H + h) * kD + v) * kD + 4 * g + 32 * w;
-    if (a.h0_dtype == 2) {
-        const float *p = reinterpret_cast<const float *>(a.h0) + sbase;
-        S[0] = *reinterpret_cast<const f32x4_t *>(p);
-        S[1] = *reinterpret_cast<const f32x4_t *>(p + 16);
-    } else if (a.h0_dtype == 1) {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(a.h0) + sbase;
+    // state: S[b][t] = S[v][16t + 4g + i] (element i) for value column v = 32cw + 16b + col
+    f32x4_t S[2][8];
+    {
+        const int64_t sb0 = ((n * H + h) * kD + 32 * cw + col) * kD + 4 * g;  // column block b adds 16*128
+        if (a.h0_dtype == 2) {
+            const float *p = reinterpret_cast<const float *>(a.h0) + sb0;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const u32x2_t u = *reinterpret_cast<const u32x2_t *>(p + 16 * t);
-            S[t] = f32x4_t{bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1])};
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    S[b][t] = *reinterpret_cast<const f32x4_t *>(p + b * 16 * kD + 16 * t);
+        } else if (a.h0_dtype == 1) {
+            const uint16_t *p = reinterpret_cast<const uint16_t *>(a.h0) + sb0;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const u32x2_t u = *reinterpret_cast<const u32x2_t *>(p + b * 16 * kD + 16 * t);
+                    S[b][t] = f32x4_t{bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1])};
+                }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    S[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-    } else {
-        S[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        S[1] = S[0];
     }
 
-    const int64_t len = a.seq_len[n];
-    const int64_t start = a.seq_start[n];
-    const int64_t off = a.seq_off[n];
-    const int64_t nch = (len + kCH - 1) / kCH;
-    const int64_t vstride = H * kD;
-    auto rec_of = [&](int64_t j) {
-        return a.recs + ((size_t)(off + j) * (size_t)H + (size_t)h) * kRecBytes;
-    };
-    auto tlen_of = [&](int64_t j) {
+    // value tile of chunk j (16 tokens x this wave's 32 columns, row-major 64 B rows) into
+    // ring slot j % kNV: lane L loads row L/4, bytes 16*(L%4); rows past the end load zeros
+    auto issue_v = [&](int64_t j) {
+        const int64_t t0 = start + j * kCH;
         const int64_t rem = len - j * kCH;
-        return rem < kCH ? (int)rem : kCH;
+        const int tl = rem < kCH ? (int)rem : kCH;
+        const __amdgpu_buffer_rsrc_t rv =
+            make_rsrc(a.v + ((size_t)t0 * (size_t)H + (size_t)h) * kD + 32 * cw, (uint32_t)(tl - 1) * rowb + 64u);
+        const uint32_t vo = (uint32_t)(lane >> 2) * rowb + (uint32_t)(lane & 3) * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vring + (j % kNV) * 1024), 16, vo, 0, 0, 0);
     };
-    auto vrow_of = [&](int64_t j) { return a.v + ((start + j * kCH) * H + h) * kD + vb * kVB; };
-
-    DmaLane dl;
-    dl.o16 = (uint32_t)lane * 16u;
-    dl.ogm = (uint32_t)(lane & 31) * 4u;
-    const uint32_t vrow_bytes = (uint32_t)(vstride * 2);
-    dl.ov[0] = (uint32_t)(lane >> 3) * vrow_bytes + (uint32_t)(lane & 7) * 4u;
-    dl.ov[1] = dl.ov[0] + 8u * vrow_bytes;
-
-    // prologue: chunks 0 .. kRing-2 in flight
 #pragma unroll
-    for (int jp = 0; jp < kRing - 1; ++jp)
+    for (int jp = 0; jp < kNV; ++jp)
         if (jp < nch)
-            dma_chunk(ring + jp * kSlot, rec_of(jp), vrow_of(jp), vrow_bytes, tlen_of(jp), w, dl);
-
-    // vmcnt bookkeeping.  Per chunk every wavefront issues exactly kDmaPerChunk ring loads
-    // and, for every chunk but a partial last one, exactly one store of output.  The ring
-    // loads of chunk j are complete once at most N later vector-memory operations are
-    // outstanding, N counting only operations certainly issued after them: the ring loads
-    // of the (up to kRing-2) later chunks already in flight, plus one output store when
-    // waiting from inside the loop.
-    auto ahead_of = [&](int64_t j) {
-        return (nch - 1 - j) < (kRing - 2) ? (nch - 1 - j) : (int64_t)(kRing - 2);
-    };
-    auto wait_chunk = [&](int64_t j, bool after_store) {
-        const int64_t ahead = ahead_of(j);
-        if (ahead >= 2) {
-            if (after_store)
-                wait_vmcnt<2 * kDmaPerChunk + 1>();
-            else
-                wait_vmcnt<2 * kDmaPerChunk>();
-        } else if (ahead == 1) {
-            if (after_store)
-                wait_vmcnt<kDmaPerChunk + 1>();
-            else
-                wait_vmcnt<kDmaPerChunk>();
-        } else {
-            wait_vmcnt<0>();
+            issue_v(jp);
+    bool spun_out = false;
+    // -I in the MFMA A layout for the k-slot order of a channel pair of tiles (2t, 2t+1):
+    // slot 8*(m/4) + m%4 holds channel m of tile 2t, slot 8*(m/4) + 4 + m%4 channel m of
+    // tile 2t+1.  Lane m + 16*(m/4) carries the -1 (bf16 0xbf80) at element m%4 or 4+m%4.
+    u32x4_t negI0 = {0u, 0u, 0u, 0u}, negI1 = negI0;
+    {
+        const int m = lane & 15;
+        if ((lane >> 4) == (m >> 2)) {
+            const int e = m & 3;
+            const uint32_t v = (e & 1) ? 0xbf800000u : 0x0000bf80u;
+            negI0[e >> 1] = v;
+            negI1[2 + (e >> 1)] = v;
         }
-    };
-
-    u32x4_t kg = {0u, 0u, 0u, 0u}, kgl = kg, qg = kg;
-    if (nch > 0) {
-        wait_chunk(0, false);
-        kg = *reinterpret_cast<const u32x4_t *>(ring + kSlotKG + lane * 16);
-        kgl = *reinterpret_cast<const u32x4_t *>(ring + kSlotKGL + lane * 16);
-        qg = *reinterpret_cast<const u32x4_t *>(ring + kSlotQG + lane * 16);
     }
     for (int64_t j = 0; j < nch; ++j) {
-        unsigned char *slot = ring + (j % kRing) * kSlot;
-        const int tlen = tlen_of(j);
-
-        // partial Z and Y over this wavefront's 32 channels
-        u32x4_t sb, sl;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const u32x2_t t0 = split_bf16x2(S[0][2 * e], S[0][2 * e + 1]);
-            const u32x2_t t1 = split_bf16x2(S[1][2 * e], S[1][2 * e + 1]);
-            sb[e] = t0[0];
-            sl[e] = t0[1];
-            sb[2 + e] = t1[0];
-            sl[2 + e] = t1[1];
+        const int s = (int)(j % kNS);
+        if (!spun_out && !lds_wait_eq(ready + s, (int)j)) {
+            spun_out = true;  // stop waiting from here on; the status word reports it
+            atomicOr(a.status, kStatusSpin);
         }
-        f32x4_t Zp = {0.f, 0.f, 0.f, 0.f}, Yp = Zp;
-        Zp = mfma32(kg, sb, Zp);
-        Zp = mfma32(kgl, sb, Zp);
-        Zp = mfma32(kg, sl, Zp);
-        Yp = mfma32(qg, sb, Yp);
-        float *pb = part + (size_t)(j & 1) * (4 * 2 * 64 * 4);
-        *reinterpret_cast<f32x4_t *>(pb + ((w * 2 + 0) * 64 + lane) * 4) = Zp;
-        *reinterpret_cast<f32x4_t *>(pb + ((w * 2 + 1) * 64 + lane) * 4) = Yp;
-        // Barrier for the partials only: they are plain LDS stores, complete once
-        // lgkmcnt reaches 0.  The ring loads (vmcnt) stay in flight across it.
+        const unsigned char *rec = lds + (size_t)s * kBlkBytes;
+        u32x4_t kg[4], kgl[4], qg[4], kd[8];
+        f32x4_t gm[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            kg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKG + (t * 64 + lane) * 16);
+            kgl[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKGL + (t * 64 + lane) * 16);
+            qg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkQG + (t * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            kd[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKD + (t * 64 + lane) * 16);
+            gm[t] = *reinterpret_cast<const f32x4_t *>(rec + kBlkGAM + (16 * t + 4 * g) * 4);
+        }
+        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(rec + kBlkTB + lane * 16);
+        const u32x4_t mq = *reinterpret_cast<const u32x4_t *>(rec + kBlkMQ + lane * 16);
         wait_lgkmcnt0();
-        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (lane == 0)
+            taken[4 * s + cw] = (int)(j / kNS) + 1;
 
-        // the rest of this chunk's operands, and the partials of all four quarters
-        const uint16_t *vs = reinterpret_cast<const uint16_t *>(slot + kSlotV);  // [token][16]
-        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(slot + kSlotTB + lane * 16);
-        const float *gs = reinterpret_cast<const float *>(slot + kSlotGAM);
-        const f32x4_t gm0 = *reinterpret_cast<const f32x4_t *>(gs + 4 * g);
-        const f32x4_t gm1 = *reinterpret_cast<const f32x4_t *>(gs + 16 + 4 * g);
-        const u32x4_t kd0 = *reinterpret_cast<const u32x4_t *>(slot + kSlotKD + lane * 16);
-        const u32x4_t kd1 = *reinterpret_cast<const u32x4_t *>(slot + kSlotKD + 1024 + lane * 16);
-        f32x4_t Z = *reinterpret_cast<const f32x4_t *>(pb + ((0 * 2 + 0) * 64 + lane) * 4);
-#pragma unroll
-        for (int q = 1; q < 4; ++q)
-            Z += *reinterpret_cast<const f32x4_t *>(pb + ((q * 2 + 0) * 64 + lane) * 4);
-        // X = V - Z (rows = tokens 4g+i of this lane's column), split hi/lo
-        float vv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            vv[i] = bf16f(vs[(4 * g + i) * kVB + col]);
-        f32x4_t X;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            X[i] = (4 * g + i < tlen ? vv[i] : 0.f) - Z[i];  // rows past the end hold stale data
-        const u32x2_t x01 = split_bf16x2(X[0], X[1]);
-        const u32x2_t x23 = split_bf16x2(X[2], X[3]);
-        const u32x4_t xhh = {x01[0], x23[0], x01[0], x23[0]};
-        // V' = Tb X, three bf16 products as two K-concatenated steps:
-        //   [Tb_hi | Tb_lo] [X_hi ; X_hi]  +  [Tb_hi | Tb_hi] [X_lo ; 0]
-        // Every accumulation chain uses a single MFMA opcode.
-        f32x4_t Vp = {0.f, 0.f, 0.f, 0.f};
-        Vp = mfma32(tb, xhh, Vp);
-        Vp = mfma32(u32x4_t{tb[0], tb[1], tb[0], tb[1]}, u32x4_t{x01[1], x23[1], 0u, 0u}, Vp);
-        const u32x2_t v01 = split_bf16x2(Vp[0], Vp[1]);
-        const u32x2_t v23 = split_bf16x2(Vp[2], Vp[3]);
-        const u32x4_t vhh = {v01[0], v23[0], v01[0], v23[0]};
-        const u32x4_t vl0 = {v01[1], v23[1], 0u, 0u};
-        // S <- S diag(gamma) + KD^T V':  [KD_hi | KD_lo] [V'_hi ; V'_hi] + [KD_hi | KD_hi] [V'_lo ; 0]
+        // value tile of chunk j: ring loads issued after it are those of chunks j+1, j+2
+        // (if they exist) and the output stores of chunks max(0, j-2) .. j-1
         {
-            f32x4_t s0 = S[0] * gm0, s1 = S[1] * gm1;
-            s0 = mfma32(kd0, vhh, s0);
-            s1 = mfma32(kd1, vhh, s1);
-            s0 = mfma32(u32x4_t{kd0[0], kd0[1], kd0[0], kd0[1]}, vl0, s0);
-            s1 = mfma32(u32x4_t{kd1[0], kd1[1], kd1[0], kd1[1]}, vl0, s1);
-            S[0] = s0;
-            S[1] = s1;
+            const int64_t later = nch - 1 - j;
+            const int nd = later < 2 ? (int)later : 2;
+            const int ns = j < 2 ? (int)j : 2;
+            wait_vmcnt_rt(nd + ns);
         }
-        // O = Y + (A_qk Tb) X_hi  with  [Mq_hi | Mq_lo] [X_hi ; X_hi].  Every wavefront forms
-        // it (one MFMA) and stores one of the four token rows it holds: row 4g + w.
-        {
-            f32x4_t Y = *reinterpret_cast<const f32x4_t *>(pb + ((0 * 2 + 1) * 64 + lane) * 4);
+        unsigned char *vt = vring + (j % kNV) * 1024;
+        float vv[2][4];
 #pragma unroll
-            for (int q = 1; q < 4; ++q)
-                Y += *reinterpret_cast<const f32x4_t *>(pb + ((q * 2 + 1) * 64 + lane) * 4);
-            const u32x4_t mq = *reinterpret_cast<const u32x4_t *>(slot + kSlotMQ + lane * 16);
-            const f32x4_t O = mfma32(mq, xhh, Y);
-            const float ow = w == 0 ? O[0] : w == 1 ? O[1] : w == 2 ? O[2] : O[3];
-            const int rr = 4 * g + w;
-            if (rr < tlen)
-                a.out[((start + j * kCH + rr) * H + h) * kD + v] = to_bf16(ow);
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vv[b][i] = bf16f(*reinterpret_cast<const uint16_t *>(vt + (4 * g + i) * 64 + (16 * b + col) * 2));
+
+        // Z = KG S^T (three products) and Y = QG S^T (one), per channel pair t of tiles
+        // (2t, 2t+1).  S splits as hi = bf16(S) and lo = S - hi; the difference is exact in
+        // fp32 and one MFMA per tile forms it: (-I) hi + S.
+        f32x4_t Z[2], Y[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            Z[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            Y[b] = Z[b];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const f32x4_t s0 = S[b][2 * t], s1 = S[b][2 * t + 1];
+                const u32x4_t sb = {pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]),
+                                    pack_bf16x2(s1[0], s1[1]), pack_bf16x2(s1[2], s1[3])};
+                const f32x4_t r0 = mfma32(negI0, sb, s0);
+                const f32x4_t r1 = mfma32(negI1, sb, s1);
+                const u32x4_t sl = {pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
+                                    pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+                Z[b] = mfma32(kg[t], sb, Z[b]);
+                Z[b] = mfma32(kgl[t], sb, Z[b]);
+                Z[b] = mfma32(kg[t], sl, Z[b]);
+                Y[b] = mfma32(qg[t], sb, Y[b]);
+            }
+        }
+        f32x4_t O[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            f32x4_t X;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                X[i] = vv[b][i] - Z[b][i];  // value rows past the chunk's end load zeros, Z is zero there
+            const u32x2_t x01 = split_bf16x2(X[0], X[1]);
+            const u32x2_t x23 = split_bf16x2(X[2], X[3]);
+            const u32x4_t xhh = {x01[0], x23[0], x01[0], x23[0]};
+            // V' = Tb X: [Tb_hi | Tb_lo] [X_hi ; X_hi] + [Tb_hi | Tb_lo] [X_lo ; 0]
+            f32x4_t Vp = {0.f, 0.f, 0.f, 0.f};
+            Vp = mfma32(tb, xhh, Vp);
+            Vp = mfma32(tb, u32x4_t{x01[1], x23[1], 0u, 0u}, Vp);
+            const u32x2_t v01 = split_bf16x2(Vp[0], Vp[1]);
+            const u32x2_t v23 = split_bf16x2(Vp[2], Vp[3]);
+            const u32x4_t vhh = {v01[0], v23[0], v01[0], v23[0]};
+            const u32x4_t vl0 = {v01[1], v23[1], 0u, 0u};
+            // S <- S diag(gamma) + KD^T V': [KD_hi | KD_lo] [V'_hi ; V'_hi] + [KD_hi | KD_lo] [V'_lo ; 0]
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                f32x4_t st = S[b][t] * gm[t];
+                st = mfma32(kd[t], vhh, st);
+                st = mfma32(kd[t], vl0, st);
+                S[b][t] = st;
+            }
+            O[b] = mfma32(mq, xhh, Y[b]);
         }
 
-        // every wavefront has finished chunk j-1 (barrier above): refill its ring slot
-        if (j + kRing - 1 < nch) {
-            const int64_t jn = j + kRing - 1;
-            dma_chunk(ring + (jn % kRing) * kSlot, rec_of(jn), vrow_of(jn), vrow_bytes, tlen_of(jn), w, dl);
-        }
-        // first operands of the next chunk
-        if (j + 1 < nch) {
-            wait_chunk(j + 1, true);
-            unsigned char *ns = ring + ((j + 1) % kRing) * kSlot;
-            kg = *reinterpret_cast<const u32x4_t *>(ns + kSlotKG + lane * 16);
-            kgl = *reinterpret_cast<const u32x4_t *>(ns + kSlotKGL + lane * 16);
-            qg = *reinterpret_cast<const u32x4_t *>(ns + kSlotQG + lane * 16);
-        }
+        // output rows 4g+i, columns 16b+col -> LDS (the value slot, already read) -> one
+        // 16-byte store per lane: row L/4, columns 8*(L%4) .. +7
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint16_t *>(vt + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
+        wait_lgkmcnt0();
+        const u32x4_t ow = *reinterpret_cast<const u32x4_t *>(vt + lane * 16);
+        wait_lgkmcnt0();
+        const int64_t rem = len - j * kCH;
+        const int tlen = rem < kCH ? (int)rem : kCH;
+        const int orow = lane >> 2;
+        if (orow < tlen)
+            *reinterpret_cast<u32x4_t *>(a.out + ((size_t)(start + j * kCH + orow) * (size_t)H + (size_t)h) * kD +
+                                         32 * cw + 8 * (lane & 3)) = ow;
+        if (j + kNV < nch)
+            issue_v(j + kNV);
     }
 
+    const int64_t sb0 = ((n * H + h) * kD + 32 * cw + col) * kD + 4 * g;
     if (a.ht_dtype == 2) {
-        float *p = reinterpret_cast<float *>(a.ht) + sbase;
-        *reinterpret_cast<f32x4_t *>(p) = S[0];
-        *reinterpret_cast<f32x4_t *>(p + 16) = S[1];
-    } else if (a.ht_dtype == 1) {
-        uint16_t *p = reinterpret_cast<uint16_t *>(a.ht) + sbase;
+        float *p = reinterpret_cast<float *>(a.ht) + sb0;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            u32x2_t u = {pack_bf16x2(S[t][0], S[t][1]), pack_bf16x2(S[t][2], S[t][3])};
-            *reinterpret_cast<u32x2_t *>(p + 16 * t) = u;
-        }
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                *reinterpret_cast<f32x4_t *>(p + b * 16 * kD + 16 * t) = S[b][t];
+    } else if (a.ht_dtype == 1) {
+        uint16_t *p = reinterpret_cast<uint16_t *>(a.ht) + sb0;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const u32x2_t u = {pack_bf16x2(S[b][t][0], S[b][t][1]), pack_bf16x2(S[b][t][2], S[b][t][3])};
+                *reinterpret_cast<u32x2_t *>(p + b * 16 * kD + 16 * t) = u;
+            }
     }
+}
+
+__global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chain = blockIdx.x;
+    const int64_t n = chain / a.H;
+    const int h = (int)(chain % a.H);
+    if (n >= a.N)
+        return;
+    const int64_t len = a.seq_len[n];
+    const int64_t start = a.seq_start[n];
+    const int64_t nch = (len + kCH - 1) / kCH;
+    if (threadIdx.x < 5 * kNS) {
+        int *fl = reinterpret_cast<int *>(lds + kOffFlags);
+        fl[threadIdx.x] = threadIdx.x < kNS ? -1 : 0;
+    }
+    if (threadIdx.x < kD) {
+        const float m1 = -kLog2e * fexp2(a.A_log[h] * kLog2e);
+        reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)h * kD + threadIdx.x];
+    }
+    __syncthreads();
+    if (wave < 4)
+        fused_producer(a, lds, wave, lane, n, h, start, len, nch);
+    else
+        fused_consumer(a, lds, wave - 4, lane, n, h, start, len, nch);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -816,37 +855,21 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_prep(const FwdArgs &f, hipStream_t s)
+hipError_t launch_fused(const FwdArgs &f, hipStream_t s)
 {
-    const int64_t waves = f.lay.n_slots * f.H;
-    if (waves == 0)
+    const int64_t chains = f.lay.n_seq * f.H;
+    if (chains == 0)
         return hipSuccess;
-    PrepArgs a;
+    FusedArgs a;
     a.q = f.q;
     a.k = f.k;
+    a.v = f.v;
     a.g = f.g;
     a.beta = f.beta;
     a.A_log = f.A_log;
     a.dt_bias = f.dt_bias;
     a.scale = f.scale;
     a.lower_bound = f.lower_bound;
-    a.H = f.H;
-    a.N = f.lay.n_seq;
-    a.n_slots = f.lay.n_slots;
-    a.n_total = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_status + 8);
-    a.seq_start = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_start);
-    a.seq_len = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_len);
-    a.seq_off = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_off);
-    a.recs = f.ws + f.lay.off_recs;
-    const int64_t blocks = cdiv(waves, 4);
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_state(const FwdArgs &f, hipStream_t s)
-{
-    StateArgs a;
-    a.v = f.v;
     a.out = f.out;
     a.h0 = f.h0;
     a.ht = f.ht;
@@ -856,16 +879,12 @@ hipError_t launch_state(const FwdArgs &f, hipStream_t s)
     a.N = f.lay.n_seq;
     a.seq_start = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_len);
-    a.seq_off = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_off);
-    a.recs = f.ws + f.lay.off_recs;
-    const int64_t chains = f.lay.n_seq * f.H;
-    const int64_t blocks = cdiv(chains, 8) * 8 * kNVB;
-    const size_t lds = (size_t)4 * kRing * kSlot + 2 * 4 * 2 * 64 * 16;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&state_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(state_kernel, dim3((unsigned)blocks), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)chains), dim3(512), kFusedLds, s, a);
     return hipGetLastError();
 }
 

@@ -107,8 +107,8 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     cu_seqlens: int64 [N+1] device tensor or None (then N = B).
     cu_seqlens_host: optional host copy (sequence or CPU tensor) for a synchronous check.
     workspace: optional uint8 device tensor of at least workspace_size(...) bytes.
-    stage_events: optional sequence of 4 raw hipEvent_t handles (ints); when given the call
-    goes through kda_fwd_timed, which records them around the three stages.
+    stage_events: optional sequence of 3 raw hipEvent_t handles (ints); when given the call
+    goes through kda_fwd_timed, which records them around the chunk-table and forward stages.
     """
     import torch
     L = lib()
@@ -154,7 +154,7 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     if stage_events is None:
         st = L.kda_fwd(*args)
     else:
-        evs = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e)) for e in stage_events])
+        evs = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(int(e)) for e in stage_events])
         st = L.kda_fwd_timed(*args, evs)
     if st != KDA_OK:
         raise KDAError(st)

@@ -106,10 +106,11 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g, c
 
 /*
  * kda_fwd_timed -- kda_fwd with stage timing, for measurement.  Same arguments and behaviour
- * as kda_fwd, plus stage_events: four hipEvent_t handles (created by the caller) that are
- * recorded on `stream` before the chunk-table stage, before the prep stage, before the state
- * stage, and after the state stage.  hipEventElapsedTime between consecutive events gives
- * each stage's duration.  Returns KDA_ERR_NULL if any of the four handles is NULL.
+ * as kda_fwd, plus stage_events: three hipEvent_t handles (created by the caller) that are
+ * recorded on `stream` before the chunk-table stage, before the forward stage (the kernel
+ * that computes out and final_state), and after it.  hipEventElapsedTime between
+ * consecutive events gives each stage's duration.  Returns KDA_ERR_NULL if any of the
+ * three handles is NULL.
  */
 kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,
                          float scale, void *out, const float *A_log, const float *dt_bias,
@@ -121,10 +122,10 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
                          void *const *stage_events);
 
 /*
- * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs.  Linear in H times the
- * number of 16-token chunk slots, ceil(T/16) + N with cu_seqlens (every sequence may end
- * in a partial chunk) or B * ceil(T/16) without (the FlashKDA article index: workspace
- * "linear scaling with attention heads and sequence tiles").  Returns 0 for invalid sizes.
+ * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs: the status word and the
+ * per-sequence chunk table (start, length, chunk offset), O(N) bytes.  The per-chunk
+ * operands never leave the chip, so nothing scales with T or H.  Returns 0 for invalid
+ * sizes.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 
@@ -133,8 +134,10 @@ const char *kda_status_string(int status);
 
 /*
  * kda_fwd_device_status -- after kda_fwd on `stream`, wait for the stream and read the
- * device status word from the workspace: 0 = inputs valid; otherwise a bit mask
- * (1: cu[0] != 0, 2: cu decreasing somewhere, 4: cu[N] != T).  Synchronises the stream.
+ * device status word from the workspace: 0 = inputs valid and the forward pass ran to
+ * completion; otherwise a bit mask (1: cu[0] != 0, 2: cu decreasing somewhere,
+ * 4: cu[N] != T, 0x100: a wavefront of the forward kernel gave up waiting for another
+ * one -- results invalid; not expected to happen).  Synchronises the stream.
  */
 kda_status kda_fwd_device_status(const void *workspace, int32_t *status_out, void *stream);
 
