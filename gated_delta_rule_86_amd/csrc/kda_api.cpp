@@ -188,7 +188,7 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
     };
     if (!mark(0) || kda::launch_chunk_table(a, s) != hipSuccess)
         return KDA_ERR_HIP;
-    if (!mark(1) || kda::launch_fused(a, s) != hipSuccess)
+    if (!mark(1) || kda::launch_forward(a, s) != hipSuccess)
         return KDA_ERR_HIP;
     if (!mark(2))
         return KDA_ERR_HIP;

@@ -16,10 +16,49 @@ constexpr size_t kAlign = 256;
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Segment plan for few, long, equal-length chains (no cu_seqlens).  The state after a
+// segment is affine in the state before it: S_end = S_begin P + F, with F the segment run
+// from S = 0 and P the segment run from S = I with v = 0.  With G segments per chain the
+// forward pass becomes: pass A (segment 0 exactly, and F, P of segments 1 .. G-2), an
+// fp32 scan S_{g+1} = S_g P_g + F_g, and pass B (segments 1 .. G-1 from S_g, with out).
+// That is three segment runs per chunk instead of one, in exchange for chains x G
+// independent work units; the plan picks G by a round count over the CUs.
+constexpr int64_t kPlanCUs = 256;   // MI355X compute units
+
+struct SegPlan {
+    int G;        // segments per chain (1 = no segmentation)
+    int64_t L;    // chunks per segment (the last may be shorter)
+};
+
+inline SegPlan plan_segments(int64_t chains, int64_t nch)
+{
+    SegPlan best{1, nch};
+    if (chains <= 0 || nch < 32 || chains >= 192)
+        return best;
+    auto rounds = [](int64_t units) { return (units + kPlanCUs - 1) / kPlanCUs; };
+    int64_t best_cost = rounds(chains) * nch;
+    for (int64_t G = 2; G <= 256 && G <= nch / 8; ++G) {
+        const int64_t L = cdiv(nch, G);
+        const int64_t Gp = cdiv(nch, L);
+        if (Gp < 2)
+            continue;
+        // pass A: 1 + 2 (Gp - 2) units per chain; pass B: Gp - 1; the scan costs about two
+        // chunk times per segment step
+        const int64_t cost = rounds(chains * (2 * Gp - 3)) * L + rounds(chains * (Gp - 1)) * L + 2 * Gp;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = SegPlan{(int)Gp, L};
+        }
+    }
+    return best;
+}
+
 struct Layout {
     int64_t n_seq;     // N (or B without cu_seqlens)
     size_t off_status; // int32 status word; int64 n_total at +8
     size_t off_seq_start, off_seq_len, off_seq_off;
+    SegPlan seg;       // segment plan (G == 1 without segmentation)
+    size_t off_seg;    // fp32 states S, F, P: 3 x [chains][G][128][128] when G > 1
     size_t total;
 };
 
@@ -46,6 +85,10 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)N, kAlign);
     L->off_seq_off = off;
     off = round_up(off + sizeof(int64_t) * (size_t)(N + 1), kAlign);
+    L->seg = varlen ? SegPlan{1, 0} : plan_segments(N * H, cdiv(T, kCH));
+    L->off_seg = off;
+    if (L->seg.G > 1)
+        off += 3 * (size_t)(N * H) * (size_t)L->seg.G * kD * kD * sizeof(float);
     L->total = off;
     return true;
 }
@@ -65,6 +108,6 @@ struct FwdArgs {
 };
 
 hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s);
-hipError_t launch_fused(const FwdArgs &a, hipStream_t s);
+hipError_t launch_forward(const FwdArgs &a, hipStream_t s);
 
 }  // namespace kda

@@ -294,7 +294,8 @@ constexpr int kOffStage = kNS * kBlkBytes;
 constexpr int kOffVring = kOffStage + 4 * kStageBytes;
 constexpr int kOffTile = kOffVring + 4 * kNV * 1024;
 constexpr int kOffDt = kOffTile + 4 * 1024;
-constexpr int kOffFlags = kOffDt + 512;
+constexpr int kOffOut = kOffDt + 512;               // per consumer: one output tile (1 KB)
+constexpr int kOffFlags = kOffOut + 4 * 1024;
 constexpr int kFusedLds = kOffFlags + 128;
 static_assert(kFusedLds <= 160 * 1024, "LDS budget");
 static_assert(kBlkBytes % 16 == 0, "slot alignment");
@@ -312,6 +313,25 @@ struct FusedArgs {
     int64_t H, N;
     const int64_t *seq_start, *seq_len;
     int32_t *status;
+    // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B (see SegPlan)
+    int pass, G;
+    int64_t L;
+    float *segS, *segF, *segP;  // [chains][G][128][128] fp32, V-major
+};
+
+// One work unit: a chunk range of one chain, where its state comes from and goes to.
+enum { kInitZero = 0, kInitBf16 = 1, kInitFp32 = 2, kInitIdentity = 3 };
+struct Unit {
+    int64_t n;
+    int h;
+    int64_t start, len;   // the sequence's first token and length
+    int64_t c0, c1;       // chunk range [c0, c1) of the sequence
+    int init_kind;        // kInit*
+    const void *init;     // 128 x 128 block (V-major) for kInitBf16 / kInitFp32
+    int fin_kind;         // 0 none, 1 bf16, 2 fp32
+    void *fin;            // 128 x 128 block
+    bool v_on;            // false: v taken as zero (the P run of a segment)
+    bool out_on;          // write out rows of this range
 };
 
 typedef __attribute__((address_space(3))) volatile int lds_flag_t;
@@ -346,7 +366,7 @@ __device__ __forceinline__ bool lds_wait_eq4(lds_flag_t *p, int want)
     return false;
 }
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 4]
+// s_waitcnt vmcnt(n) for a run-time n in [0, 5]
 __device__ __forceinline__ void wait_vmcnt_rt(int n)
 {
     switch (n) {
@@ -354,14 +374,16 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
     case 1: wait_vmcnt<1>(); break;
     case 2: wait_vmcnt<2>(); break;
     case 3: wait_vmcnt<3>(); break;
-    default: wait_vmcnt<4>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    default: wait_vmcnt<5>(); break;
     }
 }
 
-__device__ void fused_producer(const FusedArgs &a, unsigned char *lds, int p, int lane, int64_t n,
-                               int h, int64_t start, int64_t len, int64_t nch)
+__device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char *lds, int p, int lane)
 {
     const int64_t H = a.H;
+    const int h = u.h;
+    const int64_t start = u.start, len = u.len, c0 = u.c0, c1 = u.c1;
     const int r = lane & 15;   // token within the chunk
     const int qb = lane >> 4;  // channels 32*qb .. 32*qb+31
     unsigned char *stage = lds + kOffStage + p * kStageBytes;
@@ -403,9 +425,10 @@ __device__ void fused_producer(const FusedArgs &a, unsigned char *lds, int p, in
     const float lb2 = a.lower_bound * kLog2e;
 
     bool spun_out = false;
-    if (p < nch)
-        issue_stage(p);
-    for (int64_t j = p; j < nch; j += 4) {
+    if (c0 + p < c1)
+        issue_stage(c0 + p);
+    for (int64_t j = c0 + p; j < c1; j += 4) {
+        const int64_t it = j - c0;  // item index within the range: slot it % kNS
         const int64_t rem = len - j * kCH;
         const int tlen = rem < kCH ? (int)rem : kCH;
         const bool valid = r < tlen;
@@ -435,7 +458,7 @@ __device__ void fused_producer(const FusedArgs &a, unsigned char *lds, int p, in
         const uint32_t braw = *reinterpret_cast<const uint32_t *>(stage + 12288 + 4 * r);
         wait_lgkmcnt0();
         // the staging tile is consumed: fetch this wavefront's next chunk into it
-        if (j + 4 < nch)
+        if (j + 4 < c1)
             issue_stage(j + 4);
 
         const float bt = valid ? sigmoidf_fast(bf16f((uint16_t)(braw & 0xffffu))) : 0.f;
@@ -533,8 +556,8 @@ __device__ void fused_producer(const FusedArgs &a, unsigned char *lds, int p, in
         const f32x4_t MqT = transpose16(Mq, tile, lane);
 
         // ---- hand the operand block to the consumers ----
-        const int s = (int)(j % kNS);
-        if (!spun_out && !lds_wait_eq4(taken + 4 * s, (int)(j / kNS))) {
+        const int s = (int)(it % kNS);
+        if (!spun_out && !lds_wait_eq4(taken + 4 * s, (int)(it / kNS))) {
             spun_out = true;  // stop waiting from here on; the status word reports it
             atomicOr(a.status, kStatusSpin);
         }
@@ -596,14 +619,15 @@ __device__ void fused_producer(const FusedArgs &a, unsigned char *lds, int p, in
         wait_lgkmcnt0();
         __asm__ volatile("" ::: "memory");
         if (lane == 0)
-            ready[s] = (int)j;
+            ready[s] = (int)it;
     }
 }
 
-__device__ void fused_consumer(const FusedArgs &a, unsigned char *lds, int cw, int lane, int64_t n,
-                               int h, int64_t start, int64_t len, int64_t nch)
+__device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane)
 {
     const int64_t H = a.H;
+    const int h = u.h;
+    const int64_t start = u.start, len = u.len, c0 = u.c0, c1 = u.c1;
     const int g = lane >> 4;
     const int col = lane & 15;
     lds_flag_t *ready = (lds_flag_t *)(lds + kOffFlags);
@@ -614,29 +638,34 @@ __device__ void fused_consumer(const FusedArgs &a, unsigned char *lds, int cw, i
     // state: S[b][t] = S[v][16t + 4g + i] (element i) for value column v = 32cw + 16b + col
     f32x4_t S[2][8];
     {
-        const int64_t sb0 = ((n * H + h) * kD + 32 * cw + col) * kD + 4 * g;  // column block b adds 16*128
-        if (a.h0_dtype == 2) {
-            const float *p = reinterpret_cast<const float *>(a.h0) + sb0;
+        const int64_t sb0 = (int64_t)(32 * cw + col) * kD + 4 * g;  // column block b adds 16*128
+        if (u.init_kind == kInitFp32) {
+            const float *p = reinterpret_cast<const float *>(u.init) + sb0;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
                     S[b][t] = *reinterpret_cast<const f32x4_t *>(p + b * 16 * kD + 16 * t);
-        } else if (a.h0_dtype == 1) {
-            const uint16_t *p = reinterpret_cast<const uint16_t *>(a.h0) + sb0;
+        } else if (u.init_kind == kInitBf16) {
+            const uint16_t *p = reinterpret_cast<const uint16_t *>(u.init) + sb0;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
-                    const u32x2_t u = *reinterpret_cast<const u32x2_t *>(p + b * 16 * kD + 16 * t);
-                    S[b][t] = f32x4_t{bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1])};
+                    const u32x2_t w = *reinterpret_cast<const u32x2_t *>(p + b * 16 * kD + 16 * t);
+                    S[b][t] = f32x4_t{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
                 }
         } else {
+            const bool ident = u.init_kind == kInitIdentity;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    S[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 8; ++t) {
+                    const int v = 32 * cw + 16 * b + col;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[b][t][i] = (ident && v == 16 * t + 4 * g + i) ? 1.f : 0.f;
+                }
         }
     }
 
@@ -649,12 +678,14 @@ __device__ void fused_consumer(const FusedArgs &a, unsigned char *lds, int cw, i
         const __amdgpu_buffer_rsrc_t rv =
             make_rsrc(a.v + ((size_t)t0 * (size_t)H + (size_t)h) * kD + 32 * cw, (uint32_t)(tl - 1) * rowb + 64u);
         const uint32_t vo = (uint32_t)(lane >> 2) * rowb + (uint32_t)(lane & 3) * 16u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vring + (j % kNV) * 1024), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vring + ((j - c0) % kNV) * 1024), 16, vo, 0, 0, 0);
     };
+    if (u.v_on) {
 #pragma unroll
-    for (int jp = 0; jp < kNV; ++jp)
-        if (jp < nch)
-            issue_v(jp);
+        for (int jp = 0; jp < kNV; ++jp)
+            if (c0 + jp < c1)
+                issue_v(c0 + jp);
+    }
     bool spun_out = false;
     // -I in the MFMA A layout for the k-slot order of a channel pair of tiles (2t, 2t+1):
     // slot 8*(m/4) + m%4 holds channel m of tile 2t, slot 8*(m/4) + 4 + m%4 channel m of
@@ -669,48 +700,76 @@ __device__ void fused_consumer(const FusedArgs &a, unsigned char *lds, int cw, i
             negI1[2 + (e >> 1)] = v;
         }
     }
-    for (int64_t j = 0; j < nch; ++j) {
-        const int s = (int)(j % kNS);
-        if (!spun_out && !lds_wait_eq(ready + s, (int)j)) {
-            spun_out = true;  // stop waiting from here on; the status word reports it
-            atomicOr(a.status, kStatusSpin);
-        }
+    unsigned char *obuf = lds + kOffOut + cw * 1024;  // output tile of the previous chunk
+    const int orow = lane >> 2;                        // output row this lane stores
+    auto store_out = [&](int64_t jo) {
+        const int64_t rem = len - jo * kCH;
+        const u32x4_t ow = *reinterpret_cast<const u32x4_t *>(obuf + lane * 16);
+        if (orow < rem)
+            *reinterpret_cast<u32x4_t *>(a.out + ((size_t)(start + jo * kCH + orow) * (size_t)H + (size_t)h) * kD +
+                                         32 * cw + 8 * (lane & 3)) = ow;
+    };
+    for (int64_t j = c0; j < c1; ++j) {
+        const int64_t it = j - c0;  // item index within the range
+        const int s = (int)(it % kNS);
         const unsigned char *rec = lds + (size_t)s * kBlkBytes;
         u32x4_t kg[4], kgl[4], qg[4], kd[8];
         f32x4_t gm[8];
+        u32x4_t tb, mq;
+        // The operand reads go out right behind the read of ready[s]; LDS serves one
+        // wavefront's requests in order, so when that read shows chunk j the operands
+        // read after it are chunk j's.  Otherwise wait, then read them again.
+        auto read_ops = [&]() {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            kg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKG + (t * 64 + lane) * 16);
-            kgl[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKGL + (t * 64 + lane) * 16);
-            qg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkQG + (t * 64 + lane) * 16);
-        }
+            for (int t = 0; t < 4; ++t) {
+                kg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKG + (t * 64 + lane) * 16);
+                kgl[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKGL + (t * 64 + lane) * 16);
+                qg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkQG + (t * 64 + lane) * 16);
+            }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            kd[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKD + (t * 64 + lane) * 16);
-            gm[t] = *reinterpret_cast<const f32x4_t *>(rec + kBlkGAM + (16 * t + 4 * g) * 4);
-        }
-        const u32x4_t tb = *reinterpret_cast<const u32x4_t *>(rec + kBlkTB + lane * 16);
-        const u32x4_t mq = *reinterpret_cast<const u32x4_t *>(rec + kBlkMQ + lane * 16);
-        wait_lgkmcnt0();
+            for (int t = 0; t < 8; ++t) {
+                kd[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKD + (t * 64 + lane) * 16);
+                gm[t] = *reinterpret_cast<const f32x4_t *>(rec + kBlkGAM + (16 * t + 4 * g) * 4);
+            }
+            tb = *reinterpret_cast<const u32x4_t *>(rec + kBlkTB + lane * 16);
+            mq = *reinterpret_cast<const u32x4_t *>(rec + kBlkMQ + lane * 16);
+        };
+        const int seen = ready[s];
         __asm__ volatile("" ::: "memory");
-        if (lane == 0)
-            taken[4 * s + cw] = (int)(j / kNS) + 1;
-
-        // value tile of chunk j: ring loads issued after it are those of chunks j+1, j+2
-        // (if they exist) and the output stores of chunks max(0, j-2) .. j-1
-        {
-            const int64_t later = nch - 1 - j;
-            const int nd = later < 2 ? (int)later : 2;
-            const int ns = j < 2 ? (int)j : 2;
-            wait_vmcnt_rt(nd + ns);
+        read_ops();
+        if (__builtin_amdgcn_readfirstlane(seen) != (int)it) {
+            if (!spun_out && !lds_wait_eq(ready + s, (int)it)) {
+                spun_out = true;  // stop waiting from here on; the status word reports it
+                atomicOr(a.status, kStatusSpin);
+            }
+            read_ops();
         }
-        unsigned char *vt = vring + (j % kNV) * 1024;
-        float vv[2][4];
+        // the previous chunk's output tile (staged in LDS) goes to HBM
+        if (u.out_on && it > 0)
+            store_out(j - 1);
+
+        // value tile of chunk j: vector-memory operations issued after its ring load are
+        // the ring loads of chunks j+1, j+2 (those in range) and, when out is written, the
+        // output stores of the items max(0, it-3) .. it-1 (one store instruction each; its
+        // lanes for row 0 are always active)
+        float vv[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (u.v_on) {
+            const int64_t later = c1 - 1 - j;
+            const int nd = later < 2 ? (int)later : 2;
+            const int ns = !u.out_on ? 0 : it < 3 ? (int)it : 3;
+            wait_vmcnt_rt(nd + ns);
+            unsigned char *vt = vring + (it % kNV) * 1024;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vv[b][i] = bf16f(*reinterpret_cast<const uint16_t *>(vt + (4 * g + i) * 64 + (16 * b + col) * 2));
+                for (int i = 0; i < 4; ++i)
+                    vv[b][i] = bf16f(*reinterpret_cast<const uint16_t *>(vt + (4 * g + i) * 64 + (16 * b + col) * 2));
+            // the value slot is read: refill it with chunk j + kNV
+            if (j + kNV < c1) {
+                wait_lgkmcnt0();
+                issue_v(j + kNV);
+            }
+        }
 
         // Z = KG S^T (three products) and Y = QG S^T (one), per channel pair t of tiles
         // (2t, 2t+1).  S splits as hi = bf16(S) and lo = S - hi; the difference is exact in
@@ -767,43 +826,38 @@ __device__ void fused_consumer(const FusedArgs &a, unsigned char *lds, int cw, i
             O[b] = mfma32(mq, xhh, Y[b]);
         }
 
-        // output rows 4g+i, columns 16b+col -> LDS (the value slot, already read) -> one
-        // 16-byte store per lane: row L/4, columns 8*(L%4) .. +7
-        wait_lgkmcnt0();
+        // output rows 4g+i, columns 16b+col -> LDS tile; the next iteration (or the end)
+        // stores it with one 16-byte write per lane: row L/4, columns 8*(L%4) .. +7
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint16_t *>(vt + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
+                *reinterpret_cast<uint16_t *>(obuf + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
+        // every operand of chunk j is in registers (used above): release the slot
+        if (lane == 0)
+            taken[4 * s + cw] = (int)(it / kNS) + 1;
+    }
+    if (u.out_on && c1 > c0) {
         wait_lgkmcnt0();
-        const u32x4_t ow = *reinterpret_cast<const u32x4_t *>(vt + lane * 16);
-        wait_lgkmcnt0();
-        const int64_t rem = len - j * kCH;
-        const int tlen = rem < kCH ? (int)rem : kCH;
-        const int orow = lane >> 2;
-        if (orow < tlen)
-            *reinterpret_cast<u32x4_t *>(a.out + ((size_t)(start + j * kCH + orow) * (size_t)H + (size_t)h) * kD +
-                                         32 * cw + 8 * (lane & 3)) = ow;
-        if (j + kNV < nch)
-            issue_v(j + kNV);
+        store_out(c1 - 1);
     }
 
-    const int64_t sb0 = ((n * H + h) * kD + 32 * cw + col) * kD + 4 * g;
-    if (a.ht_dtype == 2) {
-        float *p = reinterpret_cast<float *>(a.ht) + sb0;
+    const int64_t sb0 = (int64_t)(32 * cw + col) * kD + 4 * g;
+    if (u.fin_kind == 2) {
+        float *p = reinterpret_cast<float *>(u.fin) + sb0;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 *reinterpret_cast<f32x4_t *>(p + b * 16 * kD + 16 * t) = S[b][t];
-    } else if (a.ht_dtype == 1) {
-        uint16_t *p = reinterpret_cast<uint16_t *>(a.ht) + sb0;
+    } else if (u.fin_kind == 1) {
+        uint16_t *p = reinterpret_cast<uint16_t *>(u.fin) + sb0;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const u32x2_t u = {pack_bf16x2(S[b][t][0], S[b][t][1]), pack_bf16x2(S[b][t][2], S[b][t][3])};
-                *reinterpret_cast<u32x2_t *>(p + b * 16 * kD + 16 * t) = u;
+                const u32x2_t w = {pack_bf16x2(S[b][t][0], S[b][t][1]), pack_bf16x2(S[b][t][2], S[b][t][3])};
+                *reinterpret_cast<u32x2_t *>(p + b * 16 * kD + 16 * t) = w;
             }
     }
 }
@@ -813,27 +867,143 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t chain = blockIdx.x;
-    const int64_t n = chain / a.H;
-    const int h = (int)(chain % a.H);
-    if (n >= a.N)
+    constexpr int64_t kBlock = (int64_t)kD * kD;
+
+    // decode the work unit (see SegPlan for the passes)
+    Unit u;
+    int64_t chain, seg = 0;
+    int kind = 0;  // pass A: 0 exact segment 0, 1 F run, 2 P run
+    if (a.pass == 0) {
+        chain = blockIdx.x;
+    } else if (a.pass == 1) {
+        const int64_t upc = 2 * (int64_t)a.G - 3;
+        chain = blockIdx.x / upc;
+        const int64_t r = blockIdx.x % upc;
+        if (r > 0) {
+            seg = 1 + (r - 1) / 2;
+            kind = 1 + (int)((r - 1) & 1);
+        }
+    } else {
+        const int64_t upc = (int64_t)a.G - 1;
+        chain = blockIdx.x / upc;
+        seg = 1 + blockIdx.x % upc;
+    }
+    u.n = chain / a.H;
+    u.h = (int)(chain % a.H);
+    if (u.n >= a.N)
         return;
-    const int64_t len = a.seq_len[n];
-    const int64_t start = a.seq_start[n];
-    const int64_t nch = (len + kCH - 1) / kCH;
+    u.len = a.seq_len[u.n];
+    u.start = a.seq_start[u.n];
+    const int64_t nch = (u.len + kCH - 1) / kCH;
+    const size_t elt = a.h0_dtype == 1 ? 2 : 4, elt_t = a.ht_dtype == 1 ? 2 : 4;
+    const void *h0c = a.h0 ? reinterpret_cast<const unsigned char *>(a.h0) + (size_t)chain * kBlock * elt : nullptr;
+    void *htc = a.ht ? reinterpret_cast<unsigned char *>(a.ht) + (size_t)chain * kBlock * elt_t : nullptr;
+    auto segbuf = [&](float *base, int64_t sg) { return base + ((size_t)chain * a.G + (size_t)sg) * kBlock; };
+    u.v_on = true;
+    u.out_on = true;
+    if (a.pass == 0) {
+        u.c0 = 0;
+        u.c1 = nch;
+        u.init_kind = a.h0_dtype;  // 0 none -> zeros, 1 bf16, 2 fp32
+        u.init = h0c;
+        u.fin_kind = a.ht_dtype;
+        u.fin = htc;
+    } else {
+        u.c0 = seg * a.L;
+        u.c1 = u.c0 + a.L < nch ? u.c0 + a.L : nch;
+        if (u.c0 > nch)
+            u.c0 = nch;
+        if (a.pass == 1 && kind == 0) {          // segment 0 from the true initial state
+            u.init_kind = a.h0_dtype;
+            u.init = h0c;
+            u.fin_kind = 2;
+            u.fin = segbuf(a.segS, 1);
+        } else if (a.pass == 1) {                // F (from zero) or P (from I, v = 0)
+            u.init_kind = kind == 1 ? kInitZero : kInitIdentity;
+            u.init = nullptr;
+            u.v_on = kind == 1;
+            u.out_on = false;
+            u.fin_kind = 2;
+            u.fin = segbuf(kind == 1 ? a.segF : a.segP, seg);
+        } else {                                 // pass B: segment seg from S_seg
+            u.init_kind = kInitFp32;
+            u.init = segbuf(a.segS, seg);
+            const bool last = seg == a.G - 1;
+            u.fin_kind = last ? a.ht_dtype : 0;
+            u.fin = last ? htc : nullptr;
+        }
+    }
+
     if (threadIdx.x < 5 * kNS) {
         int *fl = reinterpret_cast<int *>(lds + kOffFlags);
         fl[threadIdx.x] = threadIdx.x < kNS ? -1 : 0;
     }
     if (threadIdx.x < kD) {
-        const float m1 = -kLog2e * fexp2(a.A_log[h] * kLog2e);
-        reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)h * kD + threadIdx.x];
+        const float m1 = -kLog2e * fexp2(a.A_log[u.h] * kLog2e);
+        reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)u.h * kD + threadIdx.x];
     }
     __syncthreads();
     if (wave < 4)
-        fused_producer(a, lds, wave, lane, n, h, start, len, nch);
+        fused_producer(a, u, lds, wave, lane);
     else
-        fused_consumer(a, lds, wave - 4, lane, n, h, start, len, nch);
+        fused_consumer(a, u, lds, wave - 4, lane);
+}
+
+// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32.  One workgroup per
+// (chain, 16 state rows); rows of S are independent.  Thread t owns column t % 128 and
+// rows 8*(t/128) .. +7 of the block.
+struct ScanArgs {
+    float *segS, *segF, *segP;
+    int G;
+    int64_t chains;
+};
+
+__global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float s_rows[16][kD];
+    constexpr int64_t kBlock = (int64_t)kD * kD;
+    const int64_t chain = blockIdx.x >> 3;
+    if (chain >= a.chains)
+        return;
+    const int r0 = (blockIdx.x & 7) * 16;
+    const int c = threadIdx.x & 127;
+    const int half = threadIdx.x >> 7;
+    auto blk = [&](float *base, int g) { return base + ((size_t)chain * a.G + (size_t)g) * kBlock; };
+    {
+        const float *S1 = blk(a.segS, 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            s_rows[8 * half + i][c] = S1[(size_t)(r0 + 8 * half + i) * kD + c];
+    }
+    __syncthreads();
+    for (int g = 1; g + 1 < a.G; ++g) {
+        const float *P = blk(a.segP, g);
+        const float *F = blk(a.segF, g);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = F[(size_t)(r0 + 8 * half + i) * kD + c];
+        for (int k = 0; k < kD; k += 4) {
+            const float p0 = P[(size_t)(k + 0) * kD + c], p1 = P[(size_t)(k + 1) * kD + c];
+            const float p2 = P[(size_t)(k + 2) * kD + c], p3 = P[(size_t)(k + 3) * kD + c];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const f32x4_t sv = *reinterpret_cast<const f32x4_t *>(&s_rows[8 * half + i][k]);
+                acc[i] = fmaf(sv[0], p0, acc[i]);
+                acc[i] = fmaf(sv[1], p1, acc[i]);
+                acc[i] = fmaf(sv[2], p2, acc[i]);
+                acc[i] = fmaf(sv[3], p3, acc[i]);
+            }
+        }
+        __syncthreads();
+        float *Sn = blk(a.segS, g + 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            s_rows[8 * half + i][c] = acc[i];
+            Sn[(size_t)(r0 + 8 * half + i) * kD + c] = acc[i];
+        }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -855,7 +1025,7 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_fused(const FwdArgs &f, hipStream_t s)
+hipError_t launch_forward(const FwdArgs &f, hipStream_t s)
 {
     const int64_t chains = f.lay.n_seq * f.H;
     if (chains == 0)
@@ -880,11 +1050,38 @@ hipError_t launch_fused(const FwdArgs &f, hipStream_t s)
     a.seq_start = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_len);
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
+    a.G = f.lay.seg.G;
+    a.L = f.lay.seg.L;
+    const size_t seg_floats = (size_t)chains * (size_t)a.G * kD * kD;
+    a.segS = reinterpret_cast<float *>(f.ws + f.lay.off_seg);
+    a.segF = a.segS + seg_floats;
+    a.segP = a.segF + seg_floats;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)chains), dim3(512), kFusedLds, s, a);
+    if (a.G <= 1) {
+        a.pass = 0;
+        hipLaunchKernelGGL(fused_kernel, dim3((unsigned)chains), dim3(512), kFusedLds, s, a);
+        return hipGetLastError();
+    }
+    a.pass = 1;
+    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(chains * (2 * a.G - 3))), dim3(512), kFusedLds, s, a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    if (a.G > 2) {
+        ScanArgs sa;
+        sa.segS = a.segS;
+        sa.segF = a.segF;
+        sa.segP = a.segP;
+        sa.G = a.G;
+        sa.chains = chains;
+        hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(chains * 8)), dim3(256), 0, s, sa);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    a.pass = 2;
+    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
     return hipGetLastError();
 }
 

@@ -123,9 +123,12 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
 
 /*
  * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs: the status word and the
- * per-sequence chunk table (start, length, chunk offset), O(N) bytes.  The per-chunk
- * operands never leave the chip, so nothing scales with T or H.  Returns 0 for invalid
- * sizes.
+ * per-sequence chunk table (start, length, chunk offset), O(N) bytes.  Without cu_seqlens
+ * and with few long chains (B * H small, T long), each chain is cut into G segments that
+ * run in parallel (the state after a segment is affine in the state before it); that
+ * adds three fp32 128 x 128 states per chain and segment, 3 * B * H * G * 64 KiB, with G
+ * a deterministic function of (B, T, H).  The per-chunk operands never leave the chip.
+ * Returns 0 for invalid sizes.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 

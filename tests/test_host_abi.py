@@ -3,8 +3,8 @@
 * libkda.so loads and exports every function include/kda.h declares.
 * Every validation error of kda_fwd is returned before anything touches the device:
   the pointers below are never dereferenced, so fake aligned addresses are fine.
-* kda_fwd_workspace_size covers the status word and the per-sequence chunk table only:
-  it does not grow with T or H.
+* kda_fwd_workspace_size covers the status word and the per-sequence chunk table, plus,
+  for few long equal-length chains run as segments, three fp32 states per chain and segment.
 """
 import ctypes
 import os
@@ -51,10 +51,18 @@ def table_bytes(N):
 
 
 def test_workspace_size_formula():
-    for B, T, H in [(1, 64, 1), (2, 4096, 16), (3, 17, 5), (1, 0, 4), (1, 1 << 20, 8)]:
+    # many chains or short sequences: chunk table only, independent of T and H
+    for B, T, H in [(1, 64, 1), (3, 17, 5), (1, 0, 4), (2, 300, 100), (1, 1 << 20, 200)]:
         assert ws_size(B, T, H) == table_bytes(B)
-        assert ws_size(B, T, H + 3) == ws_size(B, T, H)
-    for N, T in [(8, 32000), (256, 65000), (3, 5)]:
+    # few long equal-length chains: plus three fp32 128x128 states per chain and segment
+    for B, T, H in [(2, 4096, 16), (1, 1 << 20, 8), (1, 700, 1)]:
+        extra = ws_size(B, T, H) - table_bytes(B)
+        per_seg = 3 * B * H * 128 * 128 * 4
+        assert extra > 0 and extra % per_seg == 0, (B, T, H, extra)
+        G = extra // per_seg
+        assert 2 <= G <= -(-T // 16), (B, T, H, G)
+    # with cu_seqlens: chunk table only
+    for N, T in [(8, 32000), (256, 65000), (3, 5), (1, 1 << 20)]:
         assert ws_size(1, T, 2, N, True) == table_bytes(N)
         assert ws_size(1, 2 * T, 5, N, True) == table_bytes(N)
     assert ws_size(0, 10, 1) == 0            # B < 1
