@@ -46,8 +46,10 @@ kda_status validate(const void *q, const void *k, const void *v, const void *g, 
     } else if (N != 0 && N != B) {
         return KDA_ERR_SHAPE;
     }
-    // overflow guard on element counts (tokens * heads * 128 must fit comfortably)
-    if (T > ((int64_t)1 << 40) / B || (B * T) > ((int64_t)1 << 46) / (H * kda::kD))
+    // overflow guard on element counts (tokens * heads * 128 must fit comfortably); a
+    // sequence (at most T tokens) has fewer than 2^31 chunks of 16
+    if (T > ((int64_t)1 << 40) / B || (B * T) > ((int64_t)1 << 46) / (H * kda::kD) ||
+        T >= ((int64_t)1 << 35))
         return KDA_ERR_SHAPE;
     if (K != kda::kD || V != kda::kD)
         return KDA_ERR_HEAD_DIM;

@@ -334,6 +334,127 @@ struct Unit {
     bool out_on;          // write out rows of this range
 };
 
+// A workgroup's work: one unit (segment passes), or -- whole-chain pass -- the chains
+// (n, h) for n = sub, sub + stride, ... < N of one head h, one after another.  The
+// producers then run ahead into the next chain while the consumers finish the current one.
+struct WgPlan {
+    int pass;
+    int h;
+    int64_t sub, stride;  // whole-chain pass: sequences sub, sub + stride, ...
+    int64_t n;            // segment passes: the sequence
+    int seg;              // segment passes: the segment
+    int kind;             // pass A: 0 exact segment 0, 1 F run, 2 P run
+};
+
+__device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
+{
+    constexpr int64_t kBlock = (int64_t)kD * kD;
+    int64_t n;
+    if (w.pass == 0) {
+        n = w.sub + k * w.stride;
+        if (n >= a.N)
+            return false;
+    } else {
+        if (k > 0)
+            return false;
+        n = w.n;
+    }
+    const int64_t chain = n * a.H + w.h;
+    u.n = n;
+    u.h = w.h;
+    u.len = a.seq_len[u.n];
+    u.start = a.seq_start[u.n];
+    const int64_t nch = (u.len + kCH - 1) / kCH;
+    const size_t elt = a.h0_dtype == 1 ? 2 : 4, elt_t = a.ht_dtype == 1 ? 2 : 4;
+    const void *h0c = a.h0 ? reinterpret_cast<const unsigned char *>(a.h0) + (size_t)chain * kBlock * elt : nullptr;
+    void *htc = a.ht ? reinterpret_cast<unsigned char *>(a.ht) + (size_t)chain * kBlock * elt_t : nullptr;
+    auto segbuf = [&](float *base, int64_t sg) { return base + ((size_t)chain * a.G + (size_t)sg) * kBlock; };
+    u.v_on = true;
+    u.out_on = true;
+    if (w.pass == 0) {
+        u.c0 = 0;
+        u.c1 = nch;
+        u.init_kind = a.h0_dtype;  // 0 none -> zeros, 1 bf16, 2 fp32
+        u.init = h0c;
+        u.fin_kind = a.ht_dtype;
+        u.fin = htc;
+        return true;
+    }
+    const int64_t seg = w.seg;
+    u.c0 = seg * a.L < nch ? seg * a.L : nch;
+    u.c1 = u.c0 + a.L < nch ? u.c0 + a.L : nch;
+    if (w.pass == 1 && w.kind == 0) {          // segment 0 from the true initial state
+        u.init_kind = a.h0_dtype;
+        u.init = h0c;
+        u.fin_kind = 2;
+        u.fin = segbuf(a.segS, 1);
+    } else if (w.pass == 1) {                  // F (from zero) or P (from I, v = 0)
+        u.init_kind = w.kind == 1 ? kInitZero : kInitIdentity;
+        u.init = nullptr;
+        u.v_on = w.kind == 1;
+        u.out_on = false;
+        u.fin_kind = 2;
+        u.fin = segbuf(w.kind == 1 ? a.segF : a.segP, seg);
+    } else {                                   // pass B: segment seg from S_seg
+        u.init_kind = kInitFp32;
+        u.init = segbuf(a.segS, seg);
+        const bool last = seg == a.G - 1;
+        u.fin_kind = last ? a.ht_dtype : 0;
+        u.fin = last ? htc : nullptr;
+    }
+    return true;
+}
+
+// Token range of unit k of a workgroup (what the producers need of it).  Chunk indices
+// fit 32 bits (the host rejects sequences of 2^31 chunks or more).
+struct Range {
+    int64_t start, len;  // the sequence's first token and length
+    int c0, c1;          // chunk range of the unit
+};
+__device__ bool range_at(const FusedArgs &a, const WgPlan &w, int64_t k, Range &r)
+{
+    int64_t n, seg = 0;
+    if (w.pass == 0) {
+        n = w.sub + k * w.stride;
+        if (n >= a.N)
+            return false;
+    } else {
+        if (k > 0)
+            return false;
+        n = w.n;
+        seg = w.seg;
+    }
+    r.len = a.seq_len[n];
+    r.start = a.seq_start[n];
+    const int nch = (int)((r.len + kCH - 1) / kCH);
+    if (w.pass == 0) {
+        r.c0 = 0;
+        r.c1 = nch;
+    } else {
+        const int64_t c0 = seg * a.L < nch ? seg * a.L : nch;
+        r.c0 = (int)c0;
+        r.c1 = c0 + a.L < nch ? (int)(c0 + a.L) : nch;
+    }
+    return true;
+}
+
+// Walks the workgroup's items (chunks of its units, in order) forward.
+struct ItemWalk {
+    int k = 0, base = 0;  // unit index and its first item
+    bool valid = false;
+    Range r;
+    __device__ void init(const FusedArgs &a, const WgPlan &w) { k = 0; base = 0; valid = range_at(a, w, 0, r); }
+    // position the walk on the unit holding item it (items only move forward)
+    __device__ void seek(const FusedArgs &a, const WgPlan &w, int it)
+    {
+        while (valid && it >= base + (r.c1 - r.c0)) {
+            base += r.c1 - r.c0;
+            ++k;
+            valid = range_at(a, w, k, r);
+        }
+    }
+};
+
 typedef __attribute__((address_space(3))) volatile int lds_flag_t;
 
 // Spin until *p == want (all lanes read the same LDS word).  Returns false on time-out.
@@ -379,11 +500,10 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
     }
 }
 
-__device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char *lds, int p, int lane)
+__device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int p, int lane)
 {
     const int64_t H = a.H;
-    const int h = u.h;
-    const int64_t start = u.start, len = u.len, c0 = u.c0, c1 = u.c1;
+    const int h = w.h;
     const int r = lane & 15;   // token within the chunk
     const int qb = lane >> 4;  // channels 32*qb .. 32*qb+31
     unsigned char *stage = lds + kOffStage + p * kStageBytes;
@@ -393,13 +513,14 @@ __device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char 
     lds_flag_t *taken = ready + kNS;
     const uint32_t rowb = (uint32_t)(H * kD * 2);  // bytes between consecutive tokens of a head
 
-    // Direct-to-LDS loads of chunk j: 4 loads of 16 B per lane per tensor (4 token rows
-    // each) and one 2-byte load per lane for beta.  Row t, 16-byte segment s of a tensor
-    // goes to LDS segment s ^ (t & 7) of row t, so that the reads below (8 lanes = 8 rows
-    // of one segment) hit distinct banks.  Rows past the chunk's end load zeros.
-    auto issue_stage = [&](int64_t j) {
-        const int64_t t0 = start + j * kCH;
-        const int64_t rem = len - j * kCH;
+    // Direct-to-LDS loads of chunk j of unit u: 4 loads of 16 B per lane per tensor (4
+    // token rows each) and one 2-byte load per lane for beta.  Row t, 16-byte segment s
+    // of a tensor goes to LDS segment s ^ (t & 7) of row t, so that the reads below (8
+    // lanes = 8 rows of one segment) hit distinct banks.  Rows past the chunk's end load
+    // zeros.
+    auto issue_stage = [&](const Range &u, int64_t j) {
+        const int64_t t0 = u.start + j * kCH;
+        const int64_t rem = u.len - j * kCH;
         const int tl = rem < kCH ? (int)rem : kCH;
         const size_t elem0 = ((size_t)t0 * (size_t)H + (size_t)h) * kD;
         const uint32_t nb = (uint32_t)(tl - 1) * rowb + 256u;
@@ -425,11 +546,20 @@ __device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char 
     const float lb2 = a.lower_bound * kLog2e;
 
     bool spun_out = false;
-    if (c0 + p < c1)
-        issue_stage(c0 + p);
-    for (int64_t j = c0 + p; j < c1; j += 4) {
-        const int64_t it = j - c0;  // item index within the range: slot it % kNS
-        const int64_t rem = len - j * kCH;
+    // this wavefront prepares items p, p+4, p+8, ...; `nxt` stays 4 items ahead of `cur`
+    ItemWalk cur, nxt;
+    cur.init(a, w);
+    nxt.init(a, w);
+    nxt.seek(a, w, p);
+    if (nxt.valid)
+        issue_stage(nxt.r, nxt.r.c0 + (p - nxt.base));
+    for (int it = p;; it += 4) {
+        cur.seek(a, w, it);
+        if (!cur.valid)
+            break;
+        const Range &u = cur.r;
+        const int64_t j = u.c0 + (it - cur.base);  // chunk of the sequence
+        const int64_t rem = u.len - j * kCH;
         const int tlen = rem < kCH ? (int)rem : kCH;
         const bool valid = r < tlen;
 
@@ -457,9 +587,10 @@ __device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char 
         }
         const uint32_t braw = *reinterpret_cast<const uint32_t *>(stage + 12288 + 4 * r);
         wait_lgkmcnt0();
-        // the staging tile is consumed: fetch this wavefront's next chunk into it
-        if (j + 4 < c1)
-            issue_stage(j + 4);
+        // the staging tile is consumed: fetch this wavefront's next item into it
+        nxt.seek(a, w, it + 4);
+        if (nxt.valid)
+            issue_stage(nxt.r, nxt.r.c0 + (it + 4 - nxt.base));
 
         const float bt = valid ? sigmoidf_fast(bf16f((uint16_t)(braw & 0xffffu))) : 0.f;
 
@@ -556,8 +687,8 @@ __device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char 
         const f32x4_t MqT = transpose16(Mq, tile, lane);
 
         // ---- hand the operand block to the consumers ----
-        const int s = (int)(it % kNS);
-        if (!spun_out && !lds_wait_eq4(taken + 4 * s, (int)(it / kNS))) {
+        const int s = it % kNS;
+        if (!spun_out && !lds_wait_eq4(taken + 4 * s, it / kNS)) {
             spun_out = true;  // stop waiting from here on; the status word reports it
             atomicOr(a.status, kStatusSpin);
         }
@@ -619,11 +750,14 @@ __device__ void fused_producer(const FusedArgs &a, const Unit &u, unsigned char 
         wait_lgkmcnt0();
         __asm__ volatile("" ::: "memory");
         if (lane == 0)
-            ready[s] = (int)it;
+            ready[s] = it;
     }
 }
 
-__device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane)
+// One unit's items for consumer wavefront cw: state in, chunk recurrence, state out.
+// Items of the unit are it0, it0+1, ... in the workgroup's item numbering (slots, flags).
+__device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane,
+                             int it0, bool &spun_out)
 {
     const int64_t H = a.H;
     const int h = u.h;
@@ -656,16 +790,25 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
                     S[b][t] = f32x4_t{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
                 }
         } else {
-            const bool ident = u.init_kind == kInitIdentity;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int v = 32 * cw + 16 * b + col;
+                for (int t = 0; t < 8; ++t)
+                    S[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (u.init_kind == kInitIdentity) {
+                // S[v][v] = 1: column v = 32cw + 16b + col sits in channel tile 2cw + b,
+                // element col - 4g of this lane when that lies in [0, 4)
+                const int e = col - 4 * g;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        S[b][t][i] = (ident && v == 16 * t + 4 * g + i) ? 1.f : 0.f;
-                }
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        if (t == 2 * cw + b) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                S[b][t][i] = e == i ? 1.f : 0.f;
+                        }
+            }
         }
     }
 
@@ -678,7 +821,7 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
         const __amdgpu_buffer_rsrc_t rv =
             make_rsrc(a.v + ((size_t)t0 * (size_t)H + (size_t)h) * kD + 32 * cw, (uint32_t)(tl - 1) * rowb + 64u);
         const uint32_t vo = (uint32_t)(lane >> 2) * rowb + (uint32_t)(lane & 3) * 16u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vring + ((j - c0) % kNV) * 1024), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vring + ((int)(j - c0) % kNV) * 1024), 16, vo, 0, 0, 0);
     };
     if (u.v_on) {
 #pragma unroll
@@ -686,7 +829,6 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
             if (c0 + jp < c1)
                 issue_v(c0 + jp);
     }
-    bool spun_out = false;
     // -I in the MFMA A layout for the k-slot order of a channel pair of tiles (2t, 2t+1):
     // slot 8*(m/4) + m%4 holds channel m of tile 2t, slot 8*(m/4) + 4 + m%4 channel m of
     // tile 2t+1.  Lane m + 16*(m/4) carries the -1 (bf16 0xbf80) at element m%4 or 4+m%4.
@@ -710,8 +852,9 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
                                          32 * cw + 8 * (lane & 3)) = ow;
     };
     for (int64_t j = c0; j < c1; ++j) {
-        const int64_t it = j - c0;  // item index within the range
-        const int s = (int)(it % kNS);
+        const int iu = (int)(j - c0);  // item index within the unit (value ring, store count)
+        const int it = it0 + iu;       // item index within the workgroup (operand slots)
+        const int s = it % kNS;
         const unsigned char *rec = lds + (size_t)s * kBlkBytes;
         u32x4_t kg[4], kgl[4], qg[4], kd[8];
         f32x4_t gm[8];
@@ -737,15 +880,15 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
         const int seen = ready[s];
         __asm__ volatile("" ::: "memory");
         read_ops();
-        if (__builtin_amdgcn_readfirstlane(seen) != (int)it) {
-            if (!spun_out && !lds_wait_eq(ready + s, (int)it)) {
+        if (__builtin_amdgcn_readfirstlane(seen) != it) {
+            if (!spun_out && !lds_wait_eq(ready + s, it)) {
                 spun_out = true;  // stop waiting from here on; the status word reports it
                 atomicOr(a.status, kStatusSpin);
             }
             read_ops();
         }
         // the previous chunk's output tile (staged in LDS) goes to HBM
-        if (u.out_on && it > 0)
+        if (u.out_on && iu > 0)
             store_out(j - 1);
 
         // value tile of chunk j: vector-memory operations issued after its ring load are
@@ -756,9 +899,9 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
         if (u.v_on) {
             const int64_t later = c1 - 1 - j;
             const int nd = later < 2 ? (int)later : 2;
-            const int ns = !u.out_on ? 0 : it < 3 ? (int)it : 3;
+            const int ns = !u.out_on ? 0 : iu < 3 ? iu : 3;
             wait_vmcnt_rt(nd + ns);
-            unsigned char *vt = vring + (it % kNV) * 1024;
+            unsigned char *vt = vring + (iu % kNV) * 1024;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -835,7 +978,7 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
                 *reinterpret_cast<uint16_t *>(obuf + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
         // every operand of chunk j is in registers (used above): release the slot
         if (lane == 0)
-            taken[4 * s + cw] = (int)(it / kNS) + 1;
+            taken[4 * s + cw] = it / kNS + 1;
     }
     if (u.out_on && c1 > c0) {
         wait_lgkmcnt0();
@@ -862,76 +1005,54 @@ __device__ void fused_consumer(const FusedArgs &a, const Unit &u, unsigned char 
     }
 }
 
+__device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int cw, int lane)
+{
+    bool spun_out = false;
+    int it0 = 0;
+    Unit u;
+    for (int64_t k = 0; unit_at(a, w, k, u); ++k) {
+        // the previous unit's stores are done before this unit's value-ring bookkeeping starts
+        wait_vmcnt<0>();
+        consume_unit(a, u, lds, cw, lane, it0, spun_out);
+        it0 += (int)(u.c1 - u.c0);
+    }
+}
+
 __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    constexpr int64_t kBlock = (int64_t)kD * kD;
 
-    // decode the work unit (see SegPlan for the passes)
-    Unit u;
-    int64_t chain, seg = 0;
-    int kind = 0;  // pass A: 0 exact segment 0, 1 F run, 2 P run
+    // this workgroup's work (see SegPlan for the passes)
+    WgPlan w;
+    w.pass = a.pass;
+    w.kind = 0;
+    w.seg = 0;
+    const uint32_t bid = blockIdx.x, H32 = (uint32_t)a.H;
     if (a.pass == 0) {
-        chain = blockIdx.x;
-    } else if (a.pass == 1) {
-        const int64_t upc = 2 * (int64_t)a.G - 3;
-        chain = blockIdx.x / upc;
-        const int64_t r = blockIdx.x % upc;
-        if (r > 0) {
-            seg = 1 + (r - 1) / 2;
-            kind = 1 + (int)((r - 1) & 1);
-        }
+        // heads h = block % H; the blocks of one head share its sequences round-robin
+        w.h = (int)(bid % H32);
+        w.sub = bid / H32;
+        w.stride = gridDim.x / H32;
+        w.n = 0;
     } else {
-        const int64_t upc = (int64_t)a.G - 1;
-        chain = blockIdx.x / upc;
-        seg = 1 + blockIdx.x % upc;
-    }
-    u.n = chain / a.H;
-    u.h = (int)(chain % a.H);
-    if (u.n >= a.N)
-        return;
-    u.len = a.seq_len[u.n];
-    u.start = a.seq_start[u.n];
-    const int64_t nch = (u.len + kCH - 1) / kCH;
-    const size_t elt = a.h0_dtype == 1 ? 2 : 4, elt_t = a.ht_dtype == 1 ? 2 : 4;
-    const void *h0c = a.h0 ? reinterpret_cast<const unsigned char *>(a.h0) + (size_t)chain * kBlock * elt : nullptr;
-    void *htc = a.ht ? reinterpret_cast<unsigned char *>(a.ht) + (size_t)chain * kBlock * elt_t : nullptr;
-    auto segbuf = [&](float *base, int64_t sg) { return base + ((size_t)chain * a.G + (size_t)sg) * kBlock; };
-    u.v_on = true;
-    u.out_on = true;
-    if (a.pass == 0) {
-        u.c0 = 0;
-        u.c1 = nch;
-        u.init_kind = a.h0_dtype;  // 0 none -> zeros, 1 bf16, 2 fp32
-        u.init = h0c;
-        u.fin_kind = a.ht_dtype;
-        u.fin = htc;
-    } else {
-        u.c0 = seg * a.L;
-        u.c1 = u.c0 + a.L < nch ? u.c0 + a.L : nch;
-        if (u.c0 > nch)
-            u.c0 = nch;
-        if (a.pass == 1 && kind == 0) {          // segment 0 from the true initial state
-            u.init_kind = a.h0_dtype;
-            u.init = h0c;
-            u.fin_kind = 2;
-            u.fin = segbuf(a.segS, 1);
-        } else if (a.pass == 1) {                // F (from zero) or P (from I, v = 0)
-            u.init_kind = kind == 1 ? kInitZero : kInitIdentity;
-            u.init = nullptr;
-            u.v_on = kind == 1;
-            u.out_on = false;
-            u.fin_kind = 2;
-            u.fin = segbuf(kind == 1 ? a.segF : a.segP, seg);
-        } else {                                 // pass B: segment seg from S_seg
-            u.init_kind = kInitFp32;
-            u.init = segbuf(a.segS, seg);
-            const bool last = seg == a.G - 1;
-            u.fin_kind = last ? a.ht_dtype : 0;
-            u.fin = last ? htc : nullptr;
+        const uint32_t upc = a.pass == 1 ? 2u * (uint32_t)a.G - 3u : (uint32_t)a.G - 1u;
+        const uint32_t chain = bid / upc, r = bid % upc;
+        if (a.pass == 1) {
+            if (r > 0) {
+                w.seg = 1 + (int)((r - 1) / 2);
+                w.kind = 1 + (int)((r - 1) & 1);
+            }
+        } else {
+            w.seg = 1 + (int)r;
         }
+        w.h = (int)(chain % H32);
+        w.n = chain / H32;
+        w.sub = 0;
+        w.stride = 1;
+        if (w.n >= a.N)
+            return;
     }
 
     if (threadIdx.x < 5 * kNS) {
@@ -939,14 +1060,14 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         fl[threadIdx.x] = threadIdx.x < kNS ? -1 : 0;
     }
     if (threadIdx.x < kD) {
-        const float m1 = -kLog2e * fexp2(a.A_log[u.h] * kLog2e);
-        reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)u.h * kD + threadIdx.x];
+        const float m1 = -kLog2e * fexp2(a.A_log[w.h] * kLog2e);
+        reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)w.h * kD + threadIdx.x];
     }
     __syncthreads();
     if (wave < 4)
-        fused_producer(a, u, lds, wave, lane);
+        fused_producer(a, w, lds, wave, lane);
     else
-        fused_consumer(a, u, lds, wave - 4, lane);
+        fused_consumer(a, w, lds, wave - 4, lane);
 }
 
 // Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32.  One workgroup per
@@ -1061,8 +1182,15 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s)
     if (e != hipSuccess)
         return e;
     if (a.G <= 1) {
+        // whole chains: H x per_head workgroups, each running the sequences n = sub,
+        // sub + per_head, ... of one head back to back (about one workgroup per CU)
         a.pass = 0;
-        hipLaunchKernelGGL(fused_kernel, dim3((unsigned)chains), dim3(512), kFusedLds, s, a);
+        int64_t per_head = kPlanCUs / f.H;
+        if (per_head < 1)
+            per_head = 1;
+        if (per_head > f.lay.n_seq)
+            per_head = f.lay.n_seq;
+        hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(f.H * per_head)), dim3(512), kFusedLds, s, a);
         return hipGetLastError();
     }
     a.pass = 1;
