@@ -6,11 +6,14 @@ A step is one kda_fwd call (chunk table, prep, state/output stages) over one bat
 seeded synthetic input already resident in HBM.  Default workload: B=2, T=4096, H=16,
 K=V=128, fp32 initial and final state (index 1 of workloads.config).  Prints one JSON line.
 
-roofline: the dominant kernel (largest average duration, from HIP events recorded around
-each stage on the launch stream over the timed steps) against HBM: achieved = that
-kernel's algorithmic bytes per launch / its average duration.  Algorithmic bytes of the
-forward kernel = the whole path: q, k, v, g (4 x 256 B) + beta (2 B) + out (256 B) per
-head-token, plus initial/final state.
+roofline: the dominant kernel, fused_kernel (the forward kernel), against HBM.  HIP events
+are recorded on the launch stream around every launch of every timed step.  Without
+segmentation fused_kernel runs once per step; with it (few long chains) twice, pass A and
+pass B, with seg_scan_kernel between them.  achieved = the path's algorithmic bytes per
+step / fused_kernel's time per step (the sum over its launches): q, k, v, g (4 x 256 B) +
+beta (2 B) + out (256 B) per head-token, plus initial/final state.  traffic (when the
+committed rocprofv3 summary matches the kernel source) is fused_kernel's calibrated
+FETCH_SIZE + WRITE_SIZE per step, summed the same way.
 cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
 
 --copy-calibration runs only a plain device-to-device copy of known size (for scaling the
@@ -44,9 +47,9 @@ def state_bytes(w):
 
 
 def committed_traffic(workload_name, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary of this workload
-    (profiles/kda_fwd_<workload>.md), or None when there is none or the kernel source has
-    changed since the counters were taken."""
+    """HBM bytes per step of `kernel` (summed over its launches) from the committed rocprofv3
+    summary of this workload (profiles/kda_fwd_<workload>.md), or None when there is none or
+    the kernel source has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"kda_fwd_{workload_name}.md")
     src = os.path.join(ROOT, "gated_delta_rule_86_amd", "csrc", "kda_kernels.hip")
@@ -54,7 +57,7 @@ def committed_traffic(workload_name, kernel):
         return None
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     for line in open(path):
-        if line.startswith("traffic_bytes_per_launch:"):
+        if line.startswith("traffic_bytes_per_step:"):
             fields = dict(f.split("=", 1) for f in line.split(":", 1)[1].split())
             if fields.get("source_sha256") == sha and kernel in fields:
                 return int(fields[kernel])
@@ -156,7 +159,7 @@ def main():
     ev = []
     for _ in range(args.steps):
         row = []
-        for _ in range(3):
+        for _ in range(5):
             e = ctypes.c_void_p()
             assert hip.hipEventCreate(ctypes.byref(e)) == 0
             row.append(e.value)
@@ -171,13 +174,19 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    stage_names = ["chunk_table_kernel", "fused_kernel"]
-    stage_ms = [0.0, 0.0]
+    # intervals: table, forward launch 1, scan, forward launch 2
+    iv = [0.0, 0.0, 0.0, 0.0]
     for i in range(args.steps):
-        for j in range(2):
+        for j in range(4):
             ms = ctypes.c_float()
             assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[i][j], ev[i][j + 1]) == 0
-            stage_ms[j] += ms.value / args.steps
+            iv[j] += ms.value / args.steps
+    launches = kda.forward_launches(w.B, w.T, w.H, w.N, cu is not None)
+    stage_names = ["chunk_table_kernel", "fused_kernel", "seg_scan_kernel"]
+    if launches == 2:
+        stage_ms = [iv[0], iv[1] + iv[3], iv[2]]
+    else:  # one forward launch; the later marks are recorded back to back
+        stage_ms = [iv[0], iv[1], 0.0]
     for row in ev:
         for e in row:
             hip.hipEventDestroy(e)
@@ -185,11 +194,9 @@ def main():
     ht = w.head_tokens
     ms_per_step = elapsed / args.steps * 1e3
     value = ht / (elapsed / args.steps)
-    kernel_bytes = {"chunk_table_kernel": 8 * (w.N + 1),
-                    "fused_kernel": ht * BYTES_PER_HT + state_bytes(w)}
-    dom = max(range(2), key=lambda j: stage_ms[j])
-    dname = stage_names[dom]
-    achieved = kernel_bytes[dname] / (stage_ms[dom] * 1e-3) / 1e9
+    dname = "fused_kernel"
+    kernel_bytes = ht * BYTES_PER_HT + state_bytes(w)
+    achieved = kernel_bytes / (stage_ms[1] * 1e-3) / 1e9
     path_bytes = ht * BYTES_PER_HT + state_bytes(w)
     path_gbps = path_bytes / (ms_per_step * 1e-3) / 1e9
     path_tflops = ht * FLOPS_PER_HT / (ms_per_step * 1e-3) / 1e12
@@ -209,8 +216,8 @@ def main():
         "config": dict(w.describe(), head_tokens=ht),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name, dname),
-                     "kernel": dname,
-                     "kernel_ms": stage_ms[dom], "kernel_algorithmic_bytes": kernel_bytes[dname]},
+                     "kernel": dname, "launches_per_step": launches,
+                     "kernel_ms": stage_ms[1], "kernel_algorithmic_bytes": kernel_bytes},
         "path": {"algorithmic_bytes": path_bytes, "achieved_GBps": path_gbps,
                  "hbm_frac": path_gbps / HBM_PEAK_GBPS, "achieved_TFLOPs": path_tflops,
                  "mfma_frac": path_tflops / MFMA_BF16_PEAK_TFLOPS,

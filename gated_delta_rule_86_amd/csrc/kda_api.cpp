@@ -190,9 +190,11 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
     };
     if (!mark(0) || kda::launch_chunk_table(a, s) != hipSuccess)
         return KDA_ERR_HIP;
-    if (!mark(1) || kda::launch_forward(a, s) != hipSuccess)
-        return KDA_ERR_HIP;
-    if (!mark(2))
+    hipEvent_t marks[3];
+    if (events)
+        for (int i = 0; i < 3; ++i)
+            marks[i] = static_cast<hipEvent_t>(events[2 + i]);
+    if (!mark(1) || kda::launch_forward(a, s, events ? marks : nullptr) != hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
 }
@@ -222,8 +224,11 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
                          int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *stage_events)
 {
-    if (!stage_events || !stage_events[0] || !stage_events[1] || !stage_events[2])
+    if (!stage_events)
         return KDA_ERR_NULL;
+    for (int i = 0; i < 5; ++i)
+        if (!stage_events[i])
+            return KDA_ERR_NULL;
     return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                     initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
                     B, T, H, N, K, V, workspace, workspace_bytes, stream, stage_events);

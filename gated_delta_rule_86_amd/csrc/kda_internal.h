@@ -108,6 +108,6 @@ struct FwdArgs {
 };
 
 hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s);
-hipError_t launch_forward(const FwdArgs &a, hipStream_t s);
+hipError_t launch_forward(const FwdArgs &a, hipStream_t s, hipEvent_t const *marks);
 
 }  // namespace kda

@@ -1146,11 +1146,19 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs &f, hipStream_t s)
+// marks[0..3] (optional, may be NULL): recorded after the first forward launch, after the
+// scan, after the last forward launch (a single whole-chain launch records all three
+// after it), so the caller can time each launch.
+hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *marks)
 {
+    auto mark = [&](int i) { return marks == nullptr ? hipSuccess : hipEventRecord(marks[i], s); };
     const int64_t chains = f.lay.n_seq * f.H;
-    if (chains == 0)
-        return hipSuccess;
+    if (chains == 0) {
+        hipError_t e0;
+        if ((e0 = mark(0)) != hipSuccess || (e0 = mark(1)) != hipSuccess)
+            return e0;
+        return mark(2);
+    }
     FusedArgs a;
     a.q = f.q;
     a.k = f.k;
@@ -1191,11 +1199,15 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s)
         if (per_head > f.lay.n_seq)
             per_head = f.lay.n_seq;
         hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(f.H * per_head)), dim3(512), kFusedLds, s, a);
-        return hipGetLastError();
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        if ((e = mark(0)) != hipSuccess || (e = mark(1)) != hipSuccess)
+            return e;
+        return mark(2);
     }
     a.pass = 1;
     hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(chains * (2 * a.G - 3))), dim3(512), kFusedLds, s, a);
-    if ((e = hipGetLastError()) != hipSuccess)
+    if ((e = hipGetLastError()) != hipSuccess || (e = mark(0)) != hipSuccess)
         return e;
     if (a.G > 2) {
         ScanArgs sa;
@@ -1208,9 +1220,13 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s)
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
+    if ((e = mark(1)) != hipSuccess)
+        return e;
     a.pass = 2;
     hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    return mark(2);
 }
 
 }  // namespace kda

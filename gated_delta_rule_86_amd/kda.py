@@ -75,6 +75,16 @@ def workspace_size(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -> 
     return int(lib().kda_fwd_workspace_size(B, T, H, N, 1 if varlen else 0))
 
 
+def forward_launches(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -> int:
+    """Launches of the forward kernel per call: 2 (pass A and pass B) when the chains run as
+    segments, else 1.  Segmentation shows in the workspace size (three fp32 128 x 128
+    states per chain and segment beyond the chunk table)."""
+    n = N if varlen else B
+    up = lambda x: -(-x // 256) * 256
+    table = 256 + up(8 * n) + up(8 * n) + up(8 * (n + 1))
+    return 2 if workspace_size(B, T, H, N, varlen) > table else 1
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -107,8 +117,8 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     cu_seqlens: int64 [N+1] device tensor or None (then N = B).
     cu_seqlens_host: optional host copy (sequence or CPU tensor) for a synchronous check.
     workspace: optional uint8 device tensor of at least workspace_size(...) bytes.
-    stage_events: optional sequence of 3 raw hipEvent_t handles (ints); when given the call
-    goes through kda_fwd_timed, which records them around the chunk-table and forward stages.
+    stage_events: optional sequence of 5 raw hipEvent_t handles (ints); when given the call
+    goes through kda_fwd_timed, which records them around each launch (see include/kda.h).
     """
     import torch
     L = lib()
@@ -154,7 +164,7 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     if stage_events is None:
         st = L.kda_fwd(*args)
     else:
-        evs = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(int(e)) for e in stage_events])
+        evs = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(int(e)) for e in stage_events])
         st = L.kda_fwd_timed(*args, evs)
     if st != KDA_OK:
         raise KDAError(st)

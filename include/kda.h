@@ -106,11 +106,16 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g, c
 
 /*
  * kda_fwd_timed -- kda_fwd with stage timing, for measurement.  Same arguments and behaviour
- * as kda_fwd, plus stage_events: three hipEvent_t handles (created by the caller) that are
- * recorded on `stream` before the chunk-table stage, before the forward stage (the kernel
- * that computes out and final_state), and after it.  hipEventElapsedTime between
- * consecutive events gives each stage's duration.  Returns KDA_ERR_NULL if any of the
- * three handles is NULL.
+ * as kda_fwd, plus stage_events: five hipEvent_t handles (created by the caller), recorded
+ * on `stream`:
+ *   [0] before the chunk-table kernel
+ *   [1] before the first forward-kernel launch
+ *   [2] after it
+ *   [3] after the segment scan (recorded right after [2] when there is none)
+ *   [4] after the second forward-kernel launch (right after [3] when there is none)
+ * Without segmentation (see kda_fwd_workspace_size) the forward kernel runs once; with it,
+ * pass A, the scan and pass B.  hipEventElapsedTime between consecutive events gives each
+ * launch's duration.  Returns KDA_ERR_NULL if any of the five handles is NULL.
  */
 kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,
                          float scale, void *out, const float *A_log, const float *dt_bias,
