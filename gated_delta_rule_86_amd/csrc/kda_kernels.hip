@@ -1064,66 +1064,96 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)w.h * kD + threadIdx.x];
     }
     __syncthreads();
-    if (wave < 4)
+    if (wave < 4) {
         fused_producer(a, w, lds, wave, lane);
-    else
+    } else {
+        // The consumers set the pace (producers finish ahead and wait for free slots), so
+        // they get issue priority over the producer sharing their SIMD.
+        __builtin_amdgcn_s_setprio(1);
         fused_consumer(a, w, lds, wave - 4, lane);
+    }
 }
 
-// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32.  One workgroup per
-// (chain, 16 state rows); rows of S are independent.  Thread t owns column t % 128 and
-// rows 8*(t/128) .. +7 of the block.
+// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32.  Rows of S are
+// independent, so one workgroup takes R rows of one chain (128/R workgroups per chain)
+// and keeps them in LDS across the steps.  P_g (64 KiB) goes through LDS once per step
+// with 16-byte coalesced loads; the loads of P_{g+1} and F_{g+1} are issued before step
+// g's arithmetic.  Thread t computes column t % 128 of rows (R/2)*(t/128) .. +R/2-1.
 struct ScanArgs {
     float *segS, *segF, *segP;
     int G;
     int64_t chains;
 };
 
+template <int R>
 __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float s_rows[16][kD];
+    constexpr int RH = R / 2;
+    __shared__ __attribute__((aligned(16))) float s_P[kD * kD];
+    __shared__ __attribute__((aligned(16))) float s_rows[R][kD];
     constexpr int64_t kBlock = (int64_t)kD * kD;
-    const int64_t chain = blockIdx.x >> 3;
+    constexpr int kBlocksPerChain = kD / R;
+    const int64_t chain = blockIdx.x / kBlocksPerChain;
     if (chain >= a.chains)
         return;
-    const int r0 = (blockIdx.x & 7) * 16;
-    const int c = threadIdx.x & 127;
-    const int half = threadIdx.x >> 7;
+    const int r0 = (blockIdx.x % kBlocksPerChain) * R;
+    const int tid = threadIdx.x;
+    const int c = tid & 127;
+    const int rr = RH * (tid >> 7);
     auto blk = [&](float *base, int g) { return base + ((size_t)chain * a.G + (size_t)g) * kBlock; };
     {
         const float *S1 = blk(a.segS, 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            s_rows[8 * half + i][c] = S1[(size_t)(r0 + 8 * half + i) * kD + c];
+        for (int i = 0; i < RH; ++i)
+            s_rows[rr + i][c] = S1[(size_t)(r0 + rr + i) * kD + c];
     }
-    __syncthreads();
-    for (int g = 1; g + 1 < a.G; ++g) {
-        const float *P = blk(a.segP, g);
+    // P_g and this thread's entries of F_g in registers (P: float4 t + 256 i)
+    f32x4_t pre[16];
+    float fpre[RH];
+    auto load_PF = [&](int g) {
+        const f32x4_t *P = reinterpret_cast<const f32x4_t *>(blk(a.segP, g));
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            pre[i] = P[tid + 256 * i];
         const float *F = blk(a.segF, g);
-        float acc[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] = F[(size_t)(r0 + 8 * half + i) * kD + c];
+        for (int i = 0; i < RH; ++i)
+            fpre[i] = F[(size_t)(r0 + rr + i) * kD + c];
+    };
+    if (a.G > 2)
+        load_PF(1);
+    for (int g = 1; g + 1 < a.G; ++g) {
+        float acc[RH];
+#pragma unroll
+        for (int i = 0; i < RH; ++i)
+            acc[i] = fpre[i];
+        __syncthreads();  // previous step's reads of s_P are done
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            reinterpret_cast<f32x4_t *>(s_P)[tid + 256 * i] = pre[i];
+        __syncthreads();
+        if (g + 2 < a.G)
+            load_PF(g + 1);
         for (int k = 0; k < kD; k += 4) {
-            const float p0 = P[(size_t)(k + 0) * kD + c], p1 = P[(size_t)(k + 1) * kD + c];
-            const float p2 = P[(size_t)(k + 2) * kD + c], p3 = P[(size_t)(k + 3) * kD + c];
+            f32x4_t x[RH];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const f32x4_t sv = *reinterpret_cast<const f32x4_t *>(&s_rows[8 * half + i][k]);
-                acc[i] = fmaf(sv[0], p0, acc[i]);
-                acc[i] = fmaf(sv[1], p1, acc[i]);
-                acc[i] = fmaf(sv[2], p2, acc[i]);
-                acc[i] = fmaf(sv[3], p3, acc[i]);
+            for (int i = 0; i < RH; ++i)
+                x[i] = *reinterpret_cast<const f32x4_t *>(&s_rows[rr + i][k]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pk = s_P[(k + e) * kD + c];
+#pragma unroll
+                for (int i = 0; i < RH; ++i)
+                    acc[i] = fmaf(x[i][e], pk, acc[i]);
             }
         }
-        __syncthreads();
+        __syncthreads();  // every thread has read s_rows for this step
         float *Sn = blk(a.segS, g + 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            s_rows[8 * half + i][c] = acc[i];
-            Sn[(size_t)(r0 + 8 * half + i) * kD + c] = acc[i];
+        for (int i = 0; i < RH; ++i) {
+            s_rows[rr + i][c] = acc[i];
+            Sn[(size_t)(r0 + rr + i) * kD + c] = acc[i];
         }
-        __syncthreads();
     }
 }
 
@@ -1216,7 +1246,11 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
         sa.segP = a.segP;
         sa.G = a.G;
         sa.chains = chains;
-        hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(chains * 8)), dim3(256), 0, s, sa);
+        // about 256 workgroups: 4 rows each for few chains, 16 for more
+        if (chains * (kD / 4) <= 2 * kPlanCUs)
+            hipLaunchKernelGGL(seg_scan_kernel<4>, dim3((unsigned)(chains * (kD / 4))), dim3(256), 0, s, sa);
+        else
+            hipLaunchKernelGGL(seg_scan_kernel<16>, dim3((unsigned)(chains * (kD / 16))), dim3(256), 0, s, sa);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
