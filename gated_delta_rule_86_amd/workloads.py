@@ -16,6 +16,10 @@ deviation):
   varlen lengths ~ U[1, Lmax] (inclusive); a draw is kept only if some length is
   not a multiple of 16 and the total is within 10% of N * (1 + Lmax) / 2,
   otherwise the next seed attempt is used.
+Inputs that arrive already activated (a switch of the forward pass turned off):
+  gate switch off:   g = lower_bound * U[0, 1]      (a per-token natural-log decay)
+  l2norm switch off: q, k ~ N(0, 1/128)            (norms close to 1, not exactly 1)
+  sigmoid switch off: beta ~ U[0, 1]
 Seeds: numpy SeedSequence([config_id, attempt]).spawn(9) in the order
   [lengths, q, k, v, g, beta, A_log, dt_bias, initial_state]; each tensor is drawn
   in blocks of 2^24 values, block i from child i of that tensor's seed (PCG64).
@@ -68,6 +72,7 @@ class Workload:
     state_dtype: str  # dtype of both initial and final state ("none" -> no initial, fp32 final)
     final_dtype: str
     cu_seqlens: Optional[np.ndarray]  # int64 [N+1]
+    flags: int = 7  # activation switches of the forward pass (1 gate, 2 q/k l2norm, 4 beta sigmoid)
 
     @property
     def N(self) -> int:
@@ -88,15 +93,19 @@ class Workload:
              "K": D, "V": D, "lower_bound": self.lower_bound,
              "initial_state": self.state_dtype if self.initial_state is not None else "none",
              "final_state": self.final_dtype, "varlen": self.cu_seqlens is not None}
+        if self.flags != 7:
+            d["activation_flags"] = self.flags
         return d
 
 
 _BLOCK = 1 << 24
 
 
-def _fill_normal(seq: np.random.SeedSequence, n: int, std: float, to_bf16: bool) -> np.ndarray:
-    """n draws of N(0, std) in float32 (or bf16 bits), in fixed blocks of 2^24 with one
-    spawned child seed per block, so the values do not depend on the thread count."""
+def _fill_normal(seq: np.random.SeedSequence, n: int, std: float, to_bf16: bool,
+                 uniform=None) -> np.ndarray:
+    """n draws of N(0, std) (or of U[lo, hi] when uniform = (lo, hi)) in float32 (or bf16
+    bits), in fixed blocks of 2^24 with one spawned child seed per block, so the values do not
+    depend on the thread count."""
     out = np.empty(n, dtype=np.uint16 if to_bf16 else np.float32)
     nblk = max(1, -(-n // _BLOCK))
     kids = seq.spawn(nblk)
@@ -106,9 +115,13 @@ def _fill_normal(seq: np.random.SeedSequence, n: int, std: float, to_bf16: bool)
         m = min(_BLOCK, n - lo)
         if m <= 0:
             return
-        x = np.random.Generator(np.random.PCG64(kids[i])).standard_normal(m, dtype=np.float32)
-        if std != 1.0:
-            x *= np.float32(std)
+        gen = np.random.Generator(np.random.PCG64(kids[i]))
+        if uniform is not None:
+            x = gen.uniform(uniform[0], uniform[1], size=m).astype(np.float32)
+        else:
+            x = gen.standard_normal(m, dtype=np.float32)
+            if std != 1.0:
+                x *= np.float32(std)
         out[lo:lo + m] = f32_to_bf16_bits(x) if to_bf16 else x
 
     if nblk == 1:
@@ -122,6 +135,10 @@ def _fill_normal(seq: np.random.SeedSequence, n: int, std: float, to_bf16: bool)
 
 def _normal_bf16(seq, shape, std=1.0) -> np.ndarray:
     return _fill_normal(seq, int(np.prod(shape)), std, True).reshape(shape)
+
+
+def _uniform_bf16(seq, shape, lo, hi) -> np.ndarray:
+    return _fill_normal(seq, int(np.prod(shape)), 1.0, True, uniform=(lo, hi)).reshape(shape)
 
 
 def _lengths(config_id: int, N: int, Lmax: int):
@@ -138,8 +155,10 @@ def _lengths(config_id: int, N: int, Lmax: int):
 
 def make(name: str, B: int, T: int, H: int, *, lengths=None, lower_bound=-5.0,
          scale=None, state_dtype=STATE_FP32, with_initial=True, final_dtype=None,
-         seed=0, seeds=None) -> Workload:
-    """General generator.  ``lengths`` (list) switches to varlen with B = 1, T = sum(lengths)."""
+         seed=0, seeds=None, flags=7) -> Workload:
+    """General generator.  ``lengths`` (list) switches to varlen with B = 1, T = sum(lengths).
+    ``flags``: activation switches of the forward pass; an input whose switch is off is drawn
+    already activated (see the recipe above)."""
     if seeds is None:
         seeds = np.random.SeedSequence([seed, 0]).spawn(9)
     cu = None
@@ -149,11 +168,18 @@ def make(name: str, B: int, T: int, H: int, *, lengths=None, lower_bound=-5.0,
         cu[1:] = np.cumsum(lengths)
         B, T = 1, int(cu[-1])
     N = B if cu is None else lengths.size
-    q = _normal_bf16(seeds[1], (B, T, H, D))
-    k = _normal_bf16(seeds[2], (B, T, H, D))
+    qk_std = 1.0 if flags & 2 else 1.0 / math.sqrt(D)
+    q = _normal_bf16(seeds[1], (B, T, H, D), qk_std)
+    k = _normal_bf16(seeds[2], (B, T, H, D), qk_std)
     v = _normal_bf16(seeds[3], (B, T, H, D))
-    g = _normal_bf16(seeds[4], (B, T, H, D))
-    beta = _normal_bf16(seeds[5], (B, T, H))
+    if flags & 1:
+        g = _normal_bf16(seeds[4], (B, T, H, D))
+    else:
+        g = _uniform_bf16(seeds[4], (B, T, H, D), float(lower_bound), 0.0)
+    if flags & 4:
+        beta = _normal_bf16(seeds[5], (B, T, H))
+    else:
+        beta = _uniform_bf16(seeds[5], (B, T, H), 0.0, 1.0)
     A_log = np.log(np.random.Generator(np.random.PCG64(seeds[6])).uniform(1.0, 16.0, size=H)).astype(np.float32)
     dt_bias = _fill_normal(seeds[7], H * D, 0.1, False).reshape(H, D)
     h0 = None
@@ -164,7 +190,7 @@ def make(name: str, B: int, T: int, H: int, *, lengths=None, lower_bound=-5.0,
     if final_dtype is None:
         final_dtype = STATE_FP32 if state_dtype == STATE_NONE else state_dtype
     return Workload(name, B, T, H, q, k, v, g, beta, A_log, dt_bias, float(np.float32(lower_bound)),
-                    float(np.float32(scale)), h0, state_dtype, final_dtype, cu)
+                    float(np.float32(scale)), h0, state_dtype, final_dtype, cu, int(flags))
 
 
 CONFIG_NAMES = [

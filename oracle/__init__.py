@@ -25,6 +25,9 @@ _SRC = os.path.join(_HERE, "kda_ref.c")
 _LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
 
 STATE_NONE, STATE_BF16, STATE_FP32, STATE_FP64 = 0, 1, 2, 3
+# activation switches (bit mask): gate, q/k l2norm and beta sigmoid computed in the pass
+GATE_IN_KERNEL, QK_L2NORM_IN_KERNEL, BETA_SIGMOID_IN_KERNEL = 1, 2, 4
+ALL_IN_KERNEL = 7
 
 _lib = None
 
@@ -53,13 +56,15 @@ def lib():
         L.oracle_sigmoid.argtypes = [ctypes.c_double]
         L.oracle_gate.restype = ctypes.c_double
         L.oracle_gate.argtypes = [ctypes.c_double] * 4
+        L.oracle_gate_preactivated.restype = ctypes.c_double
+        L.oracle_gate_preactivated.argtypes = [ctypes.c_double] * 2
         L.oracle_l2norm.restype = None
         L.oracle_l2norm.argtypes = [dp, i64, ctypes.c_double, dp]
         L.oracle_core.restype = ctypes.c_int
         L.oracle_core.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp]
         L.oracle_kda_fwd.restype = ctypes.c_int
         L.oracle_kda_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
-                                     vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, vp, vp,
+                                     ctypes.c_int, vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, vp, vp,
                                      ctypes.c_int]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
@@ -82,6 +87,11 @@ def sigmoid(x: float) -> float:
 def gate(g: float, A_log: float, dt_bias: float, lower_bound: float) -> float:
     """Per-channel log-decay a (natural log) for one token and channel."""
     return lib().oracle_gate(float(g), float(A_log), float(dt_bias), float(lower_bound))
+
+
+def gate_preactivated(g: float, lower_bound: float) -> float:
+    """Log-decay taken from a pre-activated gate (gate switch off): g held to [lb, 0]."""
+    return lib().oracle_gate_preactivated(float(g), float(lower_bound))
 
 
 def l2norm(x, eps: float = 1e-6):
@@ -114,11 +124,13 @@ def core(alpha, beta, kn, qn, v, scale, S0):
 
 def kda_fwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=None,
             state_dtype=None, cu_seqlens=None, heads=None, want_out=True, want_final=True,
-            nthreads=0):
+            nthreads=0, flags=ALL_IN_KERNEL):
     """Oracle forward pass on host arrays.
 
     q, k, v, g: uint16 bf16 bit arrays [B, T, H, 128]; beta: uint16 [B, T, H];
-    A_log: float32 [H]; dt_bias: float32 [H, 128];
+    A_log: float32 [H]; dt_bias: float32 [H, 128] (None allowed with the gate switch off);
+    flags: activation switches (GATE_IN_KERNEL | QK_L2NORM_IN_KERNEL | BETA_SIGMOID_IN_KERNEL);
+      a switch that is off means that input arrives already activated (see kda_ref.c);
     initial_state: None, or [N, H, 128, 128] uint16 (bf16 bits) / float32 / float64;
     cu_seqlens: None or int64 [N+1] (then B must be 1).
     heads: None (all) or a list of head indices; outputs cover only those heads.
@@ -129,8 +141,10 @@ def kda_fwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=
     for a in (q, k, v, g):
         assert a.dtype == np.uint16 and a.shape == (B, T, H, D) and a.flags.c_contiguous
     assert beta.dtype == np.uint16 and beta.shape == (B, T, H) and beta.flags.c_contiguous
-    A_log = np.ascontiguousarray(A_log, dtype=np.float32)
-    dt_bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+    if A_log is not None:
+        A_log = np.ascontiguousarray(A_log, dtype=np.float32)
+    if dt_bias is not None:
+        dt_bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
     if cu_seqlens is not None:
         cu_seqlens = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
         N = cu_seqlens.size - 1
@@ -151,7 +165,8 @@ def kda_fwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=
     out = np.empty((B, T, n_sel, D), dtype=np.float64) if want_out else None
     fin = np.empty((N, n_sel, D, D), dtype=np.float64) if want_final else None
     rc = lib().oracle_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
-                              _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                              _ptr(A_log), _ptr(dt_bias), float(lower_bound), int(flags),
+                              _ptr(initial_state),
                               sd, _ptr(cu_seqlens), B, T, H, N, _ptr(hsel),
                               n_sel, _ptr(out), _ptr(fin), int(nthreads))
     if rc != 0:

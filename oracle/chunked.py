@@ -64,12 +64,21 @@ def forward_substitution_inverse(A):
     return T
 
 
-def _activate(q, k, g, beta, A_log_h, dt_bias_h, lower_bound):
-    qn = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + EPS)
-    kn = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + EPS)
-    x = np.exp(A_log_h) * (g + dt_bias_h[None, :])
-    a = lower_bound / (1.0 + np.exp(-x))
-    bt = 1.0 / (1.0 + np.exp(-beta))
+def _activate(q, k, g, beta, A_log_h, dt_bias_h, lower_bound, flags=7):
+    """Activated inputs of one chunk.  flags bit 1: gate from logits (else g is the log-decay,
+    held to [lower_bound, 0]); bit 2: l2-normalise q and k (else as given); bit 4: sigmoid of
+    the beta logits (else beta as given)."""
+    if flags & 2:
+        qn = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + EPS)
+        kn = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + EPS)
+    else:
+        qn, kn = q, k
+    if flags & 1:
+        x = np.exp(A_log_h) * (g + dt_bias_h[None, :])
+        a = lower_bound / (1.0 + np.exp(-x))
+    else:
+        a = np.clip(g, lower_bound, 0.0)
+    bt = 1.0 / (1.0 + np.exp(-beta)) if flags & 4 else beta
     return qn, kn, a, bt
 
 
@@ -98,17 +107,22 @@ def chunk_step(S, qn, kn, v, a, bt, scale, inverse="solve"):
 
 
 def kda_fwd_chunked(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=None,
-                    cu_seqlens=None, C=16, inverse="solve"):
+                    cu_seqlens=None, C=16, inverse="solve", flags=7):
     """Chunked forward pass on host arrays (small sizes only).
 
-    Same argument meaning as ``oracle.kda_fwd``; inputs are uint16 bf16 bits, states may be
+    Same argument meaning as ``oracle.kda_fwd`` (``flags``: the activation switches, bit 1
+    gate, bit 2 q/k l2norm, bit 4 beta sigmoid); inputs are uint16 bf16 bits, states may be
     uint16 (bf16 bits), float32 or float64.  Returns (out [B, T, H, 128], final [N, H, 128, 128]).
     """
     B, T, H, D = q.shape
     qf, kf, vf, gf = (bf16_bits_to_f64(x) for x in (q, k, v, g))
     bf = bf16_bits_to_f64(beta)
-    A_log = np.asarray(A_log, dtype=np.float32).astype(np.float64)
-    dt_bias = np.asarray(dt_bias, dtype=np.float32).astype(np.float64)
+    if flags & 1:
+        A_log = np.asarray(A_log, dtype=np.float32).astype(np.float64)
+        dt_bias = np.asarray(dt_bias, dtype=np.float32).astype(np.float64)
+    else:
+        A_log = np.zeros(H)
+        dt_bias = np.zeros((H, D))
     if cu_seqlens is not None:
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         seqs = [(0, int(cu[i]), int(cu[i + 1])) for i in range(cu.size - 1)]
@@ -129,7 +143,8 @@ def kda_fwd_chunked(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initia
             for c0 in range(t0, t1, C):
                 c1 = min(c0 + C, t1)
                 qn, kn, a, bt = _activate(qf[b, c0:c1, h], kf[b, c0:c1, h], gf[b, c0:c1, h],
-                                          bf[b, c0:c1, h], A_log[h], dt_bias[h], lower_bound)
+                                          bf[b, c0:c1, h], A_log[h], dt_bias[h], lower_bound,
+                                          flags)
                 O, S = chunk_step(S, qn, kn, vf[b, c0:c1, h], a, bt, scale, inverse)
                 out[b, c0:c1, h] = O
             fin[n, h] = S

@@ -29,6 +29,15 @@
  *     7. out_t[v] = scale * sum_c S[v][c] q^_c                 (inclusive: sees token t)
  *   Equivalently S_t = S_{t-1} Diag(alpha_t) (I - beta_t k^ k^T) + beta_t v_t k^T.
  *
+ *   Activation switches (the three use_*_in_kernel flags of the "Using FlashKDA as an
+ *   FLA backend" section; the pages only name them).  With a switch off the library
+ *   takes that input as already activated:
+ *     gate off:   a_c = min(max(g_c, lb), 0)   (g holds the natural-log decay itself; A_log
+ *                 and dt_bias are unused; it is held to the same range (lb, 0] the in-kernel
+ *                 gate produces, the reading of safe_gate together with lower_bound)
+ *     l2norm off: q^ = q, k^ = k as given
+ *     sigmoid off: beta = beta as given
+ *
  *   Inputs arrive as bf16 bit patterns (uint16) or fp32 and are widened exactly
  *   to double; every intermediate is double; nothing is rounded on the way out.
  *
@@ -36,8 +45,10 @@
  * dense 128x128 transition products, chunk-size independence of an independent
  * chunked form, beta = 0 pure-decay closed form, q = k / beta = 1 retrieval,
  * orthonormal-key overwrite, varlen = separate runs, split-and-resume, linearity,
- * gate and l2norm special values.  The gate formula, eps and the decay/update
- * order are readings the pages do not pin ("parity unpinned" for those choices).
+ * gate and l2norm special values, and for the switches an exact-rational run with
+ * every switch off and a pure-decay closed form of the pre-activated gate.  The gate
+ * formula, eps, the decay/update order and the meaning of a switch that is off are
+ * readings the pages do not pin ("parity unpinned" for those choices).
  */
 #include <math.h>
 #include <stdint.h>
@@ -49,6 +60,11 @@
 
 #define ORACLE_DIM 128
 #define ORACLE_EPS 1e-6
+
+/* activation switches: bit values of the forward pass's switch mask */
+#define ORACLE_GATE_IN_KERNEL 1
+#define ORACLE_QK_L2NORM_IN_KERNEL 2
+#define ORACLE_BETA_SIGMOID_IN_KERNEL 4
 
 enum { ORACLE_STATE_NONE = 0, ORACLE_STATE_BF16 = 1, ORACLE_STATE_FP32 = 2, ORACLE_STATE_FP64 = 3 };
 
@@ -70,6 +86,13 @@ double oracle_sigmoid(double x)
 double oracle_gate(double g, double A_log, double dt_bias, double lower_bound)
 {
     return lower_bound * oracle_sigmoid(exp(A_log) * (g + dt_bias));
+}
+
+/* Pre-activated gate (gate switch off): the given log-decay held to [lb, 0]. */
+double oracle_gate_preactivated(double g, double lower_bound)
+{
+    double a = g < lower_bound ? lower_bound : g;
+    return a > 0.0 ? 0.0 : a;
 }
 
 /* y = x / sqrt(sum x^2 + eps) */
@@ -128,7 +151,8 @@ int oracle_core(int64_t T, int64_t K, int64_t V, const double *alpha, const doub
 /*
  * Full forward pass, same argument meaning as the library's kda_fwd, host memory.
  *   q, k, g: bf16 bits [B*T][H][128]; v: bf16 bits [B*T][H][128]; beta: bf16 bits [B*T][H]
- *   A_log: fp32 [H]; dt_bias: fp32 [H][128]
+ *   A_log: fp32 [H]; dt_bias: fp32 [H][128] (both may be NULL when the gate switch is off)
+ *   flags: activation switches (ORACLE_*_IN_KERNEL bits; 7 = all activations in the pass)
  *   initial_state: NULL or [N][H][128][128] of state_dtype (bf16 bits, fp32 or fp64)
  *   cu_seqlens: NULL (then N = B, sequence b is batch row b) or int64 [N+1] with B == 1
  *   heads / n_heads: the subset of heads to compute (NULL = all, in order).  Outputs are
@@ -140,7 +164,7 @@ int oracle_core(int64_t T, int64_t K, int64_t V, const double *alpha, const doub
  */
 int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                    const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
-                   double lower_bound, const void *initial_state, int state_dtype,
+                   double lower_bound, int flags, const void *initial_state, int state_dtype,
                    const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
                    const int32_t *heads, int64_t n_heads, double *out, double *final_state,
                    int nthreads)
@@ -159,6 +183,10 @@ int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
     } else {
         N = B;
     }
+    if ((flags & ~7) != 0)
+        return 5;
+    if ((flags & ORACLE_GATE_IN_KERNEL) && (!A_log || !dt_bias))
+        return 6;
     const int64_t n_sel = heads ? n_heads : H;
     if (n_sel < 1)
         return 4;
@@ -199,24 +227,33 @@ int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
             S[e] = s;
         }
 
-        const double Alog = (double)A_log[h];
+        const double Alog = (flags & ORACLE_GATE_IN_KERNEL) ? (double)A_log[h] : 0.0;
         for (int64_t t = t0; t < t1; ++t) {
             const int64_t row = (t * H + h) * D;
-            /* step 1: l2-normalised query and key */
+            /* step 1: l2-normalised query and key (or as given) */
             for (int64_t c = 0; c < D; ++c)
                 tmp[c] = bf16_bits_to_double(q[row + c]);
-            oracle_l2norm(tmp, D, ORACLE_EPS, qn);
+            if (flags & ORACLE_QK_L2NORM_IN_KERNEL)
+                oracle_l2norm(tmp, D, ORACLE_EPS, qn);
+            else
+                memcpy(qn, tmp, sizeof(double) * D);
             for (int64_t c = 0; c < D; ++c)
                 tmp[c] = bf16_bits_to_double(k[row + c]);
-            oracle_l2norm(tmp, D, ORACLE_EPS, kn);
+            if (flags & ORACLE_QK_L2NORM_IN_KERNEL)
+                oracle_l2norm(tmp, D, ORACLE_EPS, kn);
+            else
+                memcpy(kn, tmp, sizeof(double) * D);
             /* step 2: gate -> per-channel decay */
             for (int64_t c = 0; c < D; ++c) {
-                double a = oracle_gate(bf16_bits_to_double(g[row + c]), Alog,
-                                       (double)dt_bias[h * D + c], lower_bound);
+                const double gc = bf16_bits_to_double(g[row + c]);
+                double a = (flags & ORACLE_GATE_IN_KERNEL)
+                               ? oracle_gate(gc, Alog, (double)dt_bias[h * D + c], lower_bound)
+                               : oracle_gate_preactivated(gc, lower_bound);
                 alpha[c] = exp(a);
             }
             /* step 3: write strength */
-            double bt = oracle_sigmoid(bf16_bits_to_double(beta[t * H + h]));
+            const double braw = bf16_bits_to_double(beta[t * H + h]);
+            double bt = (flags & ORACLE_BETA_SIGMOID_IN_KERNEL) ? oracle_sigmoid(braw) : braw;
             for (int64_t c = 0; c < D; ++c)
                 vt[c] = bf16_bits_to_double(v[row + c]);
             /* steps 4-7 */

@@ -38,10 +38,18 @@ MUTANTS = {
     "decay_after_update": [(DECAY, ""), (READ, DECAY + READ)],
     "state_load_transposed": [("s = (double)((const float *)initial_state)[sbase + e];",
                                "s = (double)((const float *)initial_state)[sbase + (e % D) * D + e / D];")],
-    "beta_sigmoid_sign": [("oracle_sigmoid(bf16_bits_to_double(beta[t * H + h]))",
-                           "oracle_sigmoid(-bf16_bits_to_double(beta[t * H + h]))")],
+    "beta_sigmoid_sign": [("? oracle_sigmoid(braw) : braw", "? oracle_sigmoid(-braw) : braw")],
     "dt_bias_head_ignored": [("(double)dt_bias[h * D + c]", "(double)dt_bias[c]")],
     "gate_exp_of_A_log_dropped": [("oracle_sigmoid(exp(A_log) * (g + dt_bias));", "oracle_sigmoid(A_log * (g + dt_bias));")],
+    "preactivated_gate_not_held_to_range": [("    return a > 0.0 ? 0.0 : a;", "    return g;")],
+    "gate_switch_ignored": [("double a = (flags & ORACLE_GATE_IN_KERNEL)", "double a = 1")],
+    "l2norm_switch_ignored": [("            if (flags & ORACLE_QK_L2NORM_IN_KERNEL)\n"
+                               "                oracle_l2norm(tmp, D, ORACLE_EPS, kn);\n"
+                               "            else\n"
+                               "                memcpy(kn, tmp, sizeof(double) * D);",
+                               "            oracle_l2norm(tmp, D, ORACLE_EPS, kn);")],
+    "beta_switch_ignored": [("(flags & ORACLE_BETA_SIGMOID_IN_KERNEL) ? oracle_sigmoid(braw) : braw",
+                             "oracle_sigmoid(braw)")],
 }
 
 
@@ -106,7 +114,18 @@ def pin_l2norm():
     return abs(np.linalg.norm(oracle.l2norm(x)) - np.sqrt(x @ x / (x @ x + 1e-6))) <= 1e-15
 
 
-PINS = [pin_exact_core, pin_chunk_independence, pin_gate_values, pin_wiring, pin_l2norm]
+def pin_switches():
+    from test_oracle_flags import (test_all_switches_off_matches_exact_rational,
+                                   test_preactivated_gate_pure_decay_closed_form)
+    try:
+        test_all_switches_off_matches_exact_rational(1)
+        test_preactivated_gate_pure_decay_closed_form(0)
+    except AssertionError:
+        return False
+    return True
+
+
+PINS = [pin_exact_core, pin_chunk_independence, pin_gate_values, pin_wiring, pin_l2norm, pin_switches]
 
 
 def test_pins_pass_on_the_real_oracle():
