@@ -32,11 +32,15 @@ kda_status validate(const void *q, const void *k, const void *v, const void *g, 
                     float lower_bound, const void *h0, kda_state_dtype h0_dt, void *ht,
                     kda_state_dtype ht_dt, const int64_t *cu, const int64_t *cu_host, int64_t B,
                     int64_t T, int64_t H, int64_t N, int64_t K, int64_t V, void *ws,
-                    size_t ws_bytes, kda::Layout *lay)
+                    size_t ws_bytes, uint32_t flags, kda::Layout *lay)
 {
+    if ((flags & ~KDA_ALL_IN_KERNEL) != 0)
+        return KDA_ERR_FLAGS;
+    // A_log and dt_bias feed only the in-pass gate
+    const bool gate_in = (flags & KDA_GATE_IN_KERNEL) != 0;
     // token tensors may be NULL only when they hold no elements (B * T == 0)
     const bool no_tokens = (T == 0);
-    if ((!no_tokens && (!q || !k || !v || !g || !beta || !out)) || !A_log || !dt_bias)
+    if ((!no_tokens && (!q || !k || !v || !g || !beta || !out)) || (gate_in && (!A_log || !dt_bias)))
         return KDA_ERR_NULL;
     if (B < 1 || T < 0 || H < 1)
         return KDA_ERR_SHAPE;
@@ -67,7 +71,7 @@ kda_status validate(const void *q, const void *k, const void *v, const void *g, 
     if (!isfinite(scale))
         return KDA_ERR_SCALE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
-        !aligned(out, 16) || !aligned(beta, 2) || !aligned(A_log, 4) || !aligned(dt_bias, 16) ||
+        !aligned(out, 16) || !aligned(beta, 2) || (gate_in && (!aligned(A_log, 4) || !aligned(dt_bias, 16))) ||
         (h0 && !aligned(h0, 16)) || (ht && !aligned(ht, 16)) || (cu && !aligned(cu, 8)) ||
         (ws && !aligned(ws, kda::kAlign)))
         return KDA_ERR_ALIGN;
@@ -131,6 +135,7 @@ const char *kda_status_string(int s)
     case KDA_ERR_CU_SEQLENS: return "KDA_ERR_CU_SEQLENS: cu_seqlens content invalid";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP launch or query failed";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_FLAGS: return "KDA_ERR_FLAGS: unknown activation switch bits";
     default: return "KDA_ERR_UNKNOWN";
     }
 }
@@ -153,13 +158,13 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
                     void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
                     const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
                     int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
-                    void *const *events)
+                    uint32_t flags, void *const *events)
 {
     kda::Layout lay;
     kda_status st = validate(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                              initial_state, initial_state_dtype, final_state, final_state_dtype,
                              cu_seqlens, cu_seqlens_host, B, T, H, N, K, V, workspace,
-                             workspace_bytes, &lay);
+                             workspace_bytes, flags, &lay);
     if (st != KDA_OK)
         return st;
     kda::FwdArgs a;
@@ -173,6 +178,7 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
     a.dt_bias = dt_bias;
     a.scale = scale;
     a.lower_bound = lower_bound;
+    a.flags = (int)flags;
     a.h0 = initial_state;
     a.ht = final_state;
     a.h0_dtype = (int)initial_state_dtype;
@@ -212,7 +218,20 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g, c
 {
     return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                     initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
-                    B, T, H, N, K, V, workspace, workspace_bytes, stream, nullptr);
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, KDA_ALL_IN_KERNEL, nullptr);
+}
+
+kda_status kda_fwd_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                      float scale, void *out, const float *A_log, const float *dt_bias,
+                      float lower_bound, const void *initial_state, kda_state_dtype initial_state_dtype,
+                      void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                      const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                      int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                      uint32_t flags)
+{
+    return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, flags, nullptr);
 }
 
 kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -231,7 +250,8 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
             return KDA_ERR_NULL;
     return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                     initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
-                    B, T, H, N, K, V, workspace, workspace_bytes, stream, stage_events);
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, KDA_ALL_IN_KERNEL,
+                    stage_events);
 }
 
 kda_status kda_fwd_device_status(const void *workspace, int32_t *status_out, void *stream)

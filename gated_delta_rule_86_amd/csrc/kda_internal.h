@@ -98,6 +98,7 @@ struct FwdArgs {
     uint16_t *out;
     const float *A_log, *dt_bias;
     float scale, lower_bound;
+    int flags;               // activation switches (KDA_*_IN_KERNEL bits of include/kda.h)
     const void *h0;
     void *ht;
     int h0_dtype, ht_dtype;  // 0 none, 1 bf16, 2 fp32

@@ -300,12 +300,14 @@ constexpr int kFusedLds = kOffFlags + 128;
 static_assert(kFusedLds <= 160 * 1024, "LDS budget");
 static_assert(kBlkBytes % 16 == 0, "slot alignment");
 constexpr int32_t kStatusSpin = 0x100;
+constexpr int kGateIn = 1, kL2In = 2, kSigIn = 4;
 constexpr int kSpinMax = 1 << 22;
 
 struct FusedArgs {
     const uint16_t *q, *k, *v, *g, *beta;
     const float *A_log, *dt_bias;
     float scale, lower_bound;
+    int flags;  // activation switches: kGateIn | kL2In | kSigIn (others: input already activated)
     uint16_t *out;
     const void *h0;
     void *ht;
@@ -500,6 +502,9 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
     }
 }
 
+// kSw: the activation switches are read from a.flags; without it every activation runs in
+// the pass (the common case gets code with no switch logic in it).
+template <bool kSw>
 __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int p, int lane)
 {
     const int64_t H = a.H;
@@ -542,7 +547,10 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
                                                  (uint32_t)lane * (uint32_t)(H * 2), 0, 0, 0);
     };
 
-    const float m1 = -kLog2e * fexp2(a.A_log[h] * kLog2e);
+    const bool gate_in = !kSw || (a.flags & kGateIn) != 0;
+    const bool l2_in = !kSw || (a.flags & kL2In) != 0;
+    const bool sig_in = !kSw || (a.flags & kSigIn) != 0;
+    const float m1 = gate_in ? -kLog2e * fexp2(a.A_log[h] * kLog2e) : 0.f;
     const float lb2 = a.lower_bound * kLog2e;
 
     bool spun_out = false;
@@ -592,27 +600,42 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
         if (nxt.valid)
             issue_stage(nxt.r, nxt.r.c0 + (it + 4 - nxt.base));
 
-        const float bt = valid ? sigmoidf_fast(bf16f((uint16_t)(braw & 0xffffu))) : 0.f;
+        const float braw_f = bf16f((uint16_t)(braw & 0xffffu));
+        const float bt = valid ? (sig_in ? sigmoidf_fast(braw_f) : braw_f) : 0.f;
 
         ssq += __shfl_xor(ssq, 16);
         ssq += __shfl_xor(ssq, 32);
         ssk += __shfl_xor(ssk, 16);
         ssk += __shfl_xor(ssk, 32);
-        const float rq = __builtin_amdgcn_rsqf(ssq + 1e-6f) * a.scale;
-        const float rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
+        const float rq = l2_in ? __builtin_amdgcn_rsqf(ssq + 1e-6f) * a.scale : a.scale;
+        const float rk = l2_in ? __builtin_amdgcn_rsqf(ssk + 1e-6f) : 1.f;
 
         // log2-domain log-decay lb*log2e*sigmoid(x), x = exp(A_log)*(g + dt_bias):
         // sigmoid(x) = 1 / (1 + 2^(g*m1 + d1)), m1 = -log2e*exp(A_log), d1 = m1*dt_bias.
-        // Tokens past the chunk's end get a zero log-decay.
+        // A pre-activated gate is the natural-log decay itself, held to [lb, 0].  Tokens
+        // past the chunk's end get a zero log-decay.
         const float lbv = valid ? lb2 : 0.f;
         float b2[32];
+        if (gate_in) {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(dtc + 32 * qb + 4 * w);
+            for (int w = 0; w < 8; ++w) {
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(dtc + 32 * qb + 4 * w);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = 4 * w + e;
-                float av = lbv * frcp(1.0f + fexp2(fmaf(gf[c], m1, d4[e])));
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 4 * w + e;
+                    float av = lbv * frcp(1.0f + fexp2(fmaf(gf[c], m1, d4[e])));
+                    av += dpp_row_shr(av, 1);
+                    av += dpp_row_shr(av, 2);
+                    av += dpp_row_shr(av, 4);
+                    av += dpp_row_shr(av, 8);
+                    b2[c] = av;
+                }
+            }
+        } else {
+            const float gk = valid ? kLog2e : 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                float av = gk * fminf(fmaxf(gf[c], a.lower_bound), 0.f);
                 av += dpp_row_shr(av, 1);
                 av += dpp_row_shr(av, 2);
                 av += dpp_row_shr(av, 4);
@@ -1018,6 +1041,7 @@ __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned cha
     }
 }
 
+template <bool kSw>
 __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -1059,13 +1083,13 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         int *fl = reinterpret_cast<int *>(lds + kOffFlags);
         fl[threadIdx.x] = threadIdx.x < kNS ? -1 : 0;
     }
-    if (threadIdx.x < kD) {
+    if (threadIdx.x < kD && (!kSw || (a.flags & kGateIn))) {
         const float m1 = -kLog2e * fexp2(a.A_log[w.h] * kLog2e);
         reinterpret_cast<float *>(lds + kOffDt)[threadIdx.x] = m1 * a.dt_bias[(int64_t)w.h * kD + threadIdx.x];
     }
     __syncthreads();
     if (wave < 4) {
-        fused_producer(a, w, lds, wave, lane);
+        fused_producer<kSw>(a, w, lds, wave, lane);
     } else {
         // The consumers set the pace (producers finish ahead and wait for free slots), so
         // they get issue priority over the producer sharing their SIMD.
@@ -1199,6 +1223,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.dt_bias = f.dt_bias;
     a.scale = f.scale;
     a.lower_bound = f.lower_bound;
+    a.flags = f.flags;
     a.out = f.out;
     a.h0 = f.h0;
     a.ht = f.ht;
@@ -1215,7 +1240,9 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.segS = reinterpret_cast<float *>(f.ws + f.lay.off_seg);
     a.segF = a.segS + seg_floats;
     a.segP = a.segF + seg_floats;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel),
+    // a separate instantiation reads the activation switches when any is off
+    void (*fused)(FusedArgs) = f.flags == (kGateIn | kL2In | kSigIn) ? fused_kernel<false> : fused_kernel<true>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fused),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
     if (e != hipSuccess)
         return e;
@@ -1228,7 +1255,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
             per_head = 1;
         if (per_head > f.lay.n_seq)
             per_head = f.lay.n_seq;
-        hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(f.H * per_head)), dim3(512), kFusedLds, s, a);
+        hipLaunchKernelGGL(fused, dim3((unsigned)(f.H * per_head)), dim3(512), kFusedLds, s, a);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
         if ((e = mark(0)) != hipSuccess || (e = mark(1)) != hipSuccess)
@@ -1236,7 +1263,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
         return mark(2);
     }
     a.pass = 1;
-    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(chains * (2 * a.G - 3))), dim3(512), kFusedLds, s, a);
+    hipLaunchKernelGGL(fused, dim3((unsigned)(chains * (2 * a.G - 3))), dim3(512), kFusedLds, s, a);
     if ((e = hipGetLastError()) != hipSuccess || (e = mark(0)) != hipSuccess)
         return e;
     if (a.G > 2) {
@@ -1257,7 +1284,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     if ((e = mark(1)) != hipSuccess)
         return e;
     a.pass = 2;
-    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
+    hipLaunchKernelGGL(fused, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return mark(2);

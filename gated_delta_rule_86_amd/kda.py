@@ -8,6 +8,10 @@ missing or cannot be loaded, every call raises; there is no fallback path.
 
     fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
         initial_state=None, final_state=None, cu_seqlens=None)
+
+plus the keyword switches use_gate_in_kernel, use_qk_l2norm_in_kernel and
+use_beta_sigmoid_in_kernel (README, "Using FlashKDA as an FLA backend"); turning one
+off means that input arrives already activated (kda_fwd_ex in include/kda.h).
 """
 from __future__ import annotations
 
@@ -22,12 +26,15 @@ KDA_OK = 0
 STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_HEAD_DIM", 4: "KDA_ERR_DTYPE",
     5: "KDA_ERR_LOWER_BOUND", 6: "KDA_ERR_SCALE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_WORKSPACE",
-    9: "KDA_ERR_CU_SEQLENS", 10: "KDA_ERR_HIP", 11: "KDA_ERR_ALIAS",
+    9: "KDA_ERR_CU_SEQLENS", 10: "KDA_ERR_HIP", 11: "KDA_ERR_ALIAS", 12: "KDA_ERR_FLAGS",
 }
+# activation switches of kda_fwd_ex (include/kda.h)
+GATE_IN_KERNEL, QK_L2NORM_IN_KERNEL, BETA_SIGMOID_IN_KERNEL = 1, 2, 4
+ALL_IN_KERNEL = 7
 STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_timed", "kda_fwd_workspace_size", "kda_status_string",
+EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_timed", "kda_fwd_workspace_size", "kda_status_string",
            "kda_fwd_device_status", "kda_chunk_table", "kda_version")
 
 
@@ -53,6 +60,8 @@ def lib():
     L.kda_fwd.restype = ctypes.c_int
     L.kda_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, ctypes.c_int, vp,
                           ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    L.kda_fwd_ex.restype = ctypes.c_int
+    L.kda_fwd_ex.argtypes = L.kda_fwd.argtypes + [ctypes.c_uint32]
     L.kda_fwd_timed.restype = ctypes.c_int
     L.kda_fwd_timed.argtypes = L.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     L.kda_fwd_workspace_size.restype = ctypes.c_size_t
@@ -109,7 +118,8 @@ def _state_code(t) -> int:
 
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
         final_state=None, cu_seqlens=None, *, cu_seqlens_host=None, workspace=None, stream=None,
-        stage_events=None):
+        stage_events=None, use_gate_in_kernel=True, use_qk_l2norm_in_kernel=True,
+        use_beta_sigmoid_in_kernel=True):
     """KDA forward pass on torch device tensors; writes ``out`` and ``final_state`` in place.
 
     q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; out: bf16 [B, T, H, 128];
@@ -119,6 +129,9 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     workspace: optional uint8 device tensor of at least workspace_size(...) bytes.
     stage_events: optional sequence of 5 raw hipEvent_t handles (ints); when given the call
     goes through kda_fwd_timed, which records them around each launch (see include/kda.h).
+    use_*_in_kernel: activation switches.  With use_gate_in_kernel=False, g is the natural-log
+    decay itself and A_log / dt_bias may be None; with use_qk_l2norm_in_kernel=False q and k
+    are used as given; with use_beta_sigmoid_in_kernel=False beta is the write strength.
     """
     import torch
     L = lib()
@@ -134,10 +147,16 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             raise ValueError(f"{name} must be a contiguous bf16 [B, T, H, V] tensor")
     if beta.dtype != torch.bfloat16 or tuple(beta.shape) != (B, T, H) or not beta.is_contiguous():
         raise ValueError("beta must be a contiguous bf16 [B, T, H] tensor")
-    if A_log.dtype != torch.float32 or A_log.numel() != H or not A_log.is_contiguous():
-        raise ValueError("A_log must be a contiguous fp32 [H] tensor")
-    if dt_bias.dtype != torch.float32 or tuple(dt_bias.shape) != (H, K) or not dt_bias.is_contiguous():
-        raise ValueError("dt_bias must be a contiguous fp32 [H, K] tensor")
+    flags = ((GATE_IN_KERNEL if use_gate_in_kernel else 0) |
+             (QK_L2NORM_IN_KERNEL if use_qk_l2norm_in_kernel else 0) |
+             (BETA_SIGMOID_IN_KERNEL if use_beta_sigmoid_in_kernel else 0))
+    if use_gate_in_kernel or A_log is not None:
+        if A_log is None or A_log.dtype != torch.float32 or A_log.numel() != H or not A_log.is_contiguous():
+            raise ValueError("A_log must be a contiguous fp32 [H] tensor")
+    if use_gate_in_kernel or dt_bias is not None:
+        if (dt_bias is None or dt_bias.dtype != torch.float32 or tuple(dt_bias.shape) != (H, K)
+                or not dt_bias.is_contiguous()):
+            raise ValueError("dt_bias must be a contiguous fp32 [H, K] tensor")
     if initial_state is not None and final_state is not None and initial_state.dtype != final_state.dtype:
         raise ValueError("initial_state and final_state dtypes must match")
     N = B
@@ -162,8 +181,10 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             B, T, H, N if cu_seqlens is not None else B, K, V, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(stream, q.device))
     if stage_events is None:
-        st = L.kda_fwd(*args)
+        st = L.kda_fwd(*args) if flags == ALL_IN_KERNEL else L.kda_fwd_ex(*args, flags)
     else:
+        if flags != ALL_IN_KERNEL:
+            raise ValueError("stage_events (kda_fwd_timed) runs with every activation in the pass")
         evs = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(int(e)) for e in stage_events])
         st = L.kda_fwd_timed(*args, evs)
     if st != KDA_OK:

@@ -43,7 +43,7 @@ extern "C" {
 
 typedef enum kda_status {
     KDA_OK = 0,
-    KDA_ERR_NULL = 1,        /* A_log or dt_bias is NULL, or a token tensor is NULL while T > 0 */
+    KDA_ERR_NULL = 1,        /* A_log or dt_bias is NULL (in-pass gate), or a token tensor is NULL while T > 0 */
     KDA_ERR_SHAPE = 2,       /* B < 1, T < 0, H < 1, N inconsistent, or cu_seqlens with B != 1 */
     KDA_ERR_HEAD_DIM = 3,    /* K or V is not 128 */
     KDA_ERR_DTYPE = 4,       /* state dtype unknown, or initial/final state dtypes differ */
@@ -53,7 +53,8 @@ typedef enum kda_status {
     KDA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than kda_fwd_workspace_size */
     KDA_ERR_CU_SEQLENS = 9,  /* cu_seqlens_host given and cu[0] != 0, decreasing, or cu[N] != T */
     KDA_ERR_HIP = 10,        /* a HIP launch or query failed */
-    KDA_ERR_ALIAS = 11       /* out overlaps an input, or final_state overlaps a non-state input */
+    KDA_ERR_ALIAS = 11,      /* out overlaps an input, or final_state overlaps a non-state input */
+    KDA_ERR_FLAGS = 12       /* kda_fwd_ex: unknown bits in the activation switch mask */
 } kda_status;
 
 typedef enum kda_state_dtype {
@@ -103,6 +104,38 @@ kda_status kda_fwd(const void *q, const void *k, const void *v, const void *g, c
                    void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
                    const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
                    int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Activation switches for kda_fwd_ex, after the use_gate_in_kernel, use_qk_l2norm_in_kernel
+ * and use_beta_sigmoid_in_kernel flags the README section "Using FlashKDA as an FLA backend"
+ * passes to chunk_kda (the pages name them and set all three; kda_fwd is the all-set case).
+ * A switch that is off means that input arrives already activated:
+ *   KDA_GATE_IN_KERNEL off:   g holds the per-token, per-channel natural-log decay a itself
+ *                             (bf16 [B, T, H, 128]); the pass uses min(max(a, lower_bound), 0),
+ *                             the range the in-pass gate produces.  A_log and dt_bias are
+ *                             not read and may be NULL.
+ *   KDA_QK_L2NORM_IN_KERNEL off: q and k are used as given (no l2 normalisation).
+ *   KDA_BETA_SIGMOID_IN_KERNEL off: beta is the write strength itself (no sigmoid).
+ */
+#define KDA_GATE_IN_KERNEL 1u
+#define KDA_QK_L2NORM_IN_KERNEL 2u
+#define KDA_BETA_SIGMOID_IN_KERNEL 4u
+#define KDA_ALL_IN_KERNEL 7u
+
+/*
+ * kda_fwd_ex -- kda_fwd with the activation switch mask `flags` (KDA_*_IN_KERNEL bits).
+ * Same arguments, layouts, ownership and errors as kda_fwd, plus KDA_ERR_FLAGS for bits
+ * outside KDA_ALL_IN_KERNEL.  With KDA_GATE_IN_KERNEL clear, A_log and dt_bias may be NULL
+ * (they are then not checked for alignment either); lower_bound is still checked and
+ * bounds the pre-activated log-decay.  kda_fwd(...) is kda_fwd_ex(..., KDA_ALL_IN_KERNEL).
+ */
+kda_status kda_fwd_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                      float scale, void *out, const float *A_log, const float *dt_bias,
+                      float lower_bound, const void *initial_state, kda_state_dtype initial_state_dtype,
+                      void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                      const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                      int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                      uint32_t flags);
 
 /*
  * kda_fwd_timed -- kda_fwd with stage timing, for measurement.  Same arguments and behaviour

@@ -34,8 +34,9 @@ def state_tensor(a):
 def to_device(w):
     import torch
     d = {k: bf16_tensor(getattr(w, k)) for k in ("q", "k", "v", "g", "beta")}
-    d["A_log"] = torch.from_numpy(w.A_log).to(torch_dev())
-    d["dt_bias"] = torch.from_numpy(w.dt_bias).to(torch_dev())
+    gate_in = bool(w.flags & 1)  # A_log / dt_bias feed only the in-pass gate
+    d["A_log"] = torch.from_numpy(w.A_log).to(torch_dev()) if gate_in else None
+    d["dt_bias"] = torch.from_numpy(w.dt_bias).to(torch_dev()) if gate_in else None
     d["h0"] = state_tensor(w.initial_state)
     d["cu"] = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens).to(torch_dev())
     return d
@@ -64,7 +65,9 @@ def run_gpu(w, d=None, out_fill=None, final_fill=None, workspace=None, h0=None, 
     fin = final if final is not None else final_tensor(w, final_fill)
     h0t = d["h0"] if h0 is None else h0
     ws = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, out, d["A_log"], d["dt_bias"],
-                 w.lower_bound, h0t, fin, d["cu"], workspace=workspace)
+                 w.lower_bound, h0t, fin, d["cu"], workspace=workspace,
+                 use_gate_in_kernel=bool(w.flags & 1), use_qk_l2norm_in_kernel=bool(w.flags & 2),
+                 use_beta_sigmoid_in_kernel=bool(w.flags & 4))
     torch.cuda.synchronize()
     if keep_device:
         return out, fin, ws
@@ -75,8 +78,10 @@ def run_gpu(w, d=None, out_fill=None, final_fill=None, workspace=None, h0=None, 
 
 def run_oracle(w, heads=None, initial_state="default", nthreads=0):
     h0 = w.initial_state if isinstance(initial_state, str) else initial_state
-    return oracle.kda_fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound, h0,
-                          cu_seqlens=w.cu_seqlens, heads=heads, nthreads=nthreads)
+    gate_in = bool(w.flags & 1)
+    return oracle.kda_fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log if gate_in else None,
+                          w.dt_bias if gate_in else None, w.lower_bound, h0, cu_seqlens=w.cu_seqlens,
+                          heads=heads, nthreads=nthreads, flags=w.flags)
 
 
 def rel_l2(x, ref):

@@ -90,14 +90,18 @@ class Args:
         self.scale, self.lb = 0.125, -5.0
         self.ws = base + 11 * step
         self.ws_bytes = ws_size(B, T, H, self.N if varlen else B, varlen)
+        self.flags = None  # None: kda_fwd; else kda_fwd_ex with this switch mask
         assert tok < step
 
     def call(self):
         L = kda.lib()
         cu_host = None if self.cu_host is None else self.cu_host.ctypes.data
-        return L.kda_fwd(self.q, self.k, self.v, self.g, self.beta, self.scale, self.out, self.A_log,
-                         self.dt_bias, self.lb, self.h0, self.h0_dt, self.ht, self.ht_dt, self.cu, cu_host,
-                         self.B, self.T, self.H, self.N, self.K, self.V, self.ws, self.ws_bytes, None)
+        args = (self.q, self.k, self.v, self.g, self.beta, self.scale, self.out, self.A_log,
+                self.dt_bias, self.lb, self.h0, self.h0_dt, self.ht, self.ht_dt, self.cu, cu_host,
+                self.B, self.T, self.H, self.N, self.K, self.V, self.ws, self.ws_bytes, None)
+        if self.flags is None:
+            return L.kda_fwd(*args)
+        return L.kda_fwd_ex(*args, self.flags)
 
 
 def expect(code, **changes):
@@ -183,3 +187,21 @@ def test_chunk_table_argument_errors():
     assert L.kda_chunk_table(None, 1, 16, 1, 0, ctypes.c_void_p((1 << 32) + 64), 1 << 20, None, None,
                              None, None) == 7
     assert L.kda_fwd_device_status(None, None, None) == 1
+
+
+def test_activation_switch_errors():
+    expect(12, flags=8)
+    expect(12, flags=0xFFFFFFFF)
+    # in-pass gate: A_log and dt_bias are required and checked for alignment
+    expect(1, flags=kda.ALL_IN_KERNEL, A_log=None)
+    expect(1, flags=kda.GATE_IN_KERNEL, dt_bias=None)
+    expect(7, flags=kda.GATE_IN_KERNEL, dt_bias=Args().dt_bias + 4)
+    # pre-activated gate: they are not read, so NULL or misaligned pass validation (the
+    # too-small workspace, checked later, is then the first error)
+    a = Args()
+    for flags in (0, kda.QK_L2NORM_IN_KERNEL | kda.BETA_SIGMOID_IN_KERNEL):
+        expect(8, flags=flags, A_log=None, dt_bias=None, ws_bytes=a.ws_bytes - 1)
+        expect(8, flags=flags, A_log=a.A_log + 1, dt_bias=a.dt_bias + 4, ws_bytes=a.ws_bytes - 1)
+        expect(5, flags=flags, A_log=None, dt_bias=None, lb=0.5)  # lower_bound still checked
+    # the other switches do not change what is required
+    expect(1, flags=kda.GATE_IN_KERNEL, q=None)
