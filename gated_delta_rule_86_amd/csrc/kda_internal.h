@@ -53,10 +53,23 @@ inline SegPlan plan_segments(int64_t chains, int64_t nch)
     return best;
 }
 
+// Workgroups per head of the whole-chain launch: about one workgroup per CU over all
+// heads, never more than the sequences.
+inline int64_t whole_chain_groups(int64_t H, int64_t n_seq)
+{
+    int64_t p = kPlanCUs / H;
+    if (p < 1)
+        p = 1;
+    if (p > n_seq)
+        p = n_seq;
+    return p < 1 ? 1 : p;
+}
+
 struct Layout {
     int64_t n_seq;     // N (or B without cu_seqlens)
     size_t off_status; // int32 status word; int64 n_total at +8
     size_t off_seq_start, off_seq_len, off_seq_off;
+    size_t off_wg;     // int64 [kPlanCUs + 1]: first sequence of each whole-chain workgroup of a head
     SegPlan seg;       // segment plan (G == 1 without segmentation)
     size_t off_seg;    // fp32 states S, F, P: 3 x [chains][G][128][128] when G > 1
     size_t total;
@@ -85,6 +98,8 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)N, kAlign);
     L->off_seq_off = off;
     off = round_up(off + sizeof(int64_t) * (size_t)(N + 1), kAlign);
+    L->off_wg = off;
+    off = round_up(off + sizeof(int64_t) * (size_t)(kPlanCUs + 1), kAlign);
     L->seg = varlen ? SegPlan{1, 0} : plan_segments(N * H, cdiv(T, kCH));
     L->off_seg = off;
     if (L->seg.G > 1)

@@ -95,17 +95,56 @@ __device__ __forceinline__ void lds_sync_wave()
 struct TableArgs {
     const int64_t *cu;
     int64_t B, T, N;
+    int64_t P;  // whole-chain workgroups per head
     int32_t *status;
     int64_t *n_total;
     int64_t *seq_start, *seq_len, *seq_off;
+    int64_t *wg_first;  // [P + 1]
 };
 
+__device__ void chunk_table_body(const TableArgs &a, int tid);
+
+// Whole-chain workgroup split: the P workgroups of a head take contiguous runs of
+// sequences with about equal chunk counts.  Sequence i goes to workgroup
+// floor(P * mid_i / total) (at most P - 1), mid_i = (seq_off[i] + seq_off[i+1]) / 2 its
+// chunk midpoint; wg_first[s] is the first sequence of workgroup s, wg_first[P] = N.
+// With no chunks at all every sequence goes to the last workgroup.
+__device__ void partition_sequences(const TableArgs &a, int tid)
+{
+    // seq_off was written by this workgroup: make it visible to every thread's loads
+    __threadfence();
+    __syncthreads();
+    const int64_t tot = a.seq_off[a.N];
+    auto group_of = [&](int64_t i) -> int64_t {
+        if (tot <= 0)
+            return a.P - 1;
+        const int64_t g = (a.seq_off[i] + a.seq_off[i + 1]) * a.P / (2 * tot);
+        return g < a.P - 1 ? g : a.P - 1;
+    };
+    for (int64_t i = tid; i < a.N; i += 256) {
+        const int64_t lo = i == 0 ? 0 : group_of(i - 1) + 1;
+        const int64_t hi = group_of(i);
+        for (int64_t g = lo; g <= hi; ++g)
+            a.wg_first[g] = i;
+    }
+    if (tid == 0) {
+        const int64_t lo = a.N == 0 ? 0 : group_of(a.N - 1) + 1;
+        for (int64_t g = lo; g <= a.P; ++g)
+            a.wg_first[g] = a.N;
+    }
+}
+
 __global__ __launch_bounds__(256) void chunk_table_kernel(TableArgs a)
+{
+    chunk_table_body(a, threadIdx.x);
+    partition_sequences(a, threadIdx.x);
+}
+
+__device__ void chunk_table_body(const TableArgs &a, int tid)
 {
     __shared__ int s_bad;
     __shared__ int64_t s_scan[256];
     __shared__ int64_t s_carry;
-    const int tid = threadIdx.x;
     if (a.cu == nullptr) {
         const int64_t per = cdiv(a.T, kCH);
         for (int64_t b = tid; b < a.N; b += 256) {
@@ -314,6 +353,7 @@ struct FusedArgs {
     int h0_dtype, ht_dtype;
     int64_t H, N;
     const int64_t *seq_start, *seq_len;
+    const int64_t *wg_first;  // whole-chain pass: first sequence of each workgroup of a head
     int32_t *status;
     // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B (see SegPlan)
     int pass, G;
@@ -337,12 +377,12 @@ struct Unit {
 };
 
 // A workgroup's work: one unit (segment passes), or -- whole-chain pass -- the chains
-// (n, h) for n = sub, sub + stride, ... < N of one head h, one after another.  The
+// (n, h) for n = sub, sub + 1, ... < n_end of one head h, one after another.  The
 // producers then run ahead into the next chain while the consumers finish the current one.
 struct WgPlan {
     int pass;
     int h;
-    int64_t sub, stride;  // whole-chain pass: sequences sub, sub + stride, ...
+    int64_t sub, n_end;   // whole-chain pass: sequences sub, sub + 1, ... < n_end
     int64_t n;            // segment passes: the sequence
     int seg;              // segment passes: the segment
     int kind;             // pass A: 0 exact segment 0, 1 F run, 2 P run
@@ -353,8 +393,8 @@ __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
     constexpr int64_t kBlock = (int64_t)kD * kD;
     int64_t n;
     if (w.pass == 0) {
-        n = w.sub + k * w.stride;
-        if (n >= a.N)
+        n = w.sub + k;
+        if (n >= w.n_end)
             return false;
     } else {
         if (k > 0)
@@ -417,8 +457,8 @@ __device__ bool range_at(const FusedArgs &a, const WgPlan &w, int64_t k, Range &
 {
     int64_t n, seg = 0;
     if (w.pass == 0) {
-        n = w.sub + k * w.stride;
-        if (n >= a.N)
+        n = w.sub + k;
+        if (n >= w.n_end)
             return false;
     } else {
         if (k > 0)
@@ -1055,10 +1095,12 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     w.seg = 0;
     const uint32_t bid = blockIdx.x, H32 = (uint32_t)a.H;
     if (a.pass == 0) {
-        // heads h = block % H; the blocks of one head share its sequences round-robin
+        // heads h = block % H; block / H of a head takes the run of sequences the chunk
+        // table assigned to it
         w.h = (int)(bid % H32);
-        w.sub = bid / H32;
-        w.stride = gridDim.x / H32;
+        const uint32_t grp = bid / H32;
+        w.sub = a.wg_first[grp];
+        w.n_end = a.wg_first[grp + 1];
         w.n = 0;
     } else {
         const uint32_t upc = a.pass == 1 ? 2u * (uint32_t)a.G - 3u : (uint32_t)a.G - 1u;
@@ -1074,7 +1116,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         w.h = (int)(chain % H32);
         w.n = chain / H32;
         w.sub = 0;
-        w.stride = 1;
+        w.n_end = 0;
         if (w.n >= a.N)
             return;
     }
@@ -1193,6 +1235,8 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     a.N = f.lay.n_seq;
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
     a.n_total = reinterpret_cast<int64_t *>(f.ws + f.lay.off_status + 8);
+    a.P = whole_chain_groups(f.H, f.lay.n_seq);
+    a.wg_first = reinterpret_cast<int64_t *>(f.ws + f.lay.off_wg);
     a.seq_start = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_off);
@@ -1233,6 +1277,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.N = f.lay.n_seq;
     a.seq_start = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_len);
+    a.wg_first = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_wg);
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
     a.G = f.lay.seg.G;
     a.L = f.lay.seg.L;
@@ -1247,14 +1292,10 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     if (e != hipSuccess)
         return e;
     if (a.G <= 1) {
-        // whole chains: H x per_head workgroups, each running the sequences n = sub,
-        // sub + per_head, ... of one head back to back (about one workgroup per CU)
+        // whole chains: H x per_head workgroups, each running a run of sequences of one
+        // head back to back (about one workgroup per CU; runs from the chunk table)
         a.pass = 0;
-        int64_t per_head = kPlanCUs / f.H;
-        if (per_head < 1)
-            per_head = 1;
-        if (per_head > f.lay.n_seq)
-            per_head = f.lay.n_seq;
+        const int64_t per_head = whole_chain_groups(f.H, f.lay.n_seq);
         hipLaunchKernelGGL(fused, dim3((unsigned)(f.H * per_head)), dim3(512), kFusedLds, s, a);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;

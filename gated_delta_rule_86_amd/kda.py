@@ -90,7 +90,7 @@ def forward_launches(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -
     states per chain and segment beyond the chunk table)."""
     n = N if varlen else B
     up = lambda x: -(-x // 256) * 256
-    table = 256 + up(8 * n) + up(8 * n) + up(8 * (n + 1))
+    table = 256 + up(8 * n) + up(8 * n) + up(8 * (n + 1)) + up(8 * 257)
     return 2 if workspace_size(B, T, H, N, varlen) > table else 1
 
 

@@ -160,8 +160,10 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
                          void *const *stage_events);
 
 /*
- * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs: the status word and the
- * per-sequence chunk table (start, length, chunk offset), O(N) bytes.  Without cu_seqlens
+ * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs: the status word, the
+ * per-sequence chunk table (start, length, chunk offset), O(N) bytes, and a fixed 2.25 KiB
+ * table that splits the sequences into runs of about equal chunk count, one run per
+ * workgroup.  Without cu_seqlens
  * and with few long chains (B * H small, T long), each chain is cut into G segments that
  * run in parallel (the state after a segment is affine in the state before it); that
  * adds three fp32 128 x 128 states per chain and segment, 3 * B * H * G * 64 KiB, with G

@@ -3,6 +3,8 @@
 * chunk table (cu_seqlens -> per-sequence chunk offsets, total): equal, bit for bit, to a
   brute-force enumeration of 16-token chunk starts and to sum(ceil(L_i / 16)); invalid
   cu_seqlens set the documented status bits and make every sequence empty.
+* the split of a head's sequences into per-workgroup runs of about equal chunk count,
+  bit for bit against a brute-force assignment by chunk midpoint.
 * every out element and every final_state element is written (NaN sentinels vanish);
 * perturbing one sequence leaves every other sequence's out and final_state bit-identical;
 * two runs are bitwise identical, also with a workspace pre-filled with garbage;
@@ -121,3 +123,42 @@ def test_power_of_two_scaling_is_exact():
     o2, f2, _ = run_gpu(w, d2, keep_device=True)
     assert torch.equal(o2, 2 * o1)
     assert torch.equal(f2, 2 * f1)
+
+
+def expected_runs(seq_off, P):
+    """First sequence of each of the P workgroups of a head: sequence i goes to workgroup
+    floor(P * mid_i / total) (at most P - 1) with mid_i its chunk midpoint; all to the last
+    workgroup when there are no chunks.  Brute force over the sequences."""
+    N = len(seq_off) - 1
+    tot = int(seq_off[-1])
+    grp = [P - 1 if tot == 0 else min(P - 1, (int(seq_off[i]) + int(seq_off[i + 1])) * P // (2 * tot))
+           for i in range(N)]
+    return np.array([next((i for i in range(N) if grp[i] >= s), N) for s in range(P)] + [N], dtype=np.int64)
+
+
+@pytest.mark.parametrize("N,H,kind", [(1, 1, "rand"), (8, 32, "rand"), (256, 32, "rand"), (300, 1, "rand"),
+                                      (1000, 3, "rand"), (5, 4, "empty"), (9, 2, "one_long"),
+                                      (40, 8, "bad")])
+def test_workgroup_runs(N, H, kind):
+    """The whole-chain split of sequences into per-workgroup runs, bit for bit."""
+    import torch
+    rng = np.random.default_rng(N + H)
+    L = rng.integers(0, 200, size=N)
+    if kind == "empty":
+        L[:] = 0
+    elif kind == "one_long":
+        L[:] = 3
+        L[4] = 5000
+    cu = np.zeros(N + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(L)
+    T = int(cu[-1])
+    if kind == "bad":
+        cu[3] = cu[4] + 1  # decreasing: every sequence becomes empty
+    P = max(1, min(256 // H, N))
+    up = lambda x: -(-x // 256) * 256
+    ws = torch.empty(kda.workspace_size(1, T, H, N, True), dtype=torch.uint8, device=torch_dev())
+    seq_off, _, status = kda.chunk_table(torch.from_numpy(cu).to(torch_dev()), 1, T, H, workspace=ws)
+    off = 256 + 2 * up(8 * N) + up(8 * (N + 1))
+    runs = ws[off:off + 8 * (P + 1)].cpu().numpy().view(np.int64)
+    assert np.array_equal(runs, expected_runs(seq_off, P)), (runs, expected_runs(seq_off, P))
+    assert (status != 0) == (kind == "bad")

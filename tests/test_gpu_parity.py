@@ -131,11 +131,11 @@ def test_in_place_state_carry():
 
 
 def segments_of(B, T, H):
-    """Segments per chain of the forward plan, read off the workspace size (tables + three
-    fp32 128 x 128 states per chain and segment)."""
+    """Segments per chain of the forward plan, read off the workspace size (tables, the
+    workgroup-run table, three fp32 128 x 128 states per chain and segment)."""
     from gated_delta_rule_86_amd import kda
     up = lambda x: -(-x // 256) * 256
-    table = 256 + up(8 * B) + up(8 * B) + up(8 * (B + 1))
+    table = 256 + up(8 * B) + up(8 * B) + up(8 * (B + 1)) + up(8 * 257)
     extra = kda.workspace_size(B, T, H) - table
     return 1 if extra == 0 else extra // (3 * B * H * 128 * 128 * 4)
 

@@ -3,7 +3,8 @@
 * libkda.so loads and exports every function include/kda.h declares.
 * Every validation error of kda_fwd is returned before anything touches the device:
   the pointers below are never dereferenced, so fake aligned addresses are fine.
-* kda_fwd_workspace_size covers the status word and the per-sequence chunk table, plus,
+* kda_fwd_workspace_size covers the status word, the per-sequence chunk table and the
+  table of whole-chain workgroup runs (257 int64), plus,
   for few long equal-length chains run as segments, three fp32 states per chain and segment.
 """
 import ctypes
@@ -47,7 +48,7 @@ def ws_size(B, T, H, N=0, varlen=False):
 
 def table_bytes(N):
     up = lambda x: -(-x // 256) * 256
-    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1))
+    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257)
 
 
 def test_workspace_size_formula():
