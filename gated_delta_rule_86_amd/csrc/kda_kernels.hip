@@ -81,6 +81,25 @@ __device__ __forceinline__ f32x4_t mfma32(u32x4_t a, u32x4_t b, f32x4_t c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+
+// A operands that subtract B from C lane by lane: mfma32(negI0, b, c) = c - b[0..3] and
+// mfma32(negI1, b, c) = c - b[4..7], element by element in every lane (b's bf16 values
+// widened exactly).  negI0 holds -1 at A[m][8(m/4) + m%4], negI1 at A[m][8(m/4) + 4 + m%4]:
+// lane m + 16(m/4), element m%4 (resp. 4 + m%4).  With b = bf16(c) the result is the exact
+// rounding residue c - bf16(c).
+__device__ __forceinline__ void make_neg_identity(int lane, u32x4_t &negI0, u32x4_t &negI1)
+{
+    negI0 = u32x4_t{0u, 0u, 0u, 0u};
+    negI1 = negI0;
+    const int m = lane & 15;
+    if ((lane >> 4) == (m >> 2)) {
+        const int e = m & 3;
+        const uint32_t v = (e & 1) ? 0xbf800000u : 0x0000bf80u;
+        negI0[e >> 1] = v;
+        negI1[2 + (e >> 1)] = v;
+    }
+}
+
 __device__ __forceinline__ void lds_sync_wave()
 {
     // LDS traffic of one wavefront is in order; wait for it and keep the compiler from
@@ -684,46 +703,54 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             }
         }
 
-        // Gamma = 2^b, 1/Gamma = 2^-b; gamma and 1/gamma are their values at the chunk's
-        // last token (lane 15 of the row): E = Gamma/gamma, Dk = gamma/Gamma.
-        float KG[32], QG[32], KD[32], KE[32], QE[32], GL[32];
+        // Gamma = 2^b, 1/Gamma = 2^-b; gamma is Gamma at the chunk's last token (lane 15 of
+        // the row).  KG = k^ Gamma, QG = scale q^ Gamma, KI = k^ / Gamma, KD = KI gamma.
+        // A_kk = KG KI^T and A_qk = QG KI^T (gamma cancels in both).
+        float KG[32], QG[32], KD[32], KI[32], GL[32];
 #pragma unroll
         for (int c = 0; c < 32; ++c) {
             const float G = fexp2(b2[c]);
             const float Gi = fexp2(-b2[c]);
-            const float E = G * dpp_row_last(Gi);
-            const float Dk = Gi * dpp_row_last(G);
             const float kn = kf[c] * rk;
             const float qn = qf[c] * rq;
             KG[c] = kn * G;
             QG[c] = qn * G;
-            KD[c] = kn * Dk;
-            KE[c] = kn * E;
-            QE[c] = qn * E;
+            KI[c] = kn * Gi;
+            KD[c] = KI[c] * dpp_row_last(G);
             GL[c] = G;
         }
-        u32x4_t keb[4], kel[4], qeb[4], kdb[4], kdlo[4];
+        // bf16 hi/lo pairs.  KG, KI and QG go in the operand-block order: group gg holds
+        // channels 4gg .. 4gg+3 and 16+4gg .. 16+4gg+3 of the lane's 32 (the same K order
+        // on both MFMA operands, so A_kk and A_qk contract over every channel).  KD keeps
+        // the natural order (8s .. 8s+7).  lo = x - hi comes from one MFMA per 4 values:
+        // (-I) hi + x, exact in fp32.
+        u32x4_t negI0, negI1;
+        make_neg_identity(lane, negI0, negI1);
+        auto split8 = [&](const float *x0, const float *x1, u32x4_t &hi, u32x4_t &lo) {
+            hi = u32x4_t{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                         pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+            const f32x4_t r0 = mfma32(negI0, hi, f32x4_t{x0[0], x0[1], x0[2], x0[3]});
+            const f32x4_t r1 = mfma32(negI1, hi, f32x4_t{x1[0], x1[1], x1[2], x1[3]});
+            lo = u32x4_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
+                         pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+        };
+        u32x4_t kgh[4], kgl[4], qgh[4], kih[4], kil[4], kdb[4], kdlo[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c0 = 8 * s + 2 * e;
-                const u32x2_t ke = split_bf16x2(KE[c0], KE[c0 + 1]);
-                keb[s][e] = ke[0];
-                kel[s][e] = ke[1];
-                const u32x2_t kd = split_bf16x2(KD[c0], KD[c0 + 1]);
-                kdb[s][e] = kd[0];
-                kdlo[s][e] = kd[1];
-                qeb[s][e] = pack_bf16x2(QE[c0], QE[c0 + 1]);
-            }
+        for (int gg = 0; gg < 4; ++gg) {
+            split8(KG + 4 * gg, KG + 16 + 4 * gg, kgh[gg], kgl[gg]);
+            split8(KI + 4 * gg, KI + 16 + 4 * gg, kih[gg], kil[gg]);
+            qgh[gg] = u32x4_t{pack_bf16x2(QG[4 * gg], QG[4 * gg + 1]), pack_bf16x2(QG[4 * gg + 2], QG[4 * gg + 3]),
+                              pack_bf16x2(QG[16 + 4 * gg], QG[16 + 4 * gg + 1]),
+                              pack_bf16x2(QG[16 + 4 * gg + 2], QG[16 + 4 * gg + 3])};
+            split8(KD + 8 * gg, KD + 8 * gg + 4, kdb[gg], kdlo[gg]);
         }
         f32x4_t akk = {0.f, 0.f, 0.f, 0.f}, aqkT = akk;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            akk = mfma32(keb[s], kdb[s], akk);
-            akk = mfma32(kel[s], kdb[s], akk);
-            akk = mfma32(keb[s], kdlo[s], akk);
-            aqkT = mfma32(kdb[s], qeb[s], aqkT);
+        for (int gg = 0; gg < 4; ++gg) {
+            akk = mfma32(kgh[gg], kih[gg], akk);
+            akk = mfma32(kgl[gg], kih[gg], akk);
+            akk = mfma32(kgh[gg], kil[gg], akk);
+            aqkT = mfma32(kih[gg], qgh[gg], aqkT);
         }
         const int g4 = (lane >> 4) * 4, col = lane & 15;
         f32x4_t A, AqT, I4;
@@ -758,22 +785,10 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
         unsigned char *rec = lds + (size_t)s * kBlkBytes;
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-            u32x4_t wk, wl, wq;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c0 = (e < 2 ? 4 * gg : 16 + 4 * gg) + 2 * (e & 1);
-                const u32x2_t t2 = split_bf16x2(KG[c0], KG[c0 + 1]);
-                wk[e] = t2[0];
-                wl[e] = t2[1];
-            }
-            wq[0] = pack_bf16x2(QG[4 * gg], QG[4 * gg + 1]);
-            wq[1] = pack_bf16x2(QG[4 * gg + 2], QG[4 * gg + 3]);
-            wq[2] = pack_bf16x2(QG[16 + 4 * gg], QG[16 + 4 * gg + 1]);
-            wq[3] = pack_bf16x2(QG[16 + 4 * gg + 2], QG[16 + 4 * gg + 3]);
             const int o = (qb * 64 + r + 16 * gg) * 16;
-            *reinterpret_cast<u32x4_t *>(rec + kBlkKG + o) = wk;
-            *reinterpret_cast<u32x4_t *>(rec + kBlkKGL + o) = wl;
-            *reinterpret_cast<u32x4_t *>(rec + kBlkQG + o) = wq;
+            *reinterpret_cast<u32x4_t *>(rec + kBlkKG + o) = kgh[gg];
+            *reinterpret_cast<u32x4_t *>(rec + kBlkKGL + o) = kgl[gg];
+            *reinterpret_cast<u32x4_t *>(rec + kBlkQG + o) = qgh[gg];
         }
         // KD: tile ct = ch/16, lane position ch%16 + 16*(r/4), token r%4 of the hi and lo
         // quarters of the 16-byte fragment
@@ -895,16 +910,8 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     // -I in the MFMA A layout for the k-slot order of a channel pair of tiles (2t, 2t+1):
     // slot 8*(m/4) + m%4 holds channel m of tile 2t, slot 8*(m/4) + 4 + m%4 channel m of
     // tile 2t+1.  Lane m + 16*(m/4) carries the -1 (bf16 0xbf80) at element m%4 or 4+m%4.
-    u32x4_t negI0 = {0u, 0u, 0u, 0u}, negI1 = negI0;
-    {
-        const int m = lane & 15;
-        if ((lane >> 4) == (m >> 2)) {
-            const int e = m & 3;
-            const uint32_t v = (e & 1) ? 0xbf800000u : 0x0000bf80u;
-            negI0[e >> 1] = v;
-            negI1[2 + (e >> 1)] = v;
-        }
-    }
+    u32x4_t negI0, negI1;
+    make_neg_identity(lane, negI0, negI1);
     unsigned char *obuf = lds + kOffOut + cw * 1024;  // output tile of the previous chunk
     const int orow = lane >> 2;                        // output row this lane stores
     auto store_out = [&](int64_t jo) {
