@@ -561,6 +561,16 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n)
     }
 }
 
+// Four 16-byte-per-lane direct-to-LDS loads into dst + 1024*i, i = 0..3, from voffsets
+// vo[i] + 1024*i (the instruction offset carries the 1024*i on both sides).
+__device__ __forceinline__ void dma_tile16(__amdgpu_buffer_rsrc_t r, unsigned char *dst, const uint32_t *vo)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, vo[0], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, vo[1], 0, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, vo[2], 0, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, vo[3], 0, 3072, 0);
+}
+
 // kSw: the activation switches are read from a.flags; without it every activation runs in
 // the pass (the common case gets code with no switch logic in it).
 template <bool kSw>
@@ -591,17 +601,23 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + elem0, nb);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + elem0, nb);
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + elem0, nb);
+        // The 1 KB quarter i of a tile is addressed by the instruction offset 1024*i, which
+        // moves the LDS destination and the global address alike (and takes part in the
+        // range check), so the voffset drops it and M0 changes once per tensor.
+        uint32_t vo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t row = 4 * i + (lane >> 4);
             const uint32_t seg = (uint32_t)(lane & 15) ^ (row & 7u);
-            const uint32_t vo = row * rowb + seg * 16u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(stage + i * 1024), 16, vo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(stage + 4096 + i * 1024), 16, vo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void *)(stage + 8192 + i * 1024), 16, vo, 0, 0, 0);
+            vo[i] = row * rowb + seg * 16u - 1024u * i;  // row * rowb >= 1024 i: rowb >= 256
         }
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(a.beta + (size_t)t0 * (size_t)H + (size_t)h, (uint32_t)(tl - 1) * (uint32_t)(H * 2) + 2u);
+        dma_tile16(rq, stage, vo);
+        dma_tile16(rk, stage + 4096, vo);
+        dma_tile16(rg, stage + 8192, vo);
+        // (the byte count is wave-uniform; say so, or the descriptor goes through a
+        // readfirstlane loop)
+        const uint32_t nbb = __builtin_amdgcn_readfirstlane((uint32_t)(tl - 1) * (uint32_t)(H * 2) + 2u);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + (size_t)t0 * (size_t)H + (size_t)h, nbb);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage + 12288), 2,
                                                  (uint32_t)lane * (uint32_t)(H * 2), 0, 0, 0);
     };
