@@ -1163,86 +1163,90 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     }
 }
 
-// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32.  Rows of S are
-// independent, so one workgroup takes R rows of one chain (128/R workgroups per chain)
-// and keeps them in LDS across the steps.  P_g (64 KiB) goes through LDS once per step
-// with 16-byte coalesced loads; the loads of P_{g+1} and F_{g+1} are issued before step
-// g's arithmetic.  Thread t computes column t % 128 of rows (R/2)*(t/128) .. +R/2-1.
+// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32 on v_mfma_f32_16x16x4_f32.
+// Rows of S are independent: a workgroup takes 16 rows of one chain (8 workgroups per
+// chain) and keeps them in registers across the steps, in the MFMA A layout (lane m + 16k
+// holds S[m][4j + k] for step j of the contraction).  Wave w forms output columns
+// 32w .. 32w+31 (two 16-column tiles); its B operands, P_g[4j + k][c] in lane c + 16k, come
+// straight from global memory (16 lanes read 64 contiguous bytes), and those of the next
+// step, with F_g, are loaded before this step's MFMAs.  The 16 x 128 result goes back to
+// the A layout through LDS.  Workgroup b takes chain b % chains, so the 8 workgroups of a
+// chain share a slot modulo 8 (the XCD the dispatcher gives them, whose L2 then holds that
+// chain's P_g once).
 struct ScanArgs {
     float *segS, *segF, *segP;
     int G;
     int64_t chains;
 };
 
-template <int R>
 __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
 {
-    constexpr int RH = R / 2;
-    __shared__ __attribute__((aligned(16))) float s_P[kD * kD];
-    __shared__ __attribute__((aligned(16))) float s_rows[R][kD];
+    __shared__ float s_rows[16][kD + 4];
     constexpr int64_t kBlock = (int64_t)kD * kD;
-    constexpr int kBlocksPerChain = kD / R;
-    const int64_t chain = blockIdx.x / kBlocksPerChain;
-    if (chain >= a.chains)
+    const int64_t chain = blockIdx.x % a.chains;
+    const int r0 = (int)(blockIdx.x / a.chains) * 16;
+    if (r0 >= kD)
         return;
-    const int r0 = (blockIdx.x % kBlocksPerChain) * R;
-    const int tid = threadIdx.x;
-    const int c = tid & 127;
-    const int rr = RH * (tid >> 7);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m = lane & 15, kq = lane >> 4;  // A: row m, k-sub kq; B and D: column m
     auto blk = [&](float *base, int g) { return base + ((size_t)chain * a.G + (size_t)g) * kBlock; };
+    float av[32];
     {
-        const float *S1 = blk(a.segS, 1);
+        const float *S1 = blk(a.segS, 1) + (size_t)(r0 + m) * kD + kq;
 #pragma unroll
-        for (int i = 0; i < RH; ++i)
-            s_rows[rr + i][c] = S1[(size_t)(r0 + rr + i) * kD + c];
+        for (int j = 0; j < 32; ++j)
+            av[j] = S1[4 * j];
     }
-    // P_g and this thread's entries of F_g in registers (P: float4 t + 256 i)
-    f32x4_t pre[16];
-    float fpre[RH];
-    auto load_PF = [&](int g) {
-        const f32x4_t *P = reinterpret_cast<const f32x4_t *>(blk(a.segP, g));
+    float bv[2][32];
+    f32x4_t fv[2];  // F_g[r0 + 4kq + i][32w + 16t + m]: the D layout of the output tiles
+    auto load_BF = [&](int g) {
+        const float *P = blk(a.segP, g) + (size_t)kq * kD + 32 * w + m;
+        const float *F = blk(a.segF, g) + (size_t)(r0 + 4 * kq) * kD + 32 * w + m;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            pre[i] = P[tid + 256 * i];
-        const float *F = blk(a.segF, g);
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int i = 0; i < RH; ++i)
-            fpre[i] = F[(size_t)(r0 + rr + i) * kD + c];
+            for (int i = 0; i < 4; ++i)
+                fv[t][i] = F[(size_t)i * kD + 16 * t];
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                bv[t][j] = P[(size_t)(4 * j) * kD + 16 * t];
+        }
     };
-    if (a.G > 2)
-        load_PF(1);
+    load_BF(1);
     for (int g = 1; g + 1 < a.G; ++g) {
-        float acc[RH];
+        // two accumulators per tile (even and odd k-steps) keep four MFMA chains in flight
+        f32x4_t acc[2][2];
+        float bc[2][32];
 #pragma unroll
-        for (int i = 0; i < RH; ++i)
-            acc[i] = fpre[i];
-        __syncthreads();  // previous step's reads of s_P are done
+        for (int t = 0; t < 2; ++t) {
+            acc[t][0] = fv[t];
+            acc[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            reinterpret_cast<f32x4_t *>(s_P)[tid + 256 * i] = pre[i];
-        __syncthreads();
+            for (int j = 0; j < 32; ++j)
+                bc[t][j] = bv[t][j];
+        }
         if (g + 2 < a.G)
-            load_PF(g + 1);
-        for (int k = 0; k < kD; k += 4) {
-            f32x4_t x[RH];
+            load_BF(g + 1);
 #pragma unroll
-            for (int i = 0; i < RH; ++i)
-                x[i] = *reinterpret_cast<const f32x4_t *>(&s_rows[rr + i][k]);
+        for (int j = 0; j < 32; ++j) {
+            acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bc[0][j], acc[0][j & 1], 0, 0, 0);
+            acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bc[1][j], acc[1][j & 1], 0, 0, 0);
+        }
+        const f32x4_t res[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
+        // rows 4kq + i, column 32w + 16t + m: to global, and through LDS to the A layout
+        float *Sn = blk(a.segS, g + 1) + (size_t)(r0 + 4 * kq) * kD + 32 * w + m;
+        __syncthreads();  // the previous step's reads of s_rows are done
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float pk = s_P[(k + e) * kD + c];
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < RH; ++i)
-                    acc[i] = fmaf(x[i][e], pk, acc[i]);
+            for (int i = 0; i < 4; ++i) {
+                Sn[(size_t)i * kD + 16 * t] = res[t][i];
+                s_rows[4 * kq + i][32 * w + 16 * t + m] = res[t][i];
             }
-        }
-        __syncthreads();  // every thread has read s_rows for this step
-        float *Sn = blk(a.segS, g + 1);
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < RH; ++i) {
-            s_rows[rr + i][c] = acc[i];
-            Sn[(size_t)(r0 + rr + i) * kD + c] = acc[i];
-        }
+        for (int j = 0; j < 32; ++j)
+            av[j] = s_rows[m][4 * j + kq];
     }
 }
 
@@ -1337,11 +1341,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
         sa.segP = a.segP;
         sa.G = a.G;
         sa.chains = chains;
-        // about 256 workgroups: 4 rows each for few chains, 16 for more
-        if (chains * (kD / 4) <= 2 * kPlanCUs)
-            hipLaunchKernelGGL(seg_scan_kernel<4>, dim3((unsigned)(chains * (kD / 4))), dim3(256), 0, s, sa);
-        else
-            hipLaunchKernelGGL(seg_scan_kernel<16>, dim3((unsigned)(chains * (kD / 16))), dim3(256), 0, s, sa);
+        hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(chains * (kD / 16))), dim3(256), 0, s, sa);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
