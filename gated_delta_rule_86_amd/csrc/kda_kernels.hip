@@ -285,6 +285,18 @@ __device__ __forceinline__ float dpp_row_shr(float x, int n)
     return __builtin_bit_cast(float, r);
 }
 // Value of lane 15 of this lane's row of 16 (DPP row_newbcast:15).
+// Inclusive prefix sum over the 16 lanes of each row.  x is pinned to a register first
+// (an empty asm the compiler cannot see through), so the first add is not contracted with
+// the multiply that produced x and every step is one v_add_f32 with a DPP source operand.
+__device__ __forceinline__ float row_scan16(float x)
+{
+    __asm__("" : "+v"(x));
+    x = __fadd_rn(x, dpp_row_shr(x, 1));
+    x = __fadd_rn(x, dpp_row_shr(x, 2));
+    x = __fadd_rn(x, dpp_row_shr(x, 4));
+    return __fadd_rn(x, dpp_row_shr(x, 8));
+}
+
 __device__ __forceinline__ float dpp_row_last(float x)
 {
     int v = __builtin_bit_cast(int, x);
@@ -699,10 +711,7 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
                 for (int e = 0; e < 4; ++e) {
                     const int c = 4 * w + e;
                     float av = lbv * frcp(1.0f + fexp2(fmaf(gf[c], m1, d4[e])));
-                    av += dpp_row_shr(av, 1);
-                    av += dpp_row_shr(av, 2);
-                    av += dpp_row_shr(av, 4);
-                    av += dpp_row_shr(av, 8);
+                    av = row_scan16(av);
                     b2[c] = av;
                 }
             }
@@ -711,10 +720,7 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 #pragma unroll
             for (int c = 0; c < 32; ++c) {
                 float av = gk * fminf(fmaxf(gf[c], a.lower_bound), 0.f);
-                av += dpp_row_shr(av, 1);
-                av += dpp_row_shr(av, 2);
-                av += dpp_row_shr(av, 4);
-                av += dpp_row_shr(av, 8);
+                av = row_scan16(av);
                 b2[c] = av;
             }
         }
