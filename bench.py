@@ -6,8 +6,11 @@ A step is one kda_fwd call (chunk table, prep, state/output stages) over one bat
 seeded synthetic input already resident in HBM.  Default workload: B=2, T=4096, H=16,
 K=V=128, fp32 initial and final state (index 1 of workloads.config).  Prints one JSON line.
 
-roofline: the dominant kernel, fused_kernel (the forward kernel), against HBM.  HIP events
-are recorded on the launch stream around every launch of every timed step.  Without
+value and ms_per_step: K steps run back to back with nothing between the launches.  Then
+K more steps with HIP events recorded on the launch stream around every launch give each
+kernel's duration (recording an event between two launches delays the second one by a few
+microseconds, so these steps are timed separately and reported as ms_per_step_with_events).
+roofline: the dominant kernel, fused_kernel (the forward kernel), against HBM.  Without
 segmentation fused_kernel runs once per step; with it (few long chains) twice, pass A and
 pass B, with seg_scan_kernel between them.  achieved = the path's algorithmic bytes per
 step / fused_kernel's time per step (the sum over its launches): q, k, v, g (4 x 256 B) +
@@ -58,9 +61,12 @@ def committed_traffic(workload_name, kernel):
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     for line in open(path):
         if line.startswith("traffic_bytes_per_step:"):
-            fields = dict(f.split("=", 1) for f in line.split(":", 1)[1].split())
+            fields = dict(f.split("=", 1) for f in line.split(":", 1)[1].split() if "=" in f)
             if fields.get("source_sha256") == sha and kernel in fields:
-                return int(fields[kernel])
+                try:
+                    return int(fields[kernel])
+                except ValueError:
+                    return None
     return None
 
 
@@ -167,12 +173,22 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # value: K steps exactly as a caller runs them (no events between the launches)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i])
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # per-launch durations: K more steps with HIP events recorded around every launch on the
+    # launch stream (the event records sit between the launches, so these steps are not the
+    # ones the throughput comes from)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t1
 
     # intervals: table, forward launch 1, scan, forward launch 2
     iv = [0.0, 0.0, 0.0, 0.0]
@@ -218,6 +234,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name, dname),
                      "kernel": dname, "launches_per_step": launches,
                      "kernel_ms": stage_ms[1], "kernel_algorithmic_bytes": kernel_bytes},
+        "timing": {"ms_per_step_with_events": elapsed_ev / args.steps * 1e3},
         "path": {"algorithmic_bytes": path_bytes, "achieved_GBps": path_gbps,
                  "hbm_frac": path_gbps / HBM_PEAK_GBPS, "achieved_TFLOPs": path_tflops,
                  "mfma_frac": path_tflops / MFMA_BF16_PEAK_TFLOPS,
