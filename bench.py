@@ -10,7 +10,9 @@ value and ms_per_step: K steps run back to back with nothing between the launche
 K more steps with HIP events recorded on the launch stream around every launch give each
 kernel's duration (recording an event between two launches delays the second one by a few
 microseconds, so these steps are timed separately and reported as ms_per_step_with_events).
-roofline: the dominant kernel, fused_kernel (the forward kernel), against HBM.  Without
+roofline: the dominant kernel, fused_kernel (the forward kernel), against HBM; for the
+decode workload (--workload 5, one token per sequence) the step is kda_fwd_recurrent and
+the dominant kernel is recurrent_kernel.  Without
 segmentation fused_kernel runs once per step; with it (few long chains) twice, pass A and
 pass B, with seg_scan_kernel between them.  achieved = the path's algorithmic bytes per
 step / fused_kernel's time per step (the sum over its launches): q, k, v, g (4 x 256 B) +
@@ -37,6 +39,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 BYTES_PER_HT = 1282              # q, k, v, g (4 x 256) + beta (2) + out (256)
 FLOPS_PER_HT = 122880            # dense contractions per head-token (three 16x128x128 per chunk + intra-chunk)
 METRIC = "KDA fwd head-tokens/sec on 1 MI355X + % of HBM/MFMA roofline"
+DECODE_WORKLOADS = (5,)          # run through the token-by-token entry point (kda_fwd_recurrent)
 
 
 def state_bytes(w):
@@ -49,13 +52,13 @@ def state_bytes(w):
     return b
 
 
-def committed_traffic(workload_name, kernel):
+def committed_traffic(workload_name, kernel, source="kda_kernels.hip"):
     """HBM bytes per step of `kernel` (summed over its launches) from the committed rocprofv3
     summary of this workload (profiles/kda_fwd_<workload>.md), or None when there is none or
     the kernel source has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"kda_fwd_{workload_name}.md")
-    src = os.path.join(ROOT, "gated_delta_rule_86_amd", "csrc", "kda_kernels.hip")
+    src = os.path.join(ROOT, "gated_delta_rule_86_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -122,7 +125,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, help="index into workloads.config (0..4)")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="index into workloads.config (0..4; 5 = decode step, token-by-token path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -157,9 +161,12 @@ def main():
                           dtype=torch.float32 if w.final_dtype == "fp32" else torch.bfloat16)
     ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.N, cu is not None), dtype=torch.uint8, device=dev)
 
+    recurrent = args.workload in DECODE_WORKLOADS
+    entry = kda.fwd_recurrent if recurrent else kda.fwd
+
     def step(events=None):
-        kda.fwd(q, k, v, g, beta, w.scale, out, A_log, dt_bias, w.lower_bound, h0, fin, cu,
-                workspace=ws, stage_events=events)
+        entry(q, k, v, g, beta, w.scale, out, A_log, dt_bias, w.lower_bound, h0, fin, cu,
+              workspace=ws, stage_events=events)
 
     hip = hip_runtime()
     ev = []
@@ -193,16 +200,21 @@ def main():
     # intervals: table, forward launch 1, scan, forward launch 2
     iv = [0.0, 0.0, 0.0, 0.0]
     for i in range(args.steps):
-        for j in range(4):
+        for j in range(2 if recurrent else 4):
             ms = ctypes.c_float()
             assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[i][j], ev[i][j + 1]) == 0
             iv[j] += ms.value / args.steps
-    launches = kda.forward_launches(w.B, w.T, w.H, w.N, cu is not None)
-    stage_names = ["chunk_table_kernel", "fused_kernel", "seg_scan_kernel"]
-    if launches == 2:
-        stage_ms = [iv[0], iv[1] + iv[3], iv[2]]
-    else:  # one forward launch; the later marks are recorded back to back
-        stage_ms = [iv[0], iv[1], 0.0]
+    if recurrent:  # events: before the table, before the recurrent kernel, after it
+        launches = 1
+        stage_names = ["chunk_table_kernel", "recurrent_kernel"]
+        stage_ms = [iv[0], iv[1]]
+    else:
+        launches = kda.forward_launches(w.B, w.T, w.H, w.N, cu is not None)
+        stage_names = ["chunk_table_kernel", "fused_kernel", "seg_scan_kernel"]
+        if launches == 2:
+            stage_ms = [iv[0], iv[1] + iv[3], iv[2]]
+        else:  # one forward launch; the later marks are recorded back to back
+            stage_ms = [iv[0], iv[1], 0.0]
     for row in ev:
         for e in row:
             hip.hipEventDestroy(e)
@@ -210,7 +222,8 @@ def main():
     ht = w.head_tokens
     ms_per_step = elapsed / args.steps * 1e3
     value = ht / (elapsed / args.steps)
-    dname = "fused_kernel"
+    dname = "recurrent_kernel" if recurrent else "fused_kernel"
+    dsrc = "kda_recurrent.hip" if recurrent else "kda_kernels.hip"
     kernel_bytes = ht * BYTES_PER_HT + state_bytes(w)
     achieved = kernel_bytes / (stage_ms[1] * 1e-3) / 1e9
     path_bytes = ht * BYTES_PER_HT + state_bytes(w)
@@ -231,7 +244,7 @@ def main():
         "data": "synthetic",
         "config": dict(w.describe(), head_tokens=ht),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name, dname),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name, dname, dsrc),
                      "kernel": dname, "launches_per_step": launches,
                      "kernel_ms": stage_ms[1], "kernel_algorithmic_bytes": kernel_bytes},
         "timing": {"ms_per_step_with_events": elapsed_ev / args.steps * 1e3},

@@ -158,7 +158,7 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
                     void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
                     const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
                     int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
-                    uint32_t flags, void *const *events)
+                    uint32_t flags, void *const *events, bool recurrent = false)
 {
     kda::Layout lay;
     kda_status st = validate(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
@@ -200,6 +200,8 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
     if (events)
         for (int i = 0; i < 3; ++i)
             marks[i] = static_cast<hipEvent_t>(events[2 + i]);
+    if (recurrent)
+        return mark(1) && kda::launch_recurrent(a, s) == hipSuccess && mark(2) ? KDA_OK : KDA_ERR_HIP;
     if (!mark(1) || kda::launch_forward(a, s, events ? marks : nullptr) != hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
@@ -232,6 +234,40 @@ kda_status kda_fwd_ex(const void *q, const void *k, const void *v, const void *g
     return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                     initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
                     B, T, H, N, K, V, workspace, workspace_bytes, stream, flags, nullptr);
+}
+
+kda_status kda_fwd_recurrent(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                             float scale, void *out, const float *A_log, const float *dt_bias,
+                             float lower_bound, const void *initial_state,
+                             kda_state_dtype initial_state_dtype, void *final_state,
+                             kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                             const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                             int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                             uint32_t flags)
+{
+    return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, flags, nullptr, true);
+}
+
+kda_status kda_fwd_recurrent_timed(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, float scale, void *out, const float *A_log,
+                                   const float *dt_bias, float lower_bound, const void *initial_state,
+                                   kda_state_dtype initial_state_dtype, void *final_state,
+                                   kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                                   const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H,
+                                   int64_t N, int64_t K, int64_t V, void *workspace,
+                                   size_t workspace_bytes, void *stream, uint32_t flags,
+                                   void *const *stage_events)
+{
+    if (!stage_events)
+        return KDA_ERR_NULL;
+    for (int i = 0; i < 3; ++i)
+        if (!stage_events[i])
+            return KDA_ERR_NULL;
+    return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    initial_state_dtype, final_state, final_state_dtype, cu_seqlens, cu_seqlens_host,
+                    B, T, H, N, K, V, workspace, workspace_bytes, stream, flags, stage_events, true);
 }
 
 kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,

@@ -125,5 +125,7 @@ struct FwdArgs {
 
 hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t s, hipEvent_t const *marks);
+// token-by-token evaluation, one workgroup per chain (kda_recurrent.hip)
+hipError_t launch_recurrent(const FwdArgs &a, hipStream_t s);
 
 }  // namespace kda

@@ -34,7 +34,9 @@ ALL_IN_KERNEL = 7
 STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_timed", "kda_fwd_workspace_size", "kda_status_string",
+EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_recurrent", "kda_fwd_recurrent_timed", "kda_fwd_timed",
+           "kda_fwd_workspace_size",
+           "kda_status_string",
            "kda_fwd_device_status", "kda_chunk_table", "kda_version")
 
 
@@ -62,6 +64,10 @@ def lib():
                           ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
     L.kda_fwd_ex.restype = ctypes.c_int
     L.kda_fwd_ex.argtypes = L.kda_fwd.argtypes + [ctypes.c_uint32]
+    L.kda_fwd_recurrent.restype = ctypes.c_int
+    L.kda_fwd_recurrent.argtypes = L.kda_fwd.argtypes + [ctypes.c_uint32]
+    L.kda_fwd_recurrent_timed.restype = ctypes.c_int
+    L.kda_fwd_recurrent_timed.argtypes = L.kda_fwd_recurrent.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     L.kda_fwd_timed.restype = ctypes.c_int
     L.kda_fwd_timed.argtypes = L.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     L.kda_fwd_workspace_size.restype = ctypes.c_size_t
@@ -116,10 +122,20 @@ def _state_code(t) -> int:
     raise ValueError(f"state dtype must be bf16 or fp32, got {t.dtype}")
 
 
+def fwd_recurrent(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
+                  final_state=None, cu_seqlens=None, **kw):
+    """The same forward pass evaluated token by token (kda_fwd_recurrent): for the decode
+    step (one token per sequence, state in and out) and other short sequences.  Same
+    arguments and keywords as ``fwd``; stage_events takes 3 handles here (before the chunk
+    table, before the recurrent kernel, after it; kda_fwd_recurrent_timed)."""
+    return fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+               final_state, cu_seqlens, _recurrent=True, **kw)
+
+
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
         final_state=None, cu_seqlens=None, *, cu_seqlens_host=None, workspace=None, stream=None,
         stage_events=None, use_gate_in_kernel=True, use_qk_l2norm_in_kernel=True,
-        use_beta_sigmoid_in_kernel=True):
+        use_beta_sigmoid_in_kernel=True, _recurrent=False):
     """KDA forward pass on torch device tensors; writes ``out`` and ``final_state`` in place.
 
     q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; out: bf16 [B, T, H, 128];
@@ -180,7 +196,13 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             _ptr(cu_seqlens), None if host_cu is None else host_cu.ctypes.data,
             B, T, H, N if cu_seqlens is not None else B, K, V, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(stream, q.device))
-    if stage_events is None:
+    if _recurrent:
+        if stage_events is None:
+            st = L.kda_fwd_recurrent(*args, flags)
+        else:
+            evs = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(int(e)) for e in stage_events[:3]])
+            st = L.kda_fwd_recurrent_timed(*args, flags, evs)
+    elif stage_events is None:
         st = L.kda_fwd(*args) if flags == ALL_IN_KERNEL else L.kda_fwd_ex(*args, flags)
     else:
         if flags != ALL_IN_KERNEL:

@@ -199,11 +199,13 @@ CONFIG_NAMES = [
     "varlen_N8_Lmax8192_H32_bf16state_lb-2",
     "B1_T1048576_H8_fp32state",
     "varlen_N256_Lmax512_H32_fp32state",
+    "decode_B256_T1_H32_fp32state",
 ]
 
 
 def config(i: int) -> Workload:
-    """The five reference workloads (index 0..4)."""
+    """The five reference workloads (index 0..4), and a decode step (index 5: 256 sequences,
+    one token each, 32 heads, fp32 state in and out)."""
     seeds = np.random.SeedSequence([i, 0]).spawn(9)
     name = CONFIG_NAMES[i]
     if i == 0:
@@ -219,4 +221,6 @@ def config(i: int) -> Workload:
     if i == 4:
         L, seeds = _lengths(4, 256, 512)
         return make(name, 1, 0, 32, lengths=L, state_dtype=STATE_FP32, seeds=seeds)
+    if i == 5:
+        return make(name, 256, 1, 32, state_dtype=STATE_FP32, seeds=seeds)
     raise ValueError(i)

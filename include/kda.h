@@ -138,6 +138,42 @@ kda_status kda_fwd_ex(const void *q, const void *k, const void *v, const void *g
                       uint32_t flags);
 
 /*
+ * kda_fwd_recurrent -- the same forward pass evaluated token by token (the recurrence the
+ * FlashKDA article index calls the linear-time recurrence), for short sequences: the decode
+ * step (one token per sequence, state in and out, often in place) and sequences of a few
+ * tokens.  Same arguments, layouts, ownership, errors and activation switches as kda_fwd_ex,
+ * and the same workspace (kda_fwd_workspace_size).  One workgroup per (sequence, head)
+ * keeps the 128 x 128 state in fp32 registers and walks the sequence's tokens in order, so
+ * its time grows with the longest sequence; for sequences longer than a few chunks use
+ * kda_fwd.  Results agree with kda_fwd to the same tolerance against the fp64 recurrence
+ * (this path is all fp32; kda_fwd uses split-bf16 matrix products).
+ */
+kda_status kda_fwd_recurrent(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                             float scale, void *out, const float *A_log, const float *dt_bias,
+                             float lower_bound, const void *initial_state,
+                             kda_state_dtype initial_state_dtype, void *final_state,
+                             kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                             const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                             int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
+                             uint32_t flags);
+
+/*
+ * kda_fwd_recurrent_timed -- kda_fwd_recurrent with stage timing, for measurement: three
+ * hipEvent_t handles (created by the caller) recorded on `stream` before the chunk-table
+ * kernel, before the recurrent kernel and after it.  Returns KDA_ERR_NULL if any of the
+ * three is NULL.
+ */
+kda_status kda_fwd_recurrent_timed(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, float scale, void *out, const float *A_log,
+                                   const float *dt_bias, float lower_bound, const void *initial_state,
+                                   kda_state_dtype initial_state_dtype, void *final_state,
+                                   kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                                   const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H,
+                                   int64_t N, int64_t K, int64_t V, void *workspace,
+                                   size_t workspace_bytes, void *stream, uint32_t flags,
+                                   void *const *stage_events);
+
+/*
  * kda_fwd_timed -- kda_fwd with stage timing, for measurement.  Same arguments and behaviour
  * as kda_fwd, plus stage_events: five hipEvent_t handles (created by the caller), recorded
  * on `stream`:

@@ -54,7 +54,7 @@ def final_tensor(w, fill=None):
 
 
 def run_gpu(w, d=None, out_fill=None, final_fill=None, workspace=None, h0=None, final=None,
-            keep_device=False):
+            keep_device=False, recurrent=False):
     """One kda_fwd call.  Returns (out, final, workspace) -- host float64 arrays unless keep_device."""
     import torch
     if d is None:
@@ -64,7 +64,8 @@ def run_gpu(w, d=None, out_fill=None, final_fill=None, workspace=None, h0=None, 
         out.fill_(out_fill)
     fin = final if final is not None else final_tensor(w, final_fill)
     h0t = d["h0"] if h0 is None else h0
-    ws = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, out, d["A_log"], d["dt_bias"],
+    entry = kda.fwd_recurrent if recurrent else kda.fwd
+    ws = entry(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, out, d["A_log"], d["dt_bias"],
                  w.lower_bound, h0t, fin, d["cu"], workspace=workspace,
                  use_gate_in_kernel=bool(w.flags & 1), use_qk_l2norm_in_kernel=bool(w.flags & 2),
                  use_beta_sigmoid_in_kernel=bool(w.flags & 4))
