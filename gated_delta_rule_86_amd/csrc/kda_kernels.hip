@@ -36,6 +36,7 @@ namespace kda {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -297,6 +298,15 @@ __device__ __forceinline__ float row_scan16(float x)
     return __fadd_rn(x, dpp_row_shr(x, 8));
 }
 
+// Value of lane I of this lane's quad (DPP quad_perm [I, I, I, I]).  With a single use
+// the move folds into that instruction's DPP source operand.
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x)
+{
+    const int v = __builtin_bit_cast(int, x);
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, I * 0x55, 0xf, 0xf, true));
+}
+
 __device__ __forceinline__ float dpp_row_last(float x)
 {
     int v = __builtin_bit_cast(int, x);
@@ -351,8 +361,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 constexpr int kBlkKG = 0;       // K^*Gamma (hi), bf16, [4 channel pairs][64 lanes][8]
 constexpr int kBlkKGL = 4096;   // K^*Gamma (lo), same layout
 constexpr int kBlkQG = 8192;    // scale*q^*Gamma, bf16, same layout
-constexpr int kBlkKD = 12288;   // K^*gamma/Gamma (hi, lo bf16), [8 channel tiles][64 lanes][4+4]
-constexpr int kBlkGAM = 20480;  // gamma = Gamma at the chunk's last token, fp32 [128]
+constexpr int kBlkKD = 12288;   // K^*gamma/Gamma (hi, lo bf16), [8 channel tiles][4 token groups][16 slots, swizzled][4+4]
+constexpr int kBlkGAM = 20480;  // gamma = Gamma at the chunk's last token, fp32 [16][8]: channel 16t + j at 8j + t
 constexpr int kBlkTB = 20992;   // T*diag(beta) (hi, lo bf16), [64 lanes][4+4]
 constexpr int kBlkMQ = 22016;   // A_qk*T*diag(beta) (hi, lo bf16), [64 lanes][4+4]
 constexpr int kBlkBytes = 23040;
@@ -368,7 +378,7 @@ constexpr int kOffOut = kOffDt + 512;               // per consumer: one output 
 constexpr int kOffFlags = kOffOut + 4 * 1024;
 constexpr int kFusedLds = kOffFlags + 128;
 static_assert(kFusedLds <= 160 * 1024, "LDS budget");
-static_assert(kBlkBytes % 16 == 0, "slot alignment");
+static_assert(kBlkBytes % 256 == 0 && kBlkKD % 256 == 0, "slot alignment (the KD swizzle XORs address bits 4-7)");
 constexpr int32_t kStatusSpin = 0x100;
 constexpr int kGateIn = 1, kL2In = 2, kSigIn = 4;
 constexpr int kSpinMax = 1 << 22;
@@ -812,22 +822,32 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             *reinterpret_cast<u32x4_t *>(rec + kBlkKGL + o) = kgl[gg];
             *reinterpret_cast<u32x4_t *>(rec + kBlkQG + o) = qgh[gg];
         }
-        // KD: tile ct = ch/16, lane position ch%16 + 16*(r/4), token r%4 of the hi and lo
-        // quarters of the 16-byte fragment
+        // KD: channel ch = 32qb + c goes to tile ch/16, token group r/4, token r%4 of the
+        // hi and lo quarters of a 16-byte fragment.  In tile t and token group gq the
+        // fragment of channel position j sits at 16-byte slot j ^ (4gq + t/2) of the
+        // group's 256-byte row: the 16 lanes (qb, r/4) that write one channel hit 16
+        // different slots, so the 2-byte stores meet no bank conflicts, and a consumer's
+        // 16-lane group still reads the 16 slots of one row.  Every term of the address
+        // but the slot index is a multiple of 256 or below 16, so the XOR acts on bits 4-7.
+        {
+            const uint32_t kd0 = (uint32_t)(rec - lds) + (uint32_t)kBlkKD + 2048u * (uint32_t)qb +
+                                 256u * (uint32_t)(r >> 2) + 2u * (uint32_t)(r & 3) +
+                                 16u * (uint32_t)(4 * (r >> 2) + qb);
 #pragma unroll
-        for (int c = 0; c < 32; ++c) {
-            const int ch = 32 * qb + c;
-            const int o = (int)kBlkKD + (((ch >> 4) * 64 + (ch & 15) + 16 * (r >> 2)) * 16) + 2 * (r & 3);
-            const uint32_t word = (c & 1) ? kdb[c >> 3][(c & 7) >> 1] >> 16 : kdb[c >> 3][(c & 7) >> 1] & 0xffffu;
-            const uint32_t wlo = (c & 1) ? kdlo[c >> 3][(c & 7) >> 1] >> 16 : kdlo[c >> 3][(c & 7) >> 1] & 0xffffu;
-            *reinterpret_cast<uint16_t *>(rec + o) = (uint16_t)word;
-            *reinterpret_cast<uint16_t *>(rec + o + 8) = (uint16_t)wlo;
+            for (int c = 0; c < 32; ++c) {
+                const uint32_t o = (kd0 ^ (16u * (uint32_t)(c & 15))) + 1024u * (uint32_t)(c >> 4);
+                const uint32_t word = (c & 1) ? kdb[c >> 3][(c & 7) >> 1] >> 16 : kdb[c >> 3][(c & 7) >> 1] & 0xffffu;
+                const uint32_t wlo = (c & 1) ? kdlo[c >> 3][(c & 7) >> 1] >> 16 : kdlo[c >> 3][(c & 7) >> 1] & 0xffffu;
+                *reinterpret_cast<uint16_t *>(lds + o) = (uint16_t)word;
+                *reinterpret_cast<uint16_t *>(lds + o + 8) = (uint16_t)wlo;
+            }
         }
         if (r == 15) {
-            f32x4_t *gp = reinterpret_cast<f32x4_t *>(rec + kBlkGAM + (size_t)(32 * qb) * 4);
+            // channels 32qb + j and 32qb + 16 + j are tiles 2qb, 2qb + 1 of position j
+            float *gp = reinterpret_cast<float *>(rec + kBlkGAM) + 2 * qb;
 #pragma unroll
-            for (int w = 0; w < 8; ++w)
-                gp[w] = f32x4_t{GL[4 * w], GL[4 * w + 1], GL[4 * w + 2], GL[4 * w + 3]};
+            for (int j = 0; j < 16; ++j)
+                *reinterpret_cast<f32x2_t *>(gp + 8 * j) = f32x2_t{GL[j], GL[16 + j]};
         }
         {
             u32x4_t w;
@@ -943,13 +963,23 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
             *reinterpret_cast<u32x4_t *>(a.out + ((size_t)(start + jo * kCH + orow) * (size_t)H + (size_t)h) * kD +
                                          32 * cw + 8 * (lane & 3)) = ow;
     };
+    int gm_off = 0;
+    __asm__("" : "+v"(gm_off));
+    // KD fragment of channel position col, token group g, tile t: slot col ^ (4g + t/2)
+    int kdo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        kdo[k] = 256 * g + 16 * (col ^ (4 * g + k));
     for (int64_t j = c0; j < c1; ++j) {
         const int iu = (int)(j - c0);  // item index within the unit (value ring, store count)
         const int it = it0 + iu;       // item index within the workgroup (operand slots)
         const int s = it % kNS;
         const unsigned char *rec = lds + (size_t)s * kBlkBytes;
         u32x4_t kg[4], kgl[4], qg[4], kd[8];
-        f32x4_t gm[8];
+        // gamma of channel 16t + 4g + (lane & 3) is gm[b][t / 4][t % 4]; each column block b
+        // has its own copy, so every quad broadcast below has one use and folds into its
+        // multiply (gm_off is an opaque zero that keeps the two reads apart)
+        f32x4_t gm[2][2];
         u32x4_t tb, mq;
         // The operand reads go out right behind the read of ready[s]; LDS serves one
         // wavefront's requests in order, so when that read shows chunk j the operands
@@ -963,8 +993,10 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                kd[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKD + (t * 64 + lane) * 16);
-                gm[t] = *reinterpret_cast<const f32x4_t *>(rec + kBlkGAM + (16 * t + 4 * g) * 4);
+                kd[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKD + t * 1024 + kdo[t >> 1]);
+                if (t < 4)
+                    gm[t >> 1][t & 1] = *reinterpret_cast<const f32x4_t *>(
+                        rec + kBlkGAM + (8 * (4 * g + (col & 3)) + 4 * (t & 1)) * 4 + ((t >> 1) ? gm_off : 0));
             }
             tb = *reinterpret_cast<const u32x4_t *>(rec + kBlkTB + lane * 16);
             mq = *reinterpret_cast<const u32x4_t *>(rec + kBlkMQ + lane * 16);
@@ -1053,7 +1085,10 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
             // S <- S diag(gamma) + KD^T V': [KD_hi | KD_lo] [V'_hi ; V'_hi] + [KD_hi | KD_lo] [V'_lo ; 0]
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                f32x4_t st = S[b][t] * gm[t];
+                // element i is channel 16t + 4g + i: its gamma sits in lane i of this quad
+                const float gt = gm[b][t >> 2][t & 3];
+                f32x4_t st = {S[b][t][0] * quad_bcast<0>(gt), S[b][t][1] * quad_bcast<1>(gt),
+                              S[b][t][2] * quad_bcast<2>(gt), S[b][t][3] * quad_bcast<3>(gt)};
                 st = mfma32(kd[t], vhh, st);
                 st = mfma32(kd[t], vl0, st);
                 S[b][t] = st;
