@@ -594,8 +594,10 @@ __device__ __forceinline__ void dma_tile16(__amdgpu_buffer_rsrc_t r, unsigned ch
 }
 
 // kSw: the activation switches are read from a.flags; without it every activation runs in
-// the pass (the common case gets code with no switch logic in it).
-template <bool kSw>
+// the pass (the common case gets code with no switch logic in it).  kQ: the workgroup's
+// units write output rows; without it (the F and P runs of a segment) q is neither loaded
+// nor used, and the output-only operands (QG, Mq) are not formed.
+template <bool kSw, bool kQ>
 __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int p, int lane)
 {
     const int64_t H = a.H;
@@ -633,7 +635,8 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             const uint32_t seg = (uint32_t)(lane & 15) ^ (row & 7u);
             vo[i] = row * rowb + seg * 16u - 1024u * i;  // row * rowb >= 1024 i: rowb >= 256
         }
-        dma_tile16(rq, stage, vo);
+        if (kQ)
+            dma_tile16(rq, stage, vo);
         dma_tile16(rk, stage + 4096, vo);
         dma_tile16(rg, stage + 8192, vo);
         // (the byte count is wave-uniform; say so, or the descriptor goes through a
@@ -680,13 +683,14 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             const u32x4_t ug = *reinterpret_cast<const u32x4_t *>(stage + 8192 + o);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                qf[8 * w + 2 * e] = bf_lo(uq[e]);
-                qf[8 * w + 2 * e + 1] = bf_hi(uq[e]);
+                qf[8 * w + 2 * e] = kQ ? bf_lo(uq[e]) : 0.f;
+                qf[8 * w + 2 * e + 1] = kQ ? bf_hi(uq[e]) : 0.f;
                 kf[8 * w + 2 * e] = bf_lo(uk[e]);
                 kf[8 * w + 2 * e + 1] = bf_hi(uk[e]);
                 gf[8 * w + 2 * e] = bf_lo(ug[e]);
                 gf[8 * w + 2 * e + 1] = bf_hi(ug[e]);
-                ssq = dot2_bf16(uq[e], uq[e], ssq);
+                if (kQ)
+                    ssq = dot2_bf16(uq[e], uq[e], ssq);
                 ssk = dot2_bf16(uk[e], uk[e], ssk);
             }
         }
@@ -782,7 +786,8 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             akk = mfma32(kgh[gg], kih[gg], akk);
             akk = mfma32(kgl[gg], kih[gg], akk);
             akk = mfma32(kgh[gg], kil[gg], akk);
-            aqkT = mfma32(kih[gg], qgh[gg], aqkT);
+            if (kQ)
+                aqkT = mfma32(kih[gg], qgh[gg], aqkT);
         }
         const int g4 = (lane >> 4) * 4, col = lane & 15;
         f32x4_t A, AqT, I4;
@@ -804,9 +809,10 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
         const f32x4_t R2 = mm16(I4 + P2T, R1);
         const f32x4_t Tm = mm16(I4 - AT, R2);
         const f32x4_t Tb = Tm * bt;
-        const f32x4_t Mq = mm16(AqT, Tb);
         const f32x4_t TbT = transpose16(Tb, tile, lane);
-        const f32x4_t MqT = transpose16(Mq, tile, lane);
+        f32x4_t MqT = {0.f, 0.f, 0.f, 0.f};
+        if (kQ)
+            MqT = transpose16(mm16(AqT, Tb), tile, lane);
 
         // ---- hand the operand block to the consumers ----
         const int s = it % kNS;
@@ -820,7 +826,8 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             const int o = (qb * 64 + r + 16 * gg) * 16;
             *reinterpret_cast<u32x4_t *>(rec + kBlkKG + o) = kgh[gg];
             *reinterpret_cast<u32x4_t *>(rec + kBlkKGL + o) = kgl[gg];
-            *reinterpret_cast<u32x4_t *>(rec + kBlkQG + o) = qgh[gg];
+            if (kQ)
+                *reinterpret_cast<u32x4_t *>(rec + kBlkQG + o) = qgh[gg];
         }
         // KD: channel ch = 32qb + c goes to tile ch/16, token group r/4, token r%4 of the
         // hi and lo quarters of a 16-byte fragment.  In tile t and token group gq the
@@ -858,6 +865,8 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
             w[2] = pack_bf16x2(TbT[0] - h0, TbT[1] - h1);
             w[3] = pack_bf16x2(TbT[2] - h2, TbT[3] - h3);
             *reinterpret_cast<u32x4_t *>(rec + kBlkTB + (size_t)lane * 16) = w;
+        }
+        if (kQ) {
             const float m0 = bf16f(to_bf16(MqT[0])), m1 = bf16f(to_bf16(MqT[1]));
             const float m2 = bf16f(to_bf16(MqT[2])), m3 = bf16f(to_bf16(MqT[3]));
             u32x4_t m;
@@ -876,6 +885,9 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 
 // One unit's items for consumer wavefront cw: state in, chunk recurrence, state out.
 // Items of the unit are it0, it0+1, ... in the workgroup's item numbering (slots, flags).
+// kOut: the unit writes output rows (u.out_on); without it Y and O are not formed and the
+// output-only operands are not read.
+template <bool kOut>
 __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane,
                              int it0, bool &spun_out)
 {
@@ -989,7 +1001,8 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
             for (int t = 0; t < 4; ++t) {
                 kg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKG + (t * 64 + lane) * 16);
                 kgl[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKGL + (t * 64 + lane) * 16);
-                qg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkQG + (t * 64 + lane) * 16);
+                if (kOut)
+                    qg[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkQG + (t * 64 + lane) * 16);
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -999,7 +1012,8 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
                         rec + kBlkGAM + (8 * (4 * g + (col & 3)) + 4 * (t & 1)) * 4 + ((t >> 1) ? gm_off : 0));
             }
             tb = *reinterpret_cast<const u32x4_t *>(rec + kBlkTB + lane * 16);
-            mq = *reinterpret_cast<const u32x4_t *>(rec + kBlkMQ + lane * 16);
+            if (kOut)
+                mq = *reinterpret_cast<const u32x4_t *>(rec + kBlkMQ + lane * 16);
         };
         const int seen = ready[s];
         __asm__ volatile("" ::: "memory");
@@ -1012,7 +1026,7 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
             read_ops();
         }
         // the previous chunk's output tile (staged in LDS) goes to HBM
-        if (u.out_on && iu > 0)
+        if (kOut && iu > 0)
             store_out(j - 1);
 
         // value tile of chunk j: vector-memory operations issued after its ring load are
@@ -1023,7 +1037,7 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         if (u.v_on) {
             const int64_t later = c1 - 1 - j;
             const int nd = later < 2 ? (int)later : 2;
-            const int ns = !u.out_on ? 0 : iu < 3 ? iu : 3;
+            const int ns = !kOut ? 0 : iu < 3 ? iu : 3;
             wait_vmcnt_rt(nd + ns);
             unsigned char *vt = vring + (iu % kNV) * 1024;
 #pragma unroll
@@ -1061,7 +1075,8 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
                 Z[b] = mfma32(kg[t], sb, Z[b]);
                 Z[b] = mfma32(kgl[t], sb, Z[b]);
                 Z[b] = mfma32(kg[t], sl, Z[b]);
-                Y[b] = mfma32(qg[t], sb, Y[b]);
+                if (kOut)
+                    Y[b] = mfma32(qg[t], sb, Y[b]);
             }
         }
         f32x4_t O[2];
@@ -1093,21 +1108,24 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
                 st = mfma32(kd[t], vl0, st);
                 S[b][t] = st;
             }
-            O[b] = mfma32(mq, xhh, Y[b]);
+            if (kOut)
+                O[b] = mfma32(mq, xhh, Y[b]);
         }
 
         // output rows 4g+i, columns 16b+col -> LDS tile; the next iteration (or the end)
         // stores it with one 16-byte write per lane: row L/4, columns 8*(L%4) .. +7
+        if (kOut) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint16_t *>(obuf + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<uint16_t *>(obuf + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
+        }
         // every operand of chunk j is in registers (used above): release the slot
         if (lane == 0)
             taken[4 * s + cw] = it / kNS + 1;
     }
-    if (u.out_on && c1 > c0) {
+    if (kOut && c1 > c0) {
         wait_lgkmcnt0();
         store_out(c1 - 1);
     }
@@ -1140,7 +1158,10 @@ __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned cha
     for (int64_t k = 0; unit_at(a, w, k, u); ++k) {
         // the previous unit's stores are done before this unit's value-ring bookkeeping starts
         wait_vmcnt<0>();
-        consume_unit(a, u, lds, cw, lane, it0, spun_out);
+        if (u.out_on)
+            consume_unit<true>(a, u, lds, cw, lane, it0, spun_out);
+        else
+            consume_unit<false>(a, u, lds, cw, lane, it0, spun_out);
         it0 += (int)(u.c1 - u.c0);
     }
 }
@@ -1195,7 +1216,10 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     }
     __syncthreads();
     if (wave < 4) {
-        fused_producer<kSw>(a, w, lds, wave, lane);
+        if (w.pass == 1 && w.kind != 0)
+            fused_producer<kSw, false>(a, w, lds, wave, lane);
+        else
+            fused_producer<kSw, true>(a, w, lds, wave, lane);
     } else {
         // The consumers set the pace (producers finish ahead and wait for free slots), so
         // they get issue priority over the producer sharing their SIMD.
