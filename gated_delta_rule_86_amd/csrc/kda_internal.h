@@ -53,15 +53,30 @@ inline SegPlan plan_segments(int64_t chains, int64_t nch)
     return best;
 }
 
+// Column halves.  When a head has few workgroups and few sequences, the chunk table may run
+// a long sequence as two units of 64 value columns each: the producer work per chunk is
+// the same, the consumers' halves, and a half unit takes about 0.82 of a whole one.  The
+// units of a head then go to its workgroups longest first, each to the least loaded one.
+constexpr int64_t kSplitMaxP = 16;     // at most this many workgroups per head
+constexpr int64_t kSplitMaxSeq = 32;   // at most this many sequences
+constexpr int kSplitMaxK = 8;          // at most this many sequences split
+constexpr int64_t kWholeW = 100, kHalfW = 82;
+
+inline bool split_eligible(int64_t H, int64_t n_seq)
+{
+    return kPlanCUs / H <= kSplitMaxP && n_seq <= kSplitMaxSeq;
+}
+
 // Workgroups per head of the whole-chain launch: about one workgroup per CU over all
-// heads, never more than the sequences.
+// heads, never more than the units (the sequences, or twice that where halves may be used).
 inline int64_t whole_chain_groups(int64_t H, int64_t n_seq)
 {
     int64_t p = kPlanCUs / H;
     if (p < 1)
         p = 1;
-    if (p > n_seq)
-        p = n_seq;
+    const int64_t units = split_eligible(H, n_seq) ? 2 * n_seq : n_seq;
+    if (p > units)
+        p = units;
     return p < 1 ? 1 : p;
 }
 
@@ -69,7 +84,8 @@ struct Layout {
     int64_t n_seq;     // N (or B without cu_seqlens)
     size_t off_status; // int32 status word; int64 n_total at +8
     size_t off_seq_start, off_seq_len, off_seq_off;
-    size_t off_wg;     // int64 [kPlanCUs + 1]: first sequence of each whole-chain workgroup of a head
+    size_t off_wg;     // int64 [kPlanCUs + 1]: first unit of each whole-chain workgroup of a head
+    size_t off_units;  // int32 [2 N]: whole-chain units, (sequence << 2) | (0 whole, 1 + column half)
     SegPlan seg;       // segment plan (G == 1 without segmentation)
     size_t off_seg;    // fp32 states S, F, P: 3 x [chains][G][128][128] when G > 1
     size_t total;
@@ -88,6 +104,8 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
             return false;
         N = B;
     }
+    if (N >= ((int64_t)1 << 29))  // unit codes hold the sequence index in 29 bits
+        return false;
     L->n_seq = N;
     size_t off = 0;
     L->off_status = off;
@@ -100,6 +118,8 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)(N + 1), kAlign);
     L->off_wg = off;
     off = round_up(off + sizeof(int64_t) * (size_t)(kPlanCUs + 1), kAlign);
+    L->off_units = off;
+    off = round_up(off + sizeof(int32_t) * 2 * (size_t)N, kAlign);
     L->seg = varlen ? SegPlan{1, 0} : plan_segments(N * H, cdiv(T, kCH));
     L->off_seg = off;
     if (L->seg.G > 1)

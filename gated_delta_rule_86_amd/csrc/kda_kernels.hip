@@ -119,7 +119,9 @@ struct TableArgs {
     int32_t *status;
     int64_t *n_total;
     int64_t *seq_start, *seq_len, *seq_off;
-    int64_t *wg_first;  // [P + 1]
+    int64_t *wg_first;  // [P + 1]: first unit of each whole-chain workgroup of a head
+    int32_t *units;     // [2 N]: (sequence << 2) | (0 whole, 1 + column half)
+    int split;          // whole-chain pass that may split sequences into column halves
 };
 
 __device__ void chunk_table_body(const TableArgs &a, int tid);
@@ -142,6 +144,7 @@ __device__ void partition_sequences(const TableArgs &a, int tid)
         return g < a.P - 1 ? g : a.P - 1;
     };
     for (int64_t i = tid; i < a.N; i += 256) {
+        a.units[i] = (int32_t)(i << 2);
         const int64_t lo = i == 0 ? 0 : group_of(i - 1) + 1;
         const int64_t hi = group_of(i);
         for (int64_t g = lo; g <= hi; ++g)
@@ -154,10 +157,114 @@ __device__ void partition_sequences(const TableArgs &a, int tid)
     }
 }
 
+// Whole-chain plan with column halves (see split_eligible): N <= kSplitMaxSeq sequences,
+// P <= kSplitMaxP workgroups per head.  Thread k (k = 0 .. min(N, kSplitMaxK)) packs the
+// head's units when the k longest sequences run as two column halves each: units are taken
+// by weight, heaviest first (whole 100 n, half 82 n for n chunks; a tie takes the half
+// first, sequences of equal length go by index), each to the least loaded workgroup (the
+// lowest index among equals).  The k with the smallest largest load wins (the smallest k
+// among equals); its units replace the contiguous runs, workgroup s taking units
+// wg_first[s] .. wg_first[s+1]-1 in packing order.
+__device__ void plan_halves(const TableArgs &a, int tid)
+{
+    constexpr int kU = 2 * (int)kSplitMaxSeq;
+    __shared__ int64_t s_w[kSplitMaxSeq];  // chunk count of the sequence of rank r (longest first)
+    __shared__ int s_ord[kSplitMaxSeq];    // sequence of rank r
+    __shared__ int64_t s_mk[kSplitMaxK + 1];
+    __shared__ int s_code[kSplitMaxK + 1][kU];           // unit u of plan k: (seq << 2) | code
+    __shared__ unsigned char s_bin[kSplitMaxK + 1][kU];  // its workgroup
+    __shared__ int64_t s_n[kSplitMaxSeq];  // chunk count of sequence i
+    __shared__ int s_best;
+    const int N = (int)a.N, P = (int)a.P;
+    __syncthreads();
+    if (tid < N)
+        s_n[tid] = a.seq_off[tid + 1] - a.seq_off[tid];
+    __syncthreads();
+    if (tid < N) {
+        const int64_t n = s_n[tid];
+        int rank = 0;
+        for (int j = 0; j < N; ++j)
+            rank += s_n[j] > n || (s_n[j] == n && j < tid);
+        s_ord[rank] = tid;
+        s_w[rank] = n;
+    }
+    __syncthreads();
+    const int K = N < kSplitMaxK ? N : kSplitMaxK;
+    if (tid <= K) {
+        const int k = tid;
+        int64_t load[kSplitMaxP];  // constant indices only: stays in registers
+#pragma unroll
+        for (int b = 0; b < kSplitMaxP; ++b)
+            load[b] = 0;
+        int hi = 0, wi = k, u = 0;  // next half (0 .. 2k-1), next whole rank (k .. N-1)
+        while (hi < 2 * k || wi < N) {
+            const int64_t wh = hi < 2 * k ? kHalfW * s_w[hi >> 1] : -1;
+            const int64_t ww = wi < N ? kWholeW * s_w[wi] : -1;
+            int code;
+            int64_t w;
+            if (wh >= ww) {
+                code = (s_ord[hi >> 1] << 2) | (1 + (hi & 1));
+                w = wh;
+                ++hi;
+            } else {
+                code = s_ord[wi] << 2;
+                w = ww;
+                ++wi;
+            }
+            int best = 0;
+            int64_t lmin = load[0];
+#pragma unroll
+            for (int b = 1; b < kSplitMaxP; ++b)
+                if (b < P && load[b] < lmin) {
+                    lmin = load[b];
+                    best = b;
+                }
+#pragma unroll
+            for (int b = 0; b < kSplitMaxP; ++b)
+                if (b == best)
+                    load[b] += w;
+            s_code[k][u] = code;
+            s_bin[k][u] = (unsigned char)best;
+            ++u;
+        }
+        int64_t mk = 0;
+#pragma unroll
+        for (int b = 0; b < kSplitMaxP; ++b)
+            mk = b < P && load[b] > mk ? load[b] : mk;
+        s_mk[k] = mk;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int best = 0;
+        for (int k = 1; k <= K; ++k)
+            if (s_mk[k] < s_mk[best])
+                best = k;
+        s_best = best;
+    }
+    __syncthreads();
+    const int best = s_best, U = N + best;
+    if (tid < U) {
+        // position: units of lower workgroups, then earlier units of this one
+        const int b = s_bin[best][tid];
+        int pos = 0;
+        for (int v = 0; v < U; ++v)
+            pos += s_bin[best][v] < b || (s_bin[best][v] == b && v < tid);
+        a.units[pos] = s_code[best][tid];
+    }
+    if (tid <= P) {
+        int first = 0;
+        for (int v = 0; v < U; ++v)
+            first += s_bin[best][v] < tid;
+        a.wg_first[tid] = first;
+    }
+}
+
 __global__ __launch_bounds__(256) void chunk_table_kernel(TableArgs a)
 {
     chunk_table_body(a, threadIdx.x);
     partition_sequences(a, threadIdx.x);
+    if (a.split && a.N <= kSplitMaxSeq && a.P <= kSplitMaxP)
+        plan_halves(a, threadIdx.x);
 }
 
 __device__ void chunk_table_body(const TableArgs &a, int tid)
@@ -394,7 +501,8 @@ struct FusedArgs {
     int h0_dtype, ht_dtype;
     int64_t H, N;
     const int64_t *seq_start, *seq_len;
-    const int64_t *wg_first;  // whole-chain pass: first sequence of each workgroup of a head
+    const int64_t *wg_first;  // whole-chain pass: first unit of each workgroup of a head
+    const int32_t *units;     // whole-chain units: (sequence << 2) | (0 whole, 1 + column half)
     int32_t *status;
     // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B (see SegPlan)
     int pass, G;
@@ -415,15 +523,17 @@ struct Unit {
     void *fin;            // 128 x 128 block
     bool v_on;            // false: v taken as zero (the P run of a segment)
     bool out_on;          // write out rows of this range
+    int half;             // -1: all 128 value columns; 0 / 1: columns 64*half .. 64*half+63
 };
 
-// A workgroup's work: one unit (segment passes), or -- whole-chain pass -- the chains
-// (n, h) for n = sub, sub + 1, ... < n_end of one head h, one after another.  The
-// producers then run ahead into the next chain while the consumers finish the current one.
+// A workgroup's work: one unit (segment passes), or -- whole-chain pass -- the units
+// sub, sub + 1, ... < n_end of the unit list (chains (n, h) of one head h, whole or one
+// column half), one after another.  The producers then run ahead into the next unit
+// while the consumers finish the current one.
 struct WgPlan {
     int pass;
     int h;
-    int64_t sub, n_end;   // whole-chain pass: sequences sub, sub + 1, ... < n_end
+    int64_t sub, n_end;   // whole-chain pass: units sub, sub + 1, ... < n_end
     int64_t n;            // segment passes: the sequence
     int seg;              // segment passes: the segment
     int kind;             // pass A: 0 exact segment 0, 1 F run, 2 P run
@@ -433,10 +543,13 @@ __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
 {
     constexpr int64_t kBlock = (int64_t)kD * kD;
     int64_t n;
+    u.half = -1;
     if (w.pass == 0) {
-        n = w.sub + k;
-        if (n >= w.n_end)
+        if (w.sub + k >= w.n_end)
             return false;
+        const int32_t code = a.units[w.sub + k];
+        n = code >> 2;
+        u.half = (code & 3) - 1;
     } else {
         if (k > 0)
             return false;
@@ -498,9 +611,9 @@ __device__ bool range_at(const FusedArgs &a, const WgPlan &w, int64_t k, Range &
 {
     int64_t n, seg = 0;
     if (w.pass == 0) {
-        n = w.sub + k;
-        if (n >= w.n_end)
+        if (w.sub + k >= w.n_end)
             return false;
+        n = a.units[w.sub + k] >> 2;
     } else {
         if (k > 0)
             return false;
@@ -886,11 +999,15 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 // One unit's items for consumer wavefront cw: state in, chunk recurrence, state out.
 // Items of the unit are it0, it0+1, ... in the workgroup's item numbering (slots, flags).
 // kOut: the unit writes output rows (u.out_on); without it Y and O are not formed and the
-// output-only operands are not read.
-template <bool kOut>
+// output-only operands are not read.  NB: 16-column blocks of this wave -- 2 for a whole
+// unit (columns 32cw .. 32cw+31), 1 for a column half (64*half + 16cw .. +15).
+template <bool kOut, int NB>
 __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane,
                              int it0, bool &spun_out)
 {
+    const int cb0 = NB == 2 ? 32 * cw : 64 * u.half + 16 * cw;  // first value column of this wave
+    constexpr int kRowB = 32 * NB;   // bytes per token row of this wave's value and output tiles
+    constexpr int kLpr = kRowB / 16; // lanes per row of 16 bytes each
     const int64_t H = a.H;
     const int h = u.h;
     const int64_t start = u.start, len = u.len, c0 = u.c0, c1 = u.c1;
@@ -901,21 +1018,21 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     unsigned char *vring = lds + kOffVring + cw * (kNV * 1024);
     const uint32_t rowb = (uint32_t)(H * kD * 2);
 
-    // state: S[b][t] = S[v][16t + 4g + i] (element i) for value column v = 32cw + 16b + col
-    f32x4_t S[2][8];
+    // state: S[b][t] = S[v][16t + 4g + i] (element i) for value column v = cb0 + 16b + col
+    f32x4_t S[NB][8];
     {
-        const int64_t sb0 = (int64_t)(32 * cw + col) * kD + 4 * g;  // column block b adds 16*128
+        const int64_t sb0 = (int64_t)(cb0 + col) * kD + 4 * g;  // column block b adds 16*128
         if (u.init_kind == kInitFp32) {
             const float *p = reinterpret_cast<const float *>(u.init) + sb0;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
                     S[b][t] = *reinterpret_cast<const f32x4_t *>(p + b * 16 * kD + 16 * t);
         } else if (u.init_kind == kInitBf16) {
             const uint16_t *p = reinterpret_cast<const uint16_t *>(u.init) + sb0;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const u32x2_t w = *reinterpret_cast<const u32x2_t *>(p + b * 16 * kD + 16 * t);
@@ -923,19 +1040,19 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
                 }
         } else {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
                     S[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (u.init_kind == kInitIdentity) {
-                // S[v][v] = 1: column v = 32cw + 16b + col sits in channel tile 2cw + b,
+                // S[v][v] = 1: column v = cb0 + 16b + col sits in channel tile cb0/16 + b,
                 // element col - 4g of this lane when that lies in [0, 4)
                 const int e = col - 4 * g;
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int t = 0; t < 8; ++t)
-                        if (t == 2 * cw + b) {
+                        if (t == cb0 / 16 + b) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 S[b][t][i] = e == i ? 1.f : 0.f;
@@ -944,15 +1061,16 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         }
     }
 
-    // value tile of chunk j (16 tokens x this wave's 32 columns, row-major 64 B rows) into
-    // ring slot j % kNV: lane L loads row L/4, bytes 16*(L%4); rows past the end load zeros
+    // value tile of chunk j (16 tokens x this wave's 16 NB columns, row-major kRowB-byte rows)
+    // into ring slot j % kNV: lane L loads row L/kLpr, bytes 16*(L%kLpr); rows past the end
+    // (also rows 16 .. 31 when NB = 1) load zeros
     auto issue_v = [&](int64_t j) {
         const int64_t t0 = start + j * kCH;
         const int64_t rem = len - j * kCH;
         const int tl = rem < kCH ? (int)rem : kCH;
         const __amdgpu_buffer_rsrc_t rv =
-            make_rsrc(a.v + ((size_t)t0 * (size_t)H + (size_t)h) * kD + 32 * cw, (uint32_t)(tl - 1) * rowb + 64u);
-        const uint32_t vo = (uint32_t)(lane >> 2) * rowb + (uint32_t)(lane & 3) * 16u;
+            make_rsrc(a.v + ((size_t)t0 * (size_t)H + (size_t)h) * kD + cb0, (uint32_t)(tl - 1) * rowb + (uint32_t)kRowB);
+        const uint32_t vo = (uint32_t)(lane / kLpr) * rowb + (uint32_t)(lane % kLpr) * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vring + ((int)(j - c0) % kNV) * 1024), 16, vo, 0, 0, 0);
     };
     if (u.v_on) {
@@ -967,13 +1085,13 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     u32x4_t negI0, negI1;
     make_neg_identity(lane, negI0, negI1);
     unsigned char *obuf = lds + kOffOut + cw * 1024;  // output tile of the previous chunk
-    const int orow = lane >> 2;                        // output row this lane stores
+    const int orow = lane / kLpr;                      // output row this lane stores
     auto store_out = [&](int64_t jo) {
         const int64_t rem = len - jo * kCH;
         const u32x4_t ow = *reinterpret_cast<const u32x4_t *>(obuf + lane * 16);
         if (orow < rem)
             *reinterpret_cast<u32x4_t *>(a.out + ((size_t)(start + jo * kCH + orow) * (size_t)H + (size_t)h) * kD +
-                                         32 * cw + 8 * (lane & 3)) = ow;
+                                         cb0 + 8 * (lane % kLpr)) = ow;
     };
     int gm_off = 0;
     __asm__("" : "+v"(gm_off));
@@ -991,7 +1109,7 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         // gamma of channel 16t + 4g + (lane & 3) is gm[b][t / 4][t % 4]; each column block b
         // has its own copy, so every quad broadcast below has one use and folds into its
         // multiply (gm_off is an opaque zero that keeps the two reads apart)
-        f32x4_t gm[2][2];
+        f32x4_t gm[NB][2];
         u32x4_t tb, mq;
         // The operand reads go out right behind the read of ready[s]; LDS serves one
         // wavefront's requests in order, so when that read shows chunk j the operands
@@ -1007,7 +1125,7 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 kd[t] = *reinterpret_cast<const u32x4_t *>(rec + kBlkKD + t * 1024 + kdo[t >> 1]);
-                if (t < 4)
+                if (t < 2 * NB)
                     gm[t >> 1][t & 1] = *reinterpret_cast<const f32x4_t *>(
                         rec + kBlkGAM + (8 * (4 * g + (col & 3)) + 4 * (t & 1)) * 4 + ((t >> 1) ? gm_off : 0));
             }
@@ -1033,7 +1151,12 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         // the ring loads of chunks j+1, j+2 (those in range) and, when out is written, the
         // output stores of the items max(0, it-3) .. it-1 (one store instruction each; its
         // lanes for row 0 are always active)
-        float vv[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        float vv[NB][4];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vv[b][i] = 0.f;
         if (u.v_on) {
             const int64_t later = c1 - 1 - j;
             const int nd = later < 2 ? (int)later : 2;
@@ -1041,10 +1164,10 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
             wait_vmcnt_rt(nd + ns);
             unsigned char *vt = vring + (iu % kNV) * 1024;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    vv[b][i] = bf16f(*reinterpret_cast<const uint16_t *>(vt + (4 * g + i) * 64 + (16 * b + col) * 2));
+                    vv[b][i] = bf16f(*reinterpret_cast<const uint16_t *>(vt + (4 * g + i) * kRowB + (16 * b + col) * 2));
             // the value slot is read: refill it with chunk j + kNV
             if (j + kNV < c1) {
                 wait_lgkmcnt0();
@@ -1055,16 +1178,16 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         // Z = KG S^T (three products) and Y = QG S^T (one), per channel pair t of tiles
         // (2t, 2t+1).  S splits as hi = bf16(S) and lo = S - hi; the difference is exact in
         // fp32 and one MFMA per tile forms it: (-I) hi + S.
-        f32x4_t Z[2], Y[2];
+        f32x4_t Z[NB], Y[NB];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
             Z[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             Y[b] = Z[b];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 const f32x4_t s0 = S[b][2 * t], s1 = S[b][2 * t + 1];
                 const u32x4_t sb = {pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]),
                                     pack_bf16x2(s1[0], s1[1]), pack_bf16x2(s1[2], s1[3])};
@@ -1079,9 +1202,9 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
                     Y[b] = mfma32(qg[t], sb, Y[b]);
             }
         }
-        f32x4_t O[2];
+        f32x4_t O[NB];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
             f32x4_t X;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -1116,10 +1239,10 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         // stores it with one 16-byte write per lane: row L/4, columns 8*(L%4) .. +7
         if (kOut) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<uint16_t *>(obuf + (4 * g + i) * 64 + (16 * b + col) * 2) = to_bf16(O[b][i]);
+                    *reinterpret_cast<uint16_t *>(obuf + (4 * g + i) * kRowB + (16 * b + col) * 2) = to_bf16(O[b][i]);
         }
         // every operand of chunk j is in registers (used above): release the slot
         if (lane == 0)
@@ -1130,18 +1253,18 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         store_out(c1 - 1);
     }
 
-    const int64_t sb0 = (int64_t)(32 * cw + col) * kD + 4 * g;
+    const int64_t sb0 = (int64_t)(cb0 + col) * kD + 4 * g;
     if (u.fin_kind == 2) {
         float *p = reinterpret_cast<float *>(u.fin) + sb0;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 *reinterpret_cast<f32x4_t *>(p + b * 16 * kD + 16 * t) = S[b][t];
     } else if (u.fin_kind == 1) {
         uint16_t *p = reinterpret_cast<uint16_t *>(u.fin) + sb0;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const u32x2_t w = {pack_bf16x2(S[b][t][0], S[b][t][1]), pack_bf16x2(S[b][t][2], S[b][t][3])};
@@ -1150,6 +1273,9 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     }
 }
 
+// kHalves: the unit list may hold column halves (a separate kernel instantiation, so that
+// whole-unit launches carry no NB = 1 code)
+template <bool kHalves>
 __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int cw, int lane)
 {
     bool spun_out = false;
@@ -1158,15 +1284,17 @@ __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned cha
     for (int64_t k = 0; unit_at(a, w, k, u); ++k) {
         // the previous unit's stores are done before this unit's value-ring bookkeeping starts
         wait_vmcnt<0>();
-        if (u.out_on)
-            consume_unit<true>(a, u, lds, cw, lane, it0, spun_out);
+        if (!u.out_on)
+            consume_unit<false, 2>(a, u, lds, cw, lane, it0, spun_out);  // segment F, P runs: whole
+        else if (!kHalves || u.half < 0)
+            consume_unit<true, 2>(a, u, lds, cw, lane, it0, spun_out);
         else
-            consume_unit<false>(a, u, lds, cw, lane, it0, spun_out);
+            consume_unit<true, 1>(a, u, lds, cw, lane, it0, spun_out);
         it0 += (int)(u.c1 - u.c0);
     }
 }
 
-template <bool kSw>
+template <bool kSw, bool kHalves>
 __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -1224,7 +1352,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         // The consumers set the pace (producers finish ahead and wait for free slots), so
         // they get issue priority over the producer sharing their SIMD.
         __builtin_amdgcn_s_setprio(1);
-        fused_consumer(a, w, lds, wave - 4, lane);
+        fused_consumer<kHalves>(a, w, lds, wave - 4, lane);
     }
 }
 
@@ -1329,6 +1457,8 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     a.n_total = reinterpret_cast<int64_t *>(f.ws + f.lay.off_status + 8);
     a.P = whole_chain_groups(f.H, f.lay.n_seq);
     a.wg_first = reinterpret_cast<int64_t *>(f.ws + f.lay.off_wg);
+    a.units = reinterpret_cast<int32_t *>(f.ws + f.lay.off_units);
+    a.split = split_eligible(f.H, f.lay.n_seq) && f.lay.seg.G <= 1;
     a.seq_start = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_off);
@@ -1370,6 +1500,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.seq_start = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_seq_len);
     a.wg_first = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_wg);
+    a.units = reinterpret_cast<const int32_t *>(f.ws + f.lay.off_units);
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
     a.G = f.lay.seg.G;
     a.L = f.lay.seg.L;
@@ -1377,8 +1508,12 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.segS = reinterpret_cast<float *>(f.ws + f.lay.off_seg);
     a.segF = a.segS + seg_floats;
     a.segP = a.segF + seg_floats;
-    // a separate instantiation reads the activation switches when any is off
-    void (*fused)(FusedArgs) = f.flags == (kGateIn | kL2In | kSigIn) ? fused_kernel<false> : fused_kernel<true>;
+    // separate instantiations read the activation switches (when any is off) and run column
+    // halves (whole-chain launches where the chunk table may split sequences)
+    const bool sw = f.flags != (kGateIn | kL2In | kSigIn);
+    const bool halves = a.G <= 1 && split_eligible(f.H, f.lay.n_seq);
+    void (*fused)(FusedArgs) = halves ? (sw ? fused_kernel<true, true> : fused_kernel<false, true>)
+                                      : (sw ? fused_kernel<true, false> : fused_kernel<false, false>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fused),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
     if (e != hipSuccess)

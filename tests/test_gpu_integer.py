@@ -4,7 +4,9 @@
   brute-force enumeration of 16-token chunk starts and to sum(ceil(L_i / 16)); invalid
   cu_seqlens set the documented status bits and make every sequence empty.
 * the split of a head's sequences into per-workgroup runs of about equal chunk count,
-  bit for bit against a brute-force assignment by chunk midpoint.
+  bit for bit against a brute-force assignment by chunk midpoint; where a head has few
+  workgroups and few sequences, the unit list with column halves and its longest-first
+  packing, bit for bit against a replica of that plan.
 * every out element and every final_state element is written (NaN sentinels vanish);
 * perturbing one sequence leaves every other sequence's out and final_state bit-identical;
 * two runs are bitwise identical, also with a workspace pre-filled with garbage;
@@ -136,11 +138,66 @@ def expected_runs(seq_off, P):
     return np.array([next((i for i in range(N) if grp[i] >= s), N) for s in range(P)] + [N], dtype=np.int64)
 
 
+# whole-chain plan with column halves (constants of the chunk-table plan)
+SPLIT_MAX_P, SPLIT_MAX_SEQ, SPLIT_MAX_K, WHOLE_W, HALF_W = 16, 32, 8, 100, 82
+
+
+def split_eligible(H, N):
+    return 256 // H <= SPLIT_MAX_P and N <= SPLIT_MAX_SEQ
+
+
+def whole_chain_groups(H, N):
+    units = 2 * N if split_eligible(H, N) else N
+    return max(1, min(max(1, 256 // H), units))
+
+
+def pack_halves(n, order, P, k):
+    """Longest first onto P workgroups, the k longest sequences as two halves of weight
+    82 n each, the others whole at 100 n; ties take a half first, then the least loaded
+    workgroup with the lowest index.  Returns (largest load, [(seq, code, workgroup)])."""
+    halves = [(HALF_W * n[order[i // 2]], order[i // 2], 1 + (i & 1)) for i in range(2 * k)]
+    wholes = [(WHOLE_W * n[order[i]], order[i], 0) for i in range(k, len(n))]
+    load, units, hi, wi = [0] * P, [], 0, 0
+    while hi < len(halves) or wi < len(wholes):
+        wh = halves[hi][0] if hi < len(halves) else -1
+        ww = wholes[wi][0] if wi < len(wholes) else -1
+        if wh >= ww:
+            w, seq, code = halves[hi]
+            hi += 1
+        else:
+            w, seq, code = wholes[wi]
+            wi += 1
+        b = min(range(P), key=lambda i: (load[i], i))
+        load[b] += w
+        units.append((seq, code, b))
+    return max(load), units
+
+
+def expected_plan(seq_off, H):
+    """(unit codes, first unit of each workgroup, P) of a head's whole-chain launch."""
+    N = len(seq_off) - 1
+    P = whole_chain_groups(H, N)
+    if not split_eligible(H, N):
+        return np.arange(N, dtype=np.int64) << 2, expected_runs(seq_off, P), P
+    n = [int(seq_off[i + 1] - seq_off[i]) for i in range(N)]
+    order = sorted(range(N), key=lambda i: (-n[i], i))
+    mks = [pack_halves(n, order, P, k)[0] for k in range(min(SPLIT_MAX_K, N) + 1)]
+    _, units = pack_halves(n, order, P, mks.index(min(mks)))
+    codes, wg = [], []
+    for b in range(P):
+        wg.append(len(codes))
+        codes += [(sq << 2) | c for sq, c, bb in units if bb == b]
+    wg.append(len(codes))
+    return np.array(codes, dtype=np.int64), np.array(wg, dtype=np.int64), P
+
+
 @pytest.mark.parametrize("N,H,kind", [(1, 1, "rand"), (8, 32, "rand"), (256, 32, "rand"), (300, 1, "rand"),
                                       (1000, 3, "rand"), (5, 4, "empty"), (9, 2, "one_long"),
-                                      (40, 8, "bad")])
+                                      (40, 8, "bad"), (8, 32, "one_long"), (3, 16, "one_long"),
+                                      (32, 16, "rand"), (20, 32, "empty"), (12, 32, "two_long"),
+                                      (33, 32, "one_long"), (6, 64, "two_long")])
 def test_workgroup_runs(N, H, kind):
-    """The whole-chain split of sequences into per-workgroup runs, bit for bit."""
+    """The whole-chain split of sequences into per-workgroup units, bit for bit."""
     import torch
     rng = np.random.default_rng(N + H)
     L = rng.integers(0, 200, size=N)
@@ -148,17 +205,30 @@ def test_workgroup_runs(N, H, kind):
         L[:] = 0
     elif kind == "one_long":
         L[:] = 3
-        L[4] = 5000
+        L[N // 2] = 5000
+    elif kind == "two_long":
+        L[1] = 3000
+        L[N - 2] = 2200
     cu = np.zeros(N + 1, dtype=np.int64)
     cu[1:] = np.cumsum(L)
     T = int(cu[-1])
     if kind == "bad":
         cu[3] = cu[4] + 1  # decreasing: every sequence becomes empty
-    P = max(1, min(256 // H, N))
     up = lambda x: -(-x // 256) * 256
     ws = torch.empty(kda.workspace_size(1, T, H, N, True), dtype=torch.uint8, device=torch_dev())
     seq_off, _, status = kda.chunk_table(torch.from_numpy(cu).to(torch_dev()), 1, T, H, workspace=ws)
+    codes, runs_ref, P = expected_plan(seq_off, H)
     off = 256 + 2 * up(8 * N) + up(8 * (N + 1))
     runs = ws[off:off + 8 * (P + 1)].cpu().numpy().view(np.int64)
-    assert np.array_equal(runs, expected_runs(seq_off, P)), (runs, expected_runs(seq_off, P))
+    assert np.array_equal(runs, runs_ref), (runs, runs_ref)
+    off_units = off + up(8 * 257)
+    units = ws[off_units:off_units + 4 * int(runs[-1])].cpu().numpy().view(np.int32)
+    assert np.array_equal(units.astype(np.int64), codes), (units, codes)
+    # every sequence appears once whole or as both halves
+    seen = sorted((int(c) >> 2, int(c) & 3) for c in units)
+    for i in range(N):
+        mine = [c for sq, c in seen if sq == i]
+        assert mine in ([0], [1, 2]), (i, mine)
     assert (status != 0) == (kind == "bad")
+    if kind in ("one_long", "two_long") and split_eligible(H, N) and whole_chain_groups(H, N) > 1:
+        assert any(int(c) & 3 for c in units)  # the long sequences run as column halves

@@ -5,8 +5,9 @@ L2 <= 5e-3; final_state relative L2 <= 1e-3 (fp32 states) or <= 1e-2 (bf16 state
 Covers the five reference workloads (the 1M-token one on sampled prefix/suffix windows
 plus an exact split-and-resume property), ragged lengths around the 16-token chunk,
 every state-dtype combination, zero-length sequences, B > 1, T = 0, lower_bound in
-{-5, -2, -0.05, 0}, in-place state carry, and the activation switches (pre-activated gate,
-caller-normalised q/k, pre-activated beta) in all eight settings, whole-chain and segmented.
+{-5, -2, -0.05, 0}, in-place state carry, the activation switches (pre-activated gate,
+caller-normalised q/k, pre-activated beta) in all eight settings, whole-chain and segmented,
+and long sequences run as two column halves.
 """
 import numpy as np
 import pytest
@@ -132,10 +133,10 @@ def test_in_place_state_carry():
 
 def segments_of(B, T, H):
     """Segments per chain of the forward plan, read off the workspace size (tables, the
-    workgroup-run table, three fp32 128 x 128 states per chain and segment)."""
+    workgroup-run table, the unit list, three fp32 128 x 128 states per chain and segment)."""
     from gated_delta_rule_86_amd import kda
     up = lambda x: -(-x // 256) * 256
-    table = 256 + up(8 * B) + up(8 * B) + up(8 * (B + 1)) + up(8 * 257)
+    table = 256 + up(8 * B) + up(8 * B) + up(8 * (B + 1)) + up(8 * 257) + up(8 * B)
     extra = kda.workspace_size(B, T, H) - table
     return 1 if extra == 0 else extra // (3 * B * H * 128 * 128 * 4)
 
@@ -194,3 +195,44 @@ def test_preactivated_gate_held_to_range():
         g[0, 1::5, 1, 30:] = 0.75
         w.g = f32_to_bf16_bits(g)
         parity(w, f"pre-activated gate held to [{lb}, 0]")
+
+
+def plan_has_halves(w):
+    """True when the chunk table runs some sequence of w as two column halves."""
+    import torch
+    from gated_delta_rule_86_amd import kda
+    from kda_testutil import torch_dev
+    N = len(w.cu_seqlens) - 1
+    up = lambda x: -(-x // 256) * 256
+    ws = torch.zeros(kda.workspace_size(1, w.T, w.H, N, True), dtype=torch.uint8, device=torch_dev())
+    kda.chunk_table(torch.from_numpy(w.cu_seqlens).to(torch_dev()), 1, w.T, w.H, workspace=ws)
+    off = 256 + 2 * up(8 * N) + up(8 * (N + 1))
+    off_units = off + up(8 * 257)
+    units = ws[off_units:off_units + 4 * 2 * N].cpu().numpy().view(np.int32)
+    return bool(np.any((units & 3) != 0))  # entries past the list stay zero (whole)
+
+
+@pytest.mark.parametrize("H,lens,sd,flags", [
+    (32, [600, 40, 30, 50, 20, 10, 70, 25], "bf16", 7),
+    (16, [900, 33, 17], "fp32", 7),
+    (32, [1000, 517, 3, 200], "none", 7),
+    (16, [700, 20], "fp32", 0),
+])
+def test_column_halves(H, lens, sd, flags):
+    """Few long sequences on heads with few workgroups each: the longest run as two units
+    of 64 value columns (the consumers take 16 columns each), whole-chain launch."""
+    w = W.make(f"halves_H{H}", 1, 0, H, lengths=lens, seed=350 + H + len(lens), flags=flags,
+               state_dtype=sd, with_initial=sd != "none", final_dtype="fp32" if sd == "none" else None)
+    assert plan_has_halves(w)
+    parity(w, f"column halves H={H} flags={flags}")
+
+
+def test_column_halves_in_place_state():
+    w = W.make("halves_inplace", 1, 0, 32, lengths=[640, 30, 45], seed=360)
+    assert plan_has_halves(w)
+    d = to_device(w)
+    ro, rf = run_oracle(w)
+    buf = d["h0"].clone()
+    o, f, _ = run_gpu(w, d, h0=buf, final=buf)
+    check_out(o, ro, "column halves in-place")
+    check_final(buf.cpu().numpy().astype(np.float64), rf, "fp32", "column halves in-place")

@@ -3,8 +3,9 @@
 * libkda.so loads and exports every function include/kda.h declares.
 * Every validation error of kda_fwd is returned before anything touches the device:
   the pointers below are never dereferenced, so fake aligned addresses are fine.
-* kda_fwd_workspace_size covers the status word, the per-sequence chunk table and the
-  table of whole-chain workgroup runs (257 int64), plus,
+* kda_fwd_workspace_size covers the status word, the per-sequence chunk table, the
+  table of whole-chain workgroup runs (257 int64) and the whole-chain unit list (2 int32
+  per sequence), plus,
   for few long equal-length chains run as segments, three fp32 states per chain and segment.
 """
 import ctypes
@@ -48,7 +49,7 @@ def ws_size(B, T, H, N=0, varlen=False):
 
 def table_bytes(N):
     up = lambda x: -(-x // 256) * 256
-    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257)
+    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N)
 
 
 def test_workspace_size_formula():
