@@ -207,3 +207,14 @@ def test_activation_switch_errors():
         expect(5, flags=flags, A_log=None, dt_bias=None, lb=0.5)  # lower_bound still checked
     # the other switches do not change what is required
     expect(1, flags=kda.GATE_IN_KERNEL, q=None)
+
+
+def test_forward_launches_of_reference_workloads():
+    """One forward launch for whole chains, two (pass A, pass B) for segmented ones; the
+    helper reads the workspace size, so it tracks the workspace layout."""
+    assert kda.forward_launches(1, 64, 1) == 1                 # B=1 T=64 H=1
+    assert kda.forward_launches(2, 4096, 16) == 2              # few long chains: segmented
+    assert kda.forward_launches(1, 31094, 32, 8, True) == 1    # varlen: whole chains
+    assert kda.forward_launches(1, 1 << 20, 8) == 2
+    assert kda.forward_launches(1, 66285, 32, 256, True) == 1
+    assert kda.forward_launches(256, 1, 32) == 1
