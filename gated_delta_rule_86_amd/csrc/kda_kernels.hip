@@ -121,6 +121,7 @@ struct TableArgs {
     int64_t *seq_start, *seq_len, *seq_off;
     int64_t *wg_first;  // [P + 1]: first unit of each whole-chain workgroup of a head
     int32_t *units;     // [2 N]: (sequence << 2) | (0 whole, 1 + column half)
+    int whole;          // the forward pass runs whole chains (no segment plan)
     int split;          // whole-chain pass that may split sequences into column halves
 };
 
@@ -259,12 +260,56 @@ __device__ void plan_halves(const TableArgs &a, int tid)
     }
 }
 
+// Snake order for up to kSnakeMaxSeq sequences per head: sequence i of rank r by chunk
+// count (longest first, ties by index) goes to workgroup r % P in even rounds r / P and
+// to P - 1 - r % P in odd ones, as unit r / P of that workgroup.  Every workgroup then
+// holds the same number of sequences (one more for some, in the last round) and about the
+// same number of chunks, each sequence's place following from its rank alone.
+constexpr int64_t kSnakeMaxSeq = 512;
+
+__device__ void plan_snake(const TableArgs &a, int tid)
+{
+    // N <= 512; a chunk count is held to 2^31 - 1 (no sequence that fits in memory comes
+    // near it)
+    // key of sequence i: its chunk count above, kSnakeMaxSeq - 1 - i below, so that one
+    // comparison orders by count and breaks ties by index
+    __shared__ int64_t s_key[kSnakeMaxSeq];
+    const int N = (int)a.N, P = (int)a.P;
+    __syncthreads();
+    for (int i = tid; i < N; i += 256) {
+        const int64_t c = a.seq_off[i + 1] - a.seq_off[i];
+        s_key[i] = ((c < 0x7fffffff ? c : 0x7fffffff) << 10) | (int64_t)(kSnakeMaxSeq - 1 - i);
+    }
+    __syncthreads();
+    const int R = N / P, rem = N % P;  // full rounds; units of the last, partial round
+    // first unit of workgroup b: R per lower workgroup, plus the lower workgroups that take
+    // a unit in the last round (the first rem in its direction)
+    auto first = [&](int b) {
+        const int extra = (R & 1) == 0 ? (b < rem ? b : rem) : (b > P - rem ? b - (P - rem) : 0);
+        return b * R + extra;
+    };
+    for (int i = tid; i < N; i += 256) {
+        const int64_t key = s_key[i];
+        int r = 0;
+#pragma unroll 8
+        for (int j = 0; j < N; ++j)
+            r += s_key[j] > key;
+        const int rnd = r / P, pos = r - rnd * P;
+        const int b = (rnd & 1) ? P - 1 - pos : pos;
+        a.units[first(b) + rnd] = i << 2;
+    }
+    for (int b = tid; b <= P; b += 256)
+        a.wg_first[b] = first(b);
+}
+
 __global__ __launch_bounds__(256) void chunk_table_kernel(TableArgs a)
 {
     chunk_table_body(a, threadIdx.x);
     partition_sequences(a, threadIdx.x);
     if (a.split && a.N <= kSplitMaxSeq && a.P <= kSplitMaxP)
         plan_halves(a, threadIdx.x);
+    else if (a.whole && a.N <= kSnakeMaxSeq && a.P > 1)
+        plan_snake(a, threadIdx.x);
 }
 
 __device__ void chunk_table_body(const TableArgs &a, int tid)
@@ -1458,7 +1503,8 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     a.P = whole_chain_groups(f.H, f.lay.n_seq);
     a.wg_first = reinterpret_cast<int64_t *>(f.ws + f.lay.off_wg);
     a.units = reinterpret_cast<int32_t *>(f.ws + f.lay.off_units);
-    a.split = split_eligible(f.H, f.lay.n_seq) && f.lay.seg.G <= 1;
+    a.whole = f.lay.seg.G <= 1;
+    a.split = split_eligible(f.H, f.lay.n_seq) && a.whole;
     a.seq_start = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_off);

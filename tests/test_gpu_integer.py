@@ -3,10 +3,10 @@
 * chunk table (cu_seqlens -> per-sequence chunk offsets, total): equal, bit for bit, to a
   brute-force enumeration of 16-token chunk starts and to sum(ceil(L_i / 16)); invalid
   cu_seqlens set the documented status bits and make every sequence empty.
-* the split of a head's sequences into per-workgroup runs of about equal chunk count,
-  bit for bit against a brute-force assignment by chunk midpoint; where a head has few
-  workgroups and few sequences, the unit list with column halves and its longest-first
-  packing, bit for bit against a replica of that plan.
+* the split of a head's sequences into per-workgroup units, bit for bit against a replica
+  of each plan: column halves packed longest first (few workgroups and few sequences per
+  head), snake order by length (up to 512 sequences), contiguous runs of about equal chunk
+  count (brute-force assignment by chunk midpoint) beyond that.
 * every out element and every final_state element is written (NaN sentinels vanish);
 * perturbing one sequence leaves every other sequence's out and final_state bit-identical;
 * two runs are bitwise identical, also with a workspace pre-filled with garbage;
@@ -140,6 +140,7 @@ def expected_runs(seq_off, P):
 
 # whole-chain plan with column halves (constants of the chunk-table plan)
 SPLIT_MAX_P, SPLIT_MAX_SEQ, SPLIT_MAX_K, WHOLE_W, HALF_W = 16, 32, 8, 100, 82
+SNAKE_MAX_SEQ = 512
 
 
 def split_eligible(H, N):
@@ -178,7 +179,19 @@ def expected_plan(seq_off, H):
     N = len(seq_off) - 1
     P = whole_chain_groups(H, N)
     if not split_eligible(H, N):
-        return np.arange(N, dtype=np.int64) << 2, expected_runs(seq_off, P), P
+        if N > SNAKE_MAX_SEQ or P == 1:
+            return np.arange(N, dtype=np.int64) << 2, expected_runs(seq_off, P), P
+        # snake order: rank r (longest first, ties by index) -> workgroup r % P in even
+        # rounds r // P, P - 1 - r % P in odd ones
+        n = [int(seq_off[i + 1] - seq_off[i]) for i in range(N)]
+        order = sorted(range(N), key=lambda i: (-n[i], i))
+        bins = [[] for _ in range(P)]
+        for r, i in enumerate(order):
+            rnd, pos = divmod(r, P)
+            bins[pos if rnd % 2 == 0 else P - 1 - pos].append(i)
+        codes = [i << 2 for b in bins for i in b]
+        wg = np.cumsum([0] + [len(b) for b in bins])
+        return np.array(codes, dtype=np.int64), wg.astype(np.int64), P
     n = [int(seq_off[i + 1] - seq_off[i]) for i in range(N)]
     order = sorted(range(N), key=lambda i: (-n[i], i))
     mks = [pack_halves(n, order, P, k)[0] for k in range(min(SPLIT_MAX_K, N) + 1)]
@@ -195,7 +208,8 @@ def expected_plan(seq_off, H):
                                       (1000, 3, "rand"), (5, 4, "empty"), (9, 2, "one_long"),
                                       (40, 8, "bad"), (8, 32, "one_long"), (3, 16, "one_long"),
                                       (32, 16, "rand"), (20, 32, "empty"), (12, 32, "two_long"),
-                                      (33, 32, "one_long"), (6, 64, "two_long")])
+                                      (33, 32, "one_long"), (6, 64, "two_long"), (512, 32, "rand"),
+                                      (513, 32, "rand"), (257, 1, "rand"), (100, 3, "empty")])
 def test_workgroup_runs(N, H, kind):
     """The whole-chain split of sequences into per-workgroup units, bit for bit."""
     import torch
