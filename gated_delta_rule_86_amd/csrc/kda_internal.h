@@ -67,14 +67,23 @@ inline bool split_eligible(int64_t H, int64_t n_seq)
     return kPlanCUs / H <= kSplitMaxP && n_seq <= kSplitMaxSeq;
 }
 
+// The whole-chain launch may run column halves: varlen (equal-length batch rows never gain
+// from a split), whole chains (no segment plan), few sequences and workgroups per head.
+// The chunk table plans halves and the forward launch picks the kernel instance that runs
+// them under this same condition.
+inline bool split_plan(int64_t H, int64_t n_seq, int seg_G, bool varlen)
+{
+    return varlen && seg_G <= 1 && split_eligible(H, n_seq);
+}
+
 // Workgroups per head of the whole-chain launch: about one workgroup per CU over all
 // heads, never more than the units (the sequences, or twice that where halves may be used).
-inline int64_t whole_chain_groups(int64_t H, int64_t n_seq)
+inline int64_t whole_chain_groups(int64_t H, int64_t n_seq, bool varlen)
 {
     int64_t p = kPlanCUs / H;
     if (p < 1)
         p = 1;
-    const int64_t units = split_eligible(H, n_seq) ? 2 * n_seq : n_seq;
+    const int64_t units = varlen && split_eligible(H, n_seq) ? 2 * n_seq : n_seq;
     if (p > units)
         p = units;
     return p < 1 ? 1 : p;

@@ -1500,11 +1500,11 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     a.N = f.lay.n_seq;
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
     a.n_total = reinterpret_cast<int64_t *>(f.ws + f.lay.off_status + 8);
-    a.P = whole_chain_groups(f.H, f.lay.n_seq);
+    a.P = whole_chain_groups(f.H, f.lay.n_seq, f.cu != nullptr);
     a.wg_first = reinterpret_cast<int64_t *>(f.ws + f.lay.off_wg);
     a.units = reinterpret_cast<int32_t *>(f.ws + f.lay.off_units);
     a.whole = f.lay.seg.G <= 1;
-    a.split = split_eligible(f.H, f.lay.n_seq) && a.whole;
+    a.split = split_plan(f.H, f.lay.n_seq, f.lay.seg.G, f.cu != nullptr);
     a.seq_start = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_off);
@@ -1557,7 +1557,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     // separate instantiations read the activation switches (when any is off) and run column
     // halves (whole-chain launches where the chunk table may split sequences)
     const bool sw = f.flags != (kGateIn | kL2In | kSigIn);
-    const bool halves = a.G <= 1 && split_eligible(f.H, f.lay.n_seq);
+    const bool halves = split_plan(f.H, f.lay.n_seq, a.G, f.cu != nullptr);
     void (*fused)(FusedArgs) = halves ? (sw ? fused_kernel<true, true> : fused_kernel<false, true>)
                                       : (sw ? fused_kernel<true, false> : fused_kernel<false, false>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fused),
@@ -1568,7 +1568,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
         // whole chains: H x per_head workgroups, each running a run of sequences of one
         // head back to back (about one workgroup per CU; runs from the chunk table)
         a.pass = 0;
-        const int64_t per_head = whole_chain_groups(f.H, f.lay.n_seq);
+        const int64_t per_head = whole_chain_groups(f.H, f.lay.n_seq, f.cu != nullptr);
         hipLaunchKernelGGL(fused, dim3((unsigned)(f.H * per_head)), dim3(512), kFusedLds, s, a);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
