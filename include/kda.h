@@ -44,7 +44,7 @@ extern "C" {
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* A_log or dt_bias is NULL (in-pass gate), or a token tensor is NULL while T > 0 */
-    KDA_ERR_SHAPE = 2,       /* B < 1, T < 0, H < 1, N inconsistent, or cu_seqlens with B != 1 */
+    KDA_ERR_SHAPE = 2,       /* B < 1, T < 0, H < 1, N inconsistent or >= 2^29, or cu_seqlens with B != 1 */
     KDA_ERR_HEAD_DIM = 3,    /* K or V is not 128 */
     KDA_ERR_DTYPE = 4,       /* state dtype unknown, or initial/final state dtypes differ */
     KDA_ERR_LOWER_BOUND = 5, /* lower_bound not finite or outside [-5, 0] */
@@ -197,9 +197,10 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
 
 /*
  * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs: the status word, the
- * per-sequence chunk table (start, length, chunk offset), O(N) bytes, and a fixed 2.25 KiB
- * table that splits the sequences into runs of about equal chunk count, one run per
- * workgroup.  Without cu_seqlens
+ * per-sequence chunk table (start, length, chunk offset), O(N) bytes, a fixed 2.25 KiB
+ * table of the first unit of each workgroup and the unit list (8 bytes per sequence) that
+ * spreads the sequences over the workgroups with about equal chunk counts (a long sequence
+ * of a varlen batch may run as two units of 64 value columns each).  Without cu_seqlens
  * and with few long chains (B * H small, T long), each chain is cut into G segments that
  * run in parallel (the state after a segment is affine in the state before it); that
  * adds three fp32 128 x 128 states per chain and segment, 3 * B * H * G * 64 KiB, with G

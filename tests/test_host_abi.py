@@ -218,3 +218,13 @@ def test_forward_launches_of_reference_workloads():
     assert kda.forward_launches(1, 1 << 20, 8) == 2
     assert kda.forward_launches(1, 66285, 32, 256, True) == 1
     assert kda.forward_launches(256, 1, 32) == 1
+
+
+def test_sequence_count_limit():
+    """Unit codes hold the sequence index in 29 bits: N >= 2^29 is a shape error, and the
+    workspace size is 0 for it."""
+    assert ws_size(1, 100, 1, (1 << 29) - 1, True) > 0
+    assert ws_size(1, 100, 1, 1 << 29, True) == 0
+    a = Args(T=16, varlen=True, N=1)
+    a.N = 1 << 29
+    assert a.call() == 2  # KDA_ERR_SHAPE
