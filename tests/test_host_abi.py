@@ -227,4 +227,6 @@ def test_sequence_count_limit():
     assert ws_size(1, 100, 1, 1 << 29, True) == 0
     a = Args(T=16, varlen=True, N=1)
     a.N = 1 << 29
+    # no states: their fake ranges at this N would overlap the other fake buffers
+    a.h0, a.h0_dt, a.ht, a.ht_dt = None, kda.STATE_NONE, None, kda.STATE_NONE
     assert a.call() == 2  # KDA_ERR_SHAPE
