@@ -1401,16 +1401,18 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     }
 }
 
-// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, in fp32 on v_mfma_f32_16x16x4_f32.
-// Rows of S are independent: a workgroup takes 16 rows of one chain (8 workgroups per
-// chain) and keeps them in registers across the steps, in the MFMA A layout (lane m + 16k
-// holds S[m][4j + k] for step j of the contraction).  Wave w forms output columns
-// 32w .. 32w+31 (two 16-column tiles); its B operands, P_g[4j + k][c] in lane c + 16k, come
-// straight from global memory (16 lanes read 64 contiguous bytes), and those of the next
-// step, with F_g, are loaded before this step's MFMAs.  The 16 x 128 result goes back to
-// the A layout through LDS.  Workgroup b takes chain b % chains, so the 8 workgroups of a
-// chain share a slot modulo 8 (the XCD the dispatcher gives them, whose L2 then holds that
-// chain's P_g once).
+// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, on v_mfma_f32_16x16x32_bf16 with a
+// hi/lo bf16 split of both factors (three products: hi hi, lo hi, hi lo; fp32 accumulate,
+// about 16 significant bits per factor, as the chunk recurrence's state products).  Rows of
+// S are independent: a workgroup takes 16 rows of one chain (8 workgroups per chain).  For
+// contraction chunk kc (32 channels) lane m + 16kg holds S[m][32kc + 8kg + e], e = 0..7 (the
+// A operand), split from the 16 rows kept in LDS between steps.  Wave w forms output column
+// tiles 2w and 2w + 1; lane n + 16kg of chunk kc, tile t takes P[32kc + 8kg + e][16t + n]
+// (the B operand) straight from global memory (16 lanes read 64 contiguous bytes) and
+// splits it; the loads of the next step, with F_g, go out before this step's products.
+// Workgroup b takes
+// chain b % chains, so the 8 workgroups of a chain share a slot modulo 8 (the XCD the
+// dispatcher gives them, whose L2 then holds that chain's P_g once).
 struct ScanArgs {
     float *segS, *segF, *segP;
     int G;
@@ -1419,72 +1421,83 @@ struct ScanArgs {
 
 __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
 {
-    __shared__ float s_rows[16][kD + 4];
+    __shared__ __attribute__((aligned(16))) float s_rows[16][kD + 4];
     constexpr int64_t kBlock = (int64_t)kD * kD;
     const int64_t chain = blockIdx.x % a.chains;
     const int r0 = (int)(blockIdx.x / a.chains) * 16;
     if (r0 >= kD)
         return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int m = lane & 15, kq = lane >> 4;  // A: row m, k-sub kq; B and D: column m
+    const int m = lane & 15, kg = lane >> 4;  // A: row m, k-group kg; B and D: column m
     auto blk = [&](float *base, int g) { return base + ((size_t)chain * a.G + (size_t)g) * kBlock; };
-    float av[32];
-    {
-        const float *S1 = blk(a.segS, 1) + (size_t)(r0 + m) * kD + kq;
+    u32x4_t ahi[4], alo[4];
+    auto split_A = [&](const float *row) {  // row = S[r0 + m]
 #pragma unroll
-        for (int j = 0; j < 32; ++j)
-            av[j] = S1[4 * j];
-    }
-    float bv[2][32];
-    f32x4_t fv[2];  // F_g[r0 + 4kq + i][32w + 16t + m]: the D layout of the output tiles
+        for (int kc = 0; kc < 4; ++kc) {
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(row + 32 * kc + 8 * kg);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(row + 32 * kc + 8 * kg + 4);
+            const u32x2_t p0 = split_bf16x2(x0[0], x0[1]), p1 = split_bf16x2(x0[2], x0[3]);
+            const u32x2_t p2 = split_bf16x2(x1[0], x1[1]), p3 = split_bf16x2(x1[2], x1[3]);
+            ahi[kc] = u32x4_t{p0[0], p1[0], p2[0], p3[0]};
+            alo[kc] = u32x4_t{p0[1], p1[1], p2[1], p3[1]};
+        }
+    };
+    split_A(blk(a.segS, 1) + (size_t)(r0 + m) * kD);
+    float bv[2][4][8];
+    f32x4_t fv[2];  // F_g[r0 + 4kg + i][16(2w + t) + m]: the D layout of the output tiles
     auto load_BF = [&](int g) {
-        const float *P = blk(a.segP, g) + (size_t)kq * kD + 32 * w + m;
-        const float *F = blk(a.segF, g) + (size_t)(r0 + 4 * kq) * kD + 32 * w + m;
+        const float *P = blk(a.segP, g) + (size_t)(8 * kg) * kD + 32 * w + m;
+        const float *F = blk(a.segF, g) + (size_t)(r0 + 4 * kg) * kD + 32 * w + m;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 fv[t][i] = F[(size_t)i * kD + 16 * t];
 #pragma unroll
-            for (int j = 0; j < 32; ++j)
-                bv[t][j] = P[(size_t)(4 * j) * kD + 16 * t];
+            for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bv[t][kc][e] = P[(size_t)(32 * kc + e) * kD + 16 * t];
         }
     };
     load_BF(1);
     for (int g = 1; g + 1 < a.G; ++g) {
-        // two accumulators per tile (even and odd k-steps) keep four MFMA chains in flight
-        f32x4_t acc[2][2];
-        float bc[2][32];
+        f32x4_t acc[2];
+        u32x4_t ch[2][4], cl[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            acc[t][0] = fv[t];
-            acc[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc[t] = fv[t];
 #pragma unroll
-            for (int j = 0; j < 32; ++j)
-                bc[t][j] = bv[t][j];
+            for (int kc = 0; kc < 4; ++kc) {
+                const float *x = bv[t][kc];
+                const u32x2_t p0 = split_bf16x2(x[0], x[1]), p1 = split_bf16x2(x[2], x[3]);
+                const u32x2_t p2 = split_bf16x2(x[4], x[5]), p3 = split_bf16x2(x[6], x[7]);
+                ch[t][kc] = u32x4_t{p0[0], p1[0], p2[0], p3[0]};
+                cl[t][kc] = u32x4_t{p0[1], p1[1], p2[1], p3[1]};
+            }
         }
         if (g + 2 < a.G)
             load_BF(g + 1);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bc[0][j], acc[0][j & 1], 0, 0, 0);
-            acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bc[1][j], acc[1][j & 1], 0, 0, 0);
-        }
-        const f32x4_t res[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
-        // rows 4kq + i, column 32w + 16t + m: to global, and through LDS to the A layout
-        float *Sn = blk(a.segS, g + 1) + (size_t)(r0 + 4 * kq) * kD + 32 * w + m;
+        for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                acc[t] = mfma32(ahi[kc], ch[t][kc], acc[t]);
+                acc[t] = mfma32(alo[kc], ch[t][kc], acc[t]);
+                acc[t] = mfma32(ahi[kc], cl[t][kc], acc[t]);
+            }
+        // rows 4kg + i, column 32w + 16t + m: to global, and through LDS to the A layout
+        float *Sn = blk(a.segS, g + 1) + (size_t)(r0 + 4 * kg) * kD + 32 * w + m;
         __syncthreads();  // the previous step's reads of s_rows are done
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                Sn[(size_t)i * kD + 16 * t] = res[t][i];
-                s_rows[4 * kq + i][32 * w + 16 * t + m] = res[t][i];
+                Sn[(size_t)i * kD + 16 * t] = acc[t][i];
+                s_rows[4 * kg + i][32 * w + 16 * t + m] = acc[t][i];
             }
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 32; ++j)
-            av[j] = s_rows[m][4 * j + kq];
+        split_A(&s_rows[m][0]);
     }
 }
 
