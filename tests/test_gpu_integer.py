@@ -246,3 +246,19 @@ def test_workgroup_runs(N, H, kind):
     assert (status != 0) == (kind == "bad")
     if kind in ("one_long", "two_long") and split_eligible(H, N) and whole_chain_groups(H, N) > 1:
         assert any(int(c) & 3 for c in units)  # the long sequences run as column halves
+
+
+def test_segmented_workspace_garbage():
+    """Segmented batch rows (pass A, scan, pass B) with a workspace pre-filled with garbage:
+    the status word reads 0, the chunk total is right, and out and final_state are
+    bit-identical to a run on a fresh workspace."""
+    import torch
+    w = W.make("segws", 2, 900, 2, seed=405)
+    assert kda.forward_launches(2, 900, 2) == 2
+    d = to_device(w)
+    o1, f1, _ = run_gpu(w, d, keep_device=True)
+    ws = torch.full((kda.workspace_size(2, 900, 2),), 0xFF, dtype=torch.uint8, device=torch_dev())
+    o2, f2, _ = run_gpu(w, d, workspace=ws, keep_device=True)
+    assert kda.device_status(ws) == 0
+    assert int(ws[8:16].cpu().numpy().view(np.int64)[0]) == 2 * ((900 + 15) // 16)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
