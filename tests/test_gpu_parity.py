@@ -108,6 +108,13 @@ def test_varlen_fp32_many():
     parity(W.make("varlen40", 1, 0, 2, lengths=L, seed=305), "varlen N=40")
 
 
+def test_varlen_many_short_contiguous_runs():
+    """More than 512 sequences: the whole-chain launch splits them into contiguous runs of
+    about equal chunk count (above the snake-order limit)."""
+    L = np.random.default_rng(8).integers(0, 40, size=600)
+    parity(W.make("varlen600", 1, 0, 1, lengths=L, seed=309, state_dtype="bf16"), "varlen N=600")
+
+
 def test_T_zero():
     w = W.make("T0", 2, 0, 2, seed=306)
     o, f, _ = run_gpu(w)
