@@ -194,7 +194,7 @@ kda_status fwd_impl(const void *q, const void *k, const void *v, const void *g, 
     auto mark = [&](int i) {
         return events == nullptr || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
     };
-    if (!mark(0) || kda::launch_chunk_table(a, s) != hipSuccess)
+    if (!mark(0) || kda::launch_chunk_table(a, s, !recurrent) != hipSuccess)
         return KDA_ERR_HIP;
     hipEvent_t marks[3];
     if (events)

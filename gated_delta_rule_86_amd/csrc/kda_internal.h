@@ -152,7 +152,9 @@ struct FwdArgs {
     Layout lay;
 };
 
-hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s);
+// plan: also write the whole-chain workgroup plan (the forward pass reads it; the
+// token-by-token path does not)
+hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s, bool plan = true);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t s, hipEvent_t const *marks);
 // token-by-token evaluation, one workgroup per chain (kda_recurrent.hip)
 hipError_t launch_recurrent(const FwdArgs &a, hipStream_t s);

@@ -1504,7 +1504,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------
-hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
+hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s, bool plan)
 {
     TableArgs a;
     a.cu = f.cu;
@@ -1516,8 +1516,8 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s)
     a.P = whole_chain_groups(f.H, f.lay.n_seq, f.cu != nullptr);
     a.wg_first = reinterpret_cast<int64_t *>(f.ws + f.lay.off_wg);
     a.units = reinterpret_cast<int32_t *>(f.ws + f.lay.off_units);
-    a.whole = f.lay.seg.G <= 1;
-    a.split = split_plan(f.H, f.lay.n_seq, f.lay.seg.G, f.cu != nullptr);
+    a.whole = plan && f.lay.seg.G <= 1;
+    a.split = plan && split_plan(f.H, f.lay.n_seq, f.lay.seg.G, f.cu != nullptr);
     a.seq_start = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_off);
