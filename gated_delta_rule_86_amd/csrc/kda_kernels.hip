@@ -158,8 +158,8 @@ __device__ void partition_sequences(const TableArgs &a, int tid)
     }
 }
 
-// Whole-chain plan with column halves (see split_eligible): N <= kSplitMaxSeq sequences,
-// P <= kSplitMaxP workgroups per head.  Thread k (k = 0 .. min(N, kSplitMaxK)) packs the
+// Whole-chain plan with column halves (varlen launches that split_plan admits): N <=
+// kSplitMaxSeq sequences, P <= kSplitMaxP workgroups per head.  Thread k (k = 0 .. min(N, kSplitMaxK)) packs the
 // head's units when the k longest sequences run as two column halves each: units are taken
 // by weight, heaviest first (whole 100 n, half 82 n for n chunks; a tie takes the half
 // first, sequences of equal length go by index), each to the least loaded workgroup (the
@@ -269,10 +269,9 @@ constexpr int64_t kSnakeMaxSeq = 512;
 
 __device__ void plan_snake(const TableArgs &a, int tid)
 {
-    // N <= 512; a chunk count is held to 2^31 - 1 (no sequence that fits in memory comes
-    // near it)
-    // key of sequence i: its chunk count above, kSnakeMaxSeq - 1 - i below, so that one
-    // comparison orders by count and breaks ties by index
+    // Key of sequence i: its chunk count above, kSnakeMaxSeq - 1 - i below, so that one
+    // comparison orders by count and breaks ties by index (N <= 512; a count is held to
+    // 2^31 - 1, which no sequence that fits in memory comes near).
     __shared__ int64_t s_key[kSnakeMaxSeq];
     const int N = (int)a.N, P = (int)a.P;
     __syncthreads();
