@@ -136,7 +136,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the (sequence, "
+        print(f"bench.py: this library runs on one GPU only (got --gpus {args.gpus}); the (sequence, "
               "head) chains shard across GPUs with no communication, but no multi-GPU path is built.",
               file=sys.stderr)
         sys.exit(2)
