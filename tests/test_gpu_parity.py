@@ -224,6 +224,7 @@ def plan_has_halves(w):
     (16, [900, 33, 17], "fp32", 7),
     (32, [1000, 517, 3, 200], "none", 7),
     (16, [700, 20], "fp32", 0),
+    (24, [500, 30, 70], "fp32", 7),     # 10 workgroups per head
 ])
 def test_column_halves(H, lens, sd, flags):
     """Few long sequences on heads with few workgroups each: the longest run as two units
