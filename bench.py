@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload i]
 
 A step is one kda_fwd call (chunk table, prep, state/output stages) over one batch of
-seeded synthetic input already resident in HBM.  Default workload: B=2, T=4096, H=16,
-K=V=128, fp32 initial and final state (index 1 of workloads.config).  Prints one JSON line.
+seeded synthetic input already resident in HBM.  Default workload: the largest one, a single
+1,048,576-token sequence with H=8, K=V=128, fp32 initial and final state (index 3 of
+workloads.config).  Prints one JSON line.
 
 W warm-up steps (default 100: a fresh process needs some 20 ms of sustained load before the
 forward kernel reaches its steady speed) are not timed.
@@ -21,6 +22,10 @@ step / fused_kernel's time per step (the sum over its launches): q, k, v, g (4 x
 beta (2 B) + out (256 B) per head-token, plus initial/final state.  traffic (when the
 committed rocprofv3 summary matches the kernel source) is fused_kernel's calibrated
 FETCH_SIZE + WRITE_SIZE per step, summed the same way.
+flushed: K more steps, each after writing a 1 GiB scratch buffer (which evicts the 4 MiB L2
+of every XCD and the 256 MiB MALL), each timed alone with HIP events: median, p10, p90.
+Workloads whose bytes exceed the MALL many times over (the 2^20-token one moves 10.8 GB)
+time the same either way; the small ones would otherwise run out of the MALL.
 cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
 
 --copy-calibration runs only a plain device-to-device copy of known size (for scaling the
@@ -70,6 +75,27 @@ def committed_traffic(workload_name, kernel, source="kda_kernels.hip"):
             if fields.get("source_sha256") == sha and kernel in fields:
                 try:
                     return int(fields[kernel])
+                except ValueError:
+                    return None
+    return None
+
+
+def committed_counter(workload_name, key, kernel, source="kda_kernels.hip"):
+    """A per-kernel figure (a float) from the line `<key>: <kernel>=<x> ... source_sha256=...`
+    of the committed profile of this workload, or None when there is none or the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"kda_fwd_{workload_name}.md")
+    src = os.path.join(ROOT, "gated_delta_rule_86_amd", "csrc", source)
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for line in open(path):
+        if line.startswith(key + ":"):
+            fields = dict(f.split("=", 1) for f in line.split(":", 1)[1].split() if "=" in f)
+            if fields.get("source_sha256") == sha and kernel in fields:
+                try:
+                    return float(fields[kernel])
                 except ValueError:
                     return None
     return None
@@ -130,7 +156,7 @@ def main():
     # speed (the first launches of a fresh process run 6-9 % slower); 100 steps cover that
     # for every workload here
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", type=int, default=1,
+    ap.add_argument("--workload", type=int, default=3,
                     help="index into workloads.config (0..4; 5 = decode step, token-by-token path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -224,6 +250,21 @@ def main():
         for e in row:
             hip.hipEventDestroy(e)
 
+    # flushed steps: 1 GiB written before each, each step timed alone on the launch stream
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    fl_ms = []
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        fl_ms.append(e0.elapsed_time(e1))
+    del flush
+    fl_sorted = sorted(fl_ms)
+    pct = lambda p: fl_sorted[min(len(fl_sorted) - 1, max(0, int(round(p * (len(fl_sorted) - 1)))))]
+
     ht = w.head_tokens
     ms_per_step = elapsed / args.steps * 1e3
     value = ht / (elapsed / args.steps)
@@ -251,8 +292,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name, dname, dsrc),
                      "kernel": dname, "launches_per_step": launches,
-                     "kernel_ms": stage_ms[1], "kernel_algorithmic_bytes": kernel_bytes},
-        "timing": {"ms_per_step_with_events": elapsed_ev / args.steps * 1e3},
+                     "kernel_ms": stage_ms[1], "kernel_algorithmic_bytes": kernel_bytes,
+                     "frac_whole_step": path_gbps / HBM_PEAK_GBPS,
+                     "mfma_busy_frac": committed_counter(w.name, "mfma_busy", dname, dsrc)},
+        "timing": {"ms_per_step_with_events": elapsed_ev / args.steps * 1e3,
+                   "flushed_ms_p50": pct(0.5), "flushed_ms_p10": pct(0.1), "flushed_ms_p90": pct(0.9),
+                   "flushed_value_p50": ht / (pct(0.5) * 1e-3), "flush_bytes": 1 << 30},
         "path": {"algorithmic_bytes": path_bytes, "achieved_GBps": path_gbps,
                  "hbm_frac": path_gbps / HBM_PEAK_GBPS, "achieved_TFLOPs": path_tflops,
                  "mfma_frac": path_tflops / MFMA_BF16_PEAK_TFLOPS,

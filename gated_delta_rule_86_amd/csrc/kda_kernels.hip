@@ -1129,11 +1129,13 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     u32x4_t negI0, negI1;
     make_neg_identity(lane, negI0, negI1);
     unsigned char *obuf = lds + kOffOut + cw * 1024;  // output tile of the previous chunk
-    const int orow = lane / kLpr;                      // output row this lane stores
+    // output row this lane stores: 16 rows of kLpr lanes each; with NB = 1 lanes 32-63 map
+    // past row 15 and store nothing
+    const int orow = lane / kLpr;
     auto store_out = [&](int64_t jo) {
         const int64_t rem = len - jo * kCH;
         const u32x4_t ow = *reinterpret_cast<const u32x4_t *>(obuf + lane * 16);
-        if (orow < rem)
+        if (orow < kCH && orow < rem)
             *reinterpret_cast<u32x4_t *>(a.out + ((size_t)(start + jo * kCH + orow) * (size_t)H + (size_t)h) * kD +
                                          cb0 + 8 * (lane % kLpr)) = ow;
     };

@@ -191,6 +191,10 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     ws_bytes = workspace_size(B, T, H, N if cu_seqlens is not None else B, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        # allocated on the current stream; the kernels run on `stream`: keep the caching
+        # allocator from reusing the block before they have finished
+        if stream is not None and stream != torch.cuda.current_stream(q.device):
+            workspace.record_stream(stream)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
             _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
             _state_code(initial_state), _ptr(final_state), _state_code(final_state),
@@ -234,6 +238,8 @@ def chunk_table(cu_seqlens, B: int, T: int, H: int, workspace=None, stream=None)
     ws_bytes = workspace_size(B, T, H, N if cu_seqlens is not None else B, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        if stream is not None and stream != torch.cuda.current_stream(dev):
+            workspace.record_stream(stream)
     seq_off = np.zeros(N + 1, dtype=np.int64)
     n_total = ctypes.c_int64(-1)
     status = ctypes.c_int32(-1)

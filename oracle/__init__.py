@@ -66,6 +66,10 @@ def lib():
         L.oracle_kda_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
                                      ctypes.c_int, vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, vp, vp,
                                      ctypes.c_int]
+        L.oracle_kda_fwd_compare.restype = ctypes.c_int
+        L.oracle_kda_fwd_compare.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
+                                             ctypes.c_int, vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, i64,
+                                             vp, vp, vp, ctypes.c_int]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         _lib = L
@@ -172,6 +176,47 @@ def kda_fwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=
     if rc != 0:
         raise ValueError(f"oracle_kda_fwd rejected its arguments ({rc})")
     return out, fin
+
+
+def kda_fwd_compare(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, out_cmp, initial_state=None,
+                    cu_seqlens=None, heads=None, want_final=True, nthreads=0, flags=ALL_IN_KERNEL):
+    """The oracle forward pass compared token by token with another output, without storing
+    the fp64 output (bounded memory for very long sequences).
+
+    Inputs as ``kda_fwd``; out_cmp: uint16 bf16 bits [B, T, H, 128] (every head, whatever
+    ``heads`` selects).  Returns (stats float64 [N, n_sel, 3] = max|err|, sum err^2,
+    sum ref^2 per chain, final float64 [N, n_sel, 128, 128] or None).
+    """
+    B, T, H, D = q.shape
+    assert out_cmp.dtype == np.uint16 and out_cmp.shape == (B, T, H, D) and out_cmp.flags.c_contiguous
+    for a in (q, k, v, g):
+        assert a.dtype == np.uint16 and a.shape == (B, T, H, D) and a.flags.c_contiguous
+    assert beta.dtype == np.uint16 and beta.shape == (B, T, H) and beta.flags.c_contiguous
+    if A_log is not None:
+        A_log = np.ascontiguousarray(A_log, dtype=np.float32)
+    if dt_bias is not None:
+        dt_bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+    N = B
+    if cu_seqlens is not None:
+        cu_seqlens = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        N = cu_seqlens.size - 1
+    sd = STATE_NONE
+    if initial_state is not None:
+        initial_state = np.ascontiguousarray(initial_state)
+        assert initial_state.shape == (N, H, D, D)
+        sd = {np.dtype(np.uint16): STATE_BF16, np.dtype(np.float32): STATE_FP32,
+              np.dtype(np.float64): STATE_FP64}[initial_state.dtype]
+    hsel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    n_sel = H if hsel is None else hsel.size
+    stats = np.zeros((N, n_sel, 3), dtype=np.float64)
+    fin = np.empty((N, n_sel, D, D), dtype=np.float64) if want_final else None
+    rc = lib().oracle_kda_fwd_compare(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                                      _ptr(A_log), _ptr(dt_bias), float(lower_bound), int(flags),
+                                      _ptr(initial_state), sd, _ptr(cu_seqlens), B, T, H, N, _ptr(hsel),
+                                      n_sel, _ptr(out_cmp), _ptr(stats), _ptr(fin), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_kda_fwd_compare rejected its arguments ({rc})")
+    return stats, fin
 
 
 def max_threads() -> int:

@@ -162,12 +162,12 @@ int oracle_core(int64_t T, int64_t K, int64_t V, const double *alpha, const doub
  *   nthreads <= 0 means the OpenMP default.
  * Returns 0 on success, nonzero on an argument error.
  */
-int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
-                   const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
-                   double lower_bound, int flags, const void *initial_state, int state_dtype,
-                   const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
-                   const int32_t *heads, int64_t n_heads, double *out, double *final_state,
-                   int nthreads)
+static int kda_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
+                        const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
+                        double lower_bound, int flags, const void *initial_state, int state_dtype,
+                        const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
+                        const int32_t *heads, int64_t n_heads, double *out, double *final_state,
+                        const uint16_t *out_cmp, double *stats, int nthreads)
 {
     const int64_t D = ORACLE_DIM;
     if (B < 1 || T < 0 || H < 1)
@@ -227,6 +227,8 @@ int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
             S[e] = s;
         }
 
+        if (stats)
+            stats[3 * chain] = stats[3 * chain + 1] = stats[3 * chain + 2] = 0.0;
         const double Alog = (flags & ORACLE_GATE_IN_KERNEL) ? (double)A_log[h] : 0.0;
         for (int64_t t = t0; t < t1; ++t) {
             const int64_t row = (t * H + h) * D;
@@ -263,6 +265,19 @@ int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                 for (int64_t c = 0; c < D; ++c)
                     o[c] = ot[c];
             }
+            if (out_cmp) {
+                /* streaming comparison with a bf16 output of the full [B*T][H][128] layout */
+                double *st = stats + 3 * chain;
+                const uint16_t *oc = out_cmp + (t * H + h) * D;
+                for (int64_t c = 0; c < D; ++c) {
+                    const double e = bf16_bits_to_double(oc[c]) - ot[c];
+                    const double ae = e < 0.0 ? -e : e;
+                    if (!(ae <= st[0]))  /* also records a NaN */
+                        st[0] = ae;
+                    st[1] += e * e;
+                    st[2] += ot[c] * ot[c];
+                }
+            }
         }
         if (final_state) {
             double *fs = final_state + (n * n_sel + hs) * D * D;
@@ -277,6 +292,40 @@ int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
         free(ot);
     }
     return 0;
+}
+
+int oracle_kda_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
+                   const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
+                   double lower_bound, int flags, const void *initial_state, int state_dtype,
+                   const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
+                   const int32_t *heads, int64_t n_heads, double *out, double *final_state,
+                   int nthreads)
+{
+    return kda_fwd_impl(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, flags, initial_state,
+                        state_dtype, cu_seqlens, B, T, H, N, heads, n_heads, out, final_state, NULL,
+                        NULL, nthreads);
+}
+
+/*
+ * The same forward pass, comparing instead of storing the output: out_cmp holds another
+ * implementation's output as bf16 bits in the full [B*T][H][128] layout, and for every
+ * selected chain (sequence n, selected head hs; index n * n_sel + hs) stats receives
+ * { max |out_cmp - out|, sum (out_cmp - out)^2, sum out^2 } with out the fp64 oracle
+ * value.  The fp64 output itself is never stored, so very long sequences can be checked
+ * in bounded memory.  final_state as in oracle_kda_fwd.  Test infrastructure only.
+ */
+int oracle_kda_fwd_compare(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
+                           const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
+                           double lower_bound, int flags, const void *initial_state, int state_dtype,
+                           const int64_t *cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t N,
+                           const int32_t *heads, int64_t n_heads, const uint16_t *out_cmp,
+                           double *stats, double *final_state, int nthreads)
+{
+    if (!out_cmp || !stats)
+        return 7;
+    return kda_fwd_impl(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, flags, initial_state,
+                        state_dtype, cu_seqlens, B, T, H, N, heads, n_heads, NULL, final_state, out_cmp,
+                        stats, nthreads);
 }
 
 /* Threads the OpenMP runtime would use by default (for reporting). */

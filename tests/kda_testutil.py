@@ -107,3 +107,45 @@ def bf16_round_f64(x):
     """Round float64 values to bf16 (via fp32) and return them as float64."""
     from gated_delta_rule_86_amd.workloads import f32_to_bf16_bits
     return bf16_bits_to_f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+# ---- segment plan of few long equal-length chains (replica of the host plan) ----
+PLAN_CUS = 256
+
+
+def segment_plan(chains, nch):
+    """(G, L): segments per chain and chunks per segment that the forward pass picks for
+    `chains` equal-length chains of `nch` chunks (G = 1: whole chains).  The cost counts
+    rounds of the CUs over pass A (2G-3 units per chain), pass B (G-1) and the scan."""
+    rounds = lambda u: -(-u // PLAN_CUS)
+    best, best_cost = (1, nch), None
+    if chains <= 0 or nch < 32 or chains >= 192:
+        return best
+    best_cost = rounds(chains) * nch
+    G = 2
+    while G <= 256 and G <= nch // 8:
+        L = -(-nch // G)
+        Gp = -(-nch // L)
+        if Gp >= 2:
+            cost = rounds(chains * (2 * Gp - 3)) * L + rounds(chains * (Gp - 1)) * L + 2 * Gp
+            if cost < best_cost:
+                best_cost, best = cost, (Gp, L)
+        G += 1
+    return best
+
+
+def table_bytes(N):
+    """Workspace bytes before the segment states: header, per-sequence tables, the
+    workgroup-run table and the unit list."""
+    up = lambda x: -(-x // 256) * 256
+    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N)
+
+
+def segment_states(ws, B, H, G):
+    """The fp32 segment states S, F, P of a segmented call, read back from its workspace:
+    three float64 arrays [B, H, G, 128, 128] (V-major)."""
+    n = B * H * G * 128 * 128
+    off = table_bytes(B)
+    raw = ws[off:off + 3 * 4 * n].cpu().numpy().view(np.float32).astype(np.float64)
+    S, F, P = (raw[i * n:(i + 1) * n].reshape(B, H, G, 128, 128) for i in range(3))
+    return S, F, P

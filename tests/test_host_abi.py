@@ -220,6 +220,20 @@ def test_forward_launches_of_reference_workloads():
     assert kda.forward_launches(256, 1, 32) == 1
 
 
+def test_segment_plan_replica():
+    """The tests' replica of the segment plan (kda_testutil.segment_plan) picks the same
+    number of segments as the library, read off the workspace size."""
+    from kda_testutil import segment_plan
+    for B, T, H in [(1, 700, 1), (1, 8192, 2), (1, 6000, 2), (3, 4096, 2), (2, 5000, 3), (1, 4103, 1),
+                    (1, 4096, 2), (2, 4096, 16), (1, 1 << 20, 8), (3, 1500, 2), (1, 1 << 20, 1),
+                    (1, 100, 4), (5, 4000, 40)]:
+        G, L = segment_plan(B * H, -(-T // 16))
+        extra = ws_size(B, T, H) - table_bytes(B)
+        got = 1 if extra == 0 else extra // (3 * B * H * 128 * 128 * 4)
+        assert got == G, (B, T, H, got, G)
+        assert G == 1 or -(-(-(-T // 16)) // L) == G
+
+
 def test_sequence_count_limit():
     """Unit codes hold the sequence index in 29 bits: N >= 2^29 is a shape error, and the
     workspace size is 0 for it."""

@@ -8,6 +8,7 @@ Each check follows from the definition stated in oracle/kda_ref.c (FlashKDA READ
   lower_bound = 0, beta = 1, orthonormal keys -> exact delta-rule overwrite (closed form)
   varlen batch        =  its sequences run separately;  B > 1 = varlen with equal lengths
   split + resume      =  one run
+  affine segment map  S_end(S0) = S0 P + F, P the run from S0 = I with v = 0, F from S0 = 0
   linearity           (v, S0) -> (2v, 2S0) doubles out and final state exactly
   gate / sigmoid / l2norm special values and ranges
 """
@@ -115,6 +116,26 @@ def test_split_and_resume(split):
                             w.A_log, w.dt_bias, w.lower_bound, f1)  # fp64 carry
     assert np.array_equal(np.concatenate([o1, o2], axis=1), out)
     assert np.array_equal(f2, fin)
+
+
+@pytest.mark.parametrize("lb", [0.0, -0.05, -1.0])
+def test_segment_map_is_affine(lb):
+    """The state after a token range is affine in the state before it: with P the range run
+    from the identity with v = 0 and F the range run from zero, S_end(S0) = S0 P + F
+    (every token's map S -> S Diag(alpha)(I - beta k k^T) + beta v k^T is affine, and so is
+    their composition).  The segmented forward pass stands on this."""
+    w = W.make("affine", 2, 37, 2, seed=29, lower_bound=lb, state_dtype="fp32")
+    S0 = w.initial_state.astype(np.float64)
+    eye = np.broadcast_to(np.eye(D), S0.shape).copy()
+    _, S_end = run(w)
+    _, F = oracle.kda_fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound,
+                          None, want_out=False)
+    _, P = oracle.kda_fwd(w.q, w.k, np.zeros_like(w.v), w.g, w.beta, w.scale, w.A_log, w.dt_bias,
+                          w.lower_bound, eye, want_out=False)
+    pred = np.einsum("bhvc,bhcd->bhvd", S0, P) + F
+    assert np.abs(pred - S_end).max() <= 1e-13 * max(1.0, np.abs(S_end).max())
+    # and P is not trivial here: the initial state still matters at the end
+    assert np.abs(np.einsum("bhvc,bhcd->bhvd", S0, P)).max() > 1e-6
 
 
 def test_linearity_bit_exact():
