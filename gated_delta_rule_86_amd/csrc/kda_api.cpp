@@ -136,6 +136,7 @@ const char *kda_status_string(int s)
     case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP launch or query failed";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_FLAGS: return "KDA_ERR_FLAGS: unknown activation switch bits";
+    case KDA_ERR_SCRATCH: return "KDA_ERR_SCRATCH: the call needs more than kda_fwd_noalloc's static scratch";
     default: return "KDA_ERR_UNKNOWN";
     }
 }

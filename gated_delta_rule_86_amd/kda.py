@@ -27,7 +27,9 @@ STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_HEAD_DIM", 4: "KDA_ERR_DTYPE",
     5: "KDA_ERR_LOWER_BOUND", 6: "KDA_ERR_SCALE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_WORKSPACE",
     9: "KDA_ERR_CU_SEQLENS", 10: "KDA_ERR_HIP", 11: "KDA_ERR_ALIAS", 12: "KDA_ERR_FLAGS",
+    13: "KDA_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # KDA_NOALLOC_SCRATCH_BYTES
 # activation switches of kda_fwd_ex (include/kda.h)
 GATE_IN_KERNEL, QK_L2NORM_IN_KERNEL, BETA_SIGMOID_IN_KERNEL = 1, 2, 4
 ALL_IN_KERNEL = 7
@@ -35,7 +37,7 @@ STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_recurrent", "kda_fwd_recurrent_timed", "kda_fwd_timed",
-           "kda_fwd_workspace_size",
+           "kda_fwd_noalloc", "kda_fwd_workspace_size",
            "kda_status_string",
            "kda_fwd_device_status", "kda_chunk_table", "kda_version")
 
@@ -70,6 +72,8 @@ def lib():
     L.kda_fwd_recurrent_timed.argtypes = L.kda_fwd_recurrent.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     L.kda_fwd_timed.restype = ctypes.c_int
     L.kda_fwd_timed.argtypes = L.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+    L.kda_fwd_noalloc.restype = ctypes.c_int
+    L.kda_fwd_noalloc.argtypes = L.kda_fwd.argtypes[:22] + [vp, ctypes.c_uint32]
     L.kda_fwd_workspace_size.restype = ctypes.c_size_t
     L.kda_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -133,10 +137,23 @@ def fwd_recurrent(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, ini
                final_state, cu_seqlens, _recurrent=True, **kw)
 
 
+def fwd_noalloc(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
+                final_state=None, cu_seqlens=None, **kw):
+    """The same forward pass through kda_fwd_noalloc: no workspace, the library's static
+    device scratch (NOALLOC_SCRATCH_BYTES per GPU) instead; calls that overlap on one GPU
+    race.  Same arguments and keywords as ``fwd`` except workspace and stage_events.
+    Raises KDAError(KDA_ERR_SCRATCH) for problems whose workspace would exceed the scratch."""
+    for bad in ("workspace", "stage_events"):
+        if kw.get(bad) is not None:
+            raise ValueError(f"fwd_noalloc takes no {bad}")
+    return fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+               final_state, cu_seqlens, _noalloc=True, **kw)
+
+
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
         final_state=None, cu_seqlens=None, *, cu_seqlens_host=None, workspace=None, stream=None,
         stage_events=None, use_gate_in_kernel=True, use_qk_l2norm_in_kernel=True,
-        use_beta_sigmoid_in_kernel=True, _recurrent=False):
+        use_beta_sigmoid_in_kernel=True, _recurrent=False, _noalloc=False):
     """KDA forward pass on torch device tensors; writes ``out`` and ``final_state`` in place.
 
     q, k, v, g: bf16 [B, T, H, 128]; beta: bf16 [B, T, H]; out: bf16 [B, T, H, 128];
@@ -188,6 +205,16 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     if cu_seqlens_host is not None:
         import numpy as np
         host_cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int64))
+    if _noalloc:
+        st = L.kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                               _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                               _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+                               _ptr(cu_seqlens), None if host_cu is None else host_cu.ctypes.data,
+                               B, T, H, N if cu_seqlens is not None else B, K, V,
+                               _stream_handle(stream, q.device), flags)
+        if st != KDA_OK:
+            raise KDAError(st, "kda_fwd_noalloc")
+        return None
     ws_bytes = workspace_size(B, T, H, N if cu_seqlens is not None else B, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)

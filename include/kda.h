@@ -20,13 +20,15 @@
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
  *   - The caller owns every buffer; the library allocates no device memory.  Scratch
- *     space comes from the caller's workspace (size from kda_fwd_workspace_size).
+ *     space comes from the caller's workspace (size from kda_fwd_workspace_size), except
+ *     for kda_fwd_noalloc, which uses a static device array of the library.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
  *     asynchronously; no entry point synchronises the host except kda_fwd_device_status.
  *   - Arguments are fully validated on the host before anything is launched; on any
  *     error nothing is launched and an error status is returned.  Nothing throws.
- *   - No global mutable state; entry points are safe to call from several host threads
- *     on different streams with different workspaces.
+ *   - No global mutable state besides kda_fwd_noalloc's scratch and its per-device
+ *     address; the other entry points are safe to call from several host threads on
+ *     different streams with different workspaces.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -54,7 +56,8 @@ typedef enum kda_status {
     KDA_ERR_CU_SEQLENS = 9,  /* cu_seqlens_host given and cu[0] != 0, decreasing, or cu[N] != T */
     KDA_ERR_HIP = 10,        /* a HIP launch or query failed */
     KDA_ERR_ALIAS = 11,      /* out overlaps an input, or final_state overlaps a non-state input */
-    KDA_ERR_FLAGS = 12       /* kda_fwd_ex: unknown bits in the activation switch mask */
+    KDA_ERR_FLAGS = 12,      /* kda_fwd_ex: unknown bits in the activation switch mask */
+    KDA_ERR_SCRATCH = 13     /* kda_fwd_noalloc: the call needs more than KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum kda_state_dtype {
@@ -194,6 +197,32 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
                          const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
                          int64_t K, int64_t V, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *stage_events);
+
+/*
+ * kda_fwd_noalloc -- kda_fwd_ex for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * layouts, ownership, activation switches, results and errors as kda_fwd_ex, without the
+ * workspace arguments: the library's own static device scratch of KDA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB; one copy on every GPU the library runs on, held until the process ends) serves
+ * as the workspace.  The call allocates nothing.
+ *   - Returns KDA_ERR_SCRATCH, before any HIP call, when kda_fwd_workspace_size for these
+ *     sizes exceeds KDA_NOALLOC_SCRATCH_BYTES (e.g. very many sequences, or many long
+ *     equal-length chains that run as segments).
+ *   - The scratch belongs to the device of `stream` (the current device for NULL); its
+ *     address is looked up once per device.  Calls on one GPU share it: two calls that
+ *     overlap in time on one GPU (different streams, or host threads) race and give
+ *     undefined results; serialise them.  Every word a call reads from the scratch is
+ *     written earlier in the same call, so nothing needs clearing between calls.
+ *   - kda_fwd_device_status cannot read this call's status word (it is not in a caller's
+ *     buffer); validation errors are still returned.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+kda_status kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           float scale, void *out, const float *A_log, const float *dt_bias,
+                           float lower_bound, const void *initial_state, kda_state_dtype initial_state_dtype,
+                           void *final_state, kda_state_dtype final_state_dtype, const int64_t *cu_seqlens,
+                           const int64_t *cu_seqlens_host, int64_t B, int64_t T, int64_t H, int64_t N,
+                           int64_t K, int64_t V, void *stream, uint32_t flags);
 
 /*
  * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs: the status word, the

@@ -220,6 +220,26 @@ def test_forward_launches_of_reference_workloads():
     assert kda.forward_launches(256, 1, 32) == 1
 
 
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """kda_fwd_noalloc checks the workspace its sizes need against its static scratch
+    (KDA_NOALLOC_SCRATCH_BYTES) before any HIP call: KDA_ERR_SCRATCH, nothing launched."""
+    L = kda.lib()
+    cap = kda.NOALLOC_SCRATCH_BYTES
+    a = Args(T=16)
+    for N in (1 << 21, 1 << 22):
+        T = 2 * N
+        assert ws_size(1, T, 1, N, True) > cap
+        st = L.kda_fwd_noalloc(a.q, a.k, a.v, a.g, a.beta, a.scale, a.out, a.A_log, a.dt_bias, a.lb,
+                               None, kda.STATE_NONE, None, kda.STATE_NONE, 1 << 33, None, 1, T, 1, N,
+                               128, 128, None, 7)
+        assert st == 13, st  # KDA_ERR_SCRATCH
+    # every reference workload fits (the 2^20-token one, segmented, needs the most)
+    for B, T, H, N, varlen in [(1, 1 << 20, 8, 0, False), (2, 4096, 16, 0, False), (1, 31094, 32, 8, True),
+                               (1, 66285, 32, 256, True), (256, 1, 32, 0, False)]:
+        assert ws_size(B, T, H, N, varlen) <= cap, (B, T, H)
+    assert L.kda_status_string(13).decode().startswith("KDA_ERR_SCRATCH")
+
+
 def test_segment_plan_replica():
     """The tests' replica of the segment plan (kda_testutil.segment_plan) picks the same
     number of segments as the library, read off the workspace size."""
