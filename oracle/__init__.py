@@ -6,6 +6,7 @@ under ``gated_delta_rule_86_amd/`` and never imports it.
 
 Contents
   kda_ref.c   plain C token-by-token fp64 recurrence (the oracle proper)
+  kda_bwd_ref.c  its reverse-mode derivative (gradients of out and final state), fp64
   chunked.py  independent NumPy fp64 chunked form (any chunk size) + Neumann inverse
   exact.py    exact-rational (fractions.Fraction) brute force of the core recurrence
 
@@ -22,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_ref.c")
+_SRCS = [_SRC, os.path.join(_HERE, "kda_bwd_ref.c")]
 _LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
 
 STATE_NONE, STATE_BF16, STATE_FP32, STATE_FP64 = 0, 1, 2, 3
@@ -33,11 +35,12 @@ _lib = None
 
 
 def build(force: bool = False) -> str:
-    """Compile kda_ref.c into libkda_oracle.so with gcc (strict IEEE, OpenMP)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    """Compile kda_ref.c and kda_bwd_ref.c into libkda_oracle.so with gcc (strict IEEE, OpenMP)."""
+    stale = not os.path.exists(_LIB_PATH) or any(os.path.getmtime(_LIB_PATH) < os.path.getmtime(f) for f in _SRCS)
+    if force or stale:
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-               "-ffp-contract=off", "-std=c11", "-o", tmp, _SRC, "-lm"]
+               "-ffp-contract=off", "-std=c11", "-o", tmp, *_SRCS, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -70,6 +73,13 @@ def lib():
         L.oracle_kda_fwd_compare.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
                                              ctypes.c_int, vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, i64,
                                              vp, vp, vp, ctypes.c_int]
+        L.oracle_core_bwd.restype = ctypes.c_int
+        L.oracle_core_bwd.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, vp,
+                                      dp, dp, dp, dp, dp, dp, vp]
+        L.oracle_kda_bwd.restype = ctypes.c_int
+        L.oracle_kda_bwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, vp, vp, ctypes.c_double,
+                                     ctypes.c_int, vp, ctypes.c_int, vp, i64, i64, i64, i64, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         _lib = L
@@ -217,6 +227,76 @@ def kda_fwd_compare(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, out_cm
     if rc != 0:
         raise ValueError(f"oracle_kda_fwd_compare rejected its arguments ({rc})")
     return stats, fin
+
+
+def core_bwd(alpha, beta, kn, qn, v, scale, S0, dout, dST=None, want_out=False):
+    """Reverse mode of steps 4-7 on already-activated inputs (any K, V).
+
+    alpha, kn, qn: [T, K]; beta: [T]; v, dout: [T, V]; S0, dST: [V, K].  Returns a dict
+    of float64 arrays: dalpha, dkn, dqn [T, K]; dbeta [T]; dv [T, V]; dS0 [V, K]
+    (and out [T, V], the recomputed read-out, when want_out).
+    """
+    c = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+    alpha, beta, kn, qn, v, S0, dout = map(c, (alpha, beta, kn, qn, v, S0, dout))
+    T, K = alpha.shape
+    V = v.shape[1]
+    dST = None if dST is None else c(dST)
+    r = {"dalpha": np.zeros((T, K)), "dkn": np.zeros((T, K)), "dqn": np.zeros((T, K)),
+         "dbeta": np.zeros(T), "dv": np.zeros((T, V)), "dS0": np.zeros((V, K))}
+    out = np.zeros((T, V)) if want_out else None
+    rc = lib().oracle_core_bwd(T, K, V, _dptr(alpha), _dptr(beta), _dptr(kn), _dptr(qn), _dptr(v),
+                               float(scale), _dptr(S0), _dptr(dout), _ptr(dST), _dptr(r["dalpha"]),
+                               _dptr(r["dbeta"]), _dptr(r["dkn"]), _dptr(r["dqn"]), _dptr(r["dv"]),
+                               _dptr(r["dS0"]), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_core_bwd failed ({rc})")
+    if want_out:
+        r["out"] = out
+    return r
+
+
+def kda_bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, dout, initial_state=None,
+            dht=None, cu_seqlens=None, nthreads=0, flags=ALL_IN_KERNEL):
+    """Gradients of the oracle forward pass (kda_bwd_ref.c) on host arrays.
+
+    Inputs as ``kda_fwd``; dout: uint16 bf16 bits [B, T, H, 128] (dL/dout); dht: None or
+    float32 [N, H, 128, 128] (dL/dfinal_state).  Returns a dict of float64 arrays:
+    dq, dk, dv, dg [B, T, H, 128]; dbeta [B, T, H]; dA_log [H]; ddt_bias [H, 128];
+    dh0 [N, H, 128, 128].
+    """
+    B, T, H, D = q.shape
+    for a in (q, k, v, g, dout):
+        assert a.dtype == np.uint16 and a.shape == (B, T, H, D) and a.flags.c_contiguous
+    assert beta.dtype == np.uint16 and beta.shape == (B, T, H) and beta.flags.c_contiguous
+    if A_log is not None:
+        A_log = np.ascontiguousarray(A_log, dtype=np.float32)
+    if dt_bias is not None:
+        dt_bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+    N = B
+    if cu_seqlens is not None:
+        cu_seqlens = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        N = cu_seqlens.size - 1
+    sd = STATE_NONE
+    if initial_state is not None:
+        initial_state = np.ascontiguousarray(initial_state)
+        sd = {np.dtype(np.uint16): STATE_BF16, np.dtype(np.float32): STATE_FP32,
+              np.dtype(np.float64): STATE_FP64}[initial_state.dtype]
+    if dht is not None:
+        dht = np.ascontiguousarray(dht, dtype=np.float32)
+        assert dht.shape == (N, H, D, D)
+    r = {n: np.zeros((B, T, H, D)) for n in ("dq", "dk", "dv", "dg")}
+    r["dbeta"] = np.zeros((B, T, H))
+    r["dA_log"] = np.zeros(H)
+    r["ddt_bias"] = np.zeros((H, D))
+    r["dh0"] = np.zeros((N, H, D, D))
+    rc = lib().oracle_kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
+                              _ptr(dt_bias), float(lower_bound), int(flags), _ptr(initial_state), sd,
+                              _ptr(cu_seqlens), B, T, H, N, _ptr(dout), _ptr(dht), _ptr(r["dq"]),
+                              _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dg"]), _ptr(r["dbeta"]),
+                              _ptr(r["dA_log"]), _ptr(r["ddt_bias"]), _ptr(r["dh0"]), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_kda_bwd failed ({rc})")
+    return r
 
 
 def max_threads() -> int:

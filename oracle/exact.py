@@ -36,3 +36,73 @@ def core_exact(alpha, beta, kn, qn, v, scale, S0):
         out.append([scale * sum((S[i][c] * Fraction(qn[t][c]) for c in range(K)), Fraction(0))
                     for i in range(V)])
     return out, S
+
+
+class Dual:
+    """a + b eps with eps^2 = 0, over Fractions: exact forward-mode derivatives of a
+    polynomial computation."""
+    __slots__ = ("a", "b")
+
+    def __init__(self, a, b=0):
+        self.a = Fraction(a)
+        self.b = Fraction(b)
+
+    def _c(self, o):
+        return o if isinstance(o, Dual) else Dual(o)
+
+    def __add__(self, o):
+        o = self._c(o)
+        return Dual(self.a + o.a, self.b + o.b)
+
+    __radd__ = __add__
+
+    def __sub__(self, o):
+        o = self._c(o)
+        return Dual(self.a - o.a, self.b - o.b)
+
+    def __rsub__(self, o):
+        return self._c(o) - self
+
+    def __mul__(self, o):
+        o = self._c(o)
+        return Dual(self.a * o.a, self.a * o.b + self.b * o.a)
+
+    __rmul__ = __mul__
+
+
+def core_exact_jvp(alpha, beta, kn, qn, v, scale, S0, tangents):
+    """The core recurrence (as core_exact) on dual numbers: every input x carries the tangent
+    tangents[name] (same nesting as the input; names alpha, beta, kn, qn, v, S0).  Returns
+    (out, S) as nested lists of Dual; the .b parts are the exact directional derivatives."""
+    def lift(x, dx):
+        if isinstance(x, list):
+            return [lift(a, b) for a, b in zip(x, dx)]
+        return Dual(x, dx)
+
+    A = lift(alpha, tangents["alpha"])
+    Bt = lift(beta, tangents["beta"])
+    Kn = lift(kn, tangents["kn"])
+    Qn = lift(qn, tangents["qn"])
+    Vv = lift(v, tangents["v"])
+    S = lift(S0, tangents["S0"])
+    T, Vd, K = len(alpha), len(S0), len(S0[0])
+    out = []
+    for t in range(T):
+        for i in range(Vd):
+            for c in range(K):
+                S[i][c] = S[i][c] * A[t][c]
+        for i in range(Vd):
+            pred = Dual(0)
+            for c in range(K):
+                pred = pred + S[i][c] * Kn[t][c]
+            r = Vv[t][i] - pred
+            for c in range(K):
+                S[i][c] = S[i][c] + Bt[t] * r * Kn[t][c]
+        row = []
+        for i in range(Vd):
+            acc = Dual(0)
+            for c in range(K):
+                acc = acc + S[i][c] * Qn[t][c]
+            row.append(acc * scale)
+        out.append(row)
+    return out, S
