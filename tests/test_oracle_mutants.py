@@ -62,7 +62,8 @@ def mutant_oracle(name):
     with tempfile.TemporaryDirectory() as d:
         c, so = os.path.join(d, "m.c"), os.path.join(d, "libm.so")
         open(c, "w").write(src)
-        subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-o", so, c, "-lm"],
+        bwd = os.path.join(os.path.dirname(oracle.__file__), "kda_bwd_ref.c")  # unchanged
+        subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-o", so, c, bwd, "-lm"],
                        check=True)
         saved_lib, saved_path = oracle._lib, oracle._LIB_PATH
         oracle._lib, oracle._LIB_PATH = None, so
