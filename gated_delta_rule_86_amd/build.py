@@ -2,8 +2,8 @@
 
     python -m gated_delta_rule_86_amd.build
 
-Compiles csrc/kda_kernels.hip, csrc/kda_recurrent.hip and csrc/kda_noalloc.hip (device code)
-and csrc/kda_api.cpp (host C ABI) into
+Compiles csrc/kda_kernels.hip, csrc/kda_recurrent.hip, csrc/kda_noalloc.hip and
+csrc/kda_backward.hip (device code) and csrc/kda_api.cpp (host C ABI) into
 gated_delta_rule_86_amd/libkda.so.  Always rebuilds.
 """
 from __future__ import annotations
@@ -42,7 +42,8 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_recurrent.hip"),
-            os.path.join(CSRC, "kda_noalloc.hip"), os.path.join(CSRC, "kda_api.cpp")]
+            os.path.join(CSRC, "kda_noalloc.hip"), os.path.join(CSRC, "kda_backward.hip"),
+            os.path.join(CSRC, "kda_api.cpp")]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:

@@ -353,3 +353,151 @@ kda_status kda_chunk_table(const int64_t *cu_seqlens, int64_t B, int64_t T, int6
 }
 
 }  // extern "C"
+
+namespace {
+
+// Everything kda_bwd checks before touching the device.
+kda_status validate_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                        float scale, const float *A_log, const float *dt_bias, float lower_bound,
+                        const void *h0, kda_state_dtype h0_dt, const void *dout, const float *dht,
+                        const float *dq, const float *dk, const float *dv, const float *dg,
+                        const float *dbeta, const float *dA_log, const float *ddt, const float *dh0,
+                        const int64_t *cu, const int64_t *cu_host, int64_t B, int64_t T, int64_t H,
+                        int64_t N, int64_t K, int64_t V, const void *ws, size_t ws_bytes, uint32_t flags,
+                        kda::BwdLayout *bl)
+{
+    if ((flags & ~KDA_ALL_IN_KERNEL) != 0)
+        return KDA_ERR_FLAGS;
+    const bool gate_in = (flags & KDA_GATE_IN_KERNEL) != 0;
+    const bool tokens = T > 0;
+    if ((tokens && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta)) ||
+        (gate_in && (!A_log || !dt_bias)))
+        return KDA_ERR_NULL;
+    if (B < 1 || T < 0 || H < 1)
+        return KDA_ERR_SHAPE;
+    if (cu) {
+        if (B != 1 || N < 1)
+            return KDA_ERR_SHAPE;
+    } else if (N != 0 && N != B) {
+        return KDA_ERR_SHAPE;
+    }
+    if (T > ((int64_t)1 << 40) / B || (B * T) > ((int64_t)1 << 46) / (H * kda::kD) || T >= ((int64_t)1 << 35))
+        return KDA_ERR_SHAPE;
+    if (K != kda::kD || V != kda::kD)
+        return KDA_ERR_HEAD_DIM;
+    if (!(h0_dt == KDA_STATE_NONE || h0_dt == KDA_STATE_BF16 || h0_dt == KDA_STATE_FP32) ||
+        (h0 == nullptr) != (h0_dt == KDA_STATE_NONE))
+        return KDA_ERR_DTYPE;
+    if (!(lower_bound >= -5.0f && lower_bound <= 0.0f))
+        return KDA_ERR_LOWER_BOUND;
+    if (!isfinite(scale))
+        return KDA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(dout, 16) ||
+        !aligned(beta, 2) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dg, 16) ||
+        !aligned(dbeta, 4) || (gate_in && (!aligned(A_log, 4) || !aligned(dt_bias, 16))) ||
+        (dA_log && !aligned(dA_log, 4)) || (ddt && !aligned(ddt, 16)) || (h0 && !aligned(h0, 16)) ||
+        (dht && !aligned(dht, 16)) || (dh0 && !aligned(dh0, 16)) || (cu && !aligned(cu, 8)) ||
+        (ws && !aligned(ws, kda::kAlign)))
+        return KDA_ERR_ALIGN;
+    const int64_t n_seq = cu ? N : B;
+    const size_t tokh = (size_t)B * (size_t)T * (size_t)H;
+    const size_t st = (size_t)n_seq * (size_t)H * kda::kD * kda::kD;
+    const Range ins[] = {range_of(q, tokh * kda::kD * 2), range_of(k, tokh * kda::kD * 2),
+                         range_of(v, tokh * kda::kD * 2), range_of(g, tokh * kda::kD * 2),
+                         range_of(beta, tokh * 2), range_of(dout, tokh * kda::kD * 2),
+                         range_of(h0, h0 ? st * state_elem_bytes(h0_dt) : 0), range_of(dht, dht ? st * 4 : 0),
+                         range_of(A_log, gate_in ? (size_t)H * 4 : 0),
+                         range_of(dt_bias, gate_in ? (size_t)H * kda::kD * 4 : 0)};
+    const Range outs[] = {range_of(dq, tokh * kda::kD * 4), range_of(dk, tokh * kda::kD * 4),
+                          range_of(dv, tokh * kda::kD * 4), range_of(dg, tokh * kda::kD * 4),
+                          range_of(dbeta, tokh * 4), range_of(dA_log, dA_log ? (size_t)H * 4 : 0),
+                          range_of(ddt, ddt ? (size_t)H * kda::kD * 4 : 0), range_of(dh0, dh0 ? st * 4 : 0)};
+    for (const Range &o : outs) {
+        for (const Range &i : ins)
+            if (overlap(o, i))
+                return KDA_ERR_ALIAS;
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlap(o, o2))
+                return KDA_ERR_ALIAS;
+    }
+    if (!kda::make_bwd_layout(B, T, H, cu ? N : 0, cu != nullptr, bl))
+        return KDA_ERR_SHAPE;
+    if (!ws || ws_bytes < bl->total)
+        return KDA_ERR_WORKSPACE;
+    if (cu && cu_host) {
+        if (cu_host[0] != 0 || cu_host[N] != T)
+            return KDA_ERR_CU_SEQLENS;
+        for (int64_t i = 0; i < N; ++i)
+            if (cu_host[i + 1] < cu_host[i])
+                return KDA_ERR_CU_SEQLENS;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens)
+{
+    kda::BwdLayout bl;
+    if (!kda::make_bwd_layout(B, T, H, has_cu_seqlens ? N : (N == B ? B : 0), has_cu_seqlens != 0, &bl))
+        return 0;
+    return bl.total;
+}
+
+kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta, float scale,
+                   const float *A_log, const float *dt_bias, float lower_bound, const void *initial_state,
+                   kda_state_dtype initial_state_dtype, const void *dout, const float *dfinal_state, float *dq,
+                   float *dk, float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                   float *dinitial_state, const int64_t *cu_seqlens, const int64_t *cu_seqlens_host, int64_t B,
+                   int64_t T, int64_t H, int64_t N, int64_t K, int64_t V, void *workspace,
+                   size_t workspace_bytes, void *stream, uint32_t flags)
+{
+    kda::BwdLayout bl;
+    kda_status st = validate_bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state,
+                                 initial_state_dtype, dout, dfinal_state, dq, dk, dv, dg, dbeta, dA_log,
+                                 ddt_bias, dinitial_state, cu_seqlens, cu_seqlens_host, B, T, H, N, K, V,
+                                 workspace, workspace_bytes, flags, &bl);
+    if (st != KDA_OK)
+        return st;
+    kda::BwdLaunch a;
+    memset(&a, 0, sizeof a);
+    a.fwd.q = static_cast<const uint16_t *>(q);
+    a.fwd.k = static_cast<const uint16_t *>(k);
+    a.fwd.v = static_cast<const uint16_t *>(v);
+    a.fwd.g = static_cast<const uint16_t *>(g);
+    a.fwd.beta = static_cast<const uint16_t *>(beta);
+    a.fwd.A_log = A_log;
+    a.fwd.dt_bias = dt_bias;
+    a.fwd.scale = scale;
+    a.fwd.lower_bound = lower_bound;
+    a.fwd.flags = (int)flags;
+    a.fwd.h0 = initial_state;
+    a.fwd.h0_dtype = (int)initial_state_dtype;
+    a.fwd.cu = cu_seqlens;
+    a.fwd.B = B;
+    a.fwd.T = T;
+    a.fwd.H = H;
+    a.fwd.N = bl.tab.n_seq;
+    a.fwd.ws = static_cast<unsigned char *>(workspace);
+    a.fwd.lay = bl.tab;
+    a.bl = bl;
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.dht = dfinal_state;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dg = dg;
+    a.dbeta = dbeta;
+    a.dA_log = (flags & KDA_GATE_IN_KERNEL) ? dA_log : nullptr;
+    a.ddt = (flags & KDA_GATE_IN_KERNEL) ? ddt_bias : nullptr;
+    a.dh0 = dinitial_state;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::launch_chunk_table(a.fwd, s, false) != hipSuccess || kda::launch_backward(a, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+}  // extern "C"
+

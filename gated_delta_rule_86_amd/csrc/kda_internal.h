@@ -152,11 +152,57 @@ struct FwdArgs {
     Layout lay;
 };
 
+// Workspace of the backward pass: the chunk table (as the forward pass lays it out, up to
+// the segment states, which the backward pass does not use), then per token-head the
+// activated k^, q^ and alpha (fp32 [tokens][H][128]) and 1/|k|, 1/|q|, beta (fp32
+// [tokens][H]), the state before every 16-token chunk of every chain (fp32 128 x 128 each),
+// and one 16-state buffer per chain for the chunk being reversed.
+struct BwdLayout {
+    Layout tab;
+    size_t off_kn, off_qn, off_al, off_rk, off_rq, off_bt, off_ckpt, off_buf;
+    size_t total;
+};
+
+inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, BwdLayout *L)
+{
+    if (!make_layout(B, T, H, N, varlen, &L->tab))
+        return false;
+    const size_t tok = (size_t)B * (size_t)T * (size_t)H;
+    const size_t state = (size_t)kD * kD * sizeof(float);
+    const size_t chunks = varlen ? (size_t)cdiv(T, kCH) + (size_t)L->tab.n_seq : (size_t)B * (size_t)cdiv(T, kCH);
+    size_t off = L->tab.off_seg;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = round_up(off + bytes, kAlign);
+        return o;
+    };
+    L->off_kn = take(tok * kD * sizeof(float));
+    L->off_qn = take(tok * kD * sizeof(float));
+    L->off_al = take(tok * kD * sizeof(float));
+    L->off_rk = take(tok * sizeof(float));
+    L->off_rq = take(tok * sizeof(float));
+    L->off_bt = take(tok * sizeof(float));
+    L->off_ckpt = take(chunks * (size_t)H * state);
+    L->off_buf = take((size_t)L->tab.n_seq * (size_t)H * kCH * state);
+    L->total = off;
+    return true;
+}
+
+struct BwdLaunch {
+    FwdArgs fwd;  // inputs, activation switches, workspace (fwd.lay = bl.tab)
+    BwdLayout bl;
+    const uint16_t *dout;  // bf16 [B, T, H, 128]
+    const float *dht;      // fp32 [N, H, 128, 128] or NULL
+    float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt, *dh0;
+};
+
 // plan: also write the whole-chain workgroup plan (the forward pass reads it; the
 // token-by-token path does not)
 hipError_t launch_chunk_table(const FwdArgs &a, hipStream_t s, bool plan = true);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t s, hipEvent_t const *marks);
 // token-by-token evaluation, one workgroup per chain (kda_recurrent.hip)
 hipError_t launch_recurrent(const FwdArgs &a, hipStream_t s);
+// gradients (kda_backward.hip); the chunk table must have been launched first
+hipError_t launch_backward(const BwdLaunch &a, hipStream_t s);
 
 }  // namespace kda

@@ -37,7 +37,7 @@ STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_recurrent", "kda_fwd_recurrent_timed", "kda_fwd_timed",
-           "kda_fwd_noalloc", "kda_fwd_workspace_size",
+           "kda_fwd_noalloc", "kda_fwd_workspace_size", "kda_bwd", "kda_bwd_workspace_size",
            "kda_status_string",
            "kda_fwd_device_status", "kda_chunk_table", "kda_version")
 
@@ -74,6 +74,12 @@ def lib():
     L.kda_fwd_timed.argtypes = L.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     L.kda_fwd_noalloc.restype = ctypes.c_int
     L.kda_fwd_noalloc.argtypes = L.kda_fwd.argtypes[:22] + [vp, ctypes.c_uint32]
+    L.kda_bwd.restype = ctypes.c_int
+    L.kda_bwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, f32, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                          vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, ctypes.c_size_t, vp,
+                          ctypes.c_uint32]
+    L.kda_bwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     L.kda_fwd_workspace_size.restype = ctypes.c_size_t
     L.kda_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -244,6 +250,66 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     if st != KDA_OK:
         raise KDAError(st)
     return workspace
+
+
+def bwd_workspace_size(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -> int:
+    return int(lib().kda_bwd_workspace_size(B, T, H, N, 1 if varlen else 0))
+
+
+def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, dout, initial_state=None,
+        dfinal_state=None, cu_seqlens=None, *, cu_seqlens_host=None, workspace=None, stream=None,
+        use_gate_in_kernel=True, use_qk_l2norm_in_kernel=True, use_beta_sigmoid_in_kernel=True):
+    """Gradients of ``fwd``'s out and final_state (kda_bwd in include/kda.h).
+
+    Inputs as ``fwd``; dout: bf16 [B, T, H, 128] (dL/dout); dfinal_state: None or fp32
+    [N, H, 128, 128] (dL/dfinal_state).  Returns a dict of fp32 device tensors: dq, dk, dv,
+    dg [B, T, H, 128]; dbeta [B, T, H]; dA_log [H] and dt_bias [H, 128] (with the gate
+    switch on); dinitial_state [N, H, 128, 128]; and the workspace used.
+    """
+    import torch
+    L = lib()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("g", g), ("v", v), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, T, H, K) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [B, T, H, K] tensor")
+    if beta.dtype != torch.bfloat16 or tuple(beta.shape) != (B, T, H) or not beta.is_contiguous():
+        raise ValueError("beta must be a contiguous bf16 [B, T, H] tensor")
+    flags = ((GATE_IN_KERNEL if use_gate_in_kernel else 0) |
+             (QK_L2NORM_IN_KERNEL if use_qk_l2norm_in_kernel else 0) |
+             (BETA_SIGMOID_IN_KERNEL if use_beta_sigmoid_in_kernel else 0))
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if dfinal_state is not None and (dfinal_state.dtype != torch.float32 or tuple(dfinal_state.shape) != (N, H, V, K)
+                                     or not dfinal_state.is_contiguous()):
+        raise ValueError("dfinal_state must be a contiguous fp32 [N, H, V, K] tensor")
+    dev = q.device
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    r = {"dq": f32(B, T, H, K), "dk": f32(B, T, H, K), "dv": f32(B, T, H, V), "dg": f32(B, T, H, K),
+         "dbeta": f32(B, T, H), "dinitial_state": f32(N, H, V, K)}
+    if use_gate_in_kernel:
+        r["dA_log"] = f32(H)
+        r["ddt_bias"] = f32(H, K)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        import numpy as np
+        host_cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int64))
+    ws_bytes = bwd_workspace_size(B, T, H, N if cu_seqlens is not None else B, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        if stream is not None and stream != torch.cuda.current_stream(dev):
+            workspace.record_stream(stream)
+    st = L.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log), _ptr(dt_bias),
+                   float(lower_bound), _ptr(initial_state), _state_code(initial_state), _ptr(dout),
+                   _ptr(dfinal_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dg"]),
+                   _ptr(r["dbeta"]), _ptr(r.get("dA_log")), _ptr(r.get("ddt_bias")),
+                   _ptr(r["dinitial_state"]), _ptr(cu_seqlens),
+                   None if host_cu is None else host_cu.ctypes.data, B, T, H,
+                   N if cu_seqlens is not None else B, K, V, _ptr(workspace),
+                   workspace.numel() * workspace.element_size(), _stream_handle(stream, dev), flags)
+    if st != KDA_OK:
+        raise KDAError(st, "kda_bwd")
+    r["workspace"] = workspace
+    return r
 
 
 def device_status(workspace, stream=None) -> int:

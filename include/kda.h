@@ -1,8 +1,9 @@
 /*
  * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library (libkda.so).
  *
- * The one operation is the chunked forward pass of KDA as the "Kernel API" table of the
- * FlashKDA README ("MoonshotAI/FlashKDA" repository page) states it:
+ * The operation is the chunked forward pass of KDA as the "Kernel API" table of the
+ * FlashKDA README ("MoonshotAI/FlashKDA" repository page) states it (plus, in kda_bwd,
+ * its gradients):
  *
  *   fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
  *       initial_state=None, final_state=None, cu_seqlens=None)
@@ -237,6 +238,48 @@ kda_status kda_fwd_noalloc(const void *q, const void *k, const void *v, const vo
  * Returns 0 for invalid sizes.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
+
+/*
+ * kda_bwd -- gradients of kda_fwd_ex's outputs (out and final_state) with respect to its
+ * inputs, for training.  The pages describe the forward pass only; this is the reverse-mode
+ * derivative of the same per-token recurrence (stated in the comment at the top of this
+ * file), under the same activation switches.  All arithmetic is fp32; the inputs q, k, v,
+ * g, beta, scale, A_log, dt_bias, lower_bound, initial_state, cu_seqlens, B, T, H, N, K, V
+ * and flags mean exactly what they mean for kda_fwd_ex.
+ *   dout          bf16 [B, T, H, 128], 16-byte aligned: dL/dout.
+ *   dfinal_state  NULL (zero) or fp32 [N, H, 128, 128], 16-byte aligned: dL/dfinal_state.
+ *   dq, dk, dv, dg  fp32 [B, T, H, 128], 16-byte aligned, fully written: dL/dq, dL/dk,
+ *                 dL/dv and dL/dg (with the gate switch off, g is the log-decay itself and
+ *                 its gradient is zero where g lies outside (lower_bound, 0)).
+ *   dbeta         fp32 [B, T, H], 4-byte aligned: dL/dbeta (the logit when the sigmoid runs
+ *                 in the pass).
+ *   dA_log        NULL or fp32 [H]; ddt_bias  NULL or fp32 [H, 128] (16-byte aligned):
+ *                 summed over every token of every sequence.  Written only with the gate
+ *                 switch on (KDA_GATE_IN_KERNEL); NULL = not written.
+ *   dinitial_state  NULL (not written) or fp32 [N, H, 128, 128], 16-byte aligned: dL/d
+ *                 initial_state (also when initial_state is NULL, i.e. zero).
+ *   workspace     device scratch of at least kda_bwd_workspace_size(...) bytes, 256-byte
+ *                 aligned.
+ * Outputs must not overlap any input or each other (KDA_ERR_ALIAS).  Same error codes as
+ * kda_fwd_ex otherwise.  Work is enqueued on `stream`; nothing is allocated.  One
+ * workgroup per (sequence, head) walks its tokens forward and then backward, so the time
+ * grows with the longest sequence.
+ */
+kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta, float scale,
+                   const float *A_log, const float *dt_bias, float lower_bound, const void *initial_state,
+                   kda_state_dtype initial_state_dtype, const void *dout, const float *dfinal_state, float *dq,
+                   float *dk, float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                   float *dinitial_state, const int64_t *cu_seqlens, const int64_t *cu_seqlens_host, int64_t B,
+                   int64_t T, int64_t H, int64_t N, int64_t K, int64_t V, void *workspace,
+                   size_t workspace_bytes, void *stream, uint32_t flags);
+
+/*
+ * kda_bwd_workspace_size -- bytes of workspace kda_bwd needs: the chunk table, fp32 copies of
+ * the activated k^, q^ and decay (3 x 512 bytes per token-head) plus three scalars per
+ * token-head, the fp32 state before every 16-token chunk of every chain (64 KiB each), and
+ * a 1 MiB buffer per chain.  Returns 0 for invalid sizes.
+ */
+size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 
 /* Human-readable name of a kda_status value (static string; never NULL). */
 const char *kda_status_string(int status);

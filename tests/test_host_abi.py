@@ -264,3 +264,43 @@ def test_sequence_count_limit():
     # no states: their fake ranges at this N would overlap the other fake buffers
     a.h0, a.h0_dt, a.ht, a.ht_dt = None, kda.STATE_NONE, None, kda.STATE_NONE
     assert a.call() == 2  # KDA_ERR_SHAPE
+
+
+def _bwd_call(**over):
+    """kda_bwd with fake but aligned, disjoint pointers; `over` replaces arguments by name."""
+    base, step = 1 << 32, 1 << 28
+    p = {n: base + i * step for i, n in enumerate(
+        ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "h0", "dout", "dht", "dq", "dk", "dv", "dg",
+         "dbeta", "dA_log", "ddt", "dh0", "cu", "ws"])}
+    a = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], scale=0.125, A_log=p["A_log"],
+             dt_bias=p["dt_bias"], lb=-5.0, h0=p["h0"], h0_dt=kda.STATE_FP32, dout=p["dout"], dht=p["dht"],
+             dq=p["dq"], dk=p["dk"], dv=p["dv"], dg=p["dg"], dbeta=p["dbeta"], dA_log=p["dA_log"],
+             ddt=p["ddt"], dh0=p["dh0"], cu=None, cu_host=None, B=1, T=16, H=1, N=1, K=128, V=128,
+             ws=p["ws"], ws_bytes=None, flags=7)
+    a.update(over)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = kda.bwd_workspace_size(a["B"], a["T"], a["H"], a["N"], a["cu"] is not None)
+    L = kda.lib()
+    return L.kda_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["A_log"], a["dt_bias"], a["lb"],
+                     a["h0"], a["h0_dt"], a["dout"], a["dht"], a["dq"], a["dk"], a["dv"], a["dg"], a["dbeta"],
+                     a["dA_log"], a["ddt"], a["dh0"], a["cu"], a["cu_host"], a["B"], a["T"], a["H"], a["N"],
+                     a["K"], a["V"], a["ws"], a["ws_bytes"], None, a["flags"])
+
+
+def test_bwd_error_paths():
+    """kda_bwd validates everything on the host before any launch."""
+    for name in ("q", "k", "v", "g", "beta", "dout", "dq", "dk", "dv", "dg", "dbeta", "A_log", "dt_bias"):
+        assert _bwd_call(**{name: None}) == 1, name                      # KDA_ERR_NULL
+    assert _bwd_call(flags=0, A_log=None, dt_bias=None, ws_bytes=0) == 8  # gate off: no A_log needed
+    assert _bwd_call(B=0) == 2 and _bwd_call(H=0) == 2 and _bwd_call(T=-1) == 2
+    assert _bwd_call(K=64) == 3
+    assert _bwd_call(h0_dt=kda.STATE_NONE) == 4
+    assert _bwd_call(lb=0.5) == 5 and _bwd_call(scale=float("nan")) == 6
+    assert _bwd_call(dq=(1 << 32) + 10 * (1 << 28) + 4) == 7                # misaligned fp32 output
+    assert _bwd_call(dk=(1 << 32) + 10 * (1 << 28)) == 11                   # dk on top of dq
+    assert _bwd_call(dq=1 << 32) == 11                                       # an output on top of q
+    assert _bwd_call(ws_bytes=100) == 8
+    assert _bwd_call(flags=8) == 12
+    # with the gate switch off dA_log / dt_bias are not needed
+    assert kda.bwd_workspace_size(1, 16, 1) > kda.workspace_size(1, 16, 1)
+    assert kda.bwd_workspace_size(0, 16, 1) == 0
