@@ -22,32 +22,49 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // forward pass becomes: pass A (segment 0 exactly, and F, P of segments 1 .. G-2), an
 // fp32 scan S_{g+1} = S_g P_g + F_g, and pass B (segments 1 .. G-1 from S_g, with out).
 // That is three segment runs per chunk instead of one, in exchange for chains x G
-// independent work units; the plan picks G by a round count over the CUs.
+// independent work units; the plan picks G by a cost count over the CUs.  Pass A's F and
+// P units share the CUs that the chains' segment-0 units leave free, in rA rounds, so
+// segment 0 can be longer than the others; the segment-0 units come first in pass A's
+// launch order so that they start in its first wave.  Units that write out (segment 0,
+// pass B) take about 5/4 the time per chunk of the output-free F and P runs (measured on
+// the 2^20-token workload: 2.2-2.3 us against 1.8 us), so segment 0 is sized to
+// L0 ~ (4/5) rA L.  That is done only with at least kLongSeg0Chains chains: measured with
+// 32 chains (B=2 T=4096 H=16) pass A ran 10 % faster, but with 8 chains (B=1 T=2^20 H=8)
+// the F and P units that shared the chip with 8 long segment-0 units ran about 30 % slower
+// per chunk (pass A 7.3 -> 9.35 ms; segment 0 alone ran at the usual speed), for a cause
+// not found; there every segment keeps the same length.
 constexpr int64_t kPlanCUs = 256;   // MI355X compute units
+constexpr int64_t kCostOut = 5, kCostFP = 4;
+constexpr int64_t kLongSeg0Chains = 16;
 
 struct SegPlan {
     int G;        // segments per chain (1 = no segmentation)
-    int64_t L;    // chunks per segment (the last may be shorter)
+    int64_t L;    // chunks per segment 1 .. G-1 (the last may be shorter)
+    int64_t L0;   // chunks of segment 0
 };
 
 inline SegPlan plan_segments(int64_t chains, int64_t nch)
 {
-    SegPlan best{1, nch};
+    SegPlan best{1, nch, nch};
     if (chains <= 0 || nch < 32 || chains >= 192)
         return best;
-    auto rounds = [](int64_t units) { return (units + kPlanCUs - 1) / kPlanCUs; };
-    int64_t best_cost = rounds(chains) * nch;
-    for (int64_t G = 2; G <= 256 && G <= nch / 8; ++G) {
-        const int64_t L = cdiv(nch, G);
-        const int64_t Gp = cdiv(nch, L);
-        if (Gp < 2)
+    auto rounds = [](int64_t units, int64_t cus) { return (units + cus - 1) / cus; };
+    int64_t best_cost = rounds(chains, kPlanCUs) * nch * kCostOut;
+    for (int64_t G = 3; G <= 256 && G <= nch / 8; ++G) {
+        const int64_t rA = rounds(2 * chains * (G - 2), kPlanCUs - chains);
+        const int64_t rB = rounds(chains * (G - 1), kPlanCUs);
+        // kCostOut L0 = kCostFP rA L with L0 + (G - 1) L = nch (or all equal: L0 <= L)
+        const int64_t L = chains >= kLongSeg0Chains ? cdiv(nch * kCostOut, (G - 1) * kCostOut + rA * kCostFP)
+                                                    : cdiv(nch, G);
+        const int64_t L0 = nch - (G - 1) * L;
+        if (L0 < 1)
             continue;
-        // pass A: 1 + 2 (Gp - 2) units per chain; pass B: Gp - 1; the scan costs about two
-        // chunk times per segment step
-        const int64_t cost = rounds(chains * (2 * Gp - 3)) * L + rounds(chains * (Gp - 1)) * L + 2 * Gp;
+        // pass A, pass B, and the scan at about two chunk times per segment step
+        const int64_t a0 = L0 * kCostOut, afp = rA * L * kCostFP;
+        const int64_t cost = (a0 > afp ? a0 : afp) + rB * L * kCostOut + 2 * G * kCostOut;
         if (cost < best_cost) {
             best_cost = cost;
-            best = SegPlan{(int)Gp, L};
+            best = SegPlan{(int)G, L, L0};
         }
     }
     return best;
@@ -129,7 +146,7 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)(kPlanCUs + 1), kAlign);
     L->off_units = off;
     off = round_up(off + sizeof(int32_t) * 2 * (size_t)N, kAlign);
-    L->seg = varlen ? SegPlan{1, 0} : plan_segments(N * H, cdiv(T, kCH));
+    L->seg = varlen ? SegPlan{1, 0, 0} : plan_segments(N * H, cdiv(T, kCH));
     L->off_seg = off;
     if (L->seg.G > 1)
         off += 3 * (size_t)(N * H) * (size_t)L->seg.G * kD * kD * sizeof(float);

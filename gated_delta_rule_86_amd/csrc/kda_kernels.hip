@@ -550,7 +550,7 @@ struct FusedArgs {
     int32_t *status;
     // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B (see SegPlan)
     int pass, G;
-    int64_t L;
+    int64_t L, L0;  // chunks per segment 1 .. G-1 and of segment 0
     float *segS, *segF, *segP;  // [chains][G][128][128] fp32, V-major
 };
 
@@ -621,8 +621,9 @@ __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
         return true;
     }
     const int64_t seg = w.seg;
-    u.c0 = seg * a.L < nch ? seg * a.L : nch;
-    u.c1 = u.c0 + a.L < nch ? u.c0 + a.L : nch;
+    const int64_t s0 = seg == 0 ? 0 : a.L0 + (seg - 1) * a.L, s1 = seg == 0 ? a.L0 : s0 + a.L;
+    u.c0 = s0 < nch ? s0 : nch;
+    u.c1 = s1 < nch ? s1 : nch;
     if (w.pass == 1 && w.kind == 0) {          // segment 0 from the true initial state
         u.init_kind = a.h0_dtype;
         u.init = h0c;
@@ -671,9 +672,9 @@ __device__ bool range_at(const FusedArgs &a, const WgPlan &w, int64_t k, Range &
         r.c0 = 0;
         r.c1 = nch;
     } else {
-        const int64_t c0 = seg * a.L < nch ? seg * a.L : nch;
-        r.c0 = (int)c0;
-        r.c1 = c0 + a.L < nch ? (int)(c0 + a.L) : nch;
+        const int64_t s0 = seg == 0 ? 0 : a.L0 + (seg - 1) * a.L, s1 = seg == 0 ? a.L0 : s0 + a.L;
+        r.c0 = s0 < nch ? (int)s0 : nch;
+        r.c1 = s1 < nch ? (int)s1 : nch;
     }
     return true;
 }
@@ -1362,15 +1363,22 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         w.n_end = a.wg_first[grp + 1];
         w.n = 0;
     } else {
-        const uint32_t upc = a.pass == 1 ? 2u * (uint32_t)a.G - 3u : (uint32_t)a.G - 1u;
-        const uint32_t chain = bid / upc, r = bid % upc;
+        // pass A: the chains' segment-0 units first (they run longest), then the F and P
+        // units of segments 1 .. G-2, chain by chain; pass B: segments 1 .. G-1, chain by chain
+        const uint32_t nchains = (uint32_t)(a.N * a.H);
+        uint32_t chain;
         if (a.pass == 1) {
-            if (r > 0) {
-                w.seg = 1 + (int)((r - 1) / 2);
-                w.kind = 1 + (int)((r - 1) & 1);
+            if (bid < nchains) {
+                chain = bid;
+            } else {
+                const uint32_t fp = 2u * (uint32_t)a.G - 4u, r = bid - nchains;
+                chain = r / fp;
+                w.seg = 1 + (int)((r % fp) / 2);
+                w.kind = 1 + (int)(r & 1);
             }
         } else {
-            w.seg = 1 + (int)r;
+            chain = bid / ((uint32_t)a.G - 1u);
+            w.seg = 1 + (int)(bid % ((uint32_t)a.G - 1u));
         }
         w.h = (int)(chain % H32);
         w.n = chain / H32;
@@ -1564,6 +1572,7 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
     a.G = f.lay.seg.G;
     a.L = f.lay.seg.L;
+    a.L0 = f.lay.seg.L0;
     const size_t seg_floats = (size_t)chains * (size_t)a.G * kD * kD;
     a.segS = reinterpret_cast<float *>(f.ws + f.lay.off_seg);
     a.segF = a.segS + seg_floats;

@@ -113,25 +113,41 @@ def bf16_round_f64(x):
 PLAN_CUS = 256
 
 
+COST_OUT, COST_FP = 5, 4  # relative time per chunk of units with and without output
+LONG_SEG0_CHAINS = 16     # a longer segment 0 only with at least this many chains
+
+
 def segment_plan(chains, nch):
-    """(G, L): segments per chain and chunks per segment that the forward pass picks for
-    `chains` equal-length chains of `nch` chunks (G = 1: whole chains).  The cost counts
-    rounds of the CUs over pass A (2G-3 units per chain), pass B (G-1) and the scan."""
-    rounds = lambda u: -(-u // PLAN_CUS)
-    best, best_cost = (1, nch), None
+    """(G, L, L0): segments per chain, chunks per segment 1 .. G-1 and chunks of segment 0
+    that the forward pass picks for `chains` equal-length chains of `nch` chunks (G = 1:
+    whole chains).  Pass A runs the segment-0 units alongside rA rounds of F and P units on
+    the CUs they leave free, and (with at least 16 chains) segment 0 is sized so that both
+    take about as long (units that write out cost 5/4 of an output-free F or P run per
+    chunk); with fewer chains all segments are equal.  The cost counts pass A,
+    pass B (rounds of G - 1 units per chain) and the scan."""
+    rounds = lambda u, c: -(-u // c)
+    best = (1, nch, nch)
     if chains <= 0 or nch < 32 or chains >= 192:
         return best
-    best_cost = rounds(chains) * nch
-    G = 2
+    best_cost = rounds(chains, PLAN_CUS) * nch * COST_OUT
+    G = 3
     while G <= 256 and G <= nch // 8:
-        L = -(-nch // G)
-        Gp = -(-nch // L)
-        if Gp >= 2:
-            cost = rounds(chains * (2 * Gp - 3)) * L + rounds(chains * (Gp - 1)) * L + 2 * Gp
+        rA = rounds(2 * chains * (G - 2), PLAN_CUS - chains)
+        rB = rounds(chains * (G - 1), PLAN_CUS)
+        L = (-(-(nch * COST_OUT) // ((G - 1) * COST_OUT + rA * COST_FP)) if chains >= LONG_SEG0_CHAINS
+             else -(-nch // G))
+        L0 = nch - (G - 1) * L
+        if L0 >= 1:
+            cost = max(L0 * COST_OUT, rA * L * COST_FP) + rB * L * COST_OUT + 2 * G * COST_OUT
             if cost < best_cost:
-                best_cost, best = cost, (Gp, L)
+                best_cost, best = cost, (G, L, L0)
         G += 1
     return best
+
+
+def segment_bounds(G, L, L0, nch):
+    """First chunk of each segment 0 .. G-1, and nch at the end: G + 1 entries."""
+    return [0] + [min(L0 + (g - 1) * L, nch) for g in range(1, G)] + [nch]
 
 
 def table_bytes(N):

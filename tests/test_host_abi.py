@@ -247,11 +247,13 @@ def test_segment_plan_replica():
     for B, T, H in [(1, 700, 1), (1, 8192, 2), (1, 6000, 2), (3, 4096, 2), (2, 5000, 3), (1, 4103, 1),
                     (1, 4096, 2), (2, 4096, 16), (1, 1 << 20, 8), (3, 1500, 2), (1, 1 << 20, 1),
                     (1, 100, 4), (5, 4000, 40)]:
-        G, L = segment_plan(B * H, -(-T // 16))
+        nch = -(-T // 16)
+        G, L, L0 = segment_plan(B * H, nch)
         extra = ws_size(B, T, H) - table_bytes(B)
         got = 1 if extra == 0 else extra // (3 * B * H * 128 * 128 * 4)
         assert got == G, (B, T, H, got, G)
-        assert G == 1 or -(-(-(-T // 16)) // L) == G
+        # segment 0 is at least as long as the others, and the last one is not empty
+        assert G == 1 or (L0 >= 1 and L0 + (G - 2) * L < nch <= L0 + (G - 1) * L), (B, T, H, G, L, L0)
 
 
 def test_sequence_count_limit():
