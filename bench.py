@@ -148,6 +148,43 @@ def cpu_baseline(w):
             f"{threads} threads for {chains} chains)"}
 
 
+def backward_bench(args, w):
+    """Time kda_bwd on the workload's inputs with a random dL/dout and dL/dfinal_state; one JSON
+    line (head-tokens/s of the backward pass; not the headline metric)."""
+    import numpy as np
+    import torch
+    from gated_delta_rule_86_amd import kda
+    from gated_delta_rule_86_amd import workloads as W
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).to(dev)
+    q, k, v, g, beta = (t(getattr(w, n)) for n in ("q", "k", "v", "g", "beta"))
+    A_log = torch.from_numpy(w.A_log).to(dev)
+    dt_bias = torch.from_numpy(w.dt_bias).to(dev)
+    h0 = None
+    if w.initial_state is not None:
+        h0 = t(w.initial_state) if w.initial_state.dtype.name == "uint16" else torch.from_numpy(w.initial_state).to(dev)
+    cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens).to(dev)
+    rng = np.random.default_rng(0)
+    dout = t(W.f32_to_bf16_bits(rng.standard_normal(q.shape, dtype=np.float32)))
+    dht = torch.randn((w.N, w.H, 128, 128), device=dev)
+    ws = torch.empty(kda.bwd_workspace_size(w.B, w.T, w.H, w.N, cu is not None), dtype=torch.uint8, device=dev)
+    step = lambda: kda.bwd(q, k, v, g, beta, w.scale, A_log, dt_bias, w.lower_bound, dout, h0, dht, cu,
+                           workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"metric": "KDA bwd head-tokens/sec on 1 MI355X (kda_bwd)", "value": w.head_tokens / dt,
+                      "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": dt * 1e3, "higher_is_better": True, "dtype": "fp32",
+                      "data": "synthetic", "config": dict(w.describe(), head_tokens=w.head_tokens),
+                      "workspace_bytes": ws.numel()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +196,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3,
                     help="index into workloads.config (0..4; 5 = decode step, token-by-token path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time kda_bwd (gradients of out and final_state) on the workload instead")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -176,6 +215,9 @@ def main():
     from gated_delta_rule_86_amd import workloads as W
 
     w = W.config(args.workload)
+    if args.backward:
+        backward_bench(args, w)
+        return
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
     q, k, v, g, beta = (t(getattr(w, n)) for n in ("q", "k", "v", "g", "beta"))
