@@ -17,57 +17,48 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Segment plan for few, long, equal-length chains (no cu_seqlens).  The state after a
-// segment is affine in the state before it: S_end = S_begin P + F, with F the segment run
-// from S = 0 and P the segment run from S = I with v = 0.  With G segments per chain the
-// forward pass becomes: pass A (segment 0 exactly, and F, P of segments 1 .. G-2), an
-// fp32 scan S_{g+1} = S_g P_g + F_g, and pass B (segments 1 .. G-1 from S_g, with out).
-// That is three segment runs per chunk instead of one, in exchange for chains x G
-// independent work units; the plan picks G by a cost count over the CUs.  Pass A's F and
-// P units share the CUs that the chains' segment-0 units leave free, in rA rounds, so
-// segment 0 can be longer than the others; the segment-0 units come first in pass A's
-// launch order so that they start in its first wave.  Units that write out (segment 0,
-// pass B) take about 5/4 the time per chunk of the output-free F and P runs (measured on
-// the 2^20-token workload: 2.2-2.3 us against 1.8 us), so segment 0 is sized to
-// L0 ~ (4/5) rA L.  That is done only with at least kLongSeg0Chains chains: measured with
-// 32 chains (B=2 T=4096 H=16) pass A ran 10 % faster, but with 8 chains (B=1 T=2^20 H=8)
-// the F and P units that shared the chip with 8 long segment-0 units ran about 30 % slower
-// per chunk (pass A 7.3 -> 9.35 ms; segment 0 alone ran at the usual speed), for a cause
-// not found; there every segment keeps the same length.
+// segment is affine in the state before it: S_end = S_begin Phi + F, with F the segment run
+// from S = 0 and Phi the segment's transition (the run from S = I with v = 0).  A chain is
+// cut into G segments of L chunks (the last one shorter), and the forward pass runs:
+//   pass A:   segment 0 from the true initial state and segments 1 .. G-1 from S = 0, all
+//             with out; the end states S_1 and F_g and their norms.
+//   transition runs, segments 1 .. G-1: from I with v = 0.  With the in-kernel l2norm and
+//             beta sigmoid every token's transition diag(alpha)(I - beta k^ k^T) has
+//             spectral norm <= 1, so |S_g|_F <= B_g = |S_1|_F + |F_1|_F + ... + |F_{g-1}|_F,
+//             and once every entry of the run's state is below kTruncRel |F_g|_F / B_g
+//             after z chunks, S_g's share of every later state of the segment is below
+//             2^-30 |F_g|_F.  The run stops there and records z; otherwise it runs the whole
+//             segment and keeps Phi_g.
+//   scan:     S_{g+1} = F_g where the run stopped (that share dropped), else
+//             S_{g+1} = S_g Phi_g + F_g.
+//   pass B:   segments 1 .. G-1 again from S_g, with out: only the first z chunks where the
+//             share was dropped (pass A's out is right from there on), else all of them.
+// With a strong gate (the transition falls below 2^-40 within 2 - 4 chunks at lower bounds
+// -5 .. -2) that is about one segment run per chunk over chains x G units; with weak or no
+// decay every run goes the whole way (three segment runs per chunk).  G fills the CUs with
+// one round of pass A units of at least kSegMinChunks chunks each.
 constexpr int64_t kPlanCUs = 256;   // MI355X compute units
-constexpr int64_t kCostOut = 5, kCostFP = 4;
-constexpr int64_t kLongSeg0Chains = 16;
+constexpr int64_t kSegMinChunks = 16;
+constexpr float kTruncRel = 0x1p-37f;  // 2^-30 / 128
 
 struct SegPlan {
     int G;        // segments per chain (1 = no segmentation)
-    int64_t L;    // chunks per segment 1 .. G-1 (the last may be shorter)
-    int64_t L0;   // chunks of segment 0
+    int64_t L;    // chunks per segment (the last may be shorter)
 };
 
 inline SegPlan plan_segments(int64_t chains, int64_t nch)
 {
-    SegPlan best{1, nch, nch};
-    if (chains <= 0 || nch < 32 || chains >= 192)
-        return best;
-    auto rounds = [](int64_t units, int64_t cus) { return (units + cus - 1) / cus; };
-    int64_t best_cost = rounds(chains, kPlanCUs) * nch * kCostOut;
-    for (int64_t G = 3; G <= 256 && G <= nch / 8; ++G) {
-        const int64_t rA = rounds(2 * chains * (G - 2), kPlanCUs - chains);
-        const int64_t rB = rounds(chains * (G - 1), kPlanCUs);
-        // kCostOut L0 = kCostFP rA L with L0 + (G - 1) L = nch (or all equal: L0 <= L)
-        const int64_t L = chains >= kLongSeg0Chains ? cdiv(nch * kCostOut, (G - 1) * kCostOut + rA * kCostFP)
-                                                    : cdiv(nch, G);
-        const int64_t L0 = nch - (G - 1) * L;
-        if (L0 < 1)
-            continue;
-        // pass A, pass B, and the scan at about two chunk times per segment step
-        const int64_t a0 = L0 * kCostOut, afp = rA * L * kCostFP;
-        const int64_t cost = (a0 > afp ? a0 : afp) + rB * L * kCostOut + 2 * G * kCostOut;
-        if (cost < best_cost) {
-            best_cost = cost;
-            best = SegPlan{(int)G, L, L0};
-        }
-    }
-    return best;
+    const SegPlan none{1, nch};
+    if (chains <= 0 || chains > kPlanCUs / 2)
+        return none;
+    int64_t G = kPlanCUs / chains;
+    if (G > nch / kSegMinChunks)
+        G = nch / kSegMinChunks;
+    while (G >= 2 && (G - 1) * cdiv(nch, G) >= nch)  // no empty segment
+        --G;
+    if (G < 2)
+        return none;
+    return SegPlan{(int)G, cdiv(nch, G)};
 }
 
 // Column halves.  When a head has few workgroups and few sequences, the chunk table may run
@@ -114,6 +105,8 @@ struct Layout {
     size_t off_units;  // int32 [2 N]: whole-chain units, (sequence << 2) | (0 whole, 1 + column half)
     SegPlan seg;       // segment plan (G == 1 without segmentation)
     size_t off_seg;    // fp32 states S, F, P: 3 x [chains][G][128][128] when G > 1
+    size_t off_segaux; // when G > 1: int32 z [chains][G], int32 drop [chains][G],
+                       // fp32 squared norms [chains][G][4]
     size_t total;
 };
 
@@ -146,10 +139,15 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)(kPlanCUs + 1), kAlign);
     L->off_units = off;
     off = round_up(off + sizeof(int32_t) * 2 * (size_t)N, kAlign);
-    L->seg = varlen ? SegPlan{1, 0, 0} : plan_segments(N * H, cdiv(T, kCH));
+    L->seg = varlen ? SegPlan{1, 0} : plan_segments(N * H, cdiv(T, kCH));
     L->off_seg = off;
-    if (L->seg.G > 1)
-        off += 3 * (size_t)(N * H) * (size_t)L->seg.G * kD * kD * sizeof(float);
+    L->off_segaux = off;
+    if (L->seg.G > 1) {
+        const size_t units = (size_t)(N * H) * (size_t)L->seg.G;
+        off += 3 * units * kD * kD * sizeof(float);
+        L->off_segaux = off;
+        off = round_up(off + units * (2 * sizeof(int32_t) + 4 * sizeof(float)), kAlign);
+    }
     L->total = off;
     return true;
 }

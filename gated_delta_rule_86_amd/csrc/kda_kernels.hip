@@ -526,8 +526,11 @@ constexpr int kOffVring = kOffStage + 4 * kStageBytes;
 constexpr int kOffTile = kOffVring + 4 * kNV * 1024;
 constexpr int kOffDt = kOffTile + 4 * 1024;
 constexpr int kOffOut = kOffDt + 512;               // per consumer: one output tile (1 KB)
-constexpr int kOffFlags = kOffOut + 4 * 1024;
+constexpr int kOffFlags = kOffOut + 4 * 1024;   // int words: ready [kNS], taken [kNS][4],
+constexpr int kFlagStop = 5 * kNS;               // stop item of a transition run,
+constexpr int kFlagVote = kFlagStop + 1;         // consumer votes [2][4]
 constexpr int kFusedLds = kOffFlags + 128;
+static_assert(4 * (kFlagVote + 8) <= 128, "flag words");
 static_assert(kFusedLds <= 160 * 1024, "LDS budget");
 static_assert(kBlkBytes % 256 == 0 && kBlkKD % 256 == 0, "slot alignment (the KD swizzle XORs address bits 4-7)");
 constexpr int32_t kStatusSpin = 0x100;
@@ -548,10 +551,15 @@ struct FusedArgs {
     const int64_t *wg_first;  // whole-chain pass: first unit of each workgroup of a head
     const int32_t *units;     // whole-chain units: (sequence << 2) | (0 whole, 1 + column half)
     int32_t *status;
-    // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B (see SegPlan)
+    // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B, 3 = transition runs
+    // (see SegPlan)
     int pass, G;
-    int64_t L, L0;  // chunks per segment 1 .. G-1 and of segment 0
+    int64_t L;  // chunks per segment
     float *segS, *segF, *segP;  // [chains][G][128][128] fp32, V-major
+    int32_t *segZ;   // [chains][G]: chunks a transition run took before stopping, -1 = all
+    int32_t *segD;   // [chains][G]: 1 where the scan dropped S_g's share of S_{g+1}
+    float *segN;     // [chains][G][4]: squared norm of pass A's end state, per consumer
+    int trunc;       // transition runs may stop early (in-kernel l2norm and beta sigmoid)
 };
 
 // One work unit: a chunk range of one chain, where its state comes from and goes to.
@@ -568,6 +576,10 @@ struct Unit {
     bool v_on;            // false: v taken as zero (the P run of a segment)
     bool out_on;          // write out rows of this range
     int half;             // -1: all 128 value columns; 0 / 1: columns 64*half .. 64*half+63
+    float *nrm;           // pass A: squared norm of the end state, one float per consumer
+    const float *fin_src; // fp32 state written as the final state instead of the run's own
+    int32_t *zout;        // transition runs: where the chunk count before the stop goes
+    int seg;              // segment passes: the segment
 };
 
 // A workgroup's work: one unit (segment passes), or -- whole-chain pass -- the units
@@ -580,7 +592,6 @@ struct WgPlan {
     int64_t sub, n_end;   // whole-chain pass: units sub, sub + 1, ... < n_end
     int64_t n;            // segment passes: the sequence
     int seg;              // segment passes: the segment
-    int kind;             // pass A: 0 exact segment 0, 1 F run, 2 P run
 };
 
 __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
@@ -611,6 +622,9 @@ __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
     auto segbuf = [&](float *base, int64_t sg) { return base + ((size_t)chain * a.G + (size_t)sg) * kBlock; };
     u.v_on = true;
     u.out_on = true;
+    u.nrm = nullptr;
+    u.fin_src = nullptr;
+    u.zout = nullptr;
     if (w.pass == 0) {
         u.c0 = 0;
         u.c1 = nch;
@@ -621,27 +635,37 @@ __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
         return true;
     }
     const int64_t seg = w.seg;
-    const int64_t s0 = seg == 0 ? 0 : a.L0 + (seg - 1) * a.L, s1 = seg == 0 ? a.L0 : s0 + a.L;
+    const int64_t s0 = seg * a.L, s1 = s0 + a.L;
     u.c0 = s0 < nch ? s0 : nch;
     u.c1 = s1 < nch ? s1 : nch;
-    if (w.pass == 1 && w.kind == 0) {          // segment 0 from the true initial state
-        u.init_kind = a.h0_dtype;
-        u.init = h0c;
+    u.seg = (int)seg;
+    const size_t su = (size_t)chain * a.G + (size_t)seg;
+    if (w.pass == 1) {                         // pass A: segment 0 exactly, the others from 0
+        u.init_kind = seg == 0 ? a.h0_dtype : kInitZero;
+        u.init = seg == 0 ? h0c : nullptr;
         u.fin_kind = 2;
-        u.fin = segbuf(a.segS, 1);
-    } else if (w.pass == 1) {                  // F (from zero) or P (from I, v = 0)
-        u.init_kind = w.kind == 1 ? kInitZero : kInitIdentity;
+        u.fin = seg == 0 ? segbuf(a.segS, 1) : segbuf(a.segF, seg);
+        u.nrm = a.segN + 4 * su;
+    } else if (w.pass == 3) {                  // transition run: from I, v = 0, no out
+        u.init_kind = kInitIdentity;
         u.init = nullptr;
-        u.v_on = w.kind == 1;
+        u.v_on = false;
         u.out_on = false;
         u.fin_kind = 2;
-        u.fin = segbuf(w.kind == 1 ? a.segF : a.segP, seg);
-    } else {                                   // pass B: segment seg from S_seg
+        u.fin = segbuf(a.segP, seg);
+        u.zout = a.segZ + su;
+    } else {                                   // pass B: from S_seg, the first z chunks or all
+        // (a dropped share: segD = 1 exactly where the transition run stopped, segZ >= 0)
         u.init_kind = kInitFp32;
-        u.init = segbuf(a.segS, seg);
+        u.init = seg > 1 && a.segD[su - 1] ? segbuf(a.segF, seg - 1) : segbuf(a.segS, seg);
+        const bool drop = a.segD[su] != 0;
+        if (drop && u.c0 + a.segZ[su] < u.c1)
+            u.c1 = u.c0 + a.segZ[su];
         const bool last = seg == a.G - 1;
         u.fin_kind = last ? a.ht_dtype : 0;
         u.fin = last ? htc : nullptr;
+        if (last && drop)
+            u.fin_src = segbuf(a.segF, seg);
     }
     return true;
 }
@@ -672,9 +696,14 @@ __device__ bool range_at(const FusedArgs &a, const WgPlan &w, int64_t k, Range &
         r.c0 = 0;
         r.c1 = nch;
     } else {
-        const int64_t s0 = seg == 0 ? 0 : a.L0 + (seg - 1) * a.L, s1 = seg == 0 ? a.L0 : s0 + a.L;
+        const int64_t s0 = seg * a.L, s1 = s0 + a.L;
         r.c0 = s0 < nch ? (int)s0 : nch;
         r.c1 = s1 < nch ? (int)s1 : nch;
+        if (w.pass == 2) {  // the chunks pass B reruns (as unit_at)
+            const size_t su = (size_t)(n * a.H + w.h) * a.G + (size_t)seg;
+            if (a.segD[su] && r.c0 + a.segZ[su] < r.c1)
+                r.c1 = r.c0 + (int)a.segZ[su];
+        }
     }
     return true;
 }
@@ -728,6 +757,26 @@ __device__ __forceinline__ bool lds_wait_eq4(lds_flag_t *p, int want)
     return false;
 }
 
+// Spin until the four words p[0..3] all equal want (returns 1) or *stop <= item (returns 2);
+// 0 on time-out.
+__device__ __forceinline__ int lds_wait_eq4_or_stop(lds_flag_t *p, int want, lds_flag_t *stop, int item)
+{
+    for (int it = 0; it < kSpinMax; ++it) {
+        const int v0 = __builtin_amdgcn_readfirstlane(p[0]);
+        const int v1 = __builtin_amdgcn_readfirstlane(p[1]);
+        const int v2 = __builtin_amdgcn_readfirstlane(p[2]);
+        const int v3 = __builtin_amdgcn_readfirstlane(p[3]);
+        if (v0 == want && v1 == want && v2 == want && v3 == want) {
+            __asm__ volatile("" ::: "memory");
+            return 1;
+        }
+        if (__builtin_amdgcn_readfirstlane(*stop) <= item)
+            return 2;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return 0;
+}
+
 // s_waitcnt vmcnt(n) for a run-time n in [0, 5]
 __device__ __forceinline__ void wait_vmcnt_rt(int n)
 {
@@ -755,7 +804,7 @@ __device__ __forceinline__ void dma_tile16(__amdgpu_buffer_rsrc_t r, unsigned ch
 // the pass (the common case gets code with no switch logic in it).  kQ: the workgroup's
 // units write output rows; without it (the F and P runs of a segment) q is neither loaded
 // nor used, and the output-only operands (QG, Mq) are not formed.
-template <bool kSw, bool kQ>
+template <bool kSw, bool kQ, bool kStop>
 __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int p, int lane)
 {
     const int64_t H = a.H;
@@ -767,6 +816,7 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
     const float *dtc = reinterpret_cast<const float *>(lds + kOffDt);
     lds_flag_t *ready = (lds_flag_t *)(lds + kOffFlags);
     lds_flag_t *taken = ready + kNS;
+    lds_flag_t *stop = ready + kFlagStop;  // kStop: items from here on are not wanted
     const uint32_t rowb = (uint32_t)(H * kD * 2);  // bytes between consecutive tokens of a head
 
     // Direct-to-LDS loads of chunk j of unit u: 4 loads of 16 B per lane per tensor (4
@@ -820,6 +870,8 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
     if (nxt.valid)
         issue_stage(nxt.r, nxt.r.c0 + (p - nxt.base));
     for (int it = p;; it += 4) {
+        if (kStop && __builtin_amdgcn_readfirstlane(*stop) <= it)
+            break;
         cur.seek(a, w, it);
         if (!cur.valid)
             break;
@@ -974,7 +1026,17 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 
         // ---- hand the operand block to the consumers ----
         const int s = it % kNS;
-        if (!spun_out && !lds_wait_eq4(taken + 4 * s, it / kNS)) {
+        if (kStop) {
+            // a transition run that stops early never frees the slots of the items after
+            // its last: wait for the slot or for the stop word
+            const int r = spun_out ? 1 : lds_wait_eq4_or_stop(taken + 4 * s, it / kNS, stop, it);
+            if (r == 2)
+                break;
+            if (r == 0) {
+                spun_out = true;
+                atomicOr(a.status, kStatusSpin);
+            }
+        } else if (!spun_out && !lds_wait_eq4(taken + 4 * s, it / kNS)) {
             spun_out = true;  // stop waiting from here on; the status word reports it
             atomicOr(a.status, kStatusSpin);
         }
@@ -1039,6 +1101,8 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
         if (lane == 0)
             ready[s] = it;
     }
+    // a stopped run may leave the next item's staging loads in flight: they write LDS
+    wait_vmcnt<0>();
 }
 
 // One unit's items for consumer wavefront cw: state in, chunk recurrence, state out.
@@ -1046,7 +1110,17 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 // kOut: the unit writes output rows (u.out_on); without it Y and O are not formed and the
 // output-only operands are not read.  NB: 16-column blocks of this wave -- 2 for a whole
 // unit (columns 32cw .. 32cw+31), 1 for a column half (64*half + 16cw .. +15).
-template <bool kOut, int NB>
+// kP: a transition run (from I, v = 0) of segment g that, when a.trunc allows, stops after
+// the first chunk at whose end every entry of the state is below
+//   thr = kTruncRel |F_g|_F / B_g,   B_g = |S_1|_F + |F_1|_F + ... + |F_{g-1}|_F
+// (norms of pass A's end states).  B_g bounds |S_g|_F whatever the scan drops (every
+// transition has spectral norm <= 1), so the share of S_g that the scan then drops from
+// every later state of the segment is at most 128 thr B_g = 2^-30 |F_g|_F in Frobenius
+// norm.  The four consumers vote after every chunk, so they stop together, and the
+// producers are told through the stop word.  The chunk count goes to *u.zout (-1: ran to
+// the end, state written).
+// kSeg: a segment pass unit (pass A end-state norms, pass B final state taken from F).
+template <bool kOut, int NB, bool kP, bool kSeg>
 __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane,
                              int it0, bool &spun_out)
 {
@@ -1060,6 +1134,16 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     const int col = lane & 15;
     lds_flag_t *ready = (lds_flag_t *)(lds + kOffFlags);
     lds_flag_t *taken = ready + kNS;
+    int stopped = -1;  // kP: chunks run before the stop
+    float thr = 0.f;   // kP: stop once every entry is below this (NaN: never)
+    if (kP && a.trunc) {
+        const float *nr = a.segN + 4 * (size_t)((u.n * a.H + u.h) * a.G);
+        auto fro = [&](int sg) { return sqrtf(nr[4 * sg] + nr[4 * sg + 1] + nr[4 * sg + 2] + nr[4 * sg + 3]); };
+        float bound = 0.f;
+        for (int sg = 0; sg < u.seg; ++sg)
+            bound += fro(sg);
+        thr = bound == 0.f ? __builtin_inff() : kTruncRel * fro(u.seg) / bound;
+    }
     unsigned char *vring = lds + kOffVring + cw * (kNV * 1024);
     const uint32_t rowb = (uint32_t)(H * kD * 2);
 
@@ -1294,6 +1378,52 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
         // every operand of chunk j is in registers (used above): release the slot
         if (lane == 0)
             taken[4 * s + cw] = it / kNS + 1;
+        if (kP && a.trunc) {
+            // vote: 2 iu + (every entry of this wave's rows below thr); votes of
+            // consecutive chunks alternate between two sets of four words, and a wave can
+            // be at most one chunk ahead of the others here
+            bool big = false;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        big |= !(__builtin_fabsf(S[b][t][i]) < thr);  // NaN counts as big
+            const bool wbig = __builtin_amdgcn_ballot_w64(big) != 0;
+            lds_flag_t *vote = ready + kFlagVote + 4 * (iu & 1);
+            if (lane == 0)
+                vote[cw] = 2 * iu + (wbig ? 0 : 1);
+            bool small = true;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                int v = __builtin_amdgcn_readfirstlane(vote[k]);
+                for (int spin = 0; (v >> 1) != iu && !spun_out && spin < kSpinMax; ++spin) {
+                    __builtin_amdgcn_s_sleep(1);
+                    v = __builtin_amdgcn_readfirstlane(vote[k]);
+                }
+                if ((v >> 1) != iu) {
+                    if (!spun_out) {
+                        spun_out = true;
+                        atomicOr(a.status, kStatusSpin);
+                    }
+                    v = 0;  // no vote: keep running
+                }
+                small = small && (v & 1);
+            }
+            if (small) {
+                stopped = iu + 1;
+                if (cw == 0 && lane == 0)
+                    ready[kFlagStop] = it + 1;
+                break;
+            }
+        }
+    }
+    if (kP) {
+        if (cw == 0 && lane == 0)
+            *u.zout = stopped;
+        if (stopped >= 0)
+            return;  // the state is below thr: the scan drops it, nothing to write
     }
     if (kOut && c1 > c0) {
         wait_lgkmcnt0();
@@ -1301,6 +1431,29 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     }
 
     const int64_t sb0 = (int64_t)(cb0 + col) * kD + 4 * g;
+    if (kSeg && u.nrm != nullptr) {
+        float ss = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ss = fmaf(S[b][t][i], S[b][t][i], ss);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            ss += __shfl_xor(ss, o);
+        if (lane == 0)
+            u.nrm[cw] = ss;
+    }
+    if (kSeg && u.fin_src != nullptr) {
+        const float *p = u.fin_src + sb0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                S[b][t] = *reinterpret_cast<const f32x4_t *>(p + b * 16 * kD + 16 * t);
+    }
     if (u.fin_kind == 2) {
         float *p = reinterpret_cast<float *>(u.fin) + sb0;
 #pragma unroll
@@ -1322,7 +1475,10 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
 
 // kHalves: the unit list may hold column halves (a separate kernel instantiation, so that
 // whole-unit launches carry no NB = 1 code)
-template <bool kHalves>
+// kMode: launch kind of the fused kernel (below)
+constexpr int kModeWhole = 0, kModeHalves = 1, kModeSeg = 2, kModeTrans = 3;
+
+template <int kMode>
 __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int cw, int lane)
 {
     bool spun_out = false;
@@ -1331,17 +1487,22 @@ __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned cha
     for (int64_t k = 0; unit_at(a, w, k, u); ++k) {
         // the previous unit's stores are done before this unit's value-ring bookkeeping starts
         wait_vmcnt<0>();
-        if (!u.out_on)
-            consume_unit<false, 2>(a, u, lds, cw, lane, it0, spun_out);  // segment F, P runs: whole
-        else if (!kHalves || u.half < 0)
-            consume_unit<true, 2>(a, u, lds, cw, lane, it0, spun_out);
+        if (kMode == kModeTrans)
+            consume_unit<false, 2, true, false>(a, u, lds, cw, lane, it0, spun_out);
+        else if (kMode == kModeSeg)
+            consume_unit<true, 2, false, true>(a, u, lds, cw, lane, it0, spun_out);
+        else if (kMode == kModeWhole || u.half < 0)
+            consume_unit<true, 2, false, false>(a, u, lds, cw, lane, it0, spun_out);
         else
-            consume_unit<true, 1>(a, u, lds, cw, lane, it0, spun_out);
+            consume_unit<true, 1, false, false>(a, u, lds, cw, lane, it0, spun_out);
         it0 += (int)(u.c1 - u.c0);
     }
 }
 
-template <bool kSw, bool kHalves>
+// kMode: whole chains (pass 0), whole chains that may hold column halves (pass 0), segment
+// passes A and B (1, 2), transition runs (pass 3); separate instantiations, so that each
+// carries only its own code and registers.
+template <bool kSw, int kMode>
 __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -1350,11 +1511,10 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 
     // this workgroup's work (see SegPlan for the passes)
     WgPlan w;
-    w.pass = a.pass;
-    w.kind = 0;
+    w.pass = kMode == kModeWhole || kMode == kModeHalves ? 0 : kMode == kModeTrans ? 3 : a.pass;
     w.seg = 0;
     const uint32_t bid = blockIdx.x, H32 = (uint32_t)a.H;
-    if (a.pass == 0) {
+    if (w.pass == 0) {
         // heads h = block % H; block / H of a head takes the run of sequences the chunk
         // table assigned to it
         w.h = (int)(bid % H32);
@@ -1363,19 +1523,12 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         w.n_end = a.wg_first[grp + 1];
         w.n = 0;
     } else {
-        // pass A: the chains' segment-0 units first (they run longest), then the F and P
-        // units of segments 1 .. G-2, chain by chain; pass B: segments 1 .. G-1, chain by chain
-        const uint32_t nchains = (uint32_t)(a.N * a.H);
+        // pass A: segments 0 .. G-1, chain by chain; pass B and the transition runs:
+        // segments 1 .. G-1, chain by chain
         uint32_t chain;
-        if (a.pass == 1) {
-            if (bid < nchains) {
-                chain = bid;
-            } else {
-                const uint32_t fp = 2u * (uint32_t)a.G - 4u, r = bid - nchains;
-                chain = r / fp;
-                w.seg = 1 + (int)((r % fp) / 2);
-                w.kind = 1 + (int)(r & 1);
-            }
+        if (w.pass == 1) {
+            chain = bid / (uint32_t)a.G;
+            w.seg = (int)(bid % (uint32_t)a.G);
         } else {
             chain = bid / ((uint32_t)a.G - 1u);
             w.seg = 1 + (int)(bid % ((uint32_t)a.G - 1u));
@@ -1388,9 +1541,10 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
             return;
     }
 
-    if (threadIdx.x < 5 * kNS) {
+    if (threadIdx.x < kFlagVote + 8) {
         int *fl = reinterpret_cast<int *>(lds + kOffFlags);
-        fl[threadIdx.x] = threadIdx.x < kNS ? -1 : 0;
+        const int t = (int)threadIdx.x;
+        fl[t] = t < kNS ? -1 : t < kFlagStop ? 0 : t == kFlagStop ? 0x7fffffff : -1;
     }
     if (threadIdx.x < kD && (!kSw || (a.flags & kGateIn))) {
         const float m1 = -kLog2e * fexp2(a.A_log[w.h] * kLog2e);
@@ -1398,15 +1552,12 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     }
     __syncthreads();
     if (wave < 4) {
-        if (w.pass == 1 && w.kind != 0)
-            fused_producer<kSw, false>(a, w, lds, wave, lane);
-        else
-            fused_producer<kSw, true>(a, w, lds, wave, lane);
+        fused_producer<kSw, kMode != kModeTrans, kMode == kModeTrans>(a, w, lds, wave, lane);
     } else {
         // The consumers set the pace (producers finish ahead and wait for free slots), so
         // they get issue priority over the producer sharing their SIMD.
         __builtin_amdgcn_s_setprio(1);
-        fused_consumer<kHalves>(a, w, lds, wave - 4, lane);
+        fused_consumer<kMode>(a, w, lds, wave - 4, lane);
     }
 }
 
@@ -1418,12 +1569,18 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 // A operand), split from the 16 rows kept in LDS between steps.  Wave w forms output column
 // tiles 2w and 2w + 1; lane n + 16kg of chunk kc, tile t takes P[32kc + 8kg + e][16t + n]
 // (the B operand) straight from global memory (16 lanes read 64 contiguous bytes) and
-// splits it; the loads of the next step, with F_g, go out before this step's products.
-// Workgroup b takes
-// chain b % chains, so the 8 workgroups of a chain share a slot modulo 8 (the XCD the
-// dispatcher gives them, whose L2 then holds that chain's P_g once).
+// splits it; the loads of the next computed step go out before this step's products.
+// Workgroup b takes chain b % chains, so the 8 workgroups of a chain share a slot modulo 8
+// (the XCD the dispatcher gives them, whose L2 then holds that chain's P_g once).
+//
+// Dropped shares.  Where segment g's transition run stopped early (z_g >= 0: its state fell
+// below the bound that makes S_g's share negligible), S_{g+1} = F_g: nothing is computed or
+// written, and pass B and the next step read F_g.  The first workgroup of a chain records
+// the decisions for pass B.
 struct ScanArgs {
     float *segS, *segF, *segP;
+    const int32_t *segZ;
+    int32_t *segD;
     int G;
     int64_t chains;
 };
@@ -1431,6 +1588,7 @@ struct ScanArgs {
 __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
 {
     __shared__ __attribute__((aligned(16))) float s_rows[16][kD + 4];
+    __shared__ int s_drop[256];
     constexpr int64_t kBlock = (int64_t)kD * kD;
     const int64_t chain = blockIdx.x % a.chains;
     const int r0 = (int)(blockIdx.x / a.chains) * 16;
@@ -1438,6 +1596,14 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
         return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = lane & 15, kg = lane >> 4;  // A: row m, k-group kg; B and D: column m
+    const size_t su0 = (size_t)chain * a.G;
+    if ((int)threadIdx.x < a.G) {
+        const int g = threadIdx.x;
+        s_drop[g] = g > 0 && a.segZ[su0 + g] >= 0;  // (segment 0 has no transition run)
+        if (r0 == 0 && g > 0)
+            a.segD[su0 + g] = s_drop[g];
+    }
+    __syncthreads();
     auto blk = [&](float *base, int g) { return base + ((size_t)chain * a.G + (size_t)g) * kBlock; };
     u32x4_t ahi[4], alo[4];
     auto split_A = [&](const float *row) {  // row = S[r0 + m]
@@ -1451,7 +1617,6 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
             alo[kc] = u32x4_t{p0[1], p1[1], p2[1], p3[1]};
         }
     };
-    split_A(blk(a.segS, 1) + (size_t)(r0 + m) * kD);
     float bv[2][4][8];
     f32x4_t fv[2];  // F_g[r0 + 4kg + i][16(2w + t) + m]: the D layout of the output tiles
     auto load_BF = [&](int g) {
@@ -1469,8 +1634,23 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
                     bv[t][kc][e] = P[(size_t)(32 * kc + e) * kD + 16 * t];
         }
     };
-    load_BF(1);
+    // the next step >= g that is computed (G - 1 if none)
+    auto next_step = [&](int g) {
+        while (g + 1 < a.G && s_drop[g])
+            ++g;
+        return g + 1 < a.G ? g : a.G - 1;
+    };
+    int loaded = next_step(1);
+    if (loaded + 1 < a.G)
+        load_BF(loaded);
+    bool have = false;  // ahi / alo hold S_g
     for (int g = 1; g + 1 < a.G; ++g) {
+        if (s_drop[g]) {
+            have = false;  // S_{g+1} = F_g
+            continue;
+        }
+        if (!have)  // S_1, or F_{g-1} after a dropped step
+            split_A((g == 1 ? blk(a.segS, 1) : blk(a.segF, g - 1)) + (size_t)(r0 + m) * kD);
         f32x4_t acc[2];
         u32x4_t ch[2][4], cl[2][4];
 #pragma unroll
@@ -1485,8 +1665,9 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
                 cl[t][kc] = u32x4_t{p0[1], p1[1], p2[1], p3[1]};
             }
         }
-        if (g + 2 < a.G)
-            load_BF(g + 1);
+        loaded = next_step(g + 1);
+        if (loaded + 1 < a.G)
+            load_BF(loaded);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -1507,6 +1688,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
             }
         __syncthreads();
         split_A(&s_rows[m][0]);
+        have = true;
     }
 }
 
@@ -1572,17 +1754,24 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
     a.G = f.lay.seg.G;
     a.L = f.lay.seg.L;
-    a.L0 = f.lay.seg.L0;
-    const size_t seg_floats = (size_t)chains * (size_t)a.G * kD * kD;
+    const size_t seg_units = (size_t)chains * (size_t)a.G;
+    const size_t seg_floats = seg_units * kD * kD;
     a.segS = reinterpret_cast<float *>(f.ws + f.lay.off_seg);
     a.segF = a.segS + seg_floats;
     a.segP = a.segF + seg_floats;
+    a.segZ = reinterpret_cast<int32_t *>(f.ws + f.lay.off_segaux);
+    a.segD = a.segZ + seg_units;
+    a.segN = reinterpret_cast<float *>(a.segD + seg_units);
+    a.trunc = (f.flags & kL2In) && (f.flags & kSigIn);
     // separate instantiations read the activation switches (when any is off) and run column
     // halves (whole-chain launches where the chunk table may split sequences)
     const bool sw = f.flags != (kGateIn | kL2In | kSigIn);
     const bool halves = split_plan(f.H, f.lay.n_seq, a.G, f.cu != nullptr);
-    void (*fused)(FusedArgs) = halves ? (sw ? fused_kernel<true, true> : fused_kernel<false, true>)
-                                      : (sw ? fused_kernel<true, false> : fused_kernel<false, false>);
+    void (*fused)(FusedArgs) =
+        a.G > 1 ? (sw ? fused_kernel<true, kModeSeg> : fused_kernel<false, kModeSeg>)
+        : halves ? (sw ? fused_kernel<true, kModeHalves> : fused_kernel<false, kModeHalves>)
+                 : (sw ? fused_kernel<true, kModeWhole> : fused_kernel<false, kModeWhole>);
+    void (*trans)(FusedArgs) = sw ? fused_kernel<true, kModeTrans> : fused_kernel<false, kModeTrans>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fused),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
     if (e != hipSuccess)
@@ -1599,22 +1788,29 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
             return e;
         return mark(2);
     }
+    // pass A (segments 0 .. G-1 with out, end-state norms), then the transition runs of
+    // segments 1 .. G-1 (their stopping bound reads the norms)
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(trans), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kFusedLds)) != hipSuccess)
+        return e;
     a.pass = 1;
-    hipLaunchKernelGGL(fused, dim3((unsigned)(chains * (2 * a.G - 3))), dim3(512), kFusedLds, s, a);
+    hipLaunchKernelGGL(fused, dim3((unsigned)(chains * a.G)), dim3(512), kFusedLds, s, a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    a.pass = 3;
+    hipLaunchKernelGGL(trans, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
     if ((e = hipGetLastError()) != hipSuccess || (e = mark(0)) != hipSuccess)
         return e;
-    if (a.G > 2) {
-        ScanArgs sa;
-        sa.segS = a.segS;
-        sa.segF = a.segF;
-        sa.segP = a.segP;
-        sa.G = a.G;
-        sa.chains = chains;
-        hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(chains * (kD / 16))), dim3(256), 0, s, sa);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
-    }
-    if ((e = mark(1)) != hipSuccess)
+    ScanArgs sa;
+    sa.segS = a.segS;
+    sa.segF = a.segF;
+    sa.segP = a.segP;
+    sa.segZ = a.segZ;
+    sa.segD = a.segD;
+    sa.G = a.G;
+    sa.chains = chains;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(chains * (kD / 16))), dim3(256), 0, s, sa);
+    if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
         return e;
     a.pass = 2;
     hipLaunchKernelGGL(fused, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);

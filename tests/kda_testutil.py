@@ -113,41 +113,30 @@ def bf16_round_f64(x):
 PLAN_CUS = 256
 
 
-COST_OUT, COST_FP = 5, 4  # relative time per chunk of units with and without output
-LONG_SEG0_CHAINS = 16     # a longer segment 0 only with at least this many chains
+SEG_MIN_CHUNKS = 16       # shortest segment the plan makes
+TRUNC_TAU = 2.0 ** -50    # entry bound at which a segment's transition run stops
+TRUNC_M = 4096.0          # Frobenius bound on a segment's start state for dropping its share
 
 
 def segment_plan(chains, nch):
-    """(G, L, L0): segments per chain, chunks per segment 1 .. G-1 and chunks of segment 0
-    that the forward pass picks for `chains` equal-length chains of `nch` chunks (G = 1:
-    whole chains).  Pass A runs the segment-0 units alongside rA rounds of F and P units on
-    the CUs they leave free, and (with at least 16 chains) segment 0 is sized so that both
-    take about as long (units that write out cost 5/4 of an output-free F or P run per
-    chunk); with fewer chains all segments are equal.  The cost counts pass A,
-    pass B (rounds of G - 1 units per chain) and the scan."""
-    rounds = lambda u, c: -(-u // c)
-    best = (1, nch, nch)
-    if chains <= 0 or nch < 32 or chains >= 192:
-        return best
-    best_cost = rounds(chains, PLAN_CUS) * nch * COST_OUT
-    G = 3
-    while G <= 256 and G <= nch // 8:
-        rA = rounds(2 * chains * (G - 2), PLAN_CUS - chains)
-        rB = rounds(chains * (G - 1), PLAN_CUS)
-        L = (-(-(nch * COST_OUT) // ((G - 1) * COST_OUT + rA * COST_FP)) if chains >= LONG_SEG0_CHAINS
-             else -(-nch // G))
-        L0 = nch - (G - 1) * L
-        if L0 >= 1:
-            cost = max(L0 * COST_OUT, rA * L * COST_FP) + rB * L * COST_OUT + 2 * G * COST_OUT
-            if cost < best_cost:
-                best_cost, best = cost, (G, L, L0)
-        G += 1
-    return best
+    """(G, L): segments per chain and chunks per segment (the last one shorter) that the
+    forward pass picks for `chains` equal-length chains of `nch` chunks (G = 1: whole
+    chains).  G fills the 256 CUs with one round of pass A units (segments of every chain)
+    of at least 16 chunks, with no empty segment."""
+    cdiv = lambda a, b: -(-a // b)
+    if chains <= 0 or chains > PLAN_CUS // 2:
+        return 1, nch
+    G = min(PLAN_CUS // chains, nch // SEG_MIN_CHUNKS)
+    while G >= 2 and (G - 1) * cdiv(nch, G) >= nch:
+        G -= 1
+    if G < 2:
+        return 1, nch
+    return G, cdiv(nch, G)
 
 
-def segment_bounds(G, L, L0, nch):
+def segment_bounds(G, L, nch):
     """First chunk of each segment 0 .. G-1, and nch at the end: G + 1 entries."""
-    return [0] + [min(L0 + (g - 1) * L, nch) for g in range(1, G)] + [nch]
+    return [min(g * L, nch) for g in range(G)] + [nch]
 
 
 def table_bytes(N):
@@ -159,9 +148,25 @@ def table_bytes(N):
 
 def segment_states(ws, B, H, G):
     """The fp32 segment states S, F, P of a segmented call, read back from its workspace:
-    three float64 arrays [B, H, G, 128, 128] (V-major)."""
+    three float64 arrays [B, H, G, 128, 128] (V-major).  S_g (g >= 2) is written only where
+    the scan computed it; F_g, P_g (g >= 1) hold the runs from zero and from the identity
+    (P_g only where its run went the whole segment)."""
     n = B * H * G * 128 * 128
     off = table_bytes(B)
     raw = ws[off:off + 3 * 4 * n].cpu().numpy().view(np.float32).astype(np.float64)
     S, F, P = (raw[i * n:(i + 1) * n].reshape(B, H, G, 128, 128) for i in range(3))
     return S, F, P
+
+
+def segment_aux(ws, B, H, G):
+    """Per segment of a segmented call: z (chunks its transition run took before it
+    stopped, -1: the whole segment), drop (1 where the scan dropped the segment's start
+    state's share of the next one) and the squared norms of pass A's end states (per
+    consumer wavefront): int64 [B, H, G], int64 [B, H, G], float64 [B, H, G, 4]."""
+    units = B * H * G
+    off = table_bytes(B) + 3 * 4 * units * 128 * 128
+    raw = ws[off:off + units * 24].cpu().numpy()
+    z = raw[:4 * units].view(np.int32).astype(np.int64).reshape(B, H, G)
+    drop = raw[4 * units:8 * units].view(np.int32).astype(np.int64).reshape(B, H, G)
+    nrm = raw[8 * units:24 * units].view(np.float32).astype(np.float64).reshape(B, H, G, 4)
+    return z, drop, nrm

@@ -46,10 +46,10 @@ def parity(w, what):
 ])
 def test_segmented_weak_decay(B, T, H, lb, sd):
     """Segmented runs (G >= 5) where the state persists across segments."""
-    G, L, L0 = segment_plan(B * H, -(-T // 16))
+    G, L = segment_plan(B * H, -(-T // 16))
     assert G >= 5, (B, T, H, G)
     w = W.make(f"segweak_B{B}_T{T}_H{H}_lb{lb}", B, T, H, seed=400 + T + H, lower_bound=lb, state_dtype=sd)
-    parity(w, f"segmented G={G} L={L} L0={L0} lb={lb} {sd}")
+    parity(w, f"segmented G={G} L={L} lb={lb} {sd}")
 
 
 def _window(w, t0, t1, v_zero=False):
@@ -73,7 +73,7 @@ def test_segment_states_match_oracle(lb):
     over the same token ranges: F_g from zero, P_g from the identity with v = 0, S_g the
     state of the one-shot run at the segment's first token."""
     B, T, H = 1, 4096, 2
-    G, L, L0 = segment_plan(B * H, T // 16)
+    G, L = segment_plan(B * H, T // 16)
     assert G >= 5
     w = W.make(f"segstates{lb}", B, T, H, seed=420, lower_bound=lb, state_dtype="fp32")
     _, _, ws = run_gpu(w)
@@ -81,7 +81,7 @@ def test_segment_states_match_oracle(lb):
     h0 = w.initial_state.astype(np.float64)
     eye = np.broadcast_to(np.eye(128), (B, H, 128, 128)).copy()
     zero = np.zeros((B, H, 128, 128))
-    bounds = [min(16 * c, T) for c in segment_bounds(G, L, L0, T // 16)]  # first token of segment g
+    bounds = [min(16 * c, T) for c in segment_bounds(G, L, T // 16)]  # first token of segment g
     worst = {"S": 0.0, "F": 0.0, "P": 0.0}
     for g in range(1, G - 1):
         t0, t1 = bounds[g], bounds[g + 1]
@@ -99,7 +99,7 @@ def test_segment_states_match_oracle(lb):
     rP = _oracle_state(w, bounds[g], bounds[g + 1], eye, v_zero=True)
     rS1 = _oracle_state(w, 0, bounds[g + 1], h0)
     assert rel_l2(np.einsum("bhvc,bhcd->bhvd", rSg, rP) + rF, rS1) < 1e-12
-    print(f"segment states G={G} L={L} L0={L0} lb={lb}: worst relL2 " +
+    print(f"segment states G={G} L={L} lb={lb}: worst relL2 " +
           " ".join(f"{k} {v:.2e}" for k, v in worst.items()), flush=True)
 
 

@@ -57,11 +57,12 @@ def test_workspace_size_formula():
     for B, T, H in [(1, 64, 1), (3, 17, 5), (1, 0, 4), (2, 300, 100), (1, 1 << 20, 200)]:
         assert ws_size(B, T, H) == table_bytes(B)
     # few long equal-length chains: plus three fp32 128x128 states per chain and segment
+    # and 24 bytes of per-segment words (rounded up to 256)
     for B, T, H in [(2, 4096, 16), (1, 1 << 20, 8), (1, 700, 1)]:
         extra = ws_size(B, T, H) - table_bytes(B)
         per_seg = 3 * B * H * 128 * 128 * 4
-        assert extra > 0 and extra % per_seg == 0, (B, T, H, extra)
         G = extra // per_seg
+        assert extra == G * per_seg + -(-B * H * G * 24 // 256) * 256, (B, T, H, extra)
         assert 2 <= G <= -(-T // 16), (B, T, H, G)
     # with cu_seqlens: chunk table only
     for N, T in [(8, 32000), (256, 65000), (3, 5), (1, 1 << 20)]:
@@ -246,14 +247,17 @@ def test_segment_plan_replica():
     from kda_testutil import segment_plan
     for B, T, H in [(1, 700, 1), (1, 8192, 2), (1, 6000, 2), (3, 4096, 2), (2, 5000, 3), (1, 4103, 1),
                     (1, 4096, 2), (2, 4096, 16), (1, 1 << 20, 8), (3, 1500, 2), (1, 1 << 20, 1),
-                    (1, 100, 4), (5, 4000, 40)]:
+                    (1, 100, 4), (5, 4000, 40), (1, 255, 1), (1, 256, 1), (1, 540, 1), (130, 9000, 1),
+                    (1, 9000, 128), (3, 33 * 16 + 1, 1)]:
         nch = -(-T // 16)
-        G, L, L0 = segment_plan(B * H, nch)
-        extra = ws_size(B, T, H) - table_bytes(B)
-        got = 1 if extra == 0 else extra // (3 * B * H * 128 * 128 * 4)
-        assert got == G, (B, T, H, got, G)
-        # segment 0 is at least as long as the others, and the last one is not empty
-        assert G == 1 or (L0 >= 1 and L0 + (G - 2) * L < nch <= L0 + (G - 1) * L), (B, T, H, G, L, L0)
+        G, L = segment_plan(B * H, nch)
+        # segment states S, F, P (fp32 128 x 128 per chain and segment), then 24 bytes of
+        # per-segment words rounded up to 256
+        units = B * H * G
+        want = 0 if G == 1 else 3 * units * 128 * 128 * 4 + -(-units * 24 // 256) * 256
+        assert ws_size(B, T, H) - table_bytes(B) == want, (B, T, H, G)
+        # one round of pass A units, segments of at least 16 chunks, none empty
+        assert G == 1 or (B * H * G <= 256 and L >= 16 and (G - 1) * L < nch <= G * L), (B, T, H, G, L)
 
 
 def test_sequence_count_limit():
