@@ -15,9 +15,9 @@ kernel's duration (recording an event between two launches delays the second one
 microseconds, so these steps are timed separately and reported as ms_per_step_with_events).
 roofline: the dominant kernel, fused_kernel (the forward kernel), against HBM; for the
 decode workload (--workload 5, one token per sequence) the step is kda_fwd_recurrent and
-the dominant kernel is recurrent_kernel.  Without
-segmentation fused_kernel runs once per step; with it (few long chains) twice, pass A and
-pass B, with seg_scan_kernel between them.  achieved = the path's algorithmic bytes per
+the dominant kernel is recurrent_kernel.  With a
+whole-chain plan fused_kernel runs once per step; with the cut plan (long sequences)
+three times, pass A, the transition runs and pass B, with seg_scan_kernel before pass B.  achieved = the path's algorithmic bytes per
 step / fused_kernel's time per step (the sum over its launches): q, k, v, g (4 x 256 B) +
 beta (2 B) + out (256 B) per head-token, plus initial/final state.  traffic (when the
 committed rocprofv3 summary matches the kernel source) is fused_kernel's calibrated
@@ -270,7 +270,7 @@ def main():
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t1
 
-    # intervals: table, forward launch 1, scan, forward launch 2
+    # intervals: table, pass A (+ transition runs) or the one forward launch, scan, pass B
     iv = [0.0, 0.0, 0.0, 0.0]
     for i in range(args.steps):
         for j in range(2 if recurrent else 4):
@@ -284,7 +284,7 @@ def main():
     else:
         launches = kda.forward_launches(w.B, w.T, w.H, w.N, cu is not None)
         stage_names = ["chunk_table_kernel", "fused_kernel", "seg_scan_kernel"]
-        if launches == 2:
+        if launches > 1:
             stage_ms = [iv[0], iv[1] + iv[3], iv[2]]
         else:  # one forward launch; the later marks are recorded back to back
             stage_ms = [iv[0], iv[1], 0.0]

@@ -16,49 +16,57 @@ constexpr size_t kAlign = 256;
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Segment plan for few, long, equal-length chains (no cu_seqlens).  The state after a
-// segment is affine in the state before it: S_end = S_begin Phi + F, with F the segment run
-// from S = 0 and Phi the segment's transition (the run from S = I with v = 0).  A chain is
-// cut into G segments of L chunks (the last one shorter), and the forward pass runs:
-//   pass A:   segment 0 from the true initial state and segments 1 .. G-1 from S = 0, all
-//             with out; the end states S_1 and F_g and their norms.
-//   transition runs, segments 1 .. G-1: from I with v = 0.  With the in-kernel l2norm and
-//             beta sigmoid every token's transition diag(alpha)(I - beta k^ k^T) has
-//             spectral norm <= 1, so |S_g|_F <= B_g = |S_1|_F + |F_1|_F + ... + |F_{g-1}|_F,
-//             and once every entry of the run's state is below kTruncRel |F_g|_F / B_g
-//             after z chunks, S_g's share of every later state of the segment is below
-//             2^-30 |F_g|_F.  The run stops there and records z; otherwise it runs the whole
-//             segment and keeps Phi_g.
-//   scan:     S_{g+1} = F_g where the run stopped (that share dropped), else
-//             S_{g+1} = S_g Phi_g + F_g.
-//   pass B:   segments 1 .. G-1 again from S_g, with out: only the first z chunks where the
-//             share was dropped (pass A's out is right from there on), else all of them.
-// With a strong gate (the transition falls below 2^-40 within 2 - 4 chunks at lower bounds
-// -5 .. -2) that is about one segment run per chunk over chains x G units; with weak or no
-// decay every run goes the whole way (three segment runs per chunk).  G fills the CUs with
-// one round of pass A units of at least kSegMinChunks chunks each.
+// Cut plan (long sequences: batch rows or varlen).  The P workgroups of a head take equal
+// runs of the head's chunk list (its sequences one after another, in index order): run w
+// covers chunks [x_w, x_{w+1}) with x_j = floor(j C / P), C the head's chunk count, and a
+// cut x_j moved to the nearest sequence boundary when one lies within
+// min(kSnapChunks, C / (4P)) chunks.  A cut inside a sequence splits it into pieces; the
+// state after a piece is affine in the state before it: S_end = S_begin Phi + F, with F
+// the piece run from S = 0 and Phi its transition (the run from S = I with v = 0).  The
+// forward pass runs:
+//   pass A:   the P runs of every head, each piece with out: a piece starting a sequence
+//             from the true initial state, one starting at a cut from S = 0; end states go
+//             to final_state, to S_j (the exact state at the sequence's first cut) or to F_j,
+//             with their norms.
+//   transition runs, one per (head, cut inside a sequence): from I with v = 0.  With the
+//             in-kernel l2norm and beta sigmoid every token's transition
+//             diag(alpha)(I - beta k^ k^T) has spectral norm <= 1, so |S_j|_F <= B_j = |S_j0|_F
+//             + |F_j0|_F + ... + |F_{j-1}|_F (j0 the sequence's first cut), and once every
+//             entry of the run's state is below kTruncRel |F_j|_F / B_j after z chunks,
+//             S_j's share of every later state of the piece is below 2^-30 |F_j|_F.  The
+//             run stops there and records z; otherwise it runs the whole piece and keeps
+//             Phi_j.
+//   scan:     S_{j+1} = F_j where the run stopped (that share dropped), else
+//             S_{j+1} = S_j Phi_j + F_j, for consecutive cuts inside one sequence.
+//   pass B:   every piece starting at a cut again from S_j, with out: only the first z
+//             chunks where the share was dropped (pass A's out is right from there on),
+//             else all of them; a piece that ends its sequence writes final_state.
+// With a strong gate (the transition falls below 2^-40 within 2 - 5 chunks at lower bounds
+// -5 .. -2) that is about one run per chunk, over P runs per head; with weak or no decay
+// every run goes the whole way (three runs per chunk of a cut sequence).  The plan is taken
+// when the heads leave at least two workgroups each and sequences are long on average
+// (many short ones are better balanced whole, see the whole-chain plans below); runs are
+// at least kSegMinChunks chunks long.
 constexpr int64_t kPlanCUs = 256;   // MI355X compute units
 constexpr int64_t kSegMinChunks = 16;
+constexpr int64_t kCutMinAvg = 64;  // average chunks per sequence for the cut plan
+constexpr int64_t kSnapChunks = 8;
 constexpr float kTruncRel = 0x1p-37f;  // 2^-30 / 128
 
-struct SegPlan {
-    int G;        // segments per chain (1 = no segmentation)
-    int64_t L;    // chunks per segment (the last may be shorter)
-};
-
-inline SegPlan plan_segments(int64_t chains, int64_t nch)
+// Workgroups per head of the cut plan (1: whole-chain plans).  C is the head's chunk count
+// for batch rows, its lower bound ceil(T / 16) for varlen.
+inline int64_t plan_cuts(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen)
 {
-    const SegPlan none{1, nch};
-    if (chains <= 0 || chains > kPlanCUs / 2)
-        return none;
-    int64_t G = kPlanCUs / chains;
-    if (G > nch / kSegMinChunks)
-        G = nch / kSegMinChunks;
-    while (G >= 2 && (G - 1) * cdiv(nch, G) >= nch)  // no empty segment
-        --G;
-    if (G < 2)
-        return none;
-    return SegPlan{(int)G, cdiv(nch, G)};
+    if (H < 1 || H > kPlanCUs / 2)
+        return 1;
+    const int64_t nseq = varlen ? N : B;
+    const int64_t C = varlen ? cdiv(T, kCH) : B * cdiv(T, kCH);
+    if (nseq < 1 || C < nseq * kCutMinAvg)
+        return 1;
+    int64_t P = kPlanCUs / H;
+    if (P > C / kSegMinChunks)
+        P = C / kSegMinChunks;
+    return P >= 2 ? P : 1;
 }
 
 // Column halves.  When a head has few workgroups and few sequences, the chunk table may run
@@ -76,12 +84,12 @@ inline bool split_eligible(int64_t H, int64_t n_seq)
 }
 
 // The whole-chain launch may run column halves: varlen (equal-length batch rows never gain
-// from a split), whole chains (no segment plan), few sequences and workgroups per head.
+// from a split), whole chains (no cut plan), few sequences and workgroups per head.
 // The chunk table plans halves and the forward launch picks the kernel instance that runs
 // them under this same condition.
-inline bool split_plan(int64_t H, int64_t n_seq, int seg_G, bool varlen)
+inline bool split_plan(int64_t H, int64_t n_seq, int64_t cutP, bool varlen)
 {
-    return varlen && seg_G <= 1 && split_eligible(H, n_seq);
+    return varlen && cutP <= 1 && split_eligible(H, n_seq);
 }
 
 // Workgroups per head of the whole-chain launch: about one workgroup per CU over all
@@ -103,10 +111,11 @@ struct Layout {
     size_t off_seq_start, off_seq_len, off_seq_off;
     size_t off_wg;     // int64 [kPlanCUs + 1]: first unit of each whole-chain workgroup of a head
     size_t off_units;  // int32 [2 N]: whole-chain units, (sequence << 2) | (0 whole, 1 + column half)
-    SegPlan seg;       // segment plan (G == 1 without segmentation)
-    size_t off_seg;    // fp32 states S, F, P: 3 x [chains][G][128][128] when G > 1
-    size_t off_segaux; // when G > 1: int32 z [chains][G], int32 drop [chains][G],
-                       // fp32 squared norms [chains][G][4]
+    size_t off_cut;    // int32 cut_seq, cut_off, cut_first [kPlanCUs + 1] each: the cut plan
+    int64_t cutP;      // workgroups per head of the cut plan (1: whole-chain plans)
+    size_t off_seg;    // fp32 states S, F, P: 3 x [H][P][128][128] when cutP > 1
+    size_t off_segaux; // when cutP > 1: int32 z [H][P], int32 drop [H][P], fp32 squared
+                       // norms of S_j and of F_j [H][P][4] each
     size_t total;
 };
 
@@ -139,14 +148,16 @@ inline bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen,
     off = round_up(off + sizeof(int64_t) * (size_t)(kPlanCUs + 1), kAlign);
     L->off_units = off;
     off = round_up(off + sizeof(int32_t) * 2 * (size_t)N, kAlign);
-    L->seg = varlen ? SegPlan{1, 0} : plan_segments(N * H, cdiv(T, kCH));
+    L->off_cut = off;
+    off = round_up(off + sizeof(int32_t) * 3 * (size_t)(kPlanCUs + 1), kAlign);
+    L->cutP = plan_cuts(B, T, H, N, varlen);
     L->off_seg = off;
     L->off_segaux = off;
-    if (L->seg.G > 1) {
-        const size_t units = (size_t)(N * H) * (size_t)L->seg.G;
-        off += 3 * units * kD * kD * sizeof(float);
+    if (L->cutP > 1) {
+        const size_t slots = (size_t)H * (size_t)L->cutP;
+        off += 3 * slots * kD * kD * sizeof(float);
         L->off_segaux = off;
-        off = round_up(off + units * (2 * sizeof(int32_t) + 4 * sizeof(float)), kAlign);
+        off = round_up(off + slots * (2 * sizeof(int32_t) + 8 * sizeof(float)), kAlign);
     }
     L->total = off;
     return true;

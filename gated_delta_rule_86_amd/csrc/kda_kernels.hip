@@ -121,8 +121,10 @@ struct TableArgs {
     int64_t *seq_start, *seq_len, *seq_off;
     int64_t *wg_first;  // [P + 1]: first unit of each whole-chain workgroup of a head
     int32_t *units;     // [2 N]: (sequence << 2) | (0 whole, 1 + column half)
-    int whole;          // the forward pass runs whole chains (no segment plan)
+    int whole;          // the forward pass runs whole chains (no cut plan)
     int split;          // whole-chain pass that may split sequences into column halves
+    int64_t Pc;         // workgroups per head of the cut plan (0: none)
+    int32_t *cut_seq, *cut_off, *cut_first;  // [Pc + 1]: the cut plan's cuts
 };
 
 __device__ void chunk_table_body(const TableArgs &a, int tid);
@@ -301,9 +303,71 @@ __device__ void plan_snake(const TableArgs &a, int tid)
         a.wg_first[b] = first(b);
 }
 
+// Cut plan (see kda_internal.h): cut j = (sequence cut_seq[j], chunk cut_off[j] of it) at
+// chunk x_j = floor(j C / Pc) of the head's chunk list, moved to the nearest sequence
+// boundary within min(kSnapChunks, C / (4 Pc)) chunks.  The sequence of chunk x is the first
+// one ending after x (empty sequences before it stay with the run before); cut 0 = (0, 0)
+// takes leading empty sequences, cut Pc = (N, 0).  cut_first[j]: the first of the cuts
+// inside cut j's sequence (j itself for a cut at a sequence boundary).
+__device__ void plan_cut_table(const TableArgs &a, int tid)
+{
+    __shared__ int32_t s_seq[kPlanCUs + 1], s_off[kPlanCUs + 1];
+    __threadfence();
+    __syncthreads();
+    const int64_t C = a.seq_off[a.N], P = a.Pc;
+    int64_t snap = C / (4 * P);
+    if (snap > kSnapChunks)
+        snap = kSnapChunks;
+    auto holder = [&](int64_t x) {  // smallest i with seq_off[i + 1] > x, N if none
+        int64_t lo = 0, hi = a.N;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (a.seq_off[mid + 1] > x)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        return lo;
+    };
+    for (int64_t j = tid; j <= P; j += 256) {
+        int64_t x = j * C / P, i;
+        if (j == 0) {
+            i = 0;
+            x = 0;
+        } else if (j == P) {
+            i = a.N;
+            x = C;
+        } else {
+            i = holder(x);
+            if (i < a.N) {
+                const int64_t dlo = x - a.seq_off[i], dhi = a.seq_off[i + 1] - x;
+                if (dlo > 0 && dlo <= snap)
+                    x -= dlo;
+                else if (dlo > 0 && dhi <= snap)
+                    x += dhi;
+                i = holder(x);
+            }
+        }
+        a.cut_seq[j] = s_seq[j] = (int32_t)i;
+        a.cut_off[j] = s_off[j] = i < a.N ? (int32_t)(x - a.seq_off[i]) : 0;
+    }
+    __syncthreads();
+    for (int64_t j = tid; j <= P; j += 256) {
+        int64_t j0 = j;
+        if (s_off[j] > 0)
+            while (j0 > 1 && s_seq[j0 - 1] == s_seq[j] && s_off[j0 - 1] > 0)
+                --j0;
+        a.cut_first[j] = (int32_t)j0;
+    }
+}
+
 __global__ __launch_bounds__(256) void chunk_table_kernel(TableArgs a)
 {
     chunk_table_body(a, threadIdx.x);
+    if (a.Pc > 1) {
+        plan_cut_table(a, threadIdx.x);
+        return;
+    }
     partition_sequences(a, threadIdx.x);
     if (a.split && a.N <= kSplitMaxSeq && a.P <= kSplitMaxP)
         plan_halves(a, threadIdx.x);
@@ -551,14 +615,14 @@ struct FusedArgs {
     const int64_t *wg_first;  // whole-chain pass: first unit of each workgroup of a head
     const int32_t *units;     // whole-chain units: (sequence << 2) | (0 whole, 1 + column half)
     int32_t *status;
-    // segmented runs: pass 0 = whole chains, 1 = pass A, 2 = pass B, 3 = transition runs
-    // (see SegPlan)
-    int pass, G;
-    int64_t L;  // chunks per segment
-    float *segS, *segF, *segP;  // [chains][G][128][128] fp32, V-major
-    int32_t *segZ;   // [chains][G]: chunks a transition run took before stopping, -1 = all
-    int32_t *segD;   // [chains][G]: 1 where the scan dropped S_g's share of S_{g+1}
-    float *segN;     // [chains][G][4]: squared norm of pass A's end state, per consumer
+    // pass 0 = whole chains; cut plan (kda_internal.h): 1 = pass A, 2 = pass B,
+    // 3 = transition runs
+    int pass, Pc;    // Pc: workgroups per head of the cut plan
+    const int32_t *cut_seq, *cut_off, *cut_first;  // [Pc + 1]
+    float *segS, *segF, *segP;  // [H][Pc][128][128] fp32, V-major, slot (h, cut j)
+    int32_t *segZ;   // [H][Pc]: chunks a transition run took before stopping, -1 = all
+    int32_t *segD;   // [H][Pc]: 1 where the scan dropped S_j's share of S_{j+1}
+    float *segNS, *segNF;  // [H][Pc][4]: squared norms of S_j and F_j, per consumer
     int trunc;       // transition runs may stop early (in-kernel l2norm and beta sigmoid)
 };
 
@@ -579,7 +643,7 @@ struct Unit {
     float *nrm;           // pass A: squared norm of the end state, one float per consumer
     const float *fin_src; // fp32 state written as the final state instead of the run's own
     int32_t *zout;        // transition runs: where the chunk count before the stop goes
-    int seg;              // segment passes: the segment
+    float thr;            // transition runs: stop once every state entry is below this
 };
 
 // A workgroup's work: one unit (segment passes), or -- whole-chain pass -- the units
@@ -590,82 +654,162 @@ struct WgPlan {
     int pass;
     int h;
     int64_t sub, n_end;   // whole-chain pass: units sub, sub + 1, ... < n_end
-    int64_t n;            // segment passes: the sequence
-    int seg;              // segment passes: the segment
+    int64_t n;            // (unused by the cut plan)
+    int seg;              // cut plan: the run (pass A) or the cut (passes B, 3)
 };
 
+// Launch kinds of the fused kernel: whole chains (pass 0), whole chains that may hold column
+// halves (pass 0), the cut plan's pass A (1), pass B (2) and transition runs (3).  The unit
+// lookups below are instantiated per kind, so each kernel carries only its own pass.
+constexpr int kModeWhole = 0, kModeHalves = 1, kModeA = 2, kModeTrans = 3, kModeB = 4;
+
+__device__ __forceinline__ int64_t seq_chunks(const FusedArgs &a, int64_t i) { return (a.seq_len[i] + kCH - 1) / kCH; }
+
+// A piece of the cut plan: chunks [c0, c1) of sequence seq.
+struct Piece {
+    int64_t seq;
+    int c0, c1;
+};
+// Piece k of run w (pass A); false past the run's end.
+__device__ bool run_piece(const FusedArgs &a, int w, int64_t k, Piece &p)
+{
+    const int64_t i0 = a.cut_seq[w], i1 = a.cut_seq[w + 1], i = i0 + k;
+    const int o1 = a.cut_off[w + 1];
+    if (i > i1 || (i == i1 && o1 == 0))
+        return false;
+    const int64_t n = seq_chunks(a, i);
+    p.seq = i;
+    p.c0 = k == 0 ? a.cut_off[w] : 0;
+    p.c1 = i == i1 ? o1 : (int)n;
+    return !(p.c0 == p.c1 && n > 0);  // (a run with no chunks)
+}
+// The piece that starts at cut j (passes B and 3); false for a cut at a sequence boundary.
+__device__ bool cut_piece(const FusedArgs &a, int j, Piece &p)
+{
+    const int o = a.cut_off[j];
+    if (o == 0)
+        return false;
+    const int64_t i = a.cut_seq[j];
+    p.seq = i;
+    p.c0 = o;
+    p.c1 = a.cut_seq[j + 1] == i ? a.cut_off[j + 1] : (int)seq_chunks(a, i);
+    return true;
+}
+// First of the cuts inside the sequence that holds cut j (a cut inside it): j0 <= j.
+__device__ __forceinline__ int first_cut(const FusedArgs &a, int j) { return a.cut_first[j]; }
+
+template <int kMode>
 __device__ bool unit_at(const FusedArgs &a, const WgPlan &w, int64_t k, Unit &u)
 {
+    constexpr bool kWholeMode = kMode == kModeWhole || kMode == kModeHalves;
     constexpr int64_t kBlock = (int64_t)kD * kD;
-    int64_t n;
-    u.half = -1;
-    if (w.pass == 0) {
-        if (w.sub + k >= w.n_end)
-            return false;
-        const int32_t code = a.units[w.sub + k];
-        n = code >> 2;
-        u.half = (code & 3) - 1;
-    } else {
-        if (k > 0)
-            return false;
-        n = w.n;
-    }
-    const int64_t chain = n * a.H + w.h;
-    u.n = n;
-    u.h = w.h;
-    u.len = a.seq_len[u.n];
-    u.start = a.seq_start[u.n];
-    const int64_t nch = (u.len + kCH - 1) / kCH;
     const size_t elt = a.h0_dtype == 1 ? 2 : 4, elt_t = a.ht_dtype == 1 ? 2 : 4;
-    const void *h0c = a.h0 ? reinterpret_cast<const unsigned char *>(a.h0) + (size_t)chain * kBlock * elt : nullptr;
-    void *htc = a.ht ? reinterpret_cast<unsigned char *>(a.ht) + (size_t)chain * kBlock * elt_t : nullptr;
-    auto segbuf = [&](float *base, int64_t sg) { return base + ((size_t)chain * a.G + (size_t)sg) * kBlock; };
+    u.half = -1;
+    u.h = w.h;
     u.v_on = true;
     u.out_on = true;
     u.nrm = nullptr;
     u.fin_src = nullptr;
     u.zout = nullptr;
-    if (w.pass == 0) {
+    u.thr = 0.f;
+    auto states = [&](int64_t n, const void *&h0c, void *&htc) {
+        const int64_t chain = n * a.H + w.h;
+        h0c = a.h0 ? reinterpret_cast<const unsigned char *>(a.h0) + (size_t)chain * kBlock * elt : nullptr;
+        htc = a.ht ? reinterpret_cast<unsigned char *>(a.ht) + (size_t)chain * kBlock * elt_t : nullptr;
+    };
+    const void *h0c;
+    void *htc;
+    if constexpr (kWholeMode) {
+        if (w.sub + k >= w.n_end)
+            return false;
+        const int32_t code = a.units[w.sub + k];
+        u.n = code >> 2;
+        u.half = (code & 3) - 1;
+        u.len = a.seq_len[u.n];
+        u.start = a.seq_start[u.n];
+        states(u.n, h0c, htc);
         u.c0 = 0;
-        u.c1 = nch;
+        u.c1 = (u.len + kCH - 1) / kCH;
         u.init_kind = a.h0_dtype;  // 0 none -> zeros, 1 bf16, 2 fp32
         u.init = h0c;
         u.fin_kind = a.ht_dtype;
         u.fin = htc;
         return true;
     }
-    const int64_t seg = w.seg;
-    const int64_t s0 = seg * a.L, s1 = s0 + a.L;
-    u.c0 = s0 < nch ? s0 : nch;
-    u.c1 = s1 < nch ? s1 : nch;
-    u.seg = (int)seg;
-    const size_t su = (size_t)chain * a.G + (size_t)seg;
-    if (w.pass == 1) {                         // pass A: segment 0 exactly, the others from 0
-        u.init_kind = seg == 0 ? a.h0_dtype : kInitZero;
-        u.init = seg == 0 ? h0c : nullptr;
-        u.fin_kind = 2;
-        u.fin = seg == 0 ? segbuf(a.segS, 1) : segbuf(a.segF, seg);
-        u.nrm = a.segN + 4 * su;
-    } else if (w.pass == 3) {                  // transition run: from I, v = 0, no out
+    Piece p;
+    constexpr bool passA = kMode == kModeA;
+    if (passA ? !run_piece(a, w.seg, k, p) : (k > 0 || !cut_piece(a, w.seg, p)))
+        return false;
+    u.n = p.seq;
+    u.len = a.seq_len[u.n];
+    u.start = a.seq_start[u.n];
+    states(u.n, h0c, htc);
+    u.c0 = p.c0;
+    u.c1 = p.c1;
+    const int64_t nch = (u.len + kCH - 1) / kCH;
+    const size_t hs = (size_t)w.h * (size_t)a.Pc;  // slot of cut 0 of this head
+    auto slot = [&](float *base, int j) { return base + (hs + (size_t)j) * kBlock; };
+    if constexpr (passA) {
+        // pass A: run w; a piece that starts at cut w runs from zero (F_w), one that starts
+        // its sequence from the initial state, ending at cut w + 1 (S_{w+1}) or at the end
+        const int wr = w.seg;
+        if (p.c0 > 0) {
+            u.init_kind = kInitZero;
+            u.init = nullptr;
+            u.fin_kind = 2;
+            u.fin = slot(a.segF, wr);
+            u.nrm = a.segNF + 4 * (hs + wr);
+        } else {
+            u.init_kind = a.h0_dtype;
+            u.init = h0c;
+            if (p.c1 < nch) {
+                u.fin_kind = 2;
+                u.fin = slot(a.segS, wr + 1);
+                u.nrm = a.segNS + 4 * (hs + wr + 1);
+            } else {
+                u.fin_kind = a.ht_dtype;
+                u.fin = htc;
+            }
+        }
+    } else if constexpr (kMode == kModeTrans) {
+        // transition run of the piece at cut j: from I, v = 0, no out; stop bound from the
+        // norms of pass A (kda_internal.h)
+        const int j = w.seg, j0 = first_cut(a, j);
         u.init_kind = kInitIdentity;
         u.init = nullptr;
         u.v_on = false;
         u.out_on = false;
         u.fin_kind = 2;
-        u.fin = segbuf(a.segP, seg);
-        u.zout = a.segZ + su;
-    } else {                                   // pass B: from S_seg, the first z chunks or all
-        // (a dropped share: segD = 1 exactly where the transition run stopped, segZ >= 0)
+        u.fin = slot(a.segP, j);
+        u.zout = a.segZ + hs + j;
+        if (a.trunc) {
+            // |F_j0|_F + ... + |F_{j-1}|_F over the lanes (one cut each), then |S_j0|_F
+            auto fro = [&](const float *nr) { return sqrtf(nr[0] + nr[1] + nr[2] + nr[3]); };
+            const int lane = (int)(threadIdx.x & 63);
+            float part = 0.f;
+            for (int base = j0; base < j; base += 64)
+                if (base + lane < j)
+                    part += fro(a.segNF + 4 * (hs + base + lane));
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+                part += __shfl_xor(part, o);
+            const float bound = fro(a.segNS + 4 * (hs + j0)) + part;
+            u.thr = bound == 0.f ? __builtin_inff() : kTruncRel * fro(a.segNF + 4 * (hs + j)) / bound;
+        }
+    } else {
+        // pass B: the piece at cut j from S_j (F_{j-1} where the scan dropped S_{j-1}'s
+        // share), the first z chunks where S_j's share was dropped, else all of it
+        const int j = w.seg;
         u.init_kind = kInitFp32;
-        u.init = seg > 1 && a.segD[su - 1] ? segbuf(a.segF, seg - 1) : segbuf(a.segS, seg);
-        const bool drop = a.segD[su] != 0;
-        if (drop && u.c0 + a.segZ[su] < u.c1)
-            u.c1 = u.c0 + a.segZ[su];
-        const bool last = seg == a.G - 1;
+        u.init = first_cut(a, j) < j && a.segD[hs + j - 1] ? slot(a.segF, j - 1) : slot(a.segS, j);
+        const bool drop = a.segD[hs + j] != 0;
+        if (drop && u.c0 + a.segZ[hs + j] < u.c1)
+            u.c1 = u.c0 + a.segZ[hs + j];
+        const bool last = p.c1 == nch;
         u.fin_kind = last ? a.ht_dtype : 0;
         u.fin = last ? htc : nullptr;
         if (last && drop)
-            u.fin_src = segbuf(a.segF, seg);
+            u.fin_src = slot(a.segF, j);
     }
     return true;
 }
@@ -676,51 +820,50 @@ struct Range {
     int64_t start, len;  // the sequence's first token and length
     int c0, c1;          // chunk range of the unit
 };
+template <int kMode>
 __device__ bool range_at(const FusedArgs &a, const WgPlan &w, int64_t k, Range &r)
 {
-    int64_t n, seg = 0;
-    if (w.pass == 0) {
+    int64_t n;
+    if constexpr (kMode == kModeWhole || kMode == kModeHalves) {
         if (w.sub + k >= w.n_end)
             return false;
         n = a.units[w.sub + k] >> 2;
-    } else {
-        if (k > 0)
-            return false;
-        n = w.n;
-        seg = w.seg;
-    }
-    r.len = a.seq_len[n];
-    r.start = a.seq_start[n];
-    const int nch = (int)((r.len + kCH - 1) / kCH);
-    if (w.pass == 0) {
+        r.len = a.seq_len[n];
+        r.start = a.seq_start[n];
         r.c0 = 0;
-        r.c1 = nch;
-    } else {
-        const int64_t s0 = seg * a.L, s1 = s0 + a.L;
-        r.c0 = s0 < nch ? (int)s0 : nch;
-        r.c1 = s1 < nch ? (int)s1 : nch;
-        if (w.pass == 2) {  // the chunks pass B reruns (as unit_at)
-            const size_t su = (size_t)(n * a.H + w.h) * a.G + (size_t)seg;
-            if (a.segD[su] && r.c0 + a.segZ[su] < r.c1)
-                r.c1 = r.c0 + (int)a.segZ[su];
-        }
+        r.c1 = (int)((r.len + kCH - 1) / kCH);
+        return true;
+    }
+    Piece p;
+    constexpr bool passA = kMode == kModeA;
+    if (passA ? !run_piece(a, w.seg, k, p) : (k > 0 || !cut_piece(a, w.seg, p)))
+        return false;
+    r.len = a.seq_len[p.seq];
+    r.start = a.seq_start[p.seq];
+    r.c0 = p.c0;
+    r.c1 = p.c1;
+    if constexpr (kMode == kModeB) {  // the chunks pass B reruns (as unit_at)
+        const size_t sl = (size_t)w.h * (size_t)a.Pc + (size_t)w.seg;
+        if (a.segD[sl] && r.c0 + a.segZ[sl] < r.c1)
+            r.c1 = r.c0 + (int)a.segZ[sl];
     }
     return true;
 }
 
 // Walks the workgroup's items (chunks of its units, in order) forward.
+template <int kMode>
 struct ItemWalk {
     int k = 0, base = 0;  // unit index and its first item
     bool valid = false;
     Range r;
-    __device__ void init(const FusedArgs &a, const WgPlan &w) { k = 0; base = 0; valid = range_at(a, w, 0, r); }
+    __device__ void init(const FusedArgs &a, const WgPlan &w) { k = 0; base = 0; valid = range_at<kMode>(a, w, 0, r); }
     // position the walk on the unit holding item it (items only move forward)
     __device__ void seek(const FusedArgs &a, const WgPlan &w, int it)
     {
         while (valid && it >= base + (r.c1 - r.c0)) {
             base += r.c1 - r.c0;
             ++k;
-            valid = range_at(a, w, k, r);
+            valid = range_at<kMode>(a, w, k, r);
         }
     }
 };
@@ -801,12 +944,14 @@ __device__ __forceinline__ void dma_tile16(__amdgpu_buffer_rsrc_t r, unsigned ch
 }
 
 // kSw: the activation switches are read from a.flags; without it every activation runs in
-// the pass (the common case gets code with no switch logic in it).  kQ: the workgroup's
-// units write output rows; without it (the F and P runs of a segment) q is neither loaded
-// nor used, and the output-only operands (QG, Mq) are not formed.
-template <bool kSw, bool kQ, bool kStop>
+// the pass (the common case gets code with no switch logic in it).  kMode: the launch kind.
+// kQ: the workgroup's units write output rows; without it (the transition runs) q is
+// neither loaded nor used, and the output-only operands (QG, Mq) are not formed.  kStop:
+// the consumers may stop the run early (transition runs).
+template <bool kSw, int kMode>
 __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int p, int lane)
 {
+    constexpr bool kQ = kMode != kModeTrans, kStop = kMode == kModeTrans;
     const int64_t H = a.H;
     const int h = w.h;
     const int r = lane & 15;   // token within the chunk
@@ -863,7 +1008,7 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 
     bool spun_out = false;
     // this wavefront prepares items p, p+4, p+8, ...; `nxt` stays 4 items ahead of `cur`
-    ItemWalk cur, nxt;
+    ItemWalk<kMode> cur, nxt;
     cur.init(a, w);
     nxt.init(a, w);
     nxt.seek(a, w, p);
@@ -1110,15 +1255,12 @@ __device__ void fused_producer(const FusedArgs &a, const WgPlan &w, unsigned cha
 // kOut: the unit writes output rows (u.out_on); without it Y and O are not formed and the
 // output-only operands are not read.  NB: 16-column blocks of this wave -- 2 for a whole
 // unit (columns 32cw .. 32cw+31), 1 for a column half (64*half + 16cw .. +15).
-// kP: a transition run (from I, v = 0) of segment g that, when a.trunc allows, stops after
-// the first chunk at whose end every entry of the state is below
-//   thr = kTruncRel |F_g|_F / B_g,   B_g = |S_1|_F + |F_1|_F + ... + |F_{g-1}|_F
-// (norms of pass A's end states).  B_g bounds |S_g|_F whatever the scan drops (every
-// transition has spectral norm <= 1), so the share of S_g that the scan then drops from
-// every later state of the segment is at most 128 thr B_g = 2^-30 |F_g|_F in Frobenius
-// norm.  The four consumers vote after every chunk, so they stop together, and the
-// producers are told through the stop word.  The chunk count goes to *u.zout (-1: ran to
-// the end, state written).
+// kP: a transition run (from I, v = 0) of the piece at cut j that, when a.trunc allows,
+// stops after the first chunk at whose end every entry of the state is below u.thr =
+// kTruncRel |F_j|_F / B_j (the bound of kda_internal.h: S_j's share of every later state
+// of the piece is then at most 2^-30 |F_j|_F in Frobenius norm).  The four consumers vote
+// after every chunk, so they stop together, and the producers are told through the stop
+// word.  The chunk count goes to *u.zout (-1: ran to the end, state written).
 // kSeg: a segment pass unit (pass A end-state norms, pass B final state taken from F).
 template <bool kOut, int NB, bool kP, bool kSeg>
 __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *lds, int cw, int lane,
@@ -1134,16 +1276,8 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
     const int col = lane & 15;
     lds_flag_t *ready = (lds_flag_t *)(lds + kOffFlags);
     lds_flag_t *taken = ready + kNS;
-    int stopped = -1;  // kP: chunks run before the stop
-    float thr = 0.f;   // kP: stop once every entry is below this (NaN: never)
-    if (kP && a.trunc) {
-        const float *nr = a.segN + 4 * (size_t)((u.n * a.H + u.h) * a.G);
-        auto fro = [&](int sg) { return sqrtf(nr[4 * sg] + nr[4 * sg + 1] + nr[4 * sg + 2] + nr[4 * sg + 3]); };
-        float bound = 0.f;
-        for (int sg = 0; sg < u.seg; ++sg)
-            bound += fro(sg);
-        thr = bound == 0.f ? __builtin_inff() : kTruncRel * fro(u.seg) / bound;
-    }
+    int stopped = -1;     // kP: chunks run before the stop
+    const float thr = u.thr;  // kP: stop once every entry is below this (NaN: never)
     unsigned char *vring = lds + kOffVring + cw * (kNV * 1024);
     const uint32_t rowb = (uint32_t)(H * kD * 2);
 
@@ -1476,7 +1610,6 @@ __device__ void consume_unit(const FusedArgs &a, const Unit &u, unsigned char *l
 // kHalves: the unit list may hold column halves (a separate kernel instantiation, so that
 // whole-unit launches carry no NB = 1 code)
 // kMode: launch kind of the fused kernel (below)
-constexpr int kModeWhole = 0, kModeHalves = 1, kModeSeg = 2, kModeTrans = 3;
 
 template <int kMode>
 __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned char *lds, int cw, int lane)
@@ -1484,12 +1617,12 @@ __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned cha
     bool spun_out = false;
     int it0 = 0;
     Unit u;
-    for (int64_t k = 0; unit_at(a, w, k, u); ++k) {
+    for (int64_t k = 0; unit_at<kMode>(a, w, k, u); ++k) {
         // the previous unit's stores are done before this unit's value-ring bookkeeping starts
         wait_vmcnt<0>();
         if (kMode == kModeTrans)
             consume_unit<false, 2, true, false>(a, u, lds, cw, lane, it0, spun_out);
-        else if (kMode == kModeSeg)
+        else if (kMode == kModeA || kMode == kModeB)
             consume_unit<true, 2, false, true>(a, u, lds, cw, lane, it0, spun_out);
         else if (kMode == kModeWhole || u.half < 0)
             consume_unit<true, 2, false, false>(a, u, lds, cw, lane, it0, spun_out);
@@ -1511,7 +1644,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
 
     // this workgroup's work (see SegPlan for the passes)
     WgPlan w;
-    w.pass = kMode == kModeWhole || kMode == kModeHalves ? 0 : kMode == kModeTrans ? 3 : a.pass;
+    w.pass = kMode == kModeWhole || kMode == kModeHalves ? 0 : kMode == kModeA ? 1 : kMode == kModeB ? 2 : 3;
     w.seg = 0;
     const uint32_t bid = blockIdx.x, H32 = (uint32_t)a.H;
     if (w.pass == 0) {
@@ -1523,22 +1656,13 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
         w.n_end = a.wg_first[grp + 1];
         w.n = 0;
     } else {
-        // pass A: segments 0 .. G-1, chain by chain; pass B and the transition runs:
-        // segments 1 .. G-1, chain by chain
-        uint32_t chain;
-        if (w.pass == 1) {
-            chain = bid / (uint32_t)a.G;
-            w.seg = (int)(bid % (uint32_t)a.G);
-        } else {
-            chain = bid / ((uint32_t)a.G - 1u);
-            w.seg = 1 + (int)(bid % ((uint32_t)a.G - 1u));
-        }
-        w.h = (int)(chain % H32);
-        w.n = chain / H32;
+        // cut plan, head h = block % H: pass A takes run block / H, pass B and the transition
+        // runs take cut 1 + block / H
+        w.h = (int)(bid % H32);
+        w.seg = (int)(bid / H32) + (w.pass == 1 ? 0 : 1);
+        w.n = 0;
         w.sub = 0;
         w.n_end = 0;
-        if (w.n >= a.N)
-            return;
     }
 
     if (threadIdx.x < kFlagVote + 8) {
@@ -1552,7 +1676,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     }
     __syncthreads();
     if (wave < 4) {
-        fused_producer<kSw, kMode != kModeTrans, kMode == kModeTrans>(a, w, lds, wave, lane);
+        fused_producer<kSw, kMode>(a, w, lds, wave, lane);
     } else {
         // The consumers set the pace (producers finish ahead and wait for free slots), so
         // they get issue priority over the producer sharing their SIMD.
@@ -1561,50 +1685,55 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a)
     }
 }
 
-// Segment scan: S_{g+1} = S_g P_g + F_g for g = 1 .. G-2, on v_mfma_f32_16x16x32_bf16 with a
-// hi/lo bf16 split of both factors (three products: hi hi, lo hi, hi lo; fp32 accumulate,
-// about 16 significant bits per factor, as the chunk recurrence's state products).  Rows of
-// S are independent: a workgroup takes 16 rows of one chain (8 workgroups per chain).  For
-// contraction chunk kc (32 channels) lane m + 16kg holds S[m][32kc + 8kg + e], e = 0..7 (the
-// A operand), split from the 16 rows kept in LDS between steps.  Wave w forms output column
-// tiles 2w and 2w + 1; lane n + 16kg of chunk kc, tile t takes P[32kc + 8kg + e][16t + n]
-// (the B operand) straight from global memory (16 lanes read 64 contiguous bytes) and
-// splits it; the loads of the next computed step go out before this step's products.
-// Workgroup b takes chain b % chains, so the 8 workgroups of a chain share a slot modulo 8
-// (the XCD the dispatcher gives them, whose L2 then holds that chain's P_g once).
+// Cut scan: S_{j+1} = S_j P_j + F_j for consecutive cuts j, j + 1 inside one sequence, on
+// v_mfma_f32_16x16x32_bf16 with a hi/lo bf16 split of both factors (three products: hi hi,
+// lo hi, hi lo; fp32 accumulate, about 16 significant bits per factor, as the chunk
+// recurrence's state products).  Rows of S are independent: a workgroup takes 16 rows of
+// one head's states (8 workgroups per head).  For contraction chunk kc (32 channels) lane
+// m + 16kg holds S[m][32kc + 8kg + e], e = 0..7 (the A operand), split from the 16 rows
+// kept in LDS between steps.  Wave w forms output column tiles 2w and 2w + 1; lane n + 16kg
+// of chunk kc, tile t takes P[32kc + 8kg + e][16t + n] (the B operand) straight from global
+// memory (16 lanes read 64 contiguous bytes) and splits it; the loads of the next computed
+// step go out before this step's products.  Workgroup b takes head b % H, so the 8
+// workgroups of a head share a slot modulo 8 (the XCD the dispatcher gives them, whose L2
+// then holds that head's P_j once).
 //
-// Dropped shares.  Where segment g's transition run stopped early (z_g >= 0: its state fell
-// below the bound that makes S_g's share negligible), S_{g+1} = F_g: nothing is computed or
-// written, and pass B and the next step read F_g.  The first workgroup of a chain records
+// Dropped shares.  Where the transition run of cut j stopped early (z_j >= 0: its state fell
+// below the bound that makes S_j's share negligible), S_{j+1} = F_j: nothing is computed or
+// written, and pass B and the next step read F_j.  The first workgroup of a head records
 // the decisions for pass B.
 struct ScanArgs {
     float *segS, *segF, *segP;
     const int32_t *segZ;
     int32_t *segD;
-    int G;
-    int64_t chains;
+    const int32_t *cut_seq, *cut_off;
+    int Pc;
+    int64_t H;
 };
 
 __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
 {
     __shared__ __attribute__((aligned(16))) float s_rows[16][kD + 4];
-    __shared__ int s_drop[256];
+    __shared__ int s_drop[kPlanCUs + 1];
+    __shared__ int s_step[kPlanCUs + 1];  // cuts j, j + 1 both inside one sequence
     constexpr int64_t kBlock = (int64_t)kD * kD;
-    const int64_t chain = blockIdx.x % a.chains;
-    const int r0 = (int)(blockIdx.x / a.chains) * 16;
+    const int64_t h = blockIdx.x % a.H;
+    const int r0 = (int)(blockIdx.x / a.H) * 16;
     if (r0 >= kD)
         return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = lane & 15, kg = lane >> 4;  // A: row m, k-group kg; B and D: column m
-    const size_t su0 = (size_t)chain * a.G;
-    if ((int)threadIdx.x < a.G) {
-        const int g = threadIdx.x;
-        s_drop[g] = g > 0 && a.segZ[su0 + g] >= 0;  // (segment 0 has no transition run)
-        if (r0 == 0 && g > 0)
-            a.segD[su0 + g] = s_drop[g];
+    const int P = a.Pc;
+    const size_t hs = (size_t)h * (size_t)P;
+    for (int j = threadIdx.x; j < P; j += 256) {
+        const bool inner = j > 0 && a.cut_off[j] > 0;  // a cut inside a sequence
+        s_drop[j] = inner && a.segZ[hs + j] >= 0;
+        s_step[j] = inner && a.cut_off[j + 1] > 0 && a.cut_seq[j + 1] == a.cut_seq[j];
+        if (r0 == 0 && j > 0)
+            a.segD[hs + j] = s_drop[j];
     }
     __syncthreads();
-    auto blk = [&](float *base, int g) { return base + ((size_t)chain * a.G + (size_t)g) * kBlock; };
+    auto blk = [&](float *base, int j) { return base + (hs + (size_t)j) * kBlock; };
     u32x4_t ahi[4], alo[4];
     auto split_A = [&](const float *row) {  // row = S[r0 + m]
 #pragma unroll
@@ -1618,10 +1747,10 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
         }
     };
     float bv[2][4][8];
-    f32x4_t fv[2];  // F_g[r0 + 4kg + i][16(2w + t) + m]: the D layout of the output tiles
-    auto load_BF = [&](int g) {
-        const float *P = blk(a.segP, g) + (size_t)(8 * kg) * kD + 32 * w + m;
-        const float *F = blk(a.segF, g) + (size_t)(r0 + 4 * kg) * kD + 32 * w + m;
+    f32x4_t fv[2];  // F_j[r0 + 4kg + i][16(2w + t) + m]: the D layout of the output tiles
+    auto load_BF = [&](int j) {
+        const float *Pm = blk(a.segP, j) + (size_t)(8 * kg) * kD + 32 * w + m;
+        const float *F = blk(a.segF, j) + (size_t)(r0 + 4 * kg) * kD + 32 * w + m;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -1631,26 +1760,27 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
             for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    bv[t][kc][e] = P[(size_t)(32 * kc + e) * kD + 16 * t];
+                    bv[t][kc][e] = Pm[(size_t)(32 * kc + e) * kD + 16 * t];
         }
     };
-    // the next step >= g that is computed (G - 1 if none)
-    auto next_step = [&](int g) {
-        while (g + 1 < a.G && s_drop[g])
-            ++g;
-        return g + 1 < a.G ? g : a.G - 1;
+    // the next computed step >= j (P if none)
+    auto next_step = [&](int j) {
+        while (j < P && !(s_step[j] && !s_drop[j]))
+            ++j;
+        return j;
     };
     int loaded = next_step(1);
-    if (loaded + 1 < a.G)
+    if (loaded < P)
         load_BF(loaded);
-    bool have = false;  // ahi / alo hold S_g
-    for (int g = 1; g + 1 < a.G; ++g) {
-        if (s_drop[g]) {
-            have = false;  // S_{g+1} = F_g
+    bool have = false;  // ahi / alo hold S_j
+    for (int j = 1; j < P; ++j) {
+        if (!s_step[j] || s_drop[j]) {
+            have = false;  // no step, or S_{j+1} = F_j
             continue;
         }
-        if (!have)  // S_1, or F_{g-1} after a dropped step
-            split_A((g == 1 ? blk(a.segS, 1) : blk(a.segF, g - 1)) + (size_t)(r0 + m) * kD);
+        // S_j: from pass A at a sequence's first cut, F_{j-1} after a dropped step
+        if (!have)
+            split_A((s_step[j - 1] ? blk(a.segF, j - 1) : blk(a.segS, j)) + (size_t)(r0 + m) * kD);
         f32x4_t acc[2];
         u32x4_t ch[2][4], cl[2][4];
 #pragma unroll
@@ -1665,8 +1795,8 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
                 cl[t][kc] = u32x4_t{p0[1], p1[1], p2[1], p3[1]};
             }
         }
-        loaded = next_step(g + 1);
-        if (loaded + 1 < a.G)
+        loaded = next_step(j + 1);
+        if (loaded < P)
             load_BF(loaded);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
@@ -1677,7 +1807,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a)
                 acc[t] = mfma32(ahi[kc], cl[t][kc], acc[t]);
             }
         // rows 4kg + i, column 32w + 16t + m: to global, and through LDS to the A layout
-        float *Sn = blk(a.segS, g + 1) + (size_t)(r0 + 4 * kg) * kD + 32 * w + m;
+        float *Sn = blk(a.segS, j + 1) + (size_t)(r0 + 4 * kg) * kD + 32 * w + m;
         __syncthreads();  // the previous step's reads of s_rows are done
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -1707,8 +1837,12 @@ hipError_t launch_chunk_table(const FwdArgs &f, hipStream_t s, bool plan)
     a.P = whole_chain_groups(f.H, f.lay.n_seq, f.cu != nullptr);
     a.wg_first = reinterpret_cast<int64_t *>(f.ws + f.lay.off_wg);
     a.units = reinterpret_cast<int32_t *>(f.ws + f.lay.off_units);
-    a.whole = plan && f.lay.seg.G <= 1;
-    a.split = plan && split_plan(f.H, f.lay.n_seq, f.lay.seg.G, f.cu != nullptr);
+    a.whole = plan && f.lay.cutP <= 1;
+    a.split = plan && split_plan(f.H, f.lay.n_seq, f.lay.cutP, f.cu != nullptr);
+    a.Pc = plan ? f.lay.cutP : 0;
+    a.cut_seq = reinterpret_cast<int32_t *>(f.ws + f.lay.off_cut);
+    a.cut_off = a.cut_seq + (kPlanCUs + 1);
+    a.cut_first = a.cut_off + (kPlanCUs + 1);
     a.seq_start = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_start);
     a.seq_len = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_len);
     a.seq_off = reinterpret_cast<int64_t *>(f.ws + f.lay.off_seq_off);
@@ -1752,31 +1886,35 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     a.wg_first = reinterpret_cast<const int64_t *>(f.ws + f.lay.off_wg);
     a.units = reinterpret_cast<const int32_t *>(f.ws + f.lay.off_units);
     a.status = reinterpret_cast<int32_t *>(f.ws + f.lay.off_status);
-    a.G = f.lay.seg.G;
-    a.L = f.lay.seg.L;
-    const size_t seg_units = (size_t)chains * (size_t)a.G;
-    const size_t seg_floats = seg_units * kD * kD;
+    a.Pc = (int)f.lay.cutP;
+    a.cut_seq = reinterpret_cast<const int32_t *>(f.ws + f.lay.off_cut);
+    a.cut_off = a.cut_seq + (kPlanCUs + 1);
+    a.cut_first = a.cut_off + (kPlanCUs + 1);
+    const size_t slots = (size_t)f.H * (size_t)a.Pc;
+    const size_t seg_floats = slots * kD * kD;
     a.segS = reinterpret_cast<float *>(f.ws + f.lay.off_seg);
     a.segF = a.segS + seg_floats;
     a.segP = a.segF + seg_floats;
     a.segZ = reinterpret_cast<int32_t *>(f.ws + f.lay.off_segaux);
-    a.segD = a.segZ + seg_units;
-    a.segN = reinterpret_cast<float *>(a.segD + seg_units);
+    a.segD = a.segZ + slots;
+    a.segNS = reinterpret_cast<float *>(a.segD + slots);
+    a.segNF = a.segNS + 4 * slots;
     a.trunc = (f.flags & kL2In) && (f.flags & kSigIn);
     // separate instantiations read the activation switches (when any is off) and run column
     // halves (whole-chain launches where the chunk table may split sequences)
     const bool sw = f.flags != (kGateIn | kL2In | kSigIn);
-    const bool halves = split_plan(f.H, f.lay.n_seq, a.G, f.cu != nullptr);
+    const bool halves = split_plan(f.H, f.lay.n_seq, a.Pc, f.cu != nullptr);
     void (*fused)(FusedArgs) =
-        a.G > 1 ? (sw ? fused_kernel<true, kModeSeg> : fused_kernel<false, kModeSeg>)
+        a.Pc > 1 ? (sw ? fused_kernel<true, kModeA> : fused_kernel<false, kModeA>)
         : halves ? (sw ? fused_kernel<true, kModeHalves> : fused_kernel<false, kModeHalves>)
                  : (sw ? fused_kernel<true, kModeWhole> : fused_kernel<false, kModeWhole>);
     void (*trans)(FusedArgs) = sw ? fused_kernel<true, kModeTrans> : fused_kernel<false, kModeTrans>;
+    void (*passb)(FusedArgs) = sw ? fused_kernel<true, kModeB> : fused_kernel<false, kModeB>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fused),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
     if (e != hipSuccess)
         return e;
-    if (a.G <= 1) {
+    if (a.Pc <= 1) {
         // whole chains: H x per_head workgroups, each running a run of sequences of one
         // head back to back (about one workgroup per CU; runs from the chunk table)
         a.pass = 0;
@@ -1788,17 +1926,19 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
             return e;
         return mark(2);
     }
-    // pass A (segments 0 .. G-1 with out, end-state norms), then the transition runs of
-    // segments 1 .. G-1 (their stopping bound reads the norms)
+    // cut plan: pass A (the P runs of every head, with out, end-state norms), then the
+    // transition runs of cuts 1 .. P-1 (their stopping bound reads the norms)
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(trans), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kFusedLds)) != hipSuccess ||
+        (e = hipFuncSetAttribute(reinterpret_cast<const void *>(passb), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  kFusedLds)) != hipSuccess)
         return e;
     a.pass = 1;
-    hipLaunchKernelGGL(fused, dim3((unsigned)(chains * a.G)), dim3(512), kFusedLds, s, a);
+    hipLaunchKernelGGL(fused, dim3((unsigned)(f.H * a.Pc)), dim3(512), kFusedLds, s, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     a.pass = 3;
-    hipLaunchKernelGGL(trans, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
+    hipLaunchKernelGGL(trans, dim3((unsigned)(f.H * (a.Pc - 1))), dim3(512), kFusedLds, s, a);
     if ((e = hipGetLastError()) != hipSuccess || (e = mark(0)) != hipSuccess)
         return e;
     ScanArgs sa;
@@ -1807,13 +1947,15 @@ hipError_t launch_forward(const FwdArgs &f, hipStream_t s, hipEvent_t const *mar
     sa.segP = a.segP;
     sa.segZ = a.segZ;
     sa.segD = a.segD;
-    sa.G = a.G;
-    sa.chains = chains;
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(chains * (kD / 16))), dim3(256), 0, s, sa);
+    sa.cut_seq = a.cut_seq;
+    sa.cut_off = a.cut_off;
+    sa.Pc = a.Pc;
+    sa.H = f.H;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(f.H * (kD / 16))), dim3(256), 0, s, sa);
     if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
         return e;
     a.pass = 2;
-    hipLaunchKernelGGL(fused, dim3((unsigned)(chains * (a.G - 1))), dim3(512), kFusedLds, s, a);
+    hipLaunchKernelGGL(passb, dim3((unsigned)(f.H * (a.Pc - 1))), dim3(512), kFusedLds, s, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return mark(2);

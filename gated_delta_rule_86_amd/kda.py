@@ -101,14 +101,13 @@ def workspace_size(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -> 
 
 
 def forward_launches(B: int, T: int, H: int, N: int = 0, varlen: bool = False) -> int:
-    """Launches of the forward kernel per call: 2 (pass A and pass B) when the chains run as
-    segments, else 1.  Segmentation shows in the workspace size (three fp32 128 x 128
-    states per chain and segment beyond the chunk table, the workgroup runs and the unit
-    list)."""
+    """Launches of the forward kernel per call: 3 (pass A, the transition runs, pass B) with
+    the cut plan, else 1.  The cut plan shows in the workspace size (states per head and cut
+    beyond the chunk table, the workgroup runs, the unit list and the cut table)."""
     n = N if varlen else B
     up = lambda x: -(-x // 256) * 256
-    table = 256 + up(8 * n) + up(8 * n) + up(8 * (n + 1)) + up(8 * 257) + up(8 * n)
-    return 2 if workspace_size(B, T, H, N, varlen) > table else 1
+    table = 256 + up(8 * n) + up(8 * n) + up(8 * (n + 1)) + up(8 * 257) + up(8 * n) + up(12 * 257)
+    return 3 if workspace_size(B, T, H, N, varlen) > table else 1
 
 
 def _ptr(t) -> Optional[int]:

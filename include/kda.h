@@ -183,12 +183,13 @@ kda_status kda_fwd_recurrent_timed(const void *q, const void *k, const void *v, 
  * on `stream`:
  *   [0] before the chunk-table kernel
  *   [1] before the first forward-kernel launch
- *   [2] after it
- *   [3] after the segment scan (recorded right after [2] when there is none)
- *   [4] after the second forward-kernel launch (right after [3] when there is none)
- * Without segmentation (see kda_fwd_workspace_size) the forward kernel runs once; with it,
- * pass A, the scan and pass B.  hipEventElapsedTime between consecutive events gives each
- * launch's duration.  Returns KDA_ERR_NULL if any of the five handles is NULL.
+ *   [2] after it (with the cut plan: after pass A and the transition runs)
+ *   [3] after the cut scan (recorded right after [2] when there is none)
+ *   [4] after pass B (right after [3] when there is none)
+ * With the whole-chain plans (see kda_fwd_workspace_size) the forward kernel runs once;
+ * with the cut plan, pass A, the transition runs, the scan and pass B.  hipEventElapsedTime
+ * between consecutive events gives each stage's duration.  Returns KDA_ERR_NULL if any of
+ * the five handles is NULL.
  */
 kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void *g, const void *beta,
                          float scale, void *out, const float *A_log, const float *dt_bias,
@@ -207,8 +208,7 @@ kda_status kda_fwd_timed(const void *q, const void *k, const void *v, const void
  * (64 MiB; one copy on every GPU the library runs on, held until the process ends) serves
  * as the workspace.  The call allocates nothing.
  *   - Returns KDA_ERR_SCRATCH, before any HIP call, when kda_fwd_workspace_size for these
- *     sizes exceeds KDA_NOALLOC_SCRATCH_BYTES (e.g. very many sequences, or many long
- *     equal-length chains that run as segments).
+ *     sizes exceeds KDA_NOALLOC_SCRATCH_BYTES (e.g. very many sequences).
  *   - The scratch belongs to the device of `stream` (the current device for NULL); its
  *     address is looked up once per device.  Calls on one GPU share it: two calls that
  *     overlap in time on one GPU (different streams, or host threads) race and give
@@ -230,12 +230,15 @@ kda_status kda_fwd_noalloc(const void *q, const void *k, const void *v, const vo
  * per-sequence chunk table (start, length, chunk offset), O(N) bytes, a fixed 2.25 KiB
  * table of the first unit of each workgroup and the unit list (8 bytes per sequence) that
  * spreads the sequences over the workgroups with about equal chunk counts (a long sequence
- * of a varlen batch may run as two units of 64 value columns each).  Without cu_seqlens
- * and with few long chains (B * H small, T long), each chain is cut into G segments that
- * run in parallel (the state after a segment is affine in the state before it); that
- * adds three fp32 128 x 128 states per chain and segment, 3 * B * H * G * 64 KiB, with G
- * a deterministic function of (B, T, H).  The per-chunk operands never leave the chip.
- * Returns 0 for invalid sizes.
+ * of a varlen batch may run as two units of 64 value columns each), and a fixed 3.25 KiB
+ * cut table.  When sequences are long on average (at least 64 chunks of 16 tokens, about
+ * ceil(T / 16) / N for varlen) and H <= 128, the cut plan gives each head P = min(256 / H,
+ * C / 16) workgroups (C = the head's chunk count, ceil(T / 16) for varlen) that take equal
+ * runs of its chunks, cutting sequences where needed (the state after a piece is affine
+ * in the state before it); that adds three fp32 128 x 128 states per head and cut,
+ * 3 * H * P * 64 KiB, plus 40 bytes per head and cut.  P is a deterministic function of
+ * (B, T, H, N, has_cu_seqlens).  The per-chunk operands never leave the chip.  Returns 0
+ * for invalid sizes.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 

@@ -109,64 +109,131 @@ def bf16_round_f64(x):
     return bf16_bits_to_f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
 
 
-# ---- segment plan of few long equal-length chains (replica of the host plan) ----
+# ---- cut plan (replica of the host plan and of the chunk table's cuts) ----
 PLAN_CUS = 256
+SEG_MIN_CHUNKS = 16   # shortest run of the cut plan
+CUT_MIN_AVG = 64      # average chunks per sequence for the cut plan
+SNAP_CHUNKS = 8
+TRUNC_REL = 2.0 ** -37
 
 
-SEG_MIN_CHUNKS = 16       # shortest segment the plan makes
-TRUNC_TAU = 2.0 ** -50    # entry bound at which a segment's transition run stops
-TRUNC_M = 4096.0          # Frobenius bound on a segment's start state for dropping its share
+def cut_plan(B, T, H, N=0, varlen=False):
+    """Workgroups per head of the cut plan for these sizes, 1 for the whole-chain plans."""
+    if H < 1 or H > PLAN_CUS // 2:
+        return 1
+    nseq = N if varlen else B
+    C = -(-T // 16) if varlen else B * -(-T // 16)
+    if nseq < 1 or C < nseq * CUT_MIN_AVG:
+        return 1
+    P = min(PLAN_CUS // H, C // SEG_MIN_CHUNKS)
+    return P if P >= 2 else 1
 
 
-def segment_plan(chains, nch):
-    """(G, L): segments per chain and chunks per segment (the last one shorter) that the
-    forward pass picks for `chains` equal-length chains of `nch` chunks (G = 1: whole
-    chains).  G fills the 256 CUs with one round of pass A units (segments of every chain)
-    of at least 16 chunks, with no empty segment."""
-    cdiv = lambda a, b: -(-a // b)
-    if chains <= 0 or chains > PLAN_CUS // 2:
-        return 1, nch
-    G = min(PLAN_CUS // chains, nch // SEG_MIN_CHUNKS)
-    while G >= 2 and (G - 1) * cdiv(nch, G) >= nch:
-        G -= 1
-    if G < 2:
-        return 1, nch
-    return G, cdiv(nch, G)
+def expected_cuts(seq_off, P):
+    """The cuts (sequence, chunk offset) j = 0 .. P the chunk table computes from the chunk
+    offsets: x_j = floor(j C / P), moved to the nearest sequence boundary within
+    min(8, C // (4P)) chunks; the sequence of chunk x is the first one ending after x."""
+    seq_off = [int(x) for x in seq_off]
+    N, C = len(seq_off) - 1, seq_off[-1]
+    snap = min(SNAP_CHUNKS, C // (4 * P))
+
+    def holder(x):
+        return next((i for i in range(N) if seq_off[i + 1] > x), N)
+
+    cuts = []
+    for j in range(P + 1):
+        if j == 0:
+            i, x = 0, 0
+        elif j == P:
+            i, x = N, C
+        else:
+            x = j * C // P
+            i = holder(x)
+            if i < N:
+                dlo, dhi = x - seq_off[i], seq_off[i + 1] - x
+                if 0 < dlo <= snap:
+                    x -= dlo
+                elif dlo > 0 and dhi <= snap:
+                    x += dhi
+                i = holder(x)
+        cuts.append((i, x - seq_off[i] if i < N else 0))
+    return cuts
 
 
-def segment_bounds(G, L, nch):
-    """First chunk of each segment 0 .. G-1, and nch at the end: G + 1 entries."""
-    return [min(g * L, nch) for g in range(G)] + [nch]
+def pieces(seq_off, cuts):
+    """Pieces of the cut plan: (cut j or -1, sequence, c0, c1) for every run's pieces; a piece
+    that starts at a cut inside a sequence carries that cut's index."""
+    out = []
+    P = len(cuts) - 1
+    for w in range(P):
+        (i0, o0), (i1, o1) = cuts[w], cuts[w + 1]
+        i = i0
+        while i < i1 or (i == i1 and o1 > 0):
+            n = int(seq_off[i + 1] - seq_off[i])
+            c0 = o0 if i == i0 else 0
+            c1 = o1 if i == i1 else n
+            if not (c0 == c1 and n > 0):
+                out.append((w if c0 > 0 else -1, i, c0, c1))
+            i += 1
+    return out
 
 
 def table_bytes(N):
-    """Workspace bytes before the segment states: header, per-sequence tables, the
-    workgroup-run table and the unit list."""
+    """Workspace bytes before the cut-plan states: header, per-sequence tables, the
+    workgroup-run table, the unit list and the cut table."""
     up = lambda x: -(-x // 256) * 256
-    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N)
+    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N) + up(12 * 257)
 
 
-def segment_states(ws, B, H, G):
-    """The fp32 segment states S, F, P of a segmented call, read back from its workspace:
-    three float64 arrays [B, H, G, 128, 128] (V-major).  S_g (g >= 2) is written only where
-    the scan computed it; F_g, P_g (g >= 1) hold the runs from zero and from the identity
-    (P_g only where its run went the whole segment)."""
-    n = B * H * G * 128 * 128
-    off = table_bytes(B)
+def cut_table(ws, N, P):
+    """The cuts the chunk table wrote: list of (sequence, chunk offset), j = 0 .. P, and the
+    first-cut column (list of P + 1)."""
+    up = lambda x: -(-x // 256) * 256
+    off = 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N)
+    raw = ws[off:off + 12 * 257].cpu().numpy().view(np.int32)
+    return [(int(raw[j]), int(raw[257 + j])) for j in range(P + 1)], [int(raw[514 + j]) for j in range(P + 1)]
+
+
+def expected_firsts(cuts):
+    """First of the cuts inside cut j's sequence (j for a cut at a sequence boundary)."""
+    out = []
+    for j, (i, o) in enumerate(cuts):
+        j0 = j
+        if o > 0:
+            while j0 > 1 and cuts[j0 - 1][0] == i and cuts[j0 - 1][1] > 0:
+                j0 -= 1
+        out.append(j0)
+    return out
+
+
+def segment_states(ws, N, H, P):
+    """The fp32 cut states S, F, P of a cut-plan call, read back from its workspace: three
+    float64 arrays [H, P, 128, 128] (V-major), slot j = cut j.  S_j is written where pass A
+    (a sequence's first cut) or the scan computed it; F_j, P_j hold the piece's run from zero
+    and from the identity (P_j only where its transition run went the whole piece)."""
+    n = H * P * 128 * 128
+    off = table_bytes(N)
     raw = ws[off:off + 3 * 4 * n].cpu().numpy().view(np.float32).astype(np.float64)
-    S, F, P = (raw[i * n:(i + 1) * n].reshape(B, H, G, 128, 128) for i in range(3))
-    return S, F, P
+    S, F, Pm = (raw[i * n:(i + 1) * n].reshape(H, P, 128, 128) for i in range(3))
+    return S, F, Pm
 
 
-def segment_aux(ws, B, H, G):
-    """Per segment of a segmented call: z (chunks its transition run took before it
-    stopped, -1: the whole segment), drop (1 where the scan dropped the segment's start
-    state's share of the next one) and the squared norms of pass A's end states (per
-    consumer wavefront): int64 [B, H, G], int64 [B, H, G], float64 [B, H, G, 4]."""
-    units = B * H * G
-    off = table_bytes(B) + 3 * 4 * units * 128 * 128
-    raw = ws[off:off + units * 24].cpu().numpy()
-    z = raw[:4 * units].view(np.int32).astype(np.int64).reshape(B, H, G)
-    drop = raw[4 * units:8 * units].view(np.int32).astype(np.int64).reshape(B, H, G)
-    nrm = raw[8 * units:24 * units].view(np.float32).astype(np.float64).reshape(B, H, G, 4)
-    return z, drop, nrm
+def segment_aux(ws, N, H, P):
+    """Per head and cut of a cut-plan call: z (chunks its transition run took before it
+    stopped, -1: the whole piece), drop (1 where the scan dropped S_j's share) and the
+    squared norms of S_j and F_j (per consumer wavefront): int64 [H, P] twice, float64
+    [H, P, 4] twice."""
+    slots = H * P
+    off = table_bytes(N) + 3 * 4 * slots * 128 * 128
+    raw = ws[off:off + slots * 40].cpu().numpy()
+    z = raw[:4 * slots].view(np.int32).astype(np.int64).reshape(H, P)
+    drop = raw[4 * slots:8 * slots].view(np.int32).astype(np.int64).reshape(H, P)
+    nS = raw[8 * slots:24 * slots].view(np.float32).astype(np.float64).reshape(H, P, 4)
+    nF = raw[24 * slots:40 * slots].view(np.float32).astype(np.float64).reshape(H, P, 4)
+    return z, drop, nS, nF
+
+
+def seq_chunk_offsets(w):
+    """Chunk offset of every sequence of a workload (the chunk table's seq_off)."""
+    lens = w.lengths if w.cu_seqlens is not None else [w.T] * w.B
+    return np.concatenate([[0], np.cumsum([-(-int(n) // 16) for n in lens])]).astype(np.int64)

@@ -6,7 +6,8 @@
 * the split of a head's sequences into per-workgroup units, bit for bit against a replica
   of each plan: column halves packed longest first (few workgroups and few sequences per
   head), snake order by length (up to 512 sequences), contiguous runs of about equal chunk
-  count (brute-force assignment by chunk midpoint) beyond that.
+  count (brute-force assignment by chunk midpoint) beyond that; for long sequences the cut
+  plan's cuts (equal runs of the head's chunks, moved onto nearby sequence boundaries).
 * every out element and every final_state element is written (NaN sentinels vanish);
 * perturbing one sequence leaves every other sequence's out and final_state bit-identical;
 * two runs are bitwise identical, also with a workspace pre-filled with garbage;
@@ -17,7 +18,8 @@ import pytest
 
 from gated_delta_rule_86_amd import kda
 from gated_delta_rule_86_amd import workloads as W
-from kda_testutil import final_tensor, run_gpu, to_device, torch_dev
+from kda_testutil import (cut_plan, cut_table, expected_cuts, expected_firsts, final_tensor, run_gpu, to_device,
+                          torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -209,9 +211,11 @@ def expected_plan(seq_off, H):
                                       (40, 8, "bad"), (8, 32, "one_long"), (3, 16, "one_long"),
                                       (32, 16, "rand"), (20, 32, "empty"), (12, 32, "two_long"),
                                       (33, 32, "one_long"), (6, 64, "two_long"), (512, 32, "rand"),
-                                      (513, 32, "rand"), (257, 1, "rand"), (100, 3, "empty")])
+                                      (513, 32, "rand"), (257, 1, "rand"), (100, 3, "empty"),
+                                      (8, 32, "long"), (7, 4, "long_empty"), (3, 1, "long"), (20, 2, "long_empty")])
 def test_workgroup_runs(N, H, kind):
-    """The whole-chain split of sequences into per-workgroup units, bit for bit."""
+    """The split of sequences into per-workgroup units (whole-chain plans) or the cut table
+    (cut plan), bit for bit."""
     import torch
     rng = np.random.default_rng(N + H)
     L = rng.integers(0, 200, size=N)
@@ -223,6 +227,11 @@ def test_workgroup_runs(N, H, kind):
     elif kind == "two_long":
         L[1] = 3000
         L[N - 2] = 2200
+    elif kind.startswith("long"):
+        L = rng.integers(1, 8193, size=N)
+        if kind == "long_empty":
+            L[::3] = 0
+            L[1] = 16 * 97
     cu = np.zeros(N + 1, dtype=np.int64)
     cu[1:] = np.cumsum(L)
     T = int(cu[-1])
@@ -231,6 +240,14 @@ def test_workgroup_runs(N, H, kind):
     up = lambda x: -(-x // 256) * 256
     ws = torch.empty(kda.workspace_size(1, T, H, N, True), dtype=torch.uint8, device=torch_dev())
     seq_off, _, status = kda.chunk_table(torch.from_numpy(cu).to(torch_dev()), 1, T, H, workspace=ws)
+    Pc = cut_plan(1, T, H, N, True)
+    assert (Pc > 1) == kind.startswith("long") or kind == "one_long", (N, H, kind, Pc)
+    if Pc > 1:
+        cuts = expected_cuts(seq_off, Pc)
+        got = cut_table(ws, N, Pc)
+        assert got == (cuts, expected_firsts(cuts)), (got, cuts)
+        assert (status != 0) == (kind == "bad")
+        return
     codes, runs_ref, P = expected_plan(seq_off, H)
     off = 256 + 2 * up(8 * N) + up(8 * (N + 1))
     runs = ws[off:off + 8 * (P + 1)].cpu().numpy().view(np.int64)
@@ -249,16 +266,16 @@ def test_workgroup_runs(N, H, kind):
 
 
 def test_segmented_workspace_garbage():
-    """Segmented batch rows (pass A, scan, pass B) with a workspace pre-filled with garbage:
-    the status word reads 0, the chunk total is right, and out and final_state are
-    bit-identical to a run on a fresh workspace."""
+    """Cut-plan batch rows (pass A, transition runs, scan, pass B) with a workspace
+    pre-filled with garbage: the status word reads 0, the chunk total is right, and out and
+    final_state are bit-identical to a run on a fresh workspace."""
     import torch
-    w = W.make("segws", 2, 900, 2, seed=405)
-    assert kda.forward_launches(2, 900, 2) == 2
+    w = W.make("segws", 2, 1100, 2, seed=405)
+    assert kda.forward_launches(2, 1100, 2) == 3
     d = to_device(w)
     o1, f1, _ = run_gpu(w, d, keep_device=True)
-    ws = torch.full((kda.workspace_size(2, 900, 2),), 0xFF, dtype=torch.uint8, device=torch_dev())
+    ws = torch.full((kda.workspace_size(2, 1100, 2),), 0xFF, dtype=torch.uint8, device=torch_dev())
     o2, f2, _ = run_gpu(w, d, workspace=ws, keep_device=True)
     assert kda.device_status(ws) == 0
-    assert int(ws[8:16].cpu().numpy().view(np.int64)[0]) == 2 * ((900 + 15) // 16)
+    assert int(ws[8:16].cpu().numpy().view(np.int64)[0]) == 2 * ((1100 + 15) // 16)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)

@@ -1,14 +1,16 @@
-"""GPU parity of the segmented forward pass where the carried state matters.
+"""GPU parity of the cut plan where the carried state matters.
 
-Few long equal-length chains run as G segments: pass A (segment 0 from the true initial
-state; for the middle segments F = the segment run from S = 0 and P = the run from S = I
-with v = 0), a scan S_{g+1} = S_g P_g + F_g, and pass B (segments 1 .. G-1 from S_g, with
-out).  With a strong gate (lower_bound -5) the state is forgotten within a few tokens, so
-a wrong S_g would show in the first tokens of a segment only; these tests run where the
-state persists for hundreds of tokens (lower_bound -0.05) or for the whole sequence
-(lower_bound 0, no decay), and also compare F_g, P_g and S_g themselves with the fp64
-oracle run over the same token ranges.  Also here: long whole-chain sequences with weak
-decay, and isolation of a NaN to its own (sequence, head) chain.
+Long sequences run under the cut plan: the P workgroups of a head take equal runs of its
+chunks, cutting sequences into pieces.  Pass A runs every piece (a sequence's first piece
+from the true initial state, the others from S = 0: F_j), transition runs give each cut
+piece's P_j (the run from S = I with v = 0), a scan S_{j+1} = S_j P_j + F_j, and pass B
+reruns the cut pieces from S_j.  With a strong gate (lower_bound -5) the state is forgotten
+within a few tokens, so a wrong S_j would show in the first tokens of a piece only; these
+tests run where the state persists for hundreds of tokens (lower_bound -0.05) or for the
+whole sequence (lower_bound 0, no decay: no transition run stops early), and also compare
+F_j, P_j and S_j themselves with the fp64 oracle run over the same token ranges.  Also
+here: long whole-chain sequences with weak decay, and isolation of a NaN to its own
+(sequence, head) chain.
 
 Acceptance as everywhere: out max|err| <= 2e-2, relative L2 <= 5e-3; final_state relative
 L2 <= 1e-3 (fp32) / 1e-2 (bf16); the segment states are held to the fp32 bar.
@@ -19,8 +21,8 @@ import pytest
 import oracle
 from gated_delta_rule_86_amd import kda
 from gated_delta_rule_86_amd import workloads as W
-from kda_testutil import (check_final, check_out, rel_l2, run_gpu, run_oracle, segment_bounds,
-                          segment_plan, segment_states, to_device)
+from kda_testutil import (check_final, check_out, cut_plan, expected_cuts, rel_l2, run_gpu, run_oracle,
+                          segment_states, seq_chunk_offsets, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,11 +47,11 @@ def parity(w, what):
     (1, 4103, 1, 0.0, "fp32"),
 ])
 def test_segmented_weak_decay(B, T, H, lb, sd):
-    """Segmented runs (G >= 5) where the state persists across segments."""
-    G, L = segment_plan(B * H, -(-T // 16))
-    assert G >= 5, (B, T, H, G)
+    """Cut-plan runs (P >= 5 per head) where the state persists across pieces."""
+    P = cut_plan(B, T, H)
+    assert P >= 5, (B, T, H, P)
     w = W.make(f"segweak_B{B}_T{T}_H{H}_lb{lb}", B, T, H, seed=400 + T + H, lower_bound=lb, state_dtype=sd)
-    parity(w, f"segmented G={G} L={L} lb={lb} {sd}")
+    parity(w, f"cut plan P={P} lb={lb} {sd}")
 
 
 def _window(w, t0, t1, v_zero=False):
@@ -69,48 +71,51 @@ def _oracle_state(w, t0, t1, S0, v_zero=False):
 
 @pytest.mark.parametrize("lb", [0.0, -0.05])
 def test_segment_states_match_oracle(lb):
-    """F_g, P_g and S_g as the forward pass left them in its workspace, against the oracle
-    over the same token ranges: F_g from zero, P_g from the identity with v = 0, S_g the
-    state of the one-shot run at the segment's first token."""
+    """F_j, P_j and S_j as the forward pass left them in its workspace, against the oracle
+    over the same token ranges: F_j from zero, P_j from the identity with v = 0, S_j the
+    state of the one-shot run at cut j (one batch row: the cuts split it evenly)."""
     B, T, H = 1, 4096, 2
-    G, L = segment_plan(B * H, T // 16)
-    assert G >= 5
+    P = cut_plan(B, T, H)
+    assert P >= 5
     w = W.make(f"segstates{lb}", B, T, H, seed=420, lower_bound=lb, state_dtype="fp32")
     _, _, ws = run_gpu(w)
-    S, F, P = segment_states(ws, B, H, G)
+    S, F, Pm = segment_states(ws, B, H, P)
+    cuts = expected_cuts(seq_chunk_offsets(w), P)
     h0 = w.initial_state.astype(np.float64)
     eye = np.broadcast_to(np.eye(128), (B, H, 128, 128)).copy()
     zero = np.zeros((B, H, 128, 128))
-    bounds = [min(16 * c, T) for c in segment_bounds(G, L, T // 16)]  # first token of segment g
+    bounds = [16 * c for _, c in cuts[:P]] + [T]  # first token of the piece at cut j
     worst = {"S": 0.0, "F": 0.0, "P": 0.0}
-    for g in range(1, G - 1):
-        t0, t1 = bounds[g], bounds[g + 1]
+    for j in range(1, P):
+        t0, t1 = bounds[j], bounds[j + 1]
         rF = _oracle_state(w, t0, t1, zero)
         rP = _oracle_state(w, t0, t1, eye, v_zero=True)
-        worst["F"] = max(worst["F"], check_final(F[:, :, g], rF, "fp32", f"F_{g}"))
-        worst["P"] = max(worst["P"], check_final(P[:, :, g], rP, "fp32", f"P_{g}"))
-    for g in range(1, G):
-        rS = _oracle_state(w, 0, bounds[g], h0)
-        worst["S"] = max(worst["S"], check_final(S[:, :, g], rS, "fp32", f"S_{g}"))
+        rS = _oracle_state(w, 0, t0, h0)
+        worst["F"] = max(worst["F"], check_final(F[:, j], rF[0], "fp32", f"F_{j}"))
+        worst["P"] = max(worst["P"], check_final(Pm[:, j], rP[0], "fp32", f"P_{j}"))
+        worst["S"] = max(worst["S"], check_final(S[:, j], rS[0], "fp32", f"S_{j}"))
     # the affine hand-off the scan relies on, on the oracle's own states
-    g = G // 2
-    rSg = _oracle_state(w, 0, bounds[g], h0)
-    rF = _oracle_state(w, bounds[g], bounds[g + 1], zero)
-    rP = _oracle_state(w, bounds[g], bounds[g + 1], eye, v_zero=True)
-    rS1 = _oracle_state(w, 0, bounds[g + 1], h0)
-    assert rel_l2(np.einsum("bhvc,bhcd->bhvd", rSg, rP) + rF, rS1) < 1e-12
-    print(f"segment states G={G} L={L} lb={lb}: worst relL2 " +
+    j = P // 2
+    rSj = _oracle_state(w, 0, bounds[j], h0)
+    rF = _oracle_state(w, bounds[j], bounds[j + 1], zero)
+    rP = _oracle_state(w, bounds[j], bounds[j + 1], eye, v_zero=True)
+    rS1 = _oracle_state(w, 0, bounds[j + 1], h0)
+    assert rel_l2(np.einsum("bhvc,bhcd->bhvd", rSj, rP) + rF, rS1) < 1e-12
+    print(f"cut states P={P} lb={lb}: worst relL2 " +
           " ".join(f"{k} {v:.2e}" for k, v in worst.items()), flush=True)
 
 
 @pytest.mark.parametrize("lb,sd", [(0.0, "fp32"), (-0.05, "fp32"), (0.0, "bf16")])
-def test_whole_chain_weak_decay_long(lb, sd):
-    """Varlen batches run whole chains: sequences of 4100 and 5003 tokens (257 and 313
-    chunks) carried with no or weak decay."""
-    w = W.make(f"wholeweak{lb}{sd}", 1, 0, 2, lengths=[4100, 5003], seed=430, lower_bound=lb,
+@pytest.mark.parametrize("plan", ["whole", "cut"])
+def test_varlen_weak_decay_long(lb, sd, plan):
+    """Sequences of 4100 and 5003 tokens (257 and 313 chunks) carried with no or weak decay,
+    as whole chains (next to 200 short sequences, which keep the batch on the whole-chain
+    plans) and under the cut plan (alone)."""
+    lengths = [4100] + [10] * 100 + [5003] + [7] * 100 if plan == "whole" else [4100, 5003]
+    w = W.make(f"varlenweak{lb}{sd}{plan}", 1, 0, 2, lengths=lengths, seed=430, lower_bound=lb,
                state_dtype=sd)
-    assert kda.forward_launches(1, w.T, w.H, 2, True) == 1
-    parity(w, f"whole chains 4100/5003 lb={lb} {sd}")
+    assert kda.forward_launches(1, w.T, w.H, len(lengths), True) == (1 if plan == "whole" else 3)
+    parity(w, f"{plan} plan, sequences of 4100/5003 lb={lb} {sd}")
 
 
 def _nan_isolation(w, where, what):
@@ -155,5 +160,5 @@ def test_nan_confined_to_its_chain_whole():
 
 def test_nan_confined_to_its_chain_segmented():
     w = W.make("nan_seg", 3, 1500, 2, seed=441, state_dtype="fp32")
-    assert kda.forward_launches(3, 1500, 2) == 2
-    _nan_isolation(w, (1, 700, 1), "segmented launch")
+    assert kda.forward_launches(3, 1500, 2) == 3
+    _nan_isolation(w, (1, 700, 1), "cut-plan launch")

@@ -49,25 +49,28 @@ def ws_size(B, T, H, N=0, varlen=False):
 
 def table_bytes(N):
     up = lambda x: -(-x // 256) * 256
-    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N)
+    return 256 + up(8 * N) + up(8 * N) + up(8 * (N + 1)) + up(8 * 257) + up(8 * N) + up(12 * 257)
+
+
+def cut_extra(H, P):
+    """Workspace beyond the tables with the cut plan: three fp32 128 x 128 states per head and
+    cut, then 40 bytes of per-cut words (z, drop, two norms of 4 floats) rounded up to 256."""
+    return 0 if P == 1 else 3 * H * P * 128 * 128 * 4 + -(-H * P * 40 // 256) * 256
 
 
 def test_workspace_size_formula():
-    # many chains or short sequences: chunk table only, independent of T and H
-    for B, T, H in [(1, 64, 1), (3, 17, 5), (1, 0, 4), (2, 300, 100), (1, 1 << 20, 200)]:
+    # many heads or short sequences: tables only, independent of T and H
+    for B, T, H in [(1, 64, 1), (3, 17, 5), (1, 0, 4), (2, 300, 100), (1, 1 << 20, 200), (64, 1000, 4)]:
         assert ws_size(B, T, H) == table_bytes(B)
-    # few long equal-length chains: plus three fp32 128x128 states per chain and segment
-    # and 24 bytes of per-segment words (rounded up to 256)
-    for B, T, H in [(2, 4096, 16), (1, 1 << 20, 8), (1, 700, 1)]:
-        extra = ws_size(B, T, H) - table_bytes(B)
-        per_seg = 3 * B * H * 128 * 128 * 4
-        G = extra // per_seg
-        assert extra == G * per_seg + -(-B * H * G * 24 // 256) * 256, (B, T, H, extra)
-        assert 2 <= G <= -(-T // 16), (B, T, H, G)
-    # with cu_seqlens: chunk table only
-    for N, T in [(8, 32000), (256, 65000), (3, 5), (1, 1 << 20)]:
+    # long sequences: plus the cut plan's states, P = min(256 / H, C / 16) per head
+    for B, T, H, P in [(2, 4096, 16, 16), (1, 1 << 20, 8, 32), (1, 1100, 1, 4), (2, 2048, 128, 2)]:
+        assert ws_size(B, T, H) == table_bytes(B) + cut_extra(H, P), (B, T, H)
+    for N, T, H, P in [(8, 32000, 32, 8), (1, 1 << 20, 2, 128), (3, 3100, 4, 12)]:
+        assert ws_size(1, T, H, N, True) == table_bytes(N) + cut_extra(H, P), (N, T, H)
+    # with cu_seqlens and short sequences on average: tables only
+    for N, T in [(256, 65000), (3, 5), (40, 32000)]:
         assert ws_size(1, T, 2, N, True) == table_bytes(N)
-        assert ws_size(1, 2 * T, 5, N, True) == table_bytes(N)
+        assert ws_size(1, 2 * T // 3, 5, N, True) == table_bytes(N)
     assert ws_size(0, 10, 1) == 0            # B < 1
     assert ws_size(2, 10, 1, 3, True) == 0   # cu_seqlens needs B == 1
     assert ws_size(1, -1, 1) == 0
@@ -211,13 +214,13 @@ def test_activation_switch_errors():
 
 
 def test_forward_launches_of_reference_workloads():
-    """One forward launch for whole chains, two (pass A, pass B) for segmented ones; the
-    helper reads the workspace size, so it tracks the workspace layout."""
+    """One forward launch for the whole-chain plans, three (pass A, transition runs, pass B)
+    for the cut plan; the helper reads the workspace size, so it tracks the layout."""
     assert kda.forward_launches(1, 64, 1) == 1                 # B=1 T=64 H=1
-    assert kda.forward_launches(2, 4096, 16) == 2              # few long chains: segmented
-    assert kda.forward_launches(1, 31094, 32, 8, True) == 1    # varlen: whole chains
-    assert kda.forward_launches(1, 1 << 20, 8) == 2
-    assert kda.forward_launches(1, 66285, 32, 256, True) == 1
+    assert kda.forward_launches(2, 4096, 16) == 3              # long batch rows: cut plan
+    assert kda.forward_launches(1, 31094, 32, 8, True) == 3    # varlen, long on average: cut plan
+    assert kda.forward_launches(1, 1 << 20, 8) == 3
+    assert kda.forward_launches(1, 66285, 32, 256, True) == 1  # many short sequences: whole
     assert kda.forward_launches(256, 1, 32) == 1
 
 
@@ -241,23 +244,24 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     assert L.kda_status_string(13).decode().startswith("KDA_ERR_SCRATCH")
 
 
-def test_segment_plan_replica():
-    """The tests' replica of the segment plan (kda_testutil.segment_plan) picks the same
-    number of segments as the library, read off the workspace size."""
-    from kda_testutil import segment_plan
-    for B, T, H in [(1, 700, 1), (1, 8192, 2), (1, 6000, 2), (3, 4096, 2), (2, 5000, 3), (1, 4103, 1),
-                    (1, 4096, 2), (2, 4096, 16), (1, 1 << 20, 8), (3, 1500, 2), (1, 1 << 20, 1),
-                    (1, 100, 4), (5, 4000, 40), (1, 255, 1), (1, 256, 1), (1, 540, 1), (130, 9000, 1),
-                    (1, 9000, 128), (3, 33 * 16 + 1, 1)]:
-        nch = -(-T // 16)
-        G, L = segment_plan(B * H, nch)
-        # segment states S, F, P (fp32 128 x 128 per chain and segment), then 24 bytes of
-        # per-segment words rounded up to 256
-        units = B * H * G
-        want = 0 if G == 1 else 3 * units * 128 * 128 * 4 + -(-units * 24 // 256) * 256
-        assert ws_size(B, T, H) - table_bytes(B) == want, (B, T, H, G)
-        # one round of pass A units, segments of at least 16 chunks, none empty
-        assert G == 1 or (B * H * G <= 256 and L >= 16 and (G - 1) * L < nch <= G * L), (B, T, H, G, L)
+def test_cut_plan_replica():
+    """The tests' replica of the cut plan (kda_testutil.cut_plan) picks the same number of
+    workgroups per head as the library, read off the workspace size."""
+    from kda_testutil import cut_plan
+    for B, T, H, N, varlen in [(1, 700, 1, 0, False), (1, 8192, 2, 0, False), (3, 4096, 2, 0, False),
+                               (2, 5000, 3, 0, False), (1, 4103, 1, 0, False), (2, 4096, 16, 0, False),
+                               (1, 1 << 20, 8, 0, False), (3, 1500, 2, 0, False), (1, 1 << 20, 1, 0, False),
+                               (1, 100, 4, 0, False), (5, 4000, 40, 0, False), (1, 1023, 1, 0, False),
+                               (1, 1024, 1, 0, False), (130, 9000, 1, 0, False), (1, 9000, 128, 0, False),
+                               (1, 9000, 129, 0, False), (300, 2000, 1, 0, False),
+                               (1, 31094, 32, 8, True), (1, 66285, 32, 256, True), (1, 5000, 3, 5, True),
+                               (1, 1024, 2, 1, True), (1, 1023, 2, 1, True), (1, 100000, 64, 20, True)]:
+        P = cut_plan(B, T, H, N, varlen)
+        assert ws_size(B, T, H, N, varlen) == table_bytes(N if varlen else B) + cut_extra(H, P), \
+            (B, T, H, N, varlen, P)
+        # a run is at least 16 chunks
+        C = -(-T // 16) * (1 if varlen else B)
+        assert P == 1 or (2 <= P <= 256 // H and C // P >= 16), (B, T, H, N, P)
 
 
 def test_sequence_count_limit():
