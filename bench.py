@@ -46,6 +46,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 BYTES_PER_HT = 1282              # q, k, v, g (4 x 256) + beta (2) + out (256)
 FLOPS_PER_HT = 122880            # dense contractions per head-token (three 16x128x128 per chunk + intra-chunk)
 METRIC = "KDA fwd head-tokens/sec on 1 MI355X + % of HBM/MFMA roofline"
+# backward: q, k, v, g (4 x 256) + beta (2) + dL/dout (256) in; dq, dk, dv, dg (4 x 512, fp32) +
+# dbeta (4) out
+BWD_BYTES_PER_HT = 3334
 DECODE_WORKLOADS = (5,)          # run through the token-by-token entry point (kda_fwd_recurrent)
 
 
@@ -178,10 +181,20 @@ def backward_bench(args, w):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    # algorithmic bytes: the per-token tensors, plus per chain the initial state and
+    # dL/dfinal_state in and dL/dinitial_state out (fp32)
+    per = w.N * w.H * 128 * 128
+    h0_bytes = 0 if w.initial_state is None else per * (2 if w.state_dtype == "bf16" else 4)
+    path_bytes = w.head_tokens * BWD_BYTES_PER_HT + h0_bytes + 2 * 4 * per
+    achieved = path_bytes / dt / 1e9
     print(json.dumps({"metric": "KDA bwd head-tokens/sec on 1 MI355X (kda_bwd)", "value": w.head_tokens / dt,
                       "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": dt * 1e3, "higher_is_better": True, "dtype": "fp32",
                       "data": "synthetic", "config": dict(w.describe(), head_tokens=w.head_tokens),
+                      "roofline": {"bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
+                                   "frac": achieved / 8000.0, "traffic": None,
+                                   "kernel": "kda_bwd, all launches (bwd_chain_kernel takes nearly all)",
+                                   "algorithmic_bytes": path_bytes},
                       "workspace_bytes": ws.numel()}), flush=True)
 
 

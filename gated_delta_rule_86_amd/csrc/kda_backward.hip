@@ -20,8 +20,9 @@
 //                      reverse step per token.  Writes dq^, dk^, da, the beta gradient before
 //                      its sigmoid, dv, and dS_0.
 //   bwd_finish_kernel  per token-head: l2norm, gate and sigmoid chain rules, in place
-//   bwd_head_kernel    per head: dt_bias and A_log gradients summed over all tokens
-//                      (deterministic order)
+//   bwd_head_part_kernel, bwd_head_kernel
+//                      per head: dt_bias and A_log gradients summed over all tokens (fixed
+//                      token slices, then the slices in order: deterministic)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,6 +53,7 @@ struct BwdArgs {
     float *rk, *rq, *bt;     // [B*T][H]
     float *ckpt;             // [n_chunks][H][128][128]: state before chunk (seq_off[n] + j)
     float *buf;              // [chains][16][128][128]: S_{t-1} of the chunk being reversed
+    float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
 };
 
 // ---- prep: one wavefront per token-head, two channels per lane ----
@@ -106,28 +108,55 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 // a reduce-scatter over the wavefront's 64 channels (after it lane L holds row L >> 1),
 // the two half-sums of a row meet in LDS (part[wave][row]); returns nothing -- the caller
 // reads part after a barrier: full(row j of quarter vq) = part[2vq][j] + part[2vq+1][j].
-// One reduce-scatter step over lane distance O with N values left: lanes with bit O set
-// keep the upper N/2 (adding their partner's), the others the lower N/2.
-template <int O, int N>
-__device__ __forceinline__ void scatter_step(float *x, int lane)
+// One reduce-scatter step over lane bit O with N values left: lanes with bit O set keep the
+// upper N/2 values (adding their partner's), the others the lower N/2.  The partner is a lane
+// of the other side of bit O that holds the same values so far: for O = 32 and 16 the
+// lanes 32 (16) apart, exchanged with v_permlane32_swap / v_permlane16_swap (which swap one
+// half of one register with the other half of a second, so one swap serves a pair of values
+// and every lane's sum is the sum of the two swapped registers); for O = 8 and 4 the mirror
+// lane within 16 (8) lanes, for O = 2 and 1 the xor lane within 4, all by DPP.
+template <int N>
+__device__ __forceinline__ void swap_step32(float *x)
+{
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j + N / 2]), false,
+                                                        false);
+        x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+template <int N>
+__device__ __forceinline__ void swap_step16(float *x)
+{
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + N / 2]), false,
+                                                        false);
+        x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+// DPP controls: row_mirror (lane i <- 15 - i of its row), row_half_mirror (i <- 7 - i of its
+// half row), quad_perm [2,3,0,1] (xor 2), quad_perm [1,0,3,2] (xor 1)
+template <int O, int N, int kCtrl>
+__device__ __forceinline__ void dpp_step(float *x, int lane)
 {
     const bool up = (lane & O) != 0;
 #pragma unroll
     for (int j = 0; j < N / 2; ++j) {
         const float send = up ? x[j] : x[j + N / 2];
         const float keep = up ? x[j + N / 2] : x[j];
-        x[j] = keep + __shfl_xor(send, O);
+        x[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), kCtrl, 0xf, 0xf, false));
     }
 }
 
 __device__ __forceinline__ void row_reduce(float *x, float *part, int wave, int lane)
 {
-    scatter_step<32, 32>(x, lane);
-    scatter_step<16, 16>(x, lane);
-    scatter_step<8, 8>(x, lane);
-    scatter_step<4, 4>(x, lane);
-    scatter_step<2, 2>(x, lane);
-    x[0] += __shfl_xor(x[0], 1);
+    swap_step32<32>(x);
+    swap_step16<16>(x);
+    dpp_step<8, 8, 0x140>(x, lane);
+    dpp_step<4, 4, 0x141>(x, lane);
+    dpp_step<2, 2, 0x4e>(x, lane);
+    x[0] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[0]), 0xb1, 0xf, 0xf, false));
     if ((lane & 1) == 0)
         part[wave * 32 + (lane >> 1)] = x[0];
 }
@@ -138,6 +167,7 @@ __device__ __forceinline__ void bwd_barrier()
 }
 
 // 32 bf16 values (a row block of one token-head) widened, all lanes the same addresses
+// (here: LDS rows of the staged chunk)
 __device__ __forceinline__ void load_rows_bf16(const uint16_t *p, float *x)
 {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -178,11 +208,45 @@ __device__ __forceinline__ void fwd_token(float *S, float kc, float ac, float bt
     bwd_barrier();  // part is read by every thread before the next token overwrites it
 }
 
+// The per-token vectors of one chunk (up to 16 tokens), staged in LDS once per chunk so that
+// the token steps read them there instead of waiting on global memory twice per token:
+// k^, alpha, beta, the v row and, for the reverse pass, q^ and the dout row.
+struct Stage {
+    float kn[kCH][kD], al[kCH][kD], qn[kCH][kD];
+    uint16_t v[kCH][kD], dout[kCH][kD];
+    float bt[kCH];
+};
+
+// Thread tid loads 4 channels (4 (tid % 32) ..) of token tid / 32 of tokens [t0, t1) (its
+// token-head rows from th(t)); the caller puts a barrier before (readers of the previous
+// chunk) and after (readers of this one).
+template <typename TH>
+__device__ __forceinline__ void stage_chunk(const BwdArgs &a, Stage &st, int64_t t0, int64_t t1, bool rev,
+                                            TH th, int tid)
+{
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const int r = tid >> 5, c4 = 4 * (tid & 31);
+    if (t0 + r < t1) {
+        const size_t ti = th(t0 + r);
+        *reinterpret_cast<f32x4 *>(&st.kn[r][c4]) = *reinterpret_cast<const f32x4 *>(a.kn + ti * kD + c4);
+        *reinterpret_cast<f32x4 *>(&st.al[r][c4]) = *reinterpret_cast<const f32x4 *>(a.al + ti * kD + c4);
+        *reinterpret_cast<u32x2 *>(&st.v[r][c4]) = *reinterpret_cast<const u32x2 *>(a.v + ti * kD + c4);
+        if (rev) {
+            *reinterpret_cast<f32x4 *>(&st.qn[r][c4]) = *reinterpret_cast<const f32x4 *>(a.qn + ti * kD + c4);
+            *reinterpret_cast<u32x2 *>(&st.dout[r][c4]) = *reinterpret_cast<const u32x2 *>(a.dout + ti * kD + c4);
+        }
+        if ((tid & 31) == 0)
+            st.bt[r] = a.bt[ti];
+    }
+}
+
 __global__ __launch_bounds__(kBThreads) void bwd_chain_kernel(BwdArgs a)
 {
     __shared__ float s_part[8 * 32];           // row-reduction half sums
     __shared__ float s_r[kCH][kD];             // r_t of the chunk being reversed
     __shared__ float s_col[4][5][kD];          // per-quarter column sums: A, B, C, E, (u.r at c = 0)
+    __shared__ __attribute__((aligned(16))) Stage s_st;  // the chunk's per-token vectors
     const int64_t chain = blockIdx.x;
     const int64_t H = a.H;
     if (chain >= a.N * H)
@@ -218,10 +282,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_chain_kernel(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < kBRows; ++i)
             cp[(size_t)i * kD] = S[i];
-        const int64_t t1 = (j + 1) * kCH < len ? (j + 1) * kCH : len;
-        for (int64_t t = j * kCH; t < t1; ++t) {
-            const size_t ti = th(t);
-            fwd_token(S, a.kn[ti * kD + c], a.al[ti * kD + c], a.bt[ti], a.v + ti * kD + kBRows * vq, nullptr,
+        const int64_t t0 = j * kCH, t1 = (j + 1) * kCH < len ? (j + 1) * kCH : len;
+        bwd_barrier();  // the previous chunk's stage is read
+        stage_chunk(a, s_st, t0, t1, false, th, tid);
+        bwd_barrier();
+        for (int64_t t = t0; t < t1; ++t) {
+            const int r = (int)(t - t0);
+            fwd_token(S, s_st.kn[r][c], s_st.al[r][c], s_st.bt[r], &s_st.v[r][kBRows * vq], nullptr,
                       s_part, wave, lane, vq, c);
         }
     }
@@ -244,22 +311,26 @@ __global__ __launch_bounds__(kBThreads) void bwd_chain_kernel(BwdArgs a)
             for (int i = 0; i < kBRows; ++i)
                 S[i] = cp[(size_t)i * kD];
         }
+        bwd_barrier();  // the previous chunk's stage is read
+        stage_chunk(a, s_st, t0, t1, true, th, tid);
+        bwd_barrier();
         for (int64_t t = t0; t < t1; ++t) {
-            const size_t ti = th(t);
-            float *bp = buf + (size_t)(t - t0) * kBState + col;
+            const int r = (int)(t - t0);
+            float *bp = buf + (size_t)r * kBState + col;
 #pragma unroll
             for (int i = 0; i < kBRows; ++i)
                 bp[(size_t)i * kD] = S[i];
-            fwd_token(S, a.kn[ti * kD + c], a.al[ti * kD + c], a.bt[ti], a.v + ti * kD + kBRows * vq,
-                      s_r[t - t0], s_part, wave, lane, vq, c);
+            fwd_token(S, s_st.kn[r][c], s_st.al[r][c], s_st.bt[r], &s_st.v[r][kBRows * vq], s_r[r], s_part, wave,
+                      lane, vq, c);
         }
         // s_r complete (every thread reads back only the buffer entries it wrote itself)
         bwd_barrier();
         for (int64_t t = t1 - 1; t >= t0; --t) {
             const size_t ti = th(t);
-            const float kc = a.kn[ti * kD + c], qc = a.qn[ti * kD + c], ac = a.al[ti * kD + c];
-            const float bt = a.bt[ti];
-            const uint16_t *dorow = a.dout + ti * kD + kBRows * vq;
+            const int r = (int)(t - t0);
+            const float kc = s_st.kn[r][c], qc = s_st.qn[r][c], ac = s_st.al[r][c];
+            const float bt = s_st.bt[r];
+            const uint16_t *dorow = &s_st.dout[r][kBRows * vq];
             const float *bp = buf + (size_t)(t - t0) * kBState + col;
             float x[kBRows];
             {
@@ -383,36 +454,55 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a)
 }
 
 // ---- head reduction: ddt_bias[h][c] = sum_t dg, dA_log[h] = sum_{t,c} dg (g + dt_bias) ----
-__global__ __launch_bounds__(256) void bwd_head_kernel(BwdArgs a)
+// dt_bias and A_log gradients: per head, sums over every token of dg (d log-decay) and of
+// dg * (g + dt_bias) (the gate's pre-activation x = e^{A_log} (g + dt_bias) has dx/dA_log = x
+// and the d log-decay / dx factor is already in dg).  Two passes with a fixed partition and a
+// fixed order (deterministic): bwd_head_part_kernel sums kHeadSlices contiguous token ranges
+// per head (two interleaved halves of each range meet in LDS), bwd_head_kernel adds the
+// slices in order.
+__global__ __launch_bounds__(256) void bwd_head_part_kernel(BwdArgs a)
 {
-    __shared__ float s_a[2][kD];
-    const int h = blockIdx.x;
+    __shared__ float s_d[2][kD], s_a[2][kD];
+    const int h = blockIdx.x / kHeadSlices, slice = blockIdx.x % kHeadSlices;
     const int c = threadIdx.x & (kD - 1), half = threadIdx.x >> 7;
     const int64_t ntok = a.B * a.T;
+    const int64_t t0 = ntok * slice / kHeadSlices, t1 = ntok * (slice + 1) / kHeadSlices;
     const float dt = a.dt_bias[(size_t)h * kD + c];
     float sd = 0.f, sa = 0.f;
-    for (int64_t t = half; t < ntok; t += 2) {
+    for (int64_t t = t0 + half; t < t1; t += 2) {
         const size_t i = ((size_t)t * (size_t)a.H + (size_t)h) * kD + (size_t)c;
         const float d = a.dg[i];
         sd += d;
         sa = fmaf(d, bbf16(a.g[i]) + dt, sa);
     }
-    s_a[half][c] = sa;
-    __shared__ float s_d[2][kD];
     s_d[half][c] = sd;
+    s_a[half][c] = sa;
     __syncthreads();
     if (half == 0) {
-        if (a.ddt)
-            a.ddt[(size_t)h * kD + c] = s_d[0][c] + s_d[1][c];
-        float v = s_a[0][c] + s_a[1][c];
-        // sum over the 128 channels (two wavefronts): fixed order through LDS
-        s_a[0][c] = v;
+        float *part = a.hpart + ((size_t)h * kHeadSlices + (size_t)slice) * 2 * kD;
+        part[c] = s_d[0][c] + s_d[1][c];
+        part[kD + c] = s_a[0][c] + s_a[1][c];
     }
+}
+
+__global__ __launch_bounds__(kD) void bwd_head_kernel(BwdArgs a)
+{
+    __shared__ float s_a[kD];
+    const int h = blockIdx.x, c = threadIdx.x;
+    const float *part = a.hpart + (size_t)h * kHeadSlices * 2 * kD;
+    float sd = 0.f, sa = 0.f;
+    for (int sl = 0; sl < kHeadSlices; ++sl) {
+        sd += part[(size_t)sl * 2 * kD + c];
+        sa += part[(size_t)sl * 2 * kD + kD + c];
+    }
+    if (a.ddt)
+        a.ddt[(size_t)h * kD + c] = sd;
+    s_a[c] = sa;
     __syncthreads();
-    if (threadIdx.x == 0 && a.dA_log) {
-        float tot = 0.f;
+    if (c == 0 && a.dA_log) {
+        float tot = 0.f;  // over the 128 channels in order
         for (int j = 0; j < kD; ++j)
-            tot += s_a[0][j];
+            tot += s_a[j];
         a.dA_log[h] = tot;
     }
 }
@@ -460,6 +550,7 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.bt = reinterpret_cast<float *>(ws + f.bl.off_bt);
     a.ckpt = reinterpret_cast<float *>(ws + f.bl.off_ckpt);
     a.buf = reinterpret_cast<float *>(ws + f.bl.off_buf);
+    a.hpart = reinterpret_cast<float *>(ws + f.bl.off_hpart);
     const int64_t toks = a.B * a.T * a.H;
     const int64_t chains = a.N * a.H;
     if (toks > 0) {
@@ -481,9 +572,12 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
             return e;
     }
     if (a.flags & kBGateIn) {
-        hipLaunchKernelGGL(bwd_head_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_head_part_kernel, dim3((unsigned)(a.H * kHeadSlices)), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(bwd_head_kernel, dim3((unsigned)a.H), dim3(kD), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
     return hipSuccess;

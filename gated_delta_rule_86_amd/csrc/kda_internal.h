@@ -179,13 +179,16 @@ struct FwdArgs {
 };
 
 // Workspace of the backward pass: the chunk table (as the forward pass lays it out, up to
-// the segment states, which the backward pass does not use), then per token-head the
+// the cut-plan states, which the backward pass does not use), then per token-head the
 // activated k^, q^ and alpha (fp32 [tokens][H][128]) and 1/|k|, 1/|q|, beta (fp32
 // [tokens][H]), the state before every 16-token chunk of every chain (fp32 128 x 128 each),
-// and one 16-state buffer per chain for the chunk being reversed.
+// one 16-state buffer per chain for the chunk being reversed, and the per-head gradient
+// partial sums (fp32 [H][kHeadSlices][2][128]).
+constexpr int kHeadSlices = 64;  // token slices of the backward pass's per-head gradient sums
+
 struct BwdLayout {
     Layout tab;
-    size_t off_kn, off_qn, off_al, off_rk, off_rq, off_bt, off_ckpt, off_buf;
+    size_t off_kn, off_qn, off_al, off_rk, off_rq, off_bt, off_ckpt, off_buf, off_hpart;
     size_t total;
 };
 
@@ -210,6 +213,7 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
     L->off_bt = take(tok * sizeof(float));
     L->off_ckpt = take(chunks * (size_t)H * state);
     L->off_buf = take((size_t)L->tab.n_seq * (size_t)H * kCH * state);
+    L->off_hpart = take((size_t)H * kHeadSlices * 2 * kD * sizeof(float));
     L->total = off;
     return true;
 }

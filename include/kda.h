@@ -279,8 +279,9 @@ kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, c
 /*
  * kda_bwd_workspace_size -- bytes of workspace kda_bwd needs: the chunk table, fp32 copies of
  * the activated k^, q^ and decay (3 x 512 bytes per token-head) plus three scalars per
- * token-head, the fp32 state before every 16-token chunk of every chain (64 KiB each), and
- * a 1 MiB buffer per chain.  Returns 0 for invalid sizes.
+ * token-head, the fp32 state before every 16-token chunk of every chain (64 KiB each),
+ * a 1 MiB buffer per chain and 64 KiB per head of partial sums.  Returns 0 for invalid
+ * sizes.
  */
 size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 
