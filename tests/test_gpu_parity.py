@@ -36,7 +36,7 @@ def test_reference_workload(cfg):
 
 
 def test_long_context_workload():
-    """B=1, T=2^20, H=8 (segmented: pass A, scan, pass B), compared in full: every output
+    """B=1, T=2^20, H=8 (cut plan: pass A, transition runs, scan, pass B), compared in full: every output
     token of every head against the oracle run from the true initial state (streamed, the
     fp64 output is never stored), and the final state."""
     import os
