@@ -1,24 +1,40 @@
-// kda_backward.hip -- gradients of the KDA forward pass (reverse mode of the token
-// recurrence).  The pages describe a forward pass only (the news digest "FlashKDA Kernels
-// 2.22x Faster for Kimi Attention": no backward yet); this is the chain rule applied to the
-// recurrence the forward kernels evaluate (FlashKDA README "Kernel API" table and the
-// FLA-backend flags; article index "Delta Attention Algorithm: linear-time recurrence"):
+// kda_backward.hip -- gradients of the KDA forward pass.  The pages describe a forward pass
+// only (the news digest "FlashKDA Kernels 2.22x Faster for Kimi Attention": no backward yet);
+// this is the reverse mode of the recurrence the forward kernels evaluate (FlashKDA README
+// "Kernel API" table and the FLA-backend flags; article index "Delta Attention Algorithm:
+// linear-time recurrence"):
 //
 //   per token:  S' = S Diag(alpha);  r = v - S' k^;  S = S' + beta r k^T;  o = scale S q^
 //
-// Given dL/dout and dL/dS_final, with D = dL/dS after token t (V-major, D[v][c]):
-//   D += scale do q^^T;   dq^ = scale S^T do;   u = D k^;   dv = beta u;   dbeta = u . r
-//   dk^ = beta (D^T r - S'^T u);   da_c = sum_v S'[v][c] D[v][c] - beta k^_c (S'^T u)_c
-//   D <- (D - beta u k^^T) Diag(alpha)
-// and the activations' chain rules in a last parallel pass.  All arithmetic is fp32.
+// taken in the chunked form of the forward pass (16-token chunks; within a chunk, with
+// b the cumulative log-decay, Gamma = e^b per channel, gamma = Gamma of the last token):
+//   KG = k^ Gamma, KI = k^ / Gamma, QG = scale q^ Gamma, KD = k^ gamma / Gamma
+//   T = (I + strictly_lower(diag(beta) KG KI^T))^-1,  W = T diag(beta) KG,  U = T diag(beta) V
+//   V' = U - W S0^T,  O = QG S0^T + lower(QG KI^T) V',  S_end = S0 Diag(gamma) + V'^T KD
+// Reverse mode, with D = dL/dS_end and dO = dL/dO of the chunk:
+//   dV' = lower(QG KI^T)^T dO + KD D^T            dS0 = D Diag(gamma) + dO^T QG - dV'^T W
+// (neither needs S0: dL/dS runs backwards over the chunks on its own, as the state runs
+// forwards), and for the chunk's inputs, given S0, D, V' and dV':
+//   dKD = V' D,  dQG = dO S0 + dAqk KI,  dW = -dV' S0,  dgamma_c = sum_v S0[v][c] D[v][c]
+//   dAqk = lower(dO V'^T),  P = T^T dV',  Q = T^T dW,  dv = beta P
+//   dA = -strictly_lower(P U^T + Q W^T),  dbeta = rowdot(P, V) + rowdot(Q, KG) + rowdot(dA, KG KI^T)
+//   dKG = diag(beta) (Q + dA KI),  dKI = dA^T diag(beta) KG + dAqk^T QG
+//   dk^ = dKG Gamma + (dKI + dKD gamma) / Gamma,  dq^ = scale dQG Gamma
+//   db = dKG KG - dKI KI + dQG QG - dKD KD, plus sum_r dKD KD + dgamma gamma on the last row;
+//   d(log-decay) = reverse cumulative sum of db over the chunk.
+// Then the activations' chain rules.  All arithmetic is fp32 (products on the fp32 MFMA).
 //
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
-//   bwd_prep_kernel    per token-head: k^, q^ (fp32), alpha, and 1/|k|, 1/|q|, beta
-//   bwd_chain_kernel   per (sequence, head): a forward pass keeping the state at every
-//                      16-token chunk start; then chunk by chunk in reverse: the chunk's
-//                      per-token states S_{t-1} recomputed into a per-chain buffer, and the
-//                      reverse step per token.  Writes dq^, dk^, da, the beta gradient before
-//                      its sigmoid, dv, and dS_0.
+//   bwd_prep_kernel    per token-head: k^, q^, the log-decay a, and 1/|k|, 1/|q|, beta
+//   bwd_ops_kernel     per chunk-head: the chunk's operands for the two chains (-W, U, KD,
+//                      U~ = lower(QG KI^T)^T dO, QG, gamma, in the layouts they are read in)
+//   bwd_chain_kernel   per (sequence, head, role, half of the value rows): role 0 runs the
+//                      state forwards over the chunks, writing S0 and V' of every chunk; role 1
+//                      runs dL/dS backwards, writing D and dV' of every chunk and dL/dS_0.  The
+//                      value rows of a state are independent given the chunk operands, so two
+//                      workgroups take 64 rows each.
+//   bwd_grad_kernel    per chunk-head: the gradients of the chunk's tokens from S0, D, V', dV'
+//                      (dq^, dk^, d log-decay, dbeta before its sigmoid, dv)
 //   bwd_finish_kernel  per token-head: l2norm, gate and sigmoid chain rules, in place
 //   bwd_head_part_kernel, bwd_head_kernel
 //                      per head: dt_bias and A_log gradients summed over all tokens (fixed
@@ -32,11 +48,51 @@ namespace kda {
 namespace {
 
 constexpr int kBGateIn = 1, kBL2In = 2, kBSigIn = 4;
-constexpr int kBThreads = 512;   // chain kernel: thread (c = tid % 128, vq = tid / 128)
-constexpr int kBRows = 32;       // value rows per thread: 32 vq .. 32 vq + 31
 constexpr int64_t kBState = (int64_t)kD * kD;
+constexpr int kP = kD + 4;         // LDS row stride of the [16][128] fp32 tiles
+constexpr int kQ = kCH + 1;        // LDS row stride of the 16 x 16 tiles
+constexpr int kGradThreads = 512;  // bwd_ops_kernel, bwd_grad_kernel
+constexpr int kChainThreads = 256; // bwd_chain_kernel: 4 wavefronts of 16 value rows
+// operand block of a chunk-head (kBwdOps floats)
+constexpr int kOpNegW = 0, kOpU = 2048, kOpKDt = 4096, kOpKD = 6144, kOpUt = 8192, kOpQGt = 10240,
+              kOpNegWt = 12288, kOpGam = 14336;
+static_assert(kOpGam + kD == kBwdOps, "operand block layout");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bbf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+// four bf16 values widened (8-byte aligned)
+__device__ __forceinline__ f32x4 ld4_bf16(const uint16_t *p)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// The four steps of one 16-wide slice of a contraction: lane L holds a = A[L % 16][k0 + 4 (L / 16)
+// .. + 3] and b = B[k0 + 4 (L / 16) .. + 3][L % 16] (step j takes element j of both); the
+// accumulator is in the D layout (lane L, element i: row 4 (L / 16) + i, column L % 16).
+__device__ __forceinline__ f32x4 mm4(f32x4 a, f32x4 b, f32x4 c)
+{
+    c = mfma4(a[0], b[0], c);
+    c = mfma4(a[1], b[1], c);
+    c = mfma4(a[2], b[2], c);
+    return mfma4(a[3], b[3], c);
+}
+// acc + A B^T for A, B [16][nk] row-major in LDS (row stride kP), one wavefront
+__device__ __forceinline__ f32x4 mm_rows(const float *A, const float *B, int nk, f32x4 acc, int lane)
+{
+    const int m = lane & 15, g = lane >> 4;
+    for (int t = 0; t < nk; t += 16)
+        acc = mm4(ld4(A + m * kP + t + 4 * g), ld4(B + m * kP + t + 4 * g), acc);
+    return acc;
+}
 
 struct BwdArgs {
     const uint16_t *q, *k, *v, *g, *beta, *dout;
@@ -47,12 +103,13 @@ struct BwdArgs {
     int h0_dtype;
     const float *dht;
     float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt, *dh0;
-    int64_t B, T, H, N;
+    int64_t B, T, H, N, chunks;
     const int64_t *seq_start, *seq_len, *seq_off;
-    float *kn, *qn, *al;     // [B*T][H][128]
+    float *kn, *qn, *lg;     // [B*T][H][128]
     float *rk, *rq, *bt;     // [B*T][H]
-    float *ckpt;             // [n_chunks][H][128][128]: state before chunk (seq_off[n] + j)
-    float *buf;              // [chains][16][128][128]: S_{t-1} of the chunk being reversed
+    float *ops;              // [chunks][H][kBwdOps]
+    float *cks, *ckd;        // [chunks][H][128][128]: S before the chunk, dL/dS after it (transposed)
+    float *xf, *xb;          // [chunks][H][16][128]: V' and dL/dV'
     float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
 };
 
@@ -93,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
             lg = fminf(fmaxf(gv[e], a.lower_bound), 0.f);
         a.kn[base + c] = kv[e] * rk;
         a.qn[base + c] = qv[e] * rq;
-        a.al[base + c] = expf(lg);
+        a.lg[base + c] = lg;
     }
     if (lane == 0) {
         const float braw = bbf16(a.beta[th]);
@@ -103,300 +160,484 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
     }
 }
 
-// ---- chain kernel helpers ----
-// Sum over the 128 channels of x[i] (this thread: channel c, rows 32 vq + i), for all 32 i:
-// a reduce-scatter over the wavefront's 64 channels (after it lane L holds row L >> 1),
-// the two half-sums of a row meet in LDS (part[wave][row]); returns nothing -- the caller
-// reads part after a barrier: full(row j of quarter vq) = part[2vq][j] + part[2vq+1][j].
-// One reduce-scatter step over lane bit O with N values left: lanes with bit O set keep the
-// upper N/2 values (adding their partner's), the others the lower N/2.  The partner is a lane
-// of the other side of bit O that holds the same values so far: for O = 32 and 16 the
-// lanes 32 (16) apart, exchanged with v_permlane32_swap / v_permlane16_swap (which swap one
-// half of one register with the other half of a second, so one swap serves a pair of values
-// and every lane's sum is the sum of the two swapped registers); for O = 8 and 4 the mirror
-// lane within 16 (8) lanes, for O = 2 and 1 the xor lane within 4, all by DPP.
-template <int N>
-__device__ __forceinline__ void swap_step32(float *x)
+// ---- per-chunk operands (shared by bwd_ops_kernel and bwd_grad_kernel) ----
+// Chunk x of a head's chunk list: sequence n (the first with seq_off[n + 1] > x), chunk j of
+// it, first token t0 (row index), len tokens (1 .. 16).  False past the last chunk.
+struct ChunkLoc {
+    int64_t n, t0;
+    int len;
+};
+__device__ bool locate_chunk(const BwdArgs &a, int64_t x, ChunkLoc &c)
 {
-#pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j + N / 2]), false,
-                                                        false);
-        x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    if (x >= a.seq_off[a.N])
+        return false;
+    int64_t lo = 0, hi = a.N - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (a.seq_off[mid + 1] > x)
+            hi = mid;
+        else
+            lo = mid + 1;
     }
-}
-template <int N>
-__device__ __forceinline__ void swap_step16(float *x)
-{
-#pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + N / 2]), false,
-                                                        false);
-        x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-}
-// DPP controls: row_mirror (lane i <- 15 - i of its row), row_half_mirror (i <- 7 - i of its
-// half row), quad_perm [2,3,0,1] (xor 2), quad_perm [1,0,3,2] (xor 1)
-template <int O, int N, int kCtrl>
-__device__ __forceinline__ void dpp_step(float *x, int lane)
-{
-    const bool up = (lane & O) != 0;
-#pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-        const float send = up ? x[j] : x[j + N / 2];
-        const float keep = up ? x[j + N / 2] : x[j];
-        x[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), kCtrl, 0xf, 0xf, false));
-    }
+    const int64_t j = x - a.seq_off[lo];
+    c.n = lo;
+    c.t0 = a.seq_start[lo] + kCH * j;
+    const int64_t rem = a.seq_len[lo] - kCH * j;
+    c.len = rem < kCH ? (int)rem : kCH;
+    return true;
 }
 
-__device__ __forceinline__ void row_reduce(float *x, float *part, int wave, int lane)
-{
-    swap_step32<32>(x);
-    swap_step16<16>(x);
-    dpp_step<8, 8, 0x140>(x, lane);
-    dpp_step<4, 4, 0x141>(x, lane);
-    dpp_step<2, 2, 0x4e>(x, lane);
-    x[0] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[0]), 0xb1, 0xf, 0xf, false));
-    if ((lane & 1) == 0)
-        part[wave * 32 + (lane >> 1)] = x[0];
-}
+// Rows past the chunk's tokens are zero (k^, q^, v, dO, beta, log-decay), which leaves every
+// quantity of the real rows as it is and gamma the decay up to the last real token.
+struct PrepLds {
+    float KG[kCH][kP], KI[kCH][kP], QG[kCH][kP], KD[kCH][kP], Gm[kCH][kP], Gi[kCH][kP];
+    float W[kCH][kP], U[kCH][kP], V[kCH][kP], dO[kCH][kP];
+    float T[kCH][kQ], M[kCH][kQ], Aqk[kCH][kQ];  // T, KG KI^T, lower(QG KI^T)
+    float beta[kCH], gam[kD];
+};
 
-__device__ __forceinline__ void bwd_barrier()
+// kGradThreads threads; ends with a barrier.
+__device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &p, int tid)
 {
+    {  // the chunk's rows: thread -> token r = tid / 32, channels 4 (tid % 32) .. + 3
+        const int r = tid >> 5, c4 = 4 * (tid & 31);
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, ll = kk, vv = kk, oo = kk;
+        float bt = 0.f;
+        if (r < c.len) {
+            const size_t ti = (size_t)(c.t0 + r) * (size_t)a.H + (size_t)h;
+            kk = ld4(a.kn + ti * kD + c4);
+            qq = ld4(a.qn + ti * kD + c4);
+            ll = ld4(a.lg + ti * kD + c4);
+            vv = ld4_bf16(a.v + ti * kD + c4);
+            oo = ld4_bf16(a.dout + ti * kD + c4);
+            bt = a.bt[ti];
+        }
+        st4(&p.KG[r][c4], kk);  // k^ until the next step
+        st4(&p.QG[r][c4], qq);  // q^
+        st4(&p.Gm[r][c4], ll);  // log-decay
+        st4(&p.V[r][c4], vv);
+        st4(&p.dO[r][c4], oo);
+        if ((tid & 31) == 0)
+            p.beta[r] = bt;
+    }
+    __syncthreads();
+    if (tid < kD) {  // per channel: b = cumulative log-decay, Gamma, 1 / Gamma, the gated rows
+        const int ch = tid;
+        float b[kCH];
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < kCH; ++r) {
+            run += p.Gm[r][ch];
+            b[r] = run;
+        }
+        const float gam = expf(run);
+        p.gam[ch] = gam;
+#pragma unroll
+        for (int r = 0; r < kCH; ++r) {
+            const float G = expf(b[r]), Gi = expf(-b[r]), k = p.KG[r][ch];
+            p.Gm[r][ch] = G;
+            p.Gi[r][ch] = Gi;
+            p.KG[r][ch] = k * G;
+            p.KI[r][ch] = k * Gi;
+            p.KD[r][ch] = k * expf(run - b[r]);
+            p.QG[r][ch] = a.scale * p.QG[r][ch] * G;
+        }
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
+    if (wave == 0) {  // KG KI^T
+        const f32x4 acc = mm_rows(&p.KG[0][0], &p.KI[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            p.M[4 * g + i][m] = acc[i];
+    } else if (wave == 1) {  // lower(QG KI^T), diagonal included
+        const f32x4 acc = mm_rows(&p.QG[0][0], &p.KI[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            p.Aqk[4 * g + i][m] = m <= 4 * g + i ? acc[i] : 0.f;
+    }
+    __syncthreads();
+    if (tid < kCH) {  // T = (I + A)^-1, A = strictly_lower(diag(beta) M): lane s solves column s
+        const int s = tid;
+        float t[kCH];
+#pragma unroll
+        for (int r = 0; r < kCH; ++r) {
+            float x = r == s ? 1.f : 0.f;
+            const float br = p.beta[r];
+#pragma unroll
+            for (int q = 0; q < r; ++q)
+                x = fmaf(-br * p.M[r][q], t[q], x);
+            t[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < kCH; ++r)
+            p.T[r][s] = t[r];
+    }
+    __syncthreads();
+    {  // W = T diag(beta) KG, U = T diag(beta) V: thread -> channel tid % 128, rows 4 (tid / 128) ..
+        const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
+        float w[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kCH; ++s) {
+            const float bk = p.beta[s] * p.KG[s][ch], bv = p.beta[s] * p.V[s][ch];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[i] = fmaf(p.T[q4 + i][s], bk, w[i]);
+                u[i] = fmaf(p.T[q4 + i][s], bv, u[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p.W[q4 + i][ch] = w[i];
+            p.U[q4 + i][ch] = u[i];
+        }
+    }
     __syncthreads();
 }
 
-// 32 bf16 values (a row block of one token-head) widened, all lanes the same addresses
-// (here: LDS rows of the staged chunk)
-__device__ __forceinline__ void load_rows_bf16(const uint16_t *p, float *x)
+// ---- operands of the two chains, one workgroup per chunk-head ----
+__global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
 {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) PrepLds p;
+    const int64_t x = blockIdx.x / a.H;
+    const int h = (int)(blockIdx.x % a.H);
+    ChunkLoc c;
+    if (!locate_chunk(a, x, c))
+        return;
+    const int tid = threadIdx.x;
+    prep_chunk(a, c, h, p, tid);
+    float *o = a.ops + ((size_t)x * (size_t)a.H + (size_t)h) * kBwdOps;
+    const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
+    f32x4 kd, qg, nw;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(p + 8 * m);
+    for (int i = 0; i < 4; ++i) {
+        const int r = q4 + i;
+        float ut = 0.f;  // U~ = lower(QG KI^T)^T dO
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[8 * m + 2 * e] = __uint_as_float(w[e] << 16);
-            x[8 * m + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
+        for (int s = 0; s < kCH; ++s)
+            ut = fmaf(p.Aqk[s][r], p.dO[s][ch], ut);
+        o[kOpNegW + r * kD + ch] = -p.W[r][ch];
+        o[kOpU + r * kD + ch] = p.U[r][ch];
+        o[kOpKD + r * kD + ch] = p.KD[r][ch];
+        o[kOpUt + r * kD + ch] = ut;
+        kd[i] = p.KD[r][ch];
+        qg[i] = p.QG[r][ch];
+        nw[i] = -p.W[r][ch];
     }
+    st4(o + kOpKDt + ch * kCH + q4, kd);
+    st4(o + kOpQGt + ch * kCH + q4, qg);
+    st4(o + kOpNegWt + ch * kCH + q4, nw);
+    if (tid < kD)
+        o[kOpGam + tid] = p.gam[tid];
 }
 
-// One token forward: S <- S' + beta r k^^T with S' = S Diag(alpha), r = v - S' k^ (vrow:
-// this thread's 32 rows of v, bf16).  With r_lds set, the threads of channel 0 also store r
-// for their rows there.  Two barriers inside.
-__device__ __forceinline__ void fwd_token(float *S, float kc, float ac, float bt, const uint16_t *vrow,
-                                         float *r_lds, float *part, int wave, int lane, int vq, int c)
-{
-    float x[kBRows];
-#pragma unroll
-    for (int i = 0; i < kBRows; ++i) {
-        S[i] *= ac;
-        x[i] = S[i] * kc;
-    }
-    row_reduce(x, part, wave, lane);
-    bwd_barrier();
-    float vv[kBRows];
-    load_rows_bf16(vrow, vv);
-#pragma unroll
-    for (int i = 0; i < kBRows; ++i) {
-        const float r = vv[i] - (part[(2 * vq) * 32 + i] + part[(2 * vq + 1) * 32 + i]);
-        S[i] = fmaf(bt * r, kc, S[i]);
-        if (r_lds && c == 0)
-            r_lds[kBRows * vq + i] = r;
-    }
-    bwd_barrier();  // part is read by every thread before the next token overwrites it
-}
-
-// The per-token vectors of one chunk (up to 16 tokens), staged in LDS once per chunk so that
-// the token steps read them there instead of waiting on global memory twice per token:
-// k^, alpha, beta, the v row and, for the reverse pass, q^ and the dout row.
-struct Stage {
-    float kn[kCH][kD], al[kCH][kD], qn[kCH][kD];
-    uint16_t v[kCH][kD], dout[kCH][kD];
-    float bt[kCH];
+// ---- the two chains over the chunks of one (sequence, head) ----
+// One chunk's operands for one half (64 value rows) of a chain, staged in LDS.
+struct ChainStage {
+    float A0[kCH * kD];  // role 0: -W [r][c];  role 1: KD [r][c]
+    float A1[kD * kCH];  // role 0: KD^T [c][r]; role 1: QG^T [c][r]
+    float A2[kD * kCH];  // role 1: -W^T [c][r]
+    float U[kCH][64];    // role 0: U, role 1: U~ (the half's value columns)
+    float O[kCH][64];    // role 1: dO (the half's value columns)
+    float gam[kD];
 };
 
-// Thread tid loads 4 channels (4 (tid % 32) ..) of token tid / 32 of tokens [t0, t1) (its
-// token-head rows from th(t)); the caller puts a barrier before (readers of the previous
-// chunk) and after (readers of this one).
-template <typename TH>
-__device__ __forceinline__ void stage_chunk(const BwdArgs &a, Stage &st, int64_t t0, int64_t t1, bool rev,
-                                            TH th, int tid)
+// Global -> register copies of one chunk's stage (issued a chunk ahead), then register -> LDS.
+struct StageRegs {
+    f32x4 a0[2], a1[2], a2[2], u, o, gm;
+};
+__device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int hv, const float *op, int64_t t0, int len,
+                                           int h, StageRegs &r, int tid)
 {
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const int r = tid >> 5, c4 = 4 * (tid & 31);
-    if (t0 + r < t1) {
-        const size_t ti = th(t0 + r);
-        *reinterpret_cast<f32x4 *>(&st.kn[r][c4]) = *reinterpret_cast<const f32x4 *>(a.kn + ti * kD + c4);
-        *reinterpret_cast<f32x4 *>(&st.al[r][c4]) = *reinterpret_cast<const f32x4 *>(a.al + ti * kD + c4);
-        *reinterpret_cast<u32x2 *>(&st.v[r][c4]) = *reinterpret_cast<const u32x2 *>(a.v + ti * kD + c4);
-        if (rev) {
-            *reinterpret_cast<f32x4 *>(&st.qn[r][c4]) = *reinterpret_cast<const f32x4 *>(a.qn + ti * kD + c4);
-            *reinterpret_cast<u32x2 *>(&st.dout[r][c4]) = *reinterpret_cast<const u32x2 *>(a.dout + ti * kD + c4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int f = 4 * (tid + kChainThreads * e);
+        r.a0[e] = ld4(op + (role ? kOpKD : kOpNegW) + f);
+        r.a1[e] = ld4(op + (role ? kOpQGt : kOpKDt) + f);
+        if (role)
+            r.a2[e] = ld4(op + kOpNegWt + f);
+    }
+    const int row = tid >> 4, c4 = 4 * (tid & 15);
+    r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + 64 * hv + c4);
+    if (role) {
+        r.o = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (row < len)
+            r.o = ld4_bf16(a.dout + ((size_t)(t0 + row) * (size_t)a.H + (size_t)h) * kD + 64 * hv + c4);
+    }
+    if (tid < kD / 4)
+        r.gm = ld4(op + kOpGam + 4 * tid);
+}
+__device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainStage &st, int tid)
+{
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int f = 4 * (tid + kChainThreads * e);
+        st4(st.A0 + f, r.a0[e]);
+        st4(st.A1 + f, r.a1[e]);
+        if (role)
+            st4(st.A2 + f, r.a2[e]);
+    }
+    const int row = tid >> 4, c4 = 4 * (tid & 15);
+    st4(&st.U[row][c4], r.u);
+    if (role)
+        st4(&st.O[row][c4], r.o);
+    if (tid < kD / 4)
+        st4(st.gam + 4 * tid, r.gm);
+}
+
+// Workgroups: XCD-aware pairs (the two halves of a (chain, role) unit land on one XCD and
+// share its L2 for the operand reads).  Unit u: chain u / 2, role u % 2.  Wave w of half hv
+// owns value rows v0 .. v0 + 15, v0 = 64 hv + 16 w; its state is held transposed in the
+// D layout: tile ct (channels 16 ct ..) lane L element i = S[v0 + L % 16][16 ct + 4 (L / 16) + i].
+__global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) ChainStage s_st[2];
+    const int64_t bid = blockIdx.x;
+    const int xcd = (int)(bid & 7);
+    const int64_t slot = bid >> 3;
+    const int hv = (int)(slot & 1);
+    const int64_t unit = (slot >> 1) * 8 + xcd;
+    const int64_t H = a.H;
+    if (unit >= 2 * a.N * H)
+        return;
+    const int role = (int)(unit & 1);
+    const int64_t chain = unit >> 1, n = chain / H;
+    const int h = (int)(chain % H);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
+    const int v0 = 64 * hv + 16 * wave;
+    const int64_t start = a.seq_start[n], len = a.seq_len[n], off = a.seq_off[n];
+    const int64_t nch = (len + kCH - 1) / kCH;
+    auto slot_of = [&](int64_t j) { return (size_t)(off + j) * (size_t)H + (size_t)h; };
+    auto op_of = [&](int64_t j) { return a.ops + slot_of(j) * kBwdOps; };
+    auto tok_len = [&](int64_t j) { return (int)(len - kCH * j < kCH ? len - kCH * j : kCH); };
+    const size_t srow = (size_t)chain * kBState + (size_t)(v0 + m) * kD + 4 * g;  // + 16 ct
+    f32x4 S[8];
+    if (role == 0) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            if (a.h0_dtype == 2)
+                S[ct] = ld4(reinterpret_cast<const float *>(a.h0) + srow + 16 * ct);
+            else if (a.h0_dtype == 1)
+                S[ct] = ld4_bf16(reinterpret_cast<const uint16_t *>(a.h0) + srow + 16 * ct);
+            else
+                S[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if ((tid & 31) == 0)
-            st.bt[r] = a.bt[ti];
+    } else {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            S[ct] = a.dht ? ld4(a.dht + srow + 16 * ct) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    StageRegs rg;
+    if (nch > 0) {
+        const int64_t j0 = role ? nch - 1 : 0;
+        stage_load(a, role, hv, op_of(j0), start + kCH * j0, tok_len(j0), h, rg, tid);
+        stage_store(role, rg, s_st[0], tid);
+    }
+    __syncthreads();
+    for (int64_t it = 0; it < nch; ++it) {
+        const int64_t j = role ? nch - 1 - it : it, jn = role ? j - 1 : j + 1;
+        const bool more = it + 1 < nch;
+        if (more)
+            stage_load(a, role, hv, op_of(jn), start + kCH * jn, tok_len(jn), h, rg, tid);
+        const ChainStage &st = s_st[it & 1];
+        const size_t sl = slot_of(j);
+        // the state before the chunk (role 0) or dL/dS after it (role 1), as [channel][value row]
+        float *ck = (role ? a.ckd : a.cks) + sl * kBState + v0 + m;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ck[(size_t)(16 * ct + 4 * g + i) * kD] = S[ct][i];
+        // role 0: V' = U - W S^T;  role 1: dV' = U~ + KD D^T   (rows r = 4 g + i, column v0 + m)
+        f32x4 X;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            X[i] = st.U[4 * g + i][16 * wave + m];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            X = mm4(ld4(st.A0 + m * kD + 16 * ct + 4 * g), S[ct], X);
+        float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + v0 + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xo[(4 * g + i) * kD] = X[i];
+        if (role == 0) {
+            if (more) {  // S <- S Diag(gamma) + V'^T KD
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct)
+                    S[ct] = mm4(ld4(st.A1 + (16 * ct + m) * kCH + 4 * g), X, S[ct] * ld4(st.gam + 16 * ct + 4 * g));
+            }
+        } else {  // D <- D Diag(gamma) + dO^T QG - dV'^T W
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = st.O[4 * g + i][16 * wave + m];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                f32x4 acc = S[ct] * ld4(st.gam + 16 * ct + 4 * g);
+                acc = mm4(ld4(st.A1 + (16 * ct + m) * kCH + 4 * g), o, acc);
+                S[ct] = mm4(ld4(st.A2 + (16 * ct + m) * kCH + 4 * g), X, acc);
+            }
+        }
+        if (more)
+            stage_store(role, rg, s_st[(it + 1) & 1], tid);
+        __syncthreads();
+    }
+    if (role == 1 && a.dh0) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            st4(a.dh0 + srow + 16 * ct, S[ct]);
     }
 }
 
-__global__ __launch_bounds__(kBThreads) void bwd_chain_kernel(BwdArgs a)
-{
-    __shared__ float s_part[8 * 32];           // row-reduction half sums
-    __shared__ float s_r[kCH][kD];             // r_t of the chunk being reversed
-    __shared__ float s_col[4][5][kD];          // per-quarter column sums: A, B, C, E, (u.r at c = 0)
-    __shared__ __attribute__((aligned(16))) Stage s_st;  // the chunk's per-token vectors
-    const int64_t chain = blockIdx.x;
-    const int64_t H = a.H;
-    if (chain >= a.N * H)
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = tid & (kD - 1), vq = tid >> 7;
-    const int64_t n = chain / H;
-    const int h = (int)(chain % H);
-    const int64_t start = a.seq_start[n], len = a.seq_len[n], off = a.seq_off[n];
-    const int64_t nch = (len + kCH - 1) / kCH;
-    float *buf = a.buf + (size_t)chain * kCH * kBState;
-    auto ck = [&](int64_t j) { return a.ckpt + ((size_t)(off + j) * (size_t)H + (size_t)h) * kBState; };
-    auto th = [&](int64_t t) { return (size_t)(start + t) * (size_t)H + (size_t)h; };  // token-head index
-    const size_t col = (size_t)(kBRows * vq) * kD + (size_t)c;  // this thread's entry in a 128 x 128 block
+// ---- gradients of one chunk-head's tokens ----
+struct GradLds {
+    PrepLds p;
+    float Xf[kCH][kP], Xb[kCH][kP], dKD[kCH][kP], G1[kCH][kP], G2[kCH][kP];
+    float dA[kCH][kQ], dAqk[kCH][kQ];
+    float dgam[kD];
+};
 
-    // initial state
-    float S[kBRows];
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) GradLds L;
+    PrepLds &p = L.p;
+    const int64_t x = blockIdx.x / a.H;
+    const int h = (int)(blockIdx.x % a.H);
+    ChunkLoc c;
+    if (!locate_chunk(a, x, c))
+        return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
+    const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;
+    {  // V' and dV' of the chunk
+        const int r = tid >> 5, c4 = 4 * (tid & 31);
+        st4(&L.Xf[r][c4], ld4(a.xf + sl * (kCH * kD) + r * kD + c4));
+        st4(&L.Xb[r][c4], ld4(a.xb + sl * (kCH * kD) + r * kD + c4));
+    }
+    prep_chunk(a, c, h, p, tid);  // ends with a barrier
+    {  // dKD = V' D, G1 = dO S0, G2 = dV' S0, dgamma: wave w takes channels 16 w .. 16 w + 15
+        const int c0 = 16 * wave;
+        const float *cs = a.cks + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
+        const float *cd = a.ckd + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
+        f32x4 aKD = {0.f, 0.f, 0.f, 0.f}, aG1 = aKD, aG2 = aKD;
+        float dgp = 0.f;
+#pragma unroll 2
+        for (int t = 0; t < kD; t += 16) {
+            const f32x4 bs = ld4(cs + t), bd = ld4(cd + t);
+            aKD = mm4(ld4(&L.Xf[m][t + 4 * g]), bd, aKD);
+            aG1 = mm4(ld4(&p.dO[m][t + 4 * g]), bs, aG1);
+            aG2 = mm4(ld4(&L.Xb[m][t + 4 * g]), bs, aG2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dgp = fmaf(bs[j], bd[j], dgp);
+        }
+        dgp += __shfl_xor(dgp, 16);
+        dgp += __shfl_xor(dgp, 32);
+        if (g == 0)
+            L.dgam[c0 + m] = dgp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            L.dKD[4 * g + i][c0 + m] = aKD[i];
+            L.G1[4 * g + i][c0 + m] = aG1[i];
+            L.G2[4 * g + i][c0 + m] = aG2[i];
+        }
+    }
+    __syncthreads();
+    const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
+    const size_t tok0 = (size_t)c.t0 * (size_t)a.H + (size_t)h;  // token-head index of row 0
+    auto row_at = [&](int r) { return (tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)ch; };
     {
-        const size_t sb = (size_t)chain * kBState + col;
+        if (wave == 0) {  // dAqk = lower(dO V'^T)
+            const f32x4 acc = mm_rows(&p.dO[0][0], &L.Xf[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
 #pragma unroll
-        for (int i = 0; i < kBRows; ++i) {
-            float s0 = 0.f;
-            if (a.h0_dtype == 2)
-                s0 = reinterpret_cast<const float *>(a.h0)[sb + (size_t)i * kD];
-            else if (a.h0_dtype == 1)
-                s0 = bbf16(reinterpret_cast<const uint16_t *>(a.h0)[sb + (size_t)i * kD]);
-            S[i] = s0;
+            for (int i = 0; i < 4; ++i)
+                L.dAqk[4 * g + i][m] = m <= 4 * g + i ? acc[i] : 0.f;
         }
-    }
-    // forward pass: the state before every chunk
-    for (int64_t j = 0; j < nch; ++j) {
-        float *cp = ck(j) + col;
+        // P = T^T dV', Q = T^T dW = -T^T G2 (rows q4 .. q4 + 3, channel / value column ch)
+        float P[4] = {0.f, 0.f, 0.f, 0.f}, Q[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kBRows; ++i)
-            cp[(size_t)i * kD] = S[i];
-        const int64_t t0 = j * kCH, t1 = (j + 1) * kCH < len ? (j + 1) * kCH : len;
-        bwd_barrier();  // the previous chunk's stage is read
-        stage_chunk(a, s_st, t0, t1, false, th, tid);
-        bwd_barrier();
-        for (int64_t t = t0; t < t1; ++t) {
-            const int r = (int)(t - t0);
-            fwd_token(S, s_st.kn[r][c], s_st.al[r][c], s_st.bt[r], &s_st.v[r][kBRows * vq], nullptr,
-                      s_part, wave, lane, vq, c);
-        }
-    }
-    // reverse pass
-    float D[kBRows];
-    {
-        const size_t sb = (size_t)chain * kBState + col;
+        for (int s = 0; s < kCH; ++s) {
+            const float xb = L.Xb[s][ch], g2 = L.G2[s][ch];
 #pragma unroll
-        for (int i = 0; i < kBRows; ++i)
-            D[i] = a.dht ? a.dht[sb + (size_t)i * kD] : 0.f;
-    }
-    const float scale = a.scale;
-    for (int64_t j = nch - 1; j >= 0; --j) {
-        const int64_t t0 = j * kCH;
-        const int64_t t1 = t0 + kCH < len ? t0 + kCH : len;
-        // recompute the chunk: S_{t-1} into the buffer, r_t into LDS
-        {
-            const float *cp = ck(j) + col;
-#pragma unroll
-            for (int i = 0; i < kBRows; ++i)
-                S[i] = cp[(size_t)i * kD];
-        }
-        bwd_barrier();  // the previous chunk's stage is read
-        stage_chunk(a, s_st, t0, t1, true, th, tid);
-        bwd_barrier();
-        for (int64_t t = t0; t < t1; ++t) {
-            const int r = (int)(t - t0);
-            float *bp = buf + (size_t)r * kBState + col;
-#pragma unroll
-            for (int i = 0; i < kBRows; ++i)
-                bp[(size_t)i * kD] = S[i];
-            fwd_token(S, s_st.kn[r][c], s_st.al[r][c], s_st.bt[r], &s_st.v[r][kBRows * vq], s_r[r], s_part, wave,
-                      lane, vq, c);
-        }
-        // s_r complete (every thread reads back only the buffer entries it wrote itself)
-        bwd_barrier();
-        for (int64_t t = t1 - 1; t >= t0; --t) {
-            const size_t ti = th(t);
-            const int r = (int)(t - t0);
-            const float kc = s_st.kn[r][c], qc = s_st.qn[r][c], ac = s_st.al[r][c];
-            const float bt = s_st.bt[r];
-            const uint16_t *dorow = &s_st.dout[r][kBRows * vq];
-            const float *bp = buf + (size_t)(t - t0) * kBState + col;
-            float x[kBRows];
-            {
-                float dov[kBRows];
-                load_rows_bf16(dorow, dov);
-#pragma unroll
-                for (int i = 0; i < kBRows; ++i) {
-                    D[i] = fmaf(scale * dov[i], qc, D[i]);
-                    x[i] = D[i] * kc;
-                }
+            for (int i = 0; i < 4; ++i) {
+                P[i] = fmaf(p.T[s][q4 + i], xb, P[i]);
+                Q[i] = fmaf(-p.T[s][q4 + i], g2, Q[i]);
             }
-            row_reduce(x, s_part, wave, lane);
-            bwd_barrier();
-            // S' and do again (cached), so that neither is live across the reduction
-            float A = 0.f, Bs = 0.f, C = 0.f, E = 0.f, ur = 0.f;
-            {
-                float dov[kBRows];
-                load_rows_bf16(dorow, dov);
-#pragma unroll
-                for (int i = 0; i < kBRows; ++i) {
-                    const float u = s_part[(2 * vq) * 32 + i] + s_part[(2 * vq + 1) * 32 + i];
-                    const float rr = s_r[t - t0][kBRows * vq + i];
-                    const float sp = bp[(size_t)i * kD] * ac;
-                    const float st = fmaf(bt * rr, kc, sp);
-                    A = fmaf(st, dov[i], A);
-                    Bs = fmaf(D[i], rr, Bs);
-                    C = fmaf(sp, u, C);
-                    E = fmaf(sp, D[i], E);
-                    ur = fmaf(u, rr, ur);
-                    D[i] = (D[i] - bt * u * kc) * ac;
-                }
-            }
-            if (c < kBRows)  // dv for row 32 vq + c
-                a.dv[ti * kD + kBRows * vq + c] = bt * (s_part[(2 * vq) * 32 + c] + s_part[(2 * vq + 1) * 32 + c]);
-            s_col[vq][0][c] = A;
-            s_col[vq][1][c] = Bs;
-            s_col[vq][2][c] = C;
-            s_col[vq][3][c] = E;
-            if (c == 0)
-                s_col[vq][4][0] = ur;
-            bwd_barrier();
-            if (tid < kD) {
-                float sA = 0.f, sB = 0.f, sC = 0.f, sE = 0.f;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    sA += s_col[p][0][c];
-                    sB += s_col[p][1][c];
-                    sC += s_col[p][2][c];
-                    sE += s_col[p][3][c];
-                }
-                a.dq[ti * kD + c] = scale * sA;                 // dq^ (chain rule in finish)
-                a.dk[ti * kD + c] = bt * (sB - sC);             // dk^
-                a.dg[ti * kD + c] = sE - bt * kc * sC;          // d(log-decay) = dalpha * alpha
-                if (c == 0)
-                    a.dbeta[ti] = s_col[0][4][0] + s_col[1][4][0] + s_col[2][4][0] + s_col[3][4][0];
-            }
-            // s_part and s_col are rewritten after the next token's first barrier; the
-            // readers above are done by then
         }
-        bwd_barrier();  // s_r of this chunk is read by everyone before the next chunk rewrites it
-    }
-    if (a.dh0) {
-        float *p = a.dh0 + (size_t)chain * kBState + col;
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kBRows; ++i)
-            p[(size_t)i * kD] = D[i];
+        for (int i = 0; i < 4; ++i) {
+            const int r = q4 + i;
+            L.Xb[r][ch] = P[i];  // P replaces dV'
+            L.G2[r][ch] = Q[i];  // Q replaces G2
+            if (r < c.len)
+                a.dv[row_at(r)] = p.beta[r] * P[i];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {  // dA = -strictly_lower(P U^T + Q W^T)
+        f32x4 acc = mm_rows(&L.Xb[0][0], &p.U[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+        acc = mm_rows(&L.G2[0][0], &p.W[0][0], kD, acc, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            L.dA[4 * g + i][m] = m < 4 * g + i ? -acc[i] : 0.f;
+    }
+    __syncthreads();
+    {  // dbeta_r = P_r . V_r + Q_r . KG_r + dA_r . M_r: 32 lanes per row
+        const int r = tid >> 5, part = tid & 31;
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int cc = 4 * part + e;
+            s = fmaf(L.Xb[r][cc], p.V[r][cc], s);
+            s = fmaf(L.G2[r][cc], p.KG[r][cc], s);
+        }
+        if (part < kCH)
+            s = fmaf(L.dA[r][part], p.M[r][part], s);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1)
+            s += __shfl_xor(s, o);
+        if (part == 0 && r < c.len)
+            a.dbeta[tok0 + (size_t)r * (size_t)a.H] = s;
+    }
+    {  // dKG, dKI, dQG; dk^, dq^; db into Xf (free now)
+        float db[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = q4 + i;
+            float sKG = L.G2[r][ch], sQG = L.G1[r][ch], sKI = 0.f;
+#pragma unroll
+            for (int s = 0; s < kCH; ++s) {
+                const float ki = p.KI[s][ch];
+                sKG = fmaf(L.dA[r][s], ki, sKG);
+                sQG = fmaf(L.dAqk[r][s], ki, sQG);
+                sKI = fmaf(L.dA[s][r] * p.beta[s], p.KG[s][ch], sKI);
+                sKI = fmaf(L.dAqk[s][r], p.QG[s][ch], sKI);
+            }
+            const float dKG = p.beta[r] * sKG, dKD = L.dKD[r][ch];
+            const float G = p.Gm[r][ch], Gi = p.Gi[r][ch];
+            db[i] = dKG * p.KG[r][ch] - sKI * p.KI[r][ch] + sQG * p.QG[r][ch] - dKD * p.KD[r][ch];
+            if (r < c.len) {
+                a.dk[row_at(r)] = dKG * G + (sKI + dKD * p.gam[ch]) * Gi;
+                a.dq[row_at(r)] = a.scale * sQG * G;
+            }
+        }
+        __syncthreads();  // every reader of Xf (dAqk) is long done; the barrier orders the reuse
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            L.Xf[q4 + i][ch] = db[i];
+    }
+    __syncthreads();
+    if (tid < kD) {  // the last row takes the decay of the whole chunk; d log-decay by reverse sums
+        float e = L.dgam[ch] * p.gam[ch];
+#pragma unroll
+        for (int r = 0; r < kCH; ++r)
+            e = fmaf(L.dKD[r][ch], p.KD[r][ch], e);
+        float acc = e;
+        for (int r = kCH - 1; r >= 0; --r) {
+            acc += L.Xf[r][ch];
+            if (r < c.len)
+                a.dg[row_at(r)] = acc;
+        }
     }
 }
 
@@ -538,46 +779,56 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.T = f.fwd.T;
     a.H = f.fwd.H;
     a.N = f.fwd.lay.n_seq;
+    a.chunks = f.bl.chunks;
     unsigned char *ws = f.fwd.ws;
     a.seq_start = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_len);
     a.seq_off = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_off);
     a.kn = reinterpret_cast<float *>(ws + f.bl.off_kn);
     a.qn = reinterpret_cast<float *>(ws + f.bl.off_qn);
-    a.al = reinterpret_cast<float *>(ws + f.bl.off_al);
+    a.lg = reinterpret_cast<float *>(ws + f.bl.off_lg);
     a.rk = reinterpret_cast<float *>(ws + f.bl.off_rk);
     a.rq = reinterpret_cast<float *>(ws + f.bl.off_rq);
     a.bt = reinterpret_cast<float *>(ws + f.bl.off_bt);
-    a.ckpt = reinterpret_cast<float *>(ws + f.bl.off_ckpt);
-    a.buf = reinterpret_cast<float *>(ws + f.bl.off_buf);
+    a.ops = reinterpret_cast<float *>(ws + f.bl.off_ops);
+    a.cks = reinterpret_cast<float *>(ws + f.bl.off_cks);
+    a.ckd = reinterpret_cast<float *>(ws + f.bl.off_ckd);
+    a.xf = reinterpret_cast<float *>(ws + f.bl.off_xf);
+    a.xb = reinterpret_cast<float *>(ws + f.bl.off_xb);
     a.hpart = reinterpret_cast<float *>(ws + f.bl.off_hpart);
     const int64_t toks = a.B * a.T * a.H;
-    const int64_t chains = a.N * a.H;
+    const int64_t units = 2 * a.N * a.H;          // (chain, role)
+    const int64_t slots = a.chunks * a.H;         // chunk-heads (a bound)
+    auto check = [] { return hipGetLastError(); };
+    hipError_t e;
     if (toks > 0) {
         hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
+        if ((e = check()) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(bwd_ops_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
+        if ((e = check()) != hipSuccess)
             return e;
     }
-    if (chains > 0) {
-        hipLaunchKernelGGL(bwd_chain_kernel, dim3((unsigned)chains), dim3(kBThreads), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
+    if (units > 0) {
+        // two workgroups (halves) per unit, units in groups of 8 (one per XCD)
+        hipLaunchKernelGGL(bwd_chain_kernel, dim3((unsigned)(cdiv(units, 8) * 16)), dim3(kChainThreads), 0, s, a);
+        if ((e = check()) != hipSuccess)
             return e;
     }
     if (toks > 0) {
+        hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
         hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
+        if ((e = check()) != hipSuccess)
             return e;
     }
     if (a.flags & kBGateIn) {
         hipLaunchKernelGGL(bwd_head_part_kernel, dim3((unsigned)(a.H * kHeadSlices)), dim3(256), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
+        if ((e = check()) != hipSuccess)
             return e;
         hipLaunchKernelGGL(bwd_head_kernel, dim3((unsigned)a.H), dim3(kD), 0, s, a);
-        if ((e = hipGetLastError()) != hipSuccess)
+        if ((e = check()) != hipSuccess)
             return e;
     }
     return hipSuccess;

@@ -180,15 +180,20 @@ struct FwdArgs {
 
 // Workspace of the backward pass: the chunk table (as the forward pass lays it out, up to
 // the cut-plan states, which the backward pass does not use), then per token-head the
-// activated k^, q^ and alpha (fp32 [tokens][H][128]) and 1/|k|, 1/|q|, beta (fp32
-// [tokens][H]), the state before every 16-token chunk of every chain (fp32 128 x 128 each),
-// one 16-state buffer per chain for the chunk being reversed, and the per-head gradient
-// partial sums (fp32 [H][kHeadSlices][2][128]).
+// activated k^, q^ and log-decay a (fp32 [tokens][H][128]) and 1/|k|, 1/|q|, beta (fp32
+// [tokens][H]); per chunk-head (chunk x of the head's chunk list, slot x H + h) the chain
+// kernels' operand block (kBwdOps fp32), the state before the chunk and dL/dS after it (fp32
+// 128 x 128 each, stored transposed: [key channel][value row]), the chunk's corrected values
+// V' and their gradient (fp32 [16][128] each); and the per-head gradient partial sums (fp32
+// [H][kHeadSlices][2][128]).
 constexpr int kHeadSlices = 64;  // token slices of the backward pass's per-head gradient sums
+// operand block of one chunk-head: -W, U, KD^T, KD, U~, QG^T, -W^T (2048 fp32 each), gamma (128)
+constexpr int kBwdOps = 7 * kCH * kD + kD;
 
 struct BwdLayout {
     Layout tab;
-    size_t off_kn, off_qn, off_al, off_rk, off_rq, off_bt, off_ckpt, off_buf, off_hpart;
+    int64_t chunks;  // bound on the chunk count of a head (the slots per head)
+    size_t off_kn, off_qn, off_lg, off_rk, off_rq, off_bt, off_ops, off_cks, off_ckd, off_xf, off_xb, off_hpart;
     size_t total;
 };
 
@@ -198,7 +203,8 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
         return false;
     const size_t tok = (size_t)B * (size_t)T * (size_t)H;
     const size_t state = (size_t)kD * kD * sizeof(float);
-    const size_t chunks = varlen ? (size_t)cdiv(T, kCH) + (size_t)L->tab.n_seq : (size_t)B * (size_t)cdiv(T, kCH);
+    L->chunks = varlen ? cdiv(T, kCH) + L->tab.n_seq : B * cdiv(T, kCH);
+    const size_t ch = (size_t)L->chunks * (size_t)H;  // chunk-head slots
     size_t off = L->tab.off_seg;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -207,12 +213,15 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
     };
     L->off_kn = take(tok * kD * sizeof(float));
     L->off_qn = take(tok * kD * sizeof(float));
-    L->off_al = take(tok * kD * sizeof(float));
+    L->off_lg = take(tok * kD * sizeof(float));
     L->off_rk = take(tok * sizeof(float));
     L->off_rq = take(tok * sizeof(float));
     L->off_bt = take(tok * sizeof(float));
-    L->off_ckpt = take(chunks * (size_t)H * state);
-    L->off_buf = take((size_t)L->tab.n_seq * (size_t)H * kCH * state);
+    L->off_ops = take(ch * kBwdOps * sizeof(float));
+    L->off_cks = take(ch * state);
+    L->off_ckd = take(ch * state);
+    L->off_xf = take(ch * kCH * kD * sizeof(float));
+    L->off_xb = take(ch * kCH * kD * sizeof(float));
     L->off_hpart = take((size_t)H * kHeadSlices * 2 * kD * sizeof(float));
     L->total = off;
     return true;

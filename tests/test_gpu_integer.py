@@ -77,6 +77,32 @@ def test_invalid_cu_seqlens_leaves_out_and_keeps_state():
     assert np.array_equal(f, w.initial_state.astype(np.float64))
 
 
+@pytest.mark.parametrize("bad", ["decreasing", "first", "last"])
+def test_invalid_cu_seqlens_under_cut_plan(bad):
+    """Long sequences (the cut plan's launch of three passes and the scan): invalid content
+    writes no out, final_state equals initial_state and the cut table holds only empty runs."""
+    import torch
+    lengths = [0, 3000, 17, 0, 5000, 1, 2048, 900]
+    w = W.make(f"bad_cu_cut_{bad}", 1, 0, 4, lengths=lengths, seed=401, state_dtype="fp32")
+    P = cut_plan(1, w.T, w.H, len(lengths), True)
+    assert P > 1 and kda.forward_launches(1, w.T, w.H, len(lengths), True) == 3
+    cu = w.cu_seqlens.copy()
+    if bad == "decreasing":
+        cu[3] = cu[2] - 1
+    elif bad == "first":
+        cu[0] = 1
+    else:
+        cu[-1] = w.T - 1
+    d = to_device(w)
+    d["cu"] = torch.tensor(cu, dtype=torch.int64, device=torch_dev())
+    o, f, ws = run_gpu(w, d, out_fill=7.0, final_fill=-3.0)
+    assert kda.device_status(ws) == {"decreasing": 2, "first": 1, "last": 4}[bad]
+    assert np.all(o == 7.0)
+    assert np.array_equal(f, w.initial_state.astype(np.float64))
+    cuts, firsts = cut_table(ws, len(lengths), P)
+    assert cuts == [(0, 0)] + [(len(lengths), 0)] * P and firsts == list(range(P + 1))
+
+
 def test_every_output_is_written():
     import torch
     w = W.make("cover", 1, 0, 3, lengths=[1, 16, 17, 0, 40, 5], seed=401, state_dtype="bf16")
