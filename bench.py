@@ -193,7 +193,7 @@ def backward_bench(args, w):
                       "data": "synthetic", "config": dict(w.describe(), head_tokens=w.head_tokens),
                       "roofline": {"bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
                                    "frac": achieved / 8000.0, "traffic": None,
-                                   "kernel": "kda_bwd, all launches (bwd_chain_kernel takes nearly all)",
+                                   "kernel": "kda_bwd, all launches (ops, chain, state-product and gradient kernels)",
                                    "algorithmic_bytes": path_bytes},
                       "workspace_bytes": ws.numel()}), flush=True)
 

@@ -25,17 +25,18 @@
 // Then the activations' chain rules.  All arithmetic is fp32 (products on the fp32 MFMA).
 //
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
-//   bwd_prep_kernel    per token-head: k^, q^, the log-decay a, and 1/|k|, 1/|q|, beta
-//   bwd_ops_kernel     per chunk-head: the chunk's operands for the two chains (-W, U, KD,
+//   bwd_ops_kernel     per chunk-head: the chunk's activated rows (l2norm, gate, sigmoid, as
+//                      in the forward pass) and its operands for the two chains (-W, U, KD,
 //                      U~ = lower(QG KI^T)^T dO, QG, gamma, in the layouts they are read in)
 //   bwd_chain_kernel   per (sequence, head, role, half of the value rows): role 0 runs the
 //                      state forwards over the chunks, writing S0 and V' of every chunk; role 1
 //                      runs dL/dS backwards, writing D and dV' of every chunk and dL/dS_0.  The
 //                      value rows of a state are independent given the chunk operands, so two
 //                      workgroups take 64 rows each.
-//   bwd_grad_kernel    per chunk-head: the gradients of the chunk's tokens from S0, D, V', dV'
-//                      (dq^, dk^, d log-decay, dbeta before its sigmoid, dv)
-//   bwd_finish_kernel  per token-head: l2norm, gate and sigmoid chain rules, in place
+//   bwd_sgrad_kernel   per chunk-head: the products with the chunk's states (dKD, dO S0,
+//                      dV' S0, dgamma, and dAqk)
+//   bwd_grad_kernel    per chunk-head: the gradients of the chunk's tokens (dq^, dk^, d log-
+//                      decay, dbeta, dv), then the l2norm, gate and sigmoid chain rules
 //   bwd_head_part_kernel, bwd_head_kernel
 //                      per head: dt_bias and A_log gradients summed over all tokens (fixed
 //                      token slices, then the slices in order: deterministic)
@@ -105,60 +106,11 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt, *dh0;
     int64_t B, T, H, N, chunks;
     const int64_t *seq_start, *seq_len, *seq_off;
-    float *kn, *qn, *lg;     // [B*T][H][128]
-    float *rk, *rq, *bt;     // [B*T][H]
     float *ops;              // [chunks][H][kBwdOps]
     float *cks, *ckd;        // [chunks][H][128][128]: S before the chunk, dL/dS after it (transposed)
     float *xf, *xb;          // [chunks][H][16][128]: V' and dL/dV'
     float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
 };
-
-// ---- prep: one wavefront per token-head, two channels per lane ----
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
-{
-    const int lane = threadIdx.x & 63;
-    const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // token * H + head
-    if (th >= a.B * a.T * a.H)
-        return;
-    const int h = (int)(th % a.H);
-    const size_t base = (size_t)th * kD;
-    float qv[2], kv[2], gv[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int c = lane + 64 * e;
-        qv[e] = bbf16(a.q[base + c]);
-        kv[e] = bbf16(a.k[base + c]);
-        gv[e] = bbf16(a.g[base + c]);
-    }
-    float qq = qv[0] * qv[0] + qv[1] * qv[1], kk = kv[0] * kv[0] + kv[1] * kv[1];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        qq += __shfl_xor(qq, o);
-        kk += __shfl_xor(kk, o);
-    }
-    const bool l2_in = (a.flags & kBL2In) != 0;
-    const float rq = l2_in ? 1.0f / sqrtf(qq + 1e-6f) : 1.0f;
-    const float rk = l2_in ? 1.0f / sqrtf(kk + 1e-6f) : 1.0f;
-    const float eA = (a.flags & kBGateIn) ? expf(a.A_log[h]) : 0.f;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int c = lane + 64 * e;
-        float lg;
-        if (a.flags & kBGateIn)
-            lg = a.lower_bound / (1.0f + expf(-eA * (gv[e] + a.dt_bias[(size_t)h * kD + c])));
-        else
-            lg = fminf(fmaxf(gv[e], a.lower_bound), 0.f);
-        a.kn[base + c] = kv[e] * rk;
-        a.qn[base + c] = qv[e] * rq;
-        a.lg[base + c] = lg;
-    }
-    if (lane == 0) {
-        const float braw = bbf16(a.beta[th]);
-        a.rk[th] = rk;
-        a.rq[th] = rq;
-        a.bt[th] = (a.flags & kBSigIn) ? 1.0f / (1.0f + expf(-braw)) : braw;
-    }
-}
 
 // ---- per-chunk operands (shared by bwd_ops_kernel and bwd_grad_kernel) ----
 // Chunk x of a head's chunk list: sequence n (the first with seq_off[n + 1] > x), chunk j of
@@ -188,60 +140,83 @@ __device__ bool locate_chunk(const BwdArgs &a, int64_t x, ChunkLoc &c)
 }
 
 // Rows past the chunk's tokens are zero (k^, q^, v, dO, beta, log-decay), which leaves every
-// quantity of the real rows as it is and gamma the decay up to the last real token.
+// quantity of the real rows as it is and gamma the decay up to the last real token.  KD is
+// not kept: KD = KI gamma.
 struct PrepLds {
-    float KG[kCH][kP], KI[kCH][kP], QG[kCH][kP], KD[kCH][kP], Gm[kCH][kP], Gi[kCH][kP];
-    float W[kCH][kP], U[kCH][kP], V[kCH][kP], dO[kCH][kP];
+    float KG[kCH][kP], KI[kCH][kP], QG[kCH][kP], B[kCH][kP];  // B: cumulative log-decay b
+    float W[kCH][kP], U[kCH][kP];
     float T[kCH][kQ], M[kCH][kQ], Aqk[kCH][kQ];  // T, KG KI^T, lower(QG KI^T)
-    float beta[kCH], gam[kD];
+    float beta[kCH], rq[kCH], rk[kCH], gam[kD];     // beta; 1/|q|, 1/|k| (1 without the l2norm)
 };
 
 // kGradThreads threads; ends with a barrier.
 __device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &p, int tid)
 {
-    {  // the chunk's rows: thread -> token r = tid / 32, channels 4 (tid % 32) .. + 3
+    {  // the chunk's rows, activated: thread -> token r = tid / 32, channels c4 = 4 (tid % 32) .. + 3
         const int r = tid >> 5, c4 = 4 * (tid & 31);
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, ll = kk, vv = kk, oo = kk;
-        float bt = 0.f;
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, gg = kk, vv = kk;
+        float braw = 0.f;
         if (r < c.len) {
             const size_t ti = (size_t)(c.t0 + r) * (size_t)a.H + (size_t)h;
-            kk = ld4(a.kn + ti * kD + c4);
-            qq = ld4(a.qn + ti * kD + c4);
-            ll = ld4(a.lg + ti * kD + c4);
+            kk = ld4_bf16(a.k + ti * kD + c4);
+            qq = ld4_bf16(a.q + ti * kD + c4);
+            gg = ld4_bf16(a.g + ti * kD + c4);
             vv = ld4_bf16(a.v + ti * kD + c4);
-            oo = ld4_bf16(a.dout + ti * kD + c4);
-            bt = a.bt[ti];
+            braw = bbf16(a.beta[ti]);
         }
-        st4(&p.KG[r][c4], kk);  // k^ until the next step
-        st4(&p.QG[r][c4], qq);  // q^
-        st4(&p.Gm[r][c4], ll);  // log-decay
-        st4(&p.V[r][c4], vv);
-        st4(&p.dO[r][c4], oo);
-        if ((tid & 31) == 0)
-            p.beta[r] = bt;
+        // l2norm over the 128 channels of the row (32 lanes), eps 1e-6
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sk = fmaf(kk[e], kk[e], sk);
+            sq = fmaf(qq[e], qq[e], sq);
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) {
+            sk += __shfl_xor(sk, o);
+            sq += __shfl_xor(sq, o);
+        }
+        const bool l2_in = (a.flags & kBL2In) != 0;
+        const float rk = l2_in ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f, rq = l2_in ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+        // log-decay: lower_bound * sigmoid(e^A_log (g + dt_bias)), or g clamped to [lower_bound, 0]
+        f32x4 ll = {0.f, 0.f, 0.f, 0.f};
+        if (r < c.len) {
+            if (a.flags & kBGateIn) {
+                const float eA = expf(a.A_log[h]);
+                const f32x4 db = ld4(a.dt_bias + (size_t)h * kD + c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ll[e] = a.lower_bound / (1.0f + expf(-eA * (gg[e] + db[e])));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ll[e] = fminf(fmaxf(gg[e], a.lower_bound), 0.f);
+            }
+        }
+        st4(&p.KG[r][c4], kk * rk);  // k^ until the next step
+        st4(&p.QG[r][c4], qq * rq);  // q^
+        st4(&p.B[r][c4], ll);        // log-decay
+        st4(&p.U[r][c4], vv);        // v until U replaces it
+        if ((tid & 31) == 0) {
+            p.beta[r] = r < c.len ? ((a.flags & kBSigIn) ? 1.0f / (1.0f + expf(-braw)) : braw) : 0.f;
+            p.rq[r] = rq;
+            p.rk[r] = rk;
+        }
     }
     __syncthreads();
-    if (tid < kD) {  // per channel: b = cumulative log-decay, Gamma, 1 / Gamma, the gated rows
+    if (tid < kD) {  // per channel: b = cumulative log-decay; the gated rows
         const int ch = tid;
-        float b[kCH];
         float run = 0.f;
 #pragma unroll
         for (int r = 0; r < kCH; ++r) {
-            run += p.Gm[r][ch];
-            b[r] = run;
-        }
-        const float gam = expf(run);
-        p.gam[ch] = gam;
-#pragma unroll
-        for (int r = 0; r < kCH; ++r) {
-            const float G = expf(b[r]), Gi = expf(-b[r]), k = p.KG[r][ch];
-            p.Gm[r][ch] = G;
-            p.Gi[r][ch] = Gi;
+            run += p.B[r][ch];
+            p.B[r][ch] = run;
+            const float G = expf(run), Gi = expf(-run), k = p.KG[r][ch];
             p.KG[r][ch] = k * G;
             p.KI[r][ch] = k * Gi;
-            p.KD[r][ch] = k * expf(run - b[r]);
             p.QG[r][ch] = a.scale * p.QG[r][ch] * G;
         }
+        p.gam[ch] = expf(run);
     }
     __syncthreads();
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
@@ -279,13 +254,14 @@ __device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &
         float w[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kCH; ++s) {
-            const float bk = p.beta[s] * p.KG[s][ch], bv = p.beta[s] * p.V[s][ch];
+            const float bk = p.beta[s] * p.KG[s][ch], bv = p.beta[s] * p.U[s][ch];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 w[i] = fmaf(p.T[q4 + i][s], bk, w[i]);
                 u[i] = fmaf(p.T[q4 + i][s], bv, u[i]);
             }
         }
+        __syncthreads();  // every column of v is read before U replaces it
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             p.W[q4 + i][ch] = w[i];
@@ -308,6 +284,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
     prep_chunk(a, c, h, p, tid);
     float *o = a.ops + ((size_t)x * (size_t)a.H + (size_t)h) * kBwdOps;
     const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
+    float dO[kCH];  // column ch of dL/dout
+#pragma unroll
+    for (int s = 0; s < kCH; ++s)
+        dO[s] = s < c.len ? bbf16(a.dout[((size_t)(c.t0 + s) * (size_t)a.H + (size_t)h) * kD + ch]) : 0.f;
+    const float gam = p.gam[ch];
     f32x4 kd, qg, nw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -315,14 +296,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
         float ut = 0.f;  // U~ = lower(QG KI^T)^T dO
 #pragma unroll
         for (int s = 0; s < kCH; ++s)
-            ut = fmaf(p.Aqk[s][r], p.dO[s][ch], ut);
-        o[kOpNegW + r * kD + ch] = -p.W[r][ch];
-        o[kOpU + r * kD + ch] = p.U[r][ch];
-        o[kOpKD + r * kD + ch] = p.KD[r][ch];
-        o[kOpUt + r * kD + ch] = ut;
-        kd[i] = p.KD[r][ch];
+            ut = fmaf(p.Aqk[s][r], dO[s], ut);
+        kd[i] = p.KI[r][ch] * gam;
         qg[i] = p.QG[r][ch];
         nw[i] = -p.W[r][ch];
+        o[kOpNegW + r * kD + ch] = nw[i];
+        o[kOpU + r * kD + ch] = p.U[r][ch];
+        o[kOpKD + r * kD + ch] = kd[i];
+        o[kOpUt + r * kD + ch] = ut;
     }
     st4(o + kOpKDt + ch * kCH + q4, kd);
     st4(o + kOpQGt + ch * kCH + q4, qg);
@@ -343,8 +324,11 @@ struct ChainStage {
 };
 
 // Global -> register copies of one chunk's stage (issued a chunk ahead), then register -> LDS.
+// Every load is unconditional (a clamped row or column where the data is not needed) and
+// keeps its raw bits, so that nothing waits for it before the copy into LDS.
 struct StageRegs {
-    f32x4 a0[2], a1[2], a2[2], u, o, gm;
+    f32x4 a0[2], a1[2], a2[2], u, gm;
+    uint32_t o[2];  // two bf16 pairs of dO
 };
 __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int hv, const float *op, int64_t t0, int len,
                                            int h, StageRegs &r, int tid)
@@ -360,14 +344,16 @@ __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int hv, c
     const int row = tid >> 4, c4 = 4 * (tid & 15);
     r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + 64 * hv + c4);
     if (role) {
-        r.o = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (row < len)
-            r.o = ld4_bf16(a.dout + ((size_t)(t0 + row) * (size_t)a.H + (size_t)h) * kD + 64 * hv + c4);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const int rr = row < len ? row : 0;
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(a.dout + ((size_t)(t0 + rr) * (size_t)a.H + (size_t)h) * kD +
+                                                         64 * hv + c4);
+        r.o[0] = w[0];
+        r.o[1] = w[1];
     }
-    if (tid < kD / 4)
-        r.gm = ld4(op + kOpGam + 4 * tid);
+    r.gm = ld4(op + kOpGam + 4 * (tid & (kD / 4 - 1)));
 }
-__device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainStage &st, int tid)
+__device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainStage &st, int len, int tid)
 {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -379,11 +365,19 @@ __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainS
     }
     const int row = tid >> 4, c4 = 4 * (tid & 15);
     st4(&st.U[row][c4], r.u);
-    if (role)
-        st4(&st.O[row][c4], r.o);
+    if (role) {
+        const bool in = row < len;
+        st4(&st.O[row][c4], f32x4{in ? __uint_as_float(r.o[0] << 16) : 0.f,
+                                  in ? __uint_as_float(r.o[0] & 0xffff0000u) : 0.f,
+                                  in ? __uint_as_float(r.o[1] << 16) : 0.f,
+                                  in ? __uint_as_float(r.o[1] & 0xffff0000u) : 0.f});
+    }
     if (tid < kD / 4)
         st4(st.gam + 4 * tid, r.gm);
 }
+
+// s_waitcnt vmcnt(0), the other counters untouched
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
 // Workgroups: XCD-aware pairs (the two halves of a (chain, role) unit land on one XCD and
 // share its L2 for the operand reads).  Unit u: chain u / 2, role u % 2.  Wave w of half hv
@@ -427,20 +421,34 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         for (int ct = 0; ct < 8; ++ct)
             S[ct] = a.dht ? ld4(a.dht + srow + 16 * ct) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // The operands of chunk it + 1 are requested while chunk it runs.
+    wait_vmem();  // the initial state is in (so that no wait inside the loop is for it)
     StageRegs rg;
+    auto chunk_of = [&](int64_t it) { return role ? nch - 1 - it : it; };
+    auto load = [&](int64_t it) {
+        const int64_t j = chunk_of(it);
+        stage_load(a, role, hv, op_of(j), start + kCH * j, tok_len(j), h, rg, tid);
+    };
     if (nch > 0) {
-        const int64_t j0 = role ? nch - 1 : 0;
-        stage_load(a, role, hv, op_of(j0), start + kCH * j0, tok_len(j0), h, rg, tid);
-        stage_store(role, rg, s_st[0], tid);
+        load(0);
+        stage_store(role, rg, s_st[0], tok_len(chunk_of(0)), tid);
     }
     __syncthreads();
     for (int64_t it = 0; it < nch; ++it) {
-        const int64_t j = role ? nch - 1 - it : it, jn = role ? j - 1 : j + 1;
+        const int64_t j = chunk_of(it);
         const bool more = it + 1 < nch;
         if (more)
-            stage_load(a, role, hv, op_of(jn), start + kCH * jn, tok_len(jn), h, rg, tid);
+            load(it + 1);
         const ChainStage &st = s_st[it & 1];
         const size_t sl = slot_of(j);
+        f32x4 A[8];  // A operands of the first product, all read before its MFMAs
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            A[ct] = ld4(st.A0 + m * kD + 16 * ct + 4 * g);
+        f32x4 X0, X1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            X0[i] = st.U[4 * g + i][16 * wave + m];
         // the state before the chunk (role 0) or dL/dS after it (role 1), as [channel][value row]
         float *ck = (role ? a.ckd : a.cks) + sl * kBState + v0 + m;
 #pragma unroll
@@ -448,23 +456,29 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 ck[(size_t)(16 * ct + 4 * g + i) * kD] = S[ct][i];
-        // role 0: V' = U - W S^T;  role 1: dV' = U~ + KD D^T   (rows r = 4 g + i, column v0 + m)
-        f32x4 X;
+        // role 0: V' = U - W S^T;  role 1: dV' = U~ + KD D^T   (rows r = 4 g + i, column v0 + m);
+        // two accumulators (even and odd channel tiles)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            X[i] = st.U[4 * g + i][16 * wave + m];
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            X = mm4(ld4(st.A0 + m * kD + 16 * ct + 4 * g), S[ct], X);
+        for (int ct = 0; ct < 8; ct += 2) {
+            X0 = mm4(A[ct], S[ct], X0);
+            X1 = mm4(A[ct + 1], S[ct + 1], X1);
+        }
+        const f32x4 X = X0 + X1;
         float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + v0 + m;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             xo[(4 * g + i) * kD] = X[i];
         if (role == 0) {
             if (more) {  // S <- S Diag(gamma) + V'^T KD
+                f32x4 K[8], Gm[8];
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    K[ct] = ld4(st.A1 + (16 * ct + m) * kCH + 4 * g);
+                    Gm[ct] = ld4(st.gam + 16 * ct + 4 * g);
+                }
 #pragma unroll
                 for (int ct = 0; ct < 8; ++ct)
-                    S[ct] = mm4(ld4(st.A1 + (16 * ct + m) * kCH + 4 * g), X, S[ct] * ld4(st.gam + 16 * ct + 4 * g));
+                    S[ct] = mm4(K[ct], X, S[ct] * Gm[ct]);
             }
         } else {  // D <- D Diag(gamma) + dO^T QG - dV'^T W
             f32x4 o;
@@ -472,14 +486,21 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             for (int i = 0; i < 4; ++i)
                 o[i] = st.O[4 * g + i][16 * wave + m];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                f32x4 acc = S[ct] * ld4(st.gam + 16 * ct + 4 * g);
-                acc = mm4(ld4(st.A1 + (16 * ct + m) * kCH + 4 * g), o, acc);
-                S[ct] = mm4(ld4(st.A2 + (16 * ct + m) * kCH + 4 * g), X, acc);
+            for (int c4 = 0; c4 < 8; c4 += 4) {
+                f32x4 Q[4], Wt[4], Gm[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Q[e] = ld4(st.A1 + (16 * (c4 + e) + m) * kCH + 4 * g);
+                    Wt[e] = ld4(st.A2 + (16 * (c4 + e) + m) * kCH + 4 * g);
+                    Gm[e] = ld4(st.gam + 16 * (c4 + e) + 4 * g);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[c4 + e] = mm4(Wt[e], X, mm4(Q[e], o, S[c4 + e] * Gm[e]));
             }
         }
         if (more)
-            stage_store(role, rg, s_st[(it + 1) & 1], tid);
+            stage_store(role, rg, s_st[(it + 1) & 1], tok_len(chunk_of(it + 1)), tid);
         __syncthreads();
     }
     if (role == 1 && a.dh0) {
@@ -489,12 +510,83 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
     }
 }
 
+// ---- products with the chunk's states, one workgroup per chunk-head ----
+// dKD = V' D, G1 = dO S0, G2 = dV' S0 (fp32 [16][128] each), dgamma_c = sum_v S0[v][c] D[v][c]
+// and dAqk = lower(dO V'^T) ([16][16]), written over the chunk-head's operand block (read by
+// the chains, which have run).  No LDS: the A operands (rows of V', dV', dO) come straight
+// from memory into registers, the B operands (the states, stored [channel][value row]) too.
+constexpr int kSgThreads = 256;
+constexpr int kSgKD = 0, kSgG1 = 2048, kSgG2 = 4096, kSgGam = 6144, kSgAqk = 6272;
+static_assert(kSgAqk + kCH * kCH <= kBwdOps, "state products fit the operand block");
+
+__global__ __launch_bounds__(kSgThreads) void bwd_sgrad_kernel(BwdArgs a)
+{
+    const int64_t x = blockIdx.x / a.H;
+    const int h = (int)(blockIdx.x % a.H);
+    ChunkLoc c;
+    if (!locate_chunk(a, x, c))
+        return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
+    const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;
+    // lane: row m of V', dV', dO at value columns 16 t + 4 g .. + 3
+    f32x4 af[8], ab[8], ao[8];
+    {
+        const float *pf = a.xf + sl * (kCH * kD) + m * kD + 4 * g, *pb = a.xb + sl * (kCH * kD) + m * kD + 4 * g;
+        const uint16_t *po = a.dout + ((size_t)(c.t0 + m) * (size_t)a.H + (size_t)h) * kD + 4 * g;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            af[t] = ld4(pf + 16 * t);
+            ab[t] = ld4(pb + 16 * t);
+            ao[t] = m < c.len ? ld4_bf16(po + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    float *o = a.ops + sl * kBwdOps;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {  // channel tiles 2 w + e
+        const int c0 = 16 * (2 * wave + e);
+        const float *cs = a.cks + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
+        const float *cd = a.ckd + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
+        f32x4 aKD = {0.f, 0.f, 0.f, 0.f}, aG1 = aKD, aG2 = aKD;
+        float dgp = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 bs = ld4(cs + 16 * t), bd = ld4(cd + 16 * t);
+            aKD = mm4(af[t], bd, aKD);
+            aG1 = mm4(ao[t], bs, aG1);
+            aG2 = mm4(ab[t], bs, aG2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dgp = fmaf(bs[j], bd[j], dgp);
+        }
+        dgp += __shfl_xor(dgp, 16);
+        dgp += __shfl_xor(dgp, 32);
+        if (g == 0)
+            o[kSgGam + c0 + m] = dgp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int at = (4 * g + i) * kD + c0 + m;
+            o[kSgKD + at] = aKD[i];
+            o[kSgG1 + at] = aG1[i];
+            o[kSgG2 + at] = aG2[i];
+        }
+    }
+    if (wave == 0) {  // dAqk = lower(dO V'^T): A = rows of dO, B = rows of V' (both row m here)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            acc = mm4(ao[t], af[t], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[kSgAqk + (4 * g + i) * kCH + m] = m <= 4 * g + i ? acc[i] : 0.f;
+    }
+}
+
 // ---- gradients of one chunk-head's tokens ----
 struct GradLds {
     PrepLds p;
-    float Xf[kCH][kP], Xb[kCH][kP], dKD[kCH][kP], G1[kCH][kP], G2[kCH][kP];
+    float P[kCH][kP], Q[kCH][kP];  // T^T dV' and T^T dW; P then holds db
     float dA[kCH][kQ], dAqk[kCH][kQ];
-    float dgam[kD];
+    float rowdot[kGradThreads / 64][4][2];  // per wavefront: q^ . dq^ and k^ . dk^ of its four rows
 };
 
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
@@ -508,75 +600,38 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
     const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;
-    {  // V' and dV' of the chunk
-        const int r = tid >> 5, c4 = 4 * (tid & 31);
-        st4(&L.Xf[r][c4], ld4(a.xf + sl * (kCH * kD) + r * kD + c4));
-        st4(&L.Xb[r][c4], ld4(a.xb + sl * (kCH * kD) + r * kD + c4));
-    }
+    const float *sg = a.ops + sl * kBwdOps;  // the state products
+    const float *xb = a.xb + sl * (kCH * kD);
+    if (tid < kCH * kCH)
+        L.dAqk[tid >> 4][tid & 15] = sg[kSgAqk + tid];
     prep_chunk(a, c, h, p, tid);  // ends with a barrier
-    {  // dKD = V' D, G1 = dO S0, G2 = dV' S0, dgamma: wave w takes channels 16 w .. 16 w + 15
-        const int c0 = 16 * wave;
-        const float *cs = a.cks + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
-        const float *cd = a.ckd + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
-        f32x4 aKD = {0.f, 0.f, 0.f, 0.f}, aG1 = aKD, aG2 = aKD;
-        float dgp = 0.f;
-#pragma unroll 2
-        for (int t = 0; t < kD; t += 16) {
-            const f32x4 bs = ld4(cs + t), bd = ld4(cd + t);
-            aKD = mm4(ld4(&L.Xf[m][t + 4 * g]), bd, aKD);
-            aG1 = mm4(ld4(&p.dO[m][t + 4 * g]), bs, aG1);
-            aG2 = mm4(ld4(&L.Xb[m][t + 4 * g]), bs, aG2);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dgp = fmaf(bs[j], bd[j], dgp);
-        }
-        dgp += __shfl_xor(dgp, 16);
-        dgp += __shfl_xor(dgp, 32);
-        if (g == 0)
-            L.dgam[c0 + m] = dgp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            L.dKD[4 * g + i][c0 + m] = aKD[i];
-            L.G1[4 * g + i][c0 + m] = aG1[i];
-            L.G2[4 * g + i][c0 + m] = aG2[i];
-        }
-    }
-    __syncthreads();
     const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
     const size_t tok0 = (size_t)c.t0 * (size_t)a.H + (size_t)h;  // token-head index of row 0
     auto row_at = [&](int r) { return (tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)ch; };
-    {
-        if (wave == 0) {  // dAqk = lower(dO V'^T)
-            const f32x4 acc = mm_rows(&p.dO[0][0], &L.Xf[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                L.dAqk[4 * g + i][m] = m <= 4 * g + i ? acc[i] : 0.f;
-        }
-        // P = T^T dV', Q = T^T dW = -T^T G2 (rows q4 .. q4 + 3, channel / value column ch)
+    {  // P = T^T dV', Q = T^T dW = -T^T G2 (rows q4 .. q4 + 3, value column / channel ch); dv = beta P
         float P[4] = {0.f, 0.f, 0.f, 0.f}, Q[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kCH; ++s) {
-            const float xb = L.Xb[s][ch], g2 = L.G2[s][ch];
+            const float b_ = xb[s * kD + ch], g2 = sg[kSgG2 + s * kD + ch];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                P[i] = fmaf(p.T[s][q4 + i], xb, P[i]);
+                P[i] = fmaf(p.T[s][q4 + i], b_, P[i]);
                 Q[i] = fmaf(-p.T[s][q4 + i], g2, Q[i]);
             }
         }
-        __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = q4 + i;
-            L.Xb[r][ch] = P[i];  // P replaces dV'
-            L.G2[r][ch] = Q[i];  // Q replaces G2
+            L.P[r][ch] = P[i];
+            L.Q[r][ch] = Q[i];
             if (r < c.len)
                 a.dv[row_at(r)] = p.beta[r] * P[i];
         }
     }
     __syncthreads();
     if (wave == 0) {  // dA = -strictly_lower(P U^T + Q W^T)
-        f32x4 acc = mm_rows(&L.Xb[0][0], &p.U[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-        acc = mm_rows(&L.G2[0][0], &p.W[0][0], kD, acc, lane);
+        f32x4 acc = mm_rows(&L.P[0][0], &p.U[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+        acc = mm_rows(&L.Q[0][0], &p.W[0][0], kD, acc, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             L.dA[4 * g + i][m] = m < 4 * g + i ? -acc[i] : 0.f;
@@ -585,112 +640,124 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     {  // dbeta_r = P_r . V_r + Q_r . KG_r + dA_r . M_r: 32 lanes per row
         const int r = tid >> 5, part = tid & 31;
         float s = 0.f;
+        if (r < c.len) {
+            const f32x4 vv = ld4_bf16(a.v + (tok0 + (size_t)r * (size_t)a.H) * kD + 4 * part);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int cc = 4 * part + e;
-            s = fmaf(L.Xb[r][cc], p.V[r][cc], s);
-            s = fmaf(L.G2[r][cc], p.KG[r][cc], s);
+            for (int e = 0; e < 4; ++e) {
+                const int cc = 4 * part + e;
+                s = fmaf(L.P[r][cc], vv[e], s);
+                s = fmaf(L.Q[r][cc], p.KG[r][cc], s);
+            }
+            if (part < kCH)
+                s = fmaf(L.dA[r][part], p.M[r][part], s);
         }
-        if (part < kCH)
-            s = fmaf(L.dA[r][part], p.M[r][part], s);
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1)
             s += __shfl_xor(s, o);
-        if (part == 0 && r < c.len)
-            a.dbeta[tok0 + (size_t)r * (size_t)a.H] = s;
+        if (part == 0 && r < c.len) {
+            const float b = p.beta[r];  // (after the sigmoid where it runs in the pass)
+            a.dbeta[tok0 + (size_t)r * (size_t)a.H] = (a.flags & kBSigIn) ? s * b * (1.0f - b) : s;
+        }
     }
-    {  // dKG, dKI, dQG; dk^, dq^; db into Xf (free now)
-        float db[4];
+    const float gam = p.gam[ch];
+    float db[4], eKD = 0.f;      // eKD: sum over rows of dKD KD (this thread's rows)
+    float dqh[4], dkh[4];        // dq^, dk^
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // dKG, dKI, dQG; dk^, dq^, db
+        const int r = q4 + i;
+        float sKG = L.Q[r][ch], sQG = sg[kSgG1 + r * kD + ch], sKI = 0.f;
+#pragma unroll 4  // (fully unrolled, the reads of all rows are hoisted and spill)
+        for (int s = 0; s < kCH; ++s) {
+            const float ki = p.KI[s][ch];
+            sKG = fmaf(L.dA[r][s], ki, sKG);
+            sQG = fmaf(L.dAqk[r][s], ki, sQG);
+            sKI = fmaf(L.dA[s][r] * p.beta[s], p.KG[s][ch], sKI);
+            sKI = fmaf(L.dAqk[s][r], p.QG[s][ch], sKI);
+        }
+        const float dKG = p.beta[r] * sKG, dKD = sg[kSgKD + r * kD + ch];
+        const float b = p.B[r][ch], G = expf(b), Gi = expf(-b);
+        const float kd = p.KI[r][ch] * gam;
+        db[i] = dKG * p.KG[r][ch] - sKI * p.KI[r][ch] + sQG * p.QG[r][ch] - dKD * kd;
+        eKD = fmaf(dKD, kd, eKD);
+        dkh[i] = dKG * G + (sKI + dKD * gam) * Gi;
+        dqh[i] = a.scale * sQG * G;
+    }
+    // l2norm: dq = (dq^ - q^ (q^ . dq^)) / |q|, likewise dk; the row dots over the 128 channels
+    // (two wavefronts per row quarter)
+    const bool l2_in = (a.flags & kBL2In) != 0;
+    float qh[4], kh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = q4 + i;
+        qh[i] = kh[i] = 0.f;
+        if (r < c.len) {
+            qh[i] = bbf16(a.q[row_at(r)]) * p.rq[r];
+            kh[i] = bbf16(a.k[row_at(r)]) * p.rk[r];
+        }
+    }
+    if (l2_in) {
+        float pq[4], pk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = q4 + i;
-            float sKG = L.G2[r][ch], sQG = L.G1[r][ch], sKI = 0.f;
-#pragma unroll
-            for (int s = 0; s < kCH; ++s) {
-                const float ki = p.KI[s][ch];
-                sKG = fmaf(L.dA[r][s], ki, sKG);
-                sQG = fmaf(L.dAqk[r][s], ki, sQG);
-                sKI = fmaf(L.dA[s][r] * p.beta[s], p.KG[s][ch], sKI);
-                sKI = fmaf(L.dAqk[s][r], p.QG[s][ch], sKI);
-            }
-            const float dKG = p.beta[r] * sKG, dKD = L.dKD[r][ch];
-            const float G = p.Gm[r][ch], Gi = p.Gi[r][ch];
-            db[i] = dKG * p.KG[r][ch] - sKI * p.KI[r][ch] + sQG * p.QG[r][ch] - dKD * p.KD[r][ch];
-            if (r < c.len) {
-                a.dk[row_at(r)] = dKG * G + (sKI + dKD * p.gam[ch]) * Gi;
-                a.dq[row_at(r)] = a.scale * sQG * G;
-            }
+            pq[i] = qh[i] * dqh[i];
+            pk[i] = kh[i] * dkh[i];
         }
-        __syncthreads();  // every reader of Xf (dAqk) is long done; the barrier orders the reuse
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            L.Xf[q4 + i][ch] = db[i];
+        for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pq[i] += __shfl_xor(pq[i], o);
+                pk[i] += __shfl_xor(pk[i], o);
+            }
+        if (lane == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                L.rowdot[wave][i][0] = pq[i];
+                L.rowdot[wave][i][1] = pk[i];
+            }
     }
+    __syncthreads();  // every reader of P and Q is done; the row dots are in
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = q4 + i;
+        L.P[r][ch] = db[i];
+        if (r < c.len) {
+            float dq = dqh[i], dk = dkh[i];
+            if (l2_in) {
+                const int w0 = 2 * (tid >> 7);
+                const float dotq = L.rowdot[w0][i][0] + L.rowdot[w0 + 1][i][0];
+                const float dotk = L.rowdot[w0][i][1] + L.rowdot[w0 + 1][i][1];
+                dq = (dq - qh[i] * dotq) * p.rq[r];
+                dk = (dk - kh[i] * dotk) * p.rk[r];
+            }
+            a.dq[row_at(r)] = dq;
+            a.dk[row_at(r)] = dk;
+        }
+    }
+    L.Q[tid >> 7][ch] = eKD;  // the four row quarters' sums, rows 0 .. 3 of Q (free now)
     __syncthreads();
-    if (tid < kD) {  // the last row takes the decay of the whole chunk; d log-decay by reverse sums
-        float e = L.dgam[ch] * p.gam[ch];
+    if (tid < kD) {  // the last row takes the decay of the whole chunk; d log-decay by reverse
+                     // sums, then the gate's chain rule
+        const bool gate_in = (a.flags & kBGateIn) != 0;
+        const float eA = gate_in ? expf(a.A_log[h]) : 0.f, dtb = gate_in ? a.dt_bias[(size_t)h * kD + ch] : 0.f;
+        float gv[kCH];  // g of the chunk's rows at this channel, all requested before the sums
 #pragma unroll
         for (int r = 0; r < kCH; ++r)
-            e = fmaf(L.dKD[r][ch], p.KD[r][ch], e);
-        float acc = e;
+            gv[r] = bbf16(a.g[row_at(r < c.len ? r : 0)]);
+        float acc = sg[kSgGam + ch] * gam + ((L.Q[0][ch] + L.Q[1][ch]) + (L.Q[2][ch] + L.Q[3][ch]));
+#pragma unroll
         for (int r = kCH - 1; r >= 0; --r) {
-            acc += L.Xf[r][ch];
+            acc += L.P[r][ch];
+            float dgv;
+            if (gate_in) {
+                const float sgm = 1.0f / (1.0f + expf(-eA * (gv[r] + dtb)));
+                dgv = acc * a.lower_bound * sgm * (1.0f - sgm) * eA;
+            } else {
+                dgv = (gv[r] > a.lower_bound && gv[r] < 0.f) ? acc : 0.f;
+            }
             if (r < c.len)
-                a.dg[row_at(r)] = acc;
+                a.dg[row_at(r)] = dgv;
         }
-    }
-}
-
-// ---- finish: activations' chain rules, in place, one wavefront per token-head ----
-__global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a)
-{
-    const int lane = threadIdx.x & 63;
-    const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (th >= a.B * a.T * a.H)
-        return;
-    const int h = (int)(th % a.H);
-    const size_t base = (size_t)th * kD;
-    float dqn[2], dkn[2], qn[2], kn[2];
-    float pq = 0.f, pk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int c = lane + 64 * e;
-        dqn[e] = a.dq[base + c];
-        dkn[e] = a.dk[base + c];
-        qn[e] = a.qn[base + c];
-        kn[e] = a.kn[base + c];
-        pq = fmaf(qn[e], dqn[e], pq);
-        pk = fmaf(kn[e], dkn[e], pk);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        pq += __shfl_xor(pq, o);
-        pk += __shfl_xor(pk, o);
-    }
-    const bool l2_in = (a.flags & kBL2In) != 0;
-    const float rq = a.rq[th], rk = a.rk[th];
-    const float eA = (a.flags & kBGateIn) ? expf(a.A_log[h]) : 0.f;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int c = lane + 64 * e;
-        // l2norm: dq = (dq^ - q^ (q^ . dq^)) / |q|
-        a.dq[base + c] = l2_in ? (dqn[e] - qn[e] * pq) * rq : dqn[e];
-        a.dk[base + c] = l2_in ? (dkn[e] - kn[e] * pk) * rk : dkn[e];
-        const float da = a.dg[base + c];
-        const float gc = bbf16(a.g[base + c]);
-        float dgv;
-        if (a.flags & kBGateIn) {
-            const float x = eA * (gc + a.dt_bias[(size_t)h * kD + c]);
-            const float s = 1.0f / (1.0f + expf(-x));
-            dgv = da * a.lower_bound * s * (1.0f - s) * eA;
-        } else {
-            dgv = (gc > a.lower_bound && gc < 0.f) ? da : 0.f;
-        }
-        a.dg[base + c] = dgv;
-    }
-    if (lane == 0 && (a.flags & kBSigIn)) {
-        const float b = a.bt[th];
-        a.dbeta[th] = a.dbeta[th] * b * (1.0f - b);
     }
 }
 
@@ -784,12 +851,6 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.seq_start = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_len);
     a.seq_off = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_off);
-    a.kn = reinterpret_cast<float *>(ws + f.bl.off_kn);
-    a.qn = reinterpret_cast<float *>(ws + f.bl.off_qn);
-    a.lg = reinterpret_cast<float *>(ws + f.bl.off_lg);
-    a.rk = reinterpret_cast<float *>(ws + f.bl.off_rk);
-    a.rq = reinterpret_cast<float *>(ws + f.bl.off_rq);
-    a.bt = reinterpret_cast<float *>(ws + f.bl.off_bt);
     a.ops = reinterpret_cast<float *>(ws + f.bl.off_ops);
     a.cks = reinterpret_cast<float *>(ws + f.bl.off_cks);
     a.ckd = reinterpret_cast<float *>(ws + f.bl.off_ckd);
@@ -802,9 +863,6 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     auto check = [] { return hipGetLastError(); };
     hipError_t e;
     if (toks > 0) {
-        hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, a);
-        if ((e = check()) != hipSuccess)
-            return e;
         hipLaunchKernelGGL(bwd_ops_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
@@ -816,10 +874,10 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
             return e;
     }
     if (toks > 0) {
-        hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
+        hipLaunchKernelGGL(bwd_sgrad_kernel, dim3((unsigned)slots), dim3(kSgThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
     }

@@ -179,9 +179,7 @@ struct FwdArgs {
 };
 
 // Workspace of the backward pass: the chunk table (as the forward pass lays it out, up to
-// the cut-plan states, which the backward pass does not use), then per token-head the
-// activated k^, q^ and log-decay a (fp32 [tokens][H][128]) and 1/|k|, 1/|q|, beta (fp32
-// [tokens][H]); per chunk-head (chunk x of the head's chunk list, slot x H + h) the chain
+// the cut-plan states, which the backward pass does not use), then per chunk-head (chunk x of the head's chunk list, slot x H + h) the chain
 // kernels' operand block (kBwdOps fp32), the state before the chunk and dL/dS after it (fp32
 // 128 x 128 each, stored transposed: [key channel][value row]), the chunk's corrected values
 // V' and their gradient (fp32 [16][128] each); and the per-head gradient partial sums (fp32
@@ -193,7 +191,7 @@ constexpr int kBwdOps = 7 * kCH * kD + kD;
 struct BwdLayout {
     Layout tab;
     int64_t chunks;  // bound on the chunk count of a head (the slots per head)
-    size_t off_kn, off_qn, off_lg, off_rk, off_rq, off_bt, off_ops, off_cks, off_ckd, off_xf, off_xb, off_hpart;
+    size_t off_ops, off_cks, off_ckd, off_xf, off_xb, off_hpart;
     size_t total;
 };
 
@@ -201,7 +199,6 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
 {
     if (!make_layout(B, T, H, N, varlen, &L->tab))
         return false;
-    const size_t tok = (size_t)B * (size_t)T * (size_t)H;
     const size_t state = (size_t)kD * kD * sizeof(float);
     L->chunks = varlen ? cdiv(T, kCH) + L->tab.n_seq : B * cdiv(T, kCH);
     const size_t ch = (size_t)L->chunks * (size_t)H;  // chunk-head slots
@@ -211,12 +208,6 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
         off = round_up(off + bytes, kAlign);
         return o;
     };
-    L->off_kn = take(tok * kD * sizeof(float));
-    L->off_qn = take(tok * kD * sizeof(float));
-    L->off_lg = take(tok * kD * sizeof(float));
-    L->off_rk = take(tok * sizeof(float));
-    L->off_rq = take(tok * sizeof(float));
-    L->off_bt = take(tok * sizeof(float));
     L->off_ops = take(ch * kBwdOps * sizeof(float));
     L->off_cks = take(ch * state);
     L->off_ckd = take(ch * state);

@@ -90,7 +90,7 @@ def test_invalid_cu_seqlens_under_cut_plan(bad):
     if bad == "decreasing":
         cu[3] = cu[2] - 1
     elif bad == "first":
-        cu[0] = 1
+        cu[0] = -1  # (the first sequence is empty: a positive start would also break monotony)
     else:
         cu[-1] = w.T - 1
     d = to_device(w)
