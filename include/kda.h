@@ -264,9 +264,9 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int ha
  *   workspace     device scratch of at least kda_bwd_workspace_size(...) bytes, 256-byte
  *                 aligned.
  * Outputs must not overlap any input or each other (KDA_ERR_ALIAS).  Same error codes as
- * kda_fwd_ex otherwise.  Work is enqueued on `stream`; nothing is allocated.  One
- * workgroup per (sequence, head) walks its tokens forward and then backward, so the time
- * grows with the longest sequence.
+ * kda_fwd_ex otherwise.  Work is enqueued on `stream`; nothing is allocated.  The pass runs
+ * in 16-token chunks: the state runs forwards and dL/dS backwards over the chunks of each
+ * (sequence, head), and the tokens' gradients are formed per chunk in parallel.
  */
 kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta, float scale,
                    const float *A_log, const float *dt_bias, float lower_bound, const void *initial_state,
@@ -277,11 +277,11 @@ kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, c
                    size_t workspace_bytes, void *stream, uint32_t flags);
 
 /*
- * kda_bwd_workspace_size -- bytes of workspace kda_bwd needs: the chunk table, fp32 copies of
- * the activated k^, q^ and decay (3 x 512 bytes per token-head) plus three scalars per
- * token-head, the fp32 state before every 16-token chunk of every chain (64 KiB each),
- * a 1 MiB buffer per chain and 64 KiB per head of partial sums.  Returns 0 for invalid
- * sizes.
+ * kda_bwd_workspace_size -- bytes of workspace kda_bwd needs: the chunk table, then per
+ * 16-token chunk of each head (counted as ceil(T / 16) per batch row, or ceil(T / 16) + N
+ * with cu_seqlens) 56.5 KiB of chunk operands, the fp32 state before the chunk and dL/dS
+ * after it (64 KiB each) and the chunk's V' and dL/dV' (8 KiB each), and 64 KiB per head of
+ * partial sums.  Returns 0 for invalid sizes.
  */
 size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 
