@@ -50,8 +50,10 @@ namespace {
 
 constexpr int kBGateIn = 1, kBL2In = 2, kBSigIn = 4;
 constexpr int64_t kBState = (int64_t)kD * kD;
-constexpr int kP = kD + 4;         // LDS row stride of the [16][128] fp32 tiles
+constexpr int kP = kD;             // LDS row stride of the [16][128] fp32 tiles (unpadded: the
+                                   // ops kernel then fits three workgroups per CU)
 constexpr int kQ = kCH + 1;        // LDS row stride of the 16 x 16 tiles
+constexpr int kQ4 = kCH + 4;       // the same, rows 16-byte aligned
 constexpr int kGradThreads = 512;  // bwd_ops_kernel, bwd_grad_kernel
 constexpr int kChainThreads = 256; // bwd_chain_kernel: 4 wavefronts of 16 value rows
 // operand block of a chunk-head (kBwdOps floats)
@@ -204,32 +206,60 @@ __device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &
         }
     }
     __syncthreads();
-    if (tid < kD) {  // per channel: b = cumulative log-decay; the gated rows
-        const int ch = tid;
+    {  // per channel: b = cumulative log-decay, then the gated rows.  Thread -> channel tid % 128,
+       // rows 4 (tid / 128) .. + 3: local prefix sums, block totals through W (free until W
+       // is formed), then the offsets of the blocks above.
+        const int ch = tid & (kD - 1), blk = tid >> 7, r0 = 4 * blk;
+        float *tot = &p.W[0][0];
+        float l[4];
         float run = 0.f;
 #pragma unroll
-        for (int r = 0; r < kCH; ++r) {
-            run += p.B[r][ch];
-            p.B[r][ch] = run;
-            const float G = expf(run), Gi = expf(-run), k = p.KG[r][ch];
+        for (int i = 0; i < 4; ++i) {
+            run += p.B[r0 + i][ch];
+            l[i] = run;
+        }
+        tot[blk * kD + ch] = run;
+        __syncthreads();
+        float off = 0.f, all = 0.f;
+#pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2) {
+            const float t = tot[b2 * kD + ch];
+            off += b2 < blk ? t : 0.f;
+            all += t;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            const float b = off + l[i], G = expf(b), Gi = expf(-b), k = p.KG[r][ch];
+            p.B[r][ch] = b;
             p.KG[r][ch] = k * G;
             p.KI[r][ch] = k * Gi;
             p.QG[r][ch] = a.scale * p.QG[r][ch] * G;
         }
-        p.gam[ch] = expf(run);
+        if (blk == 0)
+            p.gam[ch] = expf(all);
     }
     __syncthreads();
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
-    if (wave == 0) {  // KG KI^T
-        const f32x4 acc = mm_rows(&p.KG[0][0], &p.KI[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+    {  // KG KI^T (waves 0 - 3) and QG KI^T (waves 4 - 7), 32 channels per wave; the four partial
+       // sums of each through W
+        float *part = &p.W[0][0];
+        const int k0 = 32 * (wave & 3);
+        const f32x4 acc = mm_rows(wave < 4 ? &p.KG[0][k0] : &p.QG[0][k0], &p.KI[0][k0], 32,
+                                  f32x4{0.f, 0.f, 0.f, 0.f}, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            p.M[4 * g + i][m] = acc[i];
-    } else if (wave == 1) {  // lower(QG KI^T), diagonal included
-        const f32x4 acc = mm_rows(&p.QG[0][0], &p.KI[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            p.Aqk[4 * g + i][m] = m <= 4 * g + i ? acc[i] : 0.f;
+            part[wave * (kCH * kCH) + (4 * g + i) * kCH + m] = acc[i];
+    }
+    __syncthreads();
+    {
+        const float *part = &p.W[0][0];
+        const int e = tid & (kCH * kCH - 1), r = e >> 4, s_ = e & 15, q = 4 * (tid >> 8);
+        const float v = (part[q * 256 + e] + part[(q + 1) * 256 + e]) + (part[(q + 2) * 256 + e] + part[(q + 3) * 256 + e]);
+        if (tid < kCH * kCH)
+            p.M[r][s_] = v;
+        else
+            p.Aqk[r][s_] = s_ <= r ? v : 0.f;  // diagonal included
     }
     __syncthreads();
     if (tid < kCH) {  // T = (I + A)^-1, A = strictly_lower(diag(beta) M): lane s solves column s
@@ -280,30 +310,43 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
     ChunkLoc c;
     if (!locate_chunk(a, x, c))
         return;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
+    // dO at rows 4 g + j, value column 16 w + m (the B operand of U~ below), requested before
+    // the chunk's operands are formed; raw bits, so that nothing waits for them yet
+    uint32_t od[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        od[j] = a.dout[((size_t)(c.t0 + (r < c.len ? r : 0)) * (size_t)a.H + (size_t)h) * kD + 16 * wave + m];
+        if (r >= c.len)
+            od[j] = 0;
+    }
     prep_chunk(a, c, h, p, tid);
     float *o = a.ops + ((size_t)x * (size_t)a.H + (size_t)h) * kBwdOps;
-    const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
-    float dO[kCH];  // column ch of dL/dout
+    {  // U~ = lower(QG KI^T)^T dO: wave w takes value columns 16 w .. + 15
+        f32x4 at, ob;
 #pragma unroll
-    for (int s = 0; s < kCH; ++s)
-        dO[s] = s < c.len ? bbf16(a.dout[((size_t)(c.t0 + s) * (size_t)a.H + (size_t)h) * kD + ch]) : 0.f;
+        for (int j = 0; j < 4; ++j) {
+            at[j] = p.Aqk[4 * g + j][m];  // A operand: (A_qk^T)[m][4 g + j]
+            ob[j] = __uint_as_float(od[j] << 16);
+        }
+        const f32x4 ut = mm4(at, ob, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[kOpUt + (4 * g + i) * kD + 16 * wave + m] = ut[i];
+    }
+    const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
     const float gam = p.gam[ch];
     f32x4 kd, qg, nw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = q4 + i;
-        float ut = 0.f;  // U~ = lower(QG KI^T)^T dO
-#pragma unroll
-        for (int s = 0; s < kCH; ++s)
-            ut = fmaf(p.Aqk[s][r], dO[s], ut);
         kd[i] = p.KI[r][ch] * gam;
         qg[i] = p.QG[r][ch];
         nw[i] = -p.W[r][ch];
         o[kOpNegW + r * kD + ch] = nw[i];
         o[kOpU + r * kD + ch] = p.U[r][ch];
         o[kOpKD + r * kD + ch] = kd[i];
-        o[kOpUt + r * kD + ch] = ut;
     }
     st4(o + kOpKDt + ch * kCH + q4, kd);
     st4(o + kOpQGt + ch * kCH + q4, qg);
@@ -585,8 +628,11 @@ __global__ __launch_bounds__(kSgThreads) void bwd_sgrad_kernel(BwdArgs a)
 struct GradLds {
     PrepLds p;
     float P[kCH][kP], Q[kCH][kP];  // T^T dV' and T^T dW; P then holds db
-    float dA[kCH][kQ], dAqk[kCH][kQ];
-    float rowdot[kGradThreads / 64][4][2];  // per wavefront: q^ . dq^ and k^ . dk^ of its four rows
+    float dA[kCH][kQ4], dAqk[kCH][kQ4];  // rows 16-byte aligned (MFMA A operands)
+    union {
+        float rowdot[kGradThreads / 64][kCH][2];  // per wavefront (16 channels): q^ . dq^, k^ . dk^ per row
+        float part[4][kCH][kCH];                  // dA: partial sums of four wavefronts
+    };
 };
 
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
@@ -604,21 +650,50 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     const float *xb = a.xb + sl * (kCH * kD);
     if (tid < kCH * kCH)
         L.dAqk[tid >> 4][tid & 15] = sg[kSgAqk + tid];
+    // The tail's per-element inputs (D layout: wave w, channel 16 w + m, rows 4 g + i), requested
+    // now with everything else so that the tail waits for no memory.
+    const int c0 = 16 * wave, cc = c0 + m;
+    const size_t tok0 = (size_t)c.t0 * (size_t)a.H + (size_t)h;  // token-head index of row 0
+    f32x4 tG1, tKD, tq, tk, tg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const size_t at = (tok0 + (size_t)(r < c.len ? r : 0) * (size_t)a.H) * kD + (size_t)cc;
+        tG1[i] = sg[kSgG1 + r * kD + cc];
+        tKD[i] = sg[kSgKD + r * kD + cc];
+        tq[i] = bbf16(a.q[at]);
+        tk[i] = bbf16(a.k[at]);
+        tg[i] = bbf16(a.g[at]);
+    }
+    const float tdgam = sg[kSgGam + cc];
+    uint32_t vraw[2] = {0u, 0u};  // v of row tid / 32 at channels 4 (tid % 32) .. + 3 (the dbeta rows)
+    if ((tid >> 5) < c.len) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(a.v + (tok0 + (size_t)(tid >> 5) * (size_t)a.H) * kD +
+                                                         4 * (tid & 31));
+        vraw[0] = w[0];
+        vraw[1] = w[1];
+    }
+    {  // dV' into P and G2 into Q, requested with the chunk's rows (P and Q replace them below)
+        const int r = tid >> 5, c4 = 4 * (tid & 31);
+        st4(&L.P[r][c4], ld4(xb + r * kD + c4));
+        st4(&L.Q[r][c4], ld4(sg + kSgG2 + r * kD + c4));
+    }
     prep_chunk(a, c, h, p, tid);  // ends with a barrier
     const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
-    const size_t tok0 = (size_t)c.t0 * (size_t)a.H + (size_t)h;  // token-head index of row 0
     auto row_at = [&](int r) { return (tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)ch; };
     {  // P = T^T dV', Q = T^T dW = -T^T G2 (rows q4 .. q4 + 3, value column / channel ch); dv = beta P
         float P[4] = {0.f, 0.f, 0.f, 0.f}, Q[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kCH; ++s) {
-            const float b_ = xb[s * kD + ch], g2 = sg[kSgG2 + s * kD + ch];
+            const float b_ = L.P[s][ch], g2 = L.Q[s][ch];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 P[i] = fmaf(p.T[s][q4 + i], b_, P[i]);
                 Q[i] = fmaf(-p.T[s][q4 + i], g2, Q[i]);
             }
         }
+        __syncthreads();  // every column of dV' and G2 is read
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = q4 + i;
@@ -629,19 +704,27 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         }
     }
     __syncthreads();
-    if (wave == 0) {  // dA = -strictly_lower(P U^T + Q W^T)
-        f32x4 acc = mm_rows(&L.P[0][0], &p.U[0][0], kD, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-        acc = mm_rows(&L.Q[0][0], &p.W[0][0], kD, acc, lane);
+    if (wave < 4) {  // dA = -strictly_lower(P U^T + Q W^T): wave w sums columns 32 w .. 32 w + 31
+        const int k0 = 32 * wave;
+        f32x4 acc = mm_rows(&L.P[0][k0], &p.U[0][k0], 32, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+        acc = mm_rows(&L.Q[0][k0], &p.W[0][k0], 32, acc, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            L.dA[4 * g + i][m] = m < 4 * g + i ? -acc[i] : 0.f;
+            L.part[wave][4 * g + i][m] = acc[i];
+    }
+    __syncthreads();
+    if (tid < kCH * kCH) {
+        const int r = tid >> 4, s_ = tid & 15;
+        const float v = (L.part[0][r][s_] + L.part[1][r][s_]) + (L.part[2][r][s_] + L.part[3][r][s_]);
+        L.dA[r][s_] = s_ < r ? -v : 0.f;
     }
     __syncthreads();
     {  // dbeta_r = P_r . V_r + Q_r . KG_r + dA_r . M_r: 32 lanes per row
         const int r = tid >> 5, part = tid & 31;
         float s = 0.f;
         if (r < c.len) {
-            const f32x4 vv = ld4_bf16(a.v + (tok0 + (size_t)r * (size_t)a.H) * kD + 4 * part);
+            const f32x4 vv = {__uint_as_float(vraw[0] << 16), __uint_as_float(vraw[0] & 0xffff0000u),
+                              __uint_as_float(vraw[1] << 16), __uint_as_float(vraw[1] & 0xffff0000u)};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int cc = 4 * part + e;
@@ -659,104 +742,112 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
             a.dbeta[tok0 + (size_t)r * (size_t)a.H] = (a.flags & kBSigIn) ? s * b * (1.0f - b) : s;
         }
     }
-    const float gam = p.gam[ch];
-    float db[4], eKD = 0.f;      // eKD: sum over rows of dKD KD (this thread's rows)
-    float dqh[4], dkh[4];        // dq^, dk^
+    // dKG, dKI, dQG on the MFMA: wave w takes channels c0 .. c0 + 15, c0 = 16 w; lane (g, m)
+    // holds rows 4 g + i at channel c0 + m (the D layout) from here on.
+    f32x4 sKG, sQG = tG1, sKI = {0.f, 0.f, 0.f, 0.f};
+    {
+        f32x4 ki, kgb, qg;  // B operands: rows 4 g + j at channel cc
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // dKG, dKI, dQG; dk^, dq^, db
-        const int r = q4 + i;
-        float sKG = L.Q[r][ch], sQG = sg[kSgG1 + r * kD + ch], sKI = 0.f;
-#pragma unroll 4  // (fully unrolled, the reads of all rows are hoisted and spill)
-        for (int s = 0; s < kCH; ++s) {
-            const float ki = p.KI[s][ch];
-            sKG = fmaf(L.dA[r][s], ki, sKG);
-            sQG = fmaf(L.dAqk[r][s], ki, sQG);
-            sKI = fmaf(L.dA[s][r] * p.beta[s], p.KG[s][ch], sKI);
-            sKI = fmaf(L.dAqk[s][r], p.QG[s][ch], sKI);
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * g + j;
+            ki[j] = p.KI[r][cc];
+            kgb[j] = p.beta[r] * p.KG[r][cc];
+            qg[j] = p.QG[r][cc];
+            sKG[j] = L.Q[r][cc];
         }
-        const float dKG = p.beta[r] * sKG, dKD = sg[kSgKD + r * kD + ch];
-        const float b = p.B[r][ch], G = expf(b), Gi = expf(-b);
-        const float kd = p.KI[r][ch] * gam;
-        db[i] = dKG * p.KG[r][ch] - sKI * p.KI[r][ch] + sQG * p.QG[r][ch] - dKD * kd;
-        eKD = fmaf(dKD, kd, eKD);
-        dkh[i] = dKG * G + (sKI + dKD * gam) * Gi;
-        dqh[i] = a.scale * sQG * G;
+        const f32x4 dA_r = ld4(&L.dA[m][4 * g]), dAqk_r = ld4(&L.dAqk[m][4 * g]);  // rows m
+        f32x4 dA_c, dAqk_c;                                                          // columns m
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dA_c[j] = L.dA[4 * g + j][m];
+            dAqk_c[j] = L.dAqk[4 * g + j][m];
+        }
+        sKG = mm4(dA_r, ki, sKG);      // Q + dA KI
+        sQG = mm4(dAqk_r, ki, sQG);    // G1 + dAqk KI
+        sKI = mm4(dA_c, kgb, sKI);     // dA^T diag(beta) KG
+        sKI = mm4(dAqk_c, qg, sKI);    //   + dAqk^T QG
     }
-    // l2norm: dq = (dq^ - q^ (q^ . dq^)) / |q|, likewise dk; the row dots over the 128 channels
-    // (two wavefronts per row quarter)
-    const bool l2_in = (a.flags & kBL2In) != 0;
-    float qh[4], kh[4];
+    const float gam = p.gam[cc];
+    f32x4 db, dqh, dkh, qh, kh;
+    float eKD = 0.f;  // sum over this lane's rows of dKD KD
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = q4 + i;
-        qh[i] = kh[i] = 0.f;
-        if (r < c.len) {
-            qh[i] = bbf16(a.q[row_at(r)]) * p.rq[r];
-            kh[i] = bbf16(a.k[row_at(r)]) * p.rk[r];
-        }
+        const int r = 4 * g + i;
+        const float dKG = p.beta[r] * sKG[i], dKD = tKD[i];
+        const float b = p.B[r][cc], G = expf(b), Gi = expf(-b);
+        const float kd = p.KI[r][cc] * gam;
+        db[i] = dKG * p.KG[r][cc] - sKI[i] * p.KI[r][cc] + sQG[i] * p.QG[r][cc] - dKD * kd;
+        eKD = fmaf(dKD, kd, eKD);
+        dkh[i] = dKG * G + (sKI[i] + dKD * gam) * Gi;
+        dqh[i] = a.scale * sQG[i] * G;
+        qh[i] = r < c.len ? tq[i] * p.rq[r] : 0.f;
+        kh[i] = r < c.len ? tk[i] * p.rk[r] : 0.f;
     }
+    // l2norm: dq = (dq^ - q^ (q^ . dq^)) / |q|, likewise dk; row dots over the 16 lanes of a
+    // row group, then over the eight wavefronts
+    const bool l2_in = (a.flags & kBL2In) != 0;
     if (l2_in) {
-        float pq[4], pk[4];
+        f32x4 pq = qh * dqh, pk = kh * dkh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pq[i] = qh[i] * dqh[i];
-            pk[i] = kh[i] * dkh[i];
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1)
+        for (int o = 8; o > 0; o >>= 1)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 pq[i] += __shfl_xor(pq[i], o);
                 pk[i] += __shfl_xor(pk[i], o);
             }
-        if (lane == 0)
+        if (m == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                L.rowdot[wave][i][0] = pq[i];
-                L.rowdot[wave][i][1] = pk[i];
+                L.rowdot[wave][4 * g + i][0] = pq[i];
+                L.rowdot[wave][4 * g + i][1] = pk[i];
             }
+        __syncthreads();
     }
-    __syncthreads();  // every reader of P and Q is done; the row dots are in
+    // d log-decay: reverse cumulative sum of db over the chunk's rows (this lane's four, then the
+    // row groups above it by lane exchange), plus the decay of the whole chunk
+    // (dgamma gamma + sum_r dKD KD) on every row; then the gate's chain rule.
+    float e = eKD;
+    e += __shfl_xor(e, 16);
+    e += __shfl_xor(e, 32);
+    e += tdgam * gam;
+    const float tot = (db[0] + db[1]) + (db[2] + db[3]);
+    float above = 0.f;  // sum of the row groups g' > g
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = q4 + i;
-        L.P[r][ch] = db[i];
+    for (int gg = 1; gg < 4; ++gg) {
+        const float t = __shfl(tot, m + 16 * gg);
+        above += gg > g ? t : 0.f;
+    }
+    const bool gate_in = (a.flags & kBGateIn) != 0;
+    const float eA = gate_in ? expf(a.A_log[h]) : 0.f, dtb = gate_in ? a.dt_bias[(size_t)h * kD + cc] : 0.f;
+    float run = e + above;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+        const int r = 4 * g + i;
+        run += db[i];
         if (r < c.len) {
+            const size_t at = (tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)cc;
+            const float gc = tg[i];
+            float dgv;
+            if (gate_in) {
+                const float sgm = 1.0f / (1.0f + expf(-eA * (gc + dtb)));
+                dgv = run * a.lower_bound * sgm * (1.0f - sgm) * eA;
+            } else {
+                dgv = (gc > a.lower_bound && gc < 0.f) ? run : 0.f;
+            }
+            a.dg[at] = dgv;
             float dq = dqh[i], dk = dkh[i];
             if (l2_in) {
-                const int w0 = 2 * (tid >> 7);
-                const float dotq = L.rowdot[w0][i][0] + L.rowdot[w0 + 1][i][0];
-                const float dotk = L.rowdot[w0][i][1] + L.rowdot[w0 + 1][i][1];
+                float dotq = 0.f, dotk = 0.f;
+#pragma unroll
+                for (int w = 0; w < kGradThreads / 64; ++w) {
+                    dotq += L.rowdot[w][r][0];
+                    dotk += L.rowdot[w][r][1];
+                }
                 dq = (dq - qh[i] * dotq) * p.rq[r];
                 dk = (dk - kh[i] * dotk) * p.rk[r];
             }
-            a.dq[row_at(r)] = dq;
-            a.dk[row_at(r)] = dk;
-        }
-    }
-    L.Q[tid >> 7][ch] = eKD;  // the four row quarters' sums, rows 0 .. 3 of Q (free now)
-    __syncthreads();
-    if (tid < kD) {  // the last row takes the decay of the whole chunk; d log-decay by reverse
-                     // sums, then the gate's chain rule
-        const bool gate_in = (a.flags & kBGateIn) != 0;
-        const float eA = gate_in ? expf(a.A_log[h]) : 0.f, dtb = gate_in ? a.dt_bias[(size_t)h * kD + ch] : 0.f;
-        float gv[kCH];  // g of the chunk's rows at this channel, all requested before the sums
-#pragma unroll
-        for (int r = 0; r < kCH; ++r)
-            gv[r] = bbf16(a.g[row_at(r < c.len ? r : 0)]);
-        float acc = sg[kSgGam + ch] * gam + ((L.Q[0][ch] + L.Q[1][ch]) + (L.Q[2][ch] + L.Q[3][ch]));
-#pragma unroll
-        for (int r = kCH - 1; r >= 0; --r) {
-            acc += L.P[r][ch];
-            float dgv;
-            if (gate_in) {
-                const float sgm = 1.0f / (1.0f + expf(-eA * (gv[r] + dtb)));
-                dgv = acc * a.lower_bound * sgm * (1.0f - sgm) * eA;
-            } else {
-                dgv = (gv[r] > a.lower_bound && gv[r] < 0.f) ? acc : 0.f;
-            }
-            if (r < c.len)
-                a.dg[row_at(r)] = dgv;
+            a.dq[at] = dq;
+            a.dk[at] = dk;
         }
     }
 }
