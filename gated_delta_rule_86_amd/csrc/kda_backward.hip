@@ -97,6 +97,11 @@ __device__ __forceinline__ f32x4 mm_rows(const float *A, const float *B, int nk,
     return acc;
 }
 
+// Layout of the per-chunk states and rows in the workspace, chosen so that every store of the
+// chain kernel (a wave's 16 value rows, four channels per lane) writes 256 contiguous bytes and
+// every read of the state-product kernel (four value rows at one channel) is one 16-byte load:
+//   state_at(v, c) = ((v / 16) 8 + c / 16) 256 + (c % 4) 64 + (c / 4 % 4) 16 + v % 16
+//   rows_at(r, v)  = (v / 16) 256 + (r % 4) 64 + (r / 4) 16 + v % 16     (r: row of the chunk)
 struct BwdArgs {
     const uint16_t *q, *k, *v, *g, *beta, *dout;
     const float *A_log, *dt_bias;
@@ -109,8 +114,8 @@ struct BwdArgs {
     int64_t B, T, H, N, chunks;
     const int64_t *seq_start, *seq_len, *seq_off;
     float *ops;              // [chunks][H][kBwdOps]
-    float *cks, *ckd;        // [chunks][H][128][128]: S before the chunk, dL/dS after it (transposed)
-    float *xf, *xb;          // [chunks][H][16][128]: V' and dL/dV'
+    float *cks, *ckd;        // [chunks][H][16384]: S before the chunk, dL/dS after it (state_at)
+    float *xf, *xb;          // [chunks][H][2048]: V' and dL/dV' (rows_at)
     float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
 };
 
@@ -492,13 +497,14 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             X0[i] = st.U[4 * g + i][16 * wave + m];
-        // the state before the chunk (role 0) or dL/dS after it (role 1), as [channel][value row]
-        float *ck = (role ? a.ckd : a.cks) + sl * kBState + v0 + m;
+        // the state before the chunk (role 0) or dL/dS after it (role 1), in the tiled layout
+        // (state_at): each store of the wave writes 256 contiguous bytes
+        float *ck = (role ? a.ckd : a.cks) + sl * kBState + (size_t)(v0 >> 4) * (8 * 256) + 16 * g + m;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                ck[(size_t)(16 * ct + 4 * g + i) * kD] = S[ct][i];
+                ck[256 * ct + 64 * i] = S[ct][i];
         // role 0: V' = U - W S^T;  role 1: dV' = U~ + KD D^T   (rows r = 4 g + i, column v0 + m);
         // two accumulators (even and odd channel tiles)
 #pragma unroll
@@ -507,10 +513,10 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             X1 = mm4(A[ct + 1], S[ct + 1], X1);
         }
         const f32x4 X = X0 + X1;
-        float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + v0 + m;
+        float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + (v0 >> 4) * 256 + 16 * g + m;  // (rows_at)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            xo[(4 * g + i) * kD] = X[i];
+            xo[64 * i] = X[i];
         if (role == 0) {
             if (more) {  // S <- S Diag(gamma) + V'^T KD
                 f32x4 K[8], Gm[8];
@@ -574,12 +580,13 @@ __global__ __launch_bounds__(kSgThreads) void bwd_sgrad_kernel(BwdArgs a)
     // lane: row m of V', dV', dO at value columns 16 t + 4 g .. + 3
     f32x4 af[8], ab[8], ao[8];
     {
-        const float *pf = a.xf + sl * (kCH * kD) + m * kD + 4 * g, *pb = a.xb + sl * (kCH * kD) + m * kD + 4 * g;
+        const int xr = 64 * (m & 3) + 16 * (m >> 2) + 4 * g;  // rows_at(m, 4 g) - rows_at(0, 0)
+        const float *pf = a.xf + sl * (kCH * kD) + xr, *pb = a.xb + sl * (kCH * kD) + xr;
         const uint16_t *po = a.dout + ((size_t)(c.t0 + m) * (size_t)a.H + (size_t)h) * kD + 4 * g;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            af[t] = ld4(pf + 16 * t);
-            ab[t] = ld4(pb + 16 * t);
+            af[t] = ld4(pf + 256 * t);
+            ab[t] = ld4(pb + 256 * t);
             ao[t] = m < c.len ? ld4_bf16(po + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
@@ -587,13 +594,15 @@ __global__ __launch_bounds__(kSgThreads) void bwd_sgrad_kernel(BwdArgs a)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {  // channel tiles 2 w + e
         const int c0 = 16 * (2 * wave + e);
-        const float *cs = a.cks + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
-        const float *cd = a.ckd + sl * kBState + (size_t)(c0 + m) * kD + 4 * g;
+        // state_at(16 t + 4 g, c0 + m) = 2048 t + 256 (c0 / 16) + 64 (m % 4) + 16 (m / 4) + 4 g
+        const int so = 256 * (c0 >> 4) + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
+        const float *cs = a.cks + sl * kBState + so;
+        const float *cd = a.ckd + sl * kBState + so;
         f32x4 aKD = {0.f, 0.f, 0.f, 0.f}, aG1 = aKD, aG2 = aKD;
         float dgp = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const f32x4 bs = ld4(cs + 16 * t), bd = ld4(cd + 16 * t);
+            const f32x4 bs = ld4(cs + 2048 * t), bd = ld4(cd + 2048 * t);
             aKD = mm4(af[t], bd, aKD);
             aG1 = mm4(ao[t], bs, aG1);
             aG2 = mm4(ab[t], bs, aG2);
@@ -676,7 +685,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     }
     {  // dV' into P and G2 into Q, requested with the chunk's rows (P and Q replace them below)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
-        st4(&L.P[r][c4], ld4(xb + r * kD + c4));
+        st4(&L.P[r][c4], ld4(xb + 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15)));  // (rows_at)
         st4(&L.Q[r][c4], ld4(sg + kSgG2 + r * kD + c4));
     }
     prep_chunk(a, c, h, p, tid);  // ends with a barrier

@@ -181,8 +181,8 @@ struct FwdArgs {
 // Workspace of the backward pass: the chunk table (as the forward pass lays it out, up to
 // the cut-plan states, which the backward pass does not use), then per chunk-head (chunk x of the head's chunk list, slot x H + h) the chain
 // kernels' operand block (kBwdOps fp32), the state before the chunk and dL/dS after it (fp32
-// 128 x 128 each, stored transposed: [key channel][value row]), the chunk's corrected values
-// V' and their gradient (fp32 [16][128] each); and the per-head gradient partial sums (fp32
+// 128 x 128 each, in a tiled layout of the backward kernels), the chunk's corrected values
+// V' and their gradient (fp32 16 x 128 each, tiled likewise); and the per-head gradient partial sums (fp32
 // [H][kHeadSlices][2][128]).
 constexpr int kHeadSlices = 64;  // token slices of the backward pass's per-head gradient sums
 // operand block of one chunk-head: -W, U, KD^T, KD, U~, QG^T, -W^T (2048 fp32 each), gamma (128)
