@@ -361,13 +361,22 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
 }
 
 // ---- the two chains over the chunks of one (sequence, head) ----
-// One chunk's operands for one half (64 value rows) of a chain, staged in LDS.
+// Work split (the value rows of a state are independent given the chunk's operands): with
+// kCh = 1, a (chain, role) unit takes two workgroups of 64 value rows, wave w owning 16 rows at
+// all channels; with kCh = 2 (few units: each workgroup's chunk then takes half the MFMA work
+// per wave), four workgroups of 32 rows, wave w owning 16 rows at the channels of half w % 2,
+// the first product's two half sums exchanged through LDS.  The workgroups of a unit land on
+// one XCD and share its L2 for the operand reads.  kCh = 1 reads each chunk's operands half as
+// often, which is what counts when the chains are many and HBM is the limit.
+constexpr int kChainUnitsSplit = 128;  // units (chain, role) up to which kCh = 2 is used
+
+template <int kRows>
 struct ChainStage {
     float A0[kCH * kD];  // role 0: -W [r][c];  role 1: KD [r][c]
     float A1[kD * kCH];  // role 0: KD^T [c][r]; role 1: QG^T [c][r]
     float A2[kD * kCH];  // role 1: -W^T [c][r]
-    float U[kCH][64];    // role 0: U, role 1: U~ (the half's value columns)
-    float O[kCH][64];    // role 1: dO (the half's value columns)
+    float U[kCH][kRows]; // role 0: U, role 1: U~ (the workgroup's value columns)
+    float O[kCH][kRows]; // role 1: dO (the workgroup's value columns)
     float gam[kD];
 };
 
@@ -378,9 +387,11 @@ struct StageRegs {
     f32x4 a0[2], a1[2], a2[2], u, gm;
     uint32_t o[2];  // two bf16 pairs of dO
 };
-__device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int hv, const float *op, int64_t t0, int len,
+template <int kRows>
+__device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int part, const float *op, int64_t t0, int len,
                                            int h, StageRegs &r, int tid)
 {
+    constexpr int kQ4 = kRows / 4;  // float4 columns of U, O
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int f = 4 * (tid + kChainThreads * e);
@@ -389,20 +400,22 @@ __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int hv, c
         if (role)
             r.a2[e] = ld4(op + kOpNegWt + f);
     }
-    const int row = tid >> 4, c4 = 4 * (tid & 15);
-    r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + 64 * hv + c4);
+    const int row = (tid / kQ4) & 15, c4 = 4 * (tid % kQ4);  // (kRows = 32: threads 128 .. repeat)
+    r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + kRows * part + c4);
     if (role) {
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const int rr = row < len ? row : 0;
         const u32x2 w = *reinterpret_cast<const u32x2 *>(a.dout + ((size_t)(t0 + rr) * (size_t)a.H + (size_t)h) * kD +
-                                                         64 * hv + c4);
+                                                         kRows * part + c4);
         r.o[0] = w[0];
         r.o[1] = w[1];
     }
     r.gm = ld4(op + kOpGam + 4 * (tid & (kD / 4 - 1)));
 }
-__device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainStage &st, int len, int tid)
+template <int kRows>
+__device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainStage<kRows> &st, int len, int tid)
 {
+    constexpr int kQ4 = kRows / 4;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int f = 4 * (tid + kChainThreads * e);
@@ -411,14 +424,16 @@ __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainS
         if (role)
             st4(st.A2 + f, r.a2[e]);
     }
-    const int row = tid >> 4, c4 = 4 * (tid & 15);
-    st4(&st.U[row][c4], r.u);
-    if (role) {
-        const bool in = row < len;
-        st4(&st.O[row][c4], f32x4{in ? __uint_as_float(r.o[0] << 16) : 0.f,
-                                  in ? __uint_as_float(r.o[0] & 0xffff0000u) : 0.f,
-                                  in ? __uint_as_float(r.o[1] << 16) : 0.f,
-                                  in ? __uint_as_float(r.o[1] & 0xffff0000u) : 0.f});
+    if (tid < kCH * kQ4) {
+        const int row = tid / kQ4, c4 = 4 * (tid % kQ4);
+        st4(&st.U[row][c4], r.u);
+        if (role) {
+            const bool in = row < len;
+            st4(&st.O[row][c4], f32x4{in ? __uint_as_float(r.o[0] << 16) : 0.f,
+                                      in ? __uint_as_float(r.o[0] & 0xffff0000u) : 0.f,
+                                      in ? __uint_as_float(r.o[1] << 16) : 0.f,
+                                      in ? __uint_as_float(r.o[1] & 0xffff0000u) : 0.f});
+        }
     }
     if (tid < kD / 4)
         st4(st.gam + 4 * tid, r.gm);
@@ -427,18 +442,20 @@ __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainS
 // s_waitcnt vmcnt(0), the other counters untouched
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
-// Workgroups: XCD-aware pairs (the two halves of a (chain, role) unit land on one XCD and
-// share its L2 for the operand reads).  Unit u: chain u / 2, role u % 2.  Wave w of half hv
-// owns value rows v0 .. v0 + 15, v0 = 64 hv + 16 w; its state is held transposed in the
-// D layout: tile ct (channels 16 ct ..) lane L element i = S[v0 + L % 16][16 ct + 4 (L / 16) + i].
+// Workgroup b: XCD b % 8, part (b / 8) % (2 kCh) of unit (b / (16 kCh)) 8 + b % 8; unit u:
+// chain u / 2, role u % 2.  A wave's state is held transposed in the D layout: its tile e
+// (channels 16 ct .., ct = ct0 + e) has in lane L element i S[v0 + L % 16][16 ct + 4 (L / 16) + i].
+template <int kCh>
 __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 {
-    __shared__ __attribute__((aligned(16))) ChainStage s_st[2];
+    constexpr int kRows = 64 / kCh, kTiles = 8 / kCh, kParts = 2 * kCh;
+    __shared__ __attribute__((aligned(16))) ChainStage<kRows> s_st[2];
+    __shared__ __attribute__((aligned(16))) float s_x[kCh == 2 ? kChainThreads / 64 : 1][64][4];  // half sums
     const int64_t bid = blockIdx.x;
     const int xcd = (int)(bid & 7);
     const int64_t slot = bid >> 3;
-    const int hv = (int)(slot & 1);
-    const int64_t unit = (slot >> 1) * 8 + xcd;
+    const int part = (int)(slot % kParts);
+    const int64_t unit = (slot / kParts) * 8 + xcd;
     const int64_t H = a.H;
     if (unit >= 2 * a.N * H)
         return;
@@ -446,40 +463,41 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
     const int64_t chain = unit >> 1, n = chain / H;
     const int h = (int)(chain % H);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
-    const int v0 = 64 * hv + 16 * wave;
+    const int rg = wave / kCh, hc = wave % kCh;                 // row group, channel half
+    const int v0 = kRows * part + 16 * rg, ct0 = kTiles * hc;  // value rows v0 .., channel tiles ct0 ..
     const int64_t start = a.seq_start[n], len = a.seq_len[n], off = a.seq_off[n];
     const int64_t nch = (len + kCH - 1) / kCH;
     auto slot_of = [&](int64_t j) { return (size_t)(off + j) * (size_t)H + (size_t)h; };
     auto op_of = [&](int64_t j) { return a.ops + slot_of(j) * kBwdOps; };
     auto tok_len = [&](int64_t j) { return (int)(len - kCH * j < kCH ? len - kCH * j : kCH); };
-    const size_t srow = (size_t)chain * kBState + (size_t)(v0 + m) * kD + 4 * g;  // + 16 ct
-    f32x4 S[8];
+    const size_t srow = (size_t)chain * kBState + (size_t)(v0 + m) * kD + 16 * ct0 + 4 * g;  // + 16 e
+    f32x4 S[kTiles];
     if (role == 0) {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
+        for (int e = 0; e < kTiles; ++e) {
             if (a.h0_dtype == 2)
-                S[ct] = ld4(reinterpret_cast<const float *>(a.h0) + srow + 16 * ct);
+                S[e] = ld4(reinterpret_cast<const float *>(a.h0) + srow + 16 * e);
             else if (a.h0_dtype == 1)
-                S[ct] = ld4_bf16(reinterpret_cast<const uint16_t *>(a.h0) + srow + 16 * ct);
+                S[e] = ld4_bf16(reinterpret_cast<const uint16_t *>(a.h0) + srow + 16 * e);
             else
-                S[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                S[e] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     } else {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            S[ct] = a.dht ? ld4(a.dht + srow + 16 * ct) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < kTiles; ++e)
+            S[e] = a.dht ? ld4(a.dht + srow + 16 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // The operands of chunk it + 1 are requested while chunk it runs.
     wait_vmem();  // the initial state is in (so that no wait inside the loop is for it)
-    StageRegs rg;
+    StageRegs rg_;
     auto chunk_of = [&](int64_t it) { return role ? nch - 1 - it : it; };
     auto load = [&](int64_t it) {
         const int64_t j = chunk_of(it);
-        stage_load(a, role, hv, op_of(j), start + kCH * j, tok_len(j), h, rg, tid);
+        stage_load<kRows>(a, role, part, op_of(j), start + kCH * j, tok_len(j), h, rg_, tid);
     };
     if (nch > 0) {
         load(0);
-        stage_store(role, rg, s_st[0], tok_len(chunk_of(0)), tid);
+        stage_store<kRows>(role, rg_, s_st[0], tok_len(chunk_of(0)), tid);
     }
     __syncthreads();
     for (int64_t it = 0; it < nch; ++it) {
@@ -487,61 +505,70 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         const bool more = it + 1 < nch;
         if (more)
             load(it + 1);
-        const ChainStage &st = s_st[it & 1];
+        const ChainStage<kRows> &st = s_st[it & 1];
         const size_t sl = slot_of(j);
-        f32x4 A[8];  // A operands of the first product, all read before its MFMAs
+        f32x4 A[kTiles];  // A operands of the first product (this wave's channels), read before its MFMAs
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            A[ct] = ld4(st.A0 + m * kD + 16 * ct + 4 * g);
-        f32x4 X0, X1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            X0[i] = st.U[4 * g + i][16 * wave + m];
-        // the state before the chunk (role 0) or dL/dS after it (role 1), in the tiled layout
-        // (state_at): each store of the wave writes 256 contiguous bytes
-        float *ck = (role ? a.ckd : a.cks) + sl * kBState + (size_t)(v0 >> 4) * (8 * 256) + 16 * g + m;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int e = 0; e < kTiles; ++e)
+            A[e] = ld4(st.A0 + m * kD + 16 * (ct0 + e) + 4 * g);
+        f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
+        if (hc == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                ck[256 * ct + 64 * i] = S[ct][i];
+                X0[i] = st.U[4 * g + i][16 * rg + m];
+        // the state before the chunk (role 0) or dL/dS after it (role 1), in the tiled layout
+        // (state_at): each store of the wave writes 256 contiguous bytes
+        float *ck = (role ? a.ckd : a.cks) + sl * kBState + (size_t)(v0 >> 4) * (8 * 256) + 256 * ct0 + 16 * g + m;
+#pragma unroll
+        for (int e = 0; e < kTiles; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ck[256 * e + 64 * i] = S[e][i];
         // role 0: V' = U - W S^T;  role 1: dV' = U~ + KD D^T   (rows r = 4 g + i, column v0 + m);
-        // two accumulators (even and odd channel tiles)
+        // two accumulators (even and odd tiles), then (kCh = 2) the partner wave's half sum
 #pragma unroll
-        for (int ct = 0; ct < 8; ct += 2) {
-            X0 = mm4(A[ct], S[ct], X0);
-            X1 = mm4(A[ct + 1], S[ct + 1], X1);
+        for (int e = 0; e < kTiles; e += 2) {
+            X0 = mm4(A[e], S[e], X0);
+            X1 = mm4(A[e + 1], S[e + 1], X1);
         }
-        const f32x4 X = X0 + X1;
-        float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + (v0 >> 4) * 256 + 16 * g + m;  // (rows_at)
+        f32x4 X = X0 + X1;
+        if constexpr (kCh == 2) {
+            st4(&s_x[wave][lane][0], X);
+            __syncthreads();
+            const f32x4 other = ld4(&s_x[wave ^ 1][lane][0]);
+            X = hc == 0 ? X + other : other + X;  // the same sum in both waves
+        }
+        if (hc == 0) {
+            float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + (v0 >> 4) * 256 + 16 * g + m;  // (rows_at)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            xo[64 * i] = X[i];
+            for (int i = 0; i < 4; ++i)
+                xo[64 * i] = X[i];
+        }
         if (role == 0) {
             if (more) {  // S <- S Diag(gamma) + V'^T KD
-                f32x4 K[8], Gm[8];
+                f32x4 K[kTiles], Gm[kTiles];
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) {
-                    K[ct] = ld4(st.A1 + (16 * ct + m) * kCH + 4 * g);
-                    Gm[ct] = ld4(st.gam + 16 * ct + 4 * g);
+                for (int e = 0; e < kTiles; ++e) {
+                    K[e] = ld4(st.A1 + (16 * (ct0 + e) + m) * kCH + 4 * g);
+                    Gm[e] = ld4(st.gam + 16 * (ct0 + e) + 4 * g);
                 }
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct)
-                    S[ct] = mm4(K[ct], X, S[ct] * Gm[ct]);
+                for (int e = 0; e < kTiles; ++e)
+                    S[e] = mm4(K[e], X, S[e] * Gm[e]);
             }
         } else {  // D <- D Diag(gamma) + dO^T QG - dV'^T W
             f32x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                o[i] = st.O[4 * g + i][16 * wave + m];
+                o[i] = st.O[4 * g + i][16 * rg + m];
 #pragma unroll
-            for (int c4 = 0; c4 < 8; c4 += 4) {
+            for (int c4 = 0; c4 < kTiles; c4 += 4) {
                 f32x4 Q[4], Wt[4], Gm[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    Q[e] = ld4(st.A1 + (16 * (c4 + e) + m) * kCH + 4 * g);
-                    Wt[e] = ld4(st.A2 + (16 * (c4 + e) + m) * kCH + 4 * g);
-                    Gm[e] = ld4(st.gam + 16 * (c4 + e) + 4 * g);
+                    Q[e] = ld4(st.A1 + (16 * (ct0 + c4 + e) + m) * kCH + 4 * g);
+                    Wt[e] = ld4(st.A2 + (16 * (ct0 + c4 + e) + m) * kCH + 4 * g);
+                    Gm[e] = ld4(st.gam + 16 * (ct0 + c4 + e) + 4 * g);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -549,13 +576,13 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             }
         }
         if (more)
-            stage_store(role, rg, s_st[(it + 1) & 1], tok_len(chunk_of(it + 1)), tid);
+            stage_store<kRows>(role, rg_, s_st[(it + 1) & 1], tok_len(chunk_of(it + 1)), tid);
         __syncthreads();
     }
     if (role == 1 && a.dh0) {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            st4(a.dh0 + srow + 16 * ct, S[ct]);
+        for (int e = 0; e < kTiles; ++e)
+            st4(a.dh0 + srow + 16 * e, S[e]);
     }
 }
 
@@ -968,8 +995,11 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
             return e;
     }
     if (units > 0) {
-        // two workgroups (halves) per unit, units in groups of 8 (one per XCD)
-        hipLaunchKernelGGL(bwd_chain_kernel, dim3((unsigned)(cdiv(units, 8) * 16)), dim3(kChainThreads), 0, s, a);
+        // 2 kCh workgroups per unit, units in groups of 8 (one per XCD)
+        if (units <= kChainUnitsSplit)
+            hipLaunchKernelGGL(bwd_chain_kernel<2>, dim3((unsigned)(cdiv(units, 8) * 32)), dim3(kChainThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(bwd_chain_kernel<1>, dim3((unsigned)(cdiv(units, 8) * 16)), dim3(kChainThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
     }
