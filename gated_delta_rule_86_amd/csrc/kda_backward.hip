@@ -113,6 +113,7 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt, *dh0;
     int64_t B, T, H, N, chunks;
     const int64_t *seq_start, *seq_len, *seq_off;
+    const int32_t *status;   // the chunk table's status word (nonzero: invalid cu_seqlens)
     float *ops;              // [chunks][H][kBwdOps]
     float *cks, *ckd;        // [chunks][H][16384]: S before the chunk, dL/dS after it (state_at)
     float *xf, *xb;          // [chunks][H][2048]: V' and dL/dV' (rows_at)
@@ -900,7 +901,8 @@ __global__ __launch_bounds__(256) void bwd_head_part_kernel(BwdArgs a)
     __shared__ float s_d[2][kD], s_a[2][kD];
     const int h = blockIdx.x / kHeadSlices, slice = blockIdx.x % kHeadSlices;
     const int c = threadIdx.x & (kD - 1), half = threadIdx.x >> 7;
-    const int64_t ntok = a.B * a.T;
+    // with invalid cu_seqlens no token belongs to a sequence and dg is not written: sum nothing
+    const int64_t ntok = *a.status ? 0 : a.B * a.T;
     const int64_t t0 = ntok * slice / kHeadSlices, t1 = ntok * (slice + 1) / kHeadSlices;
     const float dt = a.dt_bias[(size_t)h * kD + c];
     float sd = 0.f, sa = 0.f;
@@ -978,6 +980,7 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.seq_start = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_start);
     a.seq_len = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_len);
     a.seq_off = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_off);
+    a.status = reinterpret_cast<const int32_t *>(ws + f.fwd.lay.off_status);
     a.ops = reinterpret_cast<float *>(ws + f.bl.off_ops);
     a.cks = reinterpret_cast<float *>(ws + f.bl.off_cks);
     a.ckd = reinterpret_cast<float *>(ws + f.bl.off_ckd);

@@ -263,6 +263,9 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int ha
  *                 initial_state (also when initial_state is NULL, i.e. zero).
  *   workspace     device scratch of at least kda_bwd_workspace_size(...) bytes, 256-byte
  *                 aligned.
+ * An invalid cu_seqlens (found on the device) makes every sequence empty, as in kda_fwd:
+ * dq, dk, dv, dg and dbeta are not written, dA_log and ddt_bias are zero, and
+ * dinitial_state = dfinal_state (or zero); kda_fwd_device_status on the workspace reports it.
  * Outputs must not overlap any input or each other (KDA_ERR_ALIAS).  Same error codes as
  * kda_fwd_ex otherwise.  Work is enqueued on `stream`; nothing is allocated.  The pass runs
  * in 16-token chunks: the state runs forwards and dL/dS backwards over the chunks of each

@@ -106,3 +106,24 @@ def test_backward_T_zero():
     torch.cuda.synchronize()
     assert torch.equal(r["dinitial_state"], dht)      # nothing happens between the two states
     assert not torch.any(r["dA_log"]) and not torch.any(r["ddt_bias"])
+
+
+def test_backward_invalid_cu_seqlens():
+    """cu_seqlens that decreases (found on the device): every sequence is empty, the status
+    word reports it, dA_log and dt_bias are zero and dL/dinitial_state = dL/dfinal_state."""
+    import torch
+    w = W.make("bwd_bad_cu", 1, 0, 2, lengths=[40, 0, 70], seed=706, state_dtype="fp32")
+    dev = torch_dev()
+    rng = np.random.default_rng(12)
+    dout = W.f32_to_bf16_bits(rng.normal(size=(w.B, w.T, w.H, 128)).astype(np.float32))
+    dht = torch.randn(w.N, w.H, 128, 128, device=dev)
+    d = {n: bf16_tensor(getattr(w, n)) for n in ("q", "k", "v", "g", "beta")}
+    cu = w.cu_seqlens.copy()
+    cu[1] = cu[2] + 1  # 41 > 40: decreasing
+    r = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, torch.from_numpy(w.A_log).to(dev),
+                torch.from_numpy(w.dt_bias).to(dev), w.lower_bound, bf16_tensor(dout),
+                state_tensor(w.initial_state), dht, torch.from_numpy(cu).to(dev))
+    torch.cuda.synchronize()
+    assert kda.device_status(r["workspace"]) == 2
+    assert not torch.any(r["dA_log"]) and not torch.any(r["ddt_bias"])
+    assert torch.equal(r["dinitial_state"], dht)
