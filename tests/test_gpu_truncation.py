@@ -146,3 +146,17 @@ def test_varlen_cuts(lb, sd):
         assert np.all(z[:, inner] == -1)
     else:
         assert np.all(z[:, inner] >= 1)
+
+
+@pytest.mark.parametrize("T,H,lb", [(65536 + 37, 1, 0.0), (65536 + 37, 1, -1.0), (32768 + 5, 2, -0.05)])
+def test_largest_cut_plans(T, H, lb):
+    """The largest plans: 256 workgroups per head (H = 1, the cut table at its full 257
+    entries) and 128 (H = 2), each run cutting the one sequence; without decay no transition
+    run stops and the scan carries the state through 255 affine steps."""
+    w = W.make(f"maxcuts_T{T}_H{H}_lb{lb}", 1, T, H, seed=760 + H, lower_bound=lb, state_dtype="fp32")
+    z, drop, cuts, P = _run(w, f"largest cut plan T={T} H={H} lb={lb}")
+    assert P == 256 // H
+    inner = [j for j in range(1, P) if cuts[j][1] > 0]
+    assert len(inner) == P - 1
+    if lb == 0.0:
+        assert np.all(z[:, inner] == -1)
