@@ -88,6 +88,13 @@ def test_backward_activation_switches(flags):
     grads_parity(w, 5 + flags, True, f"flags={flags}")
 
 
+def test_backward_many_heads():
+    """160 heads: 320 chain units (the two-workgroup split of the chain kernel), more chunk
+    workgroups than CUs."""
+    w = W.make("bwd_heads160", 1, 0, 160, lengths=[50, 20], seed=707, state_dtype="fp32")
+    grads_parity(w, 13, True, "varlen 50/20 H=160")
+
+
 def test_backward_long_chains():
     """Two chains of 2100 tokens (132 chunks of checkpoints each) with weak decay."""
     w = W.make("bwd_long", 1, 2100, 2, seed=705, lower_bound=-0.05, state_dtype="fp32")

@@ -64,6 +64,16 @@ def test_lengths_around_chunks(T):
     parity(W.make(f"T{T}", 1, T, 2, seed=300 + T), f"T={T}")
 
 
+@pytest.mark.parametrize("B,T,H,lengths", [(2, 100, 129, None), (1, 70, 256, None), (1, 0, 300, [33, 0, 50]),
+                                          (1, 0, 200, [1100, 17])])
+def test_many_heads(B, T, H, lengths):
+    """More heads than the cut plan takes (128) and than CUs (256): whole chains, one
+    workgroup per head and more workgroups than CUs; varlen with an empty sequence and with
+    one long sequence."""
+    w = W.make(f"heads{H}_{T}_{lengths}", B, T, H, lengths=lengths, seed=600 + H, state_dtype="fp32")
+    parity(w, f"B={B} T={T} H={H} lengths={lengths}")
+
+
 def test_batch_and_heads():
     parity(W.make("B3_T100_H3", 3, 100, 3, seed=301), "B=3 T=100 H=3")
 
