@@ -33,10 +33,9 @@
 //                      runs dL/dS backwards, writing D and dV' of every chunk and dL/dS_0.  The
 //                      value rows of a state are independent given the chunk operands, so two
 //                      workgroups take 64 rows each.
-//   bwd_sgrad_kernel   per chunk-head: the products with the chunk's states (dKD, dO S0,
-//                      dV' S0, dgamma, and dAqk)
-//   bwd_grad_kernel    per chunk-head: the gradients of the chunk's tokens (dq^, dk^, d log-
-//                      decay, dbeta, dv), then the l2norm, gate and sigmoid chain rules
+//   bwd_grad_kernel    per chunk-head: the products with the chunk's states (dKD, dO S0,
+//                      dV' S0, dgamma) and dAqk, the gradients of the chunk's tokens (dq^, dk^,
+//                      d log-decay, dbeta, dv), then the l2norm, gate and sigmoid chain rules
 //   bwd_head_part_kernel, bwd_head_kernel
 //                      per head: dt_bias and A_log gradients summed over all tokens (fixed
 //                      token slices, then the slices in order: deterministic)
@@ -99,7 +98,8 @@ __device__ __forceinline__ f32x4 mm_rows(const float *A, const float *B, int nk,
 
 // Layout of the per-chunk states and rows in the workspace, chosen so that every store of the
 // chain kernel (a wave's 16 value rows, four channels per lane) writes 256 contiguous bytes and
-// every read of the state-product kernel (four value rows at one channel) is one 16-byte load:
+// every read of the gradient kernel's state products (four value rows at one channel) is one
+// 16-byte load:
 //   state_at(v, c) = ((v / 16) 8 + c / 16) 256 + (c % 4) 64 + (c / 4 % 4) 16 + v % 16
 //   rows_at(r, v)  = (v / 16) 256 + (r % 4) 64 + (r / 4) 16 + v % 16     (r: row of the chunk)
 struct BwdArgs {
@@ -587,80 +587,6 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
     }
 }
 
-// ---- products with the chunk's states, one workgroup per chunk-head ----
-// dKD = V' D, G1 = dO S0, G2 = dV' S0 (fp32 [16][128] each), dgamma_c = sum_v S0[v][c] D[v][c]
-// and dAqk = lower(dO V'^T) ([16][16]), written over the chunk-head's operand block (read by
-// the chains, which have run).  No LDS: the A operands (rows of V', dV', dO) come straight
-// from memory into registers, the B operands (the states, stored [channel][value row]) too.
-constexpr int kSgThreads = 256;
-constexpr int kSgKD = 0, kSgG1 = 2048, kSgG2 = 4096, kSgGam = 6144, kSgAqk = 6272;
-static_assert(kSgAqk + kCH * kCH <= kBwdOps, "state products fit the operand block");
-
-__global__ __launch_bounds__(kSgThreads) void bwd_sgrad_kernel(BwdArgs a)
-{
-    const int64_t x = blockIdx.x / a.H;
-    const int h = (int)(blockIdx.x % a.H);
-    ChunkLoc c;
-    if (!locate_chunk(a, x, c))
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
-    const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;
-    // lane: row m of V', dV', dO at value columns 16 t + 4 g .. + 3
-    f32x4 af[8], ab[8], ao[8];
-    {
-        const int xr = 64 * (m & 3) + 16 * (m >> 2) + 4 * g;  // rows_at(m, 4 g) - rows_at(0, 0)
-        const float *pf = a.xf + sl * (kCH * kD) + xr, *pb = a.xb + sl * (kCH * kD) + xr;
-        const uint16_t *po = a.dout + ((size_t)(c.t0 + m) * (size_t)a.H + (size_t)h) * kD + 4 * g;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            af[t] = ld4(pf + 256 * t);
-            ab[t] = ld4(pb + 256 * t);
-            ao[t] = m < c.len ? ld4_bf16(po + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    float *o = a.ops + sl * kBwdOps;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {  // channel tiles 2 w + e
-        const int c0 = 16 * (2 * wave + e);
-        // state_at(16 t + 4 g, c0 + m) = 2048 t + 256 (c0 / 16) + 64 (m % 4) + 16 (m / 4) + 4 g
-        const int so = 256 * (c0 >> 4) + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
-        const float *cs = a.cks + sl * kBState + so;
-        const float *cd = a.ckd + sl * kBState + so;
-        f32x4 aKD = {0.f, 0.f, 0.f, 0.f}, aG1 = aKD, aG2 = aKD;
-        float dgp = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const f32x4 bs = ld4(cs + 2048 * t), bd = ld4(cd + 2048 * t);
-            aKD = mm4(af[t], bd, aKD);
-            aG1 = mm4(ao[t], bs, aG1);
-            aG2 = mm4(ab[t], bs, aG2);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dgp = fmaf(bs[j], bd[j], dgp);
-        }
-        dgp += __shfl_xor(dgp, 16);
-        dgp += __shfl_xor(dgp, 32);
-        if (g == 0)
-            o[kSgGam + c0 + m] = dgp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int at = (4 * g + i) * kD + c0 + m;
-            o[kSgKD + at] = aKD[i];
-            o[kSgG1 + at] = aG1[i];
-            o[kSgG2 + at] = aG2[i];
-        }
-    }
-    if (wave == 0) {  // dAqk = lower(dO V'^T): A = rows of dO, B = rows of V' (both row m here)
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            acc = mm4(ao[t], af[t], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[kSgAqk + (4 * g + i) * kCH + m] = m <= 4 * g + i ? acc[i] : 0.f;
-    }
-}
-
 // ---- gradients of one chunk-head's tokens ----
 struct GradLds {
     PrepLds p;
@@ -683,26 +609,20 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
     const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;
-    const float *sg = a.ops + sl * kBwdOps;  // the state products
-    const float *xb = a.xb + sl * (kCH * kD);
-    if (tid < kCH * kCH)
-        L.dAqk[tid >> 4][tid & 15] = sg[kSgAqk + tid];
-    // The tail's per-element inputs (D layout: wave w, channel 16 w + m, rows 4 g + i), requested
-    // now with everything else so that the tail waits for no memory.
+    const float *xf = a.xf + sl * (kCH * kD), *xb = a.xb + sl * (kCH * kD);
     const int c0 = 16 * wave, cc = c0 + m;
     const size_t tok0 = (size_t)c.t0 * (size_t)a.H + (size_t)h;  // token-head index of row 0
-    f32x4 tG1, tKD, tq, tk, tg;
+    // The tail's per-element inputs (D layout: wave w, channel 16 w + m, rows 4 g + i) and the
+    // dbeta rows' v, requested first so that nothing later waits for them.
+    f32x4 tq, tk, tg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
         const size_t at = (tok0 + (size_t)(r < c.len ? r : 0) * (size_t)a.H) * kD + (size_t)cc;
-        tG1[i] = sg[kSgG1 + r * kD + cc];
-        tKD[i] = sg[kSgKD + r * kD + cc];
         tq[i] = bbf16(a.q[at]);
         tk[i] = bbf16(a.k[at]);
         tg[i] = bbf16(a.g[at]);
     }
-    const float tdgam = sg[kSgGam + cc];
     uint32_t vraw[2] = {0u, 0u};  // v of row tid / 32 at channels 4 (tid % 32) .. + 3 (the dbeta rows)
     if ((tid >> 5) < c.len) {
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -711,12 +631,53 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         vraw[0] = w[0];
         vraw[1] = w[1];
     }
-    {  // dV' into P and G2 into Q, requested with the chunk's rows (P and Q replace them below)
+    {  // dV' into P (P replaces it below)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
         st4(&L.P[r][c4], ld4(xb + 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15)));  // (rows_at)
-        st4(&L.Q[r][c4], ld4(sg + kSgG2 + r * kD + c4));
+    }
+    // The products with the chunk's states, wave w at channels c0 .. c0 + 15 (lane (g, m): rows
+    // 4 g + i, channel cc, the D layout):  dKD = V' D and G1 = dO S0 stay in registers for the
+    // tail, G2 = dV' S0 goes to Q, dgamma_c = sum_v S0[v][c] D[v][c] is summed over the lanes
+    // of a channel; waves 0 - 3 also form dAqk = lower(dO V'^T) over value columns 32 w .. + 31.
+    // A operands: rows m of V', dV', dO at value columns 16 t + 4 g .. + 3; B operands: the
+    // states at value rows 16 t + 4 g .. + 3, channel cc (state_at).
+    f32x4 tKD = {0.f, 0.f, 0.f, 0.f}, tG1 = tKD, aG2 = tKD, aQK = tKD;
+    float tdgam = 0.f;
+    {
+        const int xr = 64 * (m & 3) + 16 * (m >> 2) + 4 * g;  // rows_at(m, 4 g)
+        const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
+        const float *cs = a.cks + sl * kBState + so, *cd = a.ckd + sl * kBState + so;
+        const uint16_t *po = a.dout + ((size_t)(c.t0 + (m < c.len ? m : 0)) * (size_t)a.H + (size_t)h) * kD + 4 * g;
+#pragma unroll 2
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 af = ld4(xf + xr + 256 * t), ab = ld4(xb + xr + 256 * t);
+            const f32x4 ao = m < c.len ? ld4_bf16(po + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 bs = ld4(cs + 2048 * t), bd = ld4(cd + 2048 * t);
+            tKD = mm4(af, bd, tKD);
+            tG1 = mm4(ao, bs, tG1);
+            aG2 = mm4(ab, bs, aG2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                tdgam = fmaf(bs[j], bd[j], tdgam);
+            if ((t >> 1) == wave)
+                aQK = mm4(ao, af, aQK);
+        }
+        tdgam += __shfl_xor(tdgam, 16);
+        tdgam += __shfl_xor(tdgam, 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            L.Q[4 * g + i][cc] = aG2[i];
+        if (wave < 4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                L.part[wave][4 * g + i][m] = aQK[i];
     }
     prep_chunk(a, c, h, p, tid);  // ends with a barrier
+    if (tid < kCH * kCH) {  // dAqk: the four partial sums, lower triangle with the diagonal
+        const int r = tid >> 4, s_ = tid & 15;
+        const float v = (L.part[0][r][s_] + L.part[1][r][s_]) + (L.part[2][r][s_] + L.part[3][r][s_]);
+        L.dAqk[r][s_] = s_ <= r ? v : 0.f;
+    }
     const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
     auto row_at = [&](int r) { return (tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)ch; };
     {  // P = T^T dV', Q = T^T dW = -T^T G2 (rows q4 .. q4 + 3, value column / channel ch); dv = beta P
@@ -1007,9 +968,6 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
             return e;
     }
     if (toks > 0) {
-        hipLaunchKernelGGL(bwd_sgrad_kernel, dim3((unsigned)slots), dim3(kSgThreads), 0, s, a);
-        if ((e = check()) != hipSuccess)
-            return e;
         hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
