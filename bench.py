@@ -147,8 +147,8 @@ def cpu_baseline(w):
                    ws.initial_state, cu_seqlens=ws.cu_seqlens)
     dt = time.perf_counter() - t0
     return {"value": ws.head_tokens / dt, "unit": "head-tokens/s", "cores": min(threads, chains),
-            "kind": "oracle", "sample": f"{sample} ({ws.head_tokens} head-tokens, {dt:.2f} s wall, "
-            f"{threads} threads for {chains} chains)"}
+            "kind": "oracle", "sample": f"{sample} ({ws.head_tokens} head-tokens, {dt:.2f} s wall; one "
+            f"thread per chain, {min(threads, chains)} of the {threads} available)"}
 
 
 def backward_bench(args, w):
