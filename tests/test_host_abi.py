@@ -224,6 +224,36 @@ def test_forward_launches_of_reference_workloads():
     assert kda.forward_launches(256, 1, 32) == 1
 
 
+def test_timed_entry_points_check_their_events():
+    """kda_fwd_timed (5 handles) and kda_fwd_recurrent_timed (3) return KDA_ERR_NULL for a
+    NULL handle array or a NULL handle among those they record, and otherwise validate their
+    arguments as kda_fwd does, before any HIP call (the fake handles are never used)."""
+    L = kda.lib()
+    a = Args(T=16)
+    base = (a.q, a.k, a.v, a.g, a.beta, a.scale, a.out, a.A_log, a.dt_bias, a.lb, a.h0, a.h0_dt,
+            a.ht, a.ht_dt, a.cu, None, a.B, a.T, a.H, a.N, a.K, a.V, a.ws, a.ws_bytes, None)
+    fake = [(1 << 33) + 256 * i for i in range(5)]
+
+    def timed(n, handles, lb=None):
+        args = list(base)
+        if lb is not None:
+            args[9] = lb
+        evs = None if handles is None else (ctypes.c_void_p * len(handles))(*handles)
+        if n == 5:
+            return L.kda_fwd_timed(*args, evs)
+        return L.kda_fwd_recurrent_timed(*args, kda.ALL_IN_KERNEL, evs)
+
+    for n in (5, 3):
+        assert timed(n, None) == 1, n
+        for i in range(n):
+            h = list(fake[:n])
+            h[i] = None
+            assert timed(n, h) == 1, (n, i)
+        assert timed(n, fake[:n], lb=0.5) == 5, n          # lower_bound out of range
+    # the recurrent entry reads only its first three handles
+    assert timed(3, fake[:3] + [None, None], lb=0.5) == 5
+
+
 def test_noalloc_rejects_sizes_beyond_its_scratch():
     """kda_fwd_noalloc checks the workspace its sizes need against its static scratch
     (KDA_NOALLOC_SCRATCH_BYTES) before any HIP call: KDA_ERR_SCRATCH, nothing launched."""
