@@ -29,11 +29,15 @@
 //                      in the forward pass) and its operands for the two chains (-W, U, KD,
 //                      U~ = lower(QG KI^T)^T dO, QG, gamma, in the layouts they are read in)
 //   bwd_chain_kernel   per (sequence, head, role, half of the value rows): role 0 runs the
-//                      state forwards over the chunks, writing S0 and V' of every chunk; role 1
-//                      runs dL/dS backwards, writing D and dV' of every chunk and dL/dS_0.  The
-//                      value rows of a state are independent given the chunk operands, so two
-//                      workgroups take 64 rows each.
-//   bwd_grad_kernel    per chunk-head: the products with the chunk's states (dKD, dO S0,
+//                      state forwards over the chunks, writing V' of every chunk and S0 of the
+//                      even chunks of the sequence; role 1 runs dL/dS backwards, writing dV' of
+//                      every chunk, D of the odd chunks and dL/dS_0.  The value rows of a state
+//                      are independent given the chunk operands, so two workgroups take 64
+//                      rows each.
+//   bwd_grad_kernel    per chunk-head: the state the chain did not store, rebuilt from the
+//                      neighbouring chunk's (D of an even chunk from the next chunk's by the
+//                      dS0 step above, S0 of an odd one from the previous chunk's by the state
+//                      step), the products with the chunk's states (dKD, dO S0,
 //                      dV' S0, dgamma) and dAqk, the gradients of the chunk's tokens (dq^, dk^,
 //                      d log-decay, dbeta, dv), then the l2norm, gate and sigmoid chain rules
 //   bwd_head_part_kernel, bwd_head_kernel
@@ -115,7 +119,8 @@ struct BwdArgs {
     const int64_t *seq_start, *seq_len, *seq_off;
     const int32_t *status;   // the chunk table's status word (nonzero: invalid cu_seqlens)
     float *ops;              // [chunks][H][kBwdOps]
-    float *cks, *ckd;        // [chunks][H][16384]: S before the chunk, dL/dS after it (state_at)
+    float *ck;               // [chunks][H][16384]: S before the chunk (even chunks of a sequence)
+                             // or dL/dS after it (odd chunks), state_at
     float *xf, *xb;          // [chunks][H][2048]: V' and dL/dV' (rows_at)
     float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
 };
@@ -517,14 +522,16 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 X0[i] = st.U[4 * g + i][16 * rg + m];
-        // the state before the chunk (role 0) or dL/dS after it (role 1), in the tiled layout
-        // (state_at): each store of the wave writes 256 contiguous bytes
-        float *ck = (role ? a.ckd : a.cks) + sl * kBState + (size_t)(v0 >> 4) * (8 * 256) + 256 * ct0 + 16 * g + m;
+        // the state before an even chunk (role 0) or dL/dS after an odd one (role 1), in the
+        // tiled layout (state_at): each store of the wave writes 256 contiguous bytes
+        if ((int)(j & 1) == role) {
+            float *ck = a.ck + sl * kBState + (size_t)(v0 >> 4) * (8 * 256) + 256 * ct0 + 16 * g + m;
 #pragma unroll
-        for (int e = 0; e < kTiles; ++e)
+            for (int e = 0; e < kTiles; ++e)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ck[256 * e + 64 * i] = S[e][i];
+                for (int i = 0; i < 4; ++i)
+                    ck[256 * e + 64 * i] = S[e][i];
+        }
         // role 0: V' = U - W S^T;  role 1: dV' = U~ + KD D^T   (rows r = 4 g + i, column v0 + m);
         // two accumulators (even and odd tiles), then (kCh = 2) the partner wave's half sum
 #pragma unroll
@@ -635,6 +642,39 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
         st4(&L.P[r][c4], ld4(xb + 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15)));  // (rows_at)
     }
+    // The chain stored one of the chunk's two states: S0 for an even chunk of the sequence, D
+    // for an odd one.  The other is rebuilt from the neighbouring chunk's stored state and
+    // operands (the steps the chain took between them):
+    //   odd chunk:             S0 = S0' Diag(gamma') + V'^T KD'   (' : the previous chunk)
+    //   even chunk, not last:  D = D'' Diag(gamma'') + dO''^T QG'' - dV''^T W''   ('' : the next)
+    //   even chunk, last:      D = dL/dS_final (zero when not given)
+    // The neighbour's rows (V', or dV'' and dO'') are staged in LDS in p.KG, p.KI, which
+    // prep_chunk fills afterwards; the barrier that publishes them comes after the first
+    // value tile's loads are out, so that one wait covers both.
+    const int64_t seq0 = a.seq_off[c.n], jl = x - seq0;
+    const int kind = (jl & 1) ? 1 : (x + 1 < a.seq_off[c.n + 1] ? 0 : 2);
+    const size_t sn = kind == 0 ? sl + (size_t)a.H : kind == 1 ? sl - (size_t)a.H : sl;  // the neighbour
+    f32x4 nb0 = {0.f, 0.f, 0.f, 0.f}, nb1 = nb0;  // B operands of the rebuild: rows 4 g + j, channel cc
+    float ngam = 0.f;                             // the neighbour's gamma at channel cc
+    if (kind != 2) {
+        const float *opn = a.ops + sn * kBwdOps;
+        const int r = tid >> 5, c4 = 4 * (tid & 31);
+        const int ro = 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15);  // rows_at(r, c4)
+        if (kind == 0) {
+            st4(&p.KG[r][c4], ld4(a.xb + sn * (kCH * kD) + ro));
+            const int64_t rem = a.seq_len[c.n] - kCH * (jl + 1);  // the next chunk's tokens
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            if (r < rem)
+                o = ld4_bf16(a.dout + ((size_t)(c.t0 + kCH + r) * (size_t)a.H + (size_t)h) * kD + c4);
+            st4(&p.KI[r][c4], o);
+            nb0 = ld4(opn + kOpQGt + cc * kCH + 4 * g);
+            nb1 = ld4(opn + kOpNegWt + cc * kCH + 4 * g);
+        } else {
+            st4(&p.KG[r][c4], ld4(a.xf + sn * (kCH * kD) + ro));
+            nb0 = ld4(opn + kOpKDt + cc * kCH + 4 * g);
+        }
+        ngam = opn[kOpGam + cc];
+    }
     // The products with the chunk's states, wave w at channels c0 .. c0 + 15 (lane (g, m): rows
     // 4 g + i, channel cc, the D layout):  dKD = V' D and G1 = dO S0 stay in registers for the
     // tail, G2 = dV' S0 goes to Q, dgamma_c = sum_v S0[v][c] D[v][c] is summed over the lanes
@@ -646,13 +686,44 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     {
         const int xr = 64 * (m & 3) + 16 * (m >> 2) + 4 * g;  // rows_at(m, 4 g)
         const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
-        const float *cs = a.cks + sl * kBState + so, *cd = a.ckd + sl * kBState + so;
+        const float *cs = a.ck + sl * kBState + so;  // the stored state
+        const float *cn = a.ck + sn * kBState + so;  // the neighbour's (kinds 0, 1)
+        const float *dh =  // dL/dS_final at value row 4 g, channel cc (kind 2)
+            a.dht ? a.dht + ((size_t)c.n * (size_t)a.H + (size_t)h) * kBState + (size_t)(4 * g) * kD + cc : nullptr;
         const uint16_t *po = a.dout + ((size_t)(c.t0 + (m < c.len ? m : 0)) * (size_t)a.H + (size_t)h) * kD + 4 * g;
-#pragma unroll 2
-        for (int t = 0; t < 8; ++t) {
+        auto tile = [&](int t, bool first) {
             const f32x4 af = ld4(xf + xr + 256 * t), ab = ld4(xb + xr + 256 * t);
             const f32x4 ao = m < c.len ? ld4_bf16(po + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 bs = ld4(cs + 2048 * t), bd = ld4(cd + 2048 * t);
+            const f32x4 sx = ld4(cs + 2048 * t);
+            const f32x4 sn_ = kind != 2 ? ld4(cn + 2048 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+            if (first && kind != 2)
+                __syncthreads();
+            f32x4 bs, bd;
+            if (kind == 1) {
+                bd = sx;
+                f32x4 nv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    nv[j] = p.KG[4 * g + j][16 * t + m];
+                bs = mm4(nv, nb0, sn_ * ngam);
+            } else {
+                bs = sx;
+                if (kind == 0) {
+                    f32x4 ndv, ndo;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ndv[j] = p.KG[4 * g + j][16 * t + m];
+                        ndo[j] = p.KI[4 * g + j][16 * t + m];
+                    }
+                    bd = mm4(ndv, nb1, mm4(ndo, nb0, sn_ * ngam));
+                } else if (dh) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        bd[i] = dh[(size_t)(16 * t + i) * kD];
+                } else {
+                    bd = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
             tKD = mm4(af, bd, tKD);
             tG1 = mm4(ao, bs, tG1);
             aG2 = mm4(ab, bs, aG2);
@@ -661,7 +732,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
                 tdgam = fmaf(bs[j], bd[j], tdgam);
             if ((t >> 1) == wave)
                 aQK = mm4(ao, af, aQK);
-        }
+        };
+        tile(0, true);
+#pragma unroll 1
+        for (int t = 1; t < 8; ++t)
+            tile(t, false);
         tdgam += __shfl_xor(tdgam, 16);
         tdgam += __shfl_xor(tdgam, 32);
 #pragma unroll
@@ -672,6 +747,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
             for (int i = 0; i < 4; ++i)
                 L.part[wave][4 * g + i][m] = aQK[i];
     }
+    if (kind != 2)
+        __syncthreads();  // the staged rows are read before prep_chunk overwrites them
     prep_chunk(a, c, h, p, tid);  // ends with a barrier
     if (tid < kCH * kCH) {  // dAqk: the four partial sums, lower triangle with the diagonal
         const int r = tid >> 4, s_ = tid & 15;
@@ -943,8 +1020,7 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.seq_off = reinterpret_cast<const int64_t *>(ws + f.fwd.lay.off_seq_off);
     a.status = reinterpret_cast<const int32_t *>(ws + f.fwd.lay.off_status);
     a.ops = reinterpret_cast<float *>(ws + f.bl.off_ops);
-    a.cks = reinterpret_cast<float *>(ws + f.bl.off_cks);
-    a.ckd = reinterpret_cast<float *>(ws + f.bl.off_ckd);
+    a.ck = reinterpret_cast<float *>(ws + f.bl.off_ck);
     a.xf = reinterpret_cast<float *>(ws + f.bl.off_xf);
     a.xb = reinterpret_cast<float *>(ws + f.bl.off_xb);
     a.hpart = reinterpret_cast<float *>(ws + f.bl.off_hpart);

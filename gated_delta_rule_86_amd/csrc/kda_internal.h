@@ -179,11 +179,12 @@ struct FwdArgs {
 };
 
 // Workspace of the backward pass: the chunk table (as the forward pass lays it out, up to
-// the cut-plan states, which the backward pass does not use), then per chunk-head (chunk x of the head's chunk list, slot x H + h) the chain
-// kernels' operand block (kBwdOps fp32), the state before the chunk and dL/dS after it (fp32
-// 128 x 128 each, in a tiled layout of the backward kernels), the chunk's corrected values
-// V' and their gradient (fp32 16 x 128 each, tiled likewise); and the per-head gradient partial sums (fp32
-// [H][kHeadSlices][2][128]).
+// the cut-plan states, which the backward pass does not use), then per chunk-head (chunk x of
+// the head's chunk list, slot x H + h) the chain kernels' operand block (kBwdOps fp32), one
+// state (fp32 128 x 128, in a tiled layout of the backward kernels: the state before the chunk
+// for the even chunks of a sequence, dL/dS after it for the odd ones), the chunk's corrected
+// values V' and their gradient (fp32 16 x 128 each, tiled likewise); and the per-head gradient
+// partial sums (fp32 [H][kHeadSlices][2][128]).
 constexpr int kHeadSlices = 64;  // token slices of the backward pass's per-head gradient sums
 // operand block of one chunk-head: -W, U, KD^T, KD, U~, QG^T, -W^T (2048 fp32 each), gamma (128)
 constexpr int kBwdOps = 7 * kCH * kD + kD;
@@ -191,7 +192,7 @@ constexpr int kBwdOps = 7 * kCH * kD + kD;
 struct BwdLayout {
     Layout tab;
     int64_t chunks;  // bound on the chunk count of a head (the slots per head)
-    size_t off_ops, off_cks, off_ckd, off_xf, off_xb, off_hpart;
+    size_t off_ops, off_ck, off_xf, off_xb, off_hpart;
     size_t total;
 };
 
@@ -209,8 +210,7 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
         return o;
     };
     L->off_ops = take(ch * kBwdOps * sizeof(float));
-    L->off_cks = take(ch * state);
-    L->off_ckd = take(ch * state);
+    L->off_ck = take(ch * state);
     L->off_xf = take(ch * kCH * kD * sizeof(float));
     L->off_xb = take(ch * kCH * kD * sizeof(float));
     L->off_hpart = take((size_t)H * kHeadSlices * 2 * kD * sizeof(float));
