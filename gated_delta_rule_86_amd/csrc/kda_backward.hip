@@ -162,21 +162,41 @@ struct PrepLds {
     float beta[kCH], rq[kCH], rk[kCH], gam[kD];     // beta; 1/|q|, 1/|k| (1 without the l2norm)
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 widen_bf16(u32x2 w)
+{
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xffff0000u)};
+}
+// The chunk's raw bf16 rows as prep_chunk takes them: thread -> token r = tid / 32, channels
+// 4 (tid % 32) .. + 3 of k, q, g, v, and beta of the row (raw bits, so that nothing waits for
+// them until they are used; rows past the chunk's tokens zero).
+struct RawRows {
+    u32x2 k, q, g, v;
+    uint32_t beta;
+};
+__device__ __forceinline__ RawRows load_rows(const BwdArgs &a, const ChunkLoc &c, int h, int tid)
+{
+    const int r = tid >> 5, c4 = 4 * (tid & 31);
+    RawRows w = {u32x2{0u, 0u}, u32x2{0u, 0u}, u32x2{0u, 0u}, u32x2{0u, 0u}, 0u};
+    if (r < c.len) {
+        const size_t ti = (size_t)(c.t0 + r) * (size_t)a.H + (size_t)h;
+        w.k = *reinterpret_cast<const u32x2 *>(a.k + ti * kD + c4);
+        w.q = *reinterpret_cast<const u32x2 *>(a.q + ti * kD + c4);
+        w.g = *reinterpret_cast<const u32x2 *>(a.g + ti * kD + c4);
+        w.v = *reinterpret_cast<const u32x2 *>(a.v + ti * kD + c4);
+        w.beta = a.beta[ti];
+    }
+    return w;
+}
+
 // kGradThreads threads; ends with a barrier.
-__device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &p, int tid)
+__device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &p, int tid, const RawRows &raw)
 {
     {  // the chunk's rows, activated: thread -> token r = tid / 32, channels c4 = 4 (tid % 32) .. + 3
         const int r = tid >> 5, c4 = 4 * (tid & 31);
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, gg = kk, vv = kk;
-        float braw = 0.f;
-        if (r < c.len) {
-            const size_t ti = (size_t)(c.t0 + r) * (size_t)a.H + (size_t)h;
-            kk = ld4_bf16(a.k + ti * kD + c4);
-            qq = ld4_bf16(a.q + ti * kD + c4);
-            gg = ld4_bf16(a.g + ti * kD + c4);
-            vv = ld4_bf16(a.v + ti * kD + c4);
-            braw = bbf16(a.beta[ti]);
-        }
+        const f32x4 kk = widen_bf16(raw.k), qq = widen_bf16(raw.q), gg = widen_bf16(raw.g), vv = widen_bf16(raw.v);
+        const float braw = bbf16((uint16_t)raw.beta);
         // l2norm over the 128 channels of the row (32 lanes), eps 1e-6
         float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -332,7 +352,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
         if (r >= c.len)
             od[j] = 0;
     }
-    prep_chunk(a, c, h, p, tid);
+    prep_chunk(a, c, h, p, tid, load_rows(a, c, h, tid));
     float *o = a.ops + ((size_t)x * (size_t)a.H + (size_t)h) * kBwdOps;
     {  // U~ = lower(QG KI^T)^T dO: wave w takes value columns 16 w .. + 15
         f32x4 at, ob;
@@ -600,12 +620,12 @@ struct GradLds {
     float P[kCH][kP], Q[kCH][kP];  // T^T dV' and T^T dW; P then holds db
     float dA[kCH][kQ4], dAqk[kCH][kQ4];  // rows 16-byte aligned (MFMA A operands)
     union {
-        float rowdot[kGradThreads / 64][kCH][2];  // per wavefront (16 channels): q^ . dq^, k^ . dk^ per row
+        float rowdot[kCH][kGradThreads / 64][2];  // per row and wavefront (16 channels): q^ . dq^, k^ . dk^
         float part[4][kCH][kCH];                  // dA: partial sums of four wavefronts
     };
 };
 
-__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
+__global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4))) void bwd_grad_kernel(BwdArgs a)
 {
     __shared__ __attribute__((aligned(16))) GradLds L;
     PrepLds &p = L.p;
@@ -630,14 +650,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         tk[i] = bbf16(a.k[at]);
         tg[i] = bbf16(a.g[at]);
     }
-    uint32_t vraw[2] = {0u, 0u};  // v of row tid / 32 at channels 4 (tid % 32) .. + 3 (the dbeta rows)
-    if ((tid >> 5) < c.len) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(a.v + (tok0 + (size_t)(tid >> 5) * (size_t)a.H) * kD +
-                                                         4 * (tid & 31));
-        vraw[0] = w[0];
-        vraw[1] = w[1];
-    }
+    const RawRows raw = load_rows(a, c, h, tid);  // prep_chunk's rows; v also for the dbeta rows
     {  // dV' into P (P replaces it below)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
         st4(&L.P[r][c4], ld4(xb + 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15)));  // (rows_at)
@@ -648,9 +661,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     //   odd chunk:             S0 = S0' Diag(gamma') + V'^T KD'   (' : the previous chunk)
     //   even chunk, not last:  D = D'' Diag(gamma'') + dO''^T QG'' - dV''^T W''   ('' : the next)
     //   even chunk, last:      D = dL/dS_final (zero when not given)
-    // The neighbour's rows (V', or dV'' and dO'') are staged in LDS in p.KG, p.KI, which
-    // prep_chunk fills afterwards; the barrier that publishes them comes after the first
-    // value tile's loads are out, so that one wait covers both.
     const int64_t seq0 = a.seq_off[c.n], jl = x - seq0;
     const int kind = (jl & 1) ? 1 : (x + 1 < a.seq_off[c.n + 1] ? 0 : 2);
     const size_t sn = kind == 0 ? sl + (size_t)a.H : kind == 1 ? sl - (size_t)a.H : sl;  // the neighbour
@@ -658,22 +668,37 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     float ngam = 0.f;                             // the neighbour's gamma at channel cc
     if (kind != 2) {
         const float *opn = a.ops + sn * kBwdOps;
-        const int r = tid >> 5, c4 = 4 * (tid & 31);
-        const int ro = 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15);  // rows_at(r, c4)
         if (kind == 0) {
-            st4(&p.KG[r][c4], ld4(a.xb + sn * (kCH * kD) + ro));
-            const int64_t rem = a.seq_len[c.n] - kCH * (jl + 1);  // the next chunk's tokens
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-            if (r < rem)
-                o = ld4_bf16(a.dout + ((size_t)(c.t0 + kCH + r) * (size_t)a.H + (size_t)h) * kD + c4);
-            st4(&p.KI[r][c4], o);
             nb0 = ld4(opn + kOpQGt + cc * kCH + 4 * g);
             nb1 = ld4(opn + kOpNegWt + cc * kCH + 4 * g);
         } else {
-            st4(&p.KG[r][c4], ld4(a.xf + sn * (kCH * kD) + ro));
             nb0 = ld4(opn + kOpKDt + cc * kCH + 4 * g);
         }
         ngam = opn[kOpGam + cc];
+    }
+    // Rows staged in LDS (the space prep_chunk fills afterwards), row-major with rows padded to
+    // kRS floats so that 16 lanes reading 16 rows hit distinct banks: the chunk's V', dO and dV'
+    // and the neighbour's rows (V' or dV'', and dO'').  Only the two state tiles per step are
+    // read from global memory in the loop below, requested three steps ahead.
+    constexpr int kRS = kD + 4;
+    float *const sV = &p.KG[0][0], *const sO = sV + kCH * kRS, *const sD = sO + kCH * kRS;
+    float *const nX = sD + kCH * kRS, *const nO = nX + kCH * kRS;
+    static_assert(5 * kCH * kRS <= 6 * kCH * kP, "staging fits in KG .. U");
+    {
+        const int r = tid >> 5, c4 = 4 * (tid & 31);
+        const int ro = 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15);  // rows_at(r, c4)
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        st4(sV + r * kRS + c4, ld4(xf + ro));
+        st4(sD + r * kRS + c4, ld4(xb + ro));
+        st4(sO + r * kRS + c4, r < c.len ? ld4_bf16(a.dout + (tok0 + (size_t)r * (size_t)a.H) * kD + c4) : z);
+        if (kind == 0) {
+            const int64_t rem = a.seq_len[c.n] - kCH * (jl + 1);  // the next chunk's tokens
+            st4(nX + r * kRS + c4, ld4(a.xb + sn * (kCH * kD) + ro));
+            st4(nO + r * kRS + c4,
+                r < rem ? ld4_bf16(a.dout + ((size_t)(c.t0 + kCH + r) * (size_t)a.H + (size_t)h) * kD + c4) : z);
+        } else if (kind == 1) {
+            st4(nX + r * kRS + c4, ld4(a.xf + sn * (kCH * kD) + ro));
+        }
     }
     // The products with the chunk's states, wave w at channels c0 .. c0 + 15 (lane (g, m): rows
     // 4 g + i, channel cc, the D layout):  dKD = V' D and G1 = dO S0 stay in registers for the
@@ -684,46 +709,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
     f32x4 tKD = {0.f, 0.f, 0.f, 0.f}, tG1 = tKD, aG2 = tKD, aQK = tKD;
     float tdgam = 0.f;
     {
-        const int xr = 64 * (m & 3) + 16 * (m >> 2) + 4 * g;  // rows_at(m, 4 g)
         const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
         const float *cs = a.ck + sl * kBState + so;  // the stored state
         const float *cn = a.ck + sn * kBState + so;  // the neighbour's (kinds 0, 1)
-        const float *dh =  // dL/dS_final at value row 4 g, channel cc (kind 2)
-            a.dht ? a.dht + ((size_t)c.n * (size_t)a.H + (size_t)h) * kBState + (size_t)(4 * g) * kD + cc : nullptr;
-        const uint16_t *po = a.dout + ((size_t)(c.t0 + (m < c.len ? m : 0)) * (size_t)a.H + (size_t)h) * kD + 4 * g;
-        auto tile = [&](int t, bool first) {
-            const f32x4 af = ld4(xf + xr + 256 * t), ab = ld4(xb + xr + 256 * t);
-            const f32x4 ao = m < c.len ? ld4_bf16(po + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 sx = ld4(cs + 2048 * t);
-            const f32x4 sn_ = kind != 2 ? ld4(cn + 2048 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
-            if (first && kind != 2)
-                __syncthreads();
-            f32x4 bs, bd;
-            if (kind == 1) {
-                bd = sx;
-                f32x4 nv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    nv[j] = p.KG[4 * g + j][16 * t + m];
-                bs = mm4(nv, nb0, sn_ * ngam);
-            } else {
-                bs = sx;
-                if (kind == 0) {
-                    f32x4 ndv, ndo;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ndv[j] = p.KG[4 * g + j][16 * t + m];
-                        ndo[j] = p.KI[4 * g + j][16 * t + m];
-                    }
-                    bd = mm4(ndv, nb1, mm4(ndo, nb0, sn_ * ngam));
-                } else if (dh) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        bd[i] = dh[(size_t)(16 * t + i) * kD];
-                } else {
-                    bd = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
+        // one 16-row step t: the states at value rows 16 t .. + 15 (bs = S0, bd = D)
+        auto prod = [&](int t, f32x4 bs, f32x4 bd) {
+            const int ra = m * kRS + 16 * t + 4 * g;
+            const f32x4 af = ld4(sV + ra), ab = ld4(sD + ra), ao = ld4(sO + ra);
             tKD = mm4(af, bd, tKD);
             tG1 = mm4(ao, bs, tG1);
             aG2 = mm4(ab, bs, aG2);
@@ -733,10 +725,44 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
             if ((t >> 1) == wave)
                 aQK = mm4(ao, af, aQK);
         };
-        tile(0, true);
+        // the neighbour's rows 4 g + j at value column 16 t + m
+        auto nrow = [&](const float *X, int t) {
+            f32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = X[(4 * g + j) * kRS + 16 * t + m];
+            return v;
+        };
+        if (kind == 2) {
+            const float *dh =  // dL/dS_final at value row 4 g, channel cc
+                a.dht ? a.dht + ((size_t)c.n * (size_t)a.H + (size_t)h) * kBState + (size_t)(4 * g) * kD + cc : nullptr;
+            __syncthreads();
 #pragma unroll 1
-        for (int t = 1; t < 8; ++t)
-            tile(t, false);
+            for (int t = 0; t < 8; ++t) {
+                f32x4 bd = {0.f, 0.f, 0.f, 0.f};
+                if (dh)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        bd[i] = dh[(size_t)(16 * t + i) * kD];
+                prod(t, ld4(cs + 2048 * t), bd);
+            }
+        } else {
+            f32x4 x0 = ld4(cs), n0 = ld4(cn), x1 = ld4(cs + 2048), n1 = ld4(cn + 2048);
+            __syncthreads();  // the staged rows
+#pragma unroll 1
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 sx = x0, sy = n0;
+                const int tn = t + 2 < 8 ? t + 2 : 7;  // (the last two steps load tile 7 again)
+                x0 = x1;
+                n0 = n1;
+                x1 = ld4(cs + 2048 * tn);
+                n1 = ld4(cn + 2048 * tn);
+                if (kind == 1)
+                    prod(t, mm4(nrow(nX, t), nb0, sy * ngam), sx);
+                else
+                    prod(t, sx, mm4(nrow(nX, t), nb1, mm4(nrow(nO, t), nb0, sy * ngam)));
+            }
+        }
         tdgam += __shfl_xor(tdgam, 16);
         tdgam += __shfl_xor(tdgam, 32);
 #pragma unroll
@@ -747,9 +773,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
             for (int i = 0; i < 4; ++i)
                 L.part[wave][4 * g + i][m] = aQK[i];
     }
-    if (kind != 2)
-        __syncthreads();  // the staged rows are read before prep_chunk overwrites them
-    prep_chunk(a, c, h, p, tid);  // ends with a barrier
+    __syncthreads();  // the staged rows are read before prep_chunk overwrites them
+    prep_chunk(a, c, h, p, tid, raw);  // ends with a barrier
     if (tid < kCH * kCH) {  // dAqk: the four partial sums, lower triangle with the diagonal
         const int r = tid >> 4, s_ = tid & 15;
         const float v = (L.part[0][r][s_] + L.part[1][r][s_]) + (L.part[2][r][s_] + L.part[3][r][s_]);
@@ -798,8 +823,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         const int r = tid >> 5, part = tid & 31;
         float s = 0.f;
         if (r < c.len) {
-            const f32x4 vv = {__uint_as_float(vraw[0] << 16), __uint_as_float(vraw[0] & 0xffff0000u),
-                              __uint_as_float(vraw[1] << 16), __uint_as_float(vraw[1] & 0xffff0000u)};
+            const f32x4 vv = widen_bf16(raw.v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int cc = 4 * part + e;
@@ -873,8 +897,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
         if (m == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                L.rowdot[wave][4 * g + i][0] = pq[i];
-                L.rowdot[wave][4 * g + i][1] = pk[i];
+                L.rowdot[4 * g + i][wave][0] = pq[i];
+                L.rowdot[4 * g + i][wave][1] = pk[i];
             }
         __syncthreads();
     }
@@ -914,9 +938,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs a)
             if (l2_in) {
                 float dotq = 0.f, dotk = 0.f;
 #pragma unroll
-                for (int w = 0; w < kGradThreads / 64; ++w) {
-                    dotq += L.rowdot[w][r][0];
-                    dotk += L.rowdot[w][r][1];
+                for (int w = 0; w < kGradThreads / 64; w += 2) {
+                    const f32x4 d = ld4(&L.rowdot[r][w][0]);  // waves w, w + 1
+                    dotq += d[0];
+                    dotk += d[1];
+                    dotq += d[2];
+                    dotk += d[3];
                 }
                 dq = (dq - qh[i] * dotq) * p.rq[r];
                 dk = (dk - kh[i] * dotk) * p.rk[r];
