@@ -156,7 +156,7 @@ __device__ bool locate_chunk(const BwdArgs &a, int64_t x, ChunkLoc &c)
 // quantity of the real rows as it is and gamma the decay up to the last real token.  KD is
 // not kept: KD = KI gamma.
 struct PrepLds {
-    float KG[kCH][kP], KI[kCH][kP], QG[kCH][kP], B[kCH][kP];  // B: cumulative log-decay b
+    float KG[kCH][kP], KI[kCH][kP], QG[kCH][kP], B[kCH][kP];  // B: the log-decay, then Gamma = e^b
     float W[kCH][kP], U[kCH][kP];
     float T[kCH][kQ], M[kCH][kQ], Aqk[kCH][kQ];  // T, KG KI^T, lower(QG KI^T)
     float beta[kCH], rq[kCH], rk[kCH], gam[kD];     // beta; 1/|q|, 1/|k| (1 without the l2norm)
@@ -261,8 +261,9 @@ __device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = r0 + i;
-            const float b = off + l[i], G = expf(b), Gi = expf(-b), k = p.KG[r][ch];
-            p.B[r][ch] = b;
+            // (b >= 16 lower_bound >= -80: Gamma and 1/Gamma are normal fp32 numbers)
+            const float b = off + l[i], G = expf(b), Gi = __builtin_amdgcn_rcpf(G), k = p.KG[r][ch];
+            p.B[r][ch] = G;
             p.KG[r][ch] = k * G;
             p.KI[r][ch] = k * Gi;
             p.QG[r][ch] = a.scale * p.QG[r][ch] * G;
@@ -310,23 +311,23 @@ __device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &
             p.T[r][s] = t[r];
     }
     __syncthreads();
-    {  // W = T diag(beta) KG, U = T diag(beta) V: thread -> channel tid % 128, rows 4 (tid / 128) ..
-        const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
-        float w[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    {  // W = T diag(beta) KG, U = T diag(beta) V on the MFMA: wave w takes columns 16 w + m (D
+       // layout, rows 4 g + i)
+        const int cc = 16 * wave + m;
+        f32x4 tr, bk, bv;
 #pragma unroll
-        for (int s = 0; s < kCH; ++s) {
-            const float bk = p.beta[s] * p.KG[s][ch], bv = p.beta[s] * p.U[s][ch];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                w[i] = fmaf(p.T[q4 + i][s], bk, w[i]);
-                u[i] = fmaf(p.T[q4 + i][s], bv, u[i]);
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int s = 4 * g + j;
+            tr[j] = p.T[m][s];  // A operand: T[m][4 g + j]
+            bk[j] = p.beta[s] * p.KG[s][cc];
+            bv[j] = p.beta[s] * p.U[s][cc];
         }
+        const f32x4 w = mm4(tr, bk, f32x4{0.f, 0.f, 0.f, 0.f}), u = mm4(tr, bv, f32x4{0.f, 0.f, 0.f, 0.f});
         __syncthreads();  // every column of v is read before U replaces it
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p.W[q4 + i][ch] = w[i];
-            p.U[q4 + i][ch] = u[i];
+            p.W[4 * g + i][cc] = w[i];
+            p.U[4 * g + i][cc] = u[i];
         }
     }
     __syncthreads();
@@ -676,6 +677,12 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         }
         ngam = opn[kOpGam + cc];
     }
+    // The first two state tiles of the loop below, requested ahead of the staging loads (for the
+    // last chunk of a sequence, kind 2, the neighbour's are its own and go unused).
+    const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
+    const float *cs = a.ck + sl * kBState + so;  // the stored state
+    const float *cn = a.ck + sn * kBState + so;  // the neighbour's
+    f32x4 x0 = ld4(cs), n0 = ld4(cn), x1 = ld4(cs + 2048), n1 = ld4(cn + 2048);
     // Rows staged in LDS (the space prep_chunk fills afterwards), row-major with rows padded to
     // kRS floats so that 16 lanes reading 16 rows hit distinct banks: the chunk's V', dO and dV'
     // and the neighbour's rows (V' or dV'', and dO'').  Only the two state tiles per step are
@@ -709,9 +716,6 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     f32x4 tKD = {0.f, 0.f, 0.f, 0.f}, tG1 = tKD, aG2 = tKD, aQK = tKD;
     float tdgam = 0.f;
     {
-        const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
-        const float *cs = a.ck + sl * kBState + so;  // the stored state
-        const float *cn = a.ck + sn * kBState + so;  // the neighbour's (kinds 0, 1)
         // one 16-row step t: the states at value rows 16 t .. + 15 (bs = S0, bd = D)
         auto prod = [&](int t, f32x4 bs, f32x4 bd) {
             const int ra = m * kRS + 16 * t + 4 * g;
@@ -747,7 +751,6 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
                 prod(t, ld4(cs + 2048 * t), bd);
             }
         } else {
-            f32x4 x0 = ld4(cs), n0 = ld4(cn), x1 = ld4(cs + 2048), n1 = ld4(cn + 2048);
             __syncthreads();  // the staged rows
 #pragma unroll 1
             for (int t = 0; t < 8; ++t) {
@@ -780,27 +783,24 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         const float v = (L.part[0][r][s_] + L.part[1][r][s_]) + (L.part[2][r][s_] + L.part[3][r][s_]);
         L.dAqk[r][s_] = s_ <= r ? v : 0.f;
     }
-    const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
-    auto row_at = [&](int r) { return (tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)ch; };
-    {  // P = T^T dV', Q = T^T dW = -T^T G2 (rows q4 .. q4 + 3, value column / channel ch); dv = beta P
-        float P[4] = {0.f, 0.f, 0.f, 0.f}, Q[4] = {0.f, 0.f, 0.f, 0.f};
+    {  // P = T^T dV', Q = T^T dW = -T^T G2 on the MFMA: wave w takes columns cc = 16 w + m (D
+       // layout, rows 4 g + i); dv = beta P
+        f32x4 tt, bp, bq;
 #pragma unroll
-        for (int s = 0; s < kCH; ++s) {
-            const float b_ = L.P[s][ch], g2 = L.Q[s][ch];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                P[i] = fmaf(p.T[s][q4 + i], b_, P[i]);
-                Q[i] = fmaf(-p.T[s][q4 + i], g2, Q[i]);
-            }
+        for (int j = 0; j < 4; ++j) {
+            tt[j] = p.T[4 * g + j][m];  // A operand: (T^T)[m][4 g + j]
+            bp[j] = L.P[4 * g + j][cc];
+            bq[j] = -L.Q[4 * g + j][cc];
         }
+        const f32x4 P = mm4(tt, bp, f32x4{0.f, 0.f, 0.f, 0.f}), Q = mm4(tt, bq, f32x4{0.f, 0.f, 0.f, 0.f});
         __syncthreads();  // every column of dV' and G2 is read
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = q4 + i;
-            L.P[r][ch] = P[i];
-            L.Q[r][ch] = Q[i];
+            const int r = 4 * g + i;
+            L.P[r][cc] = P[i];
+            L.Q[r][cc] = Q[i];
             if (r < c.len)
-                a.dv[row_at(r)] = p.beta[r] * P[i];
+                a.dv[(tok0 + (size_t)r * (size_t)a.H) * kD + (size_t)cc] = p.beta[r] * P[i];
         }
     }
     __syncthreads();
@@ -873,7 +873,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
         const float dKG = p.beta[r] * sKG[i], dKD = tKD[i];
-        const float b = p.B[r][cc], G = expf(b), Gi = expf(-b);
+        const float G = p.B[r][cc], Gi = __builtin_amdgcn_rcpf(G);
         const float kd = p.KI[r][cc] * gam;
         db[i] = dKG * p.KG[r][cc] - sKI[i] * p.KI[r][cc] + sQG[i] * p.QG[r][cc] - dKD * kd;
         eKD = fmaf(dKD, kd, eKD);
@@ -928,7 +928,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
             const float gc = tg[i];
             float dgv;
             if (gate_in) {
-                const float sgm = 1.0f / (1.0f + expf(-eA * (gc + dtb)));
+                const float sgm = __builtin_amdgcn_rcpf(1.0f + expf(-eA * (gc + dtb)));
                 dgv = run * a.lower_bound * sgm * (1.0f - sgm) * eA;
             } else {
                 dgv = (gc > a.lower_bound && gc < 0.f) ? run : 0.f;
