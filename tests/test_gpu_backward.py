@@ -88,6 +88,14 @@ def test_backward_activation_switches(flags):
     grads_parity(w, 5 + flags, True, f"flags={flags}")
 
 
+@pytest.mark.parametrize("B,H", [(2, 16), (4, 16), (5, 13)])
+def test_backward_chain_splits(B, H):
+    """2 B H (chain, role) units: 64 and 128 (the chain kernel splits each unit's channels over
+    two waves, up to 128 units), 130 (no split)."""
+    w = W.make(f"bwd_split{B}x{H}", B, 40, H, seed=720 + B, state_dtype="fp32")
+    grads_parity(w, 20 + B, True, f"B={B} T=40 H={H}: {2 * B * H} chain units")
+
+
 def test_backward_many_heads():
     """160 heads: 320 chain units (the two-workgroup split of the chain kernel), more chunk
     workgroups than CUs."""
