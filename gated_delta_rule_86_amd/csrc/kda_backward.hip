@@ -476,7 +476,10 @@ template <int kCh>
 __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 {
     constexpr int kRows = 64 / kCh, kTiles = 8 / kCh, kParts = 2 * kCh;
-    __shared__ __attribute__((aligned(16))) ChainStage<kRows> s_st[2];
+    // stage buffers: one where the chains are many (kCh = 1: 33 KB of LDS, so that three
+    // workgroups fit a CU, at the price of a barrier before each refill), two otherwise
+    constexpr int kSt = kCh == 1 ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) ChainStage<kRows> s_st[kSt];
     __shared__ __attribute__((aligned(16))) float s_x[kCh == 2 ? kChainThreads / 64 : 1][64][4];  // half sums
     const int64_t bid = blockIdx.x;
     const int xcd = (int)(bid & 7);
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         const bool more = it + 1 < nch;
         if (more)
             load(it + 1);
-        const ChainStage<kRows> &st = s_st[it & 1];
+        const ChainStage<kRows> &st = s_st[kSt == 1 ? 0 : (it & 1)];
         const size_t sl = slot_of(j);
         f32x4 A[kTiles];  // A operands of the first product (this wave's channels), read before its MFMAs
 #pragma unroll
@@ -604,8 +607,10 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
                     S[c4 + e] = mm4(Wt[e], X, mm4(Q[e], o, S[c4 + e] * Gm[e]));
             }
         }
+        if (kSt == 1)
+            __syncthreads();  // every wave has read the stage of chunk it
         if (more)
-            stage_store<kRows>(role, rg_, s_st[(it + 1) & 1], tok_len(chunk_of(it + 1)), tid);
+            stage_store<kRows>(role, rg_, s_st[kSt == 1 ? 0 : ((it + 1) & 1)], tok_len(chunk_of(it + 1)), tid);
         __syncthreads();
     }
     if (role == 1 && a.dh0) {
