@@ -60,8 +60,7 @@ constexpr int kQ4 = kCH + 4;       // the same, rows 16-byte aligned
 constexpr int kGradThreads = 512;  // bwd_ops_kernel, bwd_grad_kernel
 constexpr int kChainThreads = 256; // bwd_chain_kernel: 4 wavefronts of 16 value rows
 // operand block of a chunk-head (kBwdOps floats)
-constexpr int kOpNegW = 0, kOpU = 2048, kOpKDt = 4096, kOpKD = 6144, kOpUt = 8192, kOpQGt = 10240,
-              kOpNegWt = 12288, kOpGam = 14336;
+constexpr int kOpNegW = 0, kOpU = 2048, kOpKD = 4096, kOpUt = 6144, kOpQGt = 8192, kOpGam = 10240;
 static_assert(kOpGam + kD == kBwdOps, "operand block layout");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -369,20 +368,17 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
     }
     const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
     const float gam = p.gam[ch];
-    f32x4 kd, qg, nw;
+    f32x4 kd, qg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = q4 + i;
         kd[i] = p.KI[r][ch] * gam;
         qg[i] = p.QG[r][ch];
-        nw[i] = -p.W[r][ch];
-        o[kOpNegW + r * kD + ch] = nw[i];
+        o[kOpNegW + r * kD + ch] = -p.W[r][ch];
         o[kOpU + r * kD + ch] = p.U[r][ch];
         o[kOpKD + r * kD + ch] = kd[i];
     }
-    st4(o + kOpKDt + ch * kCH + q4, kd);
     st4(o + kOpQGt + ch * kCH + q4, qg);
-    st4(o + kOpNegWt + ch * kCH + q4, nw);
     if (tid < kD)
         o[kOpGam + tid] = p.gam[tid];
 }
@@ -419,13 +415,20 @@ __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int part,
                                            int h, StageRegs &r, int tid)
 {
     constexpr int kQ4 = kRows / 4;  // float4 columns of U, O
+    // the transposed operands (role 0: KD^T, role 1: -W^T) from the row-major arrays: thread ->
+    // channel tid % 128, rows 4 (tid / 128 + 2 e) .. + 3, four loads that 64 lanes coalesce
+    const int tc = tid & (kD - 1), tr = 4 * (tid >> 7);
+    auto col4 = [&](const float *m_, int e) {
+        const float *q = m_ + (tr + 8 * e) * kD + tc;
+        return f32x4{q[0], q[kD], q[2 * kD], q[3 * kD]};
+    };
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int f = 4 * (tid + kChainThreads * e);
         r.a0[e] = ld4(op + (role ? kOpKD : kOpNegW) + f);
-        r.a1[e] = ld4(op + (role ? kOpQGt : kOpKDt) + f);
+        r.a1[e] = role ? ld4(op + kOpQGt + f) : col4(op + kOpKD, e);
         if (role)
-            r.a2[e] = ld4(op + kOpNegWt + f);
+            r.a2[e] = col4(op + kOpNegW, e);
     }
     const int row = (tid / kQ4) & 15, c4 = 4 * (tid % kQ4);  // (kRows = 32: threads 128 .. repeat)
     r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + kRows * part + c4);
@@ -443,13 +446,14 @@ template <int kRows>
 __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainStage<kRows> &st, int len, int tid)
 {
     constexpr int kQ4 = kRows / 4;
+    const int tc = tid & (kD - 1), tr = 4 * (tid >> 7);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int f = 4 * (tid + kChainThreads * e);
         st4(st.A0 + f, r.a0[e]);
-        st4(st.A1 + f, r.a1[e]);
+        st4(st.A1 + (role ? f : tc * kCH + tr + 8 * e), r.a1[e]);
         if (role)
-            st4(st.A2 + f, r.a2[e]);
+            st4(st.A2 + tc * kCH + tr + 8 * e, r.a2[e]);
     }
     if (tid < kCH * kQ4) {
         const int row = tid / kQ4, c4 = 4 * (tid % kQ4);
@@ -676,9 +680,13 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         const float *opn = a.ops + sn * kBwdOps;
         if (kind == 0) {
             nb0 = ld4(opn + kOpQGt + cc * kCH + 4 * g);
-            nb1 = ld4(opn + kOpNegWt + cc * kCH + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                nb1[j] = opn[kOpNegW + (4 * g + j) * kD + cc];
         } else {
-            nb0 = ld4(opn + kOpKDt + cc * kCH + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                nb0[j] = opn[kOpKD + (4 * g + j) * kD + cc];
         }
         ngam = opn[kOpGam + cc];
     }
