@@ -169,15 +169,22 @@ __device__ __forceinline__ f32x4 widen_bf16(u32x2 w)
 }
 // The chunk's raw bf16 rows as prep_chunk takes them: thread -> token r = tid / 32, channels
 // 4 (tid % 32) .. + 3 of k, q, g, v, and beta of the row (raw bits, so that nothing waits for
-// them until they are used; rows past the chunk's tokens zero).
+// them until they are used; rows past the chunk's tokens zero); with the gate in the pass,
+// A_log of the head and dt_bias at the thread's channels.
 struct RawRows {
     u32x2 k, q, g, v;
     uint32_t beta;
+    float A_log;
+    f32x4 dt_bias;
 };
 __device__ __forceinline__ RawRows load_rows(const BwdArgs &a, const ChunkLoc &c, int h, int tid)
 {
     const int r = tid >> 5, c4 = 4 * (tid & 31);
-    RawRows w = {u32x2{0u, 0u}, u32x2{0u, 0u}, u32x2{0u, 0u}, u32x2{0u, 0u}, 0u};
+    RawRows w = {u32x2{0u, 0u}, u32x2{0u, 0u}, u32x2{0u, 0u}, u32x2{0u, 0u}, 0u, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (a.flags & kBGateIn) {
+        w.A_log = a.A_log[h];
+        w.dt_bias = ld4(a.dt_bias + (size_t)h * kD + c4);
+    }
     if (r < c.len) {
         const size_t ti = (size_t)(c.t0 + r) * (size_t)a.H + (size_t)h;
         w.k = *reinterpret_cast<const u32x2 *>(a.k + ti * kD + c4);
@@ -214,11 +221,11 @@ __device__ void prep_chunk(const BwdArgs &a, const ChunkLoc &c, int h, PrepLds &
         f32x4 ll = {0.f, 0.f, 0.f, 0.f};
         if (r < c.len) {
             if (a.flags & kBGateIn) {
-                const float eA = expf(a.A_log[h]);
-                const f32x4 db = ld4(a.dt_bias + (size_t)h * kD + c4);
+                const float eA = expf(raw.A_log);
+                const f32x4 db = raw.dt_bias;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    ll[e] = a.lower_bound / (1.0f + expf(-eA * (gg[e] + db[e])));
+                    ll[e] = a.lower_bound * __builtin_amdgcn_rcpf(1.0f + expf(-eA * (gg[e] + db[e])));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -661,6 +668,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         tg[i] = bbf16(a.g[at]);
     }
     const RawRows raw = load_rows(a, c, h, tid);  // prep_chunk's rows; v also for the dbeta rows
+    const float dtb = (a.flags & kBGateIn) ? a.dt_bias[(size_t)h * kD + cc] : 0.f;  // the tail's gate
     {  // dV' into P (P replaces it below)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
         st4(&L.P[r][c4], ld4(xb + 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15)));  // (rows_at)
@@ -930,7 +938,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         above += gg > g ? t : 0.f;
     }
     const bool gate_in = (a.flags & kBGateIn) != 0;
-    const float eA = gate_in ? expf(a.A_log[h]) : 0.f, dtb = gate_in ? a.dt_bias[(size_t)h * kD + cc] : 0.f;
+    const float eA = gate_in ? expf(raw.A_log) : 0.f;
     float run = e + above;
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
