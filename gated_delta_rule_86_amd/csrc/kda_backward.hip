@@ -648,12 +648,21 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     PrepLds &p = L.p;
     const int64_t x = blockIdx.x / a.H;
     const int h = (int)(blockIdx.x % a.H);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
+    const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;  // (a slot of the workspace for every x)
+    const float *xf = a.xf + sl * (kCH * kD), *xb = a.xb + sl * (kCH * kD);
+    // The loads that need only the chunk's slot go out before the search for its sequence: its
+    // V' and dV' rows (thread -> row tid / 32, columns 4 (tid % 32) .. + 3, rows_at) and the
+    // first two tiles of its stored state for the loop below.
+    const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
+    const float *cs = a.ck + sl * kBState + so;  // the stored state
+    const int rr = tid >> 5, rc4 = 4 * (tid & 31);
+    const int ro = 256 * (rc4 >> 4) + 64 * (rr & 3) + 16 * (rr >> 2) + (rc4 & 15);  // rows_at(rr, rc4)
+    const f32x4 own_v = ld4(xf + ro), own_dv = ld4(xb + ro);
+    f32x4 x0 = ld4(cs), x1 = ld4(cs + 2048);
     ChunkLoc c;
     if (!locate_chunk(a, x, c))
         return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
-    const size_t sl = (size_t)x * (size_t)a.H + (size_t)h;
-    const float *xf = a.xf + sl * (kCH * kD), *xb = a.xb + sl * (kCH * kD);
     const int c0 = 16 * wave, cc = c0 + m;
     const size_t tok0 = (size_t)c.t0 * (size_t)a.H + (size_t)h;  // token-head index of row 0
     // The tail's per-element inputs (D layout: wave w, channel 16 w + m, rows 4 g + i) and the
@@ -669,10 +678,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     }
     const RawRows raw = load_rows(a, c, h, tid);  // prep_chunk's rows; v also for the dbeta rows
     const float dtb = (a.flags & kBGateIn) ? a.dt_bias[(size_t)h * kD + cc] : 0.f;  // the tail's gate
-    {  // dV' into P (P replaces it below)
-        const int r = tid >> 5, c4 = 4 * (tid & 31);
-        st4(&L.P[r][c4], ld4(xb + 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15)));  // (rows_at)
-    }
+    st4(&L.P[rr][rc4], own_dv);  // dV' into P (P replaces it below)
     // The chain stored one of the chunk's two states: S0 for an even chunk of the sequence, D
     // for an odd one.  The other is rebuilt from the neighbouring chunk's stored state and
     // operands (the steps the chain took between them):
@@ -698,26 +704,23 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         }
         ngam = opn[kOpGam + cc];
     }
-    // The first two state tiles of the loop below, requested ahead of the staging loads (for the
-    // last chunk of a sequence, kind 2, the neighbour's are its own and go unused).
-    const int so = 256 * wave + 64 * (m & 3) + 16 * (m >> 2) + 4 * g;
-    const float *cs = a.ck + sl * kBState + so;  // the stored state
-    const float *cn = a.ck + sn * kBState + so;  // the neighbour's
-    f32x4 x0 = ld4(cs), n0 = ld4(cn), x1 = ld4(cs + 2048), n1 = ld4(cn + 2048);
+    // The neighbour's first two state tiles, requested ahead of the staging loads (for the last
+    // chunk of a sequence, kind 2, the neighbour is the chunk itself and they go unused).
+    const float *cn = a.ck + sn * kBState + so;
+    f32x4 n0 = ld4(cn), n1 = ld4(cn + 2048);
     // Rows staged in LDS (the space prep_chunk fills afterwards), row-major with rows padded to
     // kRS floats so that 16 lanes reading 16 rows hit distinct banks: the chunk's V', dO and dV'
     // and the neighbour's rows (V' or dV'', and dO'').  Only the two state tiles per step are
-    // read from global memory in the loop below, requested three steps ahead.
+    // read from global memory in the loop below, requested two steps ahead.
     constexpr int kRS = kD + 4;
     float *const sV = &p.KG[0][0], *const sO = sV + kCH * kRS, *const sD = sO + kCH * kRS;
     float *const nX = sD + kCH * kRS, *const nO = nX + kCH * kRS;
     static_assert(5 * kCH * kRS <= 6 * kCH * kP, "staging fits in KG .. U");
     {
-        const int r = tid >> 5, c4 = 4 * (tid & 31);
-        const int ro = 256 * (c4 >> 4) + 64 * (r & 3) + 16 * (r >> 2) + (c4 & 15);  // rows_at(r, c4)
+        const int r = rr, c4 = rc4;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        st4(sV + r * kRS + c4, ld4(xf + ro));
-        st4(sD + r * kRS + c4, ld4(xb + ro));
+        st4(sV + r * kRS + c4, own_v);
+        st4(sD + r * kRS + c4, own_dv);
         st4(sO + r * kRS + c4, r < c.len ? ld4_bf16(a.dout + (tok0 + (size_t)r * (size_t)a.H) * kD + c4) : z);
         if (kind == 0) {
             const int64_t rem = a.seq_len[c.n] - kCH * (jl + 1);  // the next chunk's tokens
