@@ -22,7 +22,9 @@
 //   dk^ = dKG Gamma + (dKI + dKD gamma) / Gamma,  dq^ = scale dQG Gamma
 //   db = dKG KG - dKI KI + dQG QG - dKD KD, plus sum_r dKD KD + dgamma gamma on the last row;
 //   d(log-decay) = reverse cumulative sum of db over the chunk.
-// Then the activations' chain rules.  All arithmetic is fp32 (products on the fp32 MFMA).
+// Then the activations' chain rules.  All arithmetic is fp32; products on the fp32 MFMA, except
+// the two chains' products, which are three-term bf16 products (hi hi + lo hi + hi lo, about
+// 16 significant bits per factor, fp32 accumulation), as in the forward chunk recurrence.
 //
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
 //   bwd_ops_kernel     per chunk-head: the chunk's activated rows (l2norm, gate, sigmoid, as
@@ -68,6 +70,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bbf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+__device__ __forceinline__ void stu4(float *p, __attribute__((ext_vector_type(4))) uint32_t x)
+{
+    *reinterpret_cast<__attribute__((ext_vector_type(4))) uint32_t *>(p) = x;
+}
+__device__ __forceinline__ __attribute__((ext_vector_type(4))) uint32_t ldu4(const float *p)
+{
+    return *reinterpret_cast<const __attribute__((ext_vector_type(4))) uint32_t *>(p);
+}
 // four bf16 values widened (8-byte aligned)
 __device__ __forceinline__ f32x4 ld4_bf16(const uint16_t *p)
 {
@@ -90,6 +100,56 @@ __device__ __forceinline__ f32x4 mm4(f32x4 a, f32x4 b, f32x4 c)
     c = mfma4(a[2], b[2], c);
     return mfma4(a[3], b[3], c);
 }
+// Three-term bf16 products for the chain kernel (about 16 significant bits per factor, fp32
+// accumulation; the chunk recurrence of the forward pass uses the same scheme).
+// v_mfma_f32_16x16x16_bf16 takes the operands in the layout of mm4 above: lane L holds
+// A[L % 16][4 (L / 16) + j] and B[4 (L / 16) + j][L % 16], j = 0..3, as four packed bf16.  A
+// split operand is u32x4 {hi (two words), lo (two words)} with x ~ hi + lo.
+typedef short bf16x4s __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)  // round to nearest even
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ f32x4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c)
+{
+    typedef uint32_t u32x2_ __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4s, u32x2_{a0, a1}),
+                                                      __builtin_bit_cast(bf16x4s, u32x2_{b0, b1}), c, 0, 0, 0);
+}
+// c + A B: hi hi + lo hi + hi lo
+__device__ __forceinline__ f32x4 mm3(u32x4 a, u32x4 b, f32x4 c)
+{
+    c = mfma16(a[0], a[1], b[0], b[1], c);
+    c = mfma16(a[2], a[3], b[0], b[1], c);
+    return mfma16(a[0], a[1], b[2], b[3], c);
+}
+// c + A B for a B that is exactly bf16 (b: one word pair): hi B + lo B
+__device__ __forceinline__ f32x4 mm2(u32x4 a, uint32_t b0, uint32_t b1, f32x4 c)
+{
+    c = mfma16(a[0], a[1], b0, b1, c);
+    return mfma16(a[2], a[3], b0, b1, c);
+}
+// {hi, lo} of four values on the VALU
+__device__ __forceinline__ u32x4 split4(f32x4 x)
+{
+    const uint32_t h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
+    return u32x4{h0, h1, pk_bf16(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xffff0000u)),
+                 pk_bf16(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u))};
+}
+// {hi, lo} of a tile in the D layout (which is also the B operand layout): lo from the MFMA as
+// (-I) hi + x, exact in fp32; negI holds -1 (bf16) at A[m][m]: lane m + 16 (m / 4), element m % 4
+__device__ __forceinline__ u32x4 split_tile(f32x4 x, uint32_t n0, uint32_t n1)
+{
+    const uint32_t h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
+    const f32x4 r = mfma16(n0, n1, h0, h1, x);
+    return u32x4{h0, h1, pk_bf16(r[0], r[1]), pk_bf16(r[2], r[3])};
+}
+
 // acc + A B^T for A, B [16][nk] row-major in LDS (row stride kP), one wavefront
 __device__ __forceinline__ f32x4 mm_rows(const float *A, const float *B, int nk, f32x4 acc, int lane)
 {
@@ -400,6 +460,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
 // often, which is what counts when the chains are many and HBM is the limit.
 constexpr int kChainUnitsSplit = 128;  // units (chain, role) up to which kCh = 2 is used
 
+// The MFMA A operands A0, A1, A2 are held split: each group of four consecutive values (the
+// four k values of one lane) as {hi, lo} (split4), in the same 16 bytes.
 template <int kRows>
 struct ChainStage {
     float A0[kCH * kD];  // role 0: -W [r][c];  role 1: KD [r][c]
@@ -457,10 +519,10 @@ __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainS
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int f = 4 * (tid + kChainThreads * e);
-        st4(st.A0 + f, r.a0[e]);
-        st4(st.A1 + (role ? f : tc * kCH + tr + 8 * e), r.a1[e]);
+        stu4(st.A0 + f, split4(r.a0[e]));
+        stu4(st.A1 + (role ? f : tc * kCH + tr + 8 * e), split4(r.a1[e]));
         if (role)
-            st4(st.A2 + tc * kCH + tr + 8 * e, r.a2[e]);
+            stu4(st.A2 + tc * kCH + tr + 8 * e, split4(r.a2[e]));
     }
     if (tid < kCH * kQ4) {
         const int row = tid / kQ4, c4 = 4 * (tid % kQ4);
@@ -528,6 +590,15 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         for (int e = 0; e < kTiles; ++e)
             S[e] = a.dht ? ld4(a.dht + srow + 16 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // -I (bf16) as the A operand of split_tile: lane m + 16 (m / 4), element m % 4
+    uint32_t nI0 = 0u, nI1 = 0u;
+    if (g == (m >> 2)) {
+        const uint32_t v = (m & 1) ? 0xbf800000u : 0x0000bf80u;
+        if ((m & 2) == 0)
+            nI0 = v;
+        else
+            nI1 = v;
+    }
     // The operands of chunk it + 1 are requested while chunk it runs.
     wait_vmem();  // the initial state is in (so that no wait inside the loop is for it)
     StageRegs rg_;
@@ -548,10 +619,10 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             load(it + 1);
         const ChainStage<kRows> &st = s_st[kSt == 1 ? 0 : (it & 1)];
         const size_t sl = slot_of(j);
-        f32x4 A[kTiles];  // A operands of the first product (this wave's channels), read before its MFMAs
+        u32x4 A[kTiles];  // A operands of the first product (this wave's channels), read before its MFMAs
 #pragma unroll
         for (int e = 0; e < kTiles; ++e)
-            A[e] = ld4(st.A0 + m * kD + 16 * (ct0 + e) + 4 * g);
+            A[e] = ldu4(st.A0 + m * kD + 16 * (ct0 + e) + 4 * g);
         f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
         if (hc == 0)
 #pragma unroll
@@ -571,8 +642,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         // two accumulators (even and odd tiles), then (kCh = 2) the partner wave's half sum
 #pragma unroll
         for (int e = 0; e < kTiles; e += 2) {
-            X0 = mm4(A[e], S[e], X0);
-            X1 = mm4(A[e + 1], S[e + 1], X1);
+            X0 = mm3(A[e], split_tile(S[e], nI0, nI1), X0);
+            X1 = mm3(A[e + 1], split_tile(S[e + 1], nI0, nI1), X1);
         }
         f32x4 X = X0 + X1;
         if constexpr (kCh == 2) {
@@ -589,33 +660,36 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         }
         if (role == 0) {
             if (more) {  // S <- S Diag(gamma) + V'^T KD
-                f32x4 K[kTiles], Gm[kTiles];
+                const u32x4 xs = split_tile(X, nI0, nI1);
+                u32x4 K[kTiles];
+                f32x4 Gm[kTiles];
 #pragma unroll
                 for (int e = 0; e < kTiles; ++e) {
-                    K[e] = ld4(st.A1 + (16 * (ct0 + e) + m) * kCH + 4 * g);
+                    K[e] = ldu4(st.A1 + (16 * (ct0 + e) + m) * kCH + 4 * g);
                     Gm[e] = ld4(st.gam + 16 * (ct0 + e) + 4 * g);
                 }
 #pragma unroll
                 for (int e = 0; e < kTiles; ++e)
-                    S[e] = mm4(K[e], X, S[e] * Gm[e]);
+                    S[e] = mm3(K[e], xs, S[e] * Gm[e]);
             }
         } else {  // D <- D Diag(gamma) + dO^T QG - dV'^T W
-            f32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = st.O[4 * g + i][16 * rg + m];
+            // dO is bf16: its four rows as one packed word pair, no lo part
+            const uint32_t o0 = pk_bf16(st.O[4 * g][16 * rg + m], st.O[4 * g + 1][16 * rg + m]);
+            const uint32_t o1 = pk_bf16(st.O[4 * g + 2][16 * rg + m], st.O[4 * g + 3][16 * rg + m]);
+            const u32x4 xs = split_tile(X, nI0, nI1);
 #pragma unroll
             for (int c4 = 0; c4 < kTiles; c4 += 4) {
-                f32x4 Q[4], Wt[4], Gm[4];
+                u32x4 Q[4], Wt[4];
+                f32x4 Gm[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    Q[e] = ld4(st.A1 + (16 * (ct0 + c4 + e) + m) * kCH + 4 * g);
-                    Wt[e] = ld4(st.A2 + (16 * (ct0 + c4 + e) + m) * kCH + 4 * g);
+                    Q[e] = ldu4(st.A1 + (16 * (ct0 + c4 + e) + m) * kCH + 4 * g);
+                    Wt[e] = ldu4(st.A2 + (16 * (ct0 + c4 + e) + m) * kCH + 4 * g);
                     Gm[e] = ld4(st.gam + 16 * (ct0 + c4 + e) + 4 * g);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    S[c4 + e] = mm4(Wt[e], X, mm4(Q[e], o, S[c4 + e] * Gm[e]));
+                    S[c4 + e] = mm3(Wt[e], xs, mm2(Q[e], o0, o1, S[c4 + e] * Gm[e]));
             }
         }
         if (kSt == 1)
