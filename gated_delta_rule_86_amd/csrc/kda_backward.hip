@@ -23,8 +23,9 @@
 //   db = dKG KG - dKI KI + dQG QG - dKD KD, plus sum_r dKD KD + dgamma gamma on the last row;
 //   d(log-decay) = reverse cumulative sum of db over the chunk.
 // Then the activations' chain rules.  All arithmetic is fp32; products on the fp32 MFMA, except
-// the two chains' products, which are three-term bf16 products (hi hi + lo hi + hi lo, about
-// 16 significant bits per factor, fp32 accumulation), as in the forward chunk recurrence.
+// the two chains' products and the gradient kernel's products with the states, which are
+// three-term bf16 products (hi hi + lo hi + hi lo, about 16 significant bits per factor, fp32
+// accumulation), as in the forward chunk recurrence.
 //
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
 //   bwd_ops_kernel     per chunk-head: the chunk's activated rows (l2norm, gate, sigmoid, as
@@ -133,6 +134,12 @@ __device__ __forceinline__ f32x4 mm2(u32x4 a, uint32_t b0, uint32_t b1, f32x4 c)
 {
     c = mfma16(a[0], a[1], b0, b1, c);
     return mfma16(a[2], a[3], b0, b1, c);
+}
+// c + A B for an A that is exactly bf16 (a's hi words only): A hi + A lo
+__device__ __forceinline__ f32x4 mm2a(u32x4 a, u32x4 b, f32x4 c)
+{
+    c = mfma16(a[0], a[1], b[0], b[1], c);
+    return mfma16(a[0], a[1], b[2], b[3], c);
 }
 // {hi, lo} of four values on the VALU
 __device__ __forceinline__ u32x4 split4(f32x4 x)
@@ -782,59 +789,81 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     // chunk of a sequence, kind 2, the neighbour is the chunk itself and they go unused).
     const float *cn = a.ck + sn * kBState + so;
     f32x4 n0 = ld4(cn), n1 = ld4(cn + 2048);
-    // Rows staged in LDS (the space prep_chunk fills afterwards), row-major with rows padded to
-    // kRS floats so that 16 lanes reading 16 rows hit distinct banks: the chunk's V', dO and dV'
-    // and the neighbour's rows (V' or dV'', and dO'').  Only the two state tiles per step are
-    // read from global memory in the loop below, requested two steps ahead.
-    constexpr int kRS = kD + 4;
+    // Rows staged in LDS (the space prep_chunk fills afterwards) as the bf16 {hi, lo} operands of
+    // the three-term products below (each group of four values as u32x4 {hi, lo}; dO is exact
+    // in bf16, lo zero): the chunk's V', dO, dV' row-major with rows padded to kRS floats (16
+    // lanes reading 16 rows hit distinct banks), and the neighbour's rows (V' or dV'', and dO'')
+    // transposed, [value column][row] with columns padded to kNT floats, since the rebuild takes
+    // them as A operands of four rows at one column.  Only the two state tiles per step are read
+    // from global memory in the loop below, requested two steps ahead.
+    constexpr int kRS = kD + 4, kNT = kCH + 4;
     float *const sV = &p.KG[0][0], *const sO = sV + kCH * kRS, *const sD = sO + kCH * kRS;
-    float *const nX = sD + kCH * kRS, *const nO = nX + kCH * kRS;
-    static_assert(5 * kCH * kRS <= 6 * kCH * kP, "staging fits in KG .. U");
+    float *const nX = sD + kCH * kRS, *const nO = nX + kD * kNT;
+    static_assert(3 * kCH * kRS + 2 * kD * kNT <= 6 * kCH * kP, "staging fits in KG .. U");
     {
         const int r = rr, c4 = rc4;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        st4(sV + r * kRS + c4, own_v);
-        st4(sD + r * kRS + c4, own_dv);
-        st4(sO + r * kRS + c4, r < c.len ? ld4_bf16(a.dout + (tok0 + (size_t)r * (size_t)a.H) * kD + c4) : z);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        stu4(sV + r * kRS + c4, split4(own_v));
+        stu4(sD + r * kRS + c4, split4(own_dv));
+        u32x4 ow = z;
+        if (r < c.len) {
+            const u32x2 w = *reinterpret_cast<const u32x2 *>(a.dout + (tok0 + (size_t)r * (size_t)a.H) * kD + c4);
+            ow = u32x4{w[0], w[1], 0u, 0u};
+        }
+        stu4(sO + r * kRS + c4, ow);
+        // the neighbour's rows 4 q .. 4 q + 3 at value column v, q = tid / 128
+        const int v = tid & (kD - 1), q = tid >> 7;
+        const int nro = 256 * (v >> 4) + 16 * q + (v & 15);  // rows_at(4 q, v); row 4 q + i adds 64 i
         if (kind == 0) {
+            const float *xn = a.xb + sn * (kCH * kD) + nro;
+            stu4(nX + v * kNT + 4 * q, split4(f32x4{xn[0], xn[64], xn[128], xn[192]}));
             const int64_t rem = a.seq_len[c.n] - kCH * (jl + 1);  // the next chunk's tokens
-            st4(nX + r * kRS + c4, ld4(a.xb + sn * (kCH * kD) + ro));
-            st4(nO + r * kRS + c4,
-                r < rem ? ld4_bf16(a.dout + ((size_t)(c.t0 + kCH + r) * (size_t)a.H + (size_t)h) * kD + c4) : z);
+            uint32_t hw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hw[i] = 4 * q + i < rem ? a.dout[((size_t)(c.t0 + kCH + 4 * q + i) * (size_t)a.H + (size_t)h) * kD + v] : 0u;
+            stu4(nO + v * kNT + 4 * q, u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), 0u, 0u});
         } else if (kind == 1) {
-            st4(nX + r * kRS + c4, ld4(a.xf + sn * (kCH * kD) + ro));
+            const float *xn = a.xf + sn * (kCH * kD) + nro;
+            stu4(nX + v * kNT + 4 * q, split4(f32x4{xn[0], xn[64], xn[128], xn[192]}));
         }
     }
+    // -I (bf16) as the A operand of split_tile: lane m + 16 (m / 4), element m % 4
+    uint32_t nI0 = 0u, nI1 = 0u;
+    if (g == (m >> 2)) {
+        const uint32_t vv = (m & 1) ? 0xbf800000u : 0x0000bf80u;
+        if ((m & 2) == 0)
+            nI0 = vv;
+        else
+            nI1 = vv;
+    }
+    const u32x4 nb0s = split4(nb0), nb1s = split4(nb1);
     // The products with the chunk's states, wave w at channels c0 .. c0 + 15 (lane (g, m): rows
     // 4 g + i, channel cc, the D layout):  dKD = V' D and G1 = dO S0 stay in registers for the
     // tail, G2 = dV' S0 goes to Q, dgamma_c = sum_v S0[v][c] D[v][c] is summed over the lanes
     // of a channel; waves 0 - 3 also form dAqk = lower(dO V'^T) over value columns 32 w .. + 31.
     // A operands: rows m of V', dV', dO at value columns 16 t + 4 g .. + 3; B operands: the
-    // states at value rows 16 t + 4 g .. + 3, channel cc (state_at).
+    // states at value rows 16 t + 4 g .. + 3, channel cc (state_at).  Three-term bf16 products
+    // (two terms where dO, exact in bf16, is the A operand), fp32 accumulation.
     f32x4 tKD = {0.f, 0.f, 0.f, 0.f}, tG1 = tKD, aG2 = tKD, aQK = tKD;
     float tdgam = 0.f;
     {
         // one 16-row step t: the states at value rows 16 t .. + 15 (bs = S0, bd = D)
         auto prod = [&](int t, f32x4 bs, f32x4 bd) {
             const int ra = m * kRS + 16 * t + 4 * g;
-            const f32x4 af = ld4(sV + ra), ab = ld4(sD + ra), ao = ld4(sO + ra);
-            tKD = mm4(af, bd, tKD);
-            tG1 = mm4(ao, bs, tG1);
-            aG2 = mm4(ab, bs, aG2);
+            const u32x4 af = ldu4(sV + ra), ab = ldu4(sD + ra), ao = ldu4(sO + ra);
+            const u32x4 bss = split_tile(bs, nI0, nI1), bds = split_tile(bd, nI0, nI1);
+            tKD = mm3(af, bds, tKD);
+            tG1 = mm2a(ao, bss, tG1);
+            aG2 = mm3(ab, bss, aG2);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 tdgam = fmaf(bs[j], bd[j], tdgam);
             if ((t >> 1) == wave)
-                aQK = mm4(ao, af, aQK);
+                aQK = mm2a(ao, af, aQK);
         };
-        // the neighbour's rows 4 g + j at value column 16 t + m
-        auto nrow = [&](const float *X, int t) {
-            f32x4 v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[j] = X[(4 * g + j) * kRS + 16 * t + m];
-            return v;
-        };
+        // the neighbour's rows 4 g .. 4 g + 3 at value column 16 t + m
+        auto nrow = [&](const float *X, int t) { return ldu4(X + (16 * t + m) * kNT + 4 * g); };
         if (kind == 2) {
             const float *dh =  // dL/dS_final at value row 4 g, channel cc
                 a.dht ? a.dht + ((size_t)c.n * (size_t)a.H + (size_t)h) * kBState + (size_t)(4 * g) * kD + cc : nullptr;
@@ -859,9 +888,9 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
                 x1 = ld4(cs + 2048 * tn);
                 n1 = ld4(cn + 2048 * tn);
                 if (kind == 1)
-                    prod(t, mm4(nrow(nX, t), nb0, sy * ngam), sx);
+                    prod(t, mm3(nrow(nX, t), nb0s, sy * ngam), sx);
                 else
-                    prod(t, sx, mm4(nrow(nX, t), nb1, mm4(nrow(nO, t), nb0, sy * ngam)));
+                    prod(t, sx, mm3(nrow(nX, t), nb1s, mm2a(nrow(nO, t), nb0s, sy * ngam)));
             }
         }
         tdgam += __shfl_xor(tdgam, 16);
@@ -941,7 +970,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     }
     // dKG, dKI, dQG on the MFMA: wave w takes channels c0 .. c0 + 15, c0 = 16 w; lane (g, m)
     // holds rows 4 g + i at channel c0 + m (the D layout) from here on.
-    f32x4 sKG, sQG = tG1, sKI = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sKG, sQG = {0.f, 0.f, 0.f, 0.f}, sKI = sQG;
     {
         f32x4 ki, kgb, qg;  // B operands: rows 4 g + j at channel cc
 #pragma unroll
@@ -960,7 +989,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
             dAqk_c[j] = L.dAqk[4 * g + j][m];
         }
         sKG = mm4(dA_r, ki, sKG);      // Q + dA KI
-        sQG = mm4(dAqk_r, ki, sQG);    // G1 + dAqk KI
+        sQG = mm4(dAqk_r, ki, sQG) + tG1;  // G1 + dAqk KI
         sKI = mm4(dA_c, kgb, sKI);     // dA^T diag(beta) KG
         sKI = mm4(dAqk_c, qg, sKI);    //   + dAqk^T QG
     }

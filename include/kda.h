@@ -246,8 +246,8 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int ha
  * kda_bwd -- gradients of kda_fwd_ex's outputs (out and final_state) with respect to its
  * inputs, for training.  The pages describe the forward pass only; this is the reverse-mode
  * derivative of the same per-token recurrence (stated in the comment at the top of this
- * file), under the same activation switches.  All arithmetic is fp32 (the state chains'
- * products as three-term bf16 products with fp32 accumulation, about 16 significant bits per
+ * file), under the same activation switches.  All arithmetic is fp32 (the products with the
+ * states as three-term bf16 products with fp32 accumulation, about 16 significant bits per
  * factor, as in kda_fwd's chunk recurrence); the inputs q, k, v,
  * g, beta, scale, A_log, dt_bias, lower_bound, initial_state, cu_seqlens, B, T, H, N, K, V
  * and flags mean exactly what they mean for kda_fwd_ex.
