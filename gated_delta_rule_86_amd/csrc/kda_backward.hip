@@ -30,7 +30,8 @@
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
 //   bwd_ops_kernel     per chunk-head: the chunk's activated rows (l2norm, gate, sigmoid, as
 //                      in the forward pass) and its operands for the two chains (-W, U, KD,
-//                      U~ = lower(QG KI^T)^T dO, QG, gamma, in the layouts they are read in)
+//                      U~ = lower(QG KI^T)^T dO row-major, QG^T, gamma; the chain kernel forms
+//                      KD^T and -W^T itself)
 //   bwd_chain_kernel   per (sequence, head, role, half of the value rows): role 0 runs the
 //                      state forwards over the chunks, writing V' of every chunk and S0 of the
 //                      even chunks of the sequence; role 1 runs dL/dS backwards, writing dV' of
@@ -509,7 +510,6 @@ __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int part,
     const int row = (tid / kQ4) & 15, c4 = 4 * (tid % kQ4);  // (kRows = 32: threads 128 .. repeat)
     r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + kRows * part + c4);
     if (role) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const int rr = row < len ? row : 0;
         const u32x2 w = *reinterpret_cast<const u32x2 *>(a.dout + ((size_t)(t0 + rr) * (size_t)a.H + (size_t)h) * kD +
                                                          kRows * part + c4);
