@@ -29,9 +29,9 @@
 //
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
 //   bwd_ops_kernel     per chunk-head: the chunk's activated rows (l2norm, gate, sigmoid, as
-//                      in the forward pass) and its operands for the two chains (-W, U, KD,
-//                      U~ = lower(QG KI^T)^T dO row-major, QG^T, gamma; the chain kernel forms
-//                      KD^T and -W^T itself)
+//                      in the forward pass) and its operands for the two chains (-W, U, KD
+//                      row-major, QG^T, lower(QG KI^T), gamma; the chain kernel forms KD^T, -W^T
+//                      and U~ = lower(QG KI^T)^T dO itself)
 //   bwd_chain_kernel   per (sequence, head, role, half of the value rows): role 0 runs the
 //                      state forwards over the chunks, writing V' of every chunk and S0 of the
 //                      even chunks of the sequence; role 1 runs dL/dS backwards, writing dV' of
@@ -64,7 +64,7 @@ constexpr int kQ4 = kCH + 4;       // the same, rows 16-byte aligned
 constexpr int kGradThreads = 512;  // bwd_ops_kernel, bwd_grad_kernel
 constexpr int kChainThreads = 256; // bwd_chain_kernel: 4 wavefronts of 16 value rows
 // operand block of a chunk-head (kBwdOps floats)
-constexpr int kOpNegW = 0, kOpU = 2048, kOpKD = 4096, kOpUt = 6144, kOpQGt = 8192, kOpGam = 10240;
+constexpr int kOpNegW = 0, kOpU = 2048, kOpKD = 4096, kOpQGt = 6144, kOpAqk = 8192, kOpGam = 8448;
 static_assert(kOpGam + kD == kBwdOps, "operand block layout");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -417,30 +417,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_ops_kernel(BwdArgs a)
     if (!locate_chunk(a, x, c))
         return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
-    // dO at rows 4 g + j, value column 16 w + m (the B operand of U~ below), requested before
-    // the chunk's operands are formed; raw bits, so that nothing waits for them yet
-    uint32_t od[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 4 * g + j;
-        od[j] = a.dout[((size_t)(c.t0 + (r < c.len ? r : 0)) * (size_t)a.H + (size_t)h) * kD + 16 * wave + m];
-        if (r >= c.len)
-            od[j] = 0;
-    }
     prep_chunk(a, c, h, p, tid, load_rows(a, c, h, tid));
     float *o = a.ops + ((size_t)x * (size_t)a.H + (size_t)h) * kBwdOps;
-    {  // U~ = lower(QG KI^T)^T dO: wave w takes value columns 16 w .. + 15
-        f32x4 at, ob;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            at[j] = p.Aqk[4 * g + j][m];  // A operand: (A_qk^T)[m][4 g + j]
-            ob[j] = __uint_as_float(od[j] << 16);
-        }
-        const f32x4 ut = mm4(at, ob, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[kOpUt + (4 * g + i) * kD + 16 * wave + m] = ut[i];
-    }
+    if (tid < kCH * kCH)
+        o[kOpAqk + tid] = p.Aqk[tid >> 4][tid & 15];
     const int ch = tid & (kD - 1), q4 = 4 * (tid >> 7);
     const float gam = p.gam[ch];
     f32x4 kd, qg;
@@ -475,8 +455,8 @@ struct ChainStage {
     float A0[kCH * kD];  // role 0: -W [r][c];  role 1: KD [r][c]
     float A1[kD * kCH];  // role 0: KD^T [c][r]; role 1: QG^T [c][r]
     float A2[kD * kCH];  // role 1: -W^T [c][r]
-    float U[kCH][kRows]; // role 0: U, role 1: U~ (the workgroup's value columns)
-    float O[kCH][kRows]; // role 1: dO (the workgroup's value columns)
+    float Y[kCH][kRows]; // role 0: U, role 1: dO (the workgroup's value columns)
+    float Mx[kCH][kCH];  // role 1: lower(QG KI^T)
     float gam[kD];
 };
 
@@ -484,14 +464,14 @@ struct ChainStage {
 // Every load is unconditional (a clamped row or column where the data is not needed) and
 // keeps its raw bits, so that nothing waits for it before the copy into LDS.
 struct StageRegs {
-    f32x4 a0[2], a1[2], a2[2], u, gm;
-    uint32_t o[2];  // two bf16 pairs of dO
+    f32x4 a0[2], a1[2], a2[2], um, gm;  // um: role 0 U at the workgroup's columns, role 1 lower(QG KI^T)
+    uint32_t y[2];                      // two bf16 pairs of dO (role 1)
 };
 template <int kRows>
 __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int part, const float *op, int64_t t0, int len,
                                            int h, StageRegs &r, int tid)
 {
-    constexpr int kQ4 = kRows / 4;  // float4 columns of U, O
+    constexpr int kQ4 = kRows / 4;  // float4 columns of Y
     // the transposed operands (role 0: KD^T, role 1: -W^T) from the row-major arrays: thread ->
     // channel tid % 128, rows 4 (tid / 128 + 2 e) .. + 3, four loads that 64 lanes coalesce
     const int tc = tid & (kD - 1), tr = 4 * (tid >> 7);
@@ -508,13 +488,13 @@ __device__ __forceinline__ void stage_load(const BwdArgs &a, int role, int part,
             r.a2[e] = col4(op + kOpNegW, e);
     }
     const int row = (tid / kQ4) & 15, c4 = 4 * (tid % kQ4);  // (kRows = 32: threads 128 .. repeat)
-    r.u = ld4(op + (role ? kOpUt : kOpU) + row * kD + kRows * part + c4);
-    if (role) {
-        const int rr = row < len ? row : 0;
+    r.um = ld4(role ? op + kOpAqk + 4 * (tid & (kCH * kCH / 4 - 1)) : op + kOpU + row * kD + kRows * part + c4);
+    {
+        const int rr = row < len ? row : 0;  // (role 0 loads a dO row it does not use)
         const u32x2 w = *reinterpret_cast<const u32x2 *>(a.dout + ((size_t)(t0 + rr) * (size_t)a.H + (size_t)h) * kD +
                                                          kRows * part + c4);
-        r.o[0] = w[0];
-        r.o[1] = w[1];
+        r.y[0] = w[0];
+        r.y[1] = w[1];
     }
     r.gm = ld4(op + kOpGam + 4 * (tid & (kD / 4 - 1)));
 }
@@ -533,15 +513,13 @@ __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainS
     }
     if (tid < kCH * kQ4) {
         const int row = tid / kQ4, c4 = 4 * (tid % kQ4);
-        st4(&st.U[row][c4], r.u);
-        if (role) {
-            const bool in = row < len;
-            st4(&st.O[row][c4], f32x4{in ? __uint_as_float(r.o[0] << 16) : 0.f,
-                                      in ? __uint_as_float(r.o[0] & 0xffff0000u) : 0.f,
-                                      in ? __uint_as_float(r.o[1] << 16) : 0.f,
-                                      in ? __uint_as_float(r.o[1] & 0xffff0000u) : 0.f});
-        }
+        const bool in = row < len;
+        st4(&st.Y[row][c4], role ? f32x4{in ? __uint_as_float(r.y[0] << 16) : 0.f, in ? __uint_as_float(r.y[0] & 0xffff0000u) : 0.f,
+                                         in ? __uint_as_float(r.y[1] << 16) : 0.f, in ? __uint_as_float(r.y[1] & 0xffff0000u) : 0.f}
+                                 : r.um);
     }
+    if (role && tid < kCH * kCH / 4)
+        st4(&st.Mx[0][0] + 4 * tid, r.um);
     if (tid < kD / 4)
         st4(st.gam + 4 * tid, r.gm);
 }
@@ -630,11 +608,25 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 #pragma unroll
         for (int e = 0; e < kTiles; ++e)
             A[e] = ldu4(st.A0 + m * kD + 16 * (ct0 + e) + 4 * g);
-        f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
-        if (hc == 0)
+        // X starts at U (role 0) or at U~ = lower(QG KI^T)^T dO (role 1, one fp32 product, in an
+        // accumulator of its own so that it overlaps the first product) at the wave's value
+        // columns, in the first wave of a row group
+        f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0, XU = X0;
+        if (hc == 0) {
+            if (role) {
+                f32x4 ua, ub;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                X0[i] = st.U[4 * g + i][16 * rg + m];
+                for (int j = 0; j < 4; ++j) {
+                    ua[j] = st.Mx[4 * g + j][m];  // A: (A_qk^T)[m][4 g + j]
+                    ub[j] = st.Y[4 * g + j][16 * rg + m];
+                }
+                XU = mm4(ua, ub, XU);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    XU[i] = st.Y[4 * g + i][16 * rg + m];
+            }
+        }
         // the state before an even chunk (role 0) or dL/dS after an odd one (role 1), in the
         // tiled layout (state_at): each store of the wave writes 256 contiguous bytes
         if ((int)(j & 1) == role) {
@@ -652,7 +644,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             X0 = mm3(A[e], split_tile(S[e], nI0, nI1), X0);
             X1 = mm3(A[e + 1], split_tile(S[e + 1], nI0, nI1), X1);
         }
-        f32x4 X = X0 + X1;
+        f32x4 X = (X0 + X1) + XU;
         if constexpr (kCh == 2) {
             st4(&s_x[wave][lane][0], X);
             __syncthreads();
@@ -681,8 +673,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             }
         } else {  // D <- D Diag(gamma) + dO^T QG - dV'^T W
             // dO is bf16: its four rows as one packed word pair, no lo part
-            const uint32_t o0 = pk_bf16(st.O[4 * g][16 * rg + m], st.O[4 * g + 1][16 * rg + m]);
-            const uint32_t o1 = pk_bf16(st.O[4 * g + 2][16 * rg + m], st.O[4 * g + 3][16 * rg + m]);
+            const uint32_t o0 = pk_bf16(st.Y[4 * g][16 * rg + m], st.Y[4 * g + 1][16 * rg + m]);
+            const uint32_t o1 = pk_bf16(st.Y[4 * g + 2][16 * rg + m], st.Y[4 * g + 3][16 * rg + m]);
             const u32x4 xs = split_tile(X, nI0, nI1);
 #pragma unroll
             for (int c4 = 0; c4 < kTiles; c4 += 4) {

@@ -186,8 +186,9 @@ struct FwdArgs {
 // values V' and their gradient (fp32 16 x 128 each, tiled likewise); and the per-head gradient
 // partial sums (fp32 [H][kHeadSlices][2][128]).
 constexpr int kHeadSlices = 64;  // token slices of the backward pass's per-head gradient sums
-// operand block of one chunk-head: -W, U, KD, U~, QG^T (2048 fp32 each), gamma (128)
-constexpr int kBwdOps = 5 * kCH * kD + kD;
+// operand block of one chunk-head: -W, U, KD, QG^T (2048 fp32 each), lower(QG KI^T) (256),
+// gamma (128)
+constexpr int kBwdOps = 4 * kCH * kD + kCH * kCH + kD;
 
 struct BwdLayout {
     Layout tab;

@@ -284,7 +284,7 @@ kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, c
 /*
  * kda_bwd_workspace_size -- bytes of workspace kda_bwd needs: the chunk table, then per
  * 16-token chunk of each head (counted as ceil(T / 16) per batch row, or ceil(T / 16) + N
- * with cu_seqlens) 40.5 KiB of chunk operands, one fp32 state (64 KiB: the state before the
+ * with cu_seqlens) 33.5 KiB of chunk operands, one fp32 state (64 KiB: the state before the
  * chunk for the even chunks of a sequence, dL/dS after it for the odd ones) and the chunk's
  * V' and dL/dV' (8 KiB each), and 64 KiB per head of partial sums.  Returns 0 for invalid
  * sizes.
