@@ -1617,18 +1617,34 @@ __device__ void fused_consumer(const FusedArgs &a, const WgPlan &w, unsigned cha
     bool spun_out = false;
     int it0 = 0;
     Unit u;
-    for (int64_t k = 0; unit_at<kMode>(a, w, k, u); ++k) {
-        // the previous unit's stores are done before this unit's value-ring bookkeeping starts
-        wait_vmcnt<0>();
-        if (kMode == kModeTrans)
-            consume_unit<false, 2, true, false>(a, u, lds, cw, lane, it0, spun_out);
-        else if (kMode == kModeA || kMode == kModeB)
-            consume_unit<true, 2, false, true>(a, u, lds, cw, lane, it0, spun_out);
-        else if (kMode == kModeWhole || u.half < 0)
-            consume_unit<true, 2, false, false>(a, u, lds, cw, lane, it0, spun_out);
-        else
-            consume_unit<true, 1, false, false>(a, u, lds, cw, lane, it0, spun_out);
-        it0 += (int)(u.c1 - u.c0);
+    if constexpr (kMode == kModeWhole || kMode == kModeHalves) {
+        // Whole chains, several per workgroup: the next unit's lookups go out before this unit
+        // runs and complete meanwhile, and the previous unit's state and output stores may still
+        // be in flight when this one starts (vector memory operations complete in issue order,
+        // so the value ring's counted waits, with those older stores ahead of them, still mean
+        // what they say).
+        Unit next;
+        bool have = unit_at<kMode>(a, w, 0, u);
+        for (int64_t k = 0; have; ++k) {
+            const bool have_next = unit_at<kMode>(a, w, k + 1, next);
+            if (kMode == kModeWhole || u.half < 0)
+                consume_unit<true, 2, false, false>(a, u, lds, cw, lane, it0, spun_out);
+            else
+                consume_unit<true, 1, false, false>(a, u, lds, cw, lane, it0, spun_out);
+            it0 += (int)(u.c1 - u.c0);
+            u = next;
+            have = have_next;
+        }
+    } else {
+        for (int64_t k = 0; unit_at<kMode>(a, w, k, u); ++k) {
+            // the previous unit's stores are done before this unit's value-ring bookkeeping starts
+            wait_vmcnt<0>();
+            if (kMode == kModeTrans)
+                consume_unit<false, 2, true, false>(a, u, lds, cw, lane, it0, spun_out);
+            else
+                consume_unit<true, 2, false, true>(a, u, lds, cw, lane, it0, spun_out);
+            it0 += (int)(u.c1 - u.c0);
+        }
     }
 }
 
