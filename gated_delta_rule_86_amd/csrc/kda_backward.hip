@@ -190,6 +190,16 @@ struct BwdArgs {
                              // or dL/dS after it (odd chunks), state_at
     float *xf, *xb;          // [chunks][H][2048]: V' and dL/dV' (rows_at)
     float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
+    // cut plan (plen > 0): chunks per piece; per sequence the first piece index (pieces
+    // counted over the sequences, the same for every head); per (piece, head, direction) the
+    // start state, F and Phi (fp32, row-major [value row][channel]), the squared norms of F and
+    // of the start state per part, and the chunks each part's transition run took (-1: all)
+    int64_t plen;
+    int trunc;               // transition runs may stop (in-kernel l2norm and beta sigmoid)
+    int64_t *poff;           // [N + 1]
+    float *pst;              // [pieces][H][2][3][16384]
+    float *pnrm;             // [pieces][H][2][8]
+    int32_t *pz;             // [pieces][H][2][4]
 };
 
 // ---- per-chunk operands (shared by bwd_ops_kernel and bwd_grad_kernel) ----
@@ -527,40 +537,99 @@ __device__ __forceinline__ void stage_store(int role, const StageRegs &r, ChainS
 // s_waitcnt vmcnt(0), the other counters untouched
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
-// Workgroup b: XCD b % 8, part (b / 8) % (2 kCh) of unit (b / (16 kCh)) 8 + b % 8; unit u:
-// chain u / 2, role u % 2.  A wave's state is held transposed in the D layout: its tile e
-// (channels 16 ct .., ct = ct0 + e) has in lane L element i S[v0 + L % 16][16 ct + 4 (L / 16) + i].
-template <int kCh>
+// Launch kinds of the chain kernel: whole chains, and the cut plan's pass A, transition runs
+// and pass B (one workgroup per piece, direction and part).
+constexpr int kChWhole = 0, kChA = 1, kChT = 2, kChB = 3;
+constexpr int kPieceParts = 2;  // the cut plan runs bwd_chain_kernel<1, ...>
+
+// Workgroup b: XCD b % 8, part (b / 8) % (2 kCh) of unit (b / (16 kCh)) 8 + b % 8.  Whole
+// chains: unit u is chain u / 2, direction (role) u % 2.  Cut plan: unit u is piece slot
+// u / (2 H) (pieces counted over the sequences), head (u / 2) % H, direction u % 2.  A wave's
+// state is held transposed in the D layout: its tile e (channels 16 ct .., ct = ct0 + e) has in
+// lane L element i S[v0 + L % 16][16 ct + 4 (L / 16) + i].
+template <int kCh, int kMode>
 __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 {
     constexpr int kRows = 64 / kCh, kTiles = 8 / kCh, kParts = 2 * kCh;
+    constexpr bool kPiece = kMode != kChWhole;
+    static_assert(!kPiece || kParts == kPieceParts, "the cut plan runs one channel part per wave");
     // stage buffers: one where the chains are many (kCh = 1: 33 KB of LDS, so that three
     // workgroups fit a CU, at the price of a barrier before each refill), two otherwise
     constexpr int kSt = kCh == 1 ? 1 : 2;
     __shared__ __attribute__((aligned(16))) ChainStage<kRows> s_st[kSt];
     __shared__ __attribute__((aligned(16))) float s_x[kCh == 2 ? kChainThreads / 64 : 1][64][4];  // half sums
+    __shared__ int s_vote[kMode == kChT ? 2 : 1][kChainThreads / 64];  // transition runs: a wave's entries not all small
+    __shared__ float s_nrm[kChainThreads / 64];
     const int64_t bid = blockIdx.x;
     const int xcd = (int)(bid & 7);
     const int64_t slot = bid >> 3;
     const int part = (int)(slot % kParts);
     const int64_t unit = (slot / kParts) * 8 + xcd;
     const int64_t H = a.H;
-    if (unit >= 2 * a.N * H)
+    if (unit >= 2 * (kPiece ? a.poff[a.N] : a.N) * H)
         return;
     const int role = (int)(unit & 1);
-    const int64_t chain = unit >> 1, n = chain / H;
+    const int64_t chain = unit >> 1;
     const int h = (int)(chain % H);
+    // whole chains: sequence n; cut plan: piece slot q of sequence n, piece k (chunk order) of
+    // its P, w in walk order
+    int64_t n = chain / H, q = 0, P = 1, w = 0;
+    if constexpr (kPiece) {
+        q = n;
+        int64_t lo = 0, hi = a.N - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (a.poff[mid + 1] > q)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        n = lo;
+        P = a.poff[n + 1] - a.poff[n];
+        const int64_t k = q - a.poff[n];
+        w = role ? P - 1 - k : k;
+        if ((kMode == kChT || kMode == kChB) && w == 0)
+            return;  // the first piece of a walk starts from the true state in pass A
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, m = lane & 15;
     const int rg = wave / kCh, hc = wave % kCh;                 // row group, channel half
     const int v0 = kRows * part + 16 * rg, ct0 = kTiles * hc;  // value rows v0 .., channel tiles ct0 ..
     const int64_t start = a.seq_start[n], len = a.seq_len[n], off = a.seq_off[n];
     const int64_t nch = (len + kCH - 1) / kCH;
+    // the chunks [c0, c1) this workgroup walks
+    int64_t c0 = 0, c1 = nch;
+    if constexpr (kPiece) {
+        c0 = (q - a.poff[n]) * a.plen;
+        c1 = c0 + a.plen < nch ? c0 + a.plen : nch;
+    }
     auto slot_of = [&](int64_t j) { return (size_t)(off + j) * (size_t)H + (size_t)h; };
     auto op_of = [&](int64_t j) { return a.ops + slot_of(j) * kBwdOps; };
     auto tok_len = [&](int64_t j) { return (int)(len - kCH * j < kCH ? len - kCH * j : kCH); };
-    const size_t srow = (size_t)chain * kBState + (size_t)(v0 + m) * kD + 16 * ct0 + 4 * g;  // + 16 e
+    const size_t srow = (size_t)(n * H + h) * kBState + (size_t)(v0 + m) * kD + 16 * ct0 + 4 * g;  // + 16 e
+    const size_t prow = (size_t)(v0 + m) * kD + 16 * ct0 + 4 * g;  // + 16 e (piece states)
+    // cut plan: the (piece, head, direction) slot of walk piece ww of this sequence
+    auto pslot = [&](int64_t ww) {
+        const int64_t kk = role ? P - 1 - ww : ww;
+        return ((size_t)(a.poff[n] + kk) * (size_t)H + (size_t)h) * 2 + (size_t)role;
+    };
+    auto pstate = [&](int64_t ww, int which) { return a.pst + (pslot(ww) * 3 + (size_t)which) * kBState; };
     f32x4 S[kTiles];
-    if (role == 0) {
+    if (kMode == kChT) {
+        // from I: S[v][c] = (v == c)
+#pragma unroll
+        for (int e = 0; e < kTiles; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[e][i] = v0 + m == 16 * (ct0 + e) + 4 * g + i ? 1.f : 0.f;
+    } else if (kMode == kChB) {
+#pragma unroll
+        for (int e = 0; e < kTiles; ++e)
+            S[e] = ld4(pstate(w, 0) + prow + 16 * e);
+    } else if (w > 0) {
+#pragma unroll
+        for (int e = 0; e < kTiles; ++e)
+            S[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (role == 0) {
 #pragma unroll
         for (int e = 0; e < kTiles; ++e) {
             if (a.h0_dtype == 2)
@@ -575,6 +644,38 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         for (int e = 0; e < kTiles; ++e)
             S[e] = a.dht ? ld4(a.dht + srow + 16 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // the chunks this walk takes: pass B reruns the first z of a piece whose transition run
+    // stopped in every part (z the most any part took), all of it otherwise
+    int64_t n_it = c1 - c0;
+    bool dropped = false;
+    if (kMode == kChB && a.trunc) {
+        int zmax = 0;
+        dropped = true;
+#pragma unroll
+        for (int pp = 0; pp < kParts; ++pp) {
+            const int z = a.pz[pslot(w) * 4 + pp];
+            dropped = dropped && z >= 0;
+            zmax = z > zmax ? z : zmax;
+        }
+        if (dropped && zmax < n_it)
+            n_it = zmax;
+    }
+    // transition runs: the stop threshold kTruncRel |F_w|_F / (|st_1|_F + |F_1|_F + .. + |F_{w-1}|_F)
+    float thr = 0.f;
+    if (kMode == kChT && a.trunc) {
+        auto fro = [&](int64_t ww, int which) {
+            const float *p = a.pnrm + pslot(ww) * 8 + 4 * which;
+            float t = 0.f;
+#pragma unroll
+            for (int pp = 0; pp < kParts; ++pp)
+                t += p[pp];
+            return sqrtf(t);
+        };
+        float bound = fro(1, 1);
+        for (int64_t i = 1; i < w; ++i)
+            bound += fro(i, 0);
+        thr = bound == 0.f ? __builtin_inff() : kTruncRel * fro(w, 0) / bound;
+    }
     // -I (bf16) as the A operand of split_tile: lane m + 16 (m / 4), element m % 4
     uint32_t nI0 = 0u, nI1 = 0u;
     if (g == (m >> 2)) {
@@ -587,19 +688,21 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
     // The operands of chunk it + 1 are requested while chunk it runs.
     wait_vmem();  // the initial state is in (so that no wait inside the loop is for it)
     StageRegs rg_;
-    auto chunk_of = [&](int64_t it) { return role ? nch - 1 - it : it; };
+    auto chunk_of = [&](int64_t it) { return role ? c1 - 1 - it : c0 + it; };
     auto load = [&](int64_t it) {
         const int64_t j = chunk_of(it);
         stage_load<kRows>(a, role, part, op_of(j), start + kCH * j, tok_len(j), h, rg_, tid);
     };
-    if (nch > 0) {
+    if (n_it > 0) {
         load(0);
         stage_store<kRows>(role, rg_, s_st[0], tok_len(chunk_of(0)), tid);
     }
     __syncthreads();
-    for (int64_t it = 0; it < nch; ++it) {
+    int64_t z = -1;  // transition runs: chunks run before the stop
+    for (int64_t it = 0; it < n_it; ++it) {
         const int64_t j = chunk_of(it);
-        const bool more = it + 1 < nch;
+        const bool more = it + 1 < n_it;
+        const bool upd = kPiece ? j + 1 < nch : more;  // role 0: no update after a sequence's last chunk
         if (more)
             load(it + 1);
         const ChainStage<kRows> &st = s_st[kSt == 1 ? 0 : (it & 1)];
@@ -610,9 +713,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             A[e] = ldu4(st.A0 + m * kD + 16 * (ct0 + e) + 4 * g);
         // X starts at U (role 0) or at U~ = lower(QG KI^T)^T dO (role 1, one fp32 product, in an
         // accumulator of its own so that it overlaps the first product) at the wave's value
-        // columns, in the first wave of a row group
+        // columns, in the first wave of a row group; transition runs take U and dO as zero
         f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0, XU = X0;
-        if (hc == 0) {
+        if (hc == 0 && kMode != kChT) {
             if (role) {
                 f32x4 ua, ub;
 #pragma unroll
@@ -629,7 +732,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
         }
         // the state before an even chunk (role 0) or dL/dS after an odd one (role 1), in the
         // tiled layout (state_at): each store of the wave writes 256 contiguous bytes
-        if ((int)(j & 1) == role) {
+        if (kMode != kChT && (int)(j & 1) == role) {
             float *ck = a.ck + sl * kBState + (size_t)(v0 >> 4) * (8 * 256) + 256 * ct0 + 16 * g + m;
 #pragma unroll
             for (int e = 0; e < kTiles; ++e)
@@ -651,14 +754,14 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             const f32x4 other = ld4(&s_x[wave ^ 1][lane][0]);
             X = hc == 0 ? X + other : other + X;  // the same sum in both waves
         }
-        if (hc == 0) {
+        if (hc == 0 && kMode != kChT) {
             float *xo = (role ? a.xb : a.xf) + sl * (kCH * kD) + (v0 >> 4) * 256 + 16 * g + m;  // (rows_at)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 xo[64 * i] = X[i];
         }
         if (role == 0) {
-            if (more) {  // S <- S Diag(gamma) + V'^T KD
+            if (upd) {  // S <- S Diag(gamma) + V'^T KD
                 const u32x4 xs = split_tile(X, nI0, nI1);
                 u32x4 K[kTiles];
                 f32x4 Gm[kTiles];
@@ -673,8 +776,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
             }
         } else {  // D <- D Diag(gamma) + dO^T QG - dV'^T W
             // dO is bf16: its four rows as one packed word pair, no lo part
-            const uint32_t o0 = pk_bf16(st.Y[4 * g][16 * rg + m], st.Y[4 * g + 1][16 * rg + m]);
-            const uint32_t o1 = pk_bf16(st.Y[4 * g + 2][16 * rg + m], st.Y[4 * g + 3][16 * rg + m]);
+            const uint32_t o0 = kMode == kChT ? 0u : pk_bf16(st.Y[4 * g][16 * rg + m], st.Y[4 * g + 1][16 * rg + m]);
+            const uint32_t o1 = kMode == kChT ? 0u : pk_bf16(st.Y[4 * g + 2][16 * rg + m], st.Y[4 * g + 3][16 * rg + m]);
             const u32x4 xs = split_tile(X, nI0, nI1);
 #pragma unroll
             for (int c4 = 0; c4 < kTiles; c4 += 4) {
@@ -691,17 +794,212 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
                     S[c4 + e] = mm3(Wt[e], xs, mm2(Q[e], o0, o1, S[c4 + e] * Gm[e]));
             }
         }
+        if (kMode == kChT && a.trunc) {
+            // vote: this wave's entries all below thr (NaN counts as big); two vote sets, used
+            // by alternate chunks, so that a wave that runs ahead does not overwrite a vote
+            // another wave has still to read
+            bool big = false;
+#pragma unroll
+            for (int e = 0; e < kTiles; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    big |= !(__builtin_fabsf(S[e][i]) < thr);
+            const bool wbig = __builtin_amdgcn_ballot_w64(big) != 0;
+            if (lane == 0)
+                s_vote[kMode == kChT ? (it & 1) : 0][wave] = wbig ? 1 : 0;
+        }
         if (kSt == 1)
             __syncthreads();  // every wave has read the stage of chunk it
         if (more)
             stage_store<kRows>(role, rg_, s_st[kSt == 1 ? 0 : ((it + 1) & 1)], tok_len(chunk_of(it + 1)), tid);
         __syncthreads();
+        if (kMode == kChT && a.trunc) {
+            int any = 0;
+#pragma unroll
+            for (int wv = 0; wv < kChainThreads / 64; ++wv)
+                any |= s_vote[kMode == kChT ? (it & 1) : 0][wv];
+            if (!any) {
+                z = it + 1;
+                break;
+            }
+        }
     }
-    if (role == 1 && a.dh0) {
+    // squared norm of the workgroup's rows of the end state (pass A)
+    auto sum_sq = [&]() {
+        float t = 0.f;
 #pragma unroll
         for (int e = 0; e < kTiles; ++e)
-            st4(a.dh0 + srow + 16 * e, S[e]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                t = fmaf(S[e][i], S[e][i], t);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            t += __shfl_xor(t, o);
+        if (lane == 0)
+            s_nrm[wave] = t;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kChainThreads / 64; ++wv)
+            tot += s_nrm[wv];
+        return tot;
+    };
+    auto store_state = [&](float *base) {
+#pragma unroll
+        for (int e = 0; e < kTiles; ++e)
+            st4(base + prow + 16 * e, S[e]);
+    };
+    if constexpr (kMode == kChWhole) {
+        if (role == 1 && a.dh0) {
+#pragma unroll
+            for (int e = 0; e < kTiles; ++e)
+                st4(a.dh0 + srow + 16 * e, S[e]);
+        }
+    } else if constexpr (kMode == kChA) {
+        if (P == 1) {
+            if (role == 1 && a.dh0) {
+#pragma unroll
+                for (int e = 0; e < kTiles; ++e)
+                    st4(a.dh0 + srow + 16 * e, S[e]);
+            }
+        } else {
+            // w = 0: the true start state of walk piece 1; otherwise F_w
+            const int which = w == 0 ? 0 : 1;
+            store_state(pstate(w == 0 ? 1 : w, which));
+            const float t = sum_sq();
+            if (tid == 0)
+                a.pnrm[pslot(w == 0 ? 1 : w) * 8 + 4 * (1 - which) + part] = t;
+        }
+    } else if constexpr (kMode == kChT) {
+        // Phi_w's rows; a part that stopped stores zero rows: they were below thr and cannot
+        // grow, so the scan's error from them stays under the bound of a dropped share
+        if (z >= 0) {
+#pragma unroll
+            for (int e = 0; e < kTiles; ++e)
+                S[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        store_state(pstate(w, 2));
+        if (tid == 0)
+            a.pz[pslot(w) * 4 + part] = (int32_t)z;
+    } else {
+        // pass B: the walk's last piece ends at the sequence's start (role 1: dL/dS_initial),
+        // from pass A's F where only the first chunks were rerun
+        if (role == 1 && w == P - 1 && a.dh0) {
+            const bool from_f = dropped && n_it < c1 - c0;
+#pragma unroll
+            for (int e = 0; e < kTiles; ++e)
+                st4(a.dh0 + srow + 16 * e, from_f ? ld4(pstate(w, 1) + prow + 16 * e) : S[e]);
+        }
     }
+}
+
+// Cut plan, scan: per (sequence, head, direction) with three or more pieces, in walk order
+// st_{w+1} = F_w where the transition run of piece w stopped in every part, else
+// st_w Phi_w + F_w (fp32 MFMA; the rows are independent: workgroup b takes rows 16 (b % 8) ..
+// of (sequence, head, direction) b / 8 and keeps them in LDS between steps).
+__global__ __launch_bounds__(256) void bwd_piece_scan_kernel(BwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float s_rows[kCH][kD + 4];
+    const int64_t b = blockIdx.x;
+    const int rb = (int)(b & 7);
+    const int64_t u = b >> 3;
+    const int role = (int)(u & 1);
+    const int64_t chain = u >> 1, n = chain / a.H;
+    const int h = (int)(chain % a.H);
+    if (n >= a.N)
+        return;
+    const int64_t P = a.poff[n + 1] - a.poff[n];
+    if (P < 3)
+        return;
+    auto pslot = [&](int64_t ww) {
+        const int64_t kk = role ? P - 1 - ww : ww;
+        return ((size_t)(a.poff[n] + kk) * (size_t)a.H + (size_t)h) * 2 + (size_t)role;
+    };
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, m = lane & 15;
+    const size_t r0 = (size_t)(kCH * rb) * kD;  // first element of the workgroup's rows
+    {
+        const float *st1 = a.pst + pslot(1) * 3 * kBState + r0;
+        for (int i = tid; i < kCH * kD / 4; i += 256)
+            st4(&s_rows[i / (kD / 4)][4 * (i % (kD / 4))], ld4(st1 + 4 * i));
+    }
+    __syncthreads();
+    for (int64_t w = 1; w + 1 < P; ++w) {
+        const size_t sw = pslot(w);
+        const float *F = a.pst + (sw * 3 + 1) * kBState + r0, *Phi = a.pst + (sw * 3 + 2) * kBState;
+        bool dropped = a.trunc != 0;
+#pragma unroll
+        for (int pp = 0; pp < kPieceParts; ++pp)
+            dropped = dropped && a.pz[sw * 4 + pp] >= 0;
+        float *dst = a.pst + pslot(w + 1) * 3 * kBState + r0;
+        // wave wv: output columns 32 wv .. + 31 as two 16-column tiles (D layout)
+        f32x4 acc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col0 = 32 * wv + 16 * t;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][i] = F[(size_t)(4 * g + i) * kD + col0 + m];
+            if (!dropped) {
+                for (int k0 = 0; k0 < kD; k0 += 16) {
+                    const f32x4 x = ld4(&s_rows[m][k0 + 4 * g]);
+                    f32x4 y;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        y[j] = Phi[(size_t)(k0 + 4 * g + j) * kD + col0 + m];
+                    acc[t] = mm4(x, y, acc[t]);
+                }
+            }
+        }
+        __syncthreads();  // every wave has read the rows
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col0 = 32 * wv + 16 * t;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s_rows[4 * g + i][col0 + m] = acc[t][i];
+                dst[(size_t)(4 * g + i) * kD + col0 + m] = acc[t][i];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Cut plan: the first piece of every sequence, poff[n] = sum over i < n of max(1,
+// ceil(chunks_i / plen)) (a sequence without chunks keeps one empty piece, which passes dL/dS
+// of the final state to dL/dS of the initial one).
+__global__ __launch_bounds__(256) void bwd_piece_table_kernel(BwdArgs a)
+{
+    __shared__ int64_t s_scan[256];
+    __shared__ int64_t s_carry;
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        s_carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < a.N; base += 256) {
+        const int64_t i = base + tid;
+        int64_t cnt = 0;
+        if (i < a.N) {
+            const int64_t nc = (a.seq_len[i] + kCH - 1) / kCH;
+            cnt = nc > a.plen ? (nc + a.plen - 1) / a.plen : 1;
+        }
+        s_scan[tid] = cnt;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int64_t x = tid >= d ? s_scan[tid - d] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        const int64_t carry = s_carry;
+        if (i < a.N)
+            a.poff[i + 1] = carry + s_scan[tid];
+        __syncthreads();
+        if (tid == 255)
+            s_carry = carry + s_scan[255];
+        __syncthreads();
+    }
+    if (tid == 0)
+        a.poff[0] = 0;
 }
 
 // ---- gradients of one chunk-head's tokens ----
@@ -1170,22 +1468,49 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.xf = reinterpret_cast<float *>(ws + f.bl.off_xf);
     a.xb = reinterpret_cast<float *>(ws + f.bl.off_xb);
     a.hpart = reinterpret_cast<float *>(ws + f.bl.off_hpart);
+    a.plen = f.bl.plen;
+    a.trunc = (a.flags & kBL2In) && (a.flags & kBSigIn);
+    a.poff = reinterpret_cast<int64_t *>(ws + f.bl.off_poff);
+    a.pst = reinterpret_cast<float *>(ws + f.bl.off_pst);
+    a.pnrm = reinterpret_cast<float *>(ws + f.bl.off_pnrm);
+    a.pz = reinterpret_cast<int32_t *>(ws + f.bl.off_pz);
     const int64_t toks = a.B * a.T * a.H;
     const int64_t units = 2 * a.N * a.H;          // (chain, role)
     const int64_t slots = a.chunks * a.H;         // chunk-heads (a bound)
     auto check = [] { return hipGetLastError(); };
     hipError_t e;
+    if (units > 0 && a.plen > 0) {
+        hipLaunchKernelGGL(bwd_piece_table_kernel, dim3(1), dim3(256), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
+    }
     if (toks > 0) {
         hipLaunchKernelGGL(bwd_ops_kernel, dim3((unsigned)slots), dim3(kGradThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
     }
-    if (units > 0) {
+    if (units > 0 && a.plen > 0) {
+        // cut plan: pass A, transition runs, scan, pass B; 2 workgroups per (piece, head,
+        // direction), in groups of 8 (one per XCD)
+        const unsigned grid = (unsigned)(cdiv(2 * f.bl.pieces * a.H, 8) * 16);
+        hipLaunchKernelGGL((bwd_chain_kernel<1, kChA>), dim3(grid), dim3(kChainThreads), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((bwd_chain_kernel<1, kChT>), dim3(grid), dim3(kChainThreads), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(bwd_piece_scan_kernel, dim3((unsigned)(units * 8)), dim3(256), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((bwd_chain_kernel<1, kChB>), dim3(grid), dim3(kChainThreads), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
+    } else if (units > 0) {
         // 2 kCh workgroups per unit, units in groups of 8 (one per XCD)
         if (units <= kChainUnitsSplit)
-            hipLaunchKernelGGL(bwd_chain_kernel<2>, dim3((unsigned)(cdiv(units, 8) * 32)), dim3(kChainThreads), 0, s, a);
+            hipLaunchKernelGGL((bwd_chain_kernel<2, kChWhole>), dim3((unsigned)(cdiv(units, 8) * 32)), dim3(kChainThreads), 0, s, a);
         else
-            hipLaunchKernelGGL(bwd_chain_kernel<1>, dim3((unsigned)(cdiv(units, 8) * 16)), dim3(kChainThreads), 0, s, a);
+            hipLaunchKernelGGL((bwd_chain_kernel<1, kChWhole>), dim3((unsigned)(cdiv(units, 8) * 16)), dim3(kChainThreads), 0, s, a);
         if ((e = check()) != hipSuccess)
             return e;
     }

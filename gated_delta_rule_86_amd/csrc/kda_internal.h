@@ -190,10 +190,48 @@ constexpr int kHeadSlices = 64;  // token slices of the backward pass's per-head
 // gamma (128)
 constexpr int kBwdOps = 4 * kCH * kD + kCH * kCH + kD;
 
+// Backward cut plan.  Both chains of the backward pass are affine in their carried matrix:
+// the state forwards, S' = S A_j + U_j^T KD_j with A_j = Diag(gamma_j) - W_j^T KD_j, and dL/dS
+// backwards, D' = D A_j^T + dO_j^T (QG_j - A_qk,j W_j).  Where the chains are few and long, a
+// sequence is cut into pieces of L chunks (the last one shorter) and, per (sequence, head,
+// direction), its pieces in walk order w = 0 .. P-1 (chunk order forwards, reversed
+// backwards) run as the forward pass's cut plan:
+//   pass A:      every piece with its outputs; w = 0 from the true start (initial state, or
+//                dL/dS_final), the others from zero; end states and their norms kept;
+//   transitions: every piece w >= 1 from I with zero inputs.  A_j^T has the norms of A_j, so
+//                the forward plan's bound holds: with the in-kernel l2norm and sigmoid the run
+//                stops once every entry is below kTruncRel |F_w|_F / B_w, with B_w = |st_1|_F +
+//                |F_1|_F + ... + |F_{w-1}|_F, and records z (the chunks it ran);
+//   scan:        st_{w+1} = F_w where the run stopped, else st_w Phi_w + F_w (fp32);
+//   pass B:      every piece w >= 1 again from st_w with its outputs: the first z chunks where
+//                the run stopped (pass A's outputs are right from there on), else all of it.
+// The whole-chain kernel is latency-bound where the chains are few: the plan is taken when
+// sequences average kBwdCutMinAvg chunks or more and pass A then has about kBwdTargetWgs
+// workgroups (two per piece and direction), pieces of at least kBwdPieceMin chunks and
+// two or more pieces per sequence on average.
+constexpr int64_t kBwdCutMinAvg = 64;
+constexpr int64_t kBwdPieceMin = 8;
+constexpr int64_t kBwdTargetWgs = 1536;
+
+// Chunks per piece of the backward cut plan, 0 for whole chains (chunks: the chunk-count
+// bound of a head; nseq: sequences).
+inline int64_t bwd_piece_len(int64_t chunks, int64_t nseq, int64_t H)
+{
+    if (nseq < 1 || H < 1 || chunks < nseq * kBwdCutMinAvg)
+        return 0;
+    int64_t L = cdiv(chunks * H * 4, kBwdTargetWgs);
+    if (L < kBwdPieceMin)
+        L = kBwdPieceMin;
+    return chunks >= 2 * L * nseq ? L : 0;
+}
+
 struct BwdLayout {
     Layout tab;
     int64_t chunks;  // bound on the chunk count of a head (the slots per head)
+    int64_t plen;    // cut plan: chunks per piece (0: whole chains)
+    int64_t pieces;  // cut plan: bound on the pieces of a head
     size_t off_ops, off_ck, off_xf, off_xb, off_hpart;
+    size_t off_poff, off_pst, off_pnrm, off_pz;  // cut plan (0 without)
     size_t total;
 };
 
@@ -215,6 +253,18 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
     L->off_xf = take(ch * kCH * kD * sizeof(float));
     L->off_xb = take(ch * kCH * kD * sizeof(float));
     L->off_hpart = take((size_t)H * kHeadSlices * 2 * kD * sizeof(float));
+    L->plen = bwd_piece_len(L->chunks, L->tab.n_seq, H);
+    L->pieces = 0;
+    L->off_poff = L->off_pst = L->off_pnrm = L->off_pz = 0;
+    if (L->plen > 0) {
+        // per sequence max(1, ceil(chunks / L)) pieces: at most chunks / L + 1 each
+        L->pieces = cdiv(L->chunks, L->plen) + L->tab.n_seq;
+        const size_t pu = (size_t)L->pieces * (size_t)H * 2;  // (piece, head, direction) slots
+        L->off_poff = take((size_t)(L->tab.n_seq + 1) * sizeof(int64_t));
+        L->off_pst = take(pu * 3 * state);  // start state, F, Phi
+        L->off_pnrm = take(pu * 8 * sizeof(float));
+        L->off_pz = take(pu * 4 * sizeof(int32_t));
+    }
     L->total = off;
     return true;
 }

@@ -271,7 +271,12 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int ha
  * Outputs must not overlap any input or each other (KDA_ERR_ALIAS).  Same error codes as
  * kda_fwd_ex otherwise.  Work is enqueued on `stream`; nothing is allocated.  The pass runs
  * in 16-token chunks: the state runs forwards and dL/dS backwards over the chunks of each
- * (sequence, head), and the tokens' gradients are formed per chunk in parallel.
+ * (sequence, head), and the tokens' gradients are formed per chunk in parallel.  Where the
+ * sequences are few and long (64 chunks or more on average), both walks are cut into pieces
+ * that run in parallel and are joined by an affine scan (with the in-kernel l2norm and
+ * sigmoid, a start state's share that has fallen below 2^-30 of a piece's own end state is
+ * dropped, as in kda_fwd's cut plan).  Results are deterministic: fixed summation orders,
+ * no atomics.
  */
 kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta, float scale,
                    const float *A_log, const float *dt_bias, float lower_bound, const void *initial_state,
@@ -286,8 +291,11 @@ kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, c
  * 16-token chunk of each head (counted as ceil(T / 16) per batch row, or ceil(T / 16) + N
  * with cu_seqlens) 33.5 KiB of chunk operands, one fp32 state (64 KiB: the state before the
  * chunk for the even chunks of a sequence, dL/dS after it for the odd ones) and the chunk's
- * V' and dL/dV' (8 KiB each), and 64 KiB per head of partial sums.  Returns 0 for invalid
- * sizes.
+ * V' and dL/dV' (8 KiB each), and 64 KiB per head of partial sums; when the pass cuts its
+ * walks into pieces, also three fp32 states per (piece, head, direction) (pieces of L chunks,
+ * L = max(8, ceil(4 H C / 1536)) with C the chunk count above; at most ceil(C / L) + N pieces
+ * per head, N the number of sequences).
+ * Returns 0 for invalid sizes.
  */
 size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 

@@ -129,6 +129,22 @@ def cut_plan(B, T, H, N=0, varlen=False):
     return P if P >= 2 else 1
 
 
+# ---- backward cut plan (replica of the host decision) ----
+BWD_CUT_MIN_AVG = 64   # average chunks per sequence
+BWD_PIECE_MIN = 8      # chunks per piece, at least
+BWD_TARGET_WGS = 1536  # pass A workgroups aimed at
+
+
+def bwd_piece_len(B, T, H, N=0, varlen=False):
+    """Chunks per piece of the backward cut plan for these sizes, 0 for whole chains."""
+    nseq = N if varlen else B
+    chunks = -(-T // 16) + N if varlen else B * -(-T // 16)
+    if nseq < 1 or H < 1 or chunks < nseq * BWD_CUT_MIN_AVG:
+        return 0
+    L = max(BWD_PIECE_MIN, -(-(chunks * H * 4) // BWD_TARGET_WGS))
+    return L if chunks >= 2 * L * nseq else 0
+
+
 def expected_cuts(seq_off, P):
     """The cuts (sequence, chunk offset) j = 0 .. P the chunk table computes from the chunk
     offsets: x_j = floor(j C / P), moved to the nearest sequence boundary within

@@ -15,7 +15,7 @@ import pytest
 import oracle
 from gated_delta_rule_86_amd import kda
 from gated_delta_rule_86_amd import workloads as W
-from kda_testutil import bf16_tensor, rel_l2, state_tensor, torch_dev
+from kda_testutil import bf16_tensor, bwd_piece_len, rel_l2, state_tensor, torch_dev
 
 pytestmark = pytest.mark.gpu
 REL = 1e-4
@@ -107,6 +107,51 @@ def test_backward_long_chains():
     """Two chains of 2100 tokens (132 chunks of checkpoints each) with weak decay."""
     w = W.make("bwd_long", 1, 2100, 2, seed=705, lower_bound=-0.05, state_dtype="fp32")
     grads_parity(w, 9, True, "T=2100 H=2 lb=-0.05")
+
+
+def _pieces(w, L):
+    lens = np.diff(w.cu_seqlens) if w.cu_seqlens is not None else [w.T] * w.B
+    return [max(1, -(-(-(-int(n) // 16)) // L)) for n in lens]
+
+
+@pytest.mark.parametrize("lb", [0.0, -0.05, -2.0, -5.0])
+def test_backward_cut_plan_lower_bounds(lb):
+    """One long sequence per row cut into pieces (pass A, transition runs, scan, pass B):
+    without decay no transition run stops and the scan composes every piece; with a strong
+    gate the runs stop within a few chunks and pass B reruns only those."""
+    w = W.make(f"bwd_cut_lb{lb}", 1, 2048, 2, seed=730, lower_bound=lb, state_dtype="fp32")
+    L = bwd_piece_len(w.B, w.T, w.H)
+    assert L > 0 and _pieces(w, L) == [16]
+    grads_parity(w, 30, True, f"cut plan T=2048 H=2 lb={lb} (16 pieces)")
+
+
+def test_backward_cut_plan_batch_rows():
+    """Two batch rows of 1100 tokens (9 pieces each, the last one 5 chunks), bf16 initial
+    state, three heads."""
+    w = W.make("bwd_cut_rows", 2, 1100, 3, seed=731, state_dtype="bf16")
+    L = bwd_piece_len(w.B, w.T, w.H)
+    assert L == 8 and _pieces(w, L) == [9, 9]
+    grads_parity(w, 31, True, "cut plan B=2 T=1100 H=3")
+
+
+@pytest.mark.parametrize("flags,lb", [(7, -0.05), (1, -2.0)])
+def test_backward_cut_plan_varlen(flags, lb):
+    """Varlen batch on the cut plan with an empty, a one-token and a two-chunk sequence among
+    two long ones; weak decay (scan through every piece), and the l2norm and sigmoid
+    switched off (no transition run may stop: the bound needs them)."""
+    w = W.make(f"bwd_cut_var{flags}", 1, 0, 2, lengths=[3500, 0, 17, 2600, 1], seed=732 + flags,
+               lower_bound=lb, flags=flags, state_dtype="fp32")
+    L = bwd_piece_len(w.B, w.T, w.H, w.N, True)
+    assert L == 8 and _pieces(w, L) == [28, 1, 1, 21, 1]
+    grads_parity(w, 32 + flags, True, f"cut plan varlen flags={flags} lb={lb}")
+
+
+def test_backward_cut_plan_no_states():
+    """Cut plan without an initial state or a final-state gradient (both chains start from
+    zero)."""
+    w = W.make("bwd_cut_none", 1, 1600, 2, seed=733, state_dtype="none", with_initial=False)
+    assert bwd_piece_len(w.B, w.T, w.H) > 0
+    grads_parity(w, 34, False, "cut plan T=1600 H=2, no states")
 
 
 def test_backward_T_zero():
