@@ -1,7 +1,8 @@
 """Backward parity at the full sizes of the workloads the backward bench times (B=2 T=4096
 H=16 fp32 state; varlen N=8 up to 8192 tokens H=32 bf16 state, lower_bound -2; varlen N=256
-up to 512 tokens H=32 fp32 state), in the launch configuration ``bench.py --backward`` uses:
-one kda_bwd call over the whole batch with a random dL/dout and dL/dfinal_state.
+up to 512 tokens H=32 fp32 state; B=1 T=2^20 H=8 fp32 state, in windows), in the launch
+configuration ``bench.py --backward`` uses: one kda_bwd call over the whole batch with a
+random dL/dout and dL/dfinal_state.
 
 The gradients of one chain (sequence, head) depend on that chain's inputs alone, so sampled
 chains -- the longest sequence among them -- are compared with the fp64 backward oracle run
@@ -84,6 +85,60 @@ def test_backward_full_size_sampled_chains(wl, picks):
     # dt_bias and A_log gradients: their definition from the GPU's dg, summed in fp64; each entry
     # within 1e-4 of the sum of its terms' magnitudes (fp32 summation: runs of a few hundred
     # terms per thread, n eps ~ 3e-5, then 128 partial sums in a fixed order)
+    dg = r["dg"].double()
+    x = d["g"].double() + dt_bias.double()[None, None]
+    for name, exp, mag in (("ddt_bias", dg.sum(dim=(0, 1)), dg.abs().sum(dim=(0, 1))),
+                           ("dA_log", (dg * x).sum(dim=(0, 1, 3)), (dg * x).abs().sum(dim=(0, 1, 3)))):
+        got = r[name].double()
+        err = (got - exp).abs()
+        assert bool((err <= 1e-4 * mag).all()), (w.name, name, float((err / mag).max()))
+        print(f"{w.name} {name}: max |err| / sum |terms| = {float((err / mag).max()):.1e}", flush=True)
+
+
+def test_backward_long_context_windows():
+    """The 2^20-token workload (B=1 T=1,048,576 H=8, fp32 state, lower_bound -5), one kda_bwd
+    call as ``bench.py --backward --workload 3`` makes it: the backward walks run on the cut
+    plan (48 pieces of 1,366 chunks per chain and direction).  A 1M-token chain is beyond the
+    fp64 oracle, so windows are compared: the oracle runs on tokens [t0 - M, t1 + M) of a chain
+    from a zero state (the true initial state where t0 - M <= 0) and with a zero dL/dS at its
+    end (the true dL/dfinal_state where t1 + M reaches T); with this gate every token scales
+    the carried state by at most e^(-5 sigmoid(x)), so over M = 512 tokens the cut-off parts
+    fall far below fp64 rounding, and the gradients of [t0, t1) must match as for a whole
+    chain.  Windows: the first tokens (with dL/dinitial_state), one across a cut between
+    pieces, one inside a piece, and the last tokens."""
+    import torch
+    w = W.config(3)
+    dev = torch_dev()
+    rng = np.random.default_rng(903)
+    dout = W.f32_to_bf16_bits(rng.standard_normal((w.B, w.T, w.H, 128), dtype=np.float32))
+    dht = rng.standard_normal((w.N, w.H, 128, 128), dtype=np.float32)
+    d = {n: bf16_tensor(getattr(w, n)) for n in ("q", "k", "v", "g", "beta")}
+    A_log = torch.from_numpy(w.A_log).to(dev)
+    dt_bias = torch.from_numpy(w.dt_bias).to(dev)
+    print(f"case {w.name}: kda_bwd over {w.head_tokens} head-tokens", flush=True)
+    r = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, A_log, dt_bias, w.lower_bound,
+                bf16_tensor(dout), state_tensor(w.initial_state), torch.from_numpy(dht).to(dev))
+    torch.cuda.synchronize()
+    T, M, piece = w.T, 512, 1366 * 16
+    windows = [(0, 1024, 0), (3 * piece - 600, 3 * piece + 600, 5), (20 * piece + 4000, 20 * piece + 5000, 7),
+               (T - 1024, T, 3)]
+    for t0, t1, h in windows:
+        a0, a1 = max(0, t0 - M), min(T, t1 + M)
+        sl = lambda x: np.ascontiguousarray(x[0:1, a0:a1, h:h + 1])
+        h0 = np.ascontiguousarray(w.initial_state[0:1, h:h + 1]) if a0 == 0 else None
+        dh = np.ascontiguousarray(dht[0:1, h:h + 1]) if a1 == T else None
+        ref = oracle.kda_bwd(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), w.scale,
+                             np.ascontiguousarray(w.A_log[h:h + 1]), np.ascontiguousarray(w.dt_bias[h:h + 1]),
+                             w.lower_bound, sl(dout), h0, dh, flags=w.flags)
+        msg = []
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            got = r[name][0, t0:t1, h].double().cpu().numpy()
+            rl = _check(got, ref[name][0, t0 - a0:t1 - a0, 0], f"window [{t0}, {t1}) head {h} {name}")
+            msg.append(f"{name} {rl:.1e}")
+        if a0 == 0:
+            got = r["dinitial_state"][0, h].double().cpu().numpy()
+            msg.append(f"dh0 {_check(got, ref['dh0'][0, 0], f'head {h} dinitial_state'):.1e}")
+        print(f"{w.name} window [{t0}, {t1}) head {h}: relL2 " + " ".join(msg), flush=True)
     dg = r["dg"].double()
     x = d["g"].double() + dt_bias.double()[None, None]
     for name, exp, mag in (("ddt_bias", dg.sum(dim=(0, 1)), dg.abs().sum(dim=(0, 1))),
