@@ -207,11 +207,12 @@ constexpr int kBwdOps = 4 * kCH * kD + kCH * kCH + kD;
 //                the run stopped (pass A's outputs are right from there on), else all of it.
 // The whole-chain kernel is latency-bound where the chains are few: the plan is taken when
 // sequences average kBwdCutMinAvg chunks or more and pass A then has about kBwdTargetWgs
-// workgroups (two per piece and direction), pieces of at least kBwdPieceMin chunks and
-// two or more pieces per sequence on average.
+// workgroups (two per piece and direction; 768 = three per CU, one round: pass A is bound by
+// HBM either way, and fewer pieces shorten the transition runs, the scan and pass B), pieces
+// of at least kBwdPieceMin chunks and two or more pieces per sequence on average.
 constexpr int64_t kBwdCutMinAvg = 64;
 constexpr int64_t kBwdPieceMin = 8;
-constexpr int64_t kBwdTargetWgs = 1536;
+constexpr int64_t kBwdTargetWgs = 768;
 
 // Chunks per piece of the backward cut plan, 0 for whole chains (chunks: the chunk-count
 // bound of a head; nseq: sequences).

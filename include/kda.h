@@ -293,7 +293,7 @@ kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, c
  * chunk for the even chunks of a sequence, dL/dS after it for the odd ones) and the chunk's
  * V' and dL/dV' (8 KiB each), and 64 KiB per head of partial sums; when the pass cuts its
  * walks into pieces, also three fp32 states per (piece, head, direction) (pieces of L chunks,
- * L = max(8, ceil(4 H C / 1536)) with C the chunk count above; at most ceil(C / L) + N pieces
+ * L = max(8, ceil(4 H C / 768)) with C the chunk count above; at most ceil(C / L) + N pieces
  * per head, N the number of sequences).
  * Returns 0 for invalid sizes.
  */

@@ -132,7 +132,7 @@ def cut_plan(B, T, H, N=0, varlen=False):
 # ---- backward cut plan (replica of the host decision) ----
 BWD_CUT_MIN_AVG = 64   # average chunks per sequence
 BWD_PIECE_MIN = 8      # chunks per piece, at least
-BWD_TARGET_WGS = 1536  # pass A workgroups aimed at
+BWD_TARGET_WGS = 768   # pass A workgroups aimed at
 
 
 def bwd_piece_len(B, T, H, N=0, varlen=False):

@@ -98,7 +98,7 @@ def test_backward_full_size_sampled_chains(wl, picks):
 def test_backward_long_context_windows():
     """The 2^20-token workload (B=1 T=1,048,576 H=8, fp32 state, lower_bound -5), one kda_bwd
     call as ``bench.py --backward --workload 3`` makes it: the backward walks run on the cut
-    plan (48 pieces of 1,366 chunks per chain and direction).  A 1M-token chain is beyond the
+    plan (24 pieces of 2,731 chunks per chain and direction, the last one 2,723).  A 1M-token chain is beyond the
     fp64 oracle, so windows are compared: the oracle runs on tokens [t0 - M, t1 + M) of a chain
     from a zero state (the true initial state where t0 - M <= 0) and with a zero dL/dS at its
     end (the true dL/dfinal_state where t1 + M reaches T); with this gate every token scales
@@ -119,7 +119,7 @@ def test_backward_long_context_windows():
     r = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, A_log, dt_bias, w.lower_bound,
                 bf16_tensor(dout), state_tensor(w.initial_state), torch.from_numpy(dht).to(dev))
     torch.cuda.synchronize()
-    T, M, piece = w.T, 512, 1366 * 16
+    T, M, piece = w.T, 512, 2731 * 16
     windows = [(0, 1024, 0), (3 * piece - 600, 3 * piece + 600, 5), (20 * piece + 4000, 20 * piece + 5000, 7),
                (T - 1024, T, 3)]
     for t0, t1, h in windows:
