@@ -189,12 +189,20 @@ def test_backward_invalid_cu_seqlens():
     assert torch.equal(r["dinitial_state"], dht)
 
 
-def test_backward_deterministic_and_workspace_independent():
+@pytest.mark.parametrize("case", ["whole", "cut"])
+def test_backward_deterministic_and_workspace_independent(case):
     """Two kda_bwd calls give bitwise identical gradients (fixed summation orders, no atomics),
     also when the second one gets a workspace pre-filled with garbage: every per-chunk state,
-    operand and row region it reads was written by the same call."""
+    operand and row region it reads was written by the same call -- with whole-chain walks,
+    and on the cut plan (piece table, start states, F, Phi, norms and stop counts)."""
     import torch
-    w = W.make("bwd_det", 1, 0, 3, lengths=[333, 17, 0, 120], seed=708, state_dtype="fp32")
+    if case == "whole":
+        w = W.make("bwd_det", 1, 0, 3, lengths=[333, 17, 0, 120], seed=708, state_dtype="fp32")
+        assert bwd_piece_len(w.B, w.T, w.H, w.N, True) == 0
+    else:
+        w = W.make("bwd_det_cut", 1, 0, 2, lengths=[3000, 0, 1500, 40], seed=709, lower_bound=-1.0,
+                   state_dtype="fp32")
+        assert bwd_piece_len(w.B, w.T, w.H, w.N, True) > 0
     dev = torch_dev()
     rng = np.random.default_rng(14)
     dout = bf16_tensor(W.f32_to_bf16_bits(rng.normal(size=(w.B, w.T, w.H, 128)).astype(np.float32)))
