@@ -1376,31 +1376,56 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
 // dg * (g + dt_bias) (the gate's pre-activation x = e^{A_log} (g + dt_bias) has dx/dA_log = x
 // and the d log-decay / dx factor is already in dg).  Two passes with a fixed partition and a
 // fixed order (deterministic): bwd_head_part_kernel sums kHeadSlices contiguous token ranges
-// per head (two interleaved halves of each range meet in LDS), bwd_head_kernel adds the
-// slices in order.
+// per head (thread -> four channels and every eighth token of the range, four tokens' 16-byte
+// loads in flight at a time; the eight token lanes meet in LDS in order), bwd_head_kernel adds
+// the slices in order.
 __global__ __launch_bounds__(256) void bwd_head_part_kernel(BwdArgs a)
 {
-    __shared__ float s_d[2][kD], s_a[2][kD];
+    __shared__ f32x4 s_d[8][kD / 4], s_a[8][kD / 4];
     const int h = blockIdx.x / kHeadSlices, slice = blockIdx.x % kHeadSlices;
-    const int c = threadIdx.x & (kD - 1), half = threadIdx.x >> 7;
+    const int cq = threadIdx.x & (kD / 4 - 1), tl = threadIdx.x / (kD / 4);  // channels 4 cq .., token lane
     // with invalid cu_seqlens no token belongs to a sequence and dg is not written: sum nothing
     const int64_t ntok = *a.status ? 0 : a.B * a.T;
     const int64_t t0 = ntok * slice / kHeadSlices, t1 = ntok * (slice + 1) / kHeadSlices;
-    const float dt = a.dt_bias[(size_t)h * kD + c];
-    float sd = 0.f, sa = 0.f;
-    for (int64_t t = t0 + half; t < t1; t += 2) {
-        const size_t i = ((size_t)t * (size_t)a.H + (size_t)h) * kD + (size_t)c;
-        const float d = a.dg[i];
-        sd += d;
-        sa = fmaf(d, bbf16(a.g[i]) + dt, sa);
+    const f32x4 dt = ld4(a.dt_bias + (size_t)h * kD + 4 * cq);
+    const size_t rs = (size_t)a.H * kD;  // elements per token row
+    const float *dgp = a.dg + (size_t)h * kD + 4 * cq;
+    const uint16_t *gp = a.g + (size_t)h * kD + 4 * cq;
+    f32x4 sd = {0.f, 0.f, 0.f, 0.f}, sa = sd;
+    auto add = [&](f32x4 d, f32x4 gv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sd[i] += d[i];
+            sa[i] = fmaf(d[i], gv[i] + dt[i], sa[i]);
+        }
+    };
+    int64_t t = t0 + tl;
+    for (; t + 24 < t1; t += 32) {
+        f32x4 d[4], gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            d[u] = ld4(dgp + (size_t)(t + 8 * u) * rs);
+            gv[u] = ld4_bf16(gp + (size_t)(t + 8 * u) * rs);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            add(d[u], gv[u]);
     }
-    s_d[half][c] = sd;
-    s_a[half][c] = sa;
+    for (; t < t1; t += 8)
+        add(ld4(dgp + (size_t)t * rs), ld4_bf16(gp + (size_t)t * rs));
+    s_d[tl][cq] = sd;
+    s_a[tl][cq] = sa;
     __syncthreads();
-    if (half == 0) {
+    if (tl == 0) {
+        f32x4 td = s_d[0][cq], ta = s_a[0][cq];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+            td += s_d[k][cq];
+            ta += s_a[k][cq];
+        }
         float *part = a.hpart + ((size_t)h * kHeadSlices + (size_t)slice) * 2 * kD;
-        part[c] = s_d[0][c] + s_d[1][c];
-        part[kD + c] = s_a[0][c] + s_a[1][c];
+        st4(part + 4 * cq, td);
+        st4(part + kD + 4 * cq, ta);
     }
 }
 
