@@ -190,6 +190,7 @@ struct BwdArgs {
                              // or dL/dS after it (odd chunks), state_at
     float *xf, *xb;          // [chunks][H][2048]: V' and dL/dV' (rows_at)
     float *hpart;            // [H][kHeadSlices][2][128]: head-gradient partial sums
+    int32_t *cinfo;          // [chunks][4]: where each chunk lies (bwd_chunk_info_kernel)
     // cut plan (plen > 0): chunks per piece; per sequence the first piece index (pieces
     // counted over the sequences, the same for every head); per (piece, head, direction) the
     // start state, F and Phi (fp32, row-major [value row][channel]), the squared norms of F and
@@ -204,15 +205,27 @@ struct BwdArgs {
 
 // ---- per-chunk operands (shared by bwd_ops_kernel and bwd_grad_kernel) ----
 // Chunk x of a head's chunk list: sequence n (the first with seq_off[n + 1] > x), chunk j of
-// it, first token t0 (row index), len tokens (1 .. 16).  False past the last chunk.
+// it, first token t0 (row index), len tokens (1 .. 16); kind: which of its two states the
+// chain does not store (1: S0, j odd; 0: D, j even and not the last chunk; 2: the last chunk
+// with j even, D = dL/dS_final); next_len: the next chunk's tokens (kind 0).  Written once per
+// call by bwd_chunk_info_kernel as four words per chunk, {t0 low, t0 high, n (-1 past the
+// last chunk), len | kind << 8 | next_len << 16}, so that a workgroup learns it with one
+// 16-byte load instead of a search over the sequences ahead of its first dependent loads.
 struct ChunkLoc {
     int64_t n, t0;
-    int len;
+    int len, kind, next_len;
 };
-__device__ bool locate_chunk(const BwdArgs &a, int64_t x, ChunkLoc &c)
+__global__ __launch_bounds__(256) void bwd_chunk_info_kernel(BwdArgs a)
 {
-    if (x >= a.seq_off[a.N])
-        return false;
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= a.chunks)
+        return;
+    int32_t *rec = a.cinfo + 4 * x;
+    if (x >= a.seq_off[a.N]) {
+        rec[0] = rec[1] = rec[3] = 0;
+        rec[2] = -1;
+        return;
+    }
     int64_t lo = 0, hi = a.N - 1;
     while (lo < hi) {
         const int64_t mid = (lo + hi) >> 1;
@@ -221,11 +234,27 @@ __device__ bool locate_chunk(const BwdArgs &a, int64_t x, ChunkLoc &c)
         else
             lo = mid + 1;
     }
-    const int64_t j = x - a.seq_off[lo];
-    c.n = lo;
-    c.t0 = a.seq_start[lo] + kCH * j;
-    const int64_t rem = a.seq_len[lo] - kCH * j;
-    c.len = rem < kCH ? (int)rem : kCH;
+    const int64_t j = x - a.seq_off[lo], t0 = a.seq_start[lo] + kCH * j, rem = a.seq_len[lo] - kCH * j;
+    const int len = rem < kCH ? (int)rem : kCH;
+    const int kind = (j & 1) ? 1 : (x + 1 < a.seq_off[lo + 1] ? 0 : 2);
+    const int64_t nrem = rem - kCH;
+    const int next = kind == 0 ? (nrem < kCH ? (int)nrem : kCH) : 0;
+    rec[0] = (int32_t)(uint32_t)(uint64_t)t0;
+    rec[1] = (int32_t)(uint32_t)((uint64_t)t0 >> 32);
+    rec[2] = (int32_t)lo;
+    rec[3] = len | (kind << 8) | (next << 16);
+}
+__device__ __forceinline__ bool locate_chunk(const BwdArgs &a, int64_t x, ChunkLoc &c)
+{
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 r = *reinterpret_cast<const i32x4 *>(a.cinfo + 4 * x);
+    if (r[2] < 0)
+        return false;
+    c.t0 = (int64_t)(((uint64_t)(uint32_t)r[1] << 32) | (uint32_t)r[0]);
+    c.n = r[2];
+    c.len = r[3] & 0xff;
+    c.kind = (r[3] >> 8) & 0xff;
+    c.next_len = r[3] >> 16;
     return true;
 }
 
@@ -1056,8 +1085,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
     //   odd chunk:             S0 = S0' Diag(gamma') + V'^T KD'   (' : the previous chunk)
     //   even chunk, not last:  D = D'' Diag(gamma'') + dO''^T QG'' - dV''^T W''   ('' : the next)
     //   even chunk, last:      D = dL/dS_final (zero when not given)
-    const int64_t seq0 = a.seq_off[c.n], jl = x - seq0;
-    const int kind = (jl & 1) ? 1 : (x + 1 < a.seq_off[c.n + 1] ? 0 : 2);
+    const int kind = c.kind;
     const size_t sn = kind == 0 ? sl + (size_t)a.H : kind == 1 ? sl - (size_t)a.H : sl;  // the neighbour
     f32x4 nb0 = {0.f, 0.f, 0.f, 0.f}, nb1 = nb0;  // B operands of the rebuild: rows 4 g + j, channel cc
     float ngam = 0.f;                             // the neighbour's gamma at channel cc
@@ -1107,7 +1135,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(4)
         if (kind == 0) {
             const float *xn = a.xb + sn * (kCH * kD) + nro;
             stu4(nX + v * kNT + 4 * q, split4(f32x4{xn[0], xn[64], xn[128], xn[192]}));
-            const int64_t rem = a.seq_len[c.n] - kCH * (jl + 1);  // the next chunk's tokens
+            const int rem = c.next_len;  // the next chunk's tokens
             uint32_t hw[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -1493,6 +1521,7 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     a.xf = reinterpret_cast<float *>(ws + f.bl.off_xf);
     a.xb = reinterpret_cast<float *>(ws + f.bl.off_xb);
     a.hpart = reinterpret_cast<float *>(ws + f.bl.off_hpart);
+    a.cinfo = reinterpret_cast<int32_t *>(ws + f.bl.off_cinfo);
     a.plen = f.bl.plen;
     a.trunc = (a.flags & kBL2In) && (a.flags & kBSigIn);
     a.poff = reinterpret_cast<int64_t *>(ws + f.bl.off_poff);
@@ -1504,6 +1533,11 @@ hipError_t launch_backward(const BwdLaunch &f, hipStream_t s)
     const int64_t slots = a.chunks * a.H;         // chunk-heads (a bound)
     auto check = [] { return hipGetLastError(); };
     hipError_t e;
+    if (toks > 0) {
+        hipLaunchKernelGGL(bwd_chunk_info_kernel, dim3((unsigned)cdiv(a.chunks, 256)), dim3(256), 0, s, a);
+        if ((e = check()) != hipSuccess)
+            return e;
+    }
     if (units > 0 && a.plen > 0) {
         hipLaunchKernelGGL(bwd_piece_table_kernel, dim3(1), dim3(256), 0, s, a);
         if ((e = check()) != hipSuccess)

@@ -231,7 +231,7 @@ struct BwdLayout {
     int64_t chunks;  // bound on the chunk count of a head (the slots per head)
     int64_t plen;    // cut plan: chunks per piece (0: whole chains)
     int64_t pieces;  // cut plan: bound on the pieces of a head
-    size_t off_ops, off_ck, off_xf, off_xb, off_hpart;
+    size_t off_ops, off_ck, off_xf, off_xb, off_hpart, off_cinfo;
     size_t off_poff, off_pst, off_pnrm, off_pz;  // cut plan (0 without)
     size_t total;
 };
@@ -254,6 +254,7 @@ inline bool make_bwd_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool var
     L->off_xf = take(ch * kCH * kD * sizeof(float));
     L->off_xb = take(ch * kCH * kD * sizeof(float));
     L->off_hpart = take((size_t)H * kHeadSlices * 2 * kD * sizeof(float));
+    L->off_cinfo = take((size_t)L->chunks * 4 * sizeof(int32_t));  // where each chunk lies
     L->plen = bwd_piece_len(L->chunks, L->tab.n_seq, H);
     L->pieces = 0;
     L->off_poff = L->off_pst = L->off_pnrm = L->off_pz = 0;
