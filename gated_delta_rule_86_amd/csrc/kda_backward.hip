@@ -28,6 +28,11 @@
 // accumulation), as in the forward chunk recurrence.
 //
 // Kernels, in launch order (the chunk table comes first, as in the forward pass):
+//   bwd_chunk_info_kernel
+//                      per chunk: where it lies (first token, sequence, length, which state the
+//                      chain does not store), one record read by the ops and gradient kernels
+//   bwd_piece_table_kernel (cut plan only)
+//                      the first piece of every sequence
 //   bwd_ops_kernel     per chunk-head: the chunk's activated rows (l2norm, gate, sigmoid, as
 //                      in the forward pass) and its operands for the two chains (-W, U, KD
 //                      row-major, QG^T, lower(QG KI^T), gamma; the chain kernel forms KD^T, -W^T
@@ -37,7 +42,9 @@
 //                      even chunks of the sequence; role 1 runs dL/dS backwards, writing dV' of
 //                      every chunk, D of the odd chunks and dL/dS_0.  The value rows of a state
 //                      are independent given the chunk operands, so two workgroups take 64
-//                      rows each.
+//                      rows each.  Where the sequences are few and long, the cut plan
+//                      (kda_internal.h) runs it per piece instead: pass A, transition runs,
+//                      bwd_piece_scan_kernel, pass B.
 //   bwd_grad_kernel    per chunk-head: the state the chain did not store, rebuilt from the
 //                      neighbouring chunk's (D of an even chunk from the next chunk's by the
 //                      dS0 step above, S0 of an odd one from the previous chunk's by the state
@@ -581,7 +588,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs a)
 {
     constexpr int kRows = 64 / kCh, kTiles = 8 / kCh, kParts = 2 * kCh;
     constexpr bool kPiece = kMode != kChWhole;
-    static_assert(!kPiece || kParts == kPieceParts, "the cut plan runs one channel part per wave");
+    static_assert(!kPiece || kParts == kPieceParts, "the cut plan runs kCh = 1: two row parts per piece");
     // stage buffers: one where the chains are many (kCh = 1: 33 KB of LDS, so that three
     // workgroups fit a CU, at the price of a barrier before each refill), two otherwise
     constexpr int kSt = kCh == 1 ? 1 : 2;
