@@ -146,6 +146,16 @@ def test_backward_cut_plan_varlen(flags, lb):
     grads_parity(w, 32 + flags, True, f"cut plan varlen flags={flags} lb={lb}")
 
 
+def test_backward_cut_plan_short_walks():
+    """Sequences of two pieces (pass B joins them without a scan step) and of three (one scan
+    step) beside a long one and an empty one, moderate decay."""
+    w = W.make("bwd_cut_short", 1, 0, 2, lengths=[4000, 200, 300, 0], seed=736, lower_bound=-0.5,
+               state_dtype="bf16")
+    L = bwd_piece_len(w.B, w.T, w.H, w.N, True)
+    assert L == 8 and _pieces(w, L) == [32, 2, 3, 1]
+    grads_parity(w, 36, True, "cut plan varlen, walks of 32 / 2 / 3 / 1 pieces")
+
+
 def test_backward_cut_plan_no_states():
     """Cut plan without an initial state or a final-state gradient (both chains start from
     zero)."""
