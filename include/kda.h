@@ -291,11 +291,11 @@ kda_status kda_bwd(const void *q, const void *k, const void *v, const void *g, c
  * 16-token chunk of each head (counted as ceil(T / 16) per batch row, or ceil(T / 16) + N
  * with cu_seqlens) 33.5 KiB of chunk operands, one fp32 state (64 KiB: the state before the
  * chunk for the even chunks of a sequence, dL/dS after it for the odd ones) and the chunk's
- * V' and dL/dV' (8 KiB each), and 64 KiB per head of partial sums; when the pass cuts its
- * walks into pieces, also three fp32 states per (piece, head, direction) (pieces of L chunks,
- * L = max(8, ceil(4 H C / 768)) with C the chunk count above; at most ceil(C / L) + N pieces
- * per head, N the number of sequences).
- * Returns 0 for invalid sizes.
+ * V' and dL/dV' (8 KiB each), 16 bytes per chunk of location records and 64 KiB per head of
+ * partial sums; when the pass cuts its walks into pieces, also three fp32 states per (piece,
+ * head, direction) (pieces of L chunks, L = max(8, ceil(4 H C / 768)) with C the chunk count
+ * above; at most ceil(C / L) + N pieces per head, N the number of sequences).  Returns 0 for
+ * invalid sizes.
  */
 size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N, int has_cu_seqlens);
 
