@@ -62,12 +62,13 @@ def state_bytes(w):
     return b
 
 
-def committed_traffic(workload_name, kernel, source="kda_kernels.hip"):
-    """HBM bytes per step of `kernel` (summed over its launches) from the committed rocprofv3
-    summary of this workload (profiles/kda_fwd_<workload>.md), or None when there is none or
-    the kernel source has changed since the counters were taken."""
+def committed_traffic(workload_name, kernel, source="kda_kernels.hip", pass_="fwd"):
+    """HBM bytes per step of `kernel` (summed over its launches; for the backward pass, "kda_bwd":
+    every kernel of the pass) from the committed rocprofv3 summary of this workload
+    (profiles/kda_<pass_>_<workload>.md), or None when there is none or the kernel source has
+    changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"kda_fwd_{workload_name}.md")
+    path = os.path.join(ROOT, "profiles", f"kda_{pass_}_{workload_name}.md")
     src = os.path.join(ROOT, "gated_delta_rule_86_amd", "csrc", source)
     if not os.path.exists(path):
         return None
@@ -192,7 +193,8 @@ def backward_bench(args, w):
                       "ms_per_step": dt * 1e3, "higher_is_better": True, "dtype": "fp32",
                       "data": "synthetic", "config": dict(w.describe(), head_tokens=w.head_tokens),
                       "roofline": {"bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
-                                   "frac": achieved / 8000.0, "traffic": None,
+                                   "frac": achieved / 8000.0,
+                                   "traffic": committed_traffic(w.name, "kda_bwd", "kda_backward.hip", "bwd"),
                                    "kernel": "kda_bwd, all launches (ops, chain, state-product and gradient kernels)",
                                    "algorithmic_bytes": path_bytes},
                       "workspace_bytes": ws.numel()}), flush=True)
