@@ -195,7 +195,7 @@ def backward_bench(args, w):
                       "roofline": {"bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
                                    "frac": achieved / 8000.0,
                                    "traffic": committed_traffic(w.name, "kda_bwd", "kda_backward.hip", "bwd"),
-                                   "kernel": "kda_bwd, all launches (ops, chain, state-product and gradient kernels)",
+                                   "kernel": "kda_bwd, all launches (chunk records, operands, the two walks (whole or cut plan with its scan), gradients, head sums)",
                                    "algorithmic_bytes": path_bytes},
                       "workspace_bytes": ws.numel()}), flush=True)
 
